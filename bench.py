@@ -1,0 +1,189 @@
+"""Throughput of the chunked gated delta-rule prefill on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload I] [--no-cpu-baseline]
+
+A step is one gdn_prefill call over the whole workload (all heads, all chunks) with
+inputs resident in HBM.  The default workload is the headline one: one sequence of
+T=4096 tokens, 16 heads, d=128, bf16 q/k/v/o, fp32 g/beta/state, chunk 64.  Input
+sets are rotated across steps (more bytes than the 256 MB Infinity Cache) so that
+every step streams from HBM.  Prints ONE JSON line.
+
+roofline.achieved = algorithmic bytes of one launch / mean launch time, where the
+mean launch time comes from HIP events recorded on the launch stream around the
+timed steps (one kernel per step).  Algorithmic bytes per launch:
+    T*(Hk*2*Dk*s + Hv*(2*Dv*s + 8)) + N*Hv*Dv*Dk*4*(2 if an initial state else 1)
+with s = 2 (bf16) or 4 (fp32): q, k read once per key head, v read and o written once
+per value head, g and beta (fp32) read, the fp32 state read (if given) and written.
+Algorithmic FLOPs per full chunk and value head: 6*C*Dk*Dv (three state products)
++ 2*C^2*Dv (intra-chunk output) + 2*C^2*Dk (the K K^T gram) ... see `algorithmic_flops`.
+
+cpu_baseline: the fp64 CPU oracle (test infrastructure, untuned) timed on the host
+cores over the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "GDN prefill tokens/sec (H=16, d=128, T=4096) + % of MFMA/HBM roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # dense
+FP32_MFMA_PEAK_TFLOPS = 157.3
+MALL_BYTES = 256 << 20
+
+
+def algorithmic_bytes(x) -> int:
+    s = 2 if x.io == "bf16" else 4
+    T, Hk, Hv, Dk, Dv, N = x.T_tot, x.Hk, x.Hv, x.Dk, x.Dv, x.N
+    state = N * Hv * Dv * Dk * 4 * (2 if x.initial_state is not None else 1)
+    return T * (Hk * 2 * Dk * s + Hv * (2 * Dv * s + 8)) + state
+
+
+def algorithmic_flops(x, C: int = 64) -> int:
+    """Sum over chunks of n_c tokens: Hv*(6*n_c*Dk*Dv + 2*n_c^2*Dv) + Hk*2*n_c^2*Dk
+    (the three state products K S^T, Q S^T and v^T K; the intra-chunk P v product;
+    the K K^T gram per key head).  This is the method's own work, not the padded
+    tile work of any kernel."""
+    total = 0
+    for L in x.seq_lengths():
+        full, tail = divmod(int(L), C)
+        for n_c, cnt in ((C, full), (tail, 1 if tail else 0)):
+            total += cnt * (x.Hv * (6 * n_c * x.Dk * x.Dv + 2 * n_c * n_c * x.Dv)
+                            + x.Hk * 2 * n_c * n_c * x.Dk)
+    return total
+
+
+def cpu_baseline(x, repeats: int = 3) -> dict:
+    import oracle
+    oracle.load_library()
+    times = []
+    for _ in range(repeats):
+        t0 = time.perf_counter()
+        oracle.recurrent(x.q, x.k, x.v, x.g, x.beta, x.initial_state, x.cu_seqlens)
+        times.append(time.perf_counter() - t0)
+    dt = float(np.median(times))
+    return {"value": x.T_tot / dt, "unit": "tokens/s", "cores": oracle.max_threads(),
+            "kind": "oracle",
+            "sample": f"the whole workload ({x.T_tot} tokens x {x.Hv} heads), fp64 token-by-token "
+                      f"recurrence, OpenMP over (sequence, head); median of {repeats} runs, "
+                      f"{dt:.3f} s each"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", type=int, default=1)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--rotate-bytes", type=int, default=2 * MALL_BYTES,
+                    help="input copies are rotated until they span at least this many bytes")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py: this build runs on one GPU only; --gpus must be 1", file=sys.stderr)
+        return 2
+
+    import torch
+    from linear_attention_chunked_gdn_amd import gdn, inputs
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    x = inputs.make_workload(args.workload)
+    io = torch.bfloat16 if x.io == "bf16" else torch.float32
+
+    per_copy = algorithmic_bytes(x)
+    copies = max(1, -(-args.rotate_bytes // per_copy))
+    sets = []
+    for _ in range(copies):
+        t = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a)).to(dev, dt)  # noqa: E731
+        sets.append(dict(q=t(x.q, io), k=t(x.k, io), v=t(x.v, io), g=t(x.g, torch.float32),
+                         beta=t(x.beta, torch.float32),
+                         init=None if x.initial_state is None else t(x.initial_state, torch.float32),
+                         cu=t(x.cu_seqlens, torch.int32) if x.N > 1 else None,
+                         o=torch.empty((x.T_tot, x.Hv, x.Dv), dtype=io, device=dev),
+                         fs=torch.empty((x.N, x.Hv, x.Dv, x.Dk), dtype=torch.float32, device=dev)))
+
+    def step(i):
+        s = sets[i % copies]
+        gdn.prefill(s["q"], s["k"], s["v"], s["g"], s["beta"], s["init"], s["cu"],
+                    out=s["o"], final_state=s["fs"])
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = ev0.elapsed_time(ev1)
+    ms_per_step = gpu_ms / args.steps
+    tokens = x.T_tot
+
+    # parity of the timed launches' last output against the oracle (headline sizes only)
+    parity = None
+    if x.T_tot * x.Hv <= (1 << 17):
+        import oracle
+        sys.path.insert(0, os.path.join(ROOT, "tests"))
+        from gpu_support import error_stats
+        s = sets[(args.steps - 1) % copies]
+        ro, rf = oracle.recurrent(x.q, x.k, x.v, x.g, x.beta, x.initial_state, x.cu_seqlens)
+        eo = error_stats(s["o"].double().cpu().numpy(), ro)
+        ef = error_stats(s["fs"].double().cpu().numpy(), rf)
+        parity = {"o_rel_rms": eo["rel_rms"], "state_rel_rms": ef["rel_rms"],
+                  "o_nmse": eo["nmse"], "state_nmse": ef["nmse"]}
+
+    nbytes = algorithmic_bytes(x)
+    flops = algorithmic_flops(x)
+    sec = ms_per_step / 1e3
+    plan = gdn.prefill_plan(x.N, x.Hv, gdn.GDN_BF16 if x.io == "bf16" else gdn.GDN_F32)
+    mfma_peak = BF16_MFMA_PEAK_TFLOPS if x.io == "bf16" else FP32_MFMA_PEAK_TFLOPS
+    rec = {
+        "metric": METRIC,
+        "value": tokens / sec,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if x.io == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": x.name, "sequences": x.N, "tokens": x.T_tot, "Hk": x.Hk, "Hv": x.Hv,
+                   "d": x.Dk, "chunk": 64, "io": x.io, "state": "fp32",
+                   "initial_state": x.initial_state is not None},
+        "roofline": {"bound": "hbm", "achieved": nbytes / sec / 1e9, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": nbytes / sec / 1e9 / HBM_PEAK_GBS, "traffic": None},
+        "mfma": {"achieved": flops / sec / 1e12, "peak": mfma_peak, "unit": "TFLOP/s",
+                 "frac": flops / sec / 1e12 / mfma_peak, "algorithmic_flops": flops},
+        "algorithmic_bytes": nbytes,
+        "launch": {"kernel": "gdn_prefill_kernel", "dv_per_workgroup": plan["dv_per_workgroup"],
+                   "workgroups": plan["workgroups"], "lds_bytes": plan["lds_bytes"],
+                   "threads": 256, "input_copies_rotated": copies},
+        "wall_s_timed": wall,
+        "parity": parity,
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(x)
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,129 @@
+/*
+ * gdn.h -- C ABI of the MI355X (gfx950) gated delta-rule library.
+ *
+ * The library computes chunked Gated DeltaNet linear attention for prefill and a
+ * single-token decode step.  Per sequence n and value head h, with key/query head
+ * hk = h % Hk (the GQA head replication hv % Hk described on the page
+ * "Exp 2026-07-13 -- Linear-Attention Scans on the NPU", section 4), the state
+ * S (Dv x Dk, fp32) evolves token by token as
+ *
+ *     S_t = alpha_t * S_{t-1} * (I - beta_t k_t k_t^T) + beta_t * v_t k_t^T,
+ *     o_t = S_t q_t,               alpha_t = exp(g_t),
+ *
+ * i.e. the state is updated with k_t, v_t first and the output is then read with
+ * q_t from the updated state ("Empowering Hybrid Attention Models on NPUs",
+ * section 2.1).  Prefill evaluates this exactly (up to rounding) with the chunkwise
+ * Map-Reduce-Map decomposition of that page (operators #1 Gate, #2 KKT, #3 Solve,
+ * #4 W/U, #5 H, #6 O), chunk-first ordered and with the inverse factored out of
+ * the W product as in its section 5.  No scaling is applied to q.
+ *
+ * Conventions for every entry point
+ *   - All tensor arguments are DEVICE pointers owned by the caller, row-major and
+ *     contiguous, 16-byte aligned.  The library never allocates, frees or retains
+ *     device memory and keeps no pointer after the call returns.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and the
+ *     call returns without synchronising.  Inputs are never written.
+ *   - Argument errors are detected on the host before anything is enqueued; the
+ *     call then returns a non-OK status, launches nothing and records a message
+ *     retrievable with gdn_last_error() (thread-local).  A failed kernel launch
+ *     returns GDN_ERR_DEVICE.  No C++ exception crosses this interface.
+ *   - Supported shapes: Dk = Dv = 128 and chunk_size = 64; anything else returns
+ *     GDN_ERR_UNSUPPORTED.
+ */
+#ifndef GDN_MI355X_GDN_H
+#define GDN_MI355X_GDN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum gdn_status {
+    GDN_OK = 0,
+    GDN_ERR_INVALID_ARGUMENT = 1,  /* null/misaligned pointer, bad size or head counts    */
+    GDN_ERR_UNSUPPORTED = 2,       /* valid request this build does not implement         */
+    GDN_ERR_DEVICE = 3             /* the HIP runtime reported an error on launch          */
+} gdn_status;
+
+typedef enum gdn_dtype {
+    GDN_F32 = 0,   /* q, k, v, o stored as IEEE fp32; all arithmetic in fp32                   */
+    GDN_BF16 = 1   /* q, k, v, o stored as bf16; fp32 accumulation, fp32 state, bf16 products  */
+} gdn_dtype;
+
+/*
+ * gdn_prefill -- packed variable-length chunked prefill.
+ *
+ * Operation: the recurrence above over every sequence of a packed batch, each
+ * sequence starting from its own initial state ("Empowering Hybrid Attention Models
+ * on NPUs", section 3: the online stage takes Q/K/V, gates and an initial state and
+ * returns outputs plus updated states for later decoding).  Chunks of `chunk_size`
+ * tokens restart at every sequence start; a sequence's last chunk may be short.
+ *
+ *   q, k           [T_tot, Hk, Dk]  io_dtype      queries / keys, per key head
+ *   v              [T_tot, Hv, Dv]  io_dtype      values, per value head
+ *   g              [T_tot, Hv]      fp32          natural log of the decay alpha
+ *                                                 (finite; normally <= 0)
+ *   beta           [T_tot, Hv]      fp32          delta-rule write strength
+ *   initial_state  [N, Hv, Dv, Dk]  fp32 or NULL  NULL means zero states
+ *   cu_seqlens     [N+1]            int32 device  cu[0] = 0, nondecreasing,
+ *                                                 cu[N] = T_tot (precondition, not
+ *                                                 checked on the device); may be
+ *                                                 NULL only when N == 1
+ *   N, T_tot       number of sequences (>= 1) and packed tokens (>= 0)
+ *   Hk, Hv         key and value head counts, Hv % Hk == 0
+ *   Dk, Dv         head dimensions (128)
+ *   chunk_size     64
+ *   io_dtype       storage type of q, k, v and o
+ *   o              [T_tot, Hv, Dv]  io_dtype      written; must not alias an input
+ *   final_state    [N, Hv, Dv, Dk]  fp32 or NULL  written when non-NULL; may alias
+ *                                                 initial_state exactly (in-place)
+ *   stream         hipStream_t or NULL
+ *
+ * A sequence of length 0 gets final_state = initial_state (or zeros).
+ */
+gdn_status gdn_prefill(const void *q, const void *k, const void *v,
+                       const float *g, const float *beta,
+                       const float *initial_state, const int32_t *cu_seqlens,
+                       int32_t N, int32_t T_tot, int32_t Hk, int32_t Hv,
+                       int32_t Dk, int32_t Dv, int32_t chunk_size, gdn_dtype io_dtype,
+                       void *o, float *final_state, void *stream);
+
+/*
+ * gdn_decode_step -- one token per sequence, state updated in place (the
+ * token-by-token recurrence that serves decoding: "Empowering Hybrid Attention
+ * Models on NPUs", section 2.1).
+ *
+ *   q, k     [B, Hk, Dk]      io_dtype
+ *   v        [B, Hv, Dv]      io_dtype
+ *   g, beta  [B, Hv]          fp32
+ *   state    [B, Hv, Dv, Dk]  fp32, read and overwritten
+ *   o        [B, Hv, Dv]      io_dtype, written
+ */
+gdn_status gdn_decode_step(const void *q, const void *k, const void *v,
+                           const float *g, const float *beta, float *state,
+                           int32_t B, int32_t Hk, int32_t Hv, int32_t Dk, int32_t Dv,
+                           gdn_dtype io_dtype, void *o, void *stream);
+
+/*
+ * gdn_prefill_plan -- the launch shape gdn_prefill would use for these sizes,
+ * without launching anything: the width of the value-channel slice each workgroup
+ * owns (the column-wise split of S, "Empowering Hybrid Attention Models on NPUs",
+ * section 4, Figure 8(b)), the number of workgroups and the LDS bytes per
+ * workgroup.  Any output pointer may be NULL.  Host pointers.
+ */
+gdn_status gdn_prefill_plan(int32_t N, int32_t Hv, int32_t Dv, gdn_dtype io_dtype,
+                            int32_t *dv_per_workgroup, int32_t *workgroups,
+                            int32_t *lds_bytes);
+
+/* Static English name of a status code. */
+const char *gdn_status_string(gdn_status s);
+
+/* Detail of the last non-OK return on the calling thread ("" if none). */
+const char *gdn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_MI355X_GDN_H */

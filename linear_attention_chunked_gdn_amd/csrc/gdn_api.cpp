@@ -1,0 +1,201 @@
+// C-ABI entry points of the gated delta-rule library (declared in include/gdn.h):
+// argument validation, launch planning and error reporting.  All compute runs in
+// the HIP kernels of gdn_prefill.hip and gdn_decode.hip.
+#include "gdn.h"
+#include "gdn_launch.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+
+namespace {
+
+thread_local std::string g_last_error;
+
+gdn_status fail(gdn_status s, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return s;
+}
+
+gdn_status ok() {
+    g_last_error.clear();
+    return GDN_OK;
+}
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+struct Range {
+    const char *lo, *hi;
+    const char *name;
+};
+
+Range range(const void *p, size_t bytes, const char *name) {
+    const char *c = static_cast<const char *>(p);
+    return Range{c, c ? c + bytes : c, name};
+}
+
+bool overlap(const Range &a, const Range &b) {
+    if (!a.lo || !b.lo || a.lo == a.hi || b.lo == b.hi) return false;
+    return a.lo < b.hi && b.lo < a.hi;
+}
+
+constexpr int kD = 128;
+constexpr int kChunk = 64;
+
+// Value channels per workgroup.  A head's state is split into 128 / dvs independent
+// column slices; narrower slices give more workgroups for the same work at the cost
+// of recomputing the chunk's S-independent quantities in each slice.
+int choose_dvs(int32_t N, int32_t Hv, gdn_dtype dt) {
+    (void)N;
+    (void)Hv;
+    const char *env = std::getenv("GDN_DVS");
+    if (env) {
+        const int d = std::atoi(env);
+        if (gdn::prefill_lds_bytes(dt == GDN_BF16, d) > 0) return d;
+    }
+    return 16;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *gdn_status_string(gdn_status s) {
+    switch (s) {
+        case GDN_OK: return "ok";
+        case GDN_ERR_INVALID_ARGUMENT: return "invalid argument";
+        case GDN_ERR_UNSUPPORTED: return "unsupported";
+        case GDN_ERR_DEVICE: return "device error";
+    }
+    return "unknown status";
+}
+
+const char *gdn_last_error(void) { return g_last_error.c_str(); }
+
+gdn_status gdn_prefill_plan(int32_t N, int32_t Hv, int32_t Dv, gdn_dtype io_dtype,
+                            int32_t *dv_per_workgroup, int32_t *workgroups, int32_t *lds_bytes) {
+    if (io_dtype != GDN_F32 && io_dtype != GDN_BF16)
+        return fail(GDN_ERR_INVALID_ARGUMENT, "io_dtype %d is not GDN_F32 or GDN_BF16", (int)io_dtype);
+    if (N < 1 || Hv < 1) return fail(GDN_ERR_INVALID_ARGUMENT, "N=%d and Hv=%d must be >= 1", N, Hv);
+    if (Dv != kD) return fail(GDN_ERR_UNSUPPORTED, "Dv=%d (only 128 is implemented)", Dv);
+    const int dvs = choose_dvs(N, Hv, io_dtype);
+    const long long wg = (long long)N * Hv * (kD / dvs);
+    if (wg > 0x7fffffffLL) return fail(GDN_ERR_UNSUPPORTED, "%lld workgroups exceed the grid limit", wg);
+    if (dv_per_workgroup) *dv_per_workgroup = dvs;
+    if (workgroups) *workgroups = (int32_t)wg;
+    if (lds_bytes) *lds_bytes = gdn::prefill_lds_bytes(io_dtype == GDN_BF16, dvs);
+    return ok();
+}
+
+gdn_status gdn_prefill(const void *q, const void *k, const void *v, const float *g,
+                       const float *beta, const float *initial_state, const int32_t *cu_seqlens,
+                       int32_t N, int32_t T_tot, int32_t Hk, int32_t Hv, int32_t Dk, int32_t Dv,
+                       int32_t chunk_size, gdn_dtype io_dtype, void *o, float *final_state,
+                       void *stream) {
+    if (io_dtype != GDN_F32 && io_dtype != GDN_BF16)
+        return fail(GDN_ERR_INVALID_ARGUMENT, "io_dtype %d is not GDN_F32 or GDN_BF16", (int)io_dtype);
+    if (N < 1) return fail(GDN_ERR_INVALID_ARGUMENT, "N=%d must be >= 1", N);
+    if (T_tot < 0) return fail(GDN_ERR_INVALID_ARGUMENT, "T_tot=%d must be >= 0", T_tot);
+    if (Hk < 1 || Hv < 1) return fail(GDN_ERR_INVALID_ARGUMENT, "Hk=%d, Hv=%d must be >= 1", Hk, Hv);
+    if (Hv % Hk != 0)
+        return fail(GDN_ERR_INVALID_ARGUMENT, "Hv=%d is not a multiple of Hk=%d", Hv, Hk);
+    if (Dk != kD || Dv != kD)
+        return fail(GDN_ERR_UNSUPPORTED, "Dk=%d, Dv=%d (only 128 is implemented)", Dk, Dv);
+    if (chunk_size != kChunk)
+        return fail(GDN_ERR_UNSUPPORTED, "chunk_size=%d (only 64 is implemented)", chunk_size);
+    if (N > 1 && !cu_seqlens)
+        return fail(GDN_ERR_INVALID_ARGUMENT, "cu_seqlens is required when N=%d > 1", N);
+    if (T_tot > 0 && (!q || !k || !v || !g || !beta || !o))
+        return fail(GDN_ERR_INVALID_ARGUMENT, "q, k, v, g, beta and o must be non-null when T_tot > 0");
+    const void *a16[] = {q, k, v, o, initial_state, final_state};
+    const char *n16[] = {"q", "k", "v", "o", "initial_state", "final_state"};
+    for (int i = 0; i < 6; ++i)
+        if (!aligned(a16[i], 16))
+            return fail(GDN_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", n16[i]);
+    if (!aligned(g, 4) || !aligned(beta, 4) || !aligned(cu_seqlens, 4))
+        return fail(GDN_ERR_INVALID_ARGUMENT, "g, beta and cu_seqlens must be 4-byte aligned");
+
+    const size_t es = io_dtype == GDN_BF16 ? 2 : 4;
+    const size_t T = (size_t)T_tot;
+    const size_t state_bytes = (size_t)N * Hv * kD * kD * sizeof(float);
+    const Range ro = range(o, T * Hv * kD * es, "o");
+    const Range ins[] = {range(q, T * Hk * kD * es, "q"), range(k, T * Hk * kD * es, "k"),
+                         range(v, T * Hv * kD * es, "v"), range(g, T * Hv * 4, "g"),
+                         range(beta, T * Hv * 4, "beta"),
+                         range(initial_state, state_bytes, "initial_state"),
+                         range(cu_seqlens, (size_t)(N + 1) * 4, "cu_seqlens")};
+    const Range rf = range(final_state, state_bytes, "final_state");
+    for (const Range &r : ins) {
+        if (overlap(ro, r)) return fail(GDN_ERR_INVALID_ARGUMENT, "o overlaps %s", r.name);
+        if (overlap(rf, r) && !(r.lo == reinterpret_cast<const char *>(initial_state) && rf.lo == r.lo))
+            return fail(GDN_ERR_INVALID_ARGUMENT, "final_state overlaps %s", r.name);
+    }
+    if (overlap(ro, rf)) return fail(GDN_ERR_INVALID_ARGUMENT, "o overlaps final_state");
+
+    int32_t dvs = 0, wg = 0;
+    gdn_status ps = gdn_prefill_plan(N, Hv, Dv, io_dtype, &dvs, &wg, nullptr);
+    if (ps != GDN_OK) return ps;
+    if (T_tot == 0 && !final_state) return ok();   // nothing to compute or write
+
+    gdn::PrefillArgs a;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
+    a.s0 = initial_state; a.cu = cu_seqlens; a.o = o; a.sN = final_state;
+    a.N = N; a.T_tot = T_tot; a.Hk = Hk; a.Hv = Hv; a.nslices = kD / dvs;
+    (void)hipGetLastError();
+    const hipError_t e = gdn::launch_prefill(a, io_dtype == GDN_BF16, dvs, wg,
+                                             static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return fail(GDN_ERR_DEVICE, "prefill launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+gdn_status gdn_decode_step(const void *q, const void *k, const void *v, const float *g,
+                           const float *beta, float *state, int32_t B, int32_t Hk, int32_t Hv,
+                           int32_t Dk, int32_t Dv, gdn_dtype io_dtype, void *o, void *stream) {
+    if (io_dtype != GDN_F32 && io_dtype != GDN_BF16)
+        return fail(GDN_ERR_INVALID_ARGUMENT, "io_dtype %d is not GDN_F32 or GDN_BF16", (int)io_dtype);
+    if (B < 1 || Hk < 1 || Hv < 1)
+        return fail(GDN_ERR_INVALID_ARGUMENT, "B=%d, Hk=%d, Hv=%d must be >= 1", B, Hk, Hv);
+    if (Hv % Hk != 0)
+        return fail(GDN_ERR_INVALID_ARGUMENT, "Hv=%d is not a multiple of Hk=%d", Hv, Hk);
+    if (Dk != kD || Dv != kD)
+        return fail(GDN_ERR_UNSUPPORTED, "Dk=%d, Dv=%d (only 128 is implemented)", Dk, Dv);
+    if (!q || !k || !v || !g || !beta || !state || !o)
+        return fail(GDN_ERR_INVALID_ARGUMENT, "all tensor arguments of gdn_decode_step are required");
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(state, 16) || !aligned(v, 4) || !aligned(o, 4) ||
+        !aligned(g, 4) || !aligned(beta, 4))
+        return fail(GDN_ERR_INVALID_ARGUMENT, "q, k and state must be 16-byte aligned, the rest 4-byte");
+    if ((long long)B * Hv * (kD / 16) > 0x7fffffffLL)
+        return fail(GDN_ERR_UNSUPPORTED, "B*Hv too large for one launch");
+    const size_t es = io_dtype == GDN_BF16 ? 2 : 4;
+    const Range ro = range(o, (size_t)B * Hv * kD * es, "o");
+    const Range rs = range(state, (size_t)B * Hv * kD * kD * 4, "state");
+    const Range ins[] = {range(q, (size_t)B * Hk * kD * es, "q"), range(k, (size_t)B * Hk * kD * es, "k"),
+                         range(v, (size_t)B * Hv * kD * es, "v"), range(g, (size_t)B * Hv * 4, "g"),
+                         range(beta, (size_t)B * Hv * 4, "beta")};
+    for (const Range &r : ins) {
+        if (overlap(ro, r)) return fail(GDN_ERR_INVALID_ARGUMENT, "o overlaps %s", r.name);
+        if (overlap(rs, r)) return fail(GDN_ERR_INVALID_ARGUMENT, "state overlaps %s", r.name);
+    }
+    if (overlap(ro, rs)) return fail(GDN_ERR_INVALID_ARGUMENT, "o overlaps state");
+
+    gdn::DecodeArgs a;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.state = state; a.o = o;
+    a.B = B; a.Hk = Hk; a.Hv = Hv;
+    (void)hipGetLastError();
+    const hipError_t e = gdn::launch_decode(a, io_dtype == GDN_BF16, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return fail(GDN_ERR_DEVICE, "decode launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+}  // extern "C"

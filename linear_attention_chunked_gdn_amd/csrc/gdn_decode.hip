@@ -1,0 +1,105 @@
+// Single-token gated delta-rule step (decoding) for gfx950.
+//
+// For each (sequence b, value head h) with key head h % Hk, one token updates the
+// fp32 state in place and reads the output from the updated state ("Empowering
+// Hybrid Attention Models on NPUs", section 2.1: token-by-token recurrence serves
+// decoding; the state is updated with k_t, v_t, then read with q_t):
+//
+//   S <- alpha S (I - beta k k^T) + beta v k^T = alpha S - alpha beta (S k) k^T + beta v k^T
+//   o  = S q
+//
+// Every value-channel row of S evolves independently given k, q and its own v
+// entry, so the kernel is row-parallel: 16 lanes own one row (8 key channels each,
+// two 16-byte loads), the two dot products are reduced across those 16 lanes, and
+// a 256-thread workgroup covers 16 rows.  The step is bound by the state's read and
+// write (128 KiB per head).
+#include "gdn_device.h"
+#include "gdn_launch.h"
+
+namespace gdn {
+
+constexpr int DEC_D = 128;
+constexpr int DEC_ROWS = 16;   // rows per workgroup
+
+template <bool BF16>
+__device__ __forceinline__ void load8_io(const void *base, size_t off, float *x) {
+    if constexpr (BF16) {
+        const uint4 u = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(base) + off);
+        const uint16_t *e = reinterpret_cast<const uint16_t *>(&u);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = bf16_bits_to_f32(e[i]);
+    } else {
+        const float *p = reinterpret_cast<const float *>(base) + off;
+        const f32x4 a = *reinterpret_cast<const f32x4 *>(p);
+        const f32x4 b = *reinterpret_cast<const f32x4 *>(p + 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { x[i] = a[i]; x[4 + i] = b[i]; }
+    }
+}
+
+__device__ __forceinline__ float sum16(float x) {
+#pragma unroll
+    for (int m = 8; m >= 1; m >>= 1) x += __shfl_xor(x, m, 16);
+    return x;
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void gdn_decode_kernel(const DecodeArgs a) {
+    constexpr int RB = DEC_D / DEC_ROWS;
+    const int rb = blockIdx.x % RB;
+    const int bh = blockIdx.x / RB;
+    const int h = bh % a.Hv, b = bh / a.Hv, hk = h % a.Hk;
+    const int row = rb * DEC_ROWS + (threadIdx.x >> 4);
+    const int l = threadIdx.x & 15;
+
+    float *srow = a.state + (((size_t)b * a.Hv + h) * DEC_D + row) * DEC_D + 8 * l;
+    float S[8], kk[8], qq[8];
+    {
+        const f32x4 s0 = *reinterpret_cast<const f32x4 *>(srow);
+        const f32x4 s1 = *reinterpret_cast<const f32x4 *>(srow + 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { S[i] = s0[i]; S[4 + i] = s1[i]; }
+    }
+    const size_t koff = ((size_t)b * a.Hk + hk) * DEC_D + 8 * l;
+    load8_io<BF16>(a.k, koff, kk);
+    load8_io<BF16>(a.q, koff, qq);
+    float vi;
+    const size_t voff = ((size_t)b * a.Hv + h) * DEC_D + row;
+    if constexpr (BF16) vi = bf16_bits_to_f32(reinterpret_cast<const uint16_t *>(a.v)[voff]);
+    else vi = reinterpret_cast<const float *>(a.v)[voff];
+    const float alpha = __expf(a.g[(size_t)b * a.Hv + h]);
+    const float beta = a.beta[(size_t)b * a.Hv + h];
+
+    float u = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) u += S[i] * kk[i];
+    u = sum16(u);                               // (S k)_row, state before the token
+    const float erase = alpha * beta * u;
+    const float write = beta * vi;
+    float o = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        S[i] = alpha * S[i] - erase * kk[i] + write * kk[i];
+        o += S[i] * qq[i];
+    }
+    o = sum16(o);                               // (S q)_row, updated state
+    *reinterpret_cast<f32x4 *>(srow) = f32x4{S[0], S[1], S[2], S[3]};
+    *reinterpret_cast<f32x4 *>(srow + 4) = f32x4{S[4], S[5], S[6], S[7]};
+    if (l == 0) {
+        if constexpr (BF16)
+            reinterpret_cast<uint16_t *>(a.o)[voff] = __builtin_bit_cast(uint16_t, f32_to_bf16(o));
+        else
+            reinterpret_cast<float *>(a.o)[voff] = o;
+    }
+}
+
+hipError_t launch_decode(const DecodeArgs &a, bool bf16, hipStream_t stream) {
+    const int grid = a.B * a.Hv * (DEC_D / DEC_ROWS);
+    if (bf16)
+        hipLaunchKernelGGL(gdn_decode_kernel<true>, dim3(grid), dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL(gdn_decode_kernel<false>, dim3(grid), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace gdn

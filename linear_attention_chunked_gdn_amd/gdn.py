@@ -1,0 +1,170 @@
+"""Python binding of the gated delta-rule C-ABI (include/gdn.h).
+
+Argument marshalling only: tensors are checked for device, dtype, shape and
+contiguity, outputs are allocated with torch, and raw device pointers plus torch's
+current HIP stream are handed to ``gdn_prefill`` / ``gdn_decode_step`` in
+``libgdn_mi355x.so``.  Every step of the computation runs in the library's HIP
+kernels; there is no fallback: if the library is missing or the tensors are not
+on a GPU the call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+from .build import LIB_PATH
+
+GDN_F32 = 0
+GDN_BF16 = 1
+D = 128
+CHUNK = 64
+
+_lib = None
+
+
+class GDNError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+def load_library(path: str = LIB_PATH):
+    """Load the built HIP library (never builds it)."""
+    global _lib
+    if _lib is not None and path == LIB_PATH:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run `python -m linear_attention_chunked_gdn_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, fp, ip, i32 = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32
+    lib.gdn_prefill.argtypes = [vp, vp, vp, fp, fp, fp, ip, i32, i32, i32, i32, i32, i32, i32,
+                                ctypes.c_int, vp, fp, vp]
+    lib.gdn_prefill.restype = ctypes.c_int
+    lib.gdn_decode_step.argtypes = [vp, vp, vp, fp, fp, fp, i32, i32, i32, i32, i32, ctypes.c_int,
+                                    vp, vp]
+    lib.gdn_decode_step.restype = ctypes.c_int
+    p32 = ctypes.POINTER(ctypes.c_int32)
+    lib.gdn_prefill_plan.argtypes = [i32, i32, i32, ctypes.c_int, p32, p32, p32]
+    lib.gdn_prefill_plan.restype = ctypes.c_int
+    lib.gdn_status_string.argtypes = [ctypes.c_int]
+    lib.gdn_status_string.restype = ctypes.c_char_p
+    lib.gdn_last_error.argtypes = []
+    lib.gdn_last_error.restype = ctypes.c_char_p
+    if path == LIB_PATH:
+        _lib = lib
+    return lib
+
+
+def _check(lib, status: int, what: str):
+    if status != 0:
+        name = lib.gdn_status_string(status).decode()
+        detail = lib.gdn_last_error().decode()
+        raise GDNError(status, f"{what}: {name}: {detail}")
+
+
+def _io_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return GDN_BF16
+    if t.dtype == torch.float32:
+        return GDN_F32
+    raise TypeError(f"q/k/v must be bfloat16 or float32, got {t.dtype}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t: torch.Tensor, name: str, dtype, shape, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+            beta: torch.Tensor, initial_state: Optional[torch.Tensor] = None,
+            cu_seqlens: Optional[torch.Tensor] = None, chunk_size: int = CHUNK,
+            output_final_state: bool = True, out: Optional[torch.Tensor] = None,
+            final_state: Optional[torch.Tensor] = None, lib=None
+            ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Packed chunked prefill.  q, k: [T, Hk, 128]; v: [T, Hv, 128] (bf16 or fp32, all
+    the same); g, beta: [T, Hv] fp32; initial_state: [N, Hv, 128, 128] fp32 or None;
+    cu_seqlens: [N+1] int32 on the device, or None for one sequence.  Returns
+    (o [T, Hv, 128], final_state [N, Hv, 128, 128] fp32 or None)."""
+    lib = lib or load_library()
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("gdn.prefill runs on the GPU only; q is on " + str(dev))
+    io = _io_code(q)
+    T, Hk, Dk = q.shape
+    Hv, Dv = v.shape[1], v.shape[2]
+    N = 1 if cu_seqlens is None else cu_seqlens.shape[0] - 1
+    _need(q, "q", q.dtype, (T, Hk, Dk), dev)
+    _need(k, "k", q.dtype, (T, Hk, Dk), dev)
+    _need(v, "v", q.dtype, (T, Hv, Dv), dev)
+    _need(g, "g", torch.float32, (T, Hv), dev)
+    _need(beta, "beta", torch.float32, (T, Hv), dev)
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,), dev)
+    if initial_state is not None:
+        _need(initial_state, "initial_state", torch.float32, (N, Hv, Dv, Dk), dev)
+    if out is None:
+        out = torch.empty((T, Hv, Dv), dtype=q.dtype, device=dev)
+    _need(out, "out", q.dtype, (T, Hv, Dv), dev)
+    if output_final_state and final_state is None:
+        final_state = torch.empty((N, Hv, Dv, Dk), dtype=torch.float32, device=dev)
+    if final_state is not None:
+        _need(final_state, "final_state", torch.float32, (N, Hv, Dv, Dk), dev)
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        st = lib.gdn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
+                             _ptr(cu_seqlens), N, T, Hk, Hv, Dk, Dv, chunk_size, io, _ptr(out),
+                             _ptr(final_state), ctypes.c_void_p(stream))
+    _check(lib, st, "gdn_prefill")
+    return out, final_state
+
+
+def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                beta: torch.Tensor, state: torch.Tensor, out: Optional[torch.Tensor] = None,
+                lib=None) -> torch.Tensor:
+    """One token per sequence; ``state`` [B, Hv, 128, 128] fp32 is updated in place.
+    q, k: [B, Hk, 128]; v: [B, Hv, 128]; g, beta: [B, Hv].  Returns o [B, Hv, 128]."""
+    lib = lib or load_library()
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("gdn.decode_step runs on the GPU only; q is on " + str(dev))
+    io = _io_code(q)
+    B, Hk, Dk = q.shape
+    Hv, Dv = v.shape[1], v.shape[2]
+    _need(k, "k", q.dtype, (B, Hk, Dk), dev)
+    _need(v, "v", q.dtype, (B, Hv, Dv), dev)
+    _need(g, "g", torch.float32, (B, Hv), dev)
+    _need(beta, "beta", torch.float32, (B, Hv), dev)
+    _need(state, "state", torch.float32, (B, Hv, Dv, Dk), dev)
+    if out is None:
+        out = torch.empty((B, Hv, Dv), dtype=q.dtype, device=dev)
+    _need(out, "out", q.dtype, (B, Hv, Dv), dev)
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        st = lib.gdn_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state),
+                                 B, Hk, Hv, Dk, Dv, io, _ptr(out), ctypes.c_void_p(stream))
+    _check(lib, st, "gdn_decode_step")
+    return out
+
+
+def prefill_plan(N: int, Hv: int, io_dtype: int = GDN_BF16, lib=None) -> dict:
+    """Launch shape of gdn_prefill for these sizes (host only, launches nothing)."""
+    lib = lib or load_library()
+    dvs, wg, lds = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    st = lib.gdn_prefill_plan(N, Hv, D, io_dtype, ctypes.byref(dvs), ctypes.byref(wg), ctypes.byref(lds))
+    _check(lib, st, "gdn_prefill_plan")
+    return dict(dv_per_workgroup=dvs.value, workgroups=wg.value, lds_bytes=lds.value)

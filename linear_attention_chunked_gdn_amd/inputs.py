@@ -29,11 +29,16 @@ SEED_BASE = 20260000
 
 def round_to_bf16(x: np.ndarray) -> np.ndarray:
     """Round float32 values to the nearest bf16 (ties to even); return float32."""
-    x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    bias = 0x7FFF + ((u >> 16) & 1)
-    r = ((u + bias) & 0xFFFF0000).astype(np.uint32)
-    return r.view(np.float32).reshape(x.shape)
+    x = np.array(x, dtype=np.float32, copy=True, order="C")
+    u = x.view(np.uint32)
+    if not np.all(np.isfinite(x)):
+        raise ValueError("round_to_bf16 expects finite values")
+    # finite floats: u + 0x8000 stays below 2^32, so uint32 arithmetic cannot wrap
+    bias = (u >> 16) & np.uint32(1)
+    bias += np.uint32(0x7FFF)
+    u += bias
+    u &= np.uint32(0xFFFF0000)
+    return x
 
 
 def bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -44,8 +49,10 @@ def bf16_bits(x: np.ndarray) -> np.ndarray:
 
 def _l2_normalize(x: np.ndarray) -> np.ndarray:
     # per (token, head) vector, computed in float32
-    n = np.sqrt(np.sum(x.astype(np.float32) ** 2, axis=-1, keepdims=True, dtype=np.float32))
-    return (x / np.maximum(n, np.float32(1e-12))).astype(np.float32)
+    x = np.asarray(x, dtype=np.float32)
+    n = np.sqrt(np.einsum("...i,...i->...", x, x, dtype=np.float32))[..., None]
+    x /= np.maximum(n, np.float32(1e-12))
+    return x
 
 
 def _sigmoid64(x: np.ndarray) -> np.ndarray:

@@ -1,0 +1,110 @@
+"""The C-ABI library on a host without a GPU: it loads, exports every entry point
+include/gdn.h declares, and its host-side validation rejects bad arguments before
+anything is launched (no compute call is made here)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from linear_attention_chunked_gdn_amd import build, gdn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(build.LIB_PATH):
+        build.build_library()
+    return gdn.load_library()
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == sorted(
+        ["gdn_prefill", "gdn_decode_step", "gdn_prefill_plan", "gdn_status_string", "gdn_last_error"])
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", build.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (gdn_\w+)$", out, flags=re.M))
+    for name in declared_functions():
+        assert name in exported, f"{name} is declared in gdn.h but not exported"
+        assert hasattr(lib, name)
+
+
+def test_header_compiles_as_c():
+    src = f'#include "{HEADER}"\nint main(void) {{ return (int)GDN_OK; }}\n'
+    res = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-x", "c", "-", "-o", os.devnull],
+                         input=src, capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr
+
+
+def test_status_strings(lib):
+    assert lib.gdn_status_string(0) == b"ok"
+    assert lib.gdn_status_string(1) == b"invalid argument"
+    assert lib.gdn_status_string(2) == b"unsupported"
+    assert lib.gdn_status_string(3) == b"device error"
+
+
+def _prefill(lib, **over):
+    # fake, 16-byte aligned, never-dereferenced addresses: validation fails before any use
+    a = dict(q=0x10000, k=0x20000, v=0x30000, g=0x40000, beta=0x50000, s0=None, cu=None,
+             N=1, T=10, Hk=2, Hv=4, Dk=128, Dv=128, C=64, io=1, o=0x60000, fs=None)
+    a.update(over)
+    p = lambda x: None if x is None else ctypes.c_void_p(x)  # noqa: E731
+    return lib.gdn_prefill(p(a["q"]), p(a["k"]), p(a["v"]), p(a["g"]), p(a["beta"]), p(a["s0"]),
+                           p(a["cu"]), a["N"], a["T"], a["Hk"], a["Hv"], a["Dk"], a["Dv"], a["C"],
+                           a["io"], p(a["o"]), p(a["fs"]), None)
+
+
+@pytest.mark.parametrize("over,status,msg", [
+    (dict(Hv=3), 1, "multiple"),
+    (dict(Dk=64), 2, "Dk=64"),
+    (dict(Dv=256), 2, "Dv=256"),
+    (dict(C=32), 2, "chunk_size"),
+    (dict(N=0), 1, "N=0"),
+    (dict(T=-1), 1, "T_tot"),
+    (dict(N=2), 1, "cu_seqlens"),
+    (dict(q=None), 1, "non-null"),
+    (dict(io=7), 1, "io_dtype"),
+    (dict(k=0x20008), 1, "aligned"),
+    (dict(o=0x30000), 1, "overlaps"),
+    (dict(s0=0x70000, fs=0x70100), 1, "final_state overlaps"),
+])
+def test_prefill_rejects(lib, over, status, msg):
+    st = _prefill(lib, **over)
+    assert st == status
+    assert msg in lib.gdn_last_error().decode()
+
+
+def test_prefill_nothing_to_do_is_ok(lib):
+    # T_tot = 0 without a final state: valid, and nothing is launched
+    assert _prefill(lib, q=None, k=None, v=None, g=None, beta=None, o=None, T=0) == 0
+    assert lib.gdn_last_error() == b""
+
+
+def test_decode_rejects(lib):
+    p = ctypes.c_void_p
+    st = lib.gdn_decode_step(p(0x1000), p(0x2000), p(0x3000), p(0x4000), p(0x5000), None,
+                             1, 1, 1, 128, 128, 1, p(0x6000), None)
+    assert st == 1 and b"required" in lib.gdn_last_error()
+    st = lib.gdn_decode_step(p(0x1000), p(0x2000), p(0x3000), p(0x4000), p(0x5000), p(0x10000),
+                             1, 2, 3, 128, 128, 1, p(0x6000), None)
+    assert st == 1
+
+
+def test_plan(lib):
+    plan = gdn.prefill_plan(1, 16, gdn.GDN_BF16, lib=lib)
+    assert plan["workgroups"] * plan["dv_per_workgroup"] == 16 * 128
+    assert 0 < plan["lds_bytes"] <= 160 * 1024
+    plan32 = gdn.prefill_plan(1, 1, gdn.GDN_F32, lib=lib)
+    assert 0 < plan32["lds_bytes"] <= 160 * 1024
