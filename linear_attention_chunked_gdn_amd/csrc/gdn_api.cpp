@@ -1,6 +1,6 @@
 // C-ABI entry points of the gated delta-rule library (declared in include/gdn.h):
 // argument validation, launch planning and error reporting.  All compute runs in
-// the HIP kernels of gdn_prefill.hip and gdn_decode.hip.
+// the HIP kernels of gdn_prefill.hip, gdn_prefill_pipe.hip and gdn_decode.hip.
 #include "gdn.h"
 #include "gdn_launch.h"
 
@@ -51,18 +51,27 @@ bool overlap(const Range &a, const Range &b) {
 constexpr int kD = 128;
 constexpr int kChunk = 64;
 
-// Value channels per workgroup.  A head's state is split into 128 / dvs independent
-// column slices; narrower slices give more workgroups for the same work at the cost
-// of recomputing the chunk's S-independent quantities in each slice.
-int choose_dvs(int32_t N, int32_t Hv, gdn_dtype dt) {
-    (void)N;
-    (void)Hv;
+// Kernel choice.  bf16 I/O runs the software-pipelined kernel (16 value channels per
+// workgroup); fp32 I/O runs the phase-by-phase kernel with fp32 MFMAs.  GDN_KERNEL=v1
+// selects the phase-by-phase kernel for bf16 too, and GDN_DVS=16|32 its slice width
+// (for comparisons and tuning).
+struct Plan {
+    bool pipe;
+    int dvs;
+    int lds;
+};
+
+Plan choose_plan(gdn_dtype dt) {
+    const char *kern = std::getenv("GDN_KERNEL");
+    const bool force_v1 = kern && std::strcmp(kern, "v1") == 0;
+    if (dt == GDN_BF16 && !force_v1) return Plan{true, 16, gdn::prefill_pipe_lds_bytes()};
+    int dvs = 16;
     const char *env = std::getenv("GDN_DVS");
     if (env) {
         const int d = std::atoi(env);
-        if (gdn::prefill_lds_bytes(dt == GDN_BF16, d) > 0) return d;
+        if (gdn::prefill_lds_bytes(dt == GDN_BF16, d) > 0) dvs = d;
     }
-    return 16;
+    return Plan{false, dvs, gdn::prefill_lds_bytes(dt == GDN_BF16, dvs)};
 }
 
 }  // namespace
@@ -87,12 +96,12 @@ gdn_status gdn_prefill_plan(int32_t N, int32_t Hv, int32_t Dv, gdn_dtype io_dtyp
         return fail(GDN_ERR_INVALID_ARGUMENT, "io_dtype %d is not GDN_F32 or GDN_BF16", (int)io_dtype);
     if (N < 1 || Hv < 1) return fail(GDN_ERR_INVALID_ARGUMENT, "N=%d and Hv=%d must be >= 1", N, Hv);
     if (Dv != kD) return fail(GDN_ERR_UNSUPPORTED, "Dv=%d (only 128 is implemented)", Dv);
-    const int dvs = choose_dvs(N, Hv, io_dtype);
-    const long long wg = (long long)N * Hv * (kD / dvs);
+    const Plan p = choose_plan(io_dtype);
+    const long long wg = (long long)N * Hv * (kD / p.dvs);
     if (wg > 0x7fffffffLL) return fail(GDN_ERR_UNSUPPORTED, "%lld workgroups exceed the grid limit", wg);
-    if (dv_per_workgroup) *dv_per_workgroup = dvs;
+    if (dv_per_workgroup) *dv_per_workgroup = p.dvs;
     if (workgroups) *workgroups = (int32_t)wg;
-    if (lds_bytes) *lds_bytes = gdn::prefill_lds_bytes(io_dtype == GDN_BF16, dvs);
+    if (lds_bytes) *lds_bytes = p.lds;
     return ok();
 }
 
@@ -150,9 +159,11 @@ gdn_status gdn_prefill(const void *q, const void *k, const void *v, const float 
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
     a.s0 = initial_state; a.cu = cu_seqlens; a.o = o; a.sN = final_state;
     a.N = N; a.T_tot = T_tot; a.Hk = Hk; a.Hv = Hv; a.nslices = kD / dvs;
+    const Plan p = choose_plan(io_dtype);
     (void)hipGetLastError();
-    const hipError_t e = gdn::launch_prefill(a, io_dtype == GDN_BF16, dvs, wg,
-                                             static_cast<hipStream_t>(stream));
+    const hipError_t e = p.pipe ? gdn::launch_prefill_pipe(a, wg, static_cast<hipStream_t>(stream))
+                                : gdn::launch_prefill(a, io_dtype == GDN_BF16, dvs, wg,
+                                                      static_cast<hipStream_t>(stream));
     if (e != hipSuccess)
         return fail(GDN_ERR_DEVICE, "prefill launch failed: %s", hipGetErrorString(e));
     return ok();

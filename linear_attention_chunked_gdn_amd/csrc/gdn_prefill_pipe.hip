@@ -1,0 +1,577 @@
+// Wave-specialised, software-pipelined chunked gated delta-rule prefill for gfx950,
+// bf16 I/O.
+//
+// Same arithmetic as gdn_prefill.hip (see there for the chunkwise formulas, the
+// column-wise split of the state and the bf16 precision scheme), scheduled so the
+// two halves of the Map-Reduce-Map pipeline ("Empowering Hybrid Attention Models
+// on NPUs", section 2.1, Figure 1(b)) run side by side:
+//
+//   * four "map" waves do the S-independent work of chunk c+1 -- the gate scan (#1),
+//     the K K^T and Q K^T grams (#2) and the (I + A)^-1 solve (#3);
+//   * four "chain" waves hold the fp32 state slice in registers and do the
+//     S-dependent work of chunk c -- R = beta V - beta gamma K S^T, v = T R
+//     (#4/#5-read), the output (#6) and the in-place update (#5-update).
+//
+// Waves i and i+4 share SIMD i, so each SIMD interleaves one map and one chain
+// wave and the latency of one hides behind the other.  A chunk costs three
+// workgroup barriers:
+//
+//   phase 1:  chain R(c), Q S^T(c)       | map: T(c) blocks below the diagonal
+//             all waves: stage chunk c+1 into LDS, fetch chunk c+2 into registers
+//   phase 2:  chain v(c) = T(c) R(c)     | map: gate(c+1), grams(c+1) -> A, P(c+1)
+//   phase 3:  chain O(c), S update       | map: diagonal blocks of T(c+1)
+//
+// LDS holds two buffers of the chunk tiles (K, Q, V, gates) and of P; T and A are
+// single-buffered because their lifetimes do not overlap across the phases.
+// One workgroup = 8 wave64s = one (sequence, value head, 16 value channels).
+#include "gdn_device.h"
+#include "gdn_launch.h"
+
+namespace gdn {
+namespace pipe {
+
+constexpr int CH = 64;        // chunk length
+constexpr int DK = 128;
+constexpr int DV = 128;
+constexpr int DVS = 16;       // value channels per workgroup
+constexpr int THREADS = 512;   // 4 map + 4 chain waves
+constexpr int KS = DK + 8;    // bf16 row stride of K, Q and the state copy
+constexpr int TS = CH + 8;    // bf16 row stride of T, P, R^T, v^T, (lambda v)^T
+constexpr int VS = DVS + 8;   // bf16 row stride of the value tile
+constexpr int AS = CH + 4;    // fp32 row stride of A
+constexpr float LOG2E = 1.4426950408889634f;
+
+typedef __bf16 bf;
+
+struct Gate {
+    float graw[CH];   // g of the chunk (0 past its end)
+    float beta[CH];   // beta (0 past the end)
+    float gam[CH];    // gamma_t = exp(Gamma_t)
+    float lam[CH];    // lambda_t = exp(Gamma_last - Gamma_t)
+};
+
+struct __align__(16) Smem {
+    bf K[2][CH * KS];
+    bf Q[2][CH * KS];
+    bf V[2][CH * VS];
+    Gate gate[2];
+    float A[CH * AS];              // A of the chunk being mapped, strictly lower
+    bf T[CH * TS];                 // T = (I + A)^-1
+    bf Ph[2][CH * TS], Pl[2][CH * TS];   // P split into bf16 hi + lo
+    bf S[DVS * KS];                // bf16 copy of the state slice [value ch][key ch]
+    bf Rh[DVS * TS], Rl[DVS * TS];  // R^T
+    bf Vh[DVS * TS], Vl[DVS * TS];  // v^T
+    bf Wh[DVS * TS], Wl[DVS * TS];  // (diag(lambda) v)^T
+    float G2[4][CH];               // per-wave copy of Gamma * log2(e) of the mapped chunk
+};
+
+struct Stage {
+    uint4 k[2], q[2], v;
+    float g, b;
+};
+
+__device__ __forceinline__ float to_f(bf x) { return bf16_to_f32(x); }
+
+// Four consecutive values as split bf16 pairs (hi, lo).
+__device__ __forceinline__ void store4_split(bf *hi, bf *lo, float a0, float a1, float a2, float a3) {
+    bf16x4 h, l;
+    h[0] = f32_to_bf16(a0); h[1] = f32_to_bf16(a1); h[2] = f32_to_bf16(a2); h[3] = f32_to_bf16(a3);
+    l[0] = f32_to_bf16(a0 - to_f(h[0])); l[1] = f32_to_bf16(a1 - to_f(h[1]));
+    l[2] = f32_to_bf16(a2 - to_f(h[2])); l[3] = f32_to_bf16(a3 - to_f(h[3]));
+    *reinterpret_cast<bf16x4 *>(hi) = h;
+    *reinterpret_cast<bf16x4 *>(lo) = l;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave: DPP shifts inside each row of 16
+// lanes, then the totals of the earlier rows are added.
+__device__ __forceinline__ float wave_inclusive_scan(float x, int lane) {
+    // row_shr:n (dpp_ctrl 0x110 + n); lanes with no source in their row read 0
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x111, 0xF, 0xF, true));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x112, 0xF, 0xF, true));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x114, 0xF, 0xF, true));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x118, 0xF, 0xF, true));
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 15));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 31));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 47));
+    const int row = lane >> 4;
+    x += (row >= 1 ? r0 : 0.f) + (row >= 2 ? r1 : 0.f) + (row >= 3 ? r2 : 0.f);
+    return x;
+}
+
+struct Work {
+    size_t kq_base;         // byte offset of this key head in q and k
+    size_t kq_row;          // bytes between tokens in q/k
+    size_t v_row;           // bytes between tokens in v
+    size_t v_off;           // byte offset of (head, slice) in v
+    int h, bos, eos;
+};
+
+__device__ __forceinline__ void stage_load(Stage &st, const PrefillArgs &a, const Work &wk, int tok0,
+                                           int nval, int tid) {
+    const char *kb = reinterpret_cast<const char *>(a.k) + wk.kq_base;
+    const char *qb = reinterpret_cast<const char *>(a.q) + wk.kq_base;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int f = tid + THREADS * i;
+        const int row = f >> 4, seg = f & 15;
+        uint4 zk = make_uint4(0, 0, 0, 0), zq = zk;
+        if (row < nval) {
+            const size_t off = (size_t)(tok0 + row) * wk.kq_row + (size_t)seg * 16;
+            zk = *reinterpret_cast<const uint4 *>(kb + off);
+            zq = *reinterpret_cast<const uint4 *>(qb + off);
+        }
+        st.k[i] = zk;
+        st.q[i] = zq;
+    }
+    {
+        const int row = tid >> 1, seg = tid & 1;   // 64 rows x 2 segments of 16 B
+        uint4 z = make_uint4(0, 0, 0, 0);
+        if (tid < 2 * CH && row < nval)
+            z = *reinterpret_cast<const uint4 *>(reinterpret_cast<const char *>(a.v) + wk.v_off +
+                                                 (size_t)(tok0 + row) * wk.v_row + (size_t)seg * 16);
+        st.v = z;
+    }
+    st.g = 0.f;
+    st.b = 0.f;
+    if (tid < CH && tid < nval) {
+        st.g = a.g[(size_t)(tok0 + tid) * a.Hv + wk.h];
+        st.b = a.beta[(size_t)(tok0 + tid) * a.Hv + wk.h];
+    }
+}
+
+__device__ __forceinline__ void stage_commit(const Stage &st, Smem &s, int buf, int tid) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int f = tid + THREADS * i;
+        const int row = f >> 4, seg = f & 15;
+        *reinterpret_cast<uint4 *>(&s.K[buf][row * KS + seg * 8]) = st.k[i];
+        *reinterpret_cast<uint4 *>(&s.Q[buf][row * KS + seg * 8]) = st.q[i];
+    }
+    if (tid < 2 * CH) {
+        const int row = tid >> 1, seg = tid & 1;
+        *reinterpret_cast<uint4 *>(&s.V[buf][row * VS + seg * 8]) = st.v;
+    }
+    if (tid < CH) {
+        s.gate[buf].graw[tid] = st.g;
+        s.gate[buf].beta[tid] = st.b;
+    }
+}
+
+// ---------------------------------------------------------------------------------
+// Map: gate scan and grams of the chunk in buffer nb.  Map wave m computes, for one
+// gram (K K^T for m even, Q K^T for m odd), the lower tiles of the row-block pair
+// {0, 3} (m < 2) or {1, 2} (m >= 2): five 16x16 tiles per wave.  The wave keeps the
+// A fragments of its two row blocks in registers and loads each K column block once
+// for all tiles that use it.  A goes to s.A (fp32), P to s.Ph/Pl[nb].
+// ---------------------------------------------------------------------------------
+template <bool ISQ>
+__device__ __forceinline__ void gram_epilogue(Smem &s, int nb, int m, int bi, int bj, const f32x4 &acc,
+                                              int l16, int g4) {
+    const int sc = 16 * bj + l16;
+    const int r0 = 16 * bi + 4 * g4;
+    const f32x4 gr = *reinterpret_cast<const f32x4 *>(&s.G2[m][r0]);
+    const float gc = s.G2[m][sc];
+    if constexpr (!ISQ) {
+        const f32x4 br = *reinterpret_cast<const f32x4 *>(&s.gate[nb].beta[r0]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int rr = r0 + r;
+            float val = br[r] * acc[r] * __builtin_amdgcn_exp2f(gr[r] - gc);
+            if (bi == bj) val = (sc < rr) ? val : 0.f;
+            s.A[rr * AS + sc] = val;
+        }
+    } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int rr = r0 + r;
+            float p = acc[r] * __builtin_amdgcn_exp2f(gr[r] - gc);
+            if (bi == bj) p = (sc <= rr) ? p : 0.f;
+            const bf ph = f32_to_bf16(p);
+            s.Ph[nb][rr * TS + sc] = ph;
+            s.Pl[nb][rr * TS + sc] = f32_to_bf16(p - to_f(ph));
+        }
+    }
+}
+
+template <bool ISQ, int RB0, int RB1>
+__device__ __forceinline__ void gram_rows(Smem &s, int nb, int m, int l16, int g4) {
+    static_assert(RB0 < RB1 && RB0 + RB1 == 3, "row-block pairs are {0,3} and {1,2}");
+    const bf *src = ISQ ? s.Q[nb] : s.K[nb];
+    f32x4 c0[RB0 + 1], c1[RB1 + 1];
+#pragma unroll
+    for (int j = 0; j <= RB0; ++j) c0[j] = zero4();
+#pragma unroll
+    for (int j = 0; j <= RB1; ++j) c1[j] = zero4();
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+        Frag<bf> a0, a1, b[RB1 + 1];
+        a0.load8(src + (16 * RB0 + l16) * KS + 32 * kb + 8 * g4);
+        a1.load8(src + (16 * RB1 + l16) * KS + 32 * kb + 8 * g4);
+#pragma unroll
+        for (int j = 0; j <= RB1; ++j) b[j].load8(s.K[nb] + (16 * j + l16) * KS + 32 * kb + 8 * g4);
+#pragma unroll
+        for (int j = 0; j <= RB1; ++j) {
+            mma(c1[j], a1, b[j]);
+            if (j <= RB0) mma(c0[j], a0, b[j]);
+        }
+    }
+#pragma unroll
+    for (int j = 0; j <= RB0; ++j) gram_epilogue<ISQ>(s, nb, m, RB0, j, c0[j], l16, g4);
+#pragma unroll
+    for (int j = 0; j <= RB1; ++j) gram_epilogue<ISQ>(s, nb, m, RB1, j, c1[j], l16, g4);
+}
+
+// Exponent differences are only ever formed for r >= s (g <= 0 keeps them <= 0 and
+// the masked-out upper entries are discarded); every map wave runs the scan itself
+// and keeps Gamma*log2(e) in its own LDS row, so the grams need no extra barrier.
+__device__ __forceinline__ void map_gate_grams(Smem &s, int nb, int m, int lane, int l16, int g4) {
+    const float x = wave_inclusive_scan(s.gate[nb].graw[lane], lane);
+    const float x2 = x * LOG2E;
+    const float last2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x2), 63));
+    s.G2[m][lane] = x2;
+    if (m == 0) {
+        s.gate[nb].gam[lane] = __builtin_amdgcn_exp2f(x2);
+        s.gate[nb].lam[lane] = __builtin_amdgcn_exp2f(last2 - x2);
+    }
+    switch (m) {
+        case 0: gram_rows<false, 0, 3>(s, nb, m, l16, g4); break;
+        case 1: gram_rows<true, 0, 3>(s, nb, m, l16, g4); break;
+        case 2: gram_rows<false, 1, 2>(s, nb, m, l16, g4); break;
+        default: gram_rows<true, 1, 2>(s, nb, m, l16, g4); break;
+    }
+}
+
+// ---------------------------------------------------------------------------------
+// Map: diagonal block B of T = (I + A)^-1 by substitution, lane l16 computing column
+// l16 (the four lane groups compute the same column; each then writes 4 rows).  The
+// block is solved as two 8-row halves (rows 0-7, then rows 8-15 after the lower-left
+// 8x8 block's independent update), each read into registers first and solved
+// right-looking, so the updates of one step are independent of each other.
+// ---------------------------------------------------------------------------------
+__device__ __forceinline__ void map_diag_solve(Smem &s, int B, int l16, int g4) {
+    const float *ablk = &s.A[(16 * B) * AS + 16 * B];
+    float x[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) x[i] = (i == l16) ? 1.f : 0.f;
+    // rows 0..7, then rows 8..15 after subtracting the lower-left 8x8 block's share
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+        const int r0 = 8 * half;
+        if (half == 1) {
+            float b[8][8];
+#pragma unroll
+            for (int r = 0; r < 8; ++r)
+#pragma unroll
+                for (int q = 0; q < 8; q += 4) {
+                    const f32x4 t = *reinterpret_cast<const f32x4 *>(ablk + (8 + r) * AS + q);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) b[r][q + e] = t[e];
+                }
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+#pragma unroll
+                for (int r = 0; r < 8; ++r) x[8 + r] -= b[r][j] * x[j];
+        }
+        float a[8][8];
+#pragma unroll
+        for (int r = 1; r < 8; ++r)
+#pragma unroll
+            for (int q = 0; q < r; q += 4) {
+                const f32x4 t = *reinterpret_cast<const f32x4 *>(ablk + (r0 + r) * AS + r0 + q);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) a[r][q + e] = t[e];
+            }
+#pragma unroll
+        for (int j = 0; j < 7; ++j)
+#pragma unroll
+            for (int r = j + 1; r < 8; ++r) x[r0 + r] -= a[r][j] * x[r0 + j];
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const float v = g4 == 0 ? x[r] : g4 == 1 ? x[4 + r] : g4 == 2 ? x[8 + r] : x[12 + r];
+        s.T[(16 * B + 4 * g4 + r) * TS + 16 * B + l16] = f32_to_bf16(v);
+    }
+}
+
+// ---------------------------------------------------------------------------------
+// Map: blocks of column block CB below the diagonal, T_i,CB = -T_ii sum_j A_ij T_j,CB.
+// Results stay in registers (accumulator layout == B-operand layout) between steps.
+// ---------------------------------------------------------------------------------
+template <int CB>
+__device__ __forceinline__ void map_merges(Smem &s, int l16, int g4) {
+    f32x4 tcol[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) tcol[CB][r] = to_f(s.T[(16 * CB + 4 * g4 + r) * TS + 16 * CB + l16]);
+#pragma unroll
+    for (int i = CB + 1; i < 4; ++i) {
+        f32x4 X = zero4();
+#pragma unroll
+        for (int j = CB; j < i; j += 2) {
+            Frag<bf> fa, fb;
+            const float *ar = &s.A[(16 * i + l16) * AS + 16 * j + 4 * g4];
+            const f32x4 a0 = *reinterpret_cast<const f32x4 *>(ar);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                fa.set(e, a0[e]);
+                fb.set(e, tcol[j][e]);
+            }
+            if (j + 1 < i) {
+                const f32x4 a1 = *reinterpret_cast<const f32x4 *>(ar + 16);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    fa.set(4 + e, a1[e]);
+                    fb.set(4 + e, tcol[j + 1][e]);
+                }
+            } else {
+#pragma unroll
+                for (int e = 4; e < 8; ++e) {
+                    fa.set(e, 0.f);
+                    fb.set(e, 0.f);
+                }
+            }
+            mma(X, fa, fb);
+        }
+        Frag<bf> fa, fb;
+        fa.zero();
+        fb.zero();
+        fa.load4(0, &s.T[(16 * i + l16) * TS + 16 * i + 4 * g4]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) fb.set(e, -X[e]);
+        f32x4 Y = zero4();
+        mma(Y, fa, fb);
+        tcol[i] = Y;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s.T[(16 * i + 4 * g4 + r) * TS + 16 * CB + l16] = f32_to_bf16(Y[r]);
+    }
+}
+
+// ---------------------------------------------------------------------------------
+// Chain, phase 1: R = beta V - beta gamma (K S^T) and Q S^T for tokens [16W, 16W+16).
+// ---------------------------------------------------------------------------------
+__device__ __forceinline__ void chain_R(Smem &s, int buf, int W, int l16, int g4, f32x4 &qs) {
+    const bf *krow = s.K[buf] + (16 * W + l16) * KS + 8 * g4;
+    const bf *qrow = s.Q[buf] + (16 * W + l16) * KS + 8 * g4;
+    const bf *srow = s.S + l16 * KS + 8 * g4;
+    f32x4 ks = zero4();
+    qs = zero4();
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+        Frag<bf> fk, fq, fs;
+        fs.load8(srow + 32 * kb);
+        fk.load8(krow + 32 * kb);
+        fq.load8(qrow + 32 * kb);
+        mma(ks, fk, fs);
+        mma(qs, fq, fs);
+    }
+    const int t0 = 16 * W + 4 * g4;
+    const f32x4 b = *reinterpret_cast<const f32x4 *>(&s.gate[buf].beta[t0]);
+    const f32x4 gm = *reinterpret_cast<const f32x4 *>(&s.gate[buf].gam[t0]);
+    float r[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = b[i] * (to_f(s.V[buf][(t0 + i) * VS + l16]) - gm[i] * ks[i]);
+    store4_split(&s.Rh[l16 * TS + t0], &s.Rl[l16 * TS + t0], r[0], r[1], r[2], r[3]);
+}
+
+// Chain, phase 2: v = T R for tokens [16W, 16W+16); T is lower triangular, so only
+// the first W/2 + 1 blocks of 32 columns contribute.
+__device__ __forceinline__ void chain_v(Smem &s, int buf, int W, int l16, int g4) {
+    f32x4 acc = zero4();
+    const bf *trow = s.T + (16 * W + l16) * TS + 8 * g4;
+    for (int kb = 0; kb <= (W >> 1); ++kb) {
+        Frag<bf> fa, fh, fl;
+        fa.load8(trow + 32 * kb);
+        fh.load8(s.Rh + l16 * TS + 32 * kb + 8 * g4);
+        fl.load8(s.Rl + l16 * TS + 32 * kb + 8 * g4);
+        mma(acc, fa, fh);
+        mma(acc, fa, fl);
+    }
+    const int t0 = 16 * W + 4 * g4;
+    const f32x4 lm = *reinterpret_cast<const f32x4 *>(&s.gate[buf].lam[t0]);
+    store4_split(&s.Vh[l16 * TS + t0], &s.Vl[l16 * TS + t0], acc[0], acc[1], acc[2], acc[3]);
+    store4_split(&s.Wh[l16 * TS + t0], &s.Wl[l16 * TS + t0], lm[0] * acc[0], lm[1] * acc[1],
+                 lm[2] * acc[2], lm[3] * acc[3]);
+}
+
+// Chain, phase 3: output rows of wave W, then the update of key channels
+// [32W, 32W+32) of the state slice.
+__device__ __forceinline__ void chain_out_update(Smem &s, const PrefillArgs &a, int buf, int W, int l16,
+                                                 int g4, const f32x4 &qs, f32x4 (&st)[2], int h,
+                                                 int dv0, int tok0, int nval) {
+    {
+        f32x4 acc = zero4();
+        const bf *ph = s.Ph[buf] + (16 * W + l16) * TS + 8 * g4;
+        const bf *pl = s.Pl[buf] + (16 * W + l16) * TS + 8 * g4;
+        for (int kb = 0; kb <= (W >> 1); ++kb) {
+            Frag<bf> fph, fpl, fvh, fvl;
+            fph.load8(ph + 32 * kb);
+            fpl.load8(pl + 32 * kb);
+            fvh.load8(s.Vh + l16 * TS + 32 * kb + 8 * g4);
+            fvl.load8(s.Vl + l16 * TS + 32 * kb + 8 * g4);
+            mma(acc, fph, fvh);
+            mma(acc, fph, fvl);
+            mma(acc, fpl, fvh);
+        }
+        const int t0 = 16 * W + 4 * g4;
+        const f32x4 gm = *reinterpret_cast<const f32x4 *>(&s.gate[buf].gam[t0]);
+        uint16_t *ob = reinterpret_cast<uint16_t *>(a.o) + (size_t)h * DV + dv0 + l16;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = t0 + r;
+            if (t < nval) {
+                const float y = gm[r] * qs[r] + acc[r];
+                ob[(size_t)(tok0 + t) * a.Hv * DV] = __builtin_bit_cast(uint16_t, f32_to_bf16(y));
+            }
+        }
+    }
+    {
+        const float glast = s.gate[buf].gam[CH - 1];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+            Frag<bf> ka[2];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    ka[kb].set_raw(e, s.K[buf][(32 * kb + 8 * g4 + e) * KS + 32 * W + 16 * mt + l16]);
+            f32x4 acc = st[mt] * glast;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                Frag<bf> fh, fl;
+                fh.load8(s.Wh + l16 * TS + 32 * kb + 8 * g4);
+                fl.load8(s.Wl + l16 * TS + 32 * kb + 8 * g4);
+                mma(acc, ka[kb], fh);
+                mma(acc, ka[kb], fl);
+            }
+            st[mt] = acc;
+            bf16x4 t;
+            t[0] = f32_to_bf16(acc[0]); t[1] = f32_to_bf16(acc[1]);
+            t[2] = f32_to_bf16(acc[2]); t[3] = f32_to_bf16(acc[3]);
+            *reinterpret_cast<bf16x4 *>(&s.S[l16 * KS + 32 * W + 16 * mt + 4 * g4]) = t;
+        }
+    }
+}
+
+__global__ __launch_bounds__(THREADS) void gdn_prefill_pipe_kernel(const PrefillArgs a) {
+    __shared__ Smem s;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, l16 = lane & 15, g4 = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool is_map = wave < 4;
+    const int W = wave & 3;   // map: block / gram job index; chain: token tile and key block
+
+    const int G = gridDim.x;
+    int item = blockIdx.x;
+    if ((G & 7) == 0) item = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
+    const int slice = item % a.nslices;
+    const int h = (item / a.nslices) % a.Hv;
+    const int n = item / (a.nslices * a.Hv);
+    const int hk = h % a.Hk;
+    const int dv0 = slice * DVS;
+    Work wk;
+    wk.kq_base = (size_t)hk * DK * 2;
+    wk.kq_row = (size_t)a.Hk * DK * 2;
+    wk.v_row = (size_t)a.Hv * DV * 2;
+    wk.v_off = ((size_t)h * DV + dv0) * 2;
+    wk.h = h;
+    wk.bos = 0;
+    wk.eos = a.T_tot;
+    if (a.cu) {
+        wk.bos = a.cu[n];
+        wk.eos = a.cu[n + 1];
+    }
+    const int len = wk.eos > wk.bos ? wk.eos - wk.bos : 0;
+    const int nchunks = (len + CH - 1) / CH;
+
+    // State slice, held by the chain waves: S^T rows (key channels) 32W + 16mt + 4G + r,
+    // column (value channel) dv0 + l16.
+    f32x4 st[2];
+    const size_t sbase = ((size_t)n * a.Hv + h) * (size_t)DV * DK;
+    if (!is_map) {
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+            const int dk = 32 * W + 16 * mt + 4 * g4;
+            f32x4 x = zero4();
+            if (a.s0) x = *reinterpret_cast<const f32x4 *>(a.s0 + sbase + (size_t)(dv0 + l16) * DK + dk);
+            st[mt] = x;
+            bf16x4 t;
+            t[0] = f32_to_bf16(x[0]); t[1] = f32_to_bf16(x[1]); t[2] = f32_to_bf16(x[2]); t[3] = f32_to_bf16(x[3]);
+            *reinterpret_cast<bf16x4 *>(&s.S[l16 * KS + dk]) = t;
+        }
+    }
+
+    if (nchunks > 0) {
+        for (int i = tid; i < CH * TS; i += THREADS) {
+            s.T[i] = f32_to_bf16(0.f);
+            s.Ph[0][i] = s.Ph[1][i] = s.Pl[0][i] = s.Pl[1][i] = f32_to_bf16(0.f);
+        }
+        Stage stg;
+        stage_load(stg, a, wk, wk.bos, min(CH, len), tid);
+        stage_commit(stg, s, 0, tid);
+        if (nchunks > 1) stage_load(stg, a, wk, wk.bos + CH, min(CH, len - CH), tid);
+        __syncthreads();
+        if (is_map) map_gate_grams(s, 0, W, lane, l16, g4);
+        __syncthreads();
+        if (is_map) map_diag_solve(s, W, l16, g4);
+        __syncthreads();
+
+        for (int c = 0; c < nchunks; ++c) {
+            const int buf = c & 1, nb = buf ^ 1;
+            const int tok0 = wk.bos + c * CH;
+            const int nval = min(CH, wk.eos - tok0);
+            const bool has_next = c + 1 < nchunks;
+
+            // phase 1
+            f32x4 qs;
+            if (is_map) {
+                switch (W) {
+                    case 0: map_merges<0>(s, l16, g4); break;
+                    case 1: map_merges<1>(s, l16, g4); break;
+                    case 2: map_merges<2>(s, l16, g4); break;
+                    default: break;
+                }
+            } else {
+                chain_R(s, buf, W, l16, g4, qs);
+            }
+            if (has_next) {
+                stage_commit(stg, s, nb, tid);
+                if (c + 2 < nchunks) stage_load(stg, a, wk, tok0 + 2 * CH, min(CH, wk.eos - tok0 - 2 * CH), tid);
+            }
+            __syncthreads();
+
+            // phase 2
+            if (is_map) {
+                if (has_next) map_gate_grams(s, nb, W, lane, l16, g4);
+            } else {
+                chain_v(s, buf, W, l16, g4);
+            }
+            __syncthreads();
+
+            // phase 3
+            if (is_map) {
+                if (has_next) map_diag_solve(s, W, l16, g4);
+            } else {
+                chain_out_update(s, a, buf, W, l16, g4, qs, st, h, dv0, tok0, nval);
+            }
+            __syncthreads();
+        }
+    }
+
+    if (a.sN && !is_map) {
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+            const int dk = 32 * W + 16 * mt + 4 * g4;
+            *reinterpret_cast<f32x4 *>(a.sN + sbase + (size_t)(dv0 + l16) * DK + dk) = st[mt];
+        }
+    }
+}
+
+}  // namespace pipe
+
+hipError_t launch_prefill_pipe(const PrefillArgs &a, int grid, hipStream_t stream) {
+    hipLaunchKernelGGL(pipe::gdn_prefill_pipe_kernel, dim3(grid), dim3(pipe::THREADS), 0, stream, a);
+    return hipGetLastError();
+}
+
+int prefill_pipe_lds_bytes() { return (int)sizeof(pipe::Smem); }
+
+}  // namespace gdn

@@ -179,3 +179,17 @@ def test_errors_raise():
     d = to_device(x, DEV)
     with pytest.raises(gdn.GDNError):
         gdn.prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], chunk_size=32)
+
+
+@pytest.mark.parametrize("dvs", ["16", "32"])
+def test_phase_by_phase_kernel_bf16(monkeypatch, dvs):
+    # the bf16 path of the phase-by-phase kernel (the fp32 kernel's schedule), kept as a
+    # cross-check of the pipelined kernel
+    monkeypatch.setenv("GDN_KERNEL", "v1")
+    monkeypatch.setenv("GDN_DVS", dvs)
+    for x in (inputs.make_custom(40, [300, 0, 77], 2, 4, io="bf16", init_std=0.1),
+              inputs.make_workload(1)):
+        o, fs = _run(x)
+        ro, rf = _oracle(x)
+        check("o", to_f64(o), ro, x.io)
+        check("final_state", to_f64(fs), rf, x.io)
