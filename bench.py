@@ -77,6 +77,20 @@ def cpu_baseline(x, repeats: int = 3) -> dict:
                       f"{dt:.3f} s each"}
 
 
+def calibrate_copy(mib: int, steps: int) -> int:
+    """Copies of a known number of bytes, for scaling FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    n = mib << 20
+    a = torch.empty(n, dtype=torch.uint8, device="cuda:0").random_(0, 255)
+    bufs = [torch.empty(n, dtype=torch.uint8, device="cuda:0") for _ in range(2)]
+    for i in range(steps):
+        bufs[i % 2].copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes_read": n, "calibrate_copy_bytes_written": n,
+                      "copies": steps}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -86,10 +100,15 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rotate-bytes", type=int, default=2 * MALL_BYTES,
                     help="input copies are rotated until they span at least this many bytes")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="instead of the benchmark, run device-to-device copies of MIB MiB "
+                         "(the known-size reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this build runs on one GPU only; --gpus must be 1", file=sys.stderr)
         return 2
+    if args.calibrate_copy:
+        return calibrate_copy(args.calibrate_copy, args.steps)
 
     import torch
     from linear_attention_chunked_gdn_amd import gdn, inputs
