@@ -16,10 +16,12 @@
 // wave and the latency of one hides behind the other.  A chunk costs three
 // workgroup barriers:
 //
-//   phase 1:  chain R(c), Q S^T(c)       | map: T(c) blocks below the diagonal
+//   phase 1:  chain R(c)                 | map: T(c) blocks below the diagonal,
+//                                        |      gate scan of chunk c+1 (one wave)
 //             all waves: stage chunk c+1 into LDS, fetch chunk c+2 into registers
-//   phase 2:  chain v(c) = T(c) R(c)     | map: gate(c+1), grams(c+1) -> A, P(c+1)
-//   phase 3:  chain O(c), S update       | map: diagonal blocks of T(c+1)
+//   phase 2:  chain v(c) = T(c) R(c),    | map: grams(c+1) -> A, P(c+1)
+//             Q S^T(c)                   |
+//   phase 3:  chain O(c), S update       | map: diagonal blocks of T(c+1) (one wave)
 //
 // LDS holds two buffers of the chunk tiles (K, Q, V, gates) and of P; T and A are
 // single-buffered because their lifetimes do not overlap across the phases.
@@ -43,11 +45,18 @@ constexpr float LOG2E = 1.4426950408889634f;
 
 typedef __bf16 bf;
 
+// Per-chunk gate quantities, computed once by one map wave from the staged g.
+// Decays inside a chunk are exp(Gamma_r - Gamma_s), r >= s.  For r and s in different
+// 16-token blocks (r in block i > block of s) they are formed as u_r * w[i-1]_s with
+// u_r = exp(Gamma_r - Gamma_16i') (i' the block of r) and w[i-1]_s = exp(Gamma_16i -
+// Gamma_s): both exponents are <= 0 when g <= 0, so neither factor can overflow.
 struct Gate {
-    float graw[CH];   // g of the chunk (0 past its end)
-    float beta[CH];   // beta (0 past the end)
+    float beta[CH];   // beta (0 past the chunk's end)
     float gam[CH];    // gamma_t = exp(Gamma_t)
     float lam[CH];    // lambda_t = exp(Gamma_last - Gamma_t)
+    float g2[CH];     // Gamma_t * log2(e)
+    float u[CH];      // exp(Gamma_t - Gamma at the first token of t's 16-token block)
+    float w[3][CH];   // w[i-1][s] = exp(Gamma_16i - Gamma_s) for s < 16i, else 0
 };
 
 struct __align__(16) Smem {
@@ -62,7 +71,6 @@ struct __align__(16) Smem {
     bf Rh[DVS * TS], Rl[DVS * TS];  // R^T
     bf Vh[DVS * TS], Vl[DVS * TS];  // v^T
     bf Wh[DVS * TS], Wl[DVS * TS];  // (diag(lambda) v)^T
-    float G2[4][CH];               // per-wave copy of Gamma * log2(e) of the mapped chunk
 };
 
 struct Stage {
@@ -131,11 +139,13 @@ __device__ __forceinline__ void stage_load(Stage &st, const PrefillArgs &a, cons
                                                  (size_t)(tok0 + row) * wk.v_row + (size_t)seg * 16);
         st.v = z;
     }
+    // g and beta go to map wave 3 (threads 192..255), which scans them itself
     st.g = 0.f;
     st.b = 0.f;
-    if (tid < CH && tid < nval) {
-        st.g = a.g[(size_t)(tok0 + tid) * a.Hv + wk.h];
-        st.b = a.beta[(size_t)(tok0 + tid) * a.Hv + wk.h];
+    const int gt = tid - 3 * 64;
+    if (gt >= 0 && gt < CH && gt < nval) {
+        st.g = a.g[(size_t)(tok0 + gt) * a.Hv + wk.h];
+        st.b = a.beta[(size_t)(tok0 + gt) * a.Hv + wk.h];
     }
 }
 
@@ -151,50 +161,74 @@ __device__ __forceinline__ void stage_commit(const Stage &st, Smem &s, int buf, 
         const int row = tid >> 1, seg = tid & 1;
         *reinterpret_cast<uint4 *>(&s.V[buf][row * VS + seg * 8]) = st.v;
     }
-    if (tid < CH) {
-        s.gate[buf].graw[tid] = st.g;
-        s.gate[buf].beta[tid] = st.b;
-    }
+}
+
+// #1 Gate for the chunk staged in buffer buf, by map wave 3 (lane = token): the
+// inclusive scan of g and every decay factor the grams and the chain need.
+__device__ __forceinline__ void gate_scan(const Stage &st, Smem &s, int buf, int lane) {
+    const float x2 = wave_inclusive_scan(st.g, lane) * LOG2E;
+    const float last2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x2), 63));
+    const float b16 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x2), 16));
+    const float b32 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x2), 32));
+    const float b48 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x2), 48));
+    const float b0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x2), 0));
+    const int blk = lane >> 4;
+    const float start = blk == 0 ? b0 : blk == 1 ? b16 : blk == 2 ? b32 : b48;
+    Gate &gt = s.gate[buf];
+    gt.beta[lane] = st.b;
+    gt.g2[lane] = x2;
+    gt.gam[lane] = __builtin_amdgcn_exp2f(x2);
+    gt.lam[lane] = __builtin_amdgcn_exp2f(last2 - x2);
+    // u and w share one reference per 16-token block, the inclusive Gamma at the
+    // block's first token, so u_r * w_s = exp(Gamma_r - Gamma_s) exactly.
+    gt.u[lane] = __builtin_amdgcn_exp2f(x2 - start);
+    gt.w[0][lane] = lane < 16 ? __builtin_amdgcn_exp2f(b16 - x2) : 0.f;
+    gt.w[1][lane] = lane < 32 ? __builtin_amdgcn_exp2f(b32 - x2) : 0.f;
+    gt.w[2][lane] = lane < 48 ? __builtin_amdgcn_exp2f(b48 - x2) : 0.f;
 }
 
 // ---------------------------------------------------------------------------------
-// Map: gate scan and grams of the chunk in buffer nb.  Map wave m computes, for one
-// gram (K K^T for m even, Q K^T for m odd), the lower tiles of the row-block pair
-// {0, 3} (m < 2) or {1, 2} (m >= 2): five 16x16 tiles per wave.  The wave keeps the
-// A fragments of its two row blocks in registers and loads each K column block once
-// for all tiles that use it.  A goes to s.A (fp32), P to s.Ph/Pl[nb].
+// Map: grams of the chunk in buffer nb.  Map wave m computes, for one gram (K K^T for
+// m even, Q K^T for m odd), the lower tiles of the row-block pair {0, 3} (m < 2) or
+// {1, 2} (m >= 2): five 16x16 tiles per wave.  Tiles are computed transposed
+// (K_j X_i^T with X = K or Q), so each lane ends with one row and four consecutive
+// columns and writes them with one vector store.  A goes to s.A (fp32), P to
+// s.Ph/Pl[nb] (split bf16).
 // ---------------------------------------------------------------------------------
 template <bool ISQ>
-__device__ __forceinline__ void gram_epilogue(Smem &s, int nb, int m, int bi, int bj, const f32x4 &acc,
+__device__ __forceinline__ void gram_epilogue(Smem &s, int nb, int bi, int bj, const f32x4 &acc,
                                               int l16, int g4) {
-    const int sc = 16 * bj + l16;
-    const int r0 = 16 * bi + 4 * g4;
-    const f32x4 gr = *reinterpret_cast<const f32x4 *>(&s.G2[m][r0]);
-    const float gc = s.G2[m][sc];
-    if constexpr (!ISQ) {
-        const f32x4 br = *reinterpret_cast<const f32x4 *>(&s.gate[nb].beta[r0]);
+    const Gate &gt = s.gate[nb];
+    const int rr = 16 * bi + l16;          // row of this lane
+    const int c0 = 16 * bj + 4 * g4;       // first of its four columns
+    float d[4];
+    if (bi == bj) {
+        // same 16-token block: direct exponent differences, masked before use
+        const float gr = gt.g2[rr];
+        const f32x4 gc = *reinterpret_cast<const f32x4 *>(&gt.g2[c0]);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int rr = r0 + r;
-            float val = br[r] * acc[r] * __builtin_amdgcn_exp2f(gr[r] - gc);
-            if (bi == bj) val = (sc < rr) ? val : 0.f;
-            s.A[rr * AS + sc] = val;
+            const bool keep = ISQ ? (c0 + r <= rr) : (c0 + r < rr);
+            d[r] = keep ? __builtin_amdgcn_exp2f(gr - gc[r]) : 0.f;
         }
     } else {
+        const float ur = gt.u[rr];
+        const f32x4 wc = *reinterpret_cast<const f32x4 *>(&gt.w[bi - 1][c0]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int rr = r0 + r;
-            float p = acc[r] * __builtin_amdgcn_exp2f(gr[r] - gc);
-            if (bi == bj) p = (sc <= rr) ? p : 0.f;
-            const bf ph = f32_to_bf16(p);
-            s.Ph[nb][rr * TS + sc] = ph;
-            s.Pl[nb][rr * TS + sc] = f32_to_bf16(p - to_f(ph));
-        }
+        for (int r = 0; r < 4; ++r) d[r] = ur * wc[r];
+    }
+    if constexpr (!ISQ) {
+        const float br = gt.beta[rr];
+        *reinterpret_cast<f32x4 *>(&s.A[rr * AS + c0]) =
+            f32x4{br * acc[0] * d[0], br * acc[1] * d[1], br * acc[2] * d[2], br * acc[3] * d[3]};
+    } else {
+        store4_split(&s.Ph[nb][rr * TS + c0], &s.Pl[nb][rr * TS + c0], acc[0] * d[0], acc[1] * d[1],
+                     acc[2] * d[2], acc[3] * d[3]);
     }
 }
 
 template <bool ISQ, int RB0, int RB1>
-__device__ __forceinline__ void gram_rows(Smem &s, int nb, int m, int l16, int g4) {
+__device__ __forceinline__ void gram_rows(Smem &s, int nb, int l16, int g4) {
     static_assert(RB0 < RB1 && RB0 + RB1 == 3, "row-block pairs are {0,3} and {1,2}");
     const bf *src = ISQ ? s.Q[nb] : s.K[nb];
     f32x4 c0[RB0 + 1], c1[RB1 + 1];
@@ -204,56 +238,45 @@ __device__ __forceinline__ void gram_rows(Smem &s, int nb, int m, int l16, int g
     for (int j = 0; j <= RB1; ++j) c1[j] = zero4();
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-        Frag<bf> a0, a1, b[RB1 + 1];
-        a0.load8(src + (16 * RB0 + l16) * KS + 32 * kb + 8 * g4);
-        a1.load8(src + (16 * RB1 + l16) * KS + 32 * kb + 8 * g4);
+        Frag<bf> x0, x1, kj[RB1 + 1];
+        x0.load8(src + (16 * RB0 + l16) * KS + 32 * kb + 8 * g4);
+        x1.load8(src + (16 * RB1 + l16) * KS + 32 * kb + 8 * g4);
 #pragma unroll
-        for (int j = 0; j <= RB1; ++j) b[j].load8(s.K[nb] + (16 * j + l16) * KS + 32 * kb + 8 * g4);
+        for (int j = 0; j <= RB1; ++j) kj[j].load8(s.K[nb] + (16 * j + l16) * KS + 32 * kb + 8 * g4);
 #pragma unroll
         for (int j = 0; j <= RB1; ++j) {
-            mma(c1[j], a1, b[j]);
-            if (j <= RB0) mma(c0[j], a0, b[j]);
+            mma(c1[j], kj[j], x1);
+            if (j <= RB0) mma(c0[j], kj[j], x0);
         }
     }
 #pragma unroll
-    for (int j = 0; j <= RB0; ++j) gram_epilogue<ISQ>(s, nb, m, RB0, j, c0[j], l16, g4);
+    for (int j = 0; j <= RB0; ++j) gram_epilogue<ISQ>(s, nb, RB0, j, c0[j], l16, g4);
 #pragma unroll
-    for (int j = 0; j <= RB1; ++j) gram_epilogue<ISQ>(s, nb, m, RB1, j, c1[j], l16, g4);
+    for (int j = 0; j <= RB1; ++j) gram_epilogue<ISQ>(s, nb, RB1, j, c1[j], l16, g4);
 }
 
-// Exponent differences are only ever formed for r >= s (g <= 0 keeps them <= 0 and
-// the masked-out upper entries are discarded); every map wave runs the scan itself
-// and keeps Gamma*log2(e) in its own LDS row, so the grams need no extra barrier.
-__device__ __forceinline__ void map_gate_grams(Smem &s, int nb, int m, int lane, int l16, int g4) {
-    const float x = wave_inclusive_scan(s.gate[nb].graw[lane], lane);
-    const float x2 = x * LOG2E;
-    const float last2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x2), 63));
-    s.G2[m][lane] = x2;
-    if (m == 0) {
-        s.gate[nb].gam[lane] = __builtin_amdgcn_exp2f(x2);
-        s.gate[nb].lam[lane] = __builtin_amdgcn_exp2f(last2 - x2);
-    }
+__device__ __forceinline__ void map_grams(Smem &s, int nb, int m, int l16, int g4) {
     switch (m) {
-        case 0: gram_rows<false, 0, 3>(s, nb, m, l16, g4); break;
-        case 1: gram_rows<true, 0, 3>(s, nb, m, l16, g4); break;
-        case 2: gram_rows<false, 1, 2>(s, nb, m, l16, g4); break;
-        default: gram_rows<true, 1, 2>(s, nb, m, l16, g4); break;
+        case 0: gram_rows<false, 0, 3>(s, nb, l16, g4); break;
+        case 1: gram_rows<true, 0, 3>(s, nb, l16, g4); break;
+        case 2: gram_rows<false, 1, 2>(s, nb, l16, g4); break;
+        default: gram_rows<true, 1, 2>(s, nb, l16, g4); break;
     }
 }
 
 // ---------------------------------------------------------------------------------
-// Map: diagonal block B of T = (I + A)^-1 by substitution, lane l16 computing column
-// l16 (the four lane groups compute the same column; each then writes 4 rows).  The
-// block is solved as two 8-row halves (rows 0-7, then rows 8-15 after the lower-left
-// 8x8 block's independent update), each read into registers first and solved
-// right-looking, so the updates of one step are independent of each other.
+// Map: the four diagonal 16x16 blocks of T = (I + A)^-1 by substitution, all in one
+// wave: lane group G solves block G, lane l16 computing column l16 of its inverse.
+// Each block is solved as two 8-row halves (rows 0-7, then rows 8-15 after the
+// independent update by the lower-left 8x8 block), each half read into registers
+// first and solved right-looking, so the updates of one step are independent.
 // ---------------------------------------------------------------------------------
-__device__ __forceinline__ void map_diag_solve(Smem &s, int B, int l16, int g4) {
+__device__ __forceinline__ void map_diag_solve(Smem &s, int l16, int g4) {
+    const int B = g4;
     const float *ablk = &s.A[(16 * B) * AS + 16 * B];
     float x[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) x[i] = (i == l16) ? 1.f : 0.f;
-    // rows 0..7, then rows 8..15 after subtracting the lower-left 8x8 block's share
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
         const int r0 = 8 * half;
@@ -287,10 +310,7 @@ __device__ __forceinline__ void map_diag_solve(Smem &s, int B, int l16, int g4) 
             for (int r = j + 1; r < 8; ++r) x[r0 + r] -= a[r][j] * x[r0 + j];
     }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const float v = g4 == 0 ? x[r] : g4 == 1 ? x[4 + r] : g4 == 2 ? x[8 + r] : x[12 + r];
-        s.T[(16 * B + 4 * g4 + r) * TS + 16 * B + l16] = f32_to_bf16(v);
-    }
+    for (int r = 0; r < 16; ++r) s.T[(16 * B + r) * TS + 16 * B + l16] = f32_to_bf16(x[r]);
 }
 
 // ---------------------------------------------------------------------------------
@@ -346,22 +366,19 @@ __device__ __forceinline__ void map_merges(Smem &s, int l16, int g4) {
 }
 
 // ---------------------------------------------------------------------------------
-// Chain, phase 1: R = beta V - beta gamma (K S^T) and Q S^T for tokens [16W, 16W+16).
+// Chain, phase 1: R = beta V - beta gamma (K S^T) for tokens [16W, 16W+16).  The S
+// fragments stay in registers for Q S^T in phase 2.
 // ---------------------------------------------------------------------------------
-__device__ __forceinline__ void chain_R(Smem &s, int buf, int W, int l16, int g4, f32x4 &qs) {
+__device__ __forceinline__ void chain_R(Smem &s, int buf, int W, int l16, int g4, Frag<bf> (&fs)[4]) {
     const bf *krow = s.K[buf] + (16 * W + l16) * KS + 8 * g4;
-    const bf *qrow = s.Q[buf] + (16 * W + l16) * KS + 8 * g4;
     const bf *srow = s.S + l16 * KS + 8 * g4;
     f32x4 ks = zero4();
-    qs = zero4();
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-        Frag<bf> fk, fq, fs;
-        fs.load8(srow + 32 * kb);
+        Frag<bf> fk;
+        fs[kb].load8(srow + 32 * kb);
         fk.load8(krow + 32 * kb);
-        fq.load8(qrow + 32 * kb);
-        mma(ks, fk, fs);
-        mma(qs, fq, fs);
+        mma(ks, fk, fs[kb]);      // (K S^T): lane = value channel, rows = tokens
     }
     const int t0 = 16 * W + 4 * g4;
     const f32x4 b = *reinterpret_cast<const f32x4 *>(&s.gate[buf].beta[t0]);
@@ -370,6 +387,20 @@ __device__ __forceinline__ void chain_R(Smem &s, int buf, int W, int l16, int g4
 #pragma unroll
     for (int i = 0; i < 4; ++i) r[i] = b[i] * (to_f(s.V[buf][(t0 + i) * VS + l16]) - gm[i] * ks[i]);
     store4_split(&s.Rh[l16 * TS + t0], &s.Rl[l16 * TS + t0], r[0], r[1], r[2], r[3]);
+}
+
+// Chain, phase 2: (Q S^T)^T = S Q^T for tokens [16W, 16W+16) (lane = token, rows =
+// value channels), from the S fragments loaded in phase 1.
+__device__ __forceinline__ f32x4 chain_QS(Smem &s, int buf, int W, int l16, int g4, const Frag<bf> (&fs)[4]) {
+    const bf *qrow = s.Q[buf] + (16 * W + l16) * KS + 8 * g4;
+    f32x4 qs = zero4();
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+        Frag<bf> fq;
+        fq.load8(qrow + 32 * kb);
+        mma(qs, fs[kb], fq);
+    }
+    return qs;
 }
 
 // Chain, phase 2: v = T R for tokens [16W, 16W+16); T is lower triangular, so only
@@ -398,6 +429,8 @@ __device__ __forceinline__ void chain_out_update(Smem &s, const PrefillArgs &a, 
                                                  int g4, const f32x4 &qs, f32x4 (&st)[2], int h,
                                                  int dv0, int tok0, int nval) {
     {
+        // O^T = S Q^T diag(gamma) + v^T P^T: lane = token 16W + l16, rows = value
+        // channels 4G..4G+3, so each lane stores four consecutive outputs at once
         f32x4 acc = zero4();
         const bf *ph = s.Ph[buf] + (16 * W + l16) * TS + 8 * g4;
         const bf *pl = s.Pl[buf] + (16 * W + l16) * TS + 8 * g4;
@@ -407,32 +440,41 @@ __device__ __forceinline__ void chain_out_update(Smem &s, const PrefillArgs &a, 
             fpl.load8(pl + 32 * kb);
             fvh.load8(s.Vh + l16 * TS + 32 * kb + 8 * g4);
             fvl.load8(s.Vl + l16 * TS + 32 * kb + 8 * g4);
-            mma(acc, fph, fvh);
-            mma(acc, fph, fvl);
-            mma(acc, fpl, fvh);
+            mma(acc, fvh, fph);
+            mma(acc, fvl, fph);
+            mma(acc, fvh, fpl);
         }
-        const int t0 = 16 * W + 4 * g4;
-        const f32x4 gm = *reinterpret_cast<const f32x4 *>(&s.gate[buf].gam[t0]);
-        uint16_t *ob = reinterpret_cast<uint16_t *>(a.o) + (size_t)h * DV + dv0 + l16;
+        const int t = 16 * W + l16;
+        if (t < nval) {
+            const float gm = s.gate[buf].gam[t];
+            bf16x4 y;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int t = t0 + r;
-            if (t < nval) {
-                const float y = gm[r] * qs[r] + acc[r];
-                ob[(size_t)(tok0 + t) * a.Hv * DV] = __builtin_bit_cast(uint16_t, f32_to_bf16(y));
-            }
+            for (int r = 0; r < 4; ++r) y[r] = f32_to_bf16(gm * qs[r] + acc[r]);
+            *reinterpret_cast<bf16x4 *>(reinterpret_cast<uint16_t *>(a.o) +
+                                        ((size_t)(tok0 + t) * a.Hv + h) * DV + dv0 + 4 * g4) = y;
         }
     }
     {
         const float glast = s.gate[buf].gam[CH - 1];
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
+            // K^T fragments (slot e of group G = token 32kb + 8G + e, row = key channel
+            // 32W + 16mt + l16) with ds_read_b64_tr_b16: in each 16-lane group, source
+            // lane a points at 4 key channels of token t0 + a/4, and result lane m then
+            // holds key channel m of tokens t0..t0+3.
             Frag<bf> ka[2];
+            const int a_tok = l16 >> 2, a_ch = 32 * W + 16 * mt + 4 * (l16 & 3);
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    ka[kb].set_raw(e, s.K[buf][(32 * kb + 8 * g4 + e) * KS + 32 * W + 16 * mt + l16]);
+                for (int hh = 0; hh < 2; ++hh) {
+                    const int t0 = 32 * kb + 8 * g4 + 4 * hh;
+                    typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+                    const bf16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                        (lds_bf16x4 *)(&s.K[buf][(t0 + a_tok) * KS + a_ch]));
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) ka[kb].set_raw(4 * hh + e, v[e]);
+                }
             f32x4 acc = st[mt] * glast;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
@@ -507,52 +549,66 @@ __global__ __launch_bounds__(THREADS) void gdn_prefill_pipe_kernel(const Prefill
         Stage stg;
         stage_load(stg, a, wk, wk.bos, min(CH, len), tid);
         stage_commit(stg, s, 0, tid);
+        if (wave == 3) gate_scan(stg, s, 0, lane);
         if (nchunks > 1) stage_load(stg, a, wk, wk.bos + CH, min(CH, len - CH), tid);
         __syncthreads();
-        if (is_map) map_gate_grams(s, 0, W, lane, l16, g4);
-        __syncthreads();
-        if (is_map) map_diag_solve(s, W, l16, g4);
-        __syncthreads();
 
-        for (int c = 0; c < nchunks; ++c) {
-            const int buf = c & 1, nb = buf ^ 1;
-            const int tok0 = wk.bos + c * CH;
-            const int nval = min(CH, wk.eos - tok0);
-            const bool has_next = c + 1 < nchunks;
-
-            // phase 1
-            f32x4 qs;
-            if (is_map) {
+        // The two roles run separate loops with the same barrier sequence (three per
+        // chunk), so values one role keeps across a barrier do not occupy registers in
+        // the other role's code.  All 512 threads stage the next chunk in phase 1.
+        if (is_map) {
+            map_grams(s, 0, W, l16, g4);
+            __syncthreads();
+            if (wave == 0) map_diag_solve(s, l16, g4);
+            __syncthreads();
+            for (int c = 0; c < nchunks; ++c) {
+                const int nb = (c & 1) ^ 1;
+                const bool has_next = c + 1 < nchunks;
+                // phase 1
                 switch (W) {
                     case 0: map_merges<0>(s, l16, g4); break;
                     case 1: map_merges<1>(s, l16, g4); break;
                     case 2: map_merges<2>(s, l16, g4); break;
                     default: break;
                 }
-            } else {
-                chain_R(s, buf, W, l16, g4, qs);
+                if (has_next) {
+                    stage_commit(stg, s, nb, tid);
+                    if (wave == 3) gate_scan(stg, s, nb, lane);
+                    const int tok0 = wk.bos + c * CH;
+                    if (c + 2 < nchunks) stage_load(stg, a, wk, tok0 + 2 * CH, min(CH, wk.eos - tok0 - 2 * CH), tid);
+                }
+                __syncthreads();
+                // phase 2
+                if (has_next) map_grams(s, nb, W, l16, g4);
+                __syncthreads();
+                // phase 3
+                if (has_next && wave == 0) map_diag_solve(s, l16, g4);
+                __syncthreads();
             }
-            if (has_next) {
-                stage_commit(stg, s, nb, tid);
-                if (c + 2 < nchunks) stage_load(stg, a, wk, tok0 + 2 * CH, min(CH, wk.eos - tok0 - 2 * CH), tid);
-            }
+        } else {
             __syncthreads();
-
-            // phase 2
-            if (is_map) {
-                if (has_next) map_gate_grams(s, nb, W, lane, l16, g4);
-            } else {
+            __syncthreads();
+            for (int c = 0; c < nchunks; ++c) {
+                const int buf = c & 1, nb = buf ^ 1;
+                const int tok0 = wk.bos + c * CH;
+                const int nval = min(CH, wk.eos - tok0);
+                const bool has_next = c + 1 < nchunks;
+                // phase 1
+                Frag<bf> fs[4];
+                chain_R(s, buf, W, l16, g4, fs);
+                if (has_next) {
+                    stage_commit(stg, s, nb, tid);
+                    if (c + 2 < nchunks) stage_load(stg, a, wk, tok0 + 2 * CH, min(CH, wk.eos - tok0 - 2 * CH), tid);
+                }
+                __syncthreads();
+                // phase 2
                 chain_v(s, buf, W, l16, g4);
-            }
-            __syncthreads();
-
-            // phase 3
-            if (is_map) {
-                if (has_next) map_diag_solve(s, W, l16, g4);
-            } else {
+                const f32x4 qs = chain_QS(s, buf, W, l16, g4, fs);
+                __syncthreads();
+                // phase 3
                 chain_out_update(s, a, buf, W, l16, g4, qs, st, h, dv0, tok0, nval);
+                __syncthreads();
             }
-            __syncthreads();
         }
     }
 
