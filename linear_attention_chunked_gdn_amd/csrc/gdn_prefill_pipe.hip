@@ -16,14 +16,15 @@
 // wave and the latency of one hides behind the other.  A chunk costs three
 // workgroup barriers:
 //
-//   phase 1:  chain R(c)                 | map: T(c) blocks below the diagonal,
+//   phase 1:  chain R(c), Q S^T(c)       | map: T(c) blocks below the diagonal,
 //                                        |      gate scan of chunk c+1 (one wave)
-//             all waves: stage chunk c+1 into LDS, fetch chunk c+2 into registers
-//   phase 2:  chain v(c) = T(c) R(c),    | map: grams(c+1) -> A, P(c+1)
-//             Q S^T(c)                   |
-//   phase 3:  chain O(c), S update       | map: diagonal blocks of T(c+1) (one wave)
+//             all waves: k, v of chunk c+1 into LDS; fetch k, v, g, beta of c+2
+//   phase 2:  chain v(c) = T(c) R(c)     | map: K K^T(c+1) -> A
+//             all waves: q of chunk c+1 into LDS (q of c is dead); fetch q of c+2
+//   phase 3:  chain O(c), S update       | map: Q K^T(c+1) -> P(c+1), diagonal
+//                                        |      blocks of T(c+1) (one wave)
 //
-// LDS holds two buffers of the chunk tiles (K, Q, V, gates) and of P; T and A are
+// LDS holds two buffers of the k and v tiles, the gates and P; q, T and A are
 // single-buffered because their lifetimes do not overlap across the phases.
 // One workgroup = 8 wave64s = one (sequence, value head, 16 value channels).
 #include "gdn_device.h"
@@ -37,10 +38,15 @@ constexpr int DK = 128;
 constexpr int DV = 128;
 constexpr int DVS = 16;       // value channels per workgroup
 constexpr int THREADS = 512;   // 4 map + 4 chain waves
-constexpr int KS = DK + 8;    // bf16 row stride of K, Q and the state copy
-constexpr int TS = CH + 8;    // bf16 row stride of T, P, R^T, v^T, (lambda v)^T
-constexpr int VS = DVS + 8;   // bf16 row stride of the value tile
-constexpr int AS = CH + 4;    // fp32 row stride of A
+// LDS row strides, chosen by measurement on gfx950: 16-lane groups reading 16 B
+// from 16 consecutive rows are conflict-free when the row stride in bytes is 32
+// modulo 64 (288 B, 160 B); 8-byte writes across rows prefer an odd multiple of 8 B
+// (P, written in 8-byte pieces and read less often, uses 144 B).
+constexpr int KS = DK + 16;   // bf16 row stride of K and the state copy (288 B)
+constexpr int TS = CH + 16;   // bf16 row stride of T, R^T, v^T, (lambda v)^T (160 B)
+constexpr int TP = CH + 8;    // bf16 row stride of P (144 B)
+constexpr int VS = DVS + 8;   // bf16 row stride of the value tile (48 B)
+constexpr int AS = CH + 8;    // fp32 row stride of A (288 B)
 constexpr float LOG2E = 1.4426950408889634f;
 
 typedef __bf16 bf;
@@ -61,21 +67,16 @@ struct Gate {
 
 struct __align__(16) Smem {
     bf K[2][CH * KS];
-    bf Q[2][CH * KS];
+    bf Q[CH * KS];
     bf V[2][CH * VS];
     Gate gate[2];
     float A[CH * AS];              // A of the chunk being mapped, strictly lower
     bf T[CH * TS];                 // T = (I + A)^-1
-    bf Ph[2][CH * TS], Pl[2][CH * TS];   // P split into bf16 hi + lo
+    bf Ph[2][CH * TP], Pl[2][CH * TP];   // P split into bf16 hi + lo
     bf S[DVS * KS];                // bf16 copy of the state slice [value ch][key ch]
     bf Rh[DVS * TS], Rl[DVS * TS];  // R^T
     bf Vh[DVS * TS], Vl[DVS * TS];  // v^T
     bf Wh[DVS * TS], Wl[DVS * TS];  // (diag(lambda) v)^T
-};
-
-struct Stage {
-    uint4 k[2], q[2], v;
-    float g, b;
 };
 
 __device__ __forceinline__ float to_f(bf x) { return bf16_to_f32(x); }
@@ -114,59 +115,75 @@ struct Work {
     int h, bos, eos;
 };
 
+// Staged copy of one chunk's k, v, g and beta, fetched a chunk ahead.  Loads are
+// unconditional: rows past the chunk's end read the last valid token instead (finite
+// values), because a load under a branch would make the compiler wait for it at the
+// branch join.  Those rows need no zeros: their g and beta are set to 0 when the gate
+// is computed, so their rows of A, R and v vanish, and their k and v then contribute
+// nothing; their q only reaches outputs that are not stored.
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+struct Stage {
+    u32x4 k0, k1, v;   // native vectors so the stage always lives in registers
+    float g, b;
+    int nval;
+};
+struct StageQ {
+    u32x4 q0, q1;
+};
+
 __device__ __forceinline__ void stage_load(Stage &st, const PrefillArgs &a, const Work &wk, int tok0,
                                            int nval, int tid) {
     const char *kb = reinterpret_cast<const char *>(a.k) + wk.kq_base;
-    const char *qb = reinterpret_cast<const char *>(a.q) + wk.kq_base;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int f = tid + THREADS * i;
-        const int row = f >> 4, seg = f & 15;
-        uint4 zk = make_uint4(0, 0, 0, 0), zq = zk;
-        if (row < nval) {
-            const size_t off = (size_t)(tok0 + row) * wk.kq_row + (size_t)seg * 16;
-            zk = *reinterpret_cast<const uint4 *>(kb + off);
-            zq = *reinterpret_cast<const uint4 *>(qb + off);
-        }
-        st.k[i] = zk;
-        st.q[i] = zq;
-    }
     {
-        const int row = tid >> 1, seg = tid & 1;   // 64 rows x 2 segments of 16 B
-        uint4 z = make_uint4(0, 0, 0, 0);
-        if (tid < 2 * CH && row < nval)
-            z = *reinterpret_cast<const uint4 *>(reinterpret_cast<const char *>(a.v) + wk.v_off +
-                                                 (size_t)(tok0 + row) * wk.v_row + (size_t)seg * 16);
-        st.v = z;
+        const int row0 = min(tid >> 4, nval - 1), row1 = min((tid + THREADS) >> 4, nval - 1), seg = tid & 15;
+        st.k0 = *reinterpret_cast<const u32x4 *>(kb + (size_t)(tok0 + row0) * wk.kq_row + (size_t)seg * 16);
+        st.k1 = *reinterpret_cast<const u32x4 *>(kb + (size_t)(tok0 + row1) * wk.kq_row + (size_t)seg * 16);
     }
-    // g and beta go to map wave 3 (threads 192..255), which scans them itself
-    st.g = 0.f;
-    st.b = 0.f;
-    const int gt = tid - 3 * 64;
-    if (gt >= 0 && gt < CH && gt < nval) {
-        st.g = a.g[(size_t)(tok0 + gt) * a.Hv + wk.h];
-        st.b = a.beta[(size_t)(tok0 + gt) * a.Hv + wk.h];
+    {   // 64 rows x 2 segments of 16 B; threads 128..511 repeat them (cache hits) so that
+        // every field of the stage is written unconditionally
+        const int t = tid & (2 * CH - 1);
+        const int row = min(t >> 1, nval - 1), seg = t & 1;
+        st.v = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(a.v) + wk.v_off +
+                                                (size_t)(tok0 + row) * wk.v_row + (size_t)seg * 16);
     }
+    {   // g and beta of token (tid mod 64); map wave 3 (threads 192..255) scans them
+        const int row = min(tid & (CH - 1), nval - 1);
+        st.g = a.g[(size_t)(tok0 + row) * a.Hv + wk.h];
+        st.b = a.beta[(size_t)(tok0 + row) * a.Hv + wk.h];
+    }
+    st.nval = nval;
+}
+
+__device__ __forceinline__ void stage_load_q(StageQ &st, const PrefillArgs &a, const Work &wk, int tok0,
+                                             int nval, int tid) {
+    const char *qb = reinterpret_cast<const char *>(a.q) + wk.kq_base;
+    const int row0 = min(tid >> 4, nval - 1), row1 = min((tid + THREADS) >> 4, nval - 1), seg = tid & 15;
+    st.q0 = *reinterpret_cast<const u32x4 *>(qb + (size_t)(tok0 + row0) * wk.kq_row + (size_t)seg * 16);
+    st.q1 = *reinterpret_cast<const u32x4 *>(qb + (size_t)(tok0 + row1) * wk.kq_row + (size_t)seg * 16);
 }
 
 __device__ __forceinline__ void stage_commit(const Stage &st, Smem &s, int buf, int tid) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int f = tid + THREADS * i;
-        const int row = f >> 4, seg = f & 15;
-        *reinterpret_cast<uint4 *>(&s.K[buf][row * KS + seg * 8]) = st.k[i];
-        *reinterpret_cast<uint4 *>(&s.Q[buf][row * KS + seg * 8]) = st.q[i];
-    }
+    const int seg = tid & 15;
+    *reinterpret_cast<u32x4 *>(&s.K[buf][(tid >> 4) * KS + seg * 8]) = st.k0;
+    *reinterpret_cast<u32x4 *>(&s.K[buf][((tid + THREADS) >> 4) * KS + seg * 8]) = st.k1;
     if (tid < 2 * CH) {
-        const int row = tid >> 1, seg = tid & 1;
-        *reinterpret_cast<uint4 *>(&s.V[buf][row * VS + seg * 8]) = st.v;
+        const int row = tid >> 1, vseg = tid & 1;
+        *reinterpret_cast<u32x4 *>(&s.V[buf][row * VS + vseg * 8]) = st.v;
     }
+}
+
+__device__ __forceinline__ void stage_commit_q(const StageQ &st, Smem &s, int tid) {
+    const int seg = tid & 15;
+    *reinterpret_cast<u32x4 *>(&s.Q[(tid >> 4) * KS + seg * 8]) = st.q0;
+    *reinterpret_cast<u32x4 *>(&s.Q[((tid + THREADS) >> 4) * KS + seg * 8]) = st.q1;
 }
 
 // #1 Gate for the chunk staged in buffer buf, by map wave 3 (lane = token): the
 // inclusive scan of g and every decay factor the grams and the chain need.
 __device__ __forceinline__ void gate_scan(const Stage &st, Smem &s, int buf, int lane) {
-    const float x2 = wave_inclusive_scan(st.g, lane) * LOG2E;
+    const bool valid = lane < st.nval;
+    const float x2 = wave_inclusive_scan(valid ? st.g : 0.f, lane) * LOG2E;
     const float last2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x2), 63));
     const float b16 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x2), 16));
     const float b32 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x2), 32));
@@ -175,7 +192,7 @@ __device__ __forceinline__ void gate_scan(const Stage &st, Smem &s, int buf, int
     const int blk = lane >> 4;
     const float start = blk == 0 ? b0 : blk == 1 ? b16 : blk == 2 ? b32 : b48;
     Gate &gt = s.gate[buf];
-    gt.beta[lane] = st.b;
+    gt.beta[lane] = valid ? st.b : 0.f;
     gt.g2[lane] = x2;
     gt.gam[lane] = __builtin_amdgcn_exp2f(x2);
     gt.lam[lane] = __builtin_amdgcn_exp2f(last2 - x2);
@@ -189,8 +206,8 @@ __device__ __forceinline__ void gate_scan(const Stage &st, Smem &s, int buf, int
 
 // ---------------------------------------------------------------------------------
 // Map: grams of the chunk in buffer nb.  Map wave m computes, for one gram (K K^T for
-// m even, Q K^T for m odd), the lower tiles of the row-block pair {0, 3} (m < 2) or
-// {1, 2} (m >= 2): five 16x16 tiles per wave.  Tiles are computed transposed
+// m even, in phase 2; Q K^T for m odd, in phase 3), the lower tiles of the row-block
+// pair {0, 3} (m < 2) or {1, 2} (m >= 2): five 16x16 tiles per wave.  Tiles are computed transposed
 // (K_j X_i^T with X = K or Q), so each lane ends with one row and four consecutive
 // columns and writes them with one vector store.  A goes to s.A (fp32), P to
 // s.Ph/Pl[nb] (split bf16).
@@ -222,7 +239,7 @@ __device__ __forceinline__ void gram_epilogue(Smem &s, int nb, int bi, int bj, c
         *reinterpret_cast<f32x4 *>(&s.A[rr * AS + c0]) =
             f32x4{br * acc[0] * d[0], br * acc[1] * d[1], br * acc[2] * d[2], br * acc[3] * d[3]};
     } else {
-        store4_split(&s.Ph[nb][rr * TS + c0], &s.Pl[nb][rr * TS + c0], acc[0] * d[0], acc[1] * d[1],
+        store4_split(&s.Ph[nb][rr * TP + c0], &s.Pl[nb][rr * TP + c0], acc[0] * d[0], acc[1] * d[1],
                      acc[2] * d[2], acc[3] * d[3]);
     }
 }
@@ -230,7 +247,6 @@ __device__ __forceinline__ void gram_epilogue(Smem &s, int nb, int bi, int bj, c
 template <bool ISQ, int RB0, int RB1>
 __device__ __forceinline__ void gram_rows(Smem &s, int nb, int l16, int g4) {
     static_assert(RB0 < RB1 && RB0 + RB1 == 3, "row-block pairs are {0,3} and {1,2}");
-    const bf *src = ISQ ? s.Q[nb] : s.K[nb];
     f32x4 c0[RB0 + 1], c1[RB1 + 1];
 #pragma unroll
     for (int j = 0; j <= RB0; ++j) c0[j] = zero4();
@@ -239,10 +255,15 @@ __device__ __forceinline__ void gram_rows(Smem &s, int nb, int l16, int g4) {
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
         Frag<bf> x0, x1, kj[RB1 + 1];
-        x0.load8(src + (16 * RB0 + l16) * KS + 32 * kb + 8 * g4);
-        x1.load8(src + (16 * RB1 + l16) * KS + 32 * kb + 8 * g4);
 #pragma unroll
         for (int j = 0; j <= RB1; ++j) kj[j].load8(s.K[nb] + (16 * j + l16) * KS + 32 * kb + 8 * g4);
+        if constexpr (ISQ) {
+            x0.load8(s.Q + (16 * RB0 + l16) * KS + 32 * kb + 8 * g4);
+            x1.load8(s.Q + (16 * RB1 + l16) * KS + 32 * kb + 8 * g4);
+        } else {
+            x0 = kj[RB0];
+            x1 = kj[RB1];
+        }
 #pragma unroll
         for (int j = 0; j <= RB1; ++j) {
             mma(c1[j], kj[j], x1);
@@ -255,13 +276,16 @@ __device__ __forceinline__ void gram_rows(Smem &s, int nb, int l16, int g4) {
     for (int j = 0; j <= RB1; ++j) gram_epilogue<ISQ>(s, nb, RB1, j, c1[j], l16, g4);
 }
 
-__device__ __forceinline__ void map_grams(Smem &s, int nb, int m, int l16, int g4) {
-    switch (m) {
-        case 0: gram_rows<false, 0, 3>(s, nb, l16, g4); break;
-        case 1: gram_rows<true, 0, 3>(s, nb, l16, g4); break;
-        case 2: gram_rows<false, 1, 2>(s, nb, l16, g4); break;
-        default: gram_rows<true, 1, 2>(s, nb, l16, g4); break;
-    }
+// K K^T of the chunk in buffer nb: map waves 0 and 2 (row-block pairs {0,3}, {1,2}).
+__device__ __forceinline__ void map_gram_kk(Smem &s, int nb, int m, int l16, int g4) {
+    if (m == 0) gram_rows<false, 0, 3>(s, nb, l16, g4);
+    else gram_rows<false, 1, 2>(s, nb, l16, g4);
+}
+
+// Q K^T of the chunk in buffer nb (q in the single q buffer): map waves 1 and 3.
+__device__ __forceinline__ void map_gram_qk(Smem &s, int nb, int m, int l16, int g4) {
+    if (m == 1) gram_rows<true, 0, 3>(s, nb, l16, g4);
+    else gram_rows<true, 1, 2>(s, nb, l16, g4);
 }
 
 // ---------------------------------------------------------------------------------
@@ -367,7 +391,7 @@ __device__ __forceinline__ void map_merges(Smem &s, int l16, int g4) {
 
 // ---------------------------------------------------------------------------------
 // Chain, phase 1: R = beta V - beta gamma (K S^T) for tokens [16W, 16W+16).  The S
-// fragments stay in registers for Q S^T in phase 2.
+// fragments are returned for Q S^T.
 // ---------------------------------------------------------------------------------
 __device__ __forceinline__ void chain_R(Smem &s, int buf, int W, int l16, int g4, Frag<bf> (&fs)[4]) {
     const bf *krow = s.K[buf] + (16 * W + l16) * KS + 8 * g4;
@@ -389,10 +413,10 @@ __device__ __forceinline__ void chain_R(Smem &s, int buf, int W, int l16, int g4
     store4_split(&s.Rh[l16 * TS + t0], &s.Rl[l16 * TS + t0], r[0], r[1], r[2], r[3]);
 }
 
-// Chain, phase 2: (Q S^T)^T = S Q^T for tokens [16W, 16W+16) (lane = token, rows =
-// value channels), from the S fragments loaded in phase 1.
-__device__ __forceinline__ f32x4 chain_QS(Smem &s, int buf, int W, int l16, int g4, const Frag<bf> (&fs)[4]) {
-    const bf *qrow = s.Q[buf] + (16 * W + l16) * KS + 8 * g4;
+// Chain, phase 1: (Q S^T)^T = S Q^T for tokens [16W, 16W+16) (lane = token, rows =
+// value channels), from the S fragments loaded by chain_R.
+__device__ __forceinline__ f32x4 chain_QS(const Smem &s, int W, int l16, int g4, const Frag<bf> (&fs)[4]) {
+    const bf *qrow = s.Q + (16 * W + l16) * KS + 8 * g4;
     f32x4 qs = zero4();
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
@@ -432,8 +456,8 @@ __device__ __forceinline__ void chain_out_update(Smem &s, const PrefillArgs &a, 
         // O^T = S Q^T diag(gamma) + v^T P^T: lane = token 16W + l16, rows = value
         // channels 4G..4G+3, so each lane stores four consecutive outputs at once
         f32x4 acc = zero4();
-        const bf *ph = s.Ph[buf] + (16 * W + l16) * TS + 8 * g4;
-        const bf *pl = s.Pl[buf] + (16 * W + l16) * TS + 8 * g4;
+        const bf *ph = s.Ph[buf] + (16 * W + l16) * TP + 8 * g4;
+        const bf *pl = s.Pl[buf] + (16 * W + l16) * TP + 8 * g4;
         for (int kb = 0; kb <= (W >> 1); ++kb) {
             Frag<bf> fph, fpl, fvh, fvl;
             fph.load8(ph + 32 * kb);
@@ -542,28 +566,35 @@ __global__ __launch_bounds__(THREADS) void gdn_prefill_pipe_kernel(const Prefill
     }
 
     if (nchunks > 0) {
-        for (int i = tid; i < CH * TS; i += THREADS) {
-            s.T[i] = f32_to_bf16(0.f);
+        for (int i = tid; i < CH * TS; i += THREADS) s.T[i] = f32_to_bf16(0.f);
+        for (int i = tid; i < CH * TP; i += THREADS)
             s.Ph[0][i] = s.Ph[1][i] = s.Pl[0][i] = s.Pl[1][i] = f32_to_bf16(0.f);
-        }
         Stage stg;
+        StageQ stq;
         stage_load(stg, a, wk, wk.bos, min(CH, len), tid);
+        stage_load_q(stq, a, wk, wk.bos, min(CH, len), tid);
         stage_commit(stg, s, 0, tid);
+        stage_commit_q(stq, s, tid);
         if (wave == 3) gate_scan(stg, s, 0, lane);
-        if (nchunks > 1) stage_load(stg, a, wk, wk.bos + CH, min(CH, len - CH), tid);
+        if (nchunks > 1) {
+            stage_load(stg, a, wk, wk.bos + CH, min(CH, len - CH), tid);
+            stage_load_q(stq, a, wk, wk.bos + CH, min(CH, len - CH), tid);
+        }
         __syncthreads();
 
         // The two roles run separate loops with the same barrier sequence (three per
         // chunk), so values one role keeps across a barrier do not occupy registers in
-        // the other role's code.  All 512 threads stage the next chunk in phase 1.
+        // the other role's code.  All 512 threads stage the next chunk's tiles.
         if (is_map) {
-            map_grams(s, 0, W, l16, g4);
+            if (!(W & 1)) map_gram_kk(s, 0, W, l16, g4);
             __syncthreads();
+            if (W & 1) map_gram_qk(s, 0, W, l16, g4);
             if (wave == 0) map_diag_solve(s, l16, g4);
             __syncthreads();
             for (int c = 0; c < nchunks; ++c) {
                 const int nb = (c & 1) ^ 1;
                 const bool has_next = c + 1 < nchunks;
+                const int t2 = wk.bos + (c + 2) * CH;
                 // phase 1
                 switch (W) {
                     case 0: map_merges<0>(s, l16, g4); break;
@@ -574,15 +605,21 @@ __global__ __launch_bounds__(THREADS) void gdn_prefill_pipe_kernel(const Prefill
                 if (has_next) {
                     stage_commit(stg, s, nb, tid);
                     if (wave == 3) gate_scan(stg, s, nb, lane);
-                    const int tok0 = wk.bos + c * CH;
-                    if (c + 2 < nchunks) stage_load(stg, a, wk, tok0 + 2 * CH, min(CH, wk.eos - tok0 - 2 * CH), tid);
+                    if (c + 2 < nchunks) stage_load(stg, a, wk, t2, min(CH, wk.eos - t2), tid);
                 }
                 __syncthreads();
                 // phase 2
-                if (has_next) map_grams(s, nb, W, l16, g4);
+                if (has_next) {
+                    if (!(W & 1)) map_gram_kk(s, nb, W, l16, g4);
+                    stage_commit_q(stq, s, tid);
+                    if (c + 2 < nchunks) stage_load_q(stq, a, wk, t2, min(CH, wk.eos - t2), tid);
+                }
                 __syncthreads();
                 // phase 3
-                if (has_next && wave == 0) map_diag_solve(s, l16, g4);
+                if (has_next) {
+                    if (W & 1) map_gram_qk(s, nb, W, l16, g4);
+                    if (wave == 0) map_diag_solve(s, l16, g4);
+                }
                 __syncthreads();
             }
         } else {
@@ -593,17 +630,22 @@ __global__ __launch_bounds__(THREADS) void gdn_prefill_pipe_kernel(const Prefill
                 const int tok0 = wk.bos + c * CH;
                 const int nval = min(CH, wk.eos - tok0);
                 const bool has_next = c + 1 < nchunks;
+                const int t2 = tok0 + 2 * CH;
                 // phase 1
                 Frag<bf> fs[4];
                 chain_R(s, buf, W, l16, g4, fs);
+                const f32x4 qs = chain_QS(s, W, l16, g4, fs);
                 if (has_next) {
                     stage_commit(stg, s, nb, tid);
-                    if (c + 2 < nchunks) stage_load(stg, a, wk, tok0 + 2 * CH, min(CH, wk.eos - tok0 - 2 * CH), tid);
+                    if (c + 2 < nchunks) stage_load(stg, a, wk, t2, min(CH, wk.eos - t2), tid);
                 }
                 __syncthreads();
                 // phase 2
                 chain_v(s, buf, W, l16, g4);
-                const f32x4 qs = chain_QS(s, buf, W, l16, g4, fs);
+                if (has_next) {
+                    stage_commit_q(stq, s, tid);
+                    if (c + 2 < nchunks) stage_load_q(stq, a, wk, t2, min(CH, wk.eos - t2), tid);
+                }
                 __syncthreads();
                 // phase 3
                 chain_out_update(s, a, buf, W, l16, g4, qs, st, h, dv0, tok0, nval);
