@@ -30,6 +30,8 @@
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
+#include <type_traits>
+
 namespace gdn {
 namespace pipe {
 
@@ -112,6 +114,7 @@ struct Work {
     size_t kq_row;          // bytes between tokens in q/k
     size_t v_row;           // bytes between tokens in v
     size_t v_off;           // byte offset of (head, slice) in v
+    unsigned kq_row32, v_row32;   // the same strides as 32-bit values (row offsets < 2^32)
     int h, bos, eos;
 };
 
@@ -132,35 +135,43 @@ struct StageQ {
     u32x4 q0, q1;
 };
 
+// Rows of the staged tiles a thread loads: k and q rows tid/16 and tid/16 + 32 (16-byte
+// segment tid%16); v row (tid%128)/2 (segment tid%2); g, beta row tid%64.  The chunk's
+// base address is wave-uniform (scalar registers) and each lane adds a 32-bit offset;
+// rows are clamped only in a sequence's short last chunk.
 __device__ __forceinline__ void stage_load(Stage &st, const PrefillArgs &a, const Work &wk, int tok0,
                                            int nval, int tid) {
-    const char *kb = reinterpret_cast<const char *>(a.k) + wk.kq_base;
-    {
-        const int row0 = min(tid >> 4, nval - 1), row1 = min((tid + THREADS) >> 4, nval - 1), seg = tid & 15;
-        st.k0 = *reinterpret_cast<const u32x4 *>(kb + (size_t)(tok0 + row0) * wk.kq_row + (size_t)seg * 16);
-        st.k1 = *reinterpret_cast<const u32x4 *>(kb + (size_t)(tok0 + row1) * wk.kq_row + (size_t)seg * 16);
+    const char *kb = reinterpret_cast<const char *>(a.k) + wk.kq_base + (size_t)tok0 * wk.kq_row;
+    const char *vb = reinterpret_cast<const char *>(a.v) + wk.v_off + (size_t)tok0 * wk.v_row;
+    const float *gb = a.g + (size_t)tok0 * a.Hv + wk.h;
+    const float *bb = a.beta + (size_t)tok0 * a.Hv + wk.h;
+    int r0 = tid >> 4, r1 = (tid + THREADS) >> 4, rv = (tid & (2 * CH - 1)) >> 1, rg = tid & (CH - 1);
+    if (nval < CH) {
+        r0 = min(r0, nval - 1);
+        r1 = min(r1, nval - 1);
+        rv = min(rv, nval - 1);
+        rg = min(rg, nval - 1);
     }
-    {   // 64 rows x 2 segments of 16 B; threads 128..511 repeat them (cache hits) so that
-        // every field of the stage is written unconditionally
-        const int t = tid & (2 * CH - 1);
-        const int row = min(t >> 1, nval - 1), seg = t & 1;
-        st.v = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(a.v) + wk.v_off +
-                                                (size_t)(tok0 + row) * wk.v_row + (size_t)seg * 16);
-    }
-    {   // g and beta of token (tid mod 64); map wave 3 (threads 192..255) scans them
-        const int row = min(tid & (CH - 1), nval - 1);
-        st.g = a.g[(size_t)(tok0 + row) * a.Hv + wk.h];
-        st.b = a.beta[(size_t)(tok0 + row) * a.Hv + wk.h];
-    }
+    const unsigned seg = (tid & 15) * 16;
+    st.k0 = *reinterpret_cast<const u32x4 *>(kb + ((unsigned)r0 * wk.kq_row32 + seg));
+    st.k1 = *reinterpret_cast<const u32x4 *>(kb + ((unsigned)r1 * wk.kq_row32 + seg));
+    st.v = *reinterpret_cast<const u32x4 *>(vb + ((unsigned)rv * wk.v_row32 + (tid & 1) * 16));
+    st.g = gb[(unsigned)rg * (unsigned)a.Hv];
+    st.b = bb[(unsigned)rg * (unsigned)a.Hv];
     st.nval = nval;
 }
 
 __device__ __forceinline__ void stage_load_q(StageQ &st, const PrefillArgs &a, const Work &wk, int tok0,
                                              int nval, int tid) {
-    const char *qb = reinterpret_cast<const char *>(a.q) + wk.kq_base;
-    const int row0 = min(tid >> 4, nval - 1), row1 = min((tid + THREADS) >> 4, nval - 1), seg = tid & 15;
-    st.q0 = *reinterpret_cast<const u32x4 *>(qb + (size_t)(tok0 + row0) * wk.kq_row + (size_t)seg * 16);
-    st.q1 = *reinterpret_cast<const u32x4 *>(qb + (size_t)(tok0 + row1) * wk.kq_row + (size_t)seg * 16);
+    const char *qb = reinterpret_cast<const char *>(a.q) + wk.kq_base + (size_t)tok0 * wk.kq_row;
+    int r0 = tid >> 4, r1 = (tid + THREADS) >> 4;
+    if (nval < CH) {
+        r0 = min(r0, nval - 1);
+        r1 = min(r1, nval - 1);
+    }
+    const unsigned seg = (tid & 15) * 16;
+    st.q0 = *reinterpret_cast<const u32x4 *>(qb + ((unsigned)r0 * wk.kq_row32 + seg));
+    st.q1 = *reinterpret_cast<const u32x4 *>(qb + ((unsigned)r1 * wk.kq_row32 + seg));
 }
 
 __device__ __forceinline__ void stage_commit(const Stage &st, Smem &s, int buf, int tid) {
@@ -538,6 +549,8 @@ __global__ __launch_bounds__(THREADS) void gdn_prefill_pipe_kernel(const Prefill
     wk.kq_row = (size_t)a.Hk * DK * 2;
     wk.v_row = (size_t)a.Hv * DV * 2;
     wk.v_off = ((size_t)h * DV + dv0) * 2;
+    wk.kq_row32 = (unsigned)wk.kq_row;
+    wk.v_row32 = (unsigned)wk.v_row;
     wk.h = h;
     wk.bos = 0;
     wk.eos = a.T_tot;
@@ -585,14 +598,18 @@ __global__ __launch_bounds__(THREADS) void gdn_prefill_pipe_kernel(const Prefill
         // The two roles run separate loops with the same barrier sequence (three per
         // chunk), so values one role keeps across a barrier do not occupy registers in
         // the other role's code.  All 512 threads stage the next chunk's tiles.
+        // Each loop trip runs two chunks, so the LDS buffer of every access is a
+        // compile-time constant (it folds into the instruction's immediate offset).
+        using B0 = std::integral_constant<int, 0>;
+        using B1 = std::integral_constant<int, 1>;
         if (is_map) {
             if (!(W & 1)) map_gram_kk(s, 0, W, l16, g4);
             __syncthreads();
             if (W & 1) map_gram_qk(s, 0, W, l16, g4);
             if (wave == 0) map_diag_solve(s, l16, g4);
             __syncthreads();
-            for (int c = 0; c < nchunks; ++c) {
-                const int nb = (c & 1) ^ 1;
+            auto step = [&](auto bufc, int c) {
+                constexpr int nb = decltype(bufc)::value ^ 1;
                 const bool has_next = c + 1 < nchunks;
                 const int t2 = wk.bos + (c + 2) * CH;
                 // phase 1
@@ -621,12 +638,16 @@ __global__ __launch_bounds__(THREADS) void gdn_prefill_pipe_kernel(const Prefill
                     if (wave == 0) map_diag_solve(s, l16, g4);
                 }
                 __syncthreads();
+            };
+            for (int c = 0; c < nchunks; c += 2) {
+                step(B0{}, c);
+                if (c + 1 < nchunks) step(B1{}, c + 1);
             }
         } else {
             __syncthreads();
             __syncthreads();
-            for (int c = 0; c < nchunks; ++c) {
-                const int buf = c & 1, nb = buf ^ 1;
+            auto step = [&](auto bufc, int c) {
+                constexpr int buf = decltype(bufc)::value, nb = buf ^ 1;
                 const int tok0 = wk.bos + c * CH;
                 const int nval = min(CH, wk.eos - tok0);
                 const bool has_next = c + 1 < nchunks;
@@ -650,6 +671,10 @@ __global__ __launch_bounds__(THREADS) void gdn_prefill_pipe_kernel(const Prefill
                 // phase 3
                 chain_out_update(s, a, buf, W, l16, g4, qs, st, h, dv0, tok0, nval);
                 __syncthreads();
+            };
+            for (int c = 0; c < nchunks; c += 2) {
+                step(B0{}, c);
+                if (c + 1 < nchunks) step(B1{}, c + 1);
             }
         }
     }
