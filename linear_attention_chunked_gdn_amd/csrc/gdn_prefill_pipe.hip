@@ -127,7 +127,8 @@ struct Work {
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 struct Stage {
-    u32x4 k0, k1, v;   // native vectors so the stage always lives in registers
+    u32x4 k0, k1;   // native vectors so the stage always lives in registers
+    unsigned v;
     float g, b;
     int nval;
 };
@@ -136,16 +137,19 @@ struct StageQ {
 };
 
 // Rows of the staged tiles a thread loads: k and q rows tid/16 and tid/16 + 32 (16-byte
-// segment tid%16); v row (tid%128)/2 (segment tid%2); g, beta row tid%64.  The chunk's
-// base address is wave-uniform (scalar registers) and each lane adds a 32-bit offset;
-// rows are clamped only in a sequence's short last chunk.
+// segment tid%16); v row tid/8 (4-byte piece tid%8); g, beta row tid%64.  Every thread
+// loads and commits the same amount, with no branch around a load or an LDS write,
+// so the compiler's wait for a staged value covers exactly that value and not the
+// younger prefetches.  The chunk's base address is wave-uniform (scalar registers)
+// and each lane adds a 32-bit offset; rows are clamped only in a sequence's short
+// last chunk.
 __device__ __forceinline__ void stage_load(Stage &st, const PrefillArgs &a, const Work &wk, int tok0,
                                            int nval, int tid) {
     const char *kb = reinterpret_cast<const char *>(a.k) + wk.kq_base + (size_t)tok0 * wk.kq_row;
     const char *vb = reinterpret_cast<const char *>(a.v) + wk.v_off + (size_t)tok0 * wk.v_row;
     const float *gb = a.g + (size_t)tok0 * a.Hv + wk.h;
     const float *bb = a.beta + (size_t)tok0 * a.Hv + wk.h;
-    int r0 = tid >> 4, r1 = (tid + THREADS) >> 4, rv = (tid & (2 * CH - 1)) >> 1, rg = tid & (CH - 1);
+    int r0 = tid >> 4, r1 = (tid + THREADS) >> 4, rv = tid >> 3, rg = tid & (CH - 1);
     if (nval < CH) {
         r0 = min(r0, nval - 1);
         r1 = min(r1, nval - 1);
@@ -155,7 +159,7 @@ __device__ __forceinline__ void stage_load(Stage &st, const PrefillArgs &a, cons
     const unsigned seg = (tid & 15) * 16;
     st.k0 = *reinterpret_cast<const u32x4 *>(kb + ((unsigned)r0 * wk.kq_row32 + seg));
     st.k1 = *reinterpret_cast<const u32x4 *>(kb + ((unsigned)r1 * wk.kq_row32 + seg));
-    st.v = *reinterpret_cast<const u32x4 *>(vb + ((unsigned)rv * wk.v_row32 + (tid & 1) * 16));
+    st.v = *reinterpret_cast<const unsigned *>(vb + ((unsigned)rv * wk.v_row32 + (tid & 7) * 4));
     st.g = gb[(unsigned)rg * (unsigned)a.Hv];
     st.b = bb[(unsigned)rg * (unsigned)a.Hv];
     st.nval = nval;
@@ -174,14 +178,19 @@ __device__ __forceinline__ void stage_load_q(StageQ &st, const PrefillArgs &a, c
     st.q1 = *reinterpret_cast<const u32x4 *>(qb + ((unsigned)r1 * wk.kq_row32 + seg));
 }
 
+// First token of the chunk to prefetch.  Past the sequence's last chunk the last chunk
+// is fetched again (in bounds, never used), so every loop trip issues the same loads
+// and commits; the commits then land in the LDS buffer or q tile that no wave reads
+// any more.
+__device__ __forceinline__ int prefetch_tok(const Work &wk, int c, int nchunks) {
+    return wk.bos + min(c, nchunks - 1) * CH;
+}
+
 __device__ __forceinline__ void stage_commit(const Stage &st, Smem &s, int buf, int tid) {
     const int seg = tid & 15;
     *reinterpret_cast<u32x4 *>(&s.K[buf][(tid >> 4) * KS + seg * 8]) = st.k0;
     *reinterpret_cast<u32x4 *>(&s.K[buf][((tid + THREADS) >> 4) * KS + seg * 8]) = st.k1;
-    if (tid < 2 * CH) {
-        const int row = tid >> 1, vseg = tid & 1;
-        *reinterpret_cast<u32x4 *>(&s.V[buf][row * VS + vseg * 8]) = st.v;
-    }
+    *reinterpret_cast<unsigned *>(&s.V[buf][(tid >> 3) * VS + (tid & 7) * 2]) = st.v;
 }
 
 __device__ __forceinline__ void stage_commit_q(const StageQ &st, Smem &s, int tid) {
@@ -589,9 +598,10 @@ __global__ __launch_bounds__(THREADS) void gdn_prefill_pipe_kernel(const Prefill
         stage_commit(stg, s, 0, tid);
         stage_commit_q(stq, s, tid);
         if (wave == 3) gate_scan(stg, s, 0, lane);
-        if (nchunks > 1) {
-            stage_load(stg, a, wk, wk.bos + CH, min(CH, len - CH), tid);
-            stage_load_q(stq, a, wk, wk.bos + CH, min(CH, len - CH), tid);
+        {
+            const int t1 = prefetch_tok(wk, 1, nchunks), n1 = min(CH, wk.eos - t1);
+            stage_load(stg, a, wk, t1, n1, tid);
+            stage_load_q(stq, a, wk, t1, n1, tid);
         }
         __syncthreads();
 
@@ -611,7 +621,8 @@ __global__ __launch_bounds__(THREADS) void gdn_prefill_pipe_kernel(const Prefill
             auto step = [&](auto bufc, int c) {
                 constexpr int nb = decltype(bufc)::value ^ 1;
                 const bool has_next = c + 1 < nchunks;
-                const int t2 = wk.bos + (c + 2) * CH;
+                const int t2 = prefetch_tok(wk, c + 2, nchunks);
+                const int n2 = min(CH, wk.eos - t2);
                 // phase 1
                 switch (W) {
                     case 0: map_merges<0>(s, l16, g4); break;
@@ -619,18 +630,14 @@ __global__ __launch_bounds__(THREADS) void gdn_prefill_pipe_kernel(const Prefill
                     case 2: map_merges<2>(s, l16, g4); break;
                     default: break;
                 }
-                if (has_next) {
-                    stage_commit(stg, s, nb, tid);
-                    if (wave == 3) gate_scan(stg, s, nb, lane);
-                    if (c + 2 < nchunks) stage_load(stg, a, wk, t2, min(CH, wk.eos - t2), tid);
-                }
+                stage_commit(stg, s, nb, tid);
+                if (wave == 3) gate_scan(stg, s, nb, lane);
+                stage_load(stg, a, wk, t2, n2, tid);
                 __syncthreads();
                 // phase 2
-                if (has_next) {
-                    if (!(W & 1)) map_gram_kk(s, nb, W, l16, g4);
-                    stage_commit_q(stq, s, tid);
-                    if (c + 2 < nchunks) stage_load_q(stq, a, wk, t2, min(CH, wk.eos - t2), tid);
-                }
+                if (has_next && !(W & 1)) map_gram_kk(s, nb, W, l16, g4);
+                stage_commit_q(stq, s, tid);
+                stage_load_q(stq, a, wk, t2, n2, tid);
                 __syncthreads();
                 // phase 3
                 if (has_next) {
@@ -650,23 +657,19 @@ __global__ __launch_bounds__(THREADS) void gdn_prefill_pipe_kernel(const Prefill
                 constexpr int buf = decltype(bufc)::value, nb = buf ^ 1;
                 const int tok0 = wk.bos + c * CH;
                 const int nval = min(CH, wk.eos - tok0);
-                const bool has_next = c + 1 < nchunks;
-                const int t2 = tok0 + 2 * CH;
+                const int t2 = prefetch_tok(wk, c + 2, nchunks);
+                const int n2 = min(CH, wk.eos - t2);
                 // phase 1
                 Frag<bf> fs[4];
                 chain_R(s, buf, W, l16, g4, fs);
                 const f32x4 qs = chain_QS(s, W, l16, g4, fs);
-                if (has_next) {
-                    stage_commit(stg, s, nb, tid);
-                    if (c + 2 < nchunks) stage_load(stg, a, wk, t2, min(CH, wk.eos - t2), tid);
-                }
+                stage_commit(stg, s, nb, tid);
+                stage_load(stg, a, wk, t2, n2, tid);
                 __syncthreads();
                 // phase 2
                 chain_v(s, buf, W, l16, g4);
-                if (has_next) {
-                    stage_commit_q(stq, s, tid);
-                    if (c + 2 < nchunks) stage_load_q(stq, a, wk, t2, min(CH, wk.eos - t2), tid);
-                }
+                stage_commit_q(stq, s, tid);
+                stage_load_q(stq, a, wk, t2, n2, tid);
                 __syncthreads();
                 // phase 3
                 chain_out_update(s, a, buf, W, l16, g4, qs, st, h, dv0, tok0, nval);
