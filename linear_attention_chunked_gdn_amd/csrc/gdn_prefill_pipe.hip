@@ -232,13 +232,15 @@ __device__ __forceinline__ void gate_scan(const Stage &st, Smem &s, int buf, int
 // columns and writes them with one vector store.  A goes to s.A (fp32), P to
 // s.Ph/Pl[nb] (split bf16).
 // ---------------------------------------------------------------------------------
+// Per-element factor of tile (bi, bj) for this lane's row and four columns: the decay,
+// times beta of the row for K K^T.  Computed before the tile's products so the gate
+// reads overlap the MFMAs.
 template <bool ISQ>
-__device__ __forceinline__ void gram_epilogue(Smem &s, int nb, int bi, int bj, const f32x4 &acc,
-                                              int l16, int g4) {
+__device__ __forceinline__ f32x4 gram_scale(const Smem &s, int nb, int bi, int bj, int l16, int g4) {
     const Gate &gt = s.gate[nb];
     const int rr = 16 * bi + l16;          // row of this lane
     const int c0 = 16 * bj + 4 * g4;       // first of its four columns
-    float d[4];
+    f32x4 d;
     if (bi == bj) {
         // same 16-token block: direct exponent differences, masked before use
         const float gr = gt.g2[rr];
@@ -256,8 +258,21 @@ __device__ __forceinline__ void gram_epilogue(Smem &s, int nb, int bi, int bj, c
     }
     if constexpr (!ISQ) {
         const float br = gt.beta[rr];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) d[r] *= br;
+    }
+    return d;
+}
+
+// A goes to s.A (fp32), P to s.Ph/Pl[nb] (split bf16).
+template <bool ISQ>
+__device__ __forceinline__ void gram_store(Smem &s, int nb, int bi, int bj, const f32x4 &acc, const f32x4 &d,
+                                          int l16, int g4) {
+    const int rr = 16 * bi + l16;
+    const int c0 = 16 * bj + 4 * g4;
+    if constexpr (!ISQ) {
         *reinterpret_cast<f32x4 *>(&s.A[rr * AS + c0]) =
-            f32x4{br * acc[0] * d[0], br * acc[1] * d[1], br * acc[2] * d[2], br * acc[3] * d[3]};
+            f32x4{acc[0] * d[0], acc[1] * d[1], acc[2] * d[2], acc[3] * d[3]};
     } else {
         store4_split(&s.Ph[nb][rr * TP + c0], &s.Pl[nb][rr * TP + c0], acc[0] * d[0], acc[1] * d[1],
                      acc[2] * d[2], acc[3] * d[3]);
@@ -267,11 +282,17 @@ __device__ __forceinline__ void gram_epilogue(Smem &s, int nb, int bi, int bj, c
 template <bool ISQ, int RB0, int RB1>
 __device__ __forceinline__ void gram_rows(Smem &s, int nb, int l16, int g4) {
     static_assert(RB0 < RB1 && RB0 + RB1 == 3, "row-block pairs are {0,3} and {1,2}");
-    f32x4 c0[RB0 + 1], c1[RB1 + 1];
+    f32x4 c0[RB0 + 1], c1[RB1 + 1], d0[RB0 + 1], d1[RB1 + 1];
 #pragma unroll
-    for (int j = 0; j <= RB0; ++j) c0[j] = zero4();
+    for (int j = 0; j <= RB0; ++j) {
+        c0[j] = zero4();
+        d0[j] = gram_scale<ISQ>(s, nb, RB0, j, l16, g4);
+    }
 #pragma unroll
-    for (int j = 0; j <= RB1; ++j) c1[j] = zero4();
+    for (int j = 0; j <= RB1; ++j) {
+        c1[j] = zero4();
+        d1[j] = gram_scale<ISQ>(s, nb, RB1, j, l16, g4);
+    }
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
         Frag<bf> x0, x1, kj[RB1 + 1];
@@ -291,9 +312,9 @@ __device__ __forceinline__ void gram_rows(Smem &s, int nb, int l16, int g4) {
         }
     }
 #pragma unroll
-    for (int j = 0; j <= RB0; ++j) gram_epilogue<ISQ>(s, nb, RB0, j, c0[j], l16, g4);
+    for (int j = 0; j <= RB0; ++j) gram_store<ISQ>(s, nb, RB0, j, c0[j], d0[j], l16, g4);
 #pragma unroll
-    for (int j = 0; j <= RB1; ++j) gram_epilogue<ISQ>(s, nb, RB1, j, c1[j], l16, g4);
+    for (int j = 0; j <= RB1; ++j) gram_store<ISQ>(s, nb, RB1, j, c1[j], d1[j], l16, g4);
 }
 
 // K K^T of the chunk in buffer nb: map waves 0 and 2 (row-block pairs {0,3}, {1,2}).
@@ -363,7 +384,18 @@ __device__ __forceinline__ void map_diag_solve(Smem &s, int l16, int g4) {
 // ---------------------------------------------------------------------------------
 template <int CB>
 __device__ __forceinline__ void map_merges(Smem &s, int l16, int g4) {
+    // every operand read from LDS up front, so the three dependent levels wait on one
+    // round of loads instead of one per level
+    f32x4 a[4][4];       // a[i][j]: A_ij, row 16i + l16, columns 16j + 4G..+3
+    bf16x4 tii[4];       // row 16i + l16 of T_ii, columns 16i + 4G..+3
     f32x4 tcol[4];
+#pragma unroll
+    for (int i = CB + 1; i < 4; ++i) {
+#pragma unroll
+        for (int j = CB; j < i; ++j)
+            a[i][j] = *reinterpret_cast<const f32x4 *>(&s.A[(16 * i + l16) * AS + 16 * j + 4 * g4]);
+        tii[i] = *reinterpret_cast<const bf16x4 *>(&s.T[(16 * i + l16) * TS + 16 * i + 4 * g4]);
+    }
 #pragma unroll
     for (int r = 0; r < 4; ++r) tcol[CB][r] = to_f(s.T[(16 * CB + 4 * g4 + r) * TS + 16 * CB + l16]);
 #pragma unroll
@@ -372,35 +404,23 @@ __device__ __forceinline__ void map_merges(Smem &s, int l16, int g4) {
 #pragma unroll
         for (int j = CB; j < i; j += 2) {
             Frag<bf> fa, fb;
-            const float *ar = &s.A[(16 * i + l16) * AS + 16 * j + 4 * g4];
-            const f32x4 a0 = *reinterpret_cast<const f32x4 *>(ar);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                fa.set(e, a0[e]);
+                fa.set(e, a[i][j][e]);
                 fb.set(e, tcol[j][e]);
-            }
-            if (j + 1 < i) {
-                const f32x4 a1 = *reinterpret_cast<const f32x4 *>(ar + 16);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    fa.set(4 + e, a1[e]);
-                    fb.set(4 + e, tcol[j + 1][e]);
-                }
-            } else {
-#pragma unroll
-                for (int e = 4; e < 8; ++e) {
-                    fa.set(e, 0.f);
-                    fb.set(e, 0.f);
-                }
+                fa.set(4 + e, j + 1 < i ? a[i][j + 1][e] : 0.f);
+                fb.set(4 + e, j + 1 < i ? tcol[j + 1][e] : 0.f);
             }
             mma(X, fa, fb);
         }
         Frag<bf> fa, fb;
         fa.zero();
         fb.zero();
-        fa.load4(0, &s.T[(16 * i + l16) * TS + 16 * i + 4 * g4]);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) fb.set(e, -X[e]);
+        for (int e = 0; e < 4; ++e) {
+            fa.set_raw(e, tii[i][e]);
+            fb.set(e, -X[e]);
+        }
         f32x4 Y = zero4();
         mma(Y, fa, fb);
         tcol[i] = Y;
@@ -416,6 +436,16 @@ __device__ __forceinline__ void map_merges(Smem &s, int l16, int g4) {
 __device__ __forceinline__ void chain_R(Smem &s, int buf, int W, int l16, int g4, Frag<bf> (&fs)[4]) {
     const bf *krow = s.K[buf] + (16 * W + l16) * KS + 8 * g4;
     const bf *srow = s.S + l16 * KS + 8 * g4;
+    // R = beta V - (beta gamma) (K S^T): the gate and V terms are read before the products
+    const int t0 = 16 * W + 4 * g4;
+    const f32x4 b = *reinterpret_cast<const f32x4 *>(&s.gate[buf].beta[t0]);
+    const f32x4 gm = *reinterpret_cast<const f32x4 *>(&s.gate[buf].gam[t0]);
+    f32x4 bv, bg;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        bv[i] = b[i] * to_f(s.V[buf][(t0 + i) * VS + l16]);
+        bg[i] = b[i] * gm[i];
+    }
     f32x4 ks = zero4();
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
@@ -424,12 +454,9 @@ __device__ __forceinline__ void chain_R(Smem &s, int buf, int W, int l16, int g4
         fk.load8(krow + 32 * kb);
         mma(ks, fk, fs[kb]);      // (K S^T): lane = value channel, rows = tokens
     }
-    const int t0 = 16 * W + 4 * g4;
-    const f32x4 b = *reinterpret_cast<const f32x4 *>(&s.gate[buf].beta[t0]);
-    const f32x4 gm = *reinterpret_cast<const f32x4 *>(&s.gate[buf].gam[t0]);
     float r[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) r[i] = b[i] * (to_f(s.V[buf][(t0 + i) * VS + l16]) - gm[i] * ks[i]);
+    for (int i = 0; i < 4; ++i) r[i] = bv[i] - bg[i] * ks[i];
     store4_split(&s.Rh[l16 * TS + t0], &s.Rl[l16 * TS + t0], r[0], r[1], r[2], r[3]);
 }
 
@@ -450,6 +477,8 @@ __device__ __forceinline__ f32x4 chain_QS(const Smem &s, int W, int l16, int g4,
 // Chain, phase 2: v = T R for tokens [16W, 16W+16); T is lower triangular, so only
 // the first W/2 + 1 blocks of 32 columns contribute.
 __device__ __forceinline__ void chain_v(Smem &s, int buf, int W, int l16, int g4) {
+    const int t0 = 16 * W + 4 * g4;
+    const f32x4 lm = *reinterpret_cast<const f32x4 *>(&s.gate[buf].lam[t0]);
     f32x4 acc = zero4();
     const bf *trow = s.T + (16 * W + l16) * TS + 8 * g4;
     for (int kb = 0; kb <= (W >> 1); ++kb) {
@@ -460,8 +489,6 @@ __device__ __forceinline__ void chain_v(Smem &s, int buf, int W, int l16, int g4
         mma(acc, fa, fh);
         mma(acc, fa, fl);
     }
-    const int t0 = 16 * W + 4 * g4;
-    const f32x4 lm = *reinterpret_cast<const f32x4 *>(&s.gate[buf].lam[t0]);
     store4_split(&s.Vh[l16 * TS + t0], &s.Vl[l16 * TS + t0], acc[0], acc[1], acc[2], acc[3]);
     store4_split(&s.Wh[l16 * TS + t0], &s.Wl[l16 * TS + t0], lm[0] * acc[0], lm[1] * acc[1],
                  lm[2] * acc[2], lm[3] * acc[3]);
@@ -472,10 +499,13 @@ __device__ __forceinline__ void chain_v(Smem &s, int buf, int W, int l16, int g4
 __device__ __forceinline__ void chain_out_update(Smem &s, const PrefillArgs &a, int buf, int W, int l16,
                                                  int g4, const f32x4 &qs, f32x4 (&st)[2], int h,
                                                  int dv0, int tok0, int nval) {
+    const int t = 16 * W + l16;
+    const float gm = s.gate[buf].gam[t];
+    const float glast = s.gate[buf].gam[CH - 1];
     {
         // O^T = S Q^T diag(gamma) + v^T P^T: lane = token 16W + l16, rows = value
         // channels 4G..4G+3, so each lane stores four consecutive outputs at once
-        f32x4 acc = zero4();
+        f32x4 acc = qs * gm;
         const bf *ph = s.Ph[buf] + (16 * W + l16) * TP + 8 * g4;
         const bf *pl = s.Pl[buf] + (16 * W + l16) * TP + 8 * g4;
         for (int kb = 0; kb <= (W >> 1); ++kb) {
@@ -488,18 +518,15 @@ __device__ __forceinline__ void chain_out_update(Smem &s, const PrefillArgs &a, 
             mma(acc, fvl, fph);
             mma(acc, fvh, fpl);
         }
-        const int t = 16 * W + l16;
         if (t < nval) {
-            const float gm = s.gate[buf].gam[t];
             bf16x4 y;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) y[r] = f32_to_bf16(gm * qs[r] + acc[r]);
+            for (int r = 0; r < 4; ++r) y[r] = f32_to_bf16(acc[r]);
             *reinterpret_cast<bf16x4 *>(reinterpret_cast<uint16_t *>(a.o) +
                                         ((size_t)(tok0 + t) * a.Hv + h) * DV + dv0 + 4 * g4) = y;
         }
     }
     {
-        const float glast = s.gate[buf].gam[CH - 1];
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
             // K^T fragments (slot e of group G = token 32kb + 8G + e, row = key channel
