@@ -19,10 +19,10 @@
 //   phase 1:  chain R(c), Q S^T(c)       | map: T(c) blocks below the diagonal,
 //                                        |      gate scan of chunk c+1 (one wave)
 //             all waves: k, v of chunk c+1 into LDS; fetch k, v, g, beta of c+2
-//   phase 2:  chain v(c) = T(c) R(c)     | map: K K^T(c+1) -> A
+//   phase 2:  chain v(c) = T(c) R(c)     | map: K K^T(c+1) -> A (four waves)
 //             all waves: q of chunk c+1 into LDS (q of c is dead); fetch q of c+2
-//   phase 3:  chain O(c), S update       | map: Q K^T(c+1) -> P(c+1), diagonal
-//                                        |      blocks of T(c+1) (one wave)
+//   phase 3:  chain O(c), S update       | map: Q K^T(c+1) -> P(c+1) (three waves),
+//                                        |      diagonal blocks of T(c+1) (one wave)
 //
 // LDS holds two buffers of the k and v tiles, the gates and P; q, T and A are
 // single-buffered because their lifetimes do not overlap across the phases.
@@ -225,12 +225,10 @@ __device__ __forceinline__ void gate_scan(const Stage &st, Smem &s, int buf, int
 }
 
 // ---------------------------------------------------------------------------------
-// Map: grams of the chunk in buffer nb.  Map wave m computes, for one gram (K K^T for
-// m even, in phase 2; Q K^T for m odd, in phase 3), the lower tiles of the row-block
-// pair {0, 3} (m < 2) or {1, 2} (m >= 2): five 16x16 tiles per wave.  Tiles are computed transposed
-// (K_j X_i^T with X = K or Q), so each lane ends with one row and four consecutive
-// columns and writes them with one vector store.  A goes to s.A (fp32), P to
-// s.Ph/Pl[nb] (split bf16).
+// Map: grams of the chunk in buffer nb.  The ten lower 16x16 tiles of K K^T (phase 2)
+// are spread over the four map waves, those of Q K^T (phase 3) over waves 1-3.  Tiles
+// are computed transposed (K_j X_i^T with X = K or Q), so each lane ends with one row
+// and four consecutive columns and writes them with one vector store.
 // ---------------------------------------------------------------------------------
 // Per-element factor of tile (bi, bj) for this lane's row and four columns: the decay,
 // times beta of the row for K K^T.  Computed before the tile's products so the gate
@@ -279,54 +277,52 @@ __device__ __forceinline__ void gram_store(Smem &s, int nb, int bi, int bj, cons
     }
 }
 
-template <bool ISQ, int RB0, int RB1>
-__device__ __forceinline__ void gram_rows(Smem &s, int nb, int l16, int g4) {
-    static_assert(RB0 < RB1 && RB0 + RB1 == 3, "row-block pairs are {0,3} and {1,2}");
-    f32x4 c0[RB0 + 1], c1[RB1 + 1], d0[RB0 + 1], d1[RB1 + 1];
+// Up to four tiles of one gram, each given as 4 * (row block) + (column block), -1 for
+// none.  Operand fragments shared by several tiles are read once per step.
+template <bool ISQ, int T0, int T1, int T2, int T3>
+__device__ __forceinline__ void gram_tiles(Smem &s, int nb, int l16, int g4) {
+    constexpr int tl[4] = {T0, T1, T2, T3};
+    constexpr int NT = (T0 >= 0) + (T1 >= 0) + (T2 >= 0) + (T3 >= 0);
+    f32x4 c[NT], d[NT];
 #pragma unroll
-    for (int j = 0; j <= RB0; ++j) {
-        c0[j] = zero4();
-        d0[j] = gram_scale<ISQ>(s, nb, RB0, j, l16, g4);
+    for (int t = 0; t < NT; ++t) {
+        c[t] = zero4();
+        d[t] = gram_scale<ISQ>(s, nb, tl[t] >> 2, tl[t] & 3, l16, g4);
     }
-#pragma unroll
-    for (int j = 0; j <= RB1; ++j) {
-        c1[j] = zero4();
-        d1[j] = gram_scale<ISQ>(s, nb, RB1, j, l16, g4);
-    }
+    const bf *xs = ISQ ? s.Q : s.K[nb];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-        Frag<bf> x0, x1, kj[RB1 + 1];
 #pragma unroll
-        for (int j = 0; j <= RB1; ++j) kj[j].load8(s.K[nb] + (16 * j + l16) * KS + 32 * kb + 8 * g4);
-        if constexpr (ISQ) {
-            x0.load8(s.Q + (16 * RB0 + l16) * KS + 32 * kb + 8 * g4);
-            x1.load8(s.Q + (16 * RB1 + l16) * KS + 32 * kb + 8 * g4);
-        } else {
-            x0 = kj[RB0];
-            x1 = kj[RB1];
-        }
-#pragma unroll
-        for (int j = 0; j <= RB1; ++j) {
-            mma(c1[j], kj[j], x1);
-            if (j <= RB0) mma(c0[j], kj[j], x0);
+        for (int t = 0; t < NT; ++t) {
+            // tile (bi, bj) is computed transposed, K_bj X_bi^T
+            Frag<bf> kj, x;
+            kj.load8(s.K[nb] + (16 * (tl[t] & 3) + l16) * KS + 32 * kb + 8 * g4);
+            x.load8(xs + (16 * (tl[t] >> 2) + l16) * KS + 32 * kb + 8 * g4);
+            mma(c[t], kj, x);
         }
     }
 #pragma unroll
-    for (int j = 0; j <= RB0; ++j) gram_store<ISQ>(s, nb, RB0, j, c0[j], d0[j], l16, g4);
-#pragma unroll
-    for (int j = 0; j <= RB1; ++j) gram_store<ISQ>(s, nb, RB1, j, c1[j], d1[j], l16, g4);
+    for (int t = 0; t < NT; ++t) gram_store<ISQ>(s, nb, tl[t] >> 2, tl[t] & 3, c[t], d[t], l16, g4);
 }
 
-// K K^T of the chunk in buffer nb: map waves 0 and 2 (row-block pairs {0,3}, {1,2}).
+// K K^T of the chunk in buffer nb, ten tiles over the four map waves.
 __device__ __forceinline__ void map_gram_kk(Smem &s, int nb, int m, int l16, int g4) {
-    if (m == 0) gram_rows<false, 0, 3>(s, nb, l16, g4);
-    else gram_rows<false, 1, 2>(s, nb, l16, g4);
+    switch (m) {
+        case 0: gram_tiles<false, 12, 13, -1, -1>(s, nb, l16, g4); break;   // (3,0) (3,1)
+        case 1: gram_tiles<false, 14, 15, 0, -1>(s, nb, l16, g4); break;    // (3,2) (3,3) (0,0)
+        case 2: gram_tiles<false, 8, 9, 10, -1>(s, nb, l16, g4); break;     // (2,0) (2,1) (2,2)
+        default: gram_tiles<false, 4, 5, -1, -1>(s, nb, l16, g4); break;    // (1,0) (1,1)
+    }
 }
 
-// Q K^T of the chunk in buffer nb (q in the single q buffer): map waves 1 and 3.
+// Q K^T of the chunk in buffer nb (q in the single q buffer), ten tiles over map
+// waves 1-3 (wave 0 solves the diagonal blocks of T meanwhile).
 __device__ __forceinline__ void map_gram_qk(Smem &s, int nb, int m, int l16, int g4) {
-    if (m == 1) gram_rows<true, 0, 3>(s, nb, l16, g4);
-    else gram_rows<true, 1, 2>(s, nb, l16, g4);
+    switch (m) {
+        case 1: gram_tiles<true, 12, 13, 14, 15>(s, nb, l16, g4); break;    // row block 3
+        case 2: gram_tiles<true, 8, 9, 10, -1>(s, nb, l16, g4); break;      // row block 2
+        default: gram_tiles<true, 0, 4, 5, -1>(s, nb, l16, g4); break;      // row blocks 0, 1
+    }
 }
 
 // ---------------------------------------------------------------------------------
@@ -640,10 +636,10 @@ __global__ __launch_bounds__(THREADS) void gdn_prefill_pipe_kernel(const Prefill
         using B0 = std::integral_constant<int, 0>;
         using B1 = std::integral_constant<int, 1>;
         if (is_map) {
-            if (!(W & 1)) map_gram_kk(s, 0, W, l16, g4);
+            map_gram_kk(s, 0, W, l16, g4);
             __syncthreads();
-            if (W & 1) map_gram_qk(s, 0, W, l16, g4);
-            if (wave == 0) map_diag_solve(s, l16, g4);
+            if (W != 0) map_gram_qk(s, 0, W, l16, g4);
+            else map_diag_solve(s, l16, g4);
             __syncthreads();
             auto step = [&](auto bufc, int c) {
                 constexpr int nb = decltype(bufc)::value ^ 1;
@@ -662,14 +658,14 @@ __global__ __launch_bounds__(THREADS) void gdn_prefill_pipe_kernel(const Prefill
                 stage_load(stg, a, wk, t2, n2, tid);
                 __syncthreads();
                 // phase 2
-                if (has_next && !(W & 1)) map_gram_kk(s, nb, W, l16, g4);
+                if (has_next) map_gram_kk(s, nb, W, l16, g4);
                 stage_commit_q(stq, s, tid);
                 stage_load_q(stq, a, wk, t2, n2, tid);
                 __syncthreads();
                 // phase 3
                 if (has_next) {
-                    if (W & 1) map_gram_qk(s, nb, W, l16, g4);
-                    if (wave == 0) map_diag_solve(s, l16, g4);
+                    if (W != 0) map_gram_qk(s, nb, W, l16, g4);
+                    else map_diag_solve(s, l16, g4);
                 }
                 __syncthreads();
             };
