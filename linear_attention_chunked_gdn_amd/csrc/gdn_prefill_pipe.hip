@@ -68,17 +68,19 @@ struct Gate {
 };
 
 struct __align__(16) Smem {
-    bf K[2][CH * KS];
-    bf Q[CH * KS];
-    bf V[2][CH * VS];
-    Gate gate[2];
+    // The small tiles come first: a DS instruction's immediate offset reaches 64 KiB,
+    // so these are addressed from one base register plus constants.
     float A[CH * AS];              // A of the chunk being mapped, strictly lower
     bf T[CH * TS];                 // T = (I + A)^-1
-    bf Ph[2][CH * TP], Pl[2][CH * TP];   // P split into bf16 hi + lo
     bf S[DVS * KS];                // bf16 copy of the state slice [value ch][key ch]
     bf Rh[DVS * TS], Rl[DVS * TS];  // R^T
     bf Vh[DVS * TS], Vl[DVS * TS];  // v^T
     bf Wh[DVS * TS], Wl[DVS * TS];  // (diag(lambda) v)^T
+    Gate gate[2];
+    bf V[2][CH * VS];
+    bf K[2][CH * KS];
+    bf Q[CH * KS];
+    bf Ph[2][CH * TP], Pl[2][CH * TP];   // P split into bf16 hi + lo
 };
 
 __device__ __forceinline__ float to_f(bf x) { return bf16_to_f32(x); }
