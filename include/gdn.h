@@ -109,12 +109,12 @@ gdn_status gdn_decode_step(const void *q, const void *k, const void *v,
  * gdn_prefill_plan -- the launch shape gdn_prefill would use for these sizes,
  * without launching anything: the width of the value-channel slice each workgroup
  * owns (the column-wise split of S, "Empowering Hybrid Attention Models on NPUs",
- * section 4, Figure 8(b)), the number of workgroups and the LDS bytes per
- * workgroup.  Any output pointer may be NULL.  Host pointers.
+ * section 4, Figure 8(b)), the number of workgroups, the LDS bytes and the threads
+ * per workgroup.  Any output pointer may be NULL.  Host pointers.
  */
 gdn_status gdn_prefill_plan(int32_t N, int32_t Hv, int32_t Dv, gdn_dtype io_dtype,
                             int32_t *dv_per_workgroup, int32_t *workgroups,
-                            int32_t *lds_bytes);
+                            int32_t *lds_bytes, int32_t *threads_per_workgroup);
 
 /* Static English name of a status code. */
 const char *gdn_status_string(gdn_status s);

@@ -59,19 +59,21 @@ struct Plan {
     bool pipe;
     int dvs;
     int lds;
+    int threads;
 };
 
 Plan choose_plan(gdn_dtype dt) {
     const char *kern = std::getenv("GDN_KERNEL");
     const bool force_v1 = kern && std::strcmp(kern, "v1") == 0;
-    if (dt == GDN_BF16 && !force_v1) return Plan{true, 16, gdn::prefill_pipe_lds_bytes()};
+    if (dt == GDN_BF16 && !force_v1)
+        return Plan{true, 16, gdn::prefill_pipe_lds_bytes(), gdn::prefill_pipe_threads()};
     int dvs = 16;
     const char *env = std::getenv("GDN_DVS");
     if (env) {
         const int d = std::atoi(env);
         if (gdn::prefill_lds_bytes(dt == GDN_BF16, d) > 0) dvs = d;
     }
-    return Plan{false, dvs, gdn::prefill_lds_bytes(dt == GDN_BF16, dvs)};
+    return Plan{false, dvs, gdn::prefill_lds_bytes(dt == GDN_BF16, dvs), gdn::prefill_threads()};
 }
 
 }  // namespace
@@ -91,7 +93,8 @@ const char *gdn_status_string(gdn_status s) {
 const char *gdn_last_error(void) { return g_last_error.c_str(); }
 
 gdn_status gdn_prefill_plan(int32_t N, int32_t Hv, int32_t Dv, gdn_dtype io_dtype,
-                            int32_t *dv_per_workgroup, int32_t *workgroups, int32_t *lds_bytes) {
+                            int32_t *dv_per_workgroup, int32_t *workgroups, int32_t *lds_bytes,
+                            int32_t *threads_per_workgroup) {
     if (io_dtype != GDN_F32 && io_dtype != GDN_BF16)
         return fail(GDN_ERR_INVALID_ARGUMENT, "io_dtype %d is not GDN_F32 or GDN_BF16", (int)io_dtype);
     if (N < 1 || Hv < 1) return fail(GDN_ERR_INVALID_ARGUMENT, "N=%d and Hv=%d must be >= 1", N, Hv);
@@ -102,6 +105,7 @@ gdn_status gdn_prefill_plan(int32_t N, int32_t Hv, int32_t Dv, gdn_dtype io_dtyp
     if (dv_per_workgroup) *dv_per_workgroup = p.dvs;
     if (workgroups) *workgroups = (int32_t)wg;
     if (lds_bytes) *lds_bytes = p.lds;
+    if (threads_per_workgroup) *threads_per_workgroup = p.threads;
     return ok();
 }
 
@@ -151,7 +155,7 @@ gdn_status gdn_prefill(const void *q, const void *k, const void *v, const float 
     if (overlap(ro, rf)) return fail(GDN_ERR_INVALID_ARGUMENT, "o overlaps final_state");
 
     int32_t dvs = 0, wg = 0;
-    gdn_status ps = gdn_prefill_plan(N, Hv, Dv, io_dtype, &dvs, &wg, nullptr);
+    gdn_status ps = gdn_prefill_plan(N, Hv, Dv, io_dtype, &dvs, &wg, nullptr, nullptr);
     if (ps != GDN_OK) return ps;
     if (T_tot == 0 && !final_state) return ok();   // nothing to compute or write
 

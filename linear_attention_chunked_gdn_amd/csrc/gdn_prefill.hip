@@ -578,6 +578,8 @@ hipError_t launch_prefill(const PrefillArgs &a, bool bf16, int dvs, int grid, hi
     return hipErrorInvalidValue;
 }
 
+int prefill_threads() { return THREADS; }
+
 int prefill_lds_bytes(bool bf16, int dvs) {
     if (bf16) {
         switch (dvs) {

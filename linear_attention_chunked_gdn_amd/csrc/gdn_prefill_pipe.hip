@@ -725,4 +725,6 @@ hipError_t launch_prefill_pipe(const PrefillArgs &a, int grid, hipStream_t strea
 
 int prefill_pipe_lds_bytes() { return (int)sizeof(pipe::Smem); }
 
+int prefill_pipe_threads() { return pipe::THREADS; }
+
 }  // namespace gdn

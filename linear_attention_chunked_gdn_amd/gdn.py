@@ -47,7 +47,7 @@ def load_library(path: str = LIB_PATH):
                                     vp, vp]
     lib.gdn_decode_step.restype = ctypes.c_int
     p32 = ctypes.POINTER(ctypes.c_int32)
-    lib.gdn_prefill_plan.argtypes = [i32, i32, i32, ctypes.c_int, p32, p32, p32]
+    lib.gdn_prefill_plan.argtypes = [i32, i32, i32, ctypes.c_int, p32, p32, p32, p32]
     lib.gdn_prefill_plan.restype = ctypes.c_int
     lib.gdn_status_string.argtypes = [ctypes.c_int]
     lib.gdn_status_string.restype = ctypes.c_char_p
@@ -164,7 +164,9 @@ def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tens
 def prefill_plan(N: int, Hv: int, io_dtype: int = GDN_BF16, lib=None) -> dict:
     """Launch shape of gdn_prefill for these sizes (host only, launches nothing)."""
     lib = lib or load_library()
-    dvs, wg, lds = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
-    st = lib.gdn_prefill_plan(N, Hv, D, io_dtype, ctypes.byref(dvs), ctypes.byref(wg), ctypes.byref(lds))
+    dvs, wg, lds, thr = (ctypes.c_int32() for _ in range(4))
+    st = lib.gdn_prefill_plan(N, Hv, D, io_dtype, ctypes.byref(dvs), ctypes.byref(wg), ctypes.byref(lds),
+                              ctypes.byref(thr))
     _check(lib, st, "gdn_prefill_plan")
-    return dict(dv_per_workgroup=dvs.value, workgroups=wg.value, lds_bytes=lds.value)
+    return dict(dv_per_workgroup=dvs.value, workgroups=wg.value, lds_bytes=lds.value,
+                threads_per_workgroup=thr.value)

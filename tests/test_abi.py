@@ -106,5 +106,7 @@ def test_plan(lib):
     plan = gdn.prefill_plan(1, 16, gdn.GDN_BF16, lib=lib)
     assert plan["workgroups"] * plan["dv_per_workgroup"] == 16 * 128
     assert 0 < plan["lds_bytes"] <= 160 * 1024
+    assert plan["threads_per_workgroup"] in (256, 512)
     plan32 = gdn.prefill_plan(1, 1, gdn.GDN_F32, lib=lib)
     assert 0 < plan32["lds_bytes"] <= 160 * 1024
+    assert plan32["threads_per_workgroup"] % 64 == 0
