@@ -95,6 +95,27 @@ __device__ __forceinline__ void store4_split(bf *hi, bf *lo, float a0, float a1,
     *reinterpret_cast<bf16x4 *>(lo) = l;
 }
 
+// Column-per-lane results into a row-major bf16 tile with 4-byte writes.  Lane pairs
+// (2k, 2k+1) hold columns 2k and 2k+1 of the same rows; for each pair of rows the pair
+// swaps one value (DPP quad_perm [1,0,3,2]) so the even lane writes row r and the odd
+// lane row r+1, each as two adjacent bf16.  Two lanes writing the halves of one LDS
+// dword with 2-byte stores is several times slower.  `col0` points at (row 0, the
+// lane's column); rows are `stride` elements apart; NR is even.
+template <int NR>
+__device__ __forceinline__ void store_cols_paired(bf *col0, int stride, const float (&x)[NR], int l16) {
+    const bool odd = l16 & 1;
+    bf *p = col0 + (odd ? stride - 1 : 0);
+#pragma unroll
+    for (int r = 0; r < NR; r += 2) {
+        const float send = odd ? x[r] : x[r + 1];
+        const float recv = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(send), 0xB1, 0xF, 0xF, true));
+        bf16x2 w;
+        w[0] = f32_to_bf16(odd ? recv : x[r]);
+        w[1] = f32_to_bf16(odd ? x[r + 1] : recv);
+        *reinterpret_cast<bf16x2 *>(p + r * stride) = w;
+    }
+}
+
 // Inclusive prefix sum over the 64 lanes of a wave: DPP shifts inside each row of 16
 // lanes, then the totals of the earlier rows are added.
 __device__ __forceinline__ float wave_inclusive_scan(float x, int lane) {
@@ -372,8 +393,7 @@ __device__ __forceinline__ void map_diag_solve(Smem &s, int l16, int g4) {
 #pragma unroll
             for (int r = j + 1; r < 8; ++r) x[r0 + r] -= a[r][j] * x[r0 + j];
     }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) s.T[(16 * B + r) * TS + 16 * B + l16] = f32_to_bf16(x[r]);
+    store_cols_paired<16>(&s.T[(16 * B) * TS + 16 * B + l16], TS, x, l16);
 }
 
 // ---------------------------------------------------------------------------------
@@ -422,8 +442,8 @@ __device__ __forceinline__ void map_merges(Smem &s, int l16, int g4) {
         f32x4 Y = zero4();
         mma(Y, fa, fb);
         tcol[i] = Y;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) s.T[(16 * i + 4 * g4 + r) * TS + 16 * CB + l16] = f32_to_bf16(Y[r]);
+        const float y[4] = {Y[0], Y[1], Y[2], Y[3]};
+        store_cols_paired<4>(&s.T[(16 * i + 4 * g4) * TS + 16 * CB + l16], TS, y, l16);
     }
 }
 
