@@ -10,6 +10,7 @@
 // because the MFMA pairs A slot (G, e) with B slot (G, e) and sums over all 32.
 //
 //   bf16 path: one v_mfma_f32_16x16x32_bf16 per step (8 bf16 slots per lane).
+//   fp16 path: one v_mfma_f32_16x16x32_f16 per step (8 fp16 slots per lane).
 //   fp32 path: eight v_mfma_f32_16x16x4_f32 per step, MFMA e taking slot e.
 //
 // The accumulator layout is the common 16x16 one: lane l holds rows 4*(l/16)+r,
@@ -27,6 +28,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float bf16_to_f32(__bf16 x) {
     return __uint_as_float(static_cast<uint32_t>(__builtin_bit_cast(uint16_t, x)) << 16);
@@ -68,6 +72,22 @@ template <> struct Frag<__bf16> {
     }
 };
 
+template <> struct Frag<_Float16> {
+    f16x8 v;
+    __device__ __forceinline__ void zero() {
+        for (int e = 0; e < 8; ++e) v[e] = (_Float16)0.f;
+    }
+    __device__ __forceinline__ void set(int e, float x) { v[e] = (_Float16)x; }
+    __device__ __forceinline__ void set_raw(int e, _Float16 x) { v[e] = x; }
+    __device__ __forceinline__ void load8(const _Float16 *p) {
+        v = *reinterpret_cast<const f16x8 *>(p);
+    }
+    __device__ __forceinline__ void load4(int h, const _Float16 *p) {
+        f16x4 t = *reinterpret_cast<const f16x4 *>(p);
+        for (int e = 0; e < 4; ++e) v[4 * h + e] = t[e];
+    }
+};
+
 template <> struct Frag<float> {
     float v[8];
     __device__ __forceinline__ void zero() {
@@ -88,6 +108,9 @@ template <> struct Frag<float> {
 
 __device__ __forceinline__ void mma(f32x4 &acc, const Frag<__bf16> &a, const Frag<__bf16> &b) {
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma(f32x4 &acc, const Frag<_Float16> &a, const Frag<_Float16> &b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a.v, b.v, acc, 0, 0, 0);
 }
 __device__ __forceinline__ void mma(f32x4 &acc, const Frag<float> &a, const Frag<float> &b) {
     for (int e = 0; e < 8; ++e)

@@ -1,10 +1,18 @@
 // Wave-specialised, software-pipelined chunked gated delta-rule prefill for gfx950,
 // bf16 I/O.
 //
-// Same arithmetic as gdn_prefill.hip (see there for the chunkwise formulas, the
-// column-wise split of the state and the bf16 precision scheme), scheduled so the
-// two halves of the Map-Reduce-Map pipeline ("Empowering Hybrid Attention Models
-// on NPUs", section 2.1, Figure 1(b)) run side by side:
+// The chunkwise formulas and the column-wise split of the state are those of
+// gdn_prefill.hip (see there), scheduled so the two halves of the Map-Reduce-Map
+// pipeline ("Empowering Hybrid Attention Models on NPUs", section 2.1, Figure 1(b))
+// run side by side.  Operand precision of the products (fp32 accumulation always):
+//   * q, k, v and the state copy used by K S^T and Q S^T: bf16 (q, k, v exactly);
+//   * T, R, v and P, which the kernel computes: fp16 (11-bit significand), one MFMA
+//     per product; a single bf16 rounding of R, v or P would cost 1.4-3.6 % of the
+//     output RMS, fp16 costs a quarter of that.  They stay far inside fp16's range
+//     for L2-normalised q and k (|P| <= 1) and values of ordinary size;
+//   * lambda v, multiplied with the bf16 K^T in the update: split into bf16 hi + lo.
+//
+// Roles:
 //
 //   * four "map" waves do the S-independent work of chunk c+1 -- the gate scan (#1),
 //     the K K^T and Q K^T grams (#2) and the (I + A)^-1 solve (#3);
@@ -52,6 +60,7 @@ constexpr int AS = CH + 8;    // fp32 row stride of A (288 B)
 constexpr float LOG2E = 1.4426950408889634f;
 
 typedef __bf16 bf;
+typedef _Float16 hf;
 
 // Per-chunk gate quantities, computed once by one map wave from the staged g.
 // Decays inside a chunk are exp(Gamma_r - Gamma_s), r >= s.  For r and s in different
@@ -71,16 +80,16 @@ struct __align__(16) Smem {
     // The small tiles come first: a DS instruction's immediate offset reaches 64 KiB,
     // so these are addressed from one base register plus constants.
     float A[CH * AS];              // A of the chunk being mapped, strictly lower
-    bf T[CH * TS];                 // T = (I + A)^-1
+    hf T[CH * TS];                 // T = (I + A)^-1
     bf S[DVS * KS];                // bf16 copy of the state slice [value ch][key ch]
-    bf Rh[DVS * TS], Rl[DVS * TS];  // R^T
-    bf Vh[DVS * TS], Vl[DVS * TS];  // v^T
+    hf Rh[DVS * TS];               // R^T
+    hf Vh[DVS * TS];               // v^T
     bf Wh[DVS * TS], Wl[DVS * TS];  // (diag(lambda) v)^T
     Gate gate[2];
     bf V[2][CH * VS];
     bf K[2][CH * KS];
     bf Q[CH * KS];
-    bf Ph[2][CH * TP], Pl[2][CH * TP];   // P split into bf16 hi + lo
+    hf Ph[2][CH * TP];             // P
 };
 
 __device__ __forceinline__ float to_f(bf x) { return bf16_to_f32(x); }
@@ -95,24 +104,29 @@ __device__ __forceinline__ void store4_split(bf *hi, bf *lo, float a0, float a1,
     *reinterpret_cast<bf16x4 *>(lo) = l;
 }
 
-// Column-per-lane results into a row-major bf16 tile with 4-byte writes.  Lane pairs
+// Four consecutive values as fp16.
+__device__ __forceinline__ void store4_h(hf *p, float a0, float a1, float a2, float a3) {
+    *reinterpret_cast<f16x4 *>(p) = f16x4{(hf)a0, (hf)a1, (hf)a2, (hf)a3};
+}
+
+// Column-per-lane results into a row-major fp16 tile with 4-byte writes.  Lane pairs
 // (2k, 2k+1) hold columns 2k and 2k+1 of the same rows; for each pair of rows the pair
 // swaps one value (DPP quad_perm [1,0,3,2]) so the even lane writes row r and the odd
 // lane row r+1, each as two adjacent bf16.  Two lanes writing the halves of one LDS
 // dword with 2-byte stores is several times slower.  `col0` points at (row 0, the
 // lane's column); rows are `stride` elements apart; NR is even.
 template <int NR>
-__device__ __forceinline__ void store_cols_paired(bf *col0, int stride, const float (&x)[NR], int l16) {
+__device__ __forceinline__ void store_cols_paired(hf *col0, int stride, const float (&x)[NR], int l16) {
     const bool odd = l16 & 1;
-    bf *p = col0 + (odd ? stride - 1 : 0);
+    hf *p = col0 + (odd ? stride - 1 : 0);
 #pragma unroll
     for (int r = 0; r < NR; r += 2) {
         const float send = odd ? x[r] : x[r + 1];
         const float recv = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(send), 0xB1, 0xF, 0xF, true));
-        bf16x2 w;
-        w[0] = f32_to_bf16(odd ? recv : x[r]);
-        w[1] = f32_to_bf16(odd ? x[r + 1] : recv);
-        *reinterpret_cast<bf16x2 *>(p + r * stride) = w;
+        f16x2 w;
+        w[0] = (hf)(odd ? recv : x[r]);
+        w[1] = (hf)(odd ? x[r + 1] : recv);
+        *reinterpret_cast<f16x2 *>(p + r * stride) = w;
     }
 }
 
@@ -285,7 +299,7 @@ __device__ __forceinline__ f32x4 gram_scale(const Smem &s, int nb, int bi, int b
     return d;
 }
 
-// A goes to s.A (fp32), P to s.Ph/Pl[nb] (split bf16).
+// A goes to s.A (fp32), P to s.Ph[nb] (fp16).
 template <bool ISQ>
 __device__ __forceinline__ void gram_store(Smem &s, int nb, int bi, int bj, const f32x4 &acc, const f32x4 &d,
                                           int l16, int g4) {
@@ -295,8 +309,7 @@ __device__ __forceinline__ void gram_store(Smem &s, int nb, int bi, int bj, cons
         *reinterpret_cast<f32x4 *>(&s.A[rr * AS + c0]) =
             f32x4{acc[0] * d[0], acc[1] * d[1], acc[2] * d[2], acc[3] * d[3]};
     } else {
-        store4_split(&s.Ph[nb][rr * TP + c0], &s.Pl[nb][rr * TP + c0], acc[0] * d[0], acc[1] * d[1],
-                     acc[2] * d[2], acc[3] * d[3]);
+        store4_h(&s.Ph[nb][rr * TP + c0], acc[0] * d[0], acc[1] * d[1], acc[2] * d[2], acc[3] * d[3]);
     }
 }
 
@@ -405,23 +418,23 @@ __device__ __forceinline__ void map_merges(Smem &s, int l16, int g4) {
     // every operand read from LDS up front, so the three dependent levels wait on one
     // round of loads instead of one per level
     f32x4 a[4][4];       // a[i][j]: A_ij, row 16i + l16, columns 16j + 4G..+3
-    bf16x4 tii[4];       // row 16i + l16 of T_ii, columns 16i + 4G..+3
+    f16x4 tii[4];        // row 16i + l16 of T_ii, columns 16i + 4G..+3
     f32x4 tcol[4];
 #pragma unroll
     for (int i = CB + 1; i < 4; ++i) {
 #pragma unroll
         for (int j = CB; j < i; ++j)
             a[i][j] = *reinterpret_cast<const f32x4 *>(&s.A[(16 * i + l16) * AS + 16 * j + 4 * g4]);
-        tii[i] = *reinterpret_cast<const bf16x4 *>(&s.T[(16 * i + l16) * TS + 16 * i + 4 * g4]);
+        tii[i] = *reinterpret_cast<const f16x4 *>(&s.T[(16 * i + l16) * TS + 16 * i + 4 * g4]);
     }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) tcol[CB][r] = to_f(s.T[(16 * CB + 4 * g4 + r) * TS + 16 * CB + l16]);
+    for (int r = 0; r < 4; ++r) tcol[CB][r] = (float)s.T[(16 * CB + 4 * g4 + r) * TS + 16 * CB + l16];
 #pragma unroll
     for (int i = CB + 1; i < 4; ++i) {
         f32x4 X = zero4();
 #pragma unroll
         for (int j = CB; j < i; j += 2) {
-            Frag<bf> fa, fb;
+            Frag<hf> fa, fb;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 fa.set(e, a[i][j][e]);
@@ -431,7 +444,7 @@ __device__ __forceinline__ void map_merges(Smem &s, int l16, int g4) {
             }
             mma(X, fa, fb);
         }
-        Frag<bf> fa, fb;
+        Frag<hf> fa, fb;
         fa.zero();
         fb.zero();
 #pragma unroll
@@ -475,7 +488,7 @@ __device__ __forceinline__ void chain_R(Smem &s, int buf, int W, int l16, int g4
     float r[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) r[i] = bv[i] - bg[i] * ks[i];
-    store4_split(&s.Rh[l16 * TS + t0], &s.Rl[l16 * TS + t0], r[0], r[1], r[2], r[3]);
+    store4_h(&s.Rh[l16 * TS + t0], r[0], r[1], r[2], r[3]);
 }
 
 // Chain, phase 1: (Q S^T)^T = S Q^T for tokens [16W, 16W+16) (lane = token, rows =
@@ -498,16 +511,14 @@ __device__ __forceinline__ void chain_v(Smem &s, int buf, int W, int l16, int g4
     const int t0 = 16 * W + 4 * g4;
     const f32x4 lm = *reinterpret_cast<const f32x4 *>(&s.gate[buf].lam[t0]);
     f32x4 acc = zero4();
-    const bf *trow = s.T + (16 * W + l16) * TS + 8 * g4;
+    const hf *trow = s.T + (16 * W + l16) * TS + 8 * g4;
     for (int kb = 0; kb <= (W >> 1); ++kb) {
-        Frag<bf> fa, fh, fl;
+        Frag<hf> fa, fr;
         fa.load8(trow + 32 * kb);
-        fh.load8(s.Rh + l16 * TS + 32 * kb + 8 * g4);
-        fl.load8(s.Rl + l16 * TS + 32 * kb + 8 * g4);
-        mma(acc, fa, fh);
-        mma(acc, fa, fl);
+        fr.load8(s.Rh + l16 * TS + 32 * kb + 8 * g4);
+        mma(acc, fa, fr);
     }
-    store4_split(&s.Vh[l16 * TS + t0], &s.Vl[l16 * TS + t0], acc[0], acc[1], acc[2], acc[3]);
+    store4_h(&s.Vh[l16 * TS + t0], acc[0], acc[1], acc[2], acc[3]);
     store4_split(&s.Wh[l16 * TS + t0], &s.Wl[l16 * TS + t0], lm[0] * acc[0], lm[1] * acc[1],
                  lm[2] * acc[2], lm[3] * acc[3]);
 }
@@ -524,17 +535,12 @@ __device__ __forceinline__ void chain_out_update(Smem &s, const PrefillArgs &a, 
         // O^T = S Q^T diag(gamma) + v^T P^T: lane = token 16W + l16, rows = value
         // channels 4G..4G+3, so each lane stores four consecutive outputs at once
         f32x4 acc = qs * gm;
-        const bf *ph = s.Ph[buf] + (16 * W + l16) * TP + 8 * g4;
-        const bf *pl = s.Pl[buf] + (16 * W + l16) * TP + 8 * g4;
+        const hf *ph = s.Ph[buf] + (16 * W + l16) * TP + 8 * g4;
         for (int kb = 0; kb <= (W >> 1); ++kb) {
-            Frag<bf> fph, fpl, fvh, fvl;
-            fph.load8(ph + 32 * kb);
-            fpl.load8(pl + 32 * kb);
-            fvh.load8(s.Vh + l16 * TS + 32 * kb + 8 * g4);
-            fvl.load8(s.Vl + l16 * TS + 32 * kb + 8 * g4);
-            mma(acc, fvh, fph);
-            mma(acc, fvl, fph);
-            mma(acc, fvh, fpl);
+            Frag<hf> fp, fv;
+            fp.load8(ph + 32 * kb);
+            fv.load8(s.Vh + l16 * TS + 32 * kb + 8 * g4);
+            mma(acc, fv, fp);
         }
         if (t < nval) {
             bf16x4 y;
@@ -633,9 +639,8 @@ __global__ __launch_bounds__(THREADS) void gdn_prefill_pipe_kernel(const Prefill
     }
 
     if (nchunks > 0) {
-        for (int i = tid; i < CH * TS; i += THREADS) s.T[i] = f32_to_bf16(0.f);
-        for (int i = tid; i < CH * TP; i += THREADS)
-            s.Ph[0][i] = s.Ph[1][i] = s.Pl[0][i] = s.Pl[1][i] = f32_to_bf16(0.f);
+        for (int i = tid; i < CH * TS; i += THREADS) s.T[i] = (hf)0.f;
+        for (int i = tid; i < CH * TP; i += THREADS) s.Ph[0][i] = s.Ph[1][i] = (hf)0.f;
         Stage stg;
         StageQ stq;
         stage_load(stg, a, wk, wk.bos, min(CH, len), tid);
