@@ -24,16 +24,19 @@
 // wave and the latency of one hides behind the other.  A chunk costs three
 // workgroup barriers:
 //
-//   phase 1:  chain R(c), Q S^T(c)       | map: T(c) blocks below the diagonal,
-//                                        |      gate scan of chunk c+1 (one wave)
-//             all waves: k, v of chunk c+1 into LDS; fetch k, v, g, beta of c+2
-//   phase 2:  chain v(c) = T(c) R(c)     | map: K K^T(c+1) -> A (four waves)
+//   phase 1:  chain R(c), Q S^T(c)       | map: T(c) blocks below the diagonal (waves
+//                                        |      0-2), diagonal tiles of A(c+1) (wave 3)
+//             all waves: k, v, gates of chunk c+2 into LDS; fetch those of c+3
+//   phase 2:  chain v(c) = T(c) R(c)     | map: A(c+1) below the diagonal (waves 0-2),
+//                                        |      first half of the diagonal solve (3)
 //             all waves: q of chunk c+1 into LDS (q of c is dead); fetch q of c+2
-//   phase 3:  chain O(c), S update       | map: Q K^T(c+1) -> P(c+1) (three waves),
-//                                        |      diagonal blocks of T(c+1) (one wave)
+//   phase 3:  chain O(c), S update       | map: Q K^T(c+1) -> P(c+1) (waves 0-2), rest
+//                                        |      of the diagonal blocks of T(c+1) (3)
 //
-// LDS holds two buffers of the k and v tiles, the gates and P; q, T and A are
-// single-buffered because their lifetimes do not overlap across the phases.
+// LDS holds three buffers (chunk mod 3) of the k and v tiles, the gates and P, so k of
+// chunk c+1 is in place when phase 1 starts; q, T and A are single-buffered because
+// their lifetimes do not overlap across the phases (the diagonal tiles of A(c+1) and
+// the blocks of A(c) below it, read in the same phase, are disjoint).
 // One workgroup = 8 wave64s = one (sequence, value head, 16 value channels).
 #include "gdn_device.h"
 #include "gdn_launch.h"
@@ -55,7 +58,8 @@ constexpr int THREADS = 512;   // 4 map + 4 chain waves
 constexpr int KS = DK + 16;   // bf16 row stride of K and the state copy (288 B)
 constexpr int TS = CH + 16;   // bf16 row stride of T, R^T, v^T, (lambda v)^T (160 B)
 constexpr int TP = CH + 8;    // bf16 row stride of P (144 B)
-constexpr int VS = DVS + 8;   // bf16 row stride of the value tile (48 B)
+constexpr int VS = DVS;       // bf16 row stride of the value tile (32 B)
+constexpr int NBUF = 3;       // buffers of the per-chunk tiles (k, v, gates, P)
 constexpr int AS = CH + 8;    // fp32 row stride of A (288 B)
 constexpr float LOG2E = 1.4426950408889634f;
 
@@ -85,11 +89,11 @@ struct __align__(16) Smem {
     hf Rh[DVS * TS];               // R^T
     hf Vh[DVS * TS];               // v^T
     bf Wh[DVS * TS], Wl[DVS * TS];  // (diag(lambda) v)^T
-    Gate gate[2];
-    bf V[2][CH * VS];
-    bf K[2][CH * KS];
+    Gate gate[NBUF];
+    bf V[NBUF][CH * VS];
+    bf K[NBUF][CH * KS];
     bf Q[CH * KS];
-    hf Ph[2][CH * TP];             // P
+    hf Ph[NBUF][CH * TP];          // P
 };
 
 __device__ __forceinline__ float to_f(bf x) { return bf16_to_f32(x); }
@@ -341,7 +345,7 @@ __device__ __forceinline__ void gram_tiles(Smem &s, int nb, int l16, int g4) {
     for (int t = 0; t < NT; ++t) gram_store<ISQ>(s, nb, tl[t] >> 2, tl[t] & 3, c[t], d[t], l16, g4);
 }
 
-// K K^T of the chunk in buffer nb, ten tiles over the four map waves.
+// K K^T of the chunk in buffer nb, all ten tiles over the four map waves (first chunk).
 __device__ __forceinline__ void map_gram_kk(Smem &s, int nb, int m, int l16, int g4) {
     switch (m) {
         case 0: gram_tiles<false, 12, 13, -1, -1>(s, nb, l16, g4); break;   // (3,0) (3,1)
@@ -351,12 +355,22 @@ __device__ __forceinline__ void map_gram_kk(Smem &s, int nb, int m, int l16, int
     }
 }
 
-// Q K^T of the chunk in buffer nb (q in the single q buffer), ten tiles over map
-// waves 1-3 (wave 0 solves the diagonal blocks of T meanwhile).
+// K K^T tiles below the diagonal, over map waves 0-2 (the diagonal tiles are computed
+// one phase earlier by wave 3, which then solves the diagonal blocks of T from them).
+__device__ __forceinline__ void map_gram_kk_below(Smem &s, int nb, int m, int l16, int g4) {
+    switch (m) {
+        case 0: gram_tiles<false, 12, 13, -1, -1>(s, nb, l16, g4); break;   // (3,0) (3,1)
+        case 1: gram_tiles<false, 14, 8, -1, -1>(s, nb, l16, g4); break;    // (3,2) (2,0)
+        default: gram_tiles<false, 9, 4, -1, -1>(s, nb, l16, g4); break;    // (2,1) (1,0)
+    }
+}
+
+// Q K^T of the chunk in buffer nb (q in the single q buffer), ten tiles over three map
+// waves: m = 1..3 for the first chunk, m = 0..2 in the loop.
 __device__ __forceinline__ void map_gram_qk(Smem &s, int nb, int m, int l16, int g4) {
     switch (m) {
-        case 1: gram_tiles<true, 12, 13, 14, 15>(s, nb, l16, g4); break;    // row block 3
-        case 2: gram_tiles<true, 8, 9, 10, -1>(s, nb, l16, g4); break;      // row block 2
+        case 0: gram_tiles<true, 12, 13, 14, 15>(s, nb, l16, g4); break;    // row block 3
+        case 1: gram_tiles<true, 8, 9, 10, -1>(s, nb, l16, g4); break;      // row block 2
         default: gram_tiles<true, 0, 4, 5, -1>(s, nb, l16, g4); break;      // row blocks 0, 1
     }
 }
@@ -366,47 +380,59 @@ __device__ __forceinline__ void map_gram_qk(Smem &s, int nb, int m, int l16, int
 // wave: lane group G solves block G, lane l16 computing column l16 of its inverse.
 // Each block is solved as two 8-row halves (rows 0-7, then rows 8-15 after the
 // independent update by the lower-left 8x8 block), each half read into registers
-// first and solved right-looking, so the updates of one step are independent.
+// first and solved right-looking, so the updates of one step are independent.  The
+// first half runs in one phase, the update, the second half and the stores in the
+// next; x carries the columns across the barrier.
 // ---------------------------------------------------------------------------------
-__device__ __forceinline__ void map_diag_solve(Smem &s, int l16, int g4) {
-    const int B = g4;
-    const float *ablk = &s.A[(16 * B) * AS + 16 * B];
-    float x[16];
+__device__ __forceinline__ void diag_solve_first(const Smem &s, int l16, int g4, float (&x)[16]) {
+    const float *ablk = &s.A[(16 * g4) * AS + 16 * g4];
 #pragma unroll
     for (int i = 0; i < 16; ++i) x[i] = (i == l16) ? 1.f : 0.f;
+    float a[8][8];
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-        const int r0 = 8 * half;
-        if (half == 1) {
-            float b[8][8];
+    for (int r = 1; r < 8; ++r)
 #pragma unroll
-            for (int r = 0; r < 8; ++r)
+        for (int q = 0; q < r; q += 4) {
+            const f32x4 t = *reinterpret_cast<const f32x4 *>(ablk + r * AS + q);
 #pragma unroll
-                for (int q = 0; q < 8; q += 4) {
-                    const f32x4 t = *reinterpret_cast<const f32x4 *>(ablk + (8 + r) * AS + q);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) b[r][q + e] = t[e];
-                }
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-#pragma unroll
-                for (int r = 0; r < 8; ++r) x[8 + r] -= b[r][j] * x[j];
+            for (int e = 0; e < 4; ++e) a[r][q + e] = t[e];
         }
-        float a[8][8];
 #pragma unroll
-        for (int r = 1; r < 8; ++r)
+    for (int j = 0; j < 7; ++j)
 #pragma unroll
-            for (int q = 0; q < r; q += 4) {
-                const f32x4 t = *reinterpret_cast<const f32x4 *>(ablk + (r0 + r) * AS + r0 + q);
+        for (int r = j + 1; r < 8; ++r) x[r] -= a[r][j] * x[j];
+}
+
+__device__ __forceinline__ void diag_solve_second(Smem &s, int l16, int g4, float (&x)[16]) {
+    const float *bblk = &s.A[(16 * g4 + 8) * AS + 16 * g4];
+    float b[8][8];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) a[r][q + e] = t[e];
-            }
+    for (int r = 0; r < 8; ++r)
 #pragma unroll
-        for (int j = 0; j < 7; ++j)
+        for (int q = 0; q < 8; q += 4) {
+            const f32x4 t = *reinterpret_cast<const f32x4 *>(bblk + r * AS + q);
 #pragma unroll
-            for (int r = j + 1; r < 8; ++r) x[r0 + r] -= a[r][j] * x[r0 + j];
-    }
-    store_cols_paired<16>(&s.T[(16 * B) * TS + 16 * B + l16], TS, x, l16);
+            for (int e = 0; e < 4; ++e) b[r][q + e] = t[e];
+        }
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int r = 0; r < 8; ++r) x[8 + r] -= b[r][j] * x[j];
+    const float *ablk = &s.A[(16 * g4 + 8) * AS + 16 * g4 + 8];
+    float a[8][8];
+#pragma unroll
+    for (int r = 1; r < 8; ++r)
+#pragma unroll
+        for (int q = 0; q < r; q += 4) {
+            const f32x4 t = *reinterpret_cast<const f32x4 *>(ablk + r * AS + q);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) a[r][q + e] = t[e];
+        }
+#pragma unroll
+    for (int j = 0; j < 7; ++j)
+#pragma unroll
+        for (int r = j + 1; r < 8; ++r) x[8 + r] -= a[r][j] * x[8 + j];
+    store_cols_paired<16>(&s.T[(16 * g4) * TS + 16 * g4 + l16], TS, x, l16);
 }
 
 // ---------------------------------------------------------------------------------
@@ -640,94 +666,114 @@ __global__ __launch_bounds__(THREADS) void gdn_prefill_pipe_kernel(const Prefill
 
     if (nchunks > 0) {
         for (int i = tid; i < CH * TS; i += THREADS) s.T[i] = (hf)0.f;
-        for (int i = tid; i < CH * TP; i += THREADS) s.Ph[0][i] = s.Ph[1][i] = (hf)0.f;
+        for (int i = tid; i < CH * TP; i += THREADS) s.Ph[0][i] = s.Ph[1][i] = s.Ph[2][i] = (hf)0.f;
         Stage stg;
         StageQ stq;
         stage_load(stg, a, wk, wk.bos, min(CH, len), tid);
         stage_load_q(stq, a, wk, wk.bos, min(CH, len), tid);
         stage_commit(stg, s, 0, tid);
         stage_commit_q(stq, s, tid);
-        if (wave == 3) gate_scan(stg, s, 0, lane);
+        if (wave == 2) gate_scan(stg, s, 0, lane);
         {
             const int t1 = prefetch_tok(wk, 1, nchunks), n1 = min(CH, wk.eos - t1);
             stage_load(stg, a, wk, t1, n1, tid);
             stage_load_q(stq, a, wk, t1, n1, tid);
+            stage_commit(stg, s, 1, tid);
+            if (wave == 2) gate_scan(stg, s, 1, lane);
+            const int t2 = prefetch_tok(wk, 2, nchunks), n2 = min(CH, wk.eos - t2);
+            stage_load(stg, a, wk, t2, n2, tid);
         }
         __syncthreads();
 
         // The two roles run separate loops with the same barrier sequence (three per
         // chunk), so values one role keeps across a barrier do not occupy registers in
-        // the other role's code.  All 512 threads stage the next chunk's tiles.
-        // Each loop trip runs two chunks, so the LDS buffer of every access is a
-        // compile-time constant (it folds into the instruction's immediate offset).
+        // the other role's code.  All 512 threads stage the tiles of later chunks: k, v,
+        // g, beta two chunks ahead (committed in phase 1), q one chunk ahead (phase 2).
+        // Each loop trip runs three chunks, so the LDS buffer (chunk mod 3) of every
+        // access is a compile-time constant.
         using B0 = std::integral_constant<int, 0>;
         using B1 = std::integral_constant<int, 1>;
+        using B2 = std::integral_constant<int, 2>;
         if (is_map) {
+            // first chunk: K K^T, then Q K^T and the diagonal blocks of T
+            float xd[16];   // wave 3: columns of the diagonal blocks of T, across a barrier
             map_gram_kk(s, 0, W, l16, g4);
             __syncthreads();
-            if (W != 0) map_gram_qk(s, 0, W, l16, g4);
-            else map_diag_solve(s, l16, g4);
+            if (W != 0) {
+                map_gram_qk(s, 0, W - 1, l16, g4);
+            } else {
+                diag_solve_first(s, l16, g4, xd);
+                diag_solve_second(s, l16, g4, xd);
+            }
             __syncthreads();
             auto step = [&](auto bufc, int c) {
-                constexpr int nb = decltype(bufc)::value ^ 1;
+                constexpr int b0 = decltype(bufc)::value, b1 = (b0 + 1) % NBUF, b2 = (b0 + 2) % NBUF;
                 const bool has_next = c + 1 < nchunks;
-                const int t2 = prefetch_tok(wk, c + 2, nchunks);
-                const int n2 = min(CH, wk.eos - t2);
-                // phase 1
+                const int tq = prefetch_tok(wk, c + 2, nchunks), nq = min(CH, wk.eos - tq);
+                const int t3 = prefetch_tok(wk, c + 3, nchunks), n3 = min(CH, wk.eos - t3);
+                // phase 1: T(c) below the diagonal; diagonal tiles of A(c+1); k, v and
+                // gates of chunk c+2 (their buffers held chunk c-1, finished last step)
                 switch (W) {
                     case 0: map_merges<0>(s, l16, g4); break;
                     case 1: map_merges<1>(s, l16, g4); break;
                     case 2: map_merges<2>(s, l16, g4); break;
-                    default: break;
+                    default:
+                        if (has_next) gram_tiles<false, 0, 5, 10, 15>(s, b1, l16, g4);
+                        break;
                 }
-                stage_commit(stg, s, nb, tid);
-                if (wave == 3) gate_scan(stg, s, nb, lane);
-                stage_load(stg, a, wk, t2, n2, tid);
+                stage_commit(stg, s, b2, tid);
+                if (wave == 2) gate_scan(stg, s, b2, lane);
+                stage_load(stg, a, wk, t3, n3, tid);
                 __syncthreads();
-                // phase 2
-                if (has_next) map_gram_kk(s, nb, W, l16, g4);
-                stage_commit_q(stq, s, tid);
-                stage_load_q(stq, a, wk, t2, n2, tid);
-                __syncthreads();
-                // phase 3
+                // phase 2: A(c+1) below the diagonal; first half of its diagonal solve
                 if (has_next) {
-                    if (W != 0) map_gram_qk(s, nb, W, l16, g4);
-                    else map_diag_solve(s, l16, g4);
+                    if (W == 3) diag_solve_first(s, l16, g4, xd);
+                    else map_gram_kk_below(s, b1, W, l16, g4);
+                }
+                stage_commit_q(stq, s, tid);
+                stage_load_q(stq, a, wk, tq, nq, tid);
+                __syncthreads();
+                // phase 3: P(c+1); second half of the diagonal solve of T(c+1)
+                if (has_next) {
+                    if (W == 3) diag_solve_second(s, l16, g4, xd);
+                    else map_gram_qk(s, b1, W, l16, g4);
                 }
                 __syncthreads();
             };
-            for (int c = 0; c < nchunks; c += 2) {
+            for (int c = 0; c < nchunks; c += 3) {
                 step(B0{}, c);
                 if (c + 1 < nchunks) step(B1{}, c + 1);
+                if (c + 2 < nchunks) step(B2{}, c + 2);
             }
         } else {
             __syncthreads();
             __syncthreads();
             auto step = [&](auto bufc, int c) {
-                constexpr int buf = decltype(bufc)::value, nb = buf ^ 1;
+                constexpr int b0 = decltype(bufc)::value, b2 = (b0 + 2) % NBUF;
                 const int tok0 = wk.bos + c * CH;
                 const int nval = min(CH, wk.eos - tok0);
-                const int t2 = prefetch_tok(wk, c + 2, nchunks);
-                const int n2 = min(CH, wk.eos - t2);
+                const int tq = prefetch_tok(wk, c + 2, nchunks), nq = min(CH, wk.eos - tq);
+                const int t3 = prefetch_tok(wk, c + 3, nchunks), n3 = min(CH, wk.eos - t3);
                 // phase 1
                 Frag<bf> fs[4];
-                chain_R(s, buf, W, l16, g4, fs);
+                chain_R(s, b0, W, l16, g4, fs);
                 const f32x4 qs = chain_QS(s, W, l16, g4, fs);
-                stage_commit(stg, s, nb, tid);
-                stage_load(stg, a, wk, t2, n2, tid);
+                stage_commit(stg, s, b2, tid);
+                stage_load(stg, a, wk, t3, n3, tid);
                 __syncthreads();
                 // phase 2
-                chain_v(s, buf, W, l16, g4);
+                chain_v(s, b0, W, l16, g4);
                 stage_commit_q(stq, s, tid);
-                stage_load_q(stq, a, wk, t2, n2, tid);
+                stage_load_q(stq, a, wk, tq, nq, tid);
                 __syncthreads();
                 // phase 3
-                chain_out_update(s, a, buf, W, l16, g4, qs, st, h, dv0, tok0, nval);
+                chain_out_update(s, a, b0, W, l16, g4, qs, st, h, dv0, tok0, nval);
                 __syncthreads();
             };
-            for (int c = 0; c < nchunks; c += 2) {
+            for (int c = 0; c < nchunks; c += 3) {
                 step(B0{}, c);
                 if (c + 1 < nchunks) step(B1{}, c + 1);
+                if (c + 2 < nchunks) step(B2{}, c + 2);
             }
         }
     }
