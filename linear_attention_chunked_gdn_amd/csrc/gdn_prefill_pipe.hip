@@ -25,7 +25,7 @@
 // workgroup barriers:
 //
 //   phase 1:  chain R(c), Q S^T(c)       | map: T(c) blocks below the diagonal (waves
-//                                        |      0-2), diagonal tiles of A(c+1) (wave 3)
+//                                        |      0-2), diagonal tiles of A(c+1) (2, 3)
 //             all waves: k, v, gates of chunk c+2 into LDS; fetch those of c+3
 //   phase 2:  chain v(c) = T(c) R(c)     | map: A(c+1) below the diagonal (waves 0-2),
 //                                        |      first half of the diagonal solve (3)
@@ -716,9 +716,12 @@ __global__ __launch_bounds__(THREADS) void gdn_prefill_pipe_kernel(const Prefill
                 switch (W) {
                     case 0: map_merges<0>(s, l16, g4); break;
                     case 1: map_merges<1>(s, l16, g4); break;
-                    case 2: map_merges<2>(s, l16, g4); break;
+                    case 2:
+                        map_merges<2>(s, l16, g4);
+                        if (has_next) gram_tiles<false, 15, -1, -1, -1>(s, b1, l16, g4);
+                        break;
                     default:
-                        if (has_next) gram_tiles<false, 0, 5, 10, 15>(s, b1, l16, g4);
+                        if (has_next) gram_tiles<false, 0, 5, 10, -1>(s, b1, l16, g4);
                         break;
                 }
                 stage_commit(stg, s, b2, tid);
