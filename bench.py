@@ -24,6 +24,10 @@ To refresh it, profile bench.py under `rocprofv3 --pmc FETCH_SIZE` / `--pmc WRIT
 (files fetch_* / write_*) and `bench.py --calibrate-copy 256` likewise (copyfetch_* /
 copywrite_*), then run `bench.py --summarize-pmc DIR`.
 
+decode (workloads with decode steps): microseconds per gdn_decode_step, launched eagerly
+and replayed from a HIP graph (see `decode_bench`).  measured_peaks: copy bandwidth and
+a bf16 GEMM measured on this GPU, beside the published peaks used for the fractions.
+
 cpu_baseline: the fp64 CPU oracle (test infrastructure, untuned) timed on the host
 cores over the same workload.
 """
@@ -148,6 +152,100 @@ def cpu_baseline(x, min_repeats: int = 3, min_seconds: float = 5.0) -> dict:
             "sample": f"the whole workload ({x.T_tot} tokens x {x.Hv} heads), fp64 token-by-token "
                       f"recurrence, OpenMP over (sequence, head); median of {repeats} runs, "
                       f"{dt:.3f} s each"}
+
+
+def decode_bench(x, dev, state0) -> dict:
+    """The workload's single-token decode steps (gdn_decode_step, B = N), started from the
+    prefill's final state: mean time per step with the steps launched from Python (each
+    launch waits on the host), and with the same steps captured once in a HIP graph and
+    replayed (launches back to back, so the figure is the kernels' own time).  Every
+    replay is checked bitwise against the eager run."""
+    import torch
+    from linear_attention_chunked_gdn_amd import gdn
+    dec = x.decode
+    n = dec["steps"]
+    io = torch.bfloat16 if x.io == "bf16" else torch.float32
+    dq, dk, dv = (torch.from_numpy(np.ascontiguousarray(dec[k])).to(dev, io) for k in ("q", "k", "v"))
+    dg, db = (torch.from_numpy(np.ascontiguousarray(dec[k])).to(dev, torch.float32) for k in ("g", "beta"))
+    outs = torch.empty((n, x.N, x.Hv, x.Dv), dtype=io, device=dev)
+    state = torch.empty_like(state0)
+    B = x.N
+
+    def run():
+        for i in range(n):
+            sl = slice(i * B, (i + 1) * B)
+            gdn.decode_step(dq[sl], dk[sl], dv[sl], dg[sl], db[sl], state, out=outs[i])
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    state.copy_(state0)
+    run()
+    state.copy_(state0)
+    torch.cuda.synchronize()
+    e0, e1 = ev(), ev()
+    e0.record()
+    run()
+    e1.record()
+    torch.cuda.synchronize()
+    eager_us = e0.elapsed_time(e1) * 1e3 / n
+    ref_o, ref_s = outs.clone(), state.clone()
+
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        state.copy_(state0)
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    with torch.cuda.graph(graph):
+        run()
+    times, exact = [], True
+    for _ in range(5):
+        state.copy_(state0)
+        torch.cuda.synchronize()
+        e0, e1 = ev(), ev()
+        e0.record()
+        graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e3 / n)
+        exact &= bool(torch.equal(outs, ref_o)) and bool(torch.equal(state, ref_s))
+    if not exact:
+        raise RuntimeError("decode graph replay differs from the eager decode steps")
+    graph_us = float(np.median(times))
+    state_bytes = B * x.Hv * x.Dv * x.Dk * 4 * 2
+    return {"steps": n, "batch": B, "us_per_step_graph": graph_us, "us_per_step_eager": eager_us,
+            "state_bytes_per_step": state_bytes,
+            "state_GBps_graph": state_bytes / (graph_us * 1e-6) / 1e9,
+            "note": "state read + written once per step; 4 MiB at H=32 stays in the Infinity "
+                    "Cache between steps, so this is not an HBM fraction"}
+
+
+def measured_peaks(dev) -> dict:
+    """Peaks measured on this GPU beside the published ones: a 1 GiB device copy (bytes
+    read + written per second) and a 8192^3 bf16 GEMM through torch (hipBLASLt)."""
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device=dev)
+    b = torch.empty(n, dtype=torch.uint8, device=dev)
+    m = 8192
+    x = torch.randn((m, m), dtype=torch.bfloat16, device=dev)
+    y = torch.randn((m, m), dtype=torch.bfloat16, device=dev)
+    res = {}
+    for name, fn, work in (("copy_GBps", lambda: b.copy_(a), 2 * n / 1e9),
+                           ("bf16_gemm_TFLOPs", lambda: torch.mm(x, y), 2 * m ** 3 / 1e12)):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = work / (e0.elapsed_time(e1) / 10 / 1e3)
+    del a, b, x, y
+    torch.cuda.empty_cache()
+    return res
 
 
 def calibrate_copy(mib: int, steps: int) -> int:
@@ -297,6 +395,9 @@ def main() -> int:
         "wall_s_timed": wall,
         "parity": parity,
     }
+    if x.decode is not None:
+        rec["decode"] = decode_bench(x, dev, sets[(args.steps - 1) % copies]["fs"])
+    rec["measured_peaks"] = measured_peaks(dev)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(x)
     print(json.dumps(rec), flush=True)
