@@ -26,7 +26,7 @@
 //
 //   phase 1:  chain R(c), Q S^T(c)       | map: T(c) blocks below the diagonal (waves
 //                                        |      0-2), diagonal tiles of A(c+1) (2, 3)
-//             all waves: k, v, gates of chunk c+2 into LDS; fetch those of c+3
+//             all waves: k, v of chunk c+2 into LDS (gate scan: wave 1); fetch c+3
 //   phase 2:  chain v(c) = T(c) R(c)     | map: A(c+1) below the diagonal (waves 0-2),
 //                                        |      first half of the diagonal solve (3)
 //             all waves: q of chunk c+1 into LDS (q of c is dead); fetch q of c+2
@@ -384,6 +384,29 @@ __device__ __forceinline__ void map_gram_qk(Smem &s, int nb, int m, int l16, int
 // first half runs in one phase, the update, the second half and the stores in the
 // next; x carries the columns across the barrier.
 // ---------------------------------------------------------------------------------
+// Rows 8+R0 .. 8+R1-1 of a diagonal block minus the lower-left 8x8 block times rows
+// 0-7 (the update between the two halves of the substitution).
+template <int R0, int R1>
+__device__ __forceinline__ void diag_update_rows(const Smem &s, int g4, float (&x)[16]) {
+    const float *bblk = &s.A[(16 * g4 + 8) * AS + 16 * g4];
+    float b[8][8];
+#pragma unroll
+    for (int r = R0; r < R1; ++r)
+#pragma unroll
+        for (int q = 0; q < 8; q += 4) {
+            const f32x4 t = *reinterpret_cast<const f32x4 *>(bblk + r * AS + q);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) b[r][q + e] = t[e];
+        }
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int r = R0; r < R1; ++r) x[8 + r] -= b[r][j] * x[j];
+}
+
+// rows of the update done in the first phase of the solve, the rest in the second
+constexpr int DIAG_SPLIT = 0;
+
 __device__ __forceinline__ void diag_solve_first(const Smem &s, int l16, int g4, float (&x)[16]) {
     const float *ablk = &s.A[(16 * g4) * AS + 16 * g4];
 #pragma unroll
@@ -401,23 +424,11 @@ __device__ __forceinline__ void diag_solve_first(const Smem &s, int l16, int g4,
     for (int j = 0; j < 7; ++j)
 #pragma unroll
         for (int r = j + 1; r < 8; ++r) x[r] -= a[r][j] * x[j];
+    diag_update_rows<0, DIAG_SPLIT>(s, g4, x);
 }
 
 __device__ __forceinline__ void diag_solve_second(Smem &s, int l16, int g4, float (&x)[16]) {
-    const float *bblk = &s.A[(16 * g4 + 8) * AS + 16 * g4];
-    float b[8][8];
-#pragma unroll
-    for (int r = 0; r < 8; ++r)
-#pragma unroll
-        for (int q = 0; q < 8; q += 4) {
-            const f32x4 t = *reinterpret_cast<const f32x4 *>(bblk + r * AS + q);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) b[r][q + e] = t[e];
-        }
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-#pragma unroll
-        for (int r = 0; r < 8; ++r) x[8 + r] -= b[r][j] * x[j];
+    diag_update_rows<DIAG_SPLIT, 8>(s, g4, x);
     const float *ablk = &s.A[(16 * g4 + 8) * AS + 16 * g4 + 8];
     float a[8][8];
 #pragma unroll
@@ -725,7 +736,7 @@ __global__ __launch_bounds__(THREADS) void gdn_prefill_pipe_kernel(const Prefill
                         break;
                 }
                 stage_commit(stg, s, b2, tid);
-                if (wave == 2) gate_scan(stg, s, b2, lane);
+                if (wave == 1) gate_scan(stg, s, b2, lane);
                 stage_load(stg, a, wk, t3, n3, tid);
                 __syncthreads();
                 // phase 2: A(c+1) below the diagonal; first half of its diagonal solve
