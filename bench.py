@@ -1,6 +1,7 @@
 """Throughput of the chunked gated delta-rule prefill on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload I] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload I] [--io bf16|f16|f32]
+                    [--no-cpu-baseline]
 
 A step is one gdn_prefill call over the whole workload (all heads, all chunks) with
 inputs resident in HBM.  The default workload is the headline one: one sequence of
@@ -12,7 +13,7 @@ roofline.achieved = algorithmic bytes of one launch / mean launch time, where th
 mean launch time comes from HIP events recorded on the launch stream around the
 timed steps (one kernel per step).  Algorithmic bytes per launch:
     T*(Hk*2*Dk*s + Hv*(2*Dv*s + 8)) + N*Hv*Dv*Dk*4*(2 if an initial state else 1)
-with s = 2 (bf16) or 4 (fp32): q, k read once per key head, v read and o written once
+with s = 2 (bf16, fp16) or 4 (fp32): q, k read once per key head, v read and o written once
 per value head, g and beta (fp32) read, the fp32 state read (if given) and written.
 Algorithmic FLOPs per full chunk and value head: 6*C*Dk*Dv (three state products)
 + 2*C^2*Dv (intra-chunk output) + 2*C^2*Dk (the K K^T gram) ... see `algorithmic_flops`.
@@ -54,6 +55,7 @@ FP32_MFMA_PEAK_TFLOPS = 157.3
 MALL_BYTES = 256 << 20
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 CSRC = os.path.join(ROOT, "linear_attention_chunked_gdn_amd", "csrc")
+IO_CODE = {"f32": 0, "bf16": 1, "f16": 2}   # gdn_dtype
 # sources each kernel is compiled from: the HBM counters recorded for a kernel are
 # reported only while these are unchanged
 KERNEL_SOURCES = {
@@ -95,13 +97,13 @@ def _counter_median(path: str, counter: str, kernel_substr: str) -> float:
     return statistics.median(per_dispatch.values())
 
 
-def summarize_pmc(directory: str, workload: int, calib_mib: int) -> dict:
+def summarize_pmc(directory: str, workload: int, calib_mib: int, io=None) -> dict:
     """Scale the FETCH_SIZE / WRITE_SIZE counters (KiB per dispatch) of the prefill kernel by
     what the same counters read for a copy of known size; rocprofv3 runs of bench.py wrote
     fetch_, write_, copyfetch_ and copywrite_counter_collection.csv into `directory`."""
     from linear_attention_chunked_gdn_amd import gdn, inputs
-    x = inputs.make_workload(workload)
-    plan = gdn.prefill_plan(x.N, x.Hv, gdn.GDN_BF16 if x.io == "bf16" else gdn.GDN_F32)
+    x = inputs.make_workload(workload, io=io)
+    plan = gdn.prefill_plan(x.N, x.Hv, IO_CODE[x.io])
     kernel = "gdn_prefill_pipe_kernel" if plan["threads_per_workgroup"] == 512 else "gdn_prefill_kernel"
     true_kib = calib_mib * 1024.0
     f = lambda n, c, k: _counter_median(os.path.join(directory, f"{n}_counter_collection.csv"), c, k)  # noqa: E731
@@ -115,7 +117,7 @@ def summarize_pmc(directory: str, workload: int, calib_mib: int) -> dict:
 
 
 def algorithmic_bytes(x) -> int:
-    s = 2 if x.io == "bf16" else 4
+    s = 4 if x.io == "f32" else 2
     T, Hk, Hv, Dk, Dv, N = x.T_tot, x.Hk, x.Hv, x.Dk, x.Dv, x.N
     state = N * Hv * Dv * Dk * 4 * (2 if x.initial_state is not None else 1)
     return T * (Hk * 2 * Dk * s + Hv * (2 * Dv * s + 8)) + state
@@ -164,7 +166,7 @@ def decode_bench(x, dev, state0) -> dict:
     from linear_attention_chunked_gdn_amd import gdn
     dec = x.decode
     n = dec["steps"]
-    io = torch.bfloat16 if x.io == "bf16" else torch.float32
+    io = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[x.io]
     dq, dk, dv = (torch.from_numpy(np.ascontiguousarray(dec[k])).to(dev, io) for k in ("q", "k", "v"))
     dg, db = (torch.from_numpy(np.ascontiguousarray(dec[k])).to(dev, torch.float32) for k in ("g", "beta"))
     outs = torch.empty((n, x.N, x.Hv, x.Dv), dtype=io, device=dev)
@@ -268,6 +270,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", type=int, default=1)
+    ap.add_argument("--io", choices=sorted(IO_CODE), default=None,
+                    help="storage type of q, k, v, o (default: the workload's own)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rotate-bytes", type=int, default=2 * MALL_BYTES,
                     help="input copies are rotated until they span at least this many bytes")
@@ -283,7 +287,7 @@ def main() -> int:
         print("bench.py: this build runs on one GPU only; --gpus must be 1", file=sys.stderr)
         return 2
     if args.summarize_pmc:
-        entry = summarize_pmc(args.summarize_pmc, args.workload, args.calibrate_copy or 256)
+        entry = summarize_pmc(args.summarize_pmc, args.workload, args.calibrate_copy or 256, args.io)
         try:
             with open(TRAFFIC_FILE) as f:
                 table = json.load(f)
@@ -304,8 +308,8 @@ def main() -> int:
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    x = inputs.make_workload(args.workload)
-    io = torch.bfloat16 if x.io == "bf16" else torch.float32
+    x = inputs.make_workload(args.workload, io=args.io)
+    io = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[x.io]
 
     per_copy = algorithmic_bytes(x)
     copies = max(1, -(-args.rotate_bytes // per_copy))
@@ -350,11 +354,11 @@ def main() -> int:
         s = sets[(args.steps - 1) % copies]
         ro, rf = oracle.recurrent(x.q, x.k, x.v, x.g, x.beta, x.initial_state, x.cu_seqlens)
         from gpu_support import TOL_BF16_REL_RMS, TOL_F32_ABS
-        bf = x.io == "bf16"
-        eo = error_stats(s["o"].double().cpu().numpy(), ro, bf16_storage=bf)
+        half = x.io != "f32"
+        eo = error_stats(s["o"].double().cpu().numpy(), ro, storage=x.io if half else None)
         ef = error_stats(s["fs"].double().cpu().numpy(), rf)
-        # bf16: kernel error / rms beside the stored outputs' bf16 rounding (the tests' bar)
-        ok = (max(eo["kernel_rel_rms"], ef["kernel_rel_rms"]) <= TOL_BF16_REL_RMS if bf
+        # 16-bit I/O: kernel error / rms beside the stored outputs' rounding (the tests' bar)
+        ok = (max(eo["kernel_rel_rms"], ef["kernel_rel_rms"]) <= TOL_BF16_REL_RMS if half
               else max(eo["max_abs"], ef["max_abs"]) <= TOL_F32_ABS)
         parity = {"o_kernel_err_over_rms": eo["kernel_rel_rms"], "o_max_err_over_rms": eo["rel_rms"],
                   "state_err_over_rms": ef["rel_rms"], "o_nmse": eo["nmse"], "state_nmse": ef["nmse"],
@@ -363,9 +367,9 @@ def main() -> int:
     nbytes = algorithmic_bytes(x)
     flops = algorithmic_flops(x)
     sec = ms_per_step / 1e3
-    plan = gdn.prefill_plan(x.N, x.Hv, gdn.GDN_BF16 if x.io == "bf16" else gdn.GDN_F32)
+    plan = gdn.prefill_plan(x.N, x.Hv, IO_CODE[x.io])
     kernel = "gdn_prefill_pipe_kernel" if plan["threads_per_workgroup"] == 512 else "gdn_prefill_kernel"
-    mfma_peak = BF16_MFMA_PEAK_TFLOPS if x.io == "bf16" else FP32_MFMA_PEAK_TFLOPS
+    mfma_peak = FP32_MFMA_PEAK_TFLOPS if x.io == "f32" else BF16_MFMA_PEAK_TFLOPS  # fp16 = bf16 rate
     rec = {
         "metric": METRIC,
         "value": tokens / sec,
@@ -377,7 +381,7 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if x.io == "bf16" else "f32",
+        "dtype": x.io,
         "data": "synthetic",
         "config": {"workload": x.name, "sequences": x.N, "tokens": x.T_tot, "Hk": x.Hk, "Hv": x.Hv,
                    "d": x.Dk, "chunk": 64, "io": x.io, "state": "fp32",

@@ -48,7 +48,8 @@ typedef enum gdn_status {
 
 typedef enum gdn_dtype {
     GDN_F32 = 0,   /* q, k, v, o stored as IEEE fp32; all arithmetic in fp32                   */
-    GDN_BF16 = 1   /* q, k, v, o stored as bf16; fp32 accumulation, fp32 state, bf16 products  */
+    GDN_BF16 = 1,  /* q, k, v, o stored as bf16; fp32 accumulation and state, 16-bit products  */
+    GDN_F16 = 2    /* q, k, v, o stored as fp16; fp32 accumulation and state, fp16 products    */
 } gdn_dtype;
 
 /*

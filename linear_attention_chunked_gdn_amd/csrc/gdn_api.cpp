@@ -51,10 +51,10 @@ bool overlap(const Range &a, const Range &b) {
 constexpr int kD = 128;
 constexpr int kChunk = 64;
 
-// Kernel choice.  bf16 I/O runs the software-pipelined kernel (16 value channels per
-// workgroup); fp32 I/O runs the phase-by-phase kernel with fp32 MFMAs.  GDN_KERNEL=v1
-// selects the phase-by-phase kernel for bf16 too, and GDN_DVS=16|32 its slice width
-// (for comparisons and tuning).
+// Kernel choice.  bf16 and fp16 I/O run the software-pipelined kernel (16 value
+// channels per workgroup); fp32 I/O runs the phase-by-phase kernel with fp32 MFMAs.
+// GDN_KERNEL=v1 selects the phase-by-phase kernel for bf16 too, and GDN_DVS=16|32 its
+// slice width (for comparisons and tuning); fp16 I/O has only the pipelined kernel.
 struct Plan {
     bool pipe;
     int dvs;
@@ -62,10 +62,12 @@ struct Plan {
     int threads;
 };
 
+bool valid_dtype(gdn_dtype dt) { return dt == GDN_F32 || dt == GDN_BF16 || dt == GDN_F16; }
+
 Plan choose_plan(gdn_dtype dt) {
     const char *kern = std::getenv("GDN_KERNEL");
     const bool force_v1 = kern && std::strcmp(kern, "v1") == 0;
-    if (dt == GDN_BF16 && !force_v1)
+    if (dt == GDN_F16 || (dt == GDN_BF16 && !force_v1))
         return Plan{true, 16, gdn::prefill_pipe_lds_bytes(), gdn::prefill_pipe_threads()};
     int dvs = 16;
     const char *env = std::getenv("GDN_DVS");
@@ -95,8 +97,8 @@ const char *gdn_last_error(void) { return g_last_error.c_str(); }
 gdn_status gdn_prefill_plan(int32_t N, int32_t Hv, int32_t Dv, gdn_dtype io_dtype,
                             int32_t *dv_per_workgroup, int32_t *workgroups, int32_t *lds_bytes,
                             int32_t *threads_per_workgroup) {
-    if (io_dtype != GDN_F32 && io_dtype != GDN_BF16)
-        return fail(GDN_ERR_INVALID_ARGUMENT, "io_dtype %d is not GDN_F32 or GDN_BF16", (int)io_dtype);
+    if (!valid_dtype(io_dtype))
+        return fail(GDN_ERR_INVALID_ARGUMENT, "io_dtype %d is not GDN_F32, GDN_BF16 or GDN_F16", (int)io_dtype);
     if (N < 1 || Hv < 1) return fail(GDN_ERR_INVALID_ARGUMENT, "N=%d and Hv=%d must be >= 1", N, Hv);
     if (Dv != kD) return fail(GDN_ERR_UNSUPPORTED, "Dv=%d (only 128 is implemented)", Dv);
     const Plan p = choose_plan(io_dtype);
@@ -114,8 +116,8 @@ gdn_status gdn_prefill(const void *q, const void *k, const void *v, const float 
                        int32_t N, int32_t T_tot, int32_t Hk, int32_t Hv, int32_t Dk, int32_t Dv,
                        int32_t chunk_size, gdn_dtype io_dtype, void *o, float *final_state,
                        void *stream) {
-    if (io_dtype != GDN_F32 && io_dtype != GDN_BF16)
-        return fail(GDN_ERR_INVALID_ARGUMENT, "io_dtype %d is not GDN_F32 or GDN_BF16", (int)io_dtype);
+    if (!valid_dtype(io_dtype))
+        return fail(GDN_ERR_INVALID_ARGUMENT, "io_dtype %d is not GDN_F32, GDN_BF16 or GDN_F16", (int)io_dtype);
     if (N < 1) return fail(GDN_ERR_INVALID_ARGUMENT, "N=%d must be >= 1", N);
     if (T_tot < 0) return fail(GDN_ERR_INVALID_ARGUMENT, "T_tot=%d must be >= 0", T_tot);
     if (Hk < 1 || Hv < 1) return fail(GDN_ERR_INVALID_ARGUMENT, "Hk=%d, Hv=%d must be >= 1", Hk, Hv);
@@ -137,7 +139,7 @@ gdn_status gdn_prefill(const void *q, const void *k, const void *v, const float 
     if (!aligned(g, 4) || !aligned(beta, 4) || !aligned(cu_seqlens, 4))
         return fail(GDN_ERR_INVALID_ARGUMENT, "g, beta and cu_seqlens must be 4-byte aligned");
 
-    const size_t es = io_dtype == GDN_BF16 ? 2 : 4;
+    const size_t es = io_dtype == GDN_F32 ? 4 : 2;
     const size_t T = (size_t)T_tot;
     const size_t state_bytes = (size_t)N * Hv * kD * kD * sizeof(float);
     const Range ro = range(o, T * Hv * kD * es, "o");
@@ -165,7 +167,8 @@ gdn_status gdn_prefill(const void *q, const void *k, const void *v, const float 
     a.N = N; a.T_tot = T_tot; a.Hk = Hk; a.Hv = Hv; a.nslices = kD / dvs;
     const Plan p = choose_plan(io_dtype);
     (void)hipGetLastError();
-    const hipError_t e = p.pipe ? gdn::launch_prefill_pipe(a, wg, static_cast<hipStream_t>(stream))
+    const hipError_t e = p.pipe ? gdn::launch_prefill_pipe(a, io_dtype == GDN_F16, wg,
+                                                           static_cast<hipStream_t>(stream))
                                 : gdn::launch_prefill(a, io_dtype == GDN_BF16, dvs, wg,
                                                       static_cast<hipStream_t>(stream));
     if (e != hipSuccess)
@@ -176,8 +179,8 @@ gdn_status gdn_prefill(const void *q, const void *k, const void *v, const float 
 gdn_status gdn_decode_step(const void *q, const void *k, const void *v, const float *g,
                            const float *beta, float *state, int32_t B, int32_t Hk, int32_t Hv,
                            int32_t Dk, int32_t Dv, gdn_dtype io_dtype, void *o, void *stream) {
-    if (io_dtype != GDN_F32 && io_dtype != GDN_BF16)
-        return fail(GDN_ERR_INVALID_ARGUMENT, "io_dtype %d is not GDN_F32 or GDN_BF16", (int)io_dtype);
+    if (!valid_dtype(io_dtype))
+        return fail(GDN_ERR_INVALID_ARGUMENT, "io_dtype %d is not GDN_F32, GDN_BF16 or GDN_F16", (int)io_dtype);
     if (B < 1 || Hk < 1 || Hv < 1)
         return fail(GDN_ERR_INVALID_ARGUMENT, "B=%d, Hk=%d, Hv=%d must be >= 1", B, Hk, Hv);
     if (Hv % Hk != 0)
@@ -191,7 +194,7 @@ gdn_status gdn_decode_step(const void *q, const void *k, const void *v, const fl
         return fail(GDN_ERR_INVALID_ARGUMENT, "q, k and state must be 16-byte aligned, the rest 4-byte");
     if ((long long)B * Hv * (kD / 16) > 0x7fffffffLL)
         return fail(GDN_ERR_UNSUPPORTED, "B*Hv too large for one launch");
-    const size_t es = io_dtype == GDN_BF16 ? 2 : 4;
+    const size_t es = io_dtype == GDN_F32 ? 4 : 2;
     const Range ro = range(o, (size_t)B * Hv * kD * es, "o");
     const Range rs = range(state, (size_t)B * Hv * kD * kD * 4, "state");
     const Range ins[] = {range(q, (size_t)B * Hk * kD * es, "q"), range(k, (size_t)B * Hk * kD * es, "k"),
@@ -207,7 +210,7 @@ gdn_status gdn_decode_step(const void *q, const void *k, const void *v, const fl
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.state = state; a.o = o;
     a.B = B; a.Hk = Hk; a.Hv = Hv;
     (void)hipGetLastError();
-    const hipError_t e = gdn::launch_decode(a, io_dtype == GDN_BF16, static_cast<hipStream_t>(stream));
+    const hipError_t e = gdn::launch_decode(a, (int)io_dtype, static_cast<hipStream_t>(stream));
     if (e != hipSuccess)
         return fail(GDN_ERR_DEVICE, "decode launch failed: %s", hipGetErrorString(e));
     return ok();

@@ -21,13 +21,13 @@ namespace gdn {
 constexpr int DEC_D = 128;
 constexpr int DEC_ROWS = 16;   // rows per workgroup
 
-template <bool BF16>
+template <typename IO>
 __device__ __forceinline__ void load8_io(const void *base, size_t off, float *x) {
-    if constexpr (BF16) {
-        const uint4 u = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(base) + off);
-        const uint16_t *e = reinterpret_cast<const uint16_t *>(&u);
+    if constexpr (sizeof(IO) == 2) {
+        typedef IO v8 __attribute__((ext_vector_type(8)));
+        const v8 u = *reinterpret_cast<const v8 *>(reinterpret_cast<const IO *>(base) + off);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) x[i] = bf16_bits_to_f32(e[i]);
+        for (int i = 0; i < 8; ++i) x[i] = Cvt<IO>::to_f32(u[i]);
     } else {
         const float *p = reinterpret_cast<const float *>(base) + off;
         const f32x4 a = *reinterpret_cast<const f32x4 *>(p);
@@ -43,7 +43,7 @@ __device__ __forceinline__ float sum16(float x) {
     return x;
 }
 
-template <bool BF16>
+template <typename IO>
 __global__ __launch_bounds__(256) void gdn_decode_kernel(const DecodeArgs a) {
     constexpr int RB = DEC_D / DEC_ROWS;
     const int rb = blockIdx.x % RB;
@@ -61,12 +61,10 @@ __global__ __launch_bounds__(256) void gdn_decode_kernel(const DecodeArgs a) {
         for (int i = 0; i < 4; ++i) { S[i] = s0[i]; S[4 + i] = s1[i]; }
     }
     const size_t koff = ((size_t)b * a.Hk + hk) * DEC_D + 8 * l;
-    load8_io<BF16>(a.k, koff, kk);
-    load8_io<BF16>(a.q, koff, qq);
-    float vi;
+    load8_io<IO>(a.k, koff, kk);
+    load8_io<IO>(a.q, koff, qq);
     const size_t voff = ((size_t)b * a.Hv + h) * DEC_D + row;
-    if constexpr (BF16) vi = bf16_bits_to_f32(reinterpret_cast<const uint16_t *>(a.v)[voff]);
-    else vi = reinterpret_cast<const float *>(a.v)[voff];
+    const float vi = Cvt<IO>::to_f32(reinterpret_cast<const IO *>(a.v)[voff]);
     const float alpha = __expf(a.g[(size_t)b * a.Hv + h]);
     const float beta = a.beta[(size_t)b * a.Hv + h];
 
@@ -85,20 +83,17 @@ __global__ __launch_bounds__(256) void gdn_decode_kernel(const DecodeArgs a) {
     o = sum16(o);                               // (S q)_row, updated state
     *reinterpret_cast<f32x4 *>(srow) = f32x4{S[0], S[1], S[2], S[3]};
     *reinterpret_cast<f32x4 *>(srow + 4) = f32x4{S[4], S[5], S[6], S[7]};
-    if (l == 0) {
-        if constexpr (BF16)
-            reinterpret_cast<uint16_t *>(a.o)[voff] = __builtin_bit_cast(uint16_t, f32_to_bf16(o));
-        else
-            reinterpret_cast<float *>(a.o)[voff] = o;
-    }
+    if (l == 0) reinterpret_cast<IO *>(a.o)[voff] = Cvt<IO>::from_f32(o);
 }
 
-hipError_t launch_decode(const DecodeArgs &a, bool bf16, hipStream_t stream) {
+hipError_t launch_decode(const DecodeArgs &a, int io, hipStream_t stream) {
     const int grid = a.B * a.Hv * (DEC_D / DEC_ROWS);
-    if (bf16)
-        hipLaunchKernelGGL(gdn_decode_kernel<true>, dim3(grid), dim3(256), 0, stream, a);
+    if (io == 1)
+        hipLaunchKernelGGL(gdn_decode_kernel<__bf16>, dim3(grid), dim3(256), 0, stream, a);
+    else if (io == 2)
+        hipLaunchKernelGGL(gdn_decode_kernel<_Float16>, dim3(grid), dim3(256), 0, stream, a);
     else
-        hipLaunchKernelGGL(gdn_decode_kernel<false>, dim3(grid), dim3(256), 0, stream, a);
+        hipLaunchKernelGGL(gdn_decode_kernel<float>, dim3(grid), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 

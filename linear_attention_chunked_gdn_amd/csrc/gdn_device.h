@@ -46,10 +46,19 @@ template <> struct Cvt<__bf16> {
     __device__ static __forceinline__ float to_f32(__bf16 x) { return bf16_to_f32(x); }
     __device__ static __forceinline__ __bf16 from_f32(float x) { return f32_to_bf16(x); }
 };
+template <> struct Cvt<_Float16> {
+    __device__ static __forceinline__ float to_f32(_Float16 x) { return (float)x; }
+    __device__ static __forceinline__ _Float16 from_f32(float x) { return (_Float16)x; }
+};
 template <> struct Cvt<float> {
     __device__ static __forceinline__ float to_f32(float x) { return x; }
     __device__ static __forceinline__ float from_f32(float x) { return x; }
 };
+
+// Four-element vectors of a 16-bit element type (one 8-byte access).
+template <typename CT> struct Vec4;
+template <> struct Vec4<__bf16> { typedef bf16x4 type; };
+template <> struct Vec4<_Float16> { typedef f16x4 type; };
 
 // Eight slots of one MFMA step operand.
 template <typename CT> struct Frag;

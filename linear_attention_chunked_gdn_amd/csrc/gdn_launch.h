@@ -33,9 +33,10 @@ hipError_t launch_prefill(const PrefillArgs &a, bool bf16, int dvs, int grid, hi
 // LDS bytes of one prefill workgroup, -1 if (bf16, dvs) is not instantiated.
 int prefill_lds_bytes(bool bf16, int dvs);
 int prefill_threads();
-hipError_t launch_decode(const DecodeArgs &a, bool bf16, hipStream_t stream);
+// io: 0 fp32, 1 bf16, 2 fp16 (the gdn_dtype codes)
+hipError_t launch_decode(const DecodeArgs &a, int io, hipStream_t stream);
 // Software-pipelined bf16 prefill (16 value channels per workgroup).
-hipError_t launch_prefill_pipe(const PrefillArgs &a, int grid, hipStream_t stream);
+hipError_t launch_prefill_pipe(const PrefillArgs &a, bool f16, int grid, hipStream_t stream);
 int prefill_pipe_lds_bytes();
 int prefill_pipe_threads();
 

@@ -1,16 +1,18 @@
 // Wave-specialised, software-pipelined chunked gated delta-rule prefill for gfx950,
-// bf16 I/O.
+// bf16 or fp16 I/O (the kernel is a template on the 16-bit I/O type IO).
 //
 // The chunkwise formulas and the column-wise split of the state are those of
 // gdn_prefill.hip (see there), scheduled so the two halves of the Map-Reduce-Map
 // pipeline ("Empowering Hybrid Attention Models on NPUs", section 2.1, Figure 1(b))
 // run side by side.  Operand precision of the products (fp32 accumulation always):
-//   * q, k, v and the state copy used by K S^T and Q S^T: bf16 (q, k, v exactly);
+//   * q, k, v and the state copy used by K S^T and Q S^T: the I/O type (q, k, v
+//     exactly);
 //   * T, R, v and P, which the kernel computes: fp16 (11-bit significand), one MFMA
 //     per product; a single bf16 rounding of R, v or P would cost 1.4-3.6 % of the
 //     output RMS, fp16 costs a quarter of that.  They stay far inside fp16's range
 //     for L2-normalised q and k (|P| <= 1) and values of ordinary size;
-//   * lambda v, multiplied with the bf16 K^T in the update: split into bf16 hi + lo.
+//   * lambda v, multiplied with K^T in the update: bf16 hi + lo for bf16 I/O, one fp16
+//     operand for fp16 I/O.
 //
 // Roles:
 //
@@ -80,23 +82,46 @@ struct Gate {
     float w[3][CH];   // w[i-1][s] = exp(Gamma_16i - Gamma_s) for s < 16i, else 0
 };
 
+template <typename IO>
 struct __align__(16) Smem {
     // The small tiles come first: a DS instruction's immediate offset reaches 64 KiB,
     // so these are addressed from one base register plus constants.
     float A[CH * AS];              // A of the chunk being mapped, strictly lower
     hf T[CH * TS];                 // T = (I + A)^-1
-    bf S[DVS * KS];                // bf16 copy of the state slice [value ch][key ch]
+    IO S[DVS * KS];                // copy of the state slice [value ch][key ch] in IO's type
     hf Rh[DVS * TS];               // R^T
     hf Vh[DVS * TS];               // v^T
-    bf Wh[DVS * TS], Wl[DVS * TS];  // (diag(lambda) v)^T
+    IO Wh[DVS * TS], Wl[DVS * TS];  // (diag(lambda) v)^T (hi + lo for bf16 I/O)
     Gate gate[NBUF];
-    bf V[NBUF][CH * VS];
-    bf K[NBUF][CH * KS];
-    bf Q[CH * KS];
+    IO V[NBUF][CH * VS];
+    IO K[NBUF][CH * KS];
+    IO Q[CH * KS];
     hf Ph[NBUF][CH * TP];          // P
 };
 
 __device__ __forceinline__ float to_f(bf x) { return bf16_to_f32(x); }
+
+template <typename IO> constexpr bool IS_F16 = std::is_same<IO, hf>::value;
+
+// Four values rounded to IO and written with one 8-byte store.
+template <typename IO>
+__device__ __forceinline__ void store4_io(IO *p, const f32x4 &x) {
+    typename Vec4<IO>::type t;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) t[r] = Cvt<IO>::from_f32(x[r]);
+    *reinterpret_cast<typename Vec4<IO>::type *>(p) = t;
+}
+
+// ds_read_b64_tr_b16 for either 16-bit element type.
+__device__ __forceinline__ bf16x4 ds_read_tr4(const bf *p) {
+    typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)p);
+}
+__device__ __forceinline__ f16x4 ds_read_tr4(const hf *p) {
+    typedef __fp16 fp16x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) fp16x4 lds_fp16x4;
+    return __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4 *)p));
+}
 
 // Four consecutive values as split bf16 pairs (hi, lo).
 __device__ __forceinline__ void store4_split(bf *hi, bf *lo, float a0, float a1, float a2, float a3) {
@@ -227,14 +252,16 @@ __device__ __forceinline__ int prefetch_tok(const Work &wk, int c, int nchunks) 
     return wk.bos + min(c, nchunks - 1) * CH;
 }
 
-__device__ __forceinline__ void stage_commit(const Stage &st, Smem &s, int buf, int tid) {
+template <typename IO>
+__device__ __forceinline__ void stage_commit(const Stage &st, Smem<IO> &s, int buf, int tid) {
     const int seg = tid & 15;
     *reinterpret_cast<u32x4 *>(&s.K[buf][(tid >> 4) * KS + seg * 8]) = st.k0;
     *reinterpret_cast<u32x4 *>(&s.K[buf][((tid + THREADS) >> 4) * KS + seg * 8]) = st.k1;
     *reinterpret_cast<unsigned *>(&s.V[buf][(tid >> 3) * VS + (tid & 7) * 2]) = st.v;
 }
 
-__device__ __forceinline__ void stage_commit_q(const StageQ &st, Smem &s, int tid) {
+template <typename IO>
+__device__ __forceinline__ void stage_commit_q(const StageQ &st, Smem<IO> &s, int tid) {
     const int seg = tid & 15;
     *reinterpret_cast<u32x4 *>(&s.Q[(tid >> 4) * KS + seg * 8]) = st.q0;
     *reinterpret_cast<u32x4 *>(&s.Q[((tid + THREADS) >> 4) * KS + seg * 8]) = st.q1;
@@ -242,7 +269,8 @@ __device__ __forceinline__ void stage_commit_q(const StageQ &st, Smem &s, int ti
 
 // #1 Gate for the chunk staged in buffer buf, by map wave 3 (lane = token): the
 // inclusive scan of g and every decay factor the grams and the chain need.
-__device__ __forceinline__ void gate_scan(const Stage &st, Smem &s, int buf, int lane) {
+template <typename IO>
+__device__ __forceinline__ void gate_scan(const Stage &st, Smem<IO> &s, int buf, int lane) {
     const bool valid = lane < st.nval;
     const float x2 = wave_inclusive_scan(valid ? st.g : 0.f, lane) * LOG2E;
     const float last2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x2), 63));
@@ -274,8 +302,8 @@ __device__ __forceinline__ void gate_scan(const Stage &st, Smem &s, int buf, int
 // Per-element factor of tile (bi, bj) for this lane's row and four columns: the decay,
 // times beta of the row for K K^T.  Computed before the tile's products so the gate
 // reads overlap the MFMAs.
-template <bool ISQ>
-__device__ __forceinline__ f32x4 gram_scale(const Smem &s, int nb, int bi, int bj, int l16, int g4) {
+template <bool ISQ, typename IO>
+__device__ __forceinline__ f32x4 gram_scale(const Smem<IO> &s, int nb, int bi, int bj, int l16, int g4) {
     const Gate &gt = s.gate[nb];
     const int rr = 16 * bi + l16;          // row of this lane
     const int c0 = 16 * bj + 4 * g4;       // first of its four columns
@@ -304,8 +332,8 @@ __device__ __forceinline__ f32x4 gram_scale(const Smem &s, int nb, int bi, int b
 }
 
 // A goes to s.A (fp32), P to s.Ph[nb] (fp16).
-template <bool ISQ>
-__device__ __forceinline__ void gram_store(Smem &s, int nb, int bi, int bj, const f32x4 &acc, const f32x4 &d,
+template <bool ISQ, typename IO>
+__device__ __forceinline__ void gram_store(Smem<IO> &s, int nb, int bi, int bj, const f32x4 &acc, const f32x4 &d,
                                           int l16, int g4) {
     const int rr = 16 * bi + l16;
     const int c0 = 16 * bj + 4 * g4;
@@ -319,8 +347,8 @@ __device__ __forceinline__ void gram_store(Smem &s, int nb, int bi, int bj, cons
 
 // Up to four tiles of one gram, each given as 4 * (row block) + (column block), -1 for
 // none.  Operand fragments shared by several tiles are read once per step.
-template <bool ISQ, int T0, int T1, int T2, int T3>
-__device__ __forceinline__ void gram_tiles(Smem &s, int nb, int l16, int g4) {
+template <bool ISQ, int T0, int T1, int T2, int T3, typename IO>
+__device__ __forceinline__ void gram_tiles(Smem<IO> &s, int nb, int l16, int g4) {
     constexpr int tl[4] = {T0, T1, T2, T3};
     constexpr int NT = (T0 >= 0) + (T1 >= 0) + (T2 >= 0) + (T3 >= 0);
     f32x4 c[NT], d[NT];
@@ -329,13 +357,13 @@ __device__ __forceinline__ void gram_tiles(Smem &s, int nb, int l16, int g4) {
         c[t] = zero4();
         d[t] = gram_scale<ISQ>(s, nb, tl[t] >> 2, tl[t] & 3, l16, g4);
     }
-    const bf *xs = ISQ ? s.Q : s.K[nb];
+    const IO *xs = ISQ ? s.Q : s.K[nb];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             // tile (bi, bj) is computed transposed, K_bj X_bi^T
-            Frag<bf> kj, x;
+            Frag<IO> kj, x;
             kj.load8(s.K[nb] + (16 * (tl[t] & 3) + l16) * KS + 32 * kb + 8 * g4);
             x.load8(xs + (16 * (tl[t] >> 2) + l16) * KS + 32 * kb + 8 * g4);
             mma(c[t], kj, x);
@@ -346,7 +374,8 @@ __device__ __forceinline__ void gram_tiles(Smem &s, int nb, int l16, int g4) {
 }
 
 // K K^T of the chunk in buffer nb, all ten tiles over the four map waves (first chunk).
-__device__ __forceinline__ void map_gram_kk(Smem &s, int nb, int m, int l16, int g4) {
+template <typename IO>
+__device__ __forceinline__ void map_gram_kk(Smem<IO> &s, int nb, int m, int l16, int g4) {
     switch (m) {
         case 0: gram_tiles<false, 12, 13, -1, -1>(s, nb, l16, g4); break;   // (3,0) (3,1)
         case 1: gram_tiles<false, 14, 15, 0, -1>(s, nb, l16, g4); break;    // (3,2) (3,3) (0,0)
@@ -357,7 +386,8 @@ __device__ __forceinline__ void map_gram_kk(Smem &s, int nb, int m, int l16, int
 
 // K K^T tiles below the diagonal, over map waves 0-2 (the diagonal tiles are computed
 // one phase earlier by wave 3, which then solves the diagonal blocks of T from them).
-__device__ __forceinline__ void map_gram_kk_below(Smem &s, int nb, int m, int l16, int g4) {
+template <typename IO>
+__device__ __forceinline__ void map_gram_kk_below(Smem<IO> &s, int nb, int m, int l16, int g4) {
     switch (m) {
         case 0: gram_tiles<false, 12, 13, -1, -1>(s, nb, l16, g4); break;   // (3,0) (3,1)
         case 1: gram_tiles<false, 14, 8, -1, -1>(s, nb, l16, g4); break;    // (3,2) (2,0)
@@ -367,7 +397,8 @@ __device__ __forceinline__ void map_gram_kk_below(Smem &s, int nb, int m, int l1
 
 // Q K^T of the chunk in buffer nb (q in the single q buffer), ten tiles over three map
 // waves: m = 1..3 for the first chunk, m = 0..2 in the loop.
-__device__ __forceinline__ void map_gram_qk(Smem &s, int nb, int m, int l16, int g4) {
+template <typename IO>
+__device__ __forceinline__ void map_gram_qk(Smem<IO> &s, int nb, int m, int l16, int g4) {
     switch (m) {
         case 0: gram_tiles<true, 12, 13, 14, 15>(s, nb, l16, g4); break;    // row block 3
         case 1: gram_tiles<true, 8, 9, 10, -1>(s, nb, l16, g4); break;      // row block 2
@@ -386,8 +417,8 @@ __device__ __forceinline__ void map_gram_qk(Smem &s, int nb, int m, int l16, int
 // ---------------------------------------------------------------------------------
 // Rows 8+R0 .. 8+R1-1 of a diagonal block minus the lower-left 8x8 block times rows
 // 0-7 (the update between the two halves of the substitution).
-template <int R0, int R1>
-__device__ __forceinline__ void diag_update_rows(const Smem &s, int g4, float (&x)[16]) {
+template <int R0, int R1, typename IO>
+__device__ __forceinline__ void diag_update_rows(const Smem<IO> &s, int g4, float (&x)[16]) {
     const float *bblk = &s.A[(16 * g4 + 8) * AS + 16 * g4];
     float b[8][8];
 #pragma unroll
@@ -407,7 +438,8 @@ __device__ __forceinline__ void diag_update_rows(const Smem &s, int g4, float (&
 // rows of the update done in the first phase of the solve, the rest in the second
 constexpr int DIAG_SPLIT = 0;
 
-__device__ __forceinline__ void diag_solve_first(const Smem &s, int l16, int g4, float (&x)[16]) {
+template <typename IO>
+__device__ __forceinline__ void diag_solve_first(const Smem<IO> &s, int l16, int g4, float (&x)[16]) {
     const float *ablk = &s.A[(16 * g4) * AS + 16 * g4];
 #pragma unroll
     for (int i = 0; i < 16; ++i) x[i] = (i == l16) ? 1.f : 0.f;
@@ -427,7 +459,8 @@ __device__ __forceinline__ void diag_solve_first(const Smem &s, int l16, int g4,
     diag_update_rows<0, DIAG_SPLIT>(s, g4, x);
 }
 
-__device__ __forceinline__ void diag_solve_second(Smem &s, int l16, int g4, float (&x)[16]) {
+template <typename IO>
+__device__ __forceinline__ void diag_solve_second(Smem<IO> &s, int l16, int g4, float (&x)[16]) {
     diag_update_rows<DIAG_SPLIT, 8>(s, g4, x);
     const float *ablk = &s.A[(16 * g4 + 8) * AS + 16 * g4 + 8];
     float a[8][8];
@@ -450,8 +483,8 @@ __device__ __forceinline__ void diag_solve_second(Smem &s, int l16, int g4, floa
 // Map: blocks of column block CB below the diagonal, T_i,CB = -T_ii sum_j A_ij T_j,CB.
 // Results stay in registers (accumulator layout == B-operand layout) between steps.
 // ---------------------------------------------------------------------------------
-template <int CB>
-__device__ __forceinline__ void map_merges(Smem &s, int l16, int g4) {
+template <int CB, typename IO>
+__device__ __forceinline__ void map_merges(Smem<IO> &s, int l16, int g4) {
     // every operand read from LDS up front, so the three dependent levels wait on one
     // round of loads instead of one per level
     f32x4 a[4][4];       // a[i][j]: A_ij, row 16i + l16, columns 16j + 4G..+3
@@ -501,9 +534,10 @@ __device__ __forceinline__ void map_merges(Smem &s, int l16, int g4) {
 // Chain, phase 1: R = beta V - beta gamma (K S^T) for tokens [16W, 16W+16).  The S
 // fragments are returned for Q S^T.
 // ---------------------------------------------------------------------------------
-__device__ __forceinline__ void chain_R(Smem &s, int buf, int W, int l16, int g4, Frag<bf> (&fs)[4]) {
-    const bf *krow = s.K[buf] + (16 * W + l16) * KS + 8 * g4;
-    const bf *srow = s.S + l16 * KS + 8 * g4;
+template <typename IO>
+__device__ __forceinline__ void chain_R(Smem<IO> &s, int buf, int W, int l16, int g4, Frag<IO> (&fs)[4]) {
+    const IO *krow = s.K[buf] + (16 * W + l16) * KS + 8 * g4;
+    const IO *srow = s.S + l16 * KS + 8 * g4;
     // R = beta V - (beta gamma) (K S^T): the gate and V terms are read before the products
     const int t0 = 16 * W + 4 * g4;
     const f32x4 b = *reinterpret_cast<const f32x4 *>(&s.gate[buf].beta[t0]);
@@ -511,13 +545,13 @@ __device__ __forceinline__ void chain_R(Smem &s, int buf, int W, int l16, int g4
     f32x4 bv, bg;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        bv[i] = b[i] * to_f(s.V[buf][(t0 + i) * VS + l16]);
+        bv[i] = b[i] * Cvt<IO>::to_f32(s.V[buf][(t0 + i) * VS + l16]);
         bg[i] = b[i] * gm[i];
     }
     f32x4 ks = zero4();
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-        Frag<bf> fk;
+        Frag<IO> fk;
         fs[kb].load8(srow + 32 * kb);
         fk.load8(krow + 32 * kb);
         mma(ks, fk, fs[kb]);      // (K S^T): lane = value channel, rows = tokens
@@ -530,12 +564,13 @@ __device__ __forceinline__ void chain_R(Smem &s, int buf, int W, int l16, int g4
 
 // Chain, phase 1: (Q S^T)^T = S Q^T for tokens [16W, 16W+16) (lane = token, rows =
 // value channels), from the S fragments loaded by chain_R.
-__device__ __forceinline__ f32x4 chain_QS(const Smem &s, int W, int l16, int g4, const Frag<bf> (&fs)[4]) {
-    const bf *qrow = s.Q + (16 * W + l16) * KS + 8 * g4;
+template <typename IO>
+__device__ __forceinline__ f32x4 chain_QS(const Smem<IO> &s, int W, int l16, int g4, const Frag<IO> (&fs)[4]) {
+    const IO *qrow = s.Q + (16 * W + l16) * KS + 8 * g4;
     f32x4 qs = zero4();
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-        Frag<bf> fq;
+        Frag<IO> fq;
         fq.load8(qrow + 32 * kb);
         mma(qs, fs[kb], fq);
     }
@@ -544,7 +579,8 @@ __device__ __forceinline__ f32x4 chain_QS(const Smem &s, int W, int l16, int g4,
 
 // Chain, phase 2: v = T R for tokens [16W, 16W+16); T is lower triangular, so only
 // the first W/2 + 1 blocks of 32 columns contribute.
-__device__ __forceinline__ void chain_v(Smem &s, int buf, int W, int l16, int g4) {
+template <typename IO>
+__device__ __forceinline__ void chain_v(Smem<IO> &s, int buf, int W, int l16, int g4) {
     const int t0 = 16 * W + 4 * g4;
     const f32x4 lm = *reinterpret_cast<const f32x4 *>(&s.gate[buf].lam[t0]);
     f32x4 acc = zero4();
@@ -556,13 +592,19 @@ __device__ __forceinline__ void chain_v(Smem &s, int buf, int W, int l16, int g4
         mma(acc, fa, fr);
     }
     store4_h(&s.Vh[l16 * TS + t0], acc[0], acc[1], acc[2], acc[3]);
-    store4_split(&s.Wh[l16 * TS + t0], &s.Wl[l16 * TS + t0], lm[0] * acc[0], lm[1] * acc[1],
-                 lm[2] * acc[2], lm[3] * acc[3]);
+    // lambda v multiplies K^T in IO's type: one fp16 operand for fp16 I/O, bf16 hi + lo
+    // for bf16 I/O
+    if constexpr (IS_F16<IO>)
+        store4_io(&s.Wh[l16 * TS + t0], lm * acc);
+    else
+        store4_split(&s.Wh[l16 * TS + t0], &s.Wl[l16 * TS + t0], lm[0] * acc[0], lm[1] * acc[1],
+                     lm[2] * acc[2], lm[3] * acc[3]);
 }
 
 // Chain, phase 3: output rows of wave W, then the update of key channels
 // [32W, 32W+32) of the state slice.
-__device__ __forceinline__ void chain_out_update(Smem &s, const PrefillArgs &a, int buf, int W, int l16,
+template <typename IO>
+__device__ __forceinline__ void chain_out_update(Smem<IO> &s, const PrefillArgs &a, int buf, int W, int l16,
                                                  int g4, const f32x4 &qs, f32x4 (&st)[2], int h,
                                                  int dv0, int tok0, int nval) {
     const int t = 16 * W + l16;
@@ -579,13 +621,8 @@ __device__ __forceinline__ void chain_out_update(Smem &s, const PrefillArgs &a, 
             fv.load8(s.Vh + l16 * TS + 32 * kb + 8 * g4);
             mma(acc, fv, fp);
         }
-        if (t < nval) {
-            bf16x4 y;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) y[r] = f32_to_bf16(acc[r]);
-            *reinterpret_cast<bf16x4 *>(reinterpret_cast<uint16_t *>(a.o) +
-                                        ((size_t)(tok0 + t) * a.Hv + h) * DV + dv0 + 4 * g4) = y;
-        }
+        if (t < nval)
+            store4_io(reinterpret_cast<IO *>(a.o) + ((size_t)(tok0 + t) * a.Hv + h) * DV + dv0 + 4 * g4, acc);
     }
     {
 #pragma unroll
@@ -594,39 +631,38 @@ __device__ __forceinline__ void chain_out_update(Smem &s, const PrefillArgs &a, 
             // 32W + 16mt + l16) with ds_read_b64_tr_b16: in each 16-lane group, source
             // lane a points at 4 key channels of token t0 + a/4, and result lane m then
             // holds key channel m of tokens t0..t0+3.
-            Frag<bf> ka[2];
+            Frag<IO> ka[2];
             const int a_tok = l16 >> 2, a_ch = 32 * W + 16 * mt + 4 * (l16 & 3);
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int hh = 0; hh < 2; ++hh) {
                     const int t0 = 32 * kb + 8 * g4 + 4 * hh;
-                    typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
-                    const bf16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                        (lds_bf16x4 *)(&s.K[buf][(t0 + a_tok) * KS + a_ch]));
+                    const auto v = ds_read_tr4(&s.K[buf][(t0 + a_tok) * KS + a_ch]);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) ka[kb].set_raw(4 * hh + e, v[e]);
                 }
             f32x4 acc = st[mt] * glast;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
-                Frag<bf> fh, fl;
+                Frag<IO> fh;
                 fh.load8(s.Wh + l16 * TS + 32 * kb + 8 * g4);
-                fl.load8(s.Wl + l16 * TS + 32 * kb + 8 * g4);
                 mma(acc, ka[kb], fh);
-                mma(acc, ka[kb], fl);
+                if constexpr (!IS_F16<IO>) {
+                    Frag<IO> fl;
+                    fl.load8(s.Wl + l16 * TS + 32 * kb + 8 * g4);
+                    mma(acc, ka[kb], fl);
+                }
             }
             st[mt] = acc;
-            bf16x4 t;
-            t[0] = f32_to_bf16(acc[0]); t[1] = f32_to_bf16(acc[1]);
-            t[2] = f32_to_bf16(acc[2]); t[3] = f32_to_bf16(acc[3]);
-            *reinterpret_cast<bf16x4 *>(&s.S[l16 * KS + 32 * W + 16 * mt + 4 * g4]) = t;
+            store4_io(&s.S[l16 * KS + 32 * W + 16 * mt + 4 * g4], acc);
         }
     }
 }
 
+template <typename IO>
 __global__ __launch_bounds__(THREADS) void gdn_prefill_pipe_kernel(const PrefillArgs a) {
-    __shared__ Smem s;
+    __shared__ Smem<IO> s;
     const int tid = threadIdx.x;
     const int lane = tid & 63, l16 = lane & 15, g4 = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -669,9 +705,7 @@ __global__ __launch_bounds__(THREADS) void gdn_prefill_pipe_kernel(const Prefill
             f32x4 x = zero4();
             if (a.s0) x = *reinterpret_cast<const f32x4 *>(a.s0 + sbase + (size_t)(dv0 + l16) * DK + dk);
             st[mt] = x;
-            bf16x4 t;
-            t[0] = f32_to_bf16(x[0]); t[1] = f32_to_bf16(x[1]); t[2] = f32_to_bf16(x[2]); t[3] = f32_to_bf16(x[3]);
-            *reinterpret_cast<bf16x4 *>(&s.S[l16 * KS + dk]) = t;
+            store4_io(&s.S[l16 * KS + dk], x);
         }
     }
 
@@ -769,7 +803,7 @@ __global__ __launch_bounds__(THREADS) void gdn_prefill_pipe_kernel(const Prefill
                 const int tq = prefetch_tok(wk, c + 2, nchunks), nq = min(CH, wk.eos - tq);
                 const int t3 = prefetch_tok(wk, c + 3, nchunks), n3 = min(CH, wk.eos - t3);
                 // phase 1
-                Frag<bf> fs[4];
+                Frag<IO> fs[4];
                 chain_R(s, b0, W, l16, g4, fs);
                 const f32x4 qs = chain_QS(s, W, l16, g4, fs);
                 stage_commit(stg, s, b2, tid);
@@ -803,12 +837,15 @@ __global__ __launch_bounds__(THREADS) void gdn_prefill_pipe_kernel(const Prefill
 
 }  // namespace pipe
 
-hipError_t launch_prefill_pipe(const PrefillArgs &a, int grid, hipStream_t stream) {
-    hipLaunchKernelGGL(pipe::gdn_prefill_pipe_kernel, dim3(grid), dim3(pipe::THREADS), 0, stream, a);
+hipError_t launch_prefill_pipe(const PrefillArgs &a, bool f16, int grid, hipStream_t stream) {
+    if (f16)
+        hipLaunchKernelGGL(pipe::gdn_prefill_pipe_kernel<pipe::hf>, dim3(grid), dim3(pipe::THREADS), 0, stream, a);
+    else
+        hipLaunchKernelGGL(pipe::gdn_prefill_pipe_kernel<pipe::bf>, dim3(grid), dim3(pipe::THREADS), 0, stream, a);
     return hipGetLastError();
 }
 
-int prefill_pipe_lds_bytes() { return (int)sizeof(pipe::Smem); }
+int prefill_pipe_lds_bytes() { return (int)sizeof(pipe::Smem<pipe::bf>); }
 
 int prefill_pipe_threads() { return pipe::THREADS; }
 

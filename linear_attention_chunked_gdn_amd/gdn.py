@@ -19,6 +19,7 @@ from .build import LIB_PATH
 
 GDN_F32 = 0
 GDN_BF16 = 1
+GDN_F16 = 2
 D = 128
 CHUNK = 64
 
@@ -66,11 +67,13 @@ def _check(lib, status: int, what: str):
 
 
 def _io_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float16:
+        return GDN_F16
     if t.dtype == torch.bfloat16:
         return GDN_BF16
     if t.dtype == torch.float32:
         return GDN_F32
-    raise TypeError(f"q/k/v must be bfloat16 or float32, got {t.dtype}")
+    raise TypeError(f"q/k/v must be bfloat16, float16 or float32, got {t.dtype}")
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -96,8 +99,8 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
             output_final_state: bool = True, out: Optional[torch.Tensor] = None,
             final_state: Optional[torch.Tensor] = None, lib=None
             ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
-    """Packed chunked prefill.  q, k: [T, Hk, 128]; v: [T, Hv, 128] (bf16 or fp32, all
-    the same); g, beta: [T, Hv] fp32; initial_state: [N, Hv, 128, 128] fp32 or None;
+    """Packed chunked prefill.  q, k: [T, Hk, 128]; v: [T, Hv, 128] (bf16, fp16 or fp32,
+    all the same); g, beta: [T, Hv] fp32; initial_state: [N, Hv, 128, 128] fp32 or None;
     cu_seqlens: [N+1] int32 on the device, or None for one sequence.  Returns
     (o [T, Hv, 128], final_state [N, Hv, 128, 128] fp32 or None)."""
     lib = lib or load_library()

@@ -12,9 +12,10 @@ Shapes follow the packed layout of the C-ABI: q, k are [T_tot, Hk, Dk];
 v is [T_tot, Hv, Dv]; g and beta are [T_tot, Hv]; states are
 [N, Hv, Dv, Dk] (value index, then key index); cu_seqlens is [N+1] int32.
 
-Every array is numpy.  bf16 values are carried as float32 arrays whose values
-are exactly representable in bf16 (round-to-nearest-even from float32), so an
-exact upcast to fp64 gives the oracle the very values the GPU reads.
+Every array is numpy.  bf16 and fp16 values are carried as float32 arrays whose
+values are exactly representable in the storage type (round-to-nearest-even from
+float32), so an exact upcast to fp64 gives the oracle the very values the GPU
+reads.
 """
 from __future__ import annotations
 
@@ -39,6 +40,14 @@ def round_to_bf16(x: np.ndarray) -> np.ndarray:
     u += bias
     u &= np.uint32(0xFFFF0000)
     return x
+
+
+def round_to_f16(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to the nearest IEEE fp16 (ties to even); return float32."""
+    x = np.asarray(x, dtype=np.float32)
+    if not np.all(np.isfinite(x)) or np.any(np.abs(x) >= 65520.0):
+        raise ValueError("round_to_f16 expects finite values inside the fp16 range")
+    return x.astype(np.float16).astype(np.float32)
 
 
 def bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -68,10 +77,10 @@ def _softplus64(x: np.ndarray) -> np.ndarray:
 
 @dataclasses.dataclass
 class GDNInputs:
-    """One synthetic workload.  Arrays are float32 (bf16-exact when io == 'bf16')."""
+    """One synthetic workload.  Arrays are float32 (exact in the storage type io)."""
 
     name: str
-    io: str                      # 'bf16' or 'f32': storage type of q, k, v, o
+    io: str                      # 'bf16', 'f16' or 'f32': storage type of q, k, v, o
     q: np.ndarray                # [T_tot, Hk, Dk]
     k: np.ndarray                # [T_tot, Hk, Dk]
     v: np.ndarray                # [T_tot, Hv, Dv]
@@ -123,6 +132,8 @@ def draw_tokens(rng: np.random.Generator, T: int, Hk: int, Hv: int, Dk: int, Dv:
     g = (-_softplus64(g_logit.astype(np.float64) + g_shift)).astype(np.float32)
     if io == "bf16":
         q, k, v = round_to_bf16(q), round_to_bf16(k), round_to_bf16(v)
+    elif io == "f16":
+        q, k, v = round_to_f16(q), round_to_f16(k), round_to_f16(v)
     elif io != "f32":
         raise ValueError(f"unknown io type {io!r}")
     return q, k, v, g, beta
@@ -158,35 +169,43 @@ WORKLOADS = {
 }
 
 
-def make_workload(i: int, decode_steps: Optional[int] = None) -> GDNInputs:
-    """Build workload i (0..4) from its seed.  Draw order is fixed per workload."""
+def make_workload(i: int, decode_steps: Optional[int] = None, io: Optional[str] = None) -> GDNInputs:
+    """Build workload i (0..4) from its seed.  Draw order is fixed per workload.
+
+    io overrides the storage type of q, k, v, o (default: the workload's own, fp32 for
+    workload 0 and bf16 for the rest); the draws are the same, only the rounding
+    differs, and the name then carries the new type."""
     rng = np.random.default_rng(SEED_BASE + i)
+    own = "f32" if i == 0 else "bf16"
     name = WORKLOADS[i]["name"]
+    if io is not None and io != own:
+        name = name.replace(own, io)
+    io = io or own
     D = 128
     if i == 0:
-        q, k, v, g, beta = draw_tokens(rng, 256, 1, 1, D, D, "f32")
-        return GDNInputs(name, "f32", q, k, v, g, beta, np.array([0, 256], np.int32), None)
+        q, k, v, g, beta = draw_tokens(rng, 256, 1, 1, D, D, io)
+        return GDNInputs(name, io, q, k, v, g, beta, np.array([0, 256], np.int32), None)
     if i == 1:
-        q, k, v, g, beta = draw_tokens(rng, 4096, 16, 16, D, D, "bf16")
-        return GDNInputs(name, "bf16", q, k, v, g, beta, np.array([0, 4096], np.int32), None)
+        q, k, v, g, beta = draw_tokens(rng, 4096, 16, 16, D, D, io)
+        return GDNInputs(name, io, q, k, v, g, beta, np.array([0, 4096], np.int32), None)
     if i == 2:
-        q, k, v, g, beta = draw_tokens(rng, 16384, 16, 32, D, D, "bf16", g_shift=2.0)
-        return GDNInputs(name, "bf16", q, k, v, g, beta, np.array([0, 16384], np.int32), None)
+        q, k, v, g, beta = draw_tokens(rng, 16384, 16, 32, D, D, io, g_shift=2.0)
+        return GDNInputs(name, io, q, k, v, g, beta, np.array([0, 16384], np.int32), None)
     if i == 3:
         # lengths are drawn first because they fix the packed token count
         lengths = rng.integers(512, 8192, size=8, endpoint=True)
         cu = np.zeros(9, dtype=np.int32)
         cu[1:] = np.cumsum(lengths)
         T = int(cu[-1])
-        q, k, v, g, beta = draw_tokens(rng, T, 16, 16, D, D, "bf16")
+        q, k, v, g, beta = draw_tokens(rng, T, 16, 16, D, D, io)
         s0 = (rng.standard_normal((8, 16, D, D), dtype=np.float32) * np.float32(0.02)).astype(np.float32)
-        return GDNInputs(name, "bf16", q, k, v, g, beta, cu, s0)
+        return GDNInputs(name, io, q, k, v, g, beta, cu, s0)
     if i == 4:
-        q, k, v, g, beta = draw_tokens(rng, 65536, 32, 32, D, D, "bf16")
+        q, k, v, g, beta = draw_tokens(rng, 65536, 32, 32, D, D, io)
         steps = 256 if decode_steps is None else decode_steps
-        dq, dk_, dv, dg, db = draw_tokens(rng, steps, 32, 32, D, D, "bf16")
+        dq, dk_, dv, dg, db = draw_tokens(rng, steps, 32, 32, D, D, io)
         dec = dict(q=dq, k=dk_, v=dv, g=dg, beta=db, steps=steps)
-        return GDNInputs(name, "bf16", q, k, v, g, beta, np.array([0, 65536], np.int32), None, dec)
+        return GDNInputs(name, io, q, k, v, g, beta, np.array([0, 65536], np.int32), None, dec)
     raise KeyError(i)
 
 

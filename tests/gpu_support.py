@@ -11,6 +11,8 @@ Tolerances (the acceptance bar for this path):
     applies to the kernel's own error: max_i (|x_i - x_oracle_i| - |x_i| / 255) where
     |x_i| / 255 bounds the round-to-nearest-even storage rounding of the kernel's fp32
     result y_i (|y - bf16(y)| <= 2^-8 |y| and |y| <= |x| / (1 - 2^-8)).
+  * fp16 I/O: the same bar as bf16, with the fp16 storage allowance |x_i| / 2047 + 2^-25
+    (|y - fp16(y)| <= 2^-11 |y| for normal values, at most 2^-25 below the normal range).
 NMSE = sum (x - x_ref)^2 / sum x_ref^2 and the plain max |x - x_ref| / rms are
 reported beside them.
 """
@@ -21,11 +23,14 @@ import torch
 
 TOL_F32_ABS = 1e-3
 TOL_BF16_REL_RMS = 2e-2
+TOL_16BIT_REL_RMS = TOL_BF16_REL_RMS
+
+TORCH_IO = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
 
 
 def to_device(x, device="cuda"):
     """Seeded numpy inputs -> device tensors in the storage types the library takes."""
-    io = torch.bfloat16 if x.io == "bf16" else torch.float32
+    io = TORCH_IO[x.io]
 
     def t(a, dt):
         return torch.from_numpy(np.ascontiguousarray(a)).to(device=device, dtype=dt)
@@ -41,11 +46,22 @@ def to_f64(t: torch.Tensor) -> np.ndarray:
     return t.detach().to("cpu", torch.float64).numpy()
 
 
-def error_stats(got: np.ndarray, ref: np.ndarray, bf16_storage: bool = False) -> dict:
+def storage_allowance(got: np.ndarray, storage) -> np.ndarray:
+    """Bound on |y - round(y)| for the kernel's fp32 result y behind each stored value
+    got (storage: None / False = not rounded, 'bf16' or True, 'f16')."""
+    if storage in ("bf16", True):
+        return np.abs(got) / 255.0
+    if storage == "f16":
+        return np.abs(got) / 2047.0 + 2.0 ** -25
+    return np.zeros_like(got)
+
+
+def error_stats(got: np.ndarray, ref: np.ndarray, storage=None) -> dict:
+    """storage: the storage rounding to allow for, as in storage_allowance."""
     diff = np.abs(got - ref)
     rms = float(np.sqrt(np.mean(ref ** 2))) if ref.size else 0.0
     mx = float(diff.max()) if diff.size else 0.0
-    kernel_err = diff - np.abs(got) / 255.0 if bf16_storage else diff
+    kernel_err = diff - storage_allowance(got, storage)
     kmx = float(max(kernel_err.max(), 0.0)) if diff.size else 0.0
     den = float(np.sum(ref ** 2))
     return dict(max_abs=mx, rms_ref=rms, rel_rms=(mx / rms if rms > 0 else mx),
@@ -54,12 +70,12 @@ def error_stats(got: np.ndarray, ref: np.ndarray, bf16_storage: bool = False) ->
                 finite=bool(np.all(np.isfinite(got))))
 
 
-def check(name: str, got: np.ndarray, ref: np.ndarray, io: str, stored_bf16=None) -> dict:
-    """stored_bf16: whether `got` was stored as bf16 (default: io == 'bf16' and the
-    name does not mention a state)."""
-    if stored_bf16 is None:
-        stored_bf16 = io == "bf16" and "state" not in name
-    s = error_stats(got, ref, bf16_storage=stored_bf16)
+def check(name: str, got: np.ndarray, ref: np.ndarray, io: str, stored=None) -> dict:
+    """stored: the 16-bit type `got` was stored in, or None / False (default: io
+    when io is 16-bit and the name does not mention a state)."""
+    if stored is None:
+        stored = io if io != "f32" and "state" not in name else None
+    s = error_stats(got, ref, storage=stored)
     print(f"  {name}: max_abs={s['max_abs']:.3e} rms_ref={s['rms_ref']:.3e} "
           f"max/rms={s['rel_rms']:.3e} kernel/rms={s['kernel_rel_rms']:.3e} "
           f"nmse={s['nmse']:.3e}", flush=True)

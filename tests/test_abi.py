@@ -76,6 +76,8 @@ def _prefill(lib, **over):
     (dict(N=2), 1, "cu_seqlens"),
     (dict(q=None), 1, "non-null"),
     (dict(io=7), 1, "io_dtype"),
+    (dict(io=3), 1, "io_dtype"),
+    (dict(io=2, k=0x20008), 1, "aligned"),
     (dict(k=0x20008), 1, "aligned"),
     (dict(o=0x30000), 1, "overlaps"),
     (dict(s0=0x70000, fs=0x70100), 1, "final_state overlaps"),
@@ -110,3 +112,7 @@ def test_plan(lib):
     plan32 = gdn.prefill_plan(1, 1, gdn.GDN_F32, lib=lib)
     assert 0 < plan32["lds_bytes"] <= 160 * 1024
     assert plan32["threads_per_workgroup"] % 64 == 0
+    # fp16 I/O runs the same pipelined kernel as bf16, with the same launch shape
+    assert gdn.prefill_plan(1, 16, gdn.GDN_F16, lib=lib) == plan
+    with pytest.raises(gdn.GDNError):
+        gdn.prefill_plan(1, 16, 3, lib=lib)

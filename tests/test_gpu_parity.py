@@ -2,7 +2,8 @@
 
 Every workload is compared at its full size (the oracle finishes all of them in
 seconds on the host cores), plus small ragged/edge shapes that span several chunks
-and short tails.  Bar: fp32 I/O max abs <= 1e-3; bf16 I/O max abs / rms <= 2e-2,
+and short tails, with fp32, bf16 and fp16 storage of q, k, v, o.  Bar: fp32 I/O max
+abs <= 1e-3; 16-bit I/O max abs / rms <= 2e-2 beside the outputs' storage rounding,
 outputs and final states separately.
 """
 import numpy as np
@@ -10,7 +11,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_support import check, to_device, to_f64
+from gpu_support import TORCH_IO, check, to_device, to_f64
 from linear_attention_chunked_gdn_amd import gdn, inputs
 
 pytestmark = pytest.mark.gpu
@@ -37,9 +38,10 @@ def _oracle(x):
     return oracle.recurrent(x.q, x.k, x.v, x.g, x.beta, x.initial_state, x.cu_seqlens)
 
 
-@pytest.mark.parametrize("wid", [0, 1, 2, 3])
-def test_workload_prefill(wid):
-    x = inputs.make_workload(wid)
+@pytest.mark.parametrize("wid,io", [(0, None), (1, None), (2, None), (3, None),
+                                    (0, "f16"), (1, "f16"), (3, "f16")])
+def test_workload_prefill(wid, io):
+    x = inputs.make_workload(wid, io=io)
     print(f"\nworkload {wid} {x.name}: N={x.N} T={x.T_tot} Hk={x.Hk} Hv={x.Hv} io={x.io}", flush=True)
     o, fs = _run(x)
     ro, rf = _oracle(x)
@@ -47,8 +49,9 @@ def test_workload_prefill(wid):
     check("final_state", to_f64(fs), rf, x.io)
 
 
-def test_workload_long_prefill_then_decode():
-    x = inputs.make_workload(4)
+@pytest.mark.parametrize("io", ["bf16", "f16"])
+def test_workload_long_prefill_then_decode(io):
+    x = inputs.make_workload(4, io=io, decode_steps=None if io == "bf16" else 64)
     print(f"\nworkload 4 {x.name}: T={x.T_tot} H={x.Hv}, then {x.decode['steps']} decode steps",
           flush=True)
     o, fs = _run(x)
@@ -57,7 +60,7 @@ def test_workload_long_prefill_then_decode():
     check("state after prefill", to_f64(fs), rf, x.io)
     del o
     dec = x.decode
-    dq, dk, dv = (torch.from_numpy(dec[n]).to(DEV, torch.bfloat16) for n in ("q", "k", "v"))
+    dq, dk, dv = (torch.from_numpy(dec[n]).to(DEV, TORCH_IO[x.io]) for n in ("q", "k", "v"))
     dg, db = (torch.from_numpy(dec[n]).to(DEV, torch.float32) for n in ("g", "beta"))
     state = fs
     st_ref = rf
@@ -85,7 +88,7 @@ SMALL = [
 ]
 
 
-@pytest.mark.parametrize("io", ["bf16", "f32"])
+@pytest.mark.parametrize("io", ["bf16", "f16", "f32"])
 @pytest.mark.parametrize("case", range(len(SMALL)))
 def test_small_shapes(io, case):
     lengths, Hk, Hv, init_std = SMALL[case]
@@ -98,7 +101,7 @@ def test_small_shapes(io, case):
     check("final_state", to_f64(fs), rf, io)
 
 
-@pytest.mark.parametrize("io", ["bf16", "f32"])
+@pytest.mark.parametrize("io", ["bf16", "f16", "f32"])
 def test_strong_decay_long_chunks(io):
     # g = -softplus(N(0,1) + 4): the cumulative gate reaches about -270 inside one chunk,
     # far past fp32's exponent range, so decays must only be formed as masked differences
@@ -153,8 +156,9 @@ def test_state_passing_matches_one_call():
     assert torch.equal(f2, f_all)
 
 
-def test_deterministic():
-    x = inputs.make_workload(1)
+@pytest.mark.parametrize("io", ["bf16", "f16"])
+def test_deterministic(io):
+    x = inputs.make_workload(1, io=io)
     d = to_device(x, DEV)
     a = gdn.prefill(d["q"], d["k"], d["v"], d["g"], d["beta"])
     b = gdn.prefill(d["q"], d["k"], d["v"], d["g"], d["beta"])
@@ -162,8 +166,19 @@ def test_deterministic():
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
 
 
+def test_f16_values_near_the_top_of_its_range():
+    # fp16 has 5 exponent bits: v scaled to |v| ~ 1e3 keeps outputs and the state's fp16
+    # copy far above the subnormal range and far below 65504
+    x = inputs.make_custom(11, [130, 64], 1, 2, io="f16", init_std=50.0)
+    x.v = inputs.round_to_f16(x.v * np.float32(1000.0))
+    o, fs = _run(x)
+    ro, rf = _oracle(x)
+    check("o", to_f64(o), ro, "f16")
+    check("final_state", to_f64(fs), rf, "f16")
+
+
 def test_decode_step_small_fp32_and_gqa():
-    for io in ("f32", "bf16"):
+    for io in ("f32", "bf16", "f16"):
         x = inputs.make_custom(9, [1, 1, 1], 2, 4, io=io, init_std=0.3)
         d = to_device(x, DEV)
         st = d["initial_state"].clone()
