@@ -12,6 +12,11 @@ Three independent fp64 evaluations of the same function are provided:
 * ``bruteforce`` -- the closed product form of the recurrence with explicit
   Dk x Dk transition matrices (numpy), for tiny sizes only.
 
+Every function also takes a per-key-channel gate g of shape [T, Hv, Dk] (the KDA
+variant: the head's scalar decay alpha_t becomes Diag(a_t) on the key index of S,
+applied before the erase) and then evaluates that rule; a gate of shape [T, Hv] is
+the gated delta rule.
+
 Sources: "Empowering Hybrid Attention Models on NPUs" (section 2.1 for the
 recurrence and the Map-Reduce-Map operators #1-#6, section 5 for the chunk-first
 order "5-read, 6, 5-update" and the rewrite that factors the inverse out of the
@@ -52,6 +57,10 @@ def _bind(lib):
     lib.gdn_oracle_decode_step_f64.argtypes = [dp, dp, dp, dp, dp, dp, i64, i64, i64, i64, i64,
                                                dp, ctypes.c_int]
     lib.gdn_oracle_decode_step_f64.restype = ctypes.c_int
+    lib.gdn_oracle_kda_prefill_f64.argtypes = lib.gdn_oracle_prefill_f64.argtypes
+    lib.gdn_oracle_kda_prefill_f64.restype = ctypes.c_int
+    lib.gdn_oracle_kda_decode_step_f64.argtypes = lib.gdn_oracle_decode_step_f64.argtypes
+    lib.gdn_oracle_kda_decode_step_f64.restype = ctypes.c_int
     lib.gdn_oracle_max_threads.argtypes = []
     lib.gdn_oracle_max_threads.restype = ctypes.c_int
     return lib
@@ -86,13 +95,22 @@ def _cu(cu_seqlens, T: int) -> np.ndarray:
     return np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64))
 
 
+def _per_channel(g, rows: int, Hv: int, Dk: int) -> bool:
+    """True for a per-key-channel gate [rows, Hv, Dk], False for a per-head gate [rows, Hv]."""
+    if g.shape == (rows, Hv):
+        return False
+    if g.shape == (rows, Hv, Dk):
+        return True
+    raise ValueError(f"gate shape {g.shape} is neither {(rows, Hv)} nor {(rows, Hv, Dk)}")
+
+
 def recurrent(q, k, v, g, beta, initial_state=None, cu_seqlens=None, nthreads: int = 0,
               lib=None):
     """Token-by-token gated delta rule in fp64 (the definition).
 
-    q, k: [T, Hk, Dk]; v: [T, Hv, Dv]; g, beta: [T, Hv]; initial_state: [N, Hv, Dv, Dk]
-    or None; cu_seqlens: [N+1] or None (one sequence).  Returns (o [T, Hv, Dv],
-    final_state [N, Hv, Dv, Dk]) as fp64 arrays.
+    q, k: [T, Hk, Dk]; v: [T, Hv, Dv]; g: [T, Hv] (or [T, Hv, Dk] per key channel);
+    beta: [T, Hv]; initial_state: [N, Hv, Dv, Dk] or None; cu_seqlens: [N+1] or None
+    (one sequence).  Returns (o [T, Hv, Dv], final_state [N, Hv, Dv, Dk]) as fp64 arrays.
     """
     lib = lib if lib is not None else load_library()
     q, k, v, g, beta = map(_f64, (q, k, v, g, beta))
@@ -103,29 +121,33 @@ def recurrent(q, k, v, g, beta, initial_state=None, cu_seqlens=None, nthreads: i
     s0 = None if initial_state is None else _f64(initial_state)
     if s0 is not None and s0.shape != (N, Hv, Dv, Dk):
         raise ValueError(f"initial_state shape {s0.shape} != {(N, Hv, Dv, Dk)}")
+    fn = (lib.gdn_oracle_kda_prefill_f64 if _per_channel(g, T, Hv, Dk)
+          else lib.gdn_oracle_prefill_f64)
     o = np.zeros((T, Hv, Dv), dtype=np.float64)
     fs = np.zeros((N, Hv, Dv, Dk), dtype=np.float64)
-    rc = lib.gdn_oracle_prefill_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(s0),
-                                    _ptr(cu, ctypes.c_int64), N, T, Hk, Hv, Dk, Dv,
-                                    _ptr(o), _ptr(fs), int(nthreads))
+    rc = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(s0),
+            _ptr(cu, ctypes.c_int64), N, T, Hk, Hv, Dk, Dv, _ptr(o), _ptr(fs), int(nthreads))
     if rc != 0:
-        raise ValueError(f"gdn_oracle_prefill_f64 returned {rc}")
+        raise ValueError(f"oracle prefill returned {rc}")
     return o, fs
 
 
 def decode_step(q, k, v, g, beta, state, nthreads: int = 0, lib=None):
-    """One decode token per sequence.  q, k: [B, Hk, Dk]; v: [B, Hv, Dv]; g, beta: [B, Hv];
-    state: [B, Hv, Dv, Dk].  Returns (o [B, Hv, Dv], new_state); the input is not modified."""
+    """One decode token per sequence.  q, k: [B, Hk, Dk]; v: [B, Hv, Dv]; g: [B, Hv] (or
+    [B, Hv, Dk] per key channel); beta: [B, Hv]; state: [B, Hv, Dv, Dk].  Returns
+    (o [B, Hv, Dv], new_state); the input is not modified."""
     lib = lib if lib is not None else load_library()
     q, k, v, g, beta = map(_f64, (q, k, v, g, beta))
     st = np.array(state, dtype=np.float64, copy=True, order="C")
     B, Hk, Dk = q.shape
     Hv, Dv = v.shape[1], v.shape[2]
+    fn = (lib.gdn_oracle_kda_decode_step_f64 if _per_channel(g, B, Hv, Dk)
+          else lib.gdn_oracle_decode_step_f64)
     o = np.zeros((B, Hv, Dv), dtype=np.float64)
-    rc = lib.gdn_oracle_decode_step_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(st),
-                                        B, Hk, Hv, Dk, Dv, _ptr(o), int(nthreads))
+    rc = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(st), B, Hk, Hv, Dk, Dv,
+            _ptr(o), int(nthreads))
     if rc != 0:
-        raise ValueError(f"gdn_oracle_decode_step_f64 returned {rc}")
+        raise ValueError(f"oracle decode step returned {rc}")
     return o, st
 
 
@@ -181,12 +203,44 @@ def _chunk_step(S, Qc, Kc, Vc, gc, bc):
     return O, S_next
 
 
+# Per-key-channel gate (KDA).  Gamma = cumsum(g) is now [n_c, Dk] and every decay is a
+# vector over key channels, formed only as differences Gamma_r - Gamma_s with r >= s:
+#   A[r, s] = beta_r sum_j K[r, j] K[s, j] exp(Gamma[r, j] - Gamma[s, j])      (r > s)
+#   P[r, s] = sum_j Q[r, j] K[s, j] exp(Gamma[r, j] - Gamma[s, j])             (r >= s)
+#   W = T diag(beta) (K (.) exp(Gamma)),  U = T diag(beta) V,  v_c = U - W S^T
+#   O = (Q (.) exp(Gamma)) S^T + P v_c
+#   S <- S Diag(exp(Gamma_last)) + v_c^T (K (.) exp(Gamma_last - Gamma))
+# With every channel's gate equal this is the chunk step above.
+
+def _chunk_step_kda(S, Qc, Kc, Vc, Gc, bc):
+    """One chunk with a per-key-channel gate Gc [n_c, Dk].  Returns (O_c, S_next)."""
+    n_c = Gc.shape[0]
+    Gam = np.cumsum(Gc, axis=0)                           # op #1, per channel
+    r_idx, s_idx = np.tril_indices(n_c)                   # r >= s
+    Dpair = np.exp(Gam[r_idx] - Gam[s_idx])               # [pairs, Dk], masked before exp
+    P = np.zeros((n_c, n_c), dtype=np.float64)
+    P[r_idx, s_idx] = np.einsum("pj,pj,pj->p", Qc[r_idx], Kc[s_idx], Dpair)
+    KK = np.zeros((n_c, n_c), dtype=np.float64)
+    KK[r_idx, s_idx] = np.einsum("pj,pj,pj->p", Kc[r_idx], Kc[s_idx], Dpair)
+    A = np.tril(bc[:, None] * KK, k=-1)                   # op #2
+    T = forward_substitution_inverse(A)                   # op #3
+    gam = np.exp(Gam)                                     # [n_c, Dk]
+    W = T @ (bc[:, None] * (Kc * gam))                    # op #4
+    U = T @ (bc[:, None] * Vc)
+    v_c = U - W @ S.T                                     # op #5-read
+    O = (Qc * gam) @ S.T + P @ v_c                        # op #6
+    lam = np.exp(Gam[-1][None, :] - Gam)                  # [n_c, Dk]
+    S_next = S * gam[-1][None, :] + v_c.T @ (lam * Kc)    # op #5-update
+    return O, S_next
+
+
 def chunked(q, k, v, g, beta, initial_state=None, cu_seqlens=None, chunk_size: int = 64):
     """Chunkwise fp64 evaluation; chunks restart at every sequence start and the last
     chunk of a sequence may be short.  Same arguments and results as ``recurrent``."""
     q, k, v, g, beta = map(_f64, (q, k, v, g, beta))
     T, Hk, Dk = q.shape
     Hv, Dv = v.shape[1], v.shape[2]
+    step = _chunk_step_kda if _per_channel(g, T, Hv, Dk) else _chunk_step
     cu = _cu(cu_seqlens, T)
     N = cu.shape[0] - 1
     o = np.zeros((T, Hv, Dv), dtype=np.float64)
@@ -198,15 +252,16 @@ def chunked(q, k, v, g, beta, initial_state=None, cu_seqlens=None, chunk_size: i
                  else np.array(initial_state[n, h], dtype=np.float64))
             for c0 in range(int(cu[n]), int(cu[n + 1]), chunk_size):
                 c1 = min(c0 + chunk_size, int(cu[n + 1]))
-                O, S = _chunk_step(S, q[c0:c1, hk], k[c0:c1, hk], v[c0:c1, h],
-                                   g[c0:c1, h], beta[c0:c1, h])
+                O, S = step(S, q[c0:c1, hk], k[c0:c1, hk], v[c0:c1, h],
+                            g[c0:c1, h], beta[c0:c1, h])
                 o[c0:c1, h] = O
             fs[n, h] = S
     return o, fs
 
 
 # --------------------------------------------------------------------------------------
-# Closed product form (numpy, fp64), tiny sizes only.  With M_r = alpha_r (I - beta_r k_r k_r^T):
+# Closed product form (numpy, fp64), tiny sizes only.  With M_r = alpha_r (I - beta_r k_r k_r^T)
+# (per key channel: M_r = Diag(a_r) (I - beta_r k_r k_r^T)):
 #   S_t = S_0 M_1 M_2 ... M_t + sum_{s<=t} beta_s v_s k_s^T M_{s+1} ... M_t,   o_t = S_t q_t.
 # Each S_t is rebuilt from scratch from explicit Dk x Dk products, so nothing is carried
 # from one token to the next.
@@ -216,6 +271,7 @@ def bruteforce(q, k, v, g, beta, initial_state=None, cu_seqlens=None):
     q, k, v, g, beta = map(_f64, (q, k, v, g, beta))
     T, Hk, Dk = q.shape
     Hv, Dv = v.shape[1], v.shape[2]
+    per_channel = _per_channel(g, T, Hv, Dk)
     cu = _cu(cu_seqlens, T)
     N = cu.shape[0] - 1
     o = np.zeros((T, Hv, Dv), dtype=np.float64)
@@ -227,7 +283,9 @@ def bruteforce(q, k, v, g, beta, initial_state=None, cu_seqlens=None):
             hk = h % Hk
             S0 = (np.zeros((Dv, Dk)) if initial_state is None
                   else np.array(initial_state[n, h], dtype=np.float64))
-            M = [np.exp(g[r, h]) * (I - beta[r, h] * np.outer(k[r, hk], k[r, hk]))
+            decay = ((lambda r: np.diag(np.exp(g[r, h]))) if per_channel
+                     else (lambda r: np.exp(g[r, h]) * I))
+            M = [decay(r) @ (I - beta[r, h] * np.outer(k[r, hk], k[r, hk]))
                  for r in range(start, end)]
 
             def prod(a, b):  # M_a ... M_b (1-based within the sequence), identity if empty

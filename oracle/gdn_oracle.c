@@ -32,6 +32,9 @@
  * output product S q.  This is a plain evaluation of the same expression; nothing
  * is chunked, reordered across tokens or approximated.
  *
+ * A second pair of entry points (gdn_oracle_kda_*) evaluates the same rule with one
+ * decay per key channel instead of one per head; see kda_token_step below.
+ *
  * Parallelism: independent (sequence, value head) chains run on OpenMP threads.
  */
 #include <math.h>
@@ -165,6 +168,135 @@ int gdn_oracle_decode_step_f64(const double *q, const double *k, const double *v
                        exp(g[b * Hv + h]), beta[b * Hv + h], Dk, Dv, Sk, Sk + Dv);
         memcpy(o + (b * Hv + h) * Dv, Sk + Dv, sizeof(double) * (size_t)Dv);
         free(Sk);
+    }
+    return failed ? -2 : 0;
+}
+
+/*
+ * Per-key-channel decay (the KDA variant of the same delta rule, whose gate is
+ * "fine-grained": one decay per key channel instead of one per head, so its
+ * cumulative gate is Dk times larger -- "Empowering Hybrid Attention Models on NPUs",
+ * section 2.1 and the peak-memory discussion of section 7.5).  The scalar alpha_t of
+ * the gated delta rule becomes the diagonal matrix Diag(a_t), a_t[j] = exp(g[t, h, j]),
+ * acting on the key index of S, applied before the erase exactly as alpha_t is:
+ *
+ *     S <- S Diag(a_t) (I - b k_t k_t^T) + b v_t k_t^T,     o_t = S q_t
+ *
+ * evaluated as  D = S Diag(a_t);  u = D k_t;  S = D - b u k_t^T + b v_t k_t^T.
+ */
+static void kda_token_step(double *S, const double *kt, const double *vt, const double *qt,
+                           const double *gt, double b, int64_t Dk, int64_t Dv,
+                           double *a, double *u, double *ot)
+{
+    for (int64_t j = 0; j < Dk; ++j) a[j] = exp(gt[j]);
+    /* S <- S Diag(a): column j (key channel j) decays by a[j] */
+    for (int64_t i = 0; i < Dv; ++i)
+        for (int64_t j = 0; j < Dk; ++j) S[i * Dk + j] *= a[j];
+    /* u = (S Diag(a)) k_t */
+    for (int64_t i = 0; i < Dv; ++i) {
+        double acc = 0.0;
+        for (int64_t j = 0; j < Dk; ++j) acc += S[i * Dk + j] * kt[j];
+        u[i] = acc;
+    }
+    /* S <- S - b u k^T + b v k^T */
+    for (int64_t i = 0; i < Dv; ++i) {
+        const double erase = b * u[i];
+        const double write = b * vt[i];
+        for (int64_t j = 0; j < Dk; ++j)
+            S[i * Dk + j] = S[i * Dk + j] - erase * kt[j] + write * kt[j];
+    }
+    /* o_t = S q_t with the updated state */
+    for (int64_t i = 0; i < Dv; ++i) {
+        double acc = 0.0;
+        for (int64_t j = 0; j < Dk; ++j) acc += S[i * Dk + j] * qt[j];
+        ot[i] = acc;
+    }
+}
+
+/*
+ * Packed variable-length prefill with per-key-channel decay.  Arguments as for
+ * gdn_oracle_prefill_f64 except  g [T_tot, Hv, Dk]  (natural log of each channel's
+ * decay).
+ */
+int gdn_oracle_kda_prefill_f64(const double *q, const double *k, const double *v,
+                               const double *g, const double *beta,
+                               const double *initial_state, const int64_t *cu_seqlens,
+                               int64_t N, int64_t T_tot, int64_t Hk, int64_t Hv,
+                               int64_t Dk, int64_t Dv,
+                               double *o, double *final_state, int nthreads)
+{
+    if (N < 1 || T_tot < 0 || Hk < 1 || Hv < 1 || Dk < 1 || Dv < 1 || (Hv % Hk) != 0)
+        return -1;
+    if (!cu_seqlens || cu_seqlens[0] != 0 || cu_seqlens[N] != T_tot) return -1;
+    for (int64_t n = 0; n < N; ++n)
+        if (cu_seqlens[n + 1] < cu_seqlens[n]) return -1;
+    if (T_tot > 0 && (!q || !k || !v || !g || !beta || !o)) return -1;
+
+    int failed = 0;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+    const int64_t pairs = N * Hv;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t p = 0; p < pairs; ++p) {
+        const int64_t n = p / Hv, h = p % Hv, hk = h % Hk;
+        double *S = (double *)malloc(sizeof(double) * (size_t)(Dv * Dk + 2 * Dv + Dk));
+        if (!S) {
+#pragma omp atomic write
+            failed = 1;
+            continue;
+        }
+        double *u = S + Dv * Dk;
+        double *ot = u + Dv;
+        double *a = ot + Dv;
+        if (initial_state)
+            memcpy(S, initial_state + (n * Hv + h) * Dv * Dk, sizeof(double) * (size_t)(Dv * Dk));
+        else
+            memset(S, 0, sizeof(double) * (size_t)(Dv * Dk));
+        for (int64_t t = cu_seqlens[n]; t < cu_seqlens[n + 1]; ++t) {
+            kda_token_step(S, k + (t * Hk + hk) * Dk, v + (t * Hv + h) * Dv,
+                           q + (t * Hk + hk) * Dk, g + (t * Hv + h) * Dk,
+                           beta[t * Hv + h], Dk, Dv, a, u, ot);
+            memcpy(o + (t * Hv + h) * Dv, ot, sizeof(double) * (size_t)Dv);
+        }
+        if (final_state)
+            memcpy(final_state + (n * Hv + h) * Dv * Dk, S, sizeof(double) * (size_t)(Dv * Dk));
+        free(S);
+    }
+    return failed ? -2 : 0;
+}
+
+/* One decoding token per sequence with per-key-channel decay: g [B, Hv, Dk]. */
+int gdn_oracle_kda_decode_step_f64(const double *q, const double *k, const double *v,
+                                   const double *g, const double *beta, double *state,
+                                   int64_t B, int64_t Hk, int64_t Hv, int64_t Dk, int64_t Dv,
+                                   double *o, int nthreads)
+{
+    if (B < 1 || Hk < 1 || Hv < 1 || Dk < 1 || Dv < 1 || (Hv % Hk) != 0) return -1;
+    if (!q || !k || !v || !g || !beta || !state || !o) return -1;
+    int failed = 0;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+    const int64_t pairs = B * Hv;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t p = 0; p < pairs; ++p) {
+        const int64_t b = p / Hv, h = p % Hv, hk = h % Hk;
+        double *w = (double *)malloc(sizeof(double) * (size_t)(2 * Dv + Dk));
+        if (!w) {
+#pragma omp atomic write
+            failed = 1;
+            continue;
+        }
+        kda_token_step(state + (b * Hv + h) * Dv * Dk, k + (b * Hk + hk) * Dk,
+                       v + (b * Hv + h) * Dv, q + (b * Hk + hk) * Dk, g + (b * Hv + h) * Dk,
+                       beta[b * Hv + h], Dk, Dv, w + 2 * Dv, w, w + Dv);
+        memcpy(o + (b * Hv + h) * Dv, w + Dv, sizeof(double) * (size_t)Dv);
+        free(w);
     }
     return failed ? -2 : 0;
 }

@@ -27,7 +27,8 @@ def _rand_unit(rng, shape):
     return x / np.linalg.norm(x, axis=-1, keepdims=True)
 
 
-def random_case(seed, lengths, Hk, Hv, Dk, Dv, init=True, g_shift=0.0):
+def random_case(seed, lengths, Hk, Hv, Dk, Dv, init=True, g_shift=0.0, kda=False):
+    """kda: one gate per key channel, g [T, Hv, Dk], instead of one per head."""
     rng = np.random.default_rng(seed)
     T = int(sum(lengths))
     cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
@@ -35,7 +36,7 @@ def random_case(seed, lengths, Hk, Hv, Dk, Dv, init=True, g_shift=0.0):
     k = _rand_unit(rng, (T, Hk, Dk))
     v = rng.standard_normal((T, Hv, Dv))
     beta = 1.0 / (1.0 + np.exp(-rng.standard_normal((T, Hv))))
-    x = rng.standard_normal((T, Hv)) + g_shift
+    x = rng.standard_normal((T, Hv, Dk) if kda else (T, Hv)) + g_shift
     g = -(np.maximum(x, 0) + np.log1p(np.exp(-np.abs(x))))
     s0 = rng.standard_normal((len(lengths), Hv, Dv, Dk)) * 0.5 if init else None
     return dict(q=q, k=k, v=v, g=g, beta=beta, initial_state=s0, cu_seqlens=cu)
@@ -47,8 +48,8 @@ def _close(a, b, tol, what):
 
 
 # 1. hand-worked example (tests/golden/hand_worked_d2_t2.json)
-def pin_hand_example(rec):
-    with open(os.path.join(GOLDEN, "hand_worked_d2_t2.json")) as f:
+def pin_hand_example(rec, name="hand_worked_d2_t2.json"):
+    with open(os.path.join(GOLDEN, name)) as f:
         gold = json.load(f)
     inp = {k_: np.array(v_, dtype=np.float64) for k_, v_ in gold["inputs"].items()}
     o, fs = rec(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["initial_state"])
@@ -153,8 +154,8 @@ def pin_chunked(rec, big=False):
 
 
 # 7. state passing: prefill(x) == prefill(second part, init = final(prefill(first part)))
-def pin_state_passing(rec):
-    c = random_case(11, [90], 2, 4, 8, 6)
+def pin_state_passing(rec, kda=False):
+    c = random_case(11, [90], 2, 4, 8, 6, kda=kda)
     o, fs = rec(**c)
     cut = 37
     first = {kk: (vv[:cut] if kk in ("q", "k", "v", "g", "beta") else vv) for kk, vv in c.items()}
@@ -169,9 +170,9 @@ def pin_state_passing(rec):
 
 
 # 8. prefill of T tokens == prefill of T-m tokens followed by m single-token decode steps
-def pin_decode(rec, decode=None):
+def pin_decode(rec, decode=None, kda=False):
     decode = decode or oracle.decode_step
-    c = random_case(12, [40], 2, 4, 8, 6)
+    c = random_case(12, [40], 2, 4, 8, 6, kda=kda)
     o, fs = rec(**c)
     m = 5
     pre = {kk: (vv[:-m] if kk in ("q", "k", "v", "g", "beta") else vv) for kk, vv in c.items()}
@@ -185,9 +186,9 @@ def pin_decode(rec, decode=None):
 
 
 # 9. packed variable-length batch == each sequence run alone (zero-length included)
-def pin_varlen(rec):
+def pin_varlen(rec, kda=False):
     lengths = [13, 0, 29, 1, 20]
-    c = random_case(13, lengths, 1, 2, 6, 5)
+    c = random_case(13, lengths, 1, 2, 6, 5, kda=kda)
     o, fs = rec(**c)
     cu = c["cu_seqlens"]
     for n in range(len(lengths)):
@@ -203,8 +204,8 @@ def pin_varlen(rec):
 
 # 10. GQA: value head h reads key/query head h % Hk == the same run with keys/queries
 #     replicated explicitly to Hv heads
-def pin_gqa(rec):
-    c = random_case(14, [25], 2, 6, 5, 4)
+def pin_gqa(rec, kda=False):
+    c = random_case(14, [25], 2, 6, 5, 4, kda=kda)
     o, fs = rec(**c)
     rep = dict(c)
     idx = [h % 2 for h in range(6)]
@@ -216,9 +217,9 @@ def pin_gqa(rec):
 
 
 # 11. linearity in (v, S_0) jointly, and value-channel permutation equivariance
-def pin_linearity_and_permutation(rec):
-    c = random_case(15, [30], 1, 2, 6, 5)
-    d = random_case(16, [30], 1, 2, 6, 5)
+def pin_linearity_and_permutation(rec, kda=False):
+    c = random_case(15, [30], 1, 2, 6, 5, kda=kda)
+    d = random_case(16, [30], 1, 2, 6, 5, kda=kda)
     oc, fc = rec(**c)
     mix = dict(c)
     mix["v"] = c["v"] - 2.5 * d["v"]
@@ -236,6 +237,139 @@ def pin_linearity_and_permutation(rec):
     _close(fp, fc[:, :, perm, :], 1e-13, "permuted value channels (states)")
 
 
+# 12. permuting the key channels (of q, k, a per-channel gate and the key index of S_0)
+#     permutes the key index of the state and leaves the outputs unchanged
+def pin_key_permutation(rec, kda=False):
+    c = random_case(18, [40], 1, 2, 7, 5, kda=kda)
+    o, fs = rec(**c)
+    perm = np.random.default_rng(19).permutation(7)
+    pc = dict(c)
+    pc["q"], pc["k"] = c["q"][:, :, perm], c["k"][:, :, perm]
+    if kda:
+        pc["g"] = c["g"][:, :, perm]
+    pc["initial_state"] = c["initial_state"][..., perm]
+    op, fp = rec(**pc)
+    _close(op, o, 1e-13, "permuted key channels (outputs)")
+    _close(fp, fs[..., perm], 1e-13, "permuted key channels (states)")
+
+
 ALL_PINS = [pin_hand_example, pin_bruteforce, pin_beta_zero, pin_orthonormal_keys,
             pin_projection, pin_chunked, pin_state_passing, pin_decode, pin_varlen, pin_gqa,
-            pin_linearity_and_permutation]
+            pin_linearity_and_permutation, pin_key_permutation]
+
+
+# --------------------------------------------------------------------------------------
+# Per-key-channel gate (KDA).  The pages give this variant's gate only as one decay per
+# key channel; the reading pinned here is S_t = S_{t-1} Diag(a_t) (I - b_t k_t k_t^T)
+# + b_t v_t k_t^T, o_t = S_t q_t.
+# --------------------------------------------------------------------------------------
+
+# K1. hand-worked example (tests/golden/kda_hand_worked_d2_t2.json)
+def pin_kda_hand_example(rec):
+    pin_hand_example(rec, "kda_hand_worked_d2_t2.json")
+
+
+# K2. closed product form with M_r = Diag(a_r) (I - b_r k_r k_r^T), varlen + GQA
+def pin_kda_bruteforce(rec):
+    for seed, lengths, Hk, Hv, Dk, Dv in [(31, [5], 1, 1, 3, 4), (32, [3, 0, 6], 2, 4, 5, 3)]:
+        c = random_case(seed, lengths, Hk, Hv, Dk, Dv, kda=True)
+        o, fs = rec(**c)
+        ob, fb = oracle.bruteforce(**c)
+        _close(o, ob, 1e-12, f"kda bruteforce o (seed {seed})")
+        _close(fs, fb, 1e-12, f"kda bruteforce state (seed {seed})")
+
+
+# K3. beta = 0: each key channel (column of S) decays on its own,
+#     S_t = S_0 Diag(exp(Gamma_t)), o_t = S_0 (exp(Gamma_t) * q_t), Gamma_t = sum_{s<=t} g_s
+def pin_kda_beta_zero(rec):
+    c = random_case(33, [120], 1, 2, 6, 5, g_shift=0.5, kda=True)
+    c["beta"] = np.zeros_like(c["beta"])
+    o, fs = rec(**c)
+    Gam = np.cumsum(c["g"], axis=0)                       # [T, Hv, Dk]
+    S0 = c["initial_state"][0]
+    for h in range(2):
+        exp_o = (np.exp(Gam[:, h]) * c["q"][:, 0]) @ S0[h].T
+        _close(o[:, h], exp_o, 1e-12, "kda beta=0 outputs")
+        _close(fs[0, h], S0[h] * np.exp(Gam[-1, h])[None, :], 1e-12, "kda beta=0 final state")
+
+
+# K4. one-hot keys on distinct channels, zero initial state: the erase term vanishes and
+#     each token's write decays with its own channel's gate,
+#     o_t = sum_{s<=t} beta_s exp(Gamma_t[j_s] - Gamma_s[j_s]) q_t[j_s] v_s
+def pin_kda_onehot_keys(rec):
+    T, D = 9, 12
+    c = random_case(34, [T], 1, 1, D, 4, init=False, kda=True)
+    ch = np.random.default_rng(35).permutation(D)[:T]
+    c["k"] = np.zeros((T, 1, D))
+    c["k"][np.arange(T), 0, ch] = 1.0
+    o, fs = rec(**c)
+    Gam = np.cumsum(c["g"][:, 0], axis=0)
+    q, v, b = c["q"][:, 0], c["v"][:, 0], c["beta"][:, 0]
+    for t in range(T):
+        exp_o = sum(b[s] * np.exp(Gam[t, ch[s]] - Gam[s, ch[s]]) * q[t, ch[s]] * v[s]
+                    for s in range(t + 1))
+        _close(o[t, 0], exp_o, 1e-12, f"kda one-hot keys o[{t}]")
+    exp_S = np.zeros((4, D))
+    for s in range(T):
+        exp_S[:, ch[s]] += b[s] * np.exp(Gam[-1, ch[s]] - Gam[s, ch[s]]) * v[s]
+    _close(fs[0, 0], exp_S, 1e-12, "kda one-hot keys final state")
+
+
+# K5. a gate that is the same on every key channel is the gated delta rule's scalar gate
+def pin_kda_uniform_gate_is_gdn(rec):
+    c = random_case(36, [50, 17], 1, 2, 8, 6)             # scalar gate [T, Hv]
+    o, fs = rec(**c)
+    wide = dict(c)
+    wide["g"] = np.repeat(c["g"][:, :, None], 8, axis=2)
+    ow, fw = rec(**wide)
+    _close(ow, o, 1e-12, "uniform per-channel gate outputs")
+    _close(fw, fs, 1e-12, "uniform per-channel gate states")
+
+
+# K6. the chunked per-channel form equals the recurrence, for several chunk sizes, ragged
+#     tails and strong decay (the pairwise per-channel decays are formed only as masked
+#     differences, so |Gamma| far past exp's range inside one chunk is fine)
+def pin_kda_chunked(rec, big=False):
+    cases = [(37, [150], 1, 2, 16, 12, 0.0, (1, 7, 16, 64, 150)),
+             (38, [70, 0, 129], 2, 2, 8, 8, 2.0, (16, 64)),
+             (39, [100], 1, 1, 8, 8, 12.0, (64,))]
+    if big:
+        cases.append((40, [200], 1, 1, 128, 128, 0.0, (64,)))
+    for seed, lengths, Hk, Hv, Dk, Dv, shift, chunk_sizes in cases:
+        c = random_case(seed, lengths, Hk, Hv, Dk, Dv, g_shift=shift, kda=True)
+        o, fs = rec(**c)
+        for cs in chunk_sizes:
+            oc, fc = oracle.chunked(**c, chunk_size=cs)
+            scale = max(1.0, float(np.max(np.abs(o))))
+            _close(o / scale, oc / scale, 1e-11, f"kda chunked o (seed {seed}, C={cs})")
+            _close(fs / scale, fc / scale, 1e-11, f"kda chunked state (seed {seed}, C={cs})")
+
+
+def pin_kda_state_passing(rec):
+    pin_state_passing(rec, kda=True)
+
+
+def pin_kda_decode(rec, decode=None):
+    pin_decode(rec, decode=decode, kda=True)
+
+
+def pin_kda_varlen(rec):
+    pin_varlen(rec, kda=True)
+
+
+def pin_kda_gqa(rec):
+    pin_gqa(rec, kda=True)
+
+
+def pin_kda_linearity_and_permutation(rec):
+    pin_linearity_and_permutation(rec, kda=True)
+
+
+def pin_kda_key_permutation(rec):
+    pin_key_permutation(rec, kda=True)
+
+
+KDA_PINS = [pin_kda_hand_example, pin_kda_bruteforce, pin_kda_beta_zero, pin_kda_onehot_keys,
+            pin_kda_uniform_gate_is_gdn, pin_kda_chunked, pin_kda_state_passing, pin_kda_decode,
+            pin_kda_varlen, pin_kda_gqa, pin_kda_linearity_and_permutation,
+            pin_kda_key_permutation]

@@ -109,6 +109,89 @@ def test_chunked_form_mutant_is_caught(monkeypatch, name, orig, repl):
         oracle_pins.pin_chunked(oracle.recurrent)
 
 
+# Mistakes planted in the per-key-channel (KDA) part of the C oracle only: the text is
+# replaced after the KDA marker, so the gated delta rule above it is left intact.
+KDA_MARK = "static void kda_token_step("
+KDA_C_MUTANTS = [
+    ("kda decay applied to value rows", "S[i * Dk + j] *= a[j];", "S[i * Dk + j] *= a[i % Dk];"),
+    ("kda gate channels reversed", "a[j] = exp(gt[j]);", "a[j] = exp(gt[Dk - 1 - j]);"),
+    ("kda gate read as log2", "a[j] = exp(gt[j]);", "a[j] = exp2(gt[j]);"),
+    ("kda gate indexed per head", "g + (t * Hv + h) * Dk", "g + (t * Hv + h)"),
+    ("kda decode gate indexed per head", "g + (b * Hv + h) * Dk", "g + (b * Hv + h)"),
+    ("kda erase sign flipped", "- erase * kt[j]", "+ erase * kt[j]"),
+    ("kda beta dropped from the erase", "const double erase = b * u[i];",
+     "const double erase = u[i];"),
+    ("kda erase reads the state before the decay", None, "decay-after-erase"),
+    ("kda output read before the update", None, "output-first"),
+]
+
+
+def _mutate_kda(src: str, name: str, orig, repl) -> str:
+    head, tail = src[:src.index(KDA_MARK)], src[src.index(KDA_MARK):]
+    if orig is not None:
+        assert orig in tail, f"mutation anchor for {name!r} not found in the KDA part"
+        return head + tail.replace(orig, repl)
+    dec = tail.index("    /* S <- S Diag(a)")
+    ubl = tail.index("    /* u = (S Diag(a)) k_t */")
+    upd = tail.index("    /* S <- S - b u k^T + b v k^T */")
+    out = tail.index("    /* o_t = S q_t with the updated state */")
+    end = tail.index("}\n", tail.index("ot[i] = acc;", out)) + 2
+    if repl == "decay-after-erase":   # u = S k, then S <- S Diag(a), then the rank-1 terms
+        tail = tail[:dec] + tail[ubl:upd] + tail[dec:ubl] + tail[upd:]
+    else:                             # o = S q before any of the update
+        tail = tail[:dec] + tail[out:end] + tail[dec:out] + tail[end:]
+    return head + tail
+
+
+@pytest.mark.parametrize("name,orig,repl", KDA_C_MUTANTS, ids=[m[0] for m in KDA_C_MUTANTS])
+def test_kda_c_oracle_mutant_is_caught(tmp_path, name, orig, repl):
+    with open(SRC) as f:
+        src = f.read()
+    mutated = _mutate_kda(src, name, orig, repl)
+    assert mutated != src
+    msrc = tmp_path / "mutant.c"
+    msrc.write_text(mutated)
+    lib_path = str(tmp_path / "libmutant.so")
+    oracle.build(out_path=lib_path, src_path=str(msrc))
+    lib = oracle.load_library(lib_path)
+    rec = functools.partial(oracle.recurrent, lib=lib)
+    dec = functools.partial(oracle.decode_step, lib=lib)
+    failed = []
+    with np.errstate(all="ignore"):
+        for pin in oracle_pins.KDA_PINS:
+            try:
+                pin(rec, decode=dec) if pin is oracle_pins.pin_kda_decode else pin(rec)
+            except (AssertionError, ValueError, FloatingPointError) as e:  # noqa: PERF203
+                failed.append((pin.__name__, str(e).splitlines()[0][:100]))
+    assert failed, f"mutant {name!r} passed every KDA pin"
+
+
+KDA_CHUNK_MUTANTS = [
+    ("kda lambda dropped from the state update", "lam = np.exp(Gam[-1][None, :] - Gam)",
+     "lam = np.ones_like(Gam)"),
+    ("kda chunk decay of the carried state dropped", "S_next = S * gam[-1][None, :]",
+     "S_next = S"),
+    ("kda pairwise decay averaged over channels",
+     "Dpair = np.exp(Gam[r_idx] - Gam[s_idx])",
+     "Dpair = np.exp(Gam[r_idx] - Gam[s_idx]).mean(axis=1, keepdims=True)"),
+    ("kda gamma dropped from W", "(bc[:, None] * (Kc * gam))", "(bc[:, None] * Kc)"),
+    ("kda query decay dropped", "(Qc * gam) @ S.T", "Qc @ S.T"),
+    ("kda cumulative gate exclusive", "Gam = np.cumsum(Gc, axis=0)",
+     "Gam = np.cumsum(Gc, axis=0) - Gc"),
+]
+
+
+@pytest.mark.parametrize("name,orig,repl", KDA_CHUNK_MUTANTS, ids=[m[0] for m in KDA_CHUNK_MUTANTS])
+def test_kda_chunked_form_mutant_is_caught(monkeypatch, name, orig, repl):
+    src = textwrap.dedent(inspect.getsource(oracle._chunk_step_kda))
+    assert orig in src, f"mutation anchor for {name!r} not found"
+    ns = dict(oracle.__dict__)
+    exec(compile(src.replace(orig, repl), "<mutant>", "exec"), ns)  # noqa: S102
+    monkeypatch.setattr(oracle, "_chunk_step_kda", ns["_chunk_step_kda"])
+    with np.errstate(all="ignore"), pytest.raises(AssertionError):
+        oracle_pins.pin_kda_chunked(oracle.recurrent)
+
+
 def test_mutation_anchor_list_is_current():
     with open(SRC) as f:
         src = f.read()

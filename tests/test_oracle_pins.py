@@ -11,6 +11,29 @@ def test_recurrent_oracle_pin(pin):
     pin(oracle.recurrent)
 
 
+@pytest.mark.parametrize("pin", oracle_pins.KDA_PINS, ids=lambda p: p.__name__)
+def test_recurrent_oracle_kda_pin(pin):
+    pin(oracle.recurrent)
+
+
+def test_kda_chunked_form_at_full_head_size():
+    oracle_pins.pin_kda_chunked(oracle.recurrent, big=True)
+
+
+def test_kda_forms_match_hand_example():
+    oracle_pins.pin_kda_hand_example(oracle.bruteforce)
+    for cs in (1, 2, 64):
+        oracle_pins.pin_kda_hand_example(
+            lambda *a, **kw: oracle.chunked(*a, **kw, chunk_size=cs))
+
+
+def test_kda_rejects_bad_gate_shape():
+    c = oracle_pins.random_case(41, [6], 1, 1, 4, 4, kda=True)
+    c["g"] = c["g"][:, :, :3]
+    with pytest.raises(ValueError):
+        oracle.recurrent(**c)
+
+
 def test_chunked_form_at_full_head_size():
     # d = 128, chunk 64: the size at which the pages report ~1e-11 agreement
     oracle_pins.pin_chunked(oracle.recurrent, big=True)
