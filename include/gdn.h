@@ -33,6 +33,7 @@
 #ifndef GDN_MI355X_GDN_H
 #define GDN_MI355X_GDN_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -105,6 +106,64 @@ gdn_status gdn_decode_step(const void *q, const void *k, const void *v,
                            const float *g, const float *beta, float *state,
                            int32_t B, int32_t Hk, int32_t Hv, int32_t Dk, int32_t Dv,
                            gdn_dtype io_dtype, void *o, void *stream);
+
+/*
+ * Per-key-channel decay (KDA).  The gate of this variant of the delta rule is "fine
+ * grained": one decay per key channel instead of one per head, so its cumulative gate
+ * is Dk times larger ("Empowering Hybrid Attention Models on NPUs", section 2.1, and
+ * section 7.5 on peak memory).  The scalar alpha_t above becomes Diag(a_t) acting on
+ * the key index of S, applied where alpha_t is (before the erase):
+ *
+ *     S_t = S_{t-1} Diag(a_t) (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,
+ *     o_t = S_t q_t,               a_t[j] = exp(g_t[j]).
+ *
+ * With every channel's g equal this is the gated delta rule above.
+ *
+ * gdn_kda_workspace_size -- device bytes gdn_kda_prefill needs as workspace for these
+ * sizes: one 66,048-byte tile per value head and chunk slot, with T_tot / 64 + N slots
+ * (enough for any packing of N sequences into T_tot tokens).  Host pointer `bytes`.
+ */
+gdn_status gdn_kda_workspace_size(int32_t N, int32_t T_tot, int32_t Hv, int32_t chunk_size,
+                                  size_t *bytes);
+
+/*
+ * gdn_kda_prefill -- packed variable-length chunked prefill with a per-key-channel
+ * decay.  Arguments and conventions as for gdn_prefill, except:
+ *
+ *   g              [T_tot, Hv, Dk]  fp32          natural log of each key channel's
+ *                                                 decay (finite, <= 0: the chunked
+ *                                                 form multiplies decays of up to 64
+ *                                                 tokens and relies on each being <= 1);
+ *                                                 16-byte aligned
+ *   io_dtype       GDN_BF16 or GDN_F16 (GDN_F32 returns GDN_ERR_UNSUPPORTED)
+ *   workspace      device scratch owned by the caller, at least
+ *                  gdn_kda_workspace_size(...) bytes, 256-byte aligned, overlapping no
+ *                  other argument; its contents on entry are ignored and on return are
+ *                  unspecified.  May be NULL when T_tot == 0.  Two calls in flight at
+ *                  once must not share a workspace.
+ *   workspace_bytes  its size in bytes
+ *
+ * Two kernels run in order on `stream`: one per (chunk, value head) that forms the
+ * chunk's decay-weighted grams, (I + A)^-1 and decayed keys/queries into the workspace,
+ * then the chunk-by-chunk state recurrence that reads them.
+ */
+gdn_status gdn_kda_prefill(const void *q, const void *k, const void *v,
+                           const float *g, const float *beta,
+                           const float *initial_state, const int32_t *cu_seqlens,
+                           int32_t N, int32_t T_tot, int32_t Hk, int32_t Hv,
+                           int32_t Dk, int32_t Dv, int32_t chunk_size, gdn_dtype io_dtype,
+                           void *workspace, size_t workspace_bytes,
+                           void *o, float *final_state, void *stream);
+
+/*
+ * gdn_kda_decode_step -- one token per sequence with a per-key-channel decay, state
+ * updated in place.  As gdn_decode_step, except g is [B, Hv, Dk] fp32, 16-byte aligned.
+ * All three io_dtype values are supported.
+ */
+gdn_status gdn_kda_decode_step(const void *q, const void *k, const void *v,
+                               const float *g, const float *beta, float *state,
+                               int32_t B, int32_t Hk, int32_t Hv, int32_t Dk, int32_t Dv,
+                               gdn_dtype io_dtype, void *o, void *stream);
 
 /*
  * gdn_prefill_plan -- the launch shape gdn_prefill would use for these sizes,

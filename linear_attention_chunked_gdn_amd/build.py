@@ -18,7 +18,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libgdn_mi355x.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = ["gdn_api.cpp", "gdn_prefill.hip", "gdn_prefill_pipe.hip", "gdn_decode.hip"]
+SOURCES = ["gdn_api.cpp", "gdn_prefill.hip", "gdn_prefill_pipe.hip", "gdn_decode.hip",
+           "kda_map.hip", "kda_chain.hip"]
 ARCH = "gfx950"
 
 

@@ -1,6 +1,7 @@
 // C-ABI entry points of the gated delta-rule library (declared in include/gdn.h):
 // argument validation, launch planning and error reporting.  All compute runs in
-// the HIP kernels of gdn_prefill.hip, gdn_prefill_pipe.hip and gdn_decode.hip.
+// the HIP kernels of gdn_prefill.hip, gdn_prefill_pipe.hip, kda_map.hip, kda_chain.hip
+// and gdn_decode.hip.
 #include "gdn.h"
 #include "gdn_launch.h"
 
@@ -111,11 +112,18 @@ gdn_status gdn_prefill_plan(int32_t N, int32_t Hv, int32_t Dv, gdn_dtype io_dtyp
     return ok();
 }
 
-gdn_status gdn_prefill(const void *q, const void *k, const void *v, const float *g,
-                       const float *beta, const float *initial_state, const int32_t *cu_seqlens,
-                       int32_t N, int32_t T_tot, int32_t Hk, int32_t Hv, int32_t Dk, int32_t Dv,
-                       int32_t chunk_size, gdn_dtype io_dtype, void *o, float *final_state,
-                       void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Host-side checks shared by the two prefill entry points: g holds g_width values per
+// (token, value head) (1, or Dk for a per-key-channel gate); ws / ws_bytes is the
+// workspace (none for the scalar gate).
+gdn_status check_prefill(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                         const float *initial_state, const int32_t *cu_seqlens, int32_t N, int32_t T_tot,
+                         int32_t Hk, int32_t Hv, int32_t Dk, int32_t Dv, int32_t chunk_size,
+                         gdn_dtype io_dtype, const void *o, const float *final_state, size_t g_width,
+                         const void *ws, size_t ws_bytes) {
     if (!valid_dtype(io_dtype))
         return fail(GDN_ERR_INVALID_ARGUMENT, "io_dtype %d is not GDN_F32, GDN_BF16 or GDN_F16", (int)io_dtype);
     if (N < 1) return fail(GDN_ERR_INVALID_ARGUMENT, "N=%d must be >= 1", N);
@@ -136,25 +144,49 @@ gdn_status gdn_prefill(const void *q, const void *k, const void *v, const float 
     for (int i = 0; i < 6; ++i)
         if (!aligned(a16[i], 16))
             return fail(GDN_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", n16[i]);
-    if (!aligned(g, 4) || !aligned(beta, 4) || !aligned(cu_seqlens, 4))
-        return fail(GDN_ERR_INVALID_ARGUMENT, "g, beta and cu_seqlens must be 4-byte aligned");
+    if (!aligned(g, g_width > 1 ? 16 : 4) || !aligned(beta, 4) || !aligned(cu_seqlens, 4))
+        return fail(GDN_ERR_INVALID_ARGUMENT, "g must be %d-byte aligned, beta and cu_seqlens 4-byte",
+                    g_width > 1 ? 16 : 4);
 
     const size_t es = io_dtype == GDN_F32 ? 4 : 2;
     const size_t T = (size_t)T_tot;
     const size_t state_bytes = (size_t)N * Hv * kD * kD * sizeof(float);
     const Range ro = range(o, T * Hv * kD * es, "o");
     const Range ins[] = {range(q, T * Hk * kD * es, "q"), range(k, T * Hk * kD * es, "k"),
-                         range(v, T * Hv * kD * es, "v"), range(g, T * Hv * 4, "g"),
+                         range(v, T * Hv * kD * es, "v"), range(g, T * Hv * g_width * 4, "g"),
                          range(beta, T * Hv * 4, "beta"),
                          range(initial_state, state_bytes, "initial_state"),
                          range(cu_seqlens, (size_t)(N + 1) * 4, "cu_seqlens")};
     const Range rf = range(final_state, state_bytes, "final_state");
+    const Range rw = range(ws, ws_bytes, "workspace");
     for (const Range &r : ins) {
         if (overlap(ro, r)) return fail(GDN_ERR_INVALID_ARGUMENT, "o overlaps %s", r.name);
         if (overlap(rf, r) && !(r.lo == reinterpret_cast<const char *>(initial_state) && rf.lo == r.lo))
             return fail(GDN_ERR_INVALID_ARGUMENT, "final_state overlaps %s", r.name);
+        if (overlap(rw, r)) return fail(GDN_ERR_INVALID_ARGUMENT, "workspace overlaps %s", r.name);
     }
     if (overlap(ro, rf)) return fail(GDN_ERR_INVALID_ARGUMENT, "o overlaps final_state");
+    if (overlap(rw, ro) || overlap(rw, rf))
+        return fail(GDN_ERR_INVALID_ARGUMENT, "workspace overlaps an output");
+    return GDN_OK;
+}
+
+// Chunk slots of the per-key-channel prefill: chunk j of sequence n uses slot
+// cu[n] / 64 + n + j, and these never exceed T_tot / 64 + N.
+size_t kda_slots(int32_t N, int32_t T_tot) { return (size_t)T_tot / kChunk + (size_t)N; }
+
+}  // namespace
+
+extern "C" {
+
+gdn_status gdn_prefill(const void *q, const void *k, const void *v, const float *g,
+                       const float *beta, const float *initial_state, const int32_t *cu_seqlens,
+                       int32_t N, int32_t T_tot, int32_t Hk, int32_t Hv, int32_t Dk, int32_t Dv,
+                       int32_t chunk_size, gdn_dtype io_dtype, void *o, float *final_state,
+                       void *stream) {
+    const gdn_status cs = check_prefill(q, k, v, g, beta, initial_state, cu_seqlens, N, T_tot, Hk, Hv, Dk,
+                                        Dv, chunk_size, io_dtype, o, final_state, 1, nullptr, 0);
+    if (cs != GDN_OK) return cs;
 
     int32_t dvs = 0, wg = 0;
     gdn_status ps = gdn_prefill_plan(N, Hv, Dv, io_dtype, &dvs, &wg, nullptr, nullptr);
@@ -176,9 +208,60 @@ gdn_status gdn_prefill(const void *q, const void *k, const void *v, const float 
     return ok();
 }
 
-gdn_status gdn_decode_step(const void *q, const void *k, const void *v, const float *g,
-                           const float *beta, float *state, int32_t B, int32_t Hk, int32_t Hv,
-                           int32_t Dk, int32_t Dv, gdn_dtype io_dtype, void *o, void *stream) {
+gdn_status gdn_kda_workspace_size(int32_t N, int32_t T_tot, int32_t Hv, int32_t chunk_size, size_t *bytes) {
+    if (!bytes) return fail(GDN_ERR_INVALID_ARGUMENT, "bytes must be non-null");
+    if (N < 1 || T_tot < 0 || Hv < 1)
+        return fail(GDN_ERR_INVALID_ARGUMENT, "N=%d, T_tot=%d, Hv=%d out of range", N, T_tot, Hv);
+    if (chunk_size != kChunk)
+        return fail(GDN_ERR_UNSUPPORTED, "chunk_size=%d (only 64 is implemented)", chunk_size);
+    *bytes = kda_slots(N, T_tot) * (size_t)Hv * gdn::KDA_TILE_BYTES;
+    return ok();
+}
+
+gdn_status gdn_kda_prefill(const void *q, const void *k, const void *v, const float *g,
+                           const float *beta, const float *initial_state, const int32_t *cu_seqlens,
+                           int32_t N, int32_t T_tot, int32_t Hk, int32_t Hv, int32_t Dk, int32_t Dv,
+                           int32_t chunk_size, gdn_dtype io_dtype, void *workspace, size_t workspace_bytes,
+                           void *o, float *final_state, void *stream) {
+    const gdn_status cs = check_prefill(q, k, v, g, beta, initial_state, cu_seqlens, N, T_tot, Hk, Hv, Dk,
+                                        Dv, chunk_size, io_dtype, o, final_state, kD, workspace,
+                                        workspace_bytes);
+    if (cs != GDN_OK) return cs;
+    if (io_dtype == GDN_F32)
+        return fail(GDN_ERR_UNSUPPORTED, "gdn_kda_prefill takes bf16 or fp16 q, k, v, o");
+    size_t need = 0;
+    gdn_kda_workspace_size(N, T_tot, Hv, chunk_size, &need);
+    if (T_tot > 0 && (!workspace || workspace_bytes < need))
+        return fail(GDN_ERR_INVALID_ARGUMENT, "workspace of %zu bytes is smaller than the %zu required",
+                    workspace ? workspace_bytes : (size_t)0, need);
+    if (!aligned(workspace, 256)) return fail(GDN_ERR_INVALID_ARGUMENT, "workspace is not 256-byte aligned");
+    if ((long long)kda_slots(N, T_tot) * Hv > 0x7fffffffLL || (long long)N * Hv * 8 > 0x7fffffffLL)
+        return fail(GDN_ERR_UNSUPPORTED, "too many chunks or heads for one launch");
+    if (T_tot == 0 && !final_state) return ok();
+
+    gdn::KdaArgs a;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
+    a.s0 = initial_state; a.cu = cu_seqlens; a.o = o; a.sN = final_state;
+    a.ws = static_cast<char *>(workspace);
+    a.N = N; a.T_tot = T_tot; a.Hk = Hk; a.Hv = Hv;
+    a.nslots = (int32_t)kda_slots(N, T_tot);
+    const hipStream_t hs = static_cast<hipStream_t>(stream);
+    const bool f16 = io_dtype == GDN_F16;
+    (void)hipGetLastError();
+    hipError_t e = T_tot > 0 ? gdn::launch_kda_map(a, f16, hs) : hipSuccess;
+    if (e == hipSuccess) e = gdn::launch_kda_chain(a, f16, hs);
+    if (e != hipSuccess)
+        return fail(GDN_ERR_DEVICE, "kda prefill launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+}  // extern "C"
+
+namespace {
+
+gdn_status decode_impl(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                       float *state, int32_t B, int32_t Hk, int32_t Hv, int32_t Dk, int32_t Dv,
+                       gdn_dtype io_dtype, void *o, void *stream, bool per_channel) {
     if (!valid_dtype(io_dtype))
         return fail(GDN_ERR_INVALID_ARGUMENT, "io_dtype %d is not GDN_F32, GDN_BF16 or GDN_F16", (int)io_dtype);
     if (B < 1 || Hk < 1 || Hv < 1)
@@ -188,17 +271,19 @@ gdn_status gdn_decode_step(const void *q, const void *k, const void *v, const fl
     if (Dk != kD || Dv != kD)
         return fail(GDN_ERR_UNSUPPORTED, "Dk=%d, Dv=%d (only 128 is implemented)", Dk, Dv);
     if (!q || !k || !v || !g || !beta || !state || !o)
-        return fail(GDN_ERR_INVALID_ARGUMENT, "all tensor arguments of gdn_decode_step are required");
+        return fail(GDN_ERR_INVALID_ARGUMENT, "all tensor arguments of a decode step are required");
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(state, 16) || !aligned(v, 4) || !aligned(o, 4) ||
-        !aligned(g, 4) || !aligned(beta, 4))
-        return fail(GDN_ERR_INVALID_ARGUMENT, "q, k and state must be 16-byte aligned, the rest 4-byte");
+        !aligned(g, per_channel ? 16 : 4) || !aligned(beta, 4))
+        return fail(GDN_ERR_INVALID_ARGUMENT,
+                    "q, k and state must be 16-byte aligned (and g for a per-channel gate), the rest 4-byte");
     if ((long long)B * Hv * (kD / 16) > 0x7fffffffLL)
         return fail(GDN_ERR_UNSUPPORTED, "B*Hv too large for one launch");
     const size_t es = io_dtype == GDN_F32 ? 4 : 2;
     const Range ro = range(o, (size_t)B * Hv * kD * es, "o");
     const Range rs = range(state, (size_t)B * Hv * kD * kD * 4, "state");
     const Range ins[] = {range(q, (size_t)B * Hk * kD * es, "q"), range(k, (size_t)B * Hk * kD * es, "k"),
-                         range(v, (size_t)B * Hv * kD * es, "v"), range(g, (size_t)B * Hv * 4, "g"),
+                         range(v, (size_t)B * Hv * kD * es, "v"),
+                         range(g, (size_t)B * Hv * (per_channel ? kD : 1) * 4, "g"),
                          range(beta, (size_t)B * Hv * 4, "beta")};
     for (const Range &r : ins) {
         if (overlap(ro, r)) return fail(GDN_ERR_INVALID_ARGUMENT, "o overlaps %s", r.name);
@@ -210,10 +295,28 @@ gdn_status gdn_decode_step(const void *q, const void *k, const void *v, const fl
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.state = state; a.o = o;
     a.B = B; a.Hk = Hk; a.Hv = Hv;
     (void)hipGetLastError();
-    const hipError_t e = gdn::launch_decode(a, (int)io_dtype, static_cast<hipStream_t>(stream));
+    const hipStream_t hs = static_cast<hipStream_t>(stream);
+    const hipError_t e = per_channel ? gdn::launch_kda_decode(a, (int)io_dtype, hs)
+                                     : gdn::launch_decode(a, (int)io_dtype, hs);
     if (e != hipSuccess)
         return fail(GDN_ERR_DEVICE, "decode launch failed: %s", hipGetErrorString(e));
     return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+gdn_status gdn_decode_step(const void *q, const void *k, const void *v, const float *g,
+                           const float *beta, float *state, int32_t B, int32_t Hk, int32_t Hv,
+                           int32_t Dk, int32_t Dv, gdn_dtype io_dtype, void *o, void *stream) {
+    return decode_impl(q, k, v, g, beta, state, B, Hk, Hv, Dk, Dv, io_dtype, o, stream, false);
+}
+
+gdn_status gdn_kda_decode_step(const void *q, const void *k, const void *v, const float *g,
+                               const float *beta, float *state, int32_t B, int32_t Hk, int32_t Hv,
+                               int32_t Dk, int32_t Dv, gdn_dtype io_dtype, void *o, void *stream) {
+    return decode_impl(q, k, v, g, beta, state, B, Hk, Hv, Dk, Dv, io_dtype, o, stream, true);
 }
 
 }  // extern "C"

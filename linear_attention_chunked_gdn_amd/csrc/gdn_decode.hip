@@ -13,6 +13,10 @@
 // two 16-byte loads), the two dot products are reduced across those 16 lanes, and
 // a 256-thread workgroup covers 16 rows.  The step is bound by the state's read and
 // write (128 KiB per head).
+//
+// With a per-key-channel gate (KDA: g is [B, Hv, 128]) the scalar alpha becomes
+// Diag(a), a_j = exp(g_j), on the key index, applied before the erase:
+//   S <- S Diag(a) (I - beta k k^T) + beta v k^T:  D = S Diag(a), S = D - beta (D k) k^T + beta v k^T.
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
@@ -43,7 +47,7 @@ __device__ __forceinline__ float sum16(float x) {
     return x;
 }
 
-template <typename IO>
+template <typename IO, bool PER_CHANNEL>
 __global__ __launch_bounds__(256) void gdn_decode_kernel(const DecodeArgs a) {
     constexpr int RB = DEC_D / DEC_ROWS;
     const int rb = blockIdx.x % RB;
@@ -65,20 +69,38 @@ __global__ __launch_bounds__(256) void gdn_decode_kernel(const DecodeArgs a) {
     load8_io<IO>(a.q, koff, qq);
     const size_t voff = ((size_t)b * a.Hv + h) * DEC_D + row;
     const float vi = Cvt<IO>::to_f32(reinterpret_cast<const IO *>(a.v)[voff]);
-    const float alpha = __expf(a.g[(size_t)b * a.Hv + h]);
     const float beta = a.beta[(size_t)b * a.Hv + h];
-
-    float u = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) u += S[i] * kk[i];
-    u = sum16(u);                               // (S k)_row, state before the token
-    const float erase = alpha * beta * u;
-    const float write = beta * vi;
     float o = 0.f;
+    if constexpr (PER_CHANNEL) {
+        float gg[8];
+        load8_io<float>(a.g, ((size_t)b * a.Hv + h) * DEC_D + 8 * l, gg);
+        float u = 0.f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        S[i] = alpha * S[i] - erase * kk[i] + write * kk[i];
-        o += S[i] * qq[i];
+        for (int i = 0; i < 8; ++i) {
+            S[i] *= __expf(gg[i]);                // S Diag(a)
+            u += S[i] * kk[i];
+        }
+        u = sum16(u);                               // (S Diag(a) k)_row
+        const float erase = beta * u;
+        const float write = beta * vi;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            S[i] = S[i] - erase * kk[i] + write * kk[i];
+            o += S[i] * qq[i];
+        }
+    } else {
+        const float alpha = __expf(a.g[(size_t)b * a.Hv + h]);
+        float u = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) u += S[i] * kk[i];
+        u = sum16(u);                               // (S k)_row, state before the token
+        const float erase = alpha * beta * u;
+        const float write = beta * vi;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            S[i] = alpha * S[i] - erase * kk[i] + write * kk[i];
+            o += S[i] * qq[i];
+        }
     }
     o = sum16(o);                               // (S q)_row, updated state
     *reinterpret_cast<f32x4 *>(srow) = f32x4{S[0], S[1], S[2], S[3]};
@@ -86,15 +108,24 @@ __global__ __launch_bounds__(256) void gdn_decode_kernel(const DecodeArgs a) {
     if (l == 0) reinterpret_cast<IO *>(a.o)[voff] = Cvt<IO>::from_f32(o);
 }
 
-hipError_t launch_decode(const DecodeArgs &a, int io, hipStream_t stream) {
+template <bool PER_CHANNEL>
+hipError_t launch_decode_kind(const DecodeArgs &a, int io, hipStream_t stream) {
     const int grid = a.B * a.Hv * (DEC_D / DEC_ROWS);
     if (io == 1)
-        hipLaunchKernelGGL(gdn_decode_kernel<__bf16>, dim3(grid), dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((gdn_decode_kernel<__bf16, PER_CHANNEL>), dim3(grid), dim3(256), 0, stream, a);
     else if (io == 2)
-        hipLaunchKernelGGL(gdn_decode_kernel<_Float16>, dim3(grid), dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((gdn_decode_kernel<_Float16, PER_CHANNEL>), dim3(grid), dim3(256), 0, stream, a);
     else
-        hipLaunchKernelGGL(gdn_decode_kernel<float>, dim3(grid), dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((gdn_decode_kernel<float, PER_CHANNEL>), dim3(grid), dim3(256), 0, stream, a);
     return hipGetLastError();
+}
+
+hipError_t launch_decode(const DecodeArgs &a, int io, hipStream_t stream) {
+    return launch_decode_kind<false>(a, io, stream);
+}
+
+hipError_t launch_kda_decode(const DecodeArgs &a, int io, hipStream_t stream) {
+    return launch_decode_kind<true>(a, io, stream);
 }
 
 }  // namespace gdn

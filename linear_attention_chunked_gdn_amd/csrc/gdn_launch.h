@@ -28,6 +28,38 @@ struct DecodeArgs {
     int32_t B, Hk, Hv;
 };
 
+// Per-key-channel decay (KDA): g is [T_tot, Hv, 128].  The map kernel writes one
+// workspace tile per (chunk slot, value head); chunk j of sequence n uses slot
+// cu[n] / 64 + n + j, so T_tot / 64 + N slots cover every packing of the batch.
+struct KdaArgs {
+    const void *q, *k, *v;  // [T_tot, Hk, 128], [T_tot, Hk, 128], [T_tot, Hv, 128]
+    const float *g;         // [T_tot, Hv, 128]
+    const float *beta;      // [T_tot, Hv]
+    const float *s0;        // [N, Hv, 128, 128] or null
+    const int32_t *cu;      // [N+1] or null (single sequence)
+    void *o;                // [T_tot, Hv, 128]
+    float *sN;              // [N, Hv, 128, 128] or null
+    char *ws;               // nslots * Hv tiles of KDA_TILE_BYTES
+    int32_t N, T_tot, Hk, Hv;
+    int32_t nslots;
+};
+// Workspace tile of one chunk and value head (byte offsets): T = (I + A)^-1 and
+// P = tril(Q K^T (.) decays), 64 x 64 fp16 each; K (.) exp(Gamma), Q (.) exp(Gamma) and
+// K (.) exp(Gamma_last - Gamma), 64 x 128 fp16 each; exp(Gamma_last), 128 fp32.
+constexpr int KDA_OFF_T = 0;
+constexpr int KDA_OFF_P = 8192;
+constexpr int KDA_OFF_KG = 16384;
+constexpr int KDA_OFF_QG = 32768;
+constexpr int KDA_OFF_KL = 49152;
+constexpr int KDA_OFF_GL = 65536;
+constexpr size_t KDA_TILE_BYTES = 66048;
+hipError_t launch_kda_map(const KdaArgs &a, bool f16, hipStream_t stream);
+hipError_t launch_kda_chain(const KdaArgs &a, bool f16, hipStream_t stream);
+int kda_map_lds_bytes();
+int kda_chain_lds_bytes();
+// one token with a per-key-channel gate: DecodeArgs::g is [B, Hv, 128]
+hipError_t launch_kda_decode(const DecodeArgs &a, int io, hipStream_t stream);
+
 // Launch the chunked prefill with `grid` workgroups of value-channel width `dvs`.
 hipError_t launch_prefill(const PrefillArgs &a, bool bf16, int dvs, int grid, hipStream_t stream);
 // LDS bytes of one prefill workgroup, -1 if (bf16, dvs) is not instantiated.

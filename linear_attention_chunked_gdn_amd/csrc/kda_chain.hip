@@ -1,0 +1,355 @@
+// Chain half of the chunked prefill with a per-key-channel decay (KDA) for gfx950.
+//
+// The map kernel (kda_map.hip) has left, per chunk and value head, T = (I + A)^-1, P,
+// Kg = K (.) exp(Gamma), Qg = Q (.) exp(Gamma), Kl = K (.) exp(Gamma_last - Gamma) and
+// exp(Gamma_last) in a workspace tile.  What remains depends on the state S (Dv x Dk) and
+// runs chunk after chunk, as ops #4-#6 of the Map-Reduce-Map pipeline ("Empowering
+// Hybrid Attention Models on NPUs", section 2.1; the chunk-first order of section 5):
+//
+//   R = diag(beta) (V - Kg S^T),   v = T R,
+//   O = Qg S^T + P v,
+//   S <- S Diag(exp(Gamma_last)) + v^T Kl.
+//
+// With the per-channel decays folded into Kg, Qg and Kl this is the gated delta rule's
+// chain with no per-token scaling left, so the chain waves follow gdn_prefill_pipe.hip
+// (the state slice in registers, K S^T and Q S^T from a 16-bit copy of it in LDS, the
+// update in place) with every product in fp16.  The column-wise split of S is the same:
+// one workgroup per (sequence, value head, 16 value channels).
+//
+// Roles: waves 0-3 load the workspace tiles one chunk ahead and commit them to LDS;
+// waves 4-7 run the chain.  A chunk takes three barrier-separated phases:
+//   phase 1: chain R(c), Q S^T(c)     | loaders: commit T, P, Kl, exp(Gamma_last) of c
+//   phase 2: chain v(c) = T R         | loaders: commit Kg, Qg, V, beta of c + 1
+//   phase 3: chain O(c), S update     |
+// Each tile is committed after its last reader of the previous chunk and before its
+// first reader, so one LDS copy of every tile suffices.
+#include "gdn_device.h"
+#include "gdn_launch.h"
+
+#include <type_traits>
+
+namespace gdn {
+namespace kdachain {
+
+typedef _Float16 hf;
+
+constexpr int CH = 64;
+constexpr int DK = 128;
+constexpr int DV = 128;
+constexpr int DVS = 16;        // value channels per workgroup
+constexpr int THREADS = 512;   // 4 loader + 4 chain waves
+constexpr int KS = DK + 16;    // fp16 row stride of Kg, Qg, Kl and the state copy (288 B)
+constexpr int TS = CH + 16;    // fp16 row stride of T, R^T and v^T (160 B)
+constexpr int TP = CH + 8;     // fp16 row stride of P (144 B)
+constexpr int VS = DVS;
+
+template <typename IO>
+struct __align__(16) Smem {
+    hf T[CH * TS];
+    hf S[DVS * KS];            // fp16 copy of the state slice [value ch][key ch]
+    hf Rh[DVS * TS];           // R^T
+    hf Vh[DVS * TS];           // v^T
+    IO V[CH * VS];
+    float beta[CH];
+    float gl[DK];              // exp(Gamma_last) per key channel
+    hf P[CH * TP];
+    hf Kg[CH * KS];
+    hf Qg[CH * KS];
+    hf Kl[CH * KS];
+};
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// Loader registers: the tiles of one chunk between their load and their commit.
+struct StageA {       // T, P, Kl, exp(Gamma_last): read in phases 2 and 3
+    u32x4 t[2], p[2], kl[4], gl;
+};
+struct StageB {       // Kg, Qg, V, beta: read in phase 1
+    u32x4 kg[4], qg[4], v;
+    float b;
+};
+
+struct Work {
+    const char *ws;       // workspace tile of this (sequence, head) at its first chunk
+    size_t slot_stride;   // bytes from one chunk's tile to the next (Hv tiles)
+    int bos, eos, nchunks, h, dv0;
+};
+
+__device__ __forceinline__ int chunk_clamp(const Work &wk, int c) { return min(c, wk.nchunks - 1); }
+
+// Loader thread ld (0..255).  Rows past a short chunk's end read the last valid row
+// (their beta is 0, so they contribute nothing).
+__device__ __forceinline__ void load_a(StageA &st, const Work &wk, int c, int ld) {
+    const char *tile = wk.ws + (size_t)chunk_clamp(wk, c) * wk.slot_stride;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        const int idx = ld + 256 * p;   // 64 rows x 8 segments of 16 B
+        st.t[p] = *reinterpret_cast<const u32x4 *>(tile + KDA_OFF_T + idx * 16);
+        st.p[p] = *reinterpret_cast<const u32x4 *>(tile + KDA_OFF_P + idx * 16);
+    }
+#pragma unroll
+    for (int p = 0; p < 4; ++p)       // 64 rows x 16 segments
+        st.kl[p] = *reinterpret_cast<const u32x4 *>(tile + KDA_OFF_KL + (ld + 256 * p) * 16);
+    st.gl = *reinterpret_cast<const u32x4 *>(tile + KDA_OFF_GL + (ld & 31) * 16);
+}
+
+template <typename IO>
+__device__ __forceinline__ void commit_a(const StageA &st, Smem<IO> &s, int ld) {
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        const int idx = ld + 256 * p, row = idx >> 3, seg = idx & 7;
+        *reinterpret_cast<u32x4 *>(&s.T[row * TS + seg * 8]) = st.t[p];
+        *reinterpret_cast<u32x4 *>(&s.P[row * TP + seg * 8]) = st.p[p];
+    }
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const int idx = ld + 256 * p, row = idx >> 4, seg = idx & 15;
+        *reinterpret_cast<u32x4 *>(&s.Kl[row * KS + seg * 8]) = st.kl[p];
+    }
+    if (ld < 32) *reinterpret_cast<u32x4 *>(&s.gl[ld * 4]) = st.gl;
+}
+
+template <typename IO>
+__device__ __forceinline__ void load_b(StageB &st, const KdaArgs &a, const Work &wk, int c, int ld) {
+    const int cc = chunk_clamp(wk, c);
+    const char *tile = wk.ws + (size_t)cc * wk.slot_stride;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        st.kg[p] = *reinterpret_cast<const u32x4 *>(tile + KDA_OFF_KG + (ld + 256 * p) * 16);
+        st.qg[p] = *reinterpret_cast<const u32x4 *>(tile + KDA_OFF_QG + (ld + 256 * p) * 16);
+    }
+    const int tok0 = wk.bos + CH * cc, nval = min(CH, wk.eos - tok0);
+    // v: 64 rows x 2 segments of 8 values (threads 0-127; the rest repeat them)
+    const int vr = min((ld & 127) >> 1, nval - 1), vs = ld & 1;
+    st.v = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const IO *>(a.v) +
+                                            ((size_t)(tok0 + vr) * a.Hv + wk.h) * DV + wk.dv0 + 8 * vs);
+    const int br = ld & (CH - 1);
+    const float bv = a.beta[(size_t)(tok0 + min(br, nval - 1)) * a.Hv + wk.h];
+    st.b = br < nval ? bv : 0.f;
+}
+
+template <typename IO>
+__device__ __forceinline__ void commit_b(const StageB &st, Smem<IO> &s, int ld) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const int idx = ld + 256 * p, row = idx >> 4, seg = idx & 15;
+        *reinterpret_cast<u32x4 *>(&s.Kg[row * KS + seg * 8]) = st.kg[p];
+        *reinterpret_cast<u32x4 *>(&s.Qg[row * KS + seg * 8]) = st.qg[p];
+    }
+    if (ld < 128) *reinterpret_cast<u32x4 *>(&s.V[(ld >> 1) * VS + 8 * (ld & 1)]) = st.v;
+    if (ld < CH) s.beta[ld] = st.b;
+}
+
+// Phase 1: R = beta (V - Kg S^T) for tokens [16W, 16W + 16) (lane = value channel,
+// rows = tokens), then (Q S^T)^T = S Qg^T from the same S fragments.
+template <typename IO>
+__device__ __forceinline__ f32x4 chain_R_QS(Smem<IO> &s, int W, int l16, int g4) {
+    const hf *krow = s.Kg + (16 * W + l16) * KS + 8 * g4;
+    const hf *qrow = s.Qg + (16 * W + l16) * KS + 8 * g4;
+    const hf *srow = s.S + l16 * KS + 8 * g4;
+    const int t0 = 16 * W + 4 * g4;
+    const f32x4 b = *reinterpret_cast<const f32x4 *>(&s.beta[t0]);
+    f32x4 vv;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) vv[i] = Cvt<IO>::to_f32(s.V[(t0 + i) * VS + l16]);
+    Frag<hf> fs[4];
+    f32x4 ks = zero4();
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+        Frag<hf> fk;
+        fs[kb].load8(srow + 32 * kb);
+        fk.load8(krow + 32 * kb);
+        mma(ks, fk, fs[kb]);
+    }
+    f16x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = (hf)(b[i] * (vv[i] - ks[i]));
+    *reinterpret_cast<f16x4 *>(&s.Rh[l16 * TS + t0]) = r;
+    f32x4 qs = zero4();
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+        Frag<hf> fq;
+        fq.load8(qrow + 32 * kb);
+        mma(qs, fs[kb], fq);
+    }
+    return qs;
+}
+
+// Phase 2: v = T R for tokens [16W, 16W + 16); T is lower triangular, so only the
+// first W/2 + 1 blocks of 32 columns contribute.
+template <typename IO>
+__device__ __forceinline__ void chain_v(Smem<IO> &s, int W, int l16, int g4) {
+    const int t0 = 16 * W + 4 * g4;
+    f32x4 acc = zero4();
+    const hf *trow = s.T + (16 * W + l16) * TS + 8 * g4;
+    for (int kb = 0; kb <= (W >> 1); ++kb) {
+        Frag<hf> fa, fr;
+        fa.load8(trow + 32 * kb);
+        fr.load8(s.Rh + l16 * TS + 32 * kb + 8 * g4);
+        mma(acc, fa, fr);
+    }
+    f16x4 x;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = (hf)acc[i];
+    *reinterpret_cast<f16x4 *>(&s.Vh[l16 * TS + t0]) = x;
+}
+
+// Phase 3: output rows of wave W, then the update of key channels [32W, 32W + 32) of
+// the state slice: S^T rows (key channels) 32W + 16mt + 4G + r, column = value channel.
+template <typename IO>
+__device__ __forceinline__ void chain_out_update(Smem<IO> &s, const KdaArgs &a, int W, int l16, int g4,
+                                                 const f32x4 &qs, f32x4 (&st)[2], int h, int dv0,
+                                                 int tok0, int nval) {
+    const int t = 16 * W + l16;
+    {
+        // O^T = S Qg^T + v^T P^T: lane = token 16W + l16, rows = value channels 4G..4G+3
+        f32x4 acc = qs;
+        const hf *ph = s.P + (16 * W + l16) * TP + 8 * g4;
+        for (int kb = 0; kb <= (W >> 1); ++kb) {
+            Frag<hf> fp, fv;
+            fp.load8(ph + 32 * kb);
+            fv.load8(s.Vh + l16 * TS + 32 * kb + 8 * g4);
+            mma(acc, fv, fp);
+        }
+        if (t < nval) {
+            typename Vec4<IO>::type y;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) y[i] = Cvt<IO>::from_f32(acc[i]);
+            *reinterpret_cast<typename Vec4<IO>::type *>(reinterpret_cast<IO *>(a.o) +
+                                                         ((size_t)(tok0 + t) * a.Hv + h) * DV + dv0 + 4 * g4) = y;
+        }
+    }
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+        // Kl^T fragments by ds_read_b64_tr_b16 (slot e of group G = token 32kb + 8G + e,
+        // row = key channel 32W + 16mt + l16), as in gdn_prefill_pipe.hip
+        Frag<hf> ka[2];
+        const int a_tok = l16 >> 2, a_ch = 32 * W + 16 * mt + 4 * (l16 & 3);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const int t0 = 32 * kb + 8 * g4 + 4 * hh;
+                typedef __fp16 fp16x4 __attribute__((ext_vector_type(4)));
+                typedef __attribute__((address_space(3))) fp16x4 lds_fp16x4;
+                const f16x4 v = __builtin_bit_cast(
+                    f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4 *)&s.Kl[(t0 + a_tok) * KS + a_ch]));
+#pragma unroll
+                for (int e = 0; e < 4; ++e) ka[kb].set_raw(4 * hh + e, v[e]);
+            }
+        const int kc = 32 * W + 16 * mt + 4 * g4;
+        const f32x4 gl = *reinterpret_cast<const f32x4 *>(&s.gl[kc]);
+        f32x4 acc = st[mt] * gl;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            Frag<hf> fv;
+            fv.load8(s.Vh + l16 * TS + 32 * kb + 8 * g4);
+            mma(acc, ka[kb], fv);
+        }
+        st[mt] = acc;
+        f16x4 x;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] = (hf)acc[i];
+        *reinterpret_cast<f16x4 *>(&s.S[l16 * KS + kc]) = x;
+    }
+}
+
+template <typename IO>
+__global__ __launch_bounds__(THREADS) void kda_chain_kernel(const KdaArgs a) {
+    __shared__ Smem<IO> s;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, l16 = lane & 15, g4 = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool is_loader = wave < 4;
+    const int W = wave & 3;
+
+    constexpr int NSL = DV / DVS;
+    const int G = gridDim.x;
+    int item = blockIdx.x;
+    if ((G & 7) == 0) item = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
+    const int slice = item % NSL;
+    const int h = (item / NSL) % a.Hv;
+    const int n = item / (NSL * a.Hv);
+    Work wk;
+    wk.h = h;
+    wk.dv0 = slice * DVS;
+    wk.bos = a.cu ? a.cu[n] : 0;
+    wk.eos = a.cu ? a.cu[n + 1] : a.T_tot;
+    const int len = wk.eos > wk.bos ? wk.eos - wk.bos : 0;
+    wk.nchunks = (len + CH - 1) / CH;
+    wk.slot_stride = (size_t)a.Hv * KDA_TILE_BYTES;
+    wk.ws = a.ws + ((size_t)(wk.bos / CH + n) * a.Hv + h) * KDA_TILE_BYTES;
+
+    f32x4 st[2];
+    const size_t sbase = ((size_t)n * a.Hv + h) * (size_t)DV * DK;
+    if (!is_loader) {
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+            const int dk = 32 * W + 16 * mt + 4 * g4;
+            f32x4 x = zero4();
+            if (a.s0) x = *reinterpret_cast<const f32x4 *>(a.s0 + sbase + (size_t)(wk.dv0 + l16) * DK + dk);
+            st[mt] = x;
+            f16x4 y;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) y[i] = (hf)x[i];
+            *reinterpret_cast<f16x4 *>(&s.S[l16 * KS + dk]) = y;
+        }
+    }
+
+    if (wk.nchunks > 0) {
+        StageA sa;
+        StageB sb;
+        if (is_loader) {
+            load_b<IO>(sb, a, wk, 0, tid);
+            commit_b(sb, s, tid);
+            load_a(sa, wk, 0, tid);
+            load_b<IO>(sb, a, wk, 1, tid);
+        }
+        __syncthreads();
+        if (is_loader) {
+            for (int c = 0; c < wk.nchunks; ++c) {
+                commit_a(sa, s, tid);
+                load_a(sa, wk, c + 1, tid);
+                __syncthreads();
+                commit_b(sb, s, tid);
+                load_b<IO>(sb, a, wk, c + 2, tid);
+                __syncthreads();
+                __syncthreads();
+            }
+        } else {
+            for (int c = 0; c < wk.nchunks; ++c) {
+                const int tok0 = wk.bos + c * CH;
+                const int nval = min(CH, wk.eos - tok0);
+                const f32x4 qs = chain_R_QS(s, W, l16, g4);
+                __syncthreads();
+                chain_v(s, W, l16, g4);
+                __syncthreads();
+                chain_out_update(s, a, W, l16, g4, qs, st, h, wk.dv0, tok0, nval);
+                __syncthreads();
+            }
+        }
+    }
+
+    if (a.sN && !is_loader) {
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+            const int dk = 32 * W + 16 * mt + 4 * g4;
+            *reinterpret_cast<f32x4 *>(a.sN + sbase + (size_t)(wk.dv0 + l16) * DK + dk) = st[mt];
+        }
+    }
+}
+
+}  // namespace kdachain
+
+hipError_t launch_kda_chain(const KdaArgs &a, bool f16, hipStream_t stream) {
+    const dim3 grid((unsigned)a.N * (unsigned)a.Hv * (kdachain::DV / kdachain::DVS)), block(kdachain::THREADS);
+    if (f16)
+        hipLaunchKernelGGL(kdachain::kda_chain_kernel<_Float16>, grid, block, 0, stream, a);
+    else
+        hipLaunchKernelGGL(kdachain::kda_chain_kernel<__bf16>, grid, block, 0, stream, a);
+    return hipGetLastError();
+}
+
+int kda_chain_lds_bytes() { return (int)sizeof(kdachain::Smem<__bf16>); }
+
+}  // namespace gdn

@@ -3,7 +3,8 @@
 Argument marshalling only: tensors are checked for device, dtype, shape and
 contiguity, outputs are allocated with torch, and raw device pointers plus torch's
 current HIP stream are handed to ``gdn_prefill`` / ``gdn_decode_step`` in
-``libgdn_mi355x.so``.  Every step of the computation runs in the library's HIP
+``libgdn_mi355x.so`` (and the per-key-channel variants ``gdn_kda_prefill`` /
+``gdn_kda_decode_step``).  Every step of the computation runs in the library's HIP
 kernels; there is no fallback: if the library is missing or the tensors are not
 on a GPU the call raises.
 """
@@ -50,6 +51,13 @@ def load_library(path: str = LIB_PATH):
     p32 = ctypes.POINTER(ctypes.c_int32)
     lib.gdn_prefill_plan.argtypes = [i32, i32, i32, ctypes.c_int, p32, p32, p32, p32]
     lib.gdn_prefill_plan.restype = ctypes.c_int
+    lib.gdn_kda_workspace_size.argtypes = [i32, i32, i32, i32, ctypes.POINTER(ctypes.c_size_t)]
+    lib.gdn_kda_workspace_size.restype = ctypes.c_int
+    lib.gdn_kda_prefill.argtypes = [vp, vp, vp, fp, fp, fp, ip, i32, i32, i32, i32, i32, i32, i32,
+                                    ctypes.c_int, vp, ctypes.c_size_t, vp, fp, vp]
+    lib.gdn_kda_prefill.restype = ctypes.c_int
+    lib.gdn_kda_decode_step.argtypes = lib.gdn_decode_step.argtypes
+    lib.gdn_kda_decode_step.restype = ctypes.c_int
     lib.gdn_status_string.argtypes = [ctypes.c_int]
     lib.gdn_status_string.restype = ctypes.c_char_p
     lib.gdn_last_error.argtypes = []
@@ -161,6 +169,89 @@ def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tens
         st = lib.gdn_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state),
                                  B, Hk, Hv, Dk, Dv, io, _ptr(out), ctypes.c_void_p(stream))
     _check(lib, st, "gdn_decode_step")
+    return out
+
+
+def kda_workspace_size(N: int, T: int, Hv: int, chunk_size: int = CHUNK, lib=None) -> int:
+    """Workspace bytes gdn_kda_prefill needs for N sequences, T packed tokens, Hv heads."""
+    lib = lib or load_library()
+    n = ctypes.c_size_t()
+    _check(lib, lib.gdn_kda_workspace_size(N, T, Hv, chunk_size, ctypes.byref(n)), "gdn_kda_workspace_size")
+    return int(n.value)
+
+
+def kda_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                beta: torch.Tensor, initial_state: Optional[torch.Tensor] = None,
+                cu_seqlens: Optional[torch.Tensor] = None, chunk_size: int = CHUNK,
+                output_final_state: bool = True, out: Optional[torch.Tensor] = None,
+                final_state: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                lib=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Packed chunked prefill with one decay per key channel: as ``prefill`` except
+    g: [T, Hv, 128] fp32 and q, k, v bf16 or fp16.  ``workspace`` (a uint8 device tensor
+    of at least ``kda_workspace_size`` bytes) is allocated here when not given."""
+    lib = lib or load_library()
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("gdn.kda_prefill runs on the GPU only; q is on " + str(dev))
+    io = _io_code(q)
+    T, Hk, Dk = q.shape
+    Hv, Dv = v.shape[1], v.shape[2]
+    N = 1 if cu_seqlens is None else cu_seqlens.shape[0] - 1
+    _need(q, "q", q.dtype, (T, Hk, Dk), dev)
+    _need(k, "k", q.dtype, (T, Hk, Dk), dev)
+    _need(v, "v", q.dtype, (T, Hv, Dv), dev)
+    _need(g, "g", torch.float32, (T, Hv, Dk), dev)
+    _need(beta, "beta", torch.float32, (T, Hv), dev)
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,), dev)
+    if initial_state is not None:
+        _need(initial_state, "initial_state", torch.float32, (N, Hv, Dv, Dk), dev)
+    if out is None:
+        out = torch.empty((T, Hv, Dv), dtype=q.dtype, device=dev)
+    _need(out, "out", q.dtype, (T, Hv, Dv), dev)
+    if output_final_state and final_state is None:
+        final_state = torch.empty((N, Hv, Dv, Dk), dtype=torch.float32, device=dev)
+    if final_state is not None:
+        _need(final_state, "final_state", torch.float32, (N, Hv, Dv, Dk), dev)
+    need = kda_workspace_size(N, T, Hv, chunk_size, lib=lib)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    if workspace.device != dev or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor on " + str(dev))
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        st = lib.gdn_kda_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
+                                 _ptr(cu_seqlens), N, T, Hk, Hv, Dk, Dv, chunk_size, io, _ptr(workspace),
+                                 workspace.numel(), _ptr(out), _ptr(final_state), ctypes.c_void_p(stream))
+    _check(lib, st, "gdn_kda_prefill")
+    return out, final_state
+
+
+def kda_decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                    beta: torch.Tensor, state: torch.Tensor, out: Optional[torch.Tensor] = None,
+                    lib=None) -> torch.Tensor:
+    """One token per sequence with one decay per key channel: as ``decode_step`` except
+    g: [B, Hv, 128] fp32."""
+    lib = lib or load_library()
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("gdn.kda_decode_step runs on the GPU only; q is on " + str(dev))
+    io = _io_code(q)
+    B, Hk, Dk = q.shape
+    Hv, Dv = v.shape[1], v.shape[2]
+    _need(k, "k", q.dtype, (B, Hk, Dk), dev)
+    _need(v, "v", q.dtype, (B, Hv, Dv), dev)
+    _need(g, "g", torch.float32, (B, Hv, Dk), dev)
+    _need(beta, "beta", torch.float32, (B, Hv), dev)
+    _need(state, "state", torch.float32, (B, Hv, Dv, Dk), dev)
+    if out is None:
+        out = torch.empty((B, Hv, Dv), dtype=q.dtype, device=dev)
+    _need(out, "out", q.dtype, (B, Hv, Dv), dev)
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        st = lib.gdn_kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state),
+                                     B, Hk, Hv, Dk, Dv, io, _ptr(out), ctypes.c_void_p(stream))
+    _check(lib, st, "gdn_kda_decode_step")
     return out
 
 

@@ -11,6 +11,8 @@ itself.
 Shapes follow the packed layout of the C-ABI: q, k are [T_tot, Hk, Dk];
 v is [T_tot, Hv, Dv]; g and beta are [T_tot, Hv]; states are
 [N, Hv, Dv, Dk] (value index, then key index); cu_seqlens is [N+1] int32.
+With a per-key-channel gate (the KDA variant) g is [T_tot, Hv, Dk], drawn from the
+same distribution element by element.
 
 Every array is numpy.  bf16 and fp16 values are carried as float32 arrays whose
 values are exactly representable in the storage type (round-to-nearest-even from
@@ -84,7 +86,7 @@ class GDNInputs:
     q: np.ndarray                # [T_tot, Hk, Dk]
     k: np.ndarray                # [T_tot, Hk, Dk]
     v: np.ndarray                # [T_tot, Hv, Dv]
-    g: np.ndarray                # [T_tot, Hv] float32, natural log of the decay
+    g: np.ndarray                # [T_tot, Hv] (or [T_tot, Hv, Dk]) float32, log of the decay
     beta: np.ndarray             # [T_tot, Hv] float32
     cu_seqlens: np.ndarray       # [N+1] int32
     initial_state: Optional[np.ndarray]  # [N, Hv, Dv, Dk] float32 or None
@@ -114,18 +116,23 @@ class GDNInputs:
     def Dv(self) -> int:
         return int(self.v.shape[2])
 
+    @property
+    def per_channel(self) -> bool:
+        return self.g.ndim == 3
+
     def seq_lengths(self) -> np.ndarray:
         return np.diff(self.cu_seqlens.astype(np.int64))
 
 
 def draw_tokens(rng: np.random.Generator, T: int, Hk: int, Hv: int, Dk: int, Dv: int,
-                io: str, g_shift: float = 0.0):
-    """Draw q, k, v, beta, g for T tokens in the fixed order q, k, v, beta-logits, g-logits."""
+                io: str, g_shift: float = 0.0, per_channel: bool = False):
+    """Draw q, k, v, beta, g for T tokens in the fixed order q, k, v, beta-logits, g-logits
+    (g-logits [T, Hv, Dk] for a per-key-channel gate)."""
     q = rng.standard_normal((T, Hk, Dk), dtype=np.float32)
     k = rng.standard_normal((T, Hk, Dk), dtype=np.float32)
     v = rng.standard_normal((T, Hv, Dv), dtype=np.float32)
     beta_logit = rng.standard_normal((T, Hv), dtype=np.float32)
-    g_logit = rng.standard_normal((T, Hv), dtype=np.float32)
+    g_logit = rng.standard_normal((T, Hv, Dk) if per_channel else (T, Hv), dtype=np.float32)
     q = _l2_normalize(q)
     k = _l2_normalize(k)
     beta = _sigmoid64(beta_logit).astype(np.float32)
@@ -141,14 +148,14 @@ def draw_tokens(rng: np.random.Generator, T: int, Hk: int, Hv: int, Dk: int, Dv:
 
 def make_custom(seed: int, lengths, Hk: int, Hv: int, Dk: int = 128, Dv: int = 128,
                 io: str = "bf16", g_shift: float = 0.0, init_std: Optional[float] = None,
-                name: str = "custom") -> GDNInputs:
+                name: str = "custom", per_channel: bool = False) -> GDNInputs:
     """Packed batch of sequences with the given lengths (any may be 0)."""
     rng = np.random.default_rng(seed)
     lengths = np.asarray(list(lengths), dtype=np.int64)
     cu = np.zeros(len(lengths) + 1, dtype=np.int32)
     cu[1:] = np.cumsum(lengths)
     T = int(cu[-1])
-    q, k, v, g, beta = draw_tokens(rng, T, Hk, Hv, Dk, Dv, io, g_shift)
+    q, k, v, g, beta = draw_tokens(rng, T, Hk, Hv, Dk, Dv, io, g_shift, per_channel)
     s0 = None
     if init_std is not None:
         s0 = (rng.standard_normal((len(lengths), Hv, Dv, Dk), dtype=np.float32)
@@ -169,27 +176,33 @@ WORKLOADS = {
 }
 
 
-def make_workload(i: int, decode_steps: Optional[int] = None, io: Optional[str] = None) -> GDNInputs:
+def make_workload(i: int, decode_steps: Optional[int] = None, io: Optional[str] = None,
+                  per_channel: bool = False) -> GDNInputs:
     """Build workload i (0..4) from its seed.  Draw order is fixed per workload.
 
     io overrides the storage type of q, k, v, o (default: the workload's own, fp32 for
     workload 0 and bf16 for the rest); the draws are the same, only the rounding
-    differs, and the name then carries the new type."""
+    differs, and the name then carries the new type.  per_channel draws one gate per
+    key channel (the KDA variant; g-logits [T, Hv, Dk] in place of [T, Hv], so the later
+    draws differ too) and prefixes the name with "kda_"."""
     rng = np.random.default_rng(SEED_BASE + i)
     own = "f32" if i == 0 else "bf16"
     name = WORKLOADS[i]["name"]
     if io is not None and io != own:
         name = name.replace(own, io)
+    if per_channel:
+        name = "kda_" + name
     io = io or own
+    pc = per_channel
     D = 128
     if i == 0:
-        q, k, v, g, beta = draw_tokens(rng, 256, 1, 1, D, D, io)
+        q, k, v, g, beta = draw_tokens(rng, 256, 1, 1, D, D, io, per_channel=pc)
         return GDNInputs(name, io, q, k, v, g, beta, np.array([0, 256], np.int32), None)
     if i == 1:
-        q, k, v, g, beta = draw_tokens(rng, 4096, 16, 16, D, D, io)
+        q, k, v, g, beta = draw_tokens(rng, 4096, 16, 16, D, D, io, per_channel=pc)
         return GDNInputs(name, io, q, k, v, g, beta, np.array([0, 4096], np.int32), None)
     if i == 2:
-        q, k, v, g, beta = draw_tokens(rng, 16384, 16, 32, D, D, io, g_shift=2.0)
+        q, k, v, g, beta = draw_tokens(rng, 16384, 16, 32, D, D, io, g_shift=2.0, per_channel=pc)
         return GDNInputs(name, io, q, k, v, g, beta, np.array([0, 16384], np.int32), None)
     if i == 3:
         # lengths are drawn first because they fix the packed token count
@@ -197,13 +210,13 @@ def make_workload(i: int, decode_steps: Optional[int] = None, io: Optional[str] 
         cu = np.zeros(9, dtype=np.int32)
         cu[1:] = np.cumsum(lengths)
         T = int(cu[-1])
-        q, k, v, g, beta = draw_tokens(rng, T, 16, 16, D, D, io)
+        q, k, v, g, beta = draw_tokens(rng, T, 16, 16, D, D, io, per_channel=pc)
         s0 = (rng.standard_normal((8, 16, D, D), dtype=np.float32) * np.float32(0.02)).astype(np.float32)
         return GDNInputs(name, io, q, k, v, g, beta, cu, s0)
     if i == 4:
-        q, k, v, g, beta = draw_tokens(rng, 65536, 32, 32, D, D, io)
+        q, k, v, g, beta = draw_tokens(rng, 65536, 32, 32, D, D, io, per_channel=pc)
         steps = 256 if decode_steps is None else decode_steps
-        dq, dk_, dv, dg, db = draw_tokens(rng, steps, 32, 32, D, D, io)
+        dq, dk_, dv, dg, db = draw_tokens(rng, steps, 32, 32, D, D, io, per_channel=pc)
         dec = dict(q=dq, k=dk_, v=dv, g=dg, beta=db, steps=steps)
         return GDNInputs(name, io, q, k, v, g, beta, np.array([0, 65536], np.int32), None, dec)
     raise KeyError(i)

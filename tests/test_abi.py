@@ -29,7 +29,8 @@ def lib():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted(
-        ["gdn_prefill", "gdn_decode_step", "gdn_prefill_plan", "gdn_status_string", "gdn_last_error"])
+        ["gdn_prefill", "gdn_decode_step", "gdn_prefill_plan", "gdn_status_string", "gdn_last_error",
+         "gdn_kda_workspace_size", "gdn_kda_prefill", "gdn_kda_decode_step"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -116,3 +117,55 @@ def test_plan(lib):
     assert gdn.prefill_plan(1, 16, gdn.GDN_F16, lib=lib) == plan
     with pytest.raises(gdn.GDNError):
         gdn.prefill_plan(1, 16, 3, lib=lib)
+
+
+def test_kda_workspace_size(lib):
+    # one 66,048-byte tile per value head and chunk slot, T_tot / 64 + N slots
+    assert gdn.kda_workspace_size(1, 4096, 16, lib=lib) == (64 + 1) * 16 * 66048
+    assert gdn.kda_workspace_size(3, 100, 2, lib=lib) == (1 + 3) * 2 * 66048
+    with pytest.raises(gdn.GDNError):
+        gdn.kda_workspace_size(1, 10, 1, chunk_size=32, lib=lib)
+
+
+def _kda_prefill(lib, **over):
+    # fake, aligned, never-dereferenced addresses: validation fails before any use
+    a = dict(q=0x100000, k=0x200000, v=0x300000, g=0x400000, beta=0x500000, s0=None, cu=None,
+             N=1, T=10, Hk=2, Hv=4, Dk=128, Dv=128, C=64, io=1, ws=0x1000000, wsb=1 << 24,
+             o=0x600000, fs=None)
+    a.update(over)
+    p = lambda x: None if x is None else ctypes.c_void_p(x)  # noqa: E731
+    return lib.gdn_kda_prefill(p(a["q"]), p(a["k"]), p(a["v"]), p(a["g"]), p(a["beta"]), p(a["s0"]),
+                               p(a["cu"]), a["N"], a["T"], a["Hk"], a["Hv"], a["Dk"], a["Dv"], a["C"],
+                               a["io"], p(a["ws"]), a["wsb"], p(a["o"]), p(a["fs"]), None)
+
+
+@pytest.mark.parametrize("over,status,msg", [
+    (dict(io=0), 2, "bf16 or fp16"),
+    (dict(C=128), 2, "chunk_size"),
+    (dict(wsb=1000), 1, "smaller than"),
+    (dict(ws=None), 1, "smaller than"),
+    (dict(ws=0x1000080), 1, "256-byte aligned"),
+    (dict(g=0x400008), 1, "g must be 16-byte aligned"),
+    (dict(ws=0x300000), 1, "workspace overlaps v"),
+    (dict(o=0x1000000), 1, "overlaps"),
+    (dict(Hv=3), 1, "multiple"),
+])
+def test_kda_prefill_rejects(lib, over, status, msg):
+    assert _kda_prefill(lib, **over) == status
+    assert msg in lib.gdn_last_error().decode()
+
+
+def test_kda_prefill_nothing_to_do_is_ok(lib):
+    assert _kda_prefill(lib, q=None, k=None, v=None, g=None, beta=None, o=None, ws=None, wsb=0, T=0) == 0
+
+
+def test_kda_decode_rejects(lib):
+    p = ctypes.c_void_p
+    # a per-channel gate must be 16-byte aligned
+    st = lib.gdn_kda_decode_step(p(0x1000), p(0x2000), p(0x3000), p(0x4008), p(0x5000), p(0x10000),
+                                 1, 1, 1, 128, 128, 1, p(0x60000), None)
+    assert st == 1 and b"16-byte" in lib.gdn_last_error()
+    # g of [B, Hv, 128] fp32 is 512 B: a state written at 0x4100 would overlap it
+    st = lib.gdn_kda_decode_step(p(0x1000), p(0x2000), p(0x3000), p(0x4000), p(0x5000), p(0x4100),
+                                 1, 1, 1, 128, 128, 1, p(0x60000), None)
+    assert st == 1 and b"state overlaps g" in lib.gdn_last_error()
