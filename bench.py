@@ -1,7 +1,7 @@
 """Throughput of the chunked gated delta-rule prefill on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload I] [--io bf16|f16|f32]
-                    [--no-cpu-baseline]
+                    [--kda] [--no-cpu-baseline]
 
 A step is one gdn_prefill call over the whole workload (all heads, all chunks) with
 inputs resident in HBM.  The default workload is the headline one: one sequence of
@@ -31,6 +31,12 @@ a bf16 GEMM measured on this GPU, beside the published peaks used for the fracti
 
 cpu_baseline: the fp64 CPU oracle (test infrastructure, untuned) timed on the host
 cores over the same workload.
+
+--kda: the same workload with one decay per key channel (gdn_kda_prefill: a
+chunk-parallel map kernel, then the chain kernel, over a workspace allocated once
+outside the timed region).  The step is the whole call (both kernels); g adds
+T*Hv*Dk*4 bytes and the grams are per value head (see `algorithmic_bytes`,
+`algorithmic_flops`).
 """
 from __future__ import annotations
 
@@ -49,6 +55,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "GDN prefill tokens/sec (H=16, d=128, T=4096) + % of MFMA/HBM roofline"
+KDA_METRIC = "KDA prefill tokens/sec (H={H}, d=128, T={T}) + % of HBM roofline"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # dense
 FP32_MFMA_PEAK_TFLOPS = 157.3
@@ -61,6 +68,7 @@ IO_CODE = {"f32": 0, "bf16": 1, "f16": 2}   # gdn_dtype
 KERNEL_SOURCES = {
     "gdn_prefill_pipe_kernel": ["gdn_prefill_pipe.hip", "gdn_device.h", "gdn_launch.h"],
     "gdn_prefill_kernel": ["gdn_prefill.hip", "gdn_device.h", "gdn_launch.h"],
+    "kda_map_kernel+kda_chain_kernel": ["kda_map.hip", "kda_chain.hip", "gdn_device.h", "gdn_launch.h"],
 }
 
 
@@ -97,43 +105,55 @@ def _counter_median(path: str, counter: str, kernel_substr: str) -> float:
     return statistics.median(per_dispatch.values())
 
 
-def summarize_pmc(directory: str, workload: int, calib_mib: int, io=None) -> dict:
+def summarize_pmc(directory: str, workload: int, calib_mib: int, io=None, kda=False) -> dict:
     """Scale the FETCH_SIZE / WRITE_SIZE counters (KiB per dispatch) of the prefill kernel by
     what the same counters read for a copy of known size; rocprofv3 runs of bench.py wrote
-    fetch_, write_, copyfetch_ and copywrite_counter_collection.csv into `directory`."""
+    fetch_, write_, copyfetch_ and copywrite_counter_collection.csv into `directory`.  With
+    kda the step's two kernels are added (bytes per step)."""
     from linear_attention_chunked_gdn_amd import gdn, inputs
-    x = inputs.make_workload(workload, io=io)
-    plan = gdn.prefill_plan(x.N, x.Hv, IO_CODE[x.io])
-    kernel = "gdn_prefill_pipe_kernel" if plan["threads_per_workgroup"] == 512 else "gdn_prefill_kernel"
+    x = inputs.make_workload(workload, io=io, per_channel=kda)
+    if kda:
+        kernel = "kda_map_kernel+kda_chain_kernel"
+    else:
+        plan = gdn.prefill_plan(x.N, x.Hv, IO_CODE[x.io])
+        kernel = "gdn_prefill_pipe_kernel" if plan["threads_per_workgroup"] == 512 else "gdn_prefill_kernel"
     true_kib = calib_mib * 1024.0
     f = lambda n, c, k: _counter_median(os.path.join(directory, f"{n}_counter_collection.csv"), c, k)  # noqa: E731
     fscale = true_kib / f("copyfetch", "FETCH_SIZE", "")
     wscale = true_kib / f("copywrite", "WRITE_SIZE", "")
-    fetch = f("fetch", "FETCH_SIZE", kernel) * fscale * 1024
-    write = f("write", "WRITE_SIZE", kernel) * wscale * 1024
+    parts = kernel.split("+")
+    fetch = sum(f("fetch", "FETCH_SIZE", k) for k in parts) * fscale * 1024
+    write = sum(f("write", "WRITE_SIZE", k) for k in parts) * wscale * 1024
     return {f"{kernel}@{x.name}": {
         "sources_sha256": sources_sha256(kernel), "fetch_bytes": fetch, "write_bytes": write,
         "fetch_scale": fscale, "write_scale": wscale, "algorithmic_bytes": algorithmic_bytes(x)}}
 
 
 def algorithmic_bytes(x) -> int:
+    """q, k once per key head; v, o once per value head; beta and g (fp32; g per key
+    channel for KDA); the fp32 state read (if given) and written."""
     s = 4 if x.io == "f32" else 2
     T, Hk, Hv, Dk, Dv, N = x.T_tot, x.Hk, x.Hv, x.Dk, x.Dv, x.N
     state = N * Hv * Dv * Dk * 4 * (2 if x.initial_state is not None else 1)
-    return T * (Hk * 2 * Dk * s + Hv * (2 * Dv * s + 8)) + state
+    gate = 4 * (Dk if x.per_channel else 1)
+    return T * (Hk * 2 * Dk * s + Hv * (2 * Dv * s + 4 + gate)) + state
 
 
 def algorithmic_flops(x, C: int = 64) -> int:
     """Sum over chunks of n_c tokens: Hv*(6*n_c*Dk*Dv + 2*n_c^2*Dv) + Hk*2*n_c^2*Dk
     (the three state products K S^T, Q S^T and v^T K; the intra-chunk P v product;
     the K K^T gram per key head).  This is the method's own work, not the padded
-    tile work of any kernel."""
+    tile work of any kernel.  With a per-key-channel gate the decays enter the sums over
+    key channels, so both grams (K K^T and Q K^T, 4*n_c^2*Dk) are per value head."""
     total = 0
     for L in x.seq_lengths():
         full, tail = divmod(int(L), C)
         for n_c, cnt in ((C, full), (tail, 1 if tail else 0)):
-            total += cnt * (x.Hv * (6 * n_c * x.Dk * x.Dv + 2 * n_c * n_c * x.Dv)
-                            + x.Hk * 2 * n_c * n_c * x.Dk)
+            if x.per_channel:
+                total += cnt * x.Hv * (6 * n_c * x.Dk * x.Dv + 2 * n_c * n_c * x.Dv + 4 * n_c * n_c * x.Dk)
+            else:
+                total += cnt * (x.Hv * (6 * n_c * x.Dk * x.Dv + 2 * n_c * n_c * x.Dv)
+                                + x.Hk * 2 * n_c * n_c * x.Dk)
     return total
 
 
@@ -170,13 +190,14 @@ def decode_bench(x, dev, state0) -> dict:
     dq, dk, dv = (torch.from_numpy(np.ascontiguousarray(dec[k])).to(dev, io) for k in ("q", "k", "v"))
     dg, db = (torch.from_numpy(np.ascontiguousarray(dec[k])).to(dev, torch.float32) for k in ("g", "beta"))
     outs = torch.empty((n, x.N, x.Hv, x.Dv), dtype=io, device=dev)
+    step_fn = gdn.kda_decode_step if x.per_channel else gdn.decode_step
     state = torch.empty_like(state0)
     B = x.N
 
     def run():
         for i in range(n):
             sl = slice(i * B, (i + 1) * B)
-            gdn.decode_step(dq[sl], dk[sl], dv[sl], dg[sl], db[sl], state, out=outs[i])
+            step_fn(dq[sl], dk[sl], dv[sl], dg[sl], db[sl], state, out=outs[i])
 
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
     state.copy_(state0)
@@ -272,6 +293,8 @@ def main() -> int:
     ap.add_argument("--workload", type=int, default=1)
     ap.add_argument("--io", choices=sorted(IO_CODE), default=None,
                     help="storage type of q, k, v, o (default: the workload's own)")
+    ap.add_argument("--kda", action="store_true",
+                    help="one decay per key channel (gdn_kda_prefill) on the same workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rotate-bytes", type=int, default=2 * MALL_BYTES,
                     help="input copies are rotated until they span at least this many bytes")
@@ -287,7 +310,7 @@ def main() -> int:
         print("bench.py: this build runs on one GPU only; --gpus must be 1", file=sys.stderr)
         return 2
     if args.summarize_pmc:
-        entry = summarize_pmc(args.summarize_pmc, args.workload, args.calibrate_copy or 256, args.io)
+        entry = summarize_pmc(args.summarize_pmc, args.workload, args.calibrate_copy or 256, args.io, args.kda)
         try:
             with open(TRAFFIC_FILE) as f:
                 table = json.load(f)
@@ -308,7 +331,7 @@ def main() -> int:
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    x = inputs.make_workload(args.workload, io=args.io)
+    x = inputs.make_workload(args.workload, io=args.io, per_channel=args.kda)
     io = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[x.io]
 
     per_copy = algorithmic_bytes(x)
@@ -323,10 +346,17 @@ def main() -> int:
                          o=torch.empty((x.T_tot, x.Hv, x.Dv), dtype=io, device=dev),
                          fs=torch.empty((x.N, x.Hv, x.Dv, x.Dk), dtype=torch.float32, device=dev)))
 
+    ws = (torch.empty(gdn.kda_workspace_size(x.N, x.T_tot, x.Hv), dtype=torch.uint8, device=dev)
+          if args.kda else None)
+
     def step(i):
         s = sets[i % copies]
-        gdn.prefill(s["q"], s["k"], s["v"], s["g"], s["beta"], s["init"], s["cu"],
-                    out=s["o"], final_state=s["fs"])
+        if args.kda:
+            gdn.kda_prefill(s["q"], s["k"], s["v"], s["g"], s["beta"], s["init"], s["cu"],
+                            out=s["o"], final_state=s["fs"], workspace=ws)
+        else:
+            gdn.prefill(s["q"], s["k"], s["v"], s["g"], s["beta"], s["init"], s["cu"],
+                        out=s["o"], final_state=s["fs"])
 
     for i in range(args.warmup):
         step(i)
@@ -367,11 +397,21 @@ def main() -> int:
     nbytes = algorithmic_bytes(x)
     flops = algorithmic_flops(x)
     sec = ms_per_step / 1e3
-    plan = gdn.prefill_plan(x.N, x.Hv, IO_CODE[x.io])
-    kernel = "gdn_prefill_pipe_kernel" if plan["threads_per_workgroup"] == 512 else "gdn_prefill_kernel"
+    if args.kda:
+        kernel = "kda_map_kernel+kda_chain_kernel"
+        launch = {"kernel": kernel, "map_workgroups": (x.T_tot // 64 + x.N) * x.Hv,
+                  "chain_workgroups": x.N * x.Hv * 8, "workspace_bytes": int(ws.numel()),
+                  "input_copies_rotated": copies}
+    else:
+        plan = gdn.prefill_plan(x.N, x.Hv, IO_CODE[x.io])
+        kernel = "gdn_prefill_pipe_kernel" if plan["threads_per_workgroup"] == 512 else "gdn_prefill_kernel"
+        launch = {"kernel": kernel,
+                  "dv_per_workgroup": plan["dv_per_workgroup"], "workgroups": plan["workgroups"],
+                  "lds_bytes": plan["lds_bytes"], "threads": plan["threads_per_workgroup"],
+                  "input_copies_rotated": copies}
     mfma_peak = FP32_MFMA_PEAK_TFLOPS if x.io == "f32" else BF16_MFMA_PEAK_TFLOPS  # fp16 = bf16 rate
     rec = {
-        "metric": METRIC,
+        "metric": KDA_METRIC.format(H=x.Hv, T=x.T_tot) if args.kda else METRIC,
         "value": tokens / sec,
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -392,10 +432,7 @@ def main() -> int:
         "mfma": {"achieved": flops / sec / 1e12, "peak": mfma_peak, "unit": "TFLOP/s",
                  "frac": flops / sec / 1e12 / mfma_peak, "algorithmic_flops": flops},
         "algorithmic_bytes": nbytes,
-        "launch": {"kernel": kernel,
-                   "dv_per_workgroup": plan["dv_per_workgroup"], "workgroups": plan["workgroups"],
-                   "lds_bytes": plan["lds_bytes"], "threads": plan["threads_per_workgroup"],
-                   "input_copies_rotated": copies},
+        "launch": launch,
         "wall_s_timed": wall,
         "parity": parity,
     }
