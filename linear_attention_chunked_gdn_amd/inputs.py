@@ -125,18 +125,24 @@ class GDNInputs:
 
 
 def draw_tokens(rng: np.random.Generator, T: int, Hk: int, Hv: int, Dk: int, Dv: int,
-                io: str, g_shift: float = 0.0, per_channel: bool = False):
+                io: str, g_shift: float = 0.0, per_channel: bool = False, raw: bool = False):
     """Draw q, k, v, beta, g for T tokens in the fixed order q, k, v, beta-logits, g-logits
-    (g-logits [T, Hv, Dk] for a per-key-channel gate)."""
+    (g-logits [T, Hv, Dk] for a per-key-channel gate).  raw: return the draws as a
+    linear-attention layer's projections would hand them over -- q, k not normalised,
+    beta and g as their logits (g-logits plus g_shift) -- for the fused prologue."""
     q = rng.standard_normal((T, Hk, Dk), dtype=np.float32)
     k = rng.standard_normal((T, Hk, Dk), dtype=np.float32)
     v = rng.standard_normal((T, Hv, Dv), dtype=np.float32)
     beta_logit = rng.standard_normal((T, Hv), dtype=np.float32)
     g_logit = rng.standard_normal((T, Hv, Dk) if per_channel else (T, Hv), dtype=np.float32)
-    q = _l2_normalize(q)
-    k = _l2_normalize(k)
-    beta = _sigmoid64(beta_logit).astype(np.float32)
-    g = (-_softplus64(g_logit.astype(np.float64) + g_shift)).astype(np.float32)
+    if raw:
+        beta = beta_logit
+        g = (g_logit.astype(np.float64) + g_shift).astype(np.float32)
+    else:
+        q = _l2_normalize(q)
+        k = _l2_normalize(k)
+        beta = _sigmoid64(beta_logit).astype(np.float32)
+        g = (-_softplus64(g_logit.astype(np.float64) + g_shift)).astype(np.float32)
     if io == "bf16":
         q, k, v = round_to_bf16(q), round_to_bf16(k), round_to_bf16(v)
     elif io == "f16":
@@ -148,14 +154,15 @@ def draw_tokens(rng: np.random.Generator, T: int, Hk: int, Hv: int, Dk: int, Dv:
 
 def make_custom(seed: int, lengths, Hk: int, Hv: int, Dk: int = 128, Dv: int = 128,
                 io: str = "bf16", g_shift: float = 0.0, init_std: Optional[float] = None,
-                name: str = "custom", per_channel: bool = False) -> GDNInputs:
-    """Packed batch of sequences with the given lengths (any may be 0)."""
+                name: str = "custom", per_channel: bool = False, raw: bool = False) -> GDNInputs:
+    """Packed batch of sequences with the given lengths (any may be 0); raw as in
+    draw_tokens."""
     rng = np.random.default_rng(seed)
     lengths = np.asarray(list(lengths), dtype=np.int64)
     cu = np.zeros(len(lengths) + 1, dtype=np.int32)
     cu[1:] = np.cumsum(lengths)
     T = int(cu[-1])
-    q, k, v, g, beta = draw_tokens(rng, T, Hk, Hv, Dk, Dv, io, g_shift, per_channel)
+    q, k, v, g, beta = draw_tokens(rng, T, Hk, Hv, Dk, Dv, io, g_shift, per_channel, raw)
     s0 = None
     if init_std is not None:
         s0 = (rng.standard_normal((len(lengths), Hv, Dv, Dk), dtype=np.float32)

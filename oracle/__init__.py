@@ -157,6 +157,48 @@ def max_threads(lib=None) -> int:
 
 
 # --------------------------------------------------------------------------------------
+# Input prologue (numpy, fp64): the steps that turn a linear-attention layer's projection
+# outputs into the recurrence's inputs -- q, k scaled to unit L2 norm per (token, head),
+# beta = sigmoid(x), g = -softplus(x) -- which the fused entry points apply while
+# loading.  Flags as in include/gdn.h: 1 = q/k L2 norm, 2 = beta sigmoid, 4 = g softplus.
+# Plain definitions: x / max(||x||_2, 1e-12); 1 / (1 + e^-x); softplus(x) = log(1 + e^x),
+# evaluated as max(x, 0) + log1p(e^-|x|) so that it cannot overflow.
+# --------------------------------------------------------------------------------------
+
+PROLOGUE_QK_L2NORM = 1
+PROLOGUE_BETA_SIGMOID = 2
+PROLOGUE_G_SOFTPLUS = 4
+
+
+def l2_normalize(x) -> np.ndarray:
+    x = _f64(x)
+    norm = np.sqrt(np.sum(x * x, axis=-1, keepdims=True))
+    return x / np.maximum(norm, 1e-12)
+
+
+def sigmoid(x) -> np.ndarray:
+    x = _f64(x)
+    return 1.0 / (1.0 + np.exp(-x))
+
+
+def softplus(x) -> np.ndarray:
+    x = _f64(x)
+    return np.maximum(x, 0.0) + np.log1p(np.exp(-np.abs(x)))
+
+
+def prologue(q, k, g, beta, flags: int):
+    """(q, k, g, beta) after the prologue steps selected by flags (fp64)."""
+    q, k, g, beta = map(_f64, (q, k, g, beta))
+    if flags & PROLOGUE_QK_L2NORM:
+        q, k = l2_normalize(q), l2_normalize(k)
+    if flags & PROLOGUE_BETA_SIGMOID:
+        beta = sigmoid(beta)
+    if flags & PROLOGUE_G_SOFTPLUS:
+        g = -softplus(g)
+    return q, k, g, beta
+
+
+# --------------------------------------------------------------------------------------
 # Chunkwise form (numpy, fp64): the Map-Reduce-Map pipeline, used to pin the algebra the
 # GPU kernels rely on.  Notation per chunk of n_c tokens, state S (Dv x Dk):
 #   Gamma = cumsum(g)  (op #1, Gate);  gamma = exp(Gamma)

@@ -373,3 +373,49 @@ KDA_PINS = [pin_kda_hand_example, pin_kda_bruteforce, pin_kda_beta_zero, pin_kda
             pin_kda_uniform_gate_is_gdn, pin_kda_chunked, pin_kda_state_passing, pin_kda_decode,
             pin_kda_varlen, pin_kda_gqa, pin_kda_linearity_and_permutation,
             pin_kda_key_permutation]
+
+
+# --------------------------------------------------------------------------------------
+# Input prologue: q/k L2 norm, beta = sigmoid, g = -softplus (the fused entry points).
+# --------------------------------------------------------------------------------------
+
+# P1. closed-form values and identities of the three maps
+def pin_prologue_values(_rec=None):
+    ln3 = np.log(3.0)
+    _close(oracle.sigmoid(np.array([0.0, ln3, -ln3])), [0.5, 0.75, 0.25], 1e-15, "sigmoid values")
+    _close(oracle.softplus(np.array([0.0, np.log(np.e - 1.0)])), [np.log(2.0), 1.0], 1e-15,
+           "softplus values")
+    x = np.linspace(-30.0, 30.0, 121)
+    _close(oracle.softplus(x) - oracle.softplus(-x), x, 1e-12, "softplus(x) - softplus(-x) = x")
+    _close(oracle.sigmoid(x) + oracle.sigmoid(-x), np.ones_like(x), 1e-15, "sigmoid symmetry")
+    # far tails: softplus(x) -> x and e^x, relative to their size
+    big = oracle.softplus(np.array([700.0, -700.0]))
+    assert big[0] == 700.0 and abs(big[1] / np.exp(-700.0) - 1.0) < 1e-12, "softplus tails"
+    rows = np.array([[3.0, 4.0, 0.0], [0.0, 0.0, 0.0], [1e-30, 0.0, 0.0]])
+    _close(oracle.l2_normalize(rows), [[0.6, 0.8, 0.0], [0.0, 0.0, 0.0], [1e-18, 0.0, 0.0]], 1e-15,
+           "l2 normalisation (3-4-5 row, zero row, a row below the 1e-12 floor)")
+    rng = np.random.default_rng(42)
+    y = rng.standard_normal((20, 3, 16))
+    _close(np.linalg.norm(oracle.l2_normalize(y), axis=-1), np.ones((20, 3)), 1e-14, "unit norms")
+    _close(oracle.l2_normalize(7.5 * y), oracle.l2_normalize(y), 1e-15, "scale invariance")
+
+
+# P2. the prologue applied by the oracle to raw draws equals the input generator's own
+#     recipe for the same draws (fp32 normalisation, fp64 sigmoid / softplus cast to fp32):
+#     two independent implementations, agreeing to fp32 rounding
+def pin_prologue_matches_generator(_rec=None):
+    from linear_attention_chunked_gdn_amd import inputs
+    for per_channel in (False, True):
+        raw = inputs.make_custom(51, [40, 9], 2, 4, Dk=16, Dv=8, io="f32", g_shift=1.0,
+                                 per_channel=per_channel, raw=True)
+        ref = inputs.make_custom(51, [40, 9], 2, 4, Dk=16, Dv=8, io="f32", g_shift=1.0,
+                                 per_channel=per_channel)
+        q, k, g, b = oracle.prologue(raw.q, raw.k, raw.g, raw.beta, 7)
+        _close(q, ref.q, 2e-7, "prologue q")
+        _close(k, ref.k, 2e-7, "prologue k")
+        _close(g, ref.g, 1e-6, "prologue g")
+        _close(b, ref.beta, 1e-7, "prologue beta")
+        _close(raw.v, ref.v, 0.0, "v is drawn the same")
+
+
+PROLOGUE_PINS = [pin_prologue_values, pin_prologue_matches_generator]

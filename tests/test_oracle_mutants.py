@@ -192,6 +192,38 @@ def test_kda_chunked_form_mutant_is_caught(monkeypatch, name, orig, repl):
         oracle_pins.pin_kda_chunked(oracle.recurrent)
 
 
+PROLOGUE_MUTANTS = [
+    ("sigmoid of -x", "sigmoid", "return 1.0 / (1.0 + np.exp(-x))", "return 1.0 / (1.0 + np.exp(x))"),
+    ("softplus without its max term", "softplus", "return np.maximum(x, 0.0) + np.log1p(np.exp(-np.abs(x)))",
+     "return np.log1p(np.exp(-np.abs(x)))"),
+    ("softplus as log(e^x) only", "softplus", "return np.maximum(x, 0.0) + np.log1p(np.exp(-np.abs(x)))",
+     "return np.maximum(x, 0.0)"),
+    ("L1 norm instead of L2", "l2_normalize", "norm = np.sqrt(np.sum(x * x, axis=-1, keepdims=True))",
+     "norm = np.sum(np.abs(x), axis=-1, keepdims=True)"),
+    ("norm over the head axis", "l2_normalize", "norm = np.sqrt(np.sum(x * x, axis=-1, keepdims=True))",
+     "norm = np.sqrt(np.sum(x * x, axis=-2, keepdims=True))"),
+    ("g = +softplus", "prologue", "g = -softplus(g)", "g = softplus(g)"),
+    ("beta flag ignored", "prologue", "beta = sigmoid(beta)", "beta = beta"),
+]
+
+
+@pytest.mark.parametrize("name,fn,orig,repl", PROLOGUE_MUTANTS, ids=[m[0] for m in PROLOGUE_MUTANTS])
+def test_prologue_mutant_is_caught(monkeypatch, name, fn, orig, repl):
+    src = textwrap.dedent(inspect.getsource(getattr(oracle, fn)))
+    assert orig in src, f"mutation anchor for {name!r} not found"
+    ns = dict(oracle.__dict__)
+    exec(compile(src.replace(orig, repl), "<mutant>", "exec"), ns)  # noqa: S102
+    monkeypatch.setattr(oracle, fn, ns[fn])
+    failed = 0
+    with np.errstate(all="ignore"):
+        for pin in oracle_pins.PROLOGUE_PINS:
+            try:
+                pin()
+            except (AssertionError, ValueError, FloatingPointError):
+                failed += 1
+    assert failed, f"mutant {name!r} passed every prologue pin"
+
+
 def test_mutation_anchor_list_is_current():
     with open(SRC) as f:
         src = f.read()

@@ -34,6 +34,11 @@ def test_kda_rejects_bad_gate_shape():
         oracle.recurrent(**c)
 
 
+@pytest.mark.parametrize("pin", oracle_pins.PROLOGUE_PINS, ids=lambda p: p.__name__)
+def test_prologue_pin(pin):
+    pin()
+
+
 def test_chunked_form_at_full_head_size():
     # d = 128, chunk 64: the size at which the pages report ~1e-11 agreement
     oracle_pins.pin_chunked(oracle.recurrent, big=True)
