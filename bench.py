@@ -1,7 +1,7 @@
 """Throughput of the chunked gated delta-rule prefill on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload I] [--io bf16|f16|f32]
-                    [--kda] [--no-cpu-baseline]
+                    [--kda] [--prologue] [--no-cpu-baseline]
 
 A step is one gdn_prefill call over the whole workload (all heads, all chunks) with
 inputs resident in HBM.  The default workload is the headline one: one sequence of
@@ -31,6 +31,10 @@ a bf16 GEMM measured on this GPU, beside the published peaks used for the fracti
 
 cpu_baseline: the fp64 CPU oracle (test infrastructure, untuned) timed on the host
 cores over the same workload.
+
+--prologue: the same workload's draws before the input prologue (q, k unnormalised,
+beta and g logits), run through gdn_prefill_fused with all three prologue steps; the
+oracle applies the same steps for the parity block.
 
 --kda: the same workload with one decay per key channel (gdn_kda_prefill: a
 chunk-parallel map kernel, then the chain kernel, over a workspace allocated once
@@ -68,6 +72,8 @@ IO_CODE = {"f32": 0, "bf16": 1, "f16": 2}   # gdn_dtype
 KERNEL_SOURCES = {
     "gdn_prefill_pipe_kernel": ["gdn_prefill_pipe.hip", "gdn_device.h", "gdn_launch.h"],
     "gdn_prefill_kernel": ["gdn_prefill.hip", "gdn_device.h", "gdn_launch.h"],
+    "gdn_prefill_pipe_kernel(prologue)": ["gdn_prefill_pipe.hip", "gdn_prefill_pipe_prologue.hip",
+                                          "gdn_device.h", "gdn_launch.h"],
     "kda_map_kernel+kda_chain_kernel": ["kda_map.hip", "kda_chain.hip", "gdn_device.h", "gdn_launch.h"],
 }
 
@@ -157,15 +163,16 @@ def algorithmic_flops(x, C: int = 64) -> int:
     return total
 
 
-def cpu_baseline(x, min_repeats: int = 3, min_seconds: float = 5.0) -> dict:
-    """Median wall time of whole-workload oracle runs: at least min_repeats runs and at
-    least min_seconds of CPU work in total."""
+def cpu_baseline(x, min_repeats: int = 3, min_seconds: float = 5.0, prologue: int = 0) -> dict:
+    """Median wall time of whole-workload oracle runs (with the input prologue's steps
+    when given): at least min_repeats runs and at least min_seconds of CPU work in total."""
     import oracle
     oracle.load_library()
     times = []
     while len(times) < min_repeats or sum(times) < min_seconds:
         t0 = time.perf_counter()
-        oracle.recurrent(x.q, x.k, x.v, x.g, x.beta, x.initial_state, x.cu_seqlens)
+        q, k, g, b = oracle.prologue(x.q, x.k, x.g, x.beta, prologue)
+        oracle.recurrent(q, k, x.v, g, b, x.initial_state, x.cu_seqlens)
         times.append(time.perf_counter() - t0)
     repeats = len(times)
     dt = float(np.median(times))
@@ -295,6 +302,8 @@ def main() -> int:
                     help="storage type of q, k, v, o (default: the workload's own)")
     ap.add_argument("--kda", action="store_true",
                     help="one decay per key channel (gdn_kda_prefill) on the same workload")
+    ap.add_argument("--prologue", action="store_true",
+                    help="raw inputs through gdn_prefill_fused with the q/k norm, sigmoid and softplus steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rotate-bytes", type=int, default=2 * MALL_BYTES,
                     help="input copies are rotated until they span at least this many bytes")
@@ -331,7 +340,11 @@ def main() -> int:
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    x = inputs.make_workload(args.workload, io=args.io, per_channel=args.kda)
+    if args.prologue and args.kda:
+        print("bench.py: --prologue applies to the scalar-gate prefill only", file=sys.stderr)
+        return 2
+    x = inputs.make_workload(args.workload, io=args.io, per_channel=args.kda, raw=args.prologue)
+    pro = gdn.PROLOGUE_ALL if args.prologue else 0
     io = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[x.io]
 
     per_copy = algorithmic_bytes(x)
@@ -356,7 +369,7 @@ def main() -> int:
                             out=s["o"], final_state=s["fs"], workspace=ws)
         else:
             gdn.prefill(s["q"], s["k"], s["v"], s["g"], s["beta"], s["init"], s["cu"],
-                        out=s["o"], final_state=s["fs"])
+                        out=s["o"], final_state=s["fs"], prologue=pro)
 
     for i in range(args.warmup):
         step(i)
@@ -382,7 +395,8 @@ def main() -> int:
         sys.path.insert(0, os.path.join(ROOT, "tests"))
         from gpu_support import error_stats
         s = sets[(args.steps - 1) % copies]
-        ro, rf = oracle.recurrent(x.q, x.k, x.v, x.g, x.beta, x.initial_state, x.cu_seqlens)
+        q_, k_, g_, b_ = oracle.prologue(x.q, x.k, x.g, x.beta, pro)
+        ro, rf = oracle.recurrent(q_, k_, x.v, g_, b_, x.initial_state, x.cu_seqlens)
         from gpu_support import TOL_BF16_REL_RMS, TOL_F32_ABS
         half = x.io != "f32"
         eo = error_stats(s["o"].double().cpu().numpy(), ro, storage=x.io if half else None)
@@ -405,7 +419,9 @@ def main() -> int:
     else:
         plan = gdn.prefill_plan(x.N, x.Hv, IO_CODE[x.io])
         kernel = "gdn_prefill_pipe_kernel" if plan["threads_per_workgroup"] == 512 else "gdn_prefill_kernel"
-        launch = {"kernel": kernel,
+        if pro:
+            kernel += "(prologue)"
+        launch = {"kernel": kernel, "prologue_flags": pro,
                   "dv_per_workgroup": plan["dv_per_workgroup"], "workgroups": plan["workgroups"],
                   "lds_bytes": plan["lds_bytes"], "threads": plan["threads_per_workgroup"],
                   "input_copies_rotated": copies}
@@ -440,7 +456,7 @@ def main() -> int:
         rec["decode"] = decode_bench(x, dev, sets[(args.steps - 1) % copies]["fs"])
     rec["measured_peaks"] = measured_peaks(dev)
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(x)
+        rec["cpu_baseline"] = cpu_baseline(x, prologue=pro)
     print(json.dumps(rec), flush=True)
     return 0
 

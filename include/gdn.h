@@ -54,6 +54,22 @@ typedef enum gdn_dtype {
 } gdn_dtype;
 
 /*
+ * Input prologue flags (bitwise or) of gdn_prefill_fused and gdn_decode_step_fused: the
+ * steps that turn a linear-attention layer's projection outputs into the recurrence's
+ * inputs, applied inside the kernels' load path.  "Empowering Hybrid Attention Models on
+ * NPUs", section 7 (the full-layer implementation notes before 7.1), counts a layer's
+ * input projections as part of it and fuses their operators; these are the elementwise
+ * and per-row steps between those projections and the recurrence.
+ */
+typedef enum gdn_prologue_flags {
+    GDN_PROLOGUE_QK_L2NORM = 1,     /* q, k rows (per token and key head) divided by
+                                       max(||x||_2, 1e-12), computed in fp32           */
+    GDN_PROLOGUE_BETA_SIGMOID = 2,  /* beta = 1 / (1 + exp(-x)) of the beta argument    */
+    GDN_PROLOGUE_G_SOFTPLUS = 4     /* g = -softplus(x) = -log(1 + exp(x)) of the g
+                                       argument, so the decay exp(g) lies in (0, 1)     */
+} gdn_prologue_flags;
+
+/*
  * gdn_prefill -- packed variable-length chunked prefill.
  *
  * Operation: the recurrence above over every sequence of a packed batch, each
@@ -106,6 +122,30 @@ gdn_status gdn_decode_step(const void *q, const void *k, const void *v,
                            const float *g, const float *beta, float *state,
                            int32_t B, int32_t Hk, int32_t Hv, int32_t Dk, int32_t Dv,
                            gdn_dtype io_dtype, void *o, void *stream);
+
+/*
+ * gdn_prefill_fused -- gdn_prefill with the input prologue applied in the kernel's load
+ * path: `prologue` is a bitwise or of gdn_prologue_flags, and q, k, g, beta are the
+ * values before the selected steps (unnormalised q/k rows, beta and g logits).  The L2
+ * norms are taken in fp32 from the stored q/k and folded into the kernel's per-row
+ * factors, so q and k themselves enter the products unchanged.  io_dtype GDN_BF16 or
+ * GDN_F16 (GDN_F32 returns GDN_ERR_UNSUPPORTED); unknown flag bits return
+ * GDN_ERR_INVALID_ARGUMENT.  Everything else as gdn_prefill.
+ */
+gdn_status gdn_prefill_fused(const void *q, const void *k, const void *v,
+                             const float *g, const float *beta,
+                             const float *initial_state, const int32_t *cu_seqlens,
+                             int32_t N, int32_t T_tot, int32_t Hk, int32_t Hv,
+                             int32_t Dk, int32_t Dv, int32_t chunk_size, gdn_dtype io_dtype,
+                             uint32_t prologue, void *o, float *final_state, void *stream);
+
+/*
+ * gdn_decode_step_fused -- gdn_decode_step with the input prologue (any io_dtype).
+ */
+gdn_status gdn_decode_step_fused(const void *q, const void *k, const void *v,
+                                 const float *g, const float *beta, float *state,
+                                 int32_t B, int32_t Hk, int32_t Hv, int32_t Dk, int32_t Dv,
+                                 gdn_dtype io_dtype, uint32_t prologue, void *o, void *stream);
 
 /*
  * Per-key-channel decay (KDA).  The gate of this variant of the delta rule is "fine

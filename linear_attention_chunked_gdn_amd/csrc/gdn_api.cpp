@@ -50,6 +50,7 @@ bool overlap(const Range &a, const Range &b) {
 }
 
 constexpr int kD = 128;
+constexpr uint32_t kPrologueAll = GDN_PROLOGUE_QK_L2NORM | GDN_PROLOGUE_BETA_SIGMOID | GDN_PROLOGUE_G_SOFTPLUS;
 constexpr int kChunk = 64;
 
 // Kernel choice.  bf16 and fp16 I/O run the software-pipelined kernel (16 value
@@ -197,12 +198,43 @@ gdn_status gdn_prefill(const void *q, const void *k, const void *v, const float 
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
     a.s0 = initial_state; a.cu = cu_seqlens; a.o = o; a.sN = final_state;
     a.N = N; a.T_tot = T_tot; a.Hk = Hk; a.Hv = Hv; a.nslices = kD / dvs;
+    a.prologue = 0;
     const Plan p = choose_plan(io_dtype);
     (void)hipGetLastError();
     const hipError_t e = p.pipe ? gdn::launch_prefill_pipe(a, io_dtype == GDN_F16, wg,
                                                            static_cast<hipStream_t>(stream))
                                 : gdn::launch_prefill(a, io_dtype == GDN_BF16, dvs, wg,
                                                       static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return fail(GDN_ERR_DEVICE, "prefill launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+gdn_status gdn_prefill_fused(const void *q, const void *k, const void *v, const float *g,
+                             const float *beta, const float *initial_state, const int32_t *cu_seqlens,
+                             int32_t N, int32_t T_tot, int32_t Hk, int32_t Hv, int32_t Dk, int32_t Dv,
+                             int32_t chunk_size, gdn_dtype io_dtype, uint32_t prologue, void *o,
+                             float *final_state, void *stream) {
+    const gdn_status cs = check_prefill(q, k, v, g, beta, initial_state, cu_seqlens, N, T_tot, Hk, Hv, Dk,
+                                        Dv, chunk_size, io_dtype, o, final_state, 1, nullptr, 0);
+    if (cs != GDN_OK) return cs;
+    if (prologue & ~kPrologueAll)
+        return fail(GDN_ERR_INVALID_ARGUMENT, "prologue flags 0x%x include unknown bits", prologue);
+    if (io_dtype == GDN_F32)
+        return fail(GDN_ERR_UNSUPPORTED, "gdn_prefill_fused takes bf16 or fp16 q, k, v, o");
+    int32_t dvs = 0, wg = 0;
+    gdn_status ps = gdn_prefill_plan(N, Hv, Dv, io_dtype, &dvs, &wg, nullptr, nullptr);
+    if (ps != GDN_OK) return ps;
+    if (T_tot == 0 && !final_state) return ok();
+
+    gdn::PrefillArgs a;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
+    a.s0 = initial_state; a.cu = cu_seqlens; a.o = o; a.sN = final_state;
+    a.N = N; a.T_tot = T_tot; a.Hk = Hk; a.Hv = Hv; a.nslices = kD / dvs;
+    a.prologue = prologue;
+    (void)hipGetLastError();
+    const hipError_t e = gdn::launch_prefill_pipe_prologue(a, io_dtype == GDN_F16, wg,
+                                                           static_cast<hipStream_t>(stream));
     if (e != hipSuccess)
         return fail(GDN_ERR_DEVICE, "prefill launch failed: %s", hipGetErrorString(e));
     return ok();
@@ -261,7 +293,9 @@ namespace {
 
 gdn_status decode_impl(const void *q, const void *k, const void *v, const float *g, const float *beta,
                        float *state, int32_t B, int32_t Hk, int32_t Hv, int32_t Dk, int32_t Dv,
-                       gdn_dtype io_dtype, void *o, void *stream, bool per_channel) {
+                       gdn_dtype io_dtype, void *o, void *stream, bool per_channel, uint32_t prologue) {
+    if (prologue & ~kPrologueAll)
+        return fail(GDN_ERR_INVALID_ARGUMENT, "prologue flags 0x%x include unknown bits", prologue);
     if (!valid_dtype(io_dtype))
         return fail(GDN_ERR_INVALID_ARGUMENT, "io_dtype %d is not GDN_F32, GDN_BF16 or GDN_F16", (int)io_dtype);
     if (B < 1 || Hk < 1 || Hv < 1)
@@ -294,6 +328,7 @@ gdn_status decode_impl(const void *q, const void *k, const void *v, const float 
     gdn::DecodeArgs a;
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.state = state; a.o = o;
     a.B = B; a.Hk = Hk; a.Hv = Hv;
+    a.prologue = prologue;
     (void)hipGetLastError();
     const hipStream_t hs = static_cast<hipStream_t>(stream);
     const hipError_t e = per_channel ? gdn::launch_kda_decode(a, (int)io_dtype, hs)
@@ -310,13 +345,20 @@ extern "C" {
 gdn_status gdn_decode_step(const void *q, const void *k, const void *v, const float *g,
                            const float *beta, float *state, int32_t B, int32_t Hk, int32_t Hv,
                            int32_t Dk, int32_t Dv, gdn_dtype io_dtype, void *o, void *stream) {
-    return decode_impl(q, k, v, g, beta, state, B, Hk, Hv, Dk, Dv, io_dtype, o, stream, false);
+    return decode_impl(q, k, v, g, beta, state, B, Hk, Hv, Dk, Dv, io_dtype, o, stream, false, 0);
+}
+
+gdn_status gdn_decode_step_fused(const void *q, const void *k, const void *v, const float *g,
+                                 const float *beta, float *state, int32_t B, int32_t Hk, int32_t Hv,
+                                 int32_t Dk, int32_t Dv, gdn_dtype io_dtype, uint32_t prologue, void *o,
+                                 void *stream) {
+    return decode_impl(q, k, v, g, beta, state, B, Hk, Hv, Dk, Dv, io_dtype, o, stream, false, prologue);
 }
 
 gdn_status gdn_kda_decode_step(const void *q, const void *k, const void *v, const float *g,
                                const float *beta, float *state, int32_t B, int32_t Hk, int32_t Hv,
                                int32_t Dk, int32_t Dv, gdn_dtype io_dtype, void *o, void *stream) {
-    return decode_impl(q, k, v, g, beta, state, B, Hk, Hv, Dk, Dv, io_dtype, o, stream, true);
+    return decode_impl(q, k, v, g, beta, state, B, Hk, Hv, Dk, Dv, io_dtype, o, stream, true, 0);
 }
 
 }  // extern "C"

@@ -17,6 +17,10 @@
 // With a per-key-channel gate (KDA: g is [B, Hv, 128]) the scalar alpha becomes
 // Diag(a), a_j = exp(g_j), on the key index, applied before the erase:
 //   S <- S Diag(a) (I - beta k k^T) + beta v k^T:  D = S Diag(a), S = D - beta (D k) k^T + beta v k^T.
+//
+// DecodeArgs::prologue (GDN_PROLOGUE_* flags) applies the input prologue first: q and k
+// divided by max(||x||_2, 1e-12) (the norms reduced over the row's 16 lanes), beta =
+// sigmoid(beta), g = -softplus(g) (per channel for the per-channel gate).
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
@@ -47,6 +51,9 @@ __device__ __forceinline__ float sum16(float x) {
     return x;
 }
 
+// softplus(x) = max(x, 0) + log(1 + e^-|x|), which cannot overflow
+__device__ __forceinline__ float softplus_f(float x) { return fmaxf(x, 0.f) + __logf(1.f + __expf(-fabsf(x))); }
+
 template <typename IO, bool PER_CHANNEL>
 __global__ __launch_bounds__(256) void gdn_decode_kernel(const DecodeArgs a) {
     constexpr int RB = DEC_D / DEC_ROWS;
@@ -69,7 +76,24 @@ __global__ __launch_bounds__(256) void gdn_decode_kernel(const DecodeArgs a) {
     load8_io<IO>(a.q, koff, qq);
     const size_t voff = ((size_t)b * a.Hv + h) * DEC_D + row;
     const float vi = Cvt<IO>::to_f32(reinterpret_cast<const IO *>(a.v)[voff]);
-    const float beta = a.beta[(size_t)b * a.Hv + h];
+    if (a.prologue & GDN_PROLOGUE_QK_L2NORM) {
+        float sk = 0.f, sq = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            sk += kk[i] * kk[i];
+            sq += qq[i] * qq[i];
+        }
+        const float rk = 1.f / fmaxf(sqrtf(sum16(sk)), 1e-12f);
+        const float rq = 1.f / fmaxf(sqrtf(sum16(sq)), 1e-12f);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            kk[i] *= rk;
+            qq[i] *= rq;
+        }
+    }
+    float beta = a.beta[(size_t)b * a.Hv + h];
+    if (a.prologue & GDN_PROLOGUE_BETA_SIGMOID) beta = 1.f / (1.f + __expf(-beta));
+    const bool do_softplus = a.prologue & GDN_PROLOGUE_G_SOFTPLUS;
     float o = 0.f;
     if constexpr (PER_CHANNEL) {
         float gg[8];
@@ -77,6 +101,7 @@ __global__ __launch_bounds__(256) void gdn_decode_kernel(const DecodeArgs a) {
         float u = 0.f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
+            if (do_softplus) gg[i] = -softplus_f(gg[i]);
             S[i] *= __expf(gg[i]);                // S Diag(a)
             u += S[i] * kk[i];
         }
@@ -89,7 +114,9 @@ __global__ __launch_bounds__(256) void gdn_decode_kernel(const DecodeArgs a) {
             o += S[i] * qq[i];
         }
     } else {
-        const float alpha = __expf(a.g[(size_t)b * a.Hv + h]);
+        float gs = a.g[(size_t)b * a.Hv + h];
+        if (do_softplus) gs = -softplus_f(gs);
+        const float alpha = __expf(gs);
         float u = 0.f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) u += S[i] * kk[i];

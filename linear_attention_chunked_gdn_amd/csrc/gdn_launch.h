@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "gdn.h"
+
 namespace gdn {
 
 struct PrefillArgs {
@@ -18,6 +20,7 @@ struct PrefillArgs {
     float *sN;              // [N, Hv, 128, 128] or null
     int32_t N, T_tot, Hk, Hv;
     int32_t nslices;        // value-channel slices per (sequence, head)
+    uint32_t prologue;      // GDN_PROLOGUE_* flags (the prologue kernel only)
 };
 
 struct DecodeArgs {
@@ -26,6 +29,7 @@ struct DecodeArgs {
     float *state;           // [B, Hv, 128, 128]
     void *o;                // [B, Hv, 128]
     int32_t B, Hk, Hv;
+    uint32_t prologue;      // GDN_PROLOGUE_* flags
 };
 
 // Per-key-channel decay (KDA): g is [T_tot, Hv, 128].  The map kernel writes one
@@ -71,5 +75,8 @@ hipError_t launch_decode(const DecodeArgs &a, int io, hipStream_t stream);
 hipError_t launch_prefill_pipe(const PrefillArgs &a, bool f16, int grid, hipStream_t stream);
 int prefill_pipe_lds_bytes();
 int prefill_pipe_threads();
+// The same kernel with the fused input prologue (a.prologue flags).
+hipError_t launch_prefill_pipe_prologue(const PrefillArgs &a, bool f16, int grid, hipStream_t stream);
+int prefill_pipe_prologue_lds_bytes();
 
 }  // namespace gdn

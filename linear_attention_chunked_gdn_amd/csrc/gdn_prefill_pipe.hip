@@ -40,13 +40,32 @@
 // their lifetimes do not overlap across the phases (the diagonal tiles of A(c+1) and
 // the blocks of A(c) below it, read in the same phase, are disjoint).
 // One workgroup = 8 wave64s = one (sequence, value head, 16 value channels).
+//
+// Fused input prologue (compiled when GDN_PIPE_PROLOGUE is 1, by
+// gdn_prefill_pipe_prologue.hip, as a kernel of its own): q and k arrive unnormalised and
+// beta, g as their logits.  The gate scan applies beta = sigmoid(x) and g = -softplus(x).
+// The L2 norms of the q and k rows are reduced in fp32 while the rows are staged (the
+// 16 lanes that commit a row), and 1 / ||row|| is kept per token; q and k stay exact
+// 16-bit MFMA operands and the reciprocal norms are folded into the per-row factors the
+// kernel applies anyway: the grams' decay factors (r_row * r_col), beta gamma in R,
+// lambda in the update and gamma on Q S^T.
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
 #include <type_traits>
 
+#ifndef GDN_PIPE_PROLOGUE
+#define GDN_PIPE_PROLOGUE 0
+#endif
+
 namespace gdn {
+#if GDN_PIPE_PROLOGUE
+namespace pipe_pro {
+#else
 namespace pipe {
+#endif
+
+constexpr bool PRO = GDN_PIPE_PROLOGUE != 0;
 
 constexpr int CH = 64;        // chunk length
 constexpr int DK = 128;
@@ -80,6 +99,9 @@ struct Gate {
     float g2[CH];     // Gamma_t * log2(e)
     float u[CH];      // exp(Gamma_t - Gamma at the first token of t's 16-token block)
     float w[3][CH];   // w[i-1][s] = exp(Gamma_16i - Gamma_s) for s < 16i, else 0
+#if GDN_PIPE_PROLOGUE
+    float rn[2][CH];  // 1 / ||k_t|| and 1 / ||q_t|| (input prologue)
+#endif
 };
 
 template <typename IO>
@@ -202,6 +224,26 @@ struct StageQ {
     u32x4 q0, q1;
 };
 
+// 1 / max(||x||_2, 1e-12) for the row whose 16-byte pieces (8 values each) the 16 lanes
+// of this lane's DPP row hold; every lane of the row gets the result (row rotations).
+template <typename IO>
+__device__ __forceinline__ float row_rnorm(const u32x4 &piece) {
+    typedef IO v8 __attribute__((ext_vector_type(8)));
+    const v8 x = __builtin_bit_cast(v8, piece);
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float f = Cvt<IO>::to_f32(x[e]);
+        ss += f * f;
+    }
+    // row_ror:8, 4, 2, 1 (dpp_ctrl 0x120 + n)
+    ss += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(ss), 0x128, 0xF, 0xF, false));
+    ss += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(ss), 0x124, 0xF, 0xF, false));
+    ss += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(ss), 0x122, 0xF, 0xF, false));
+    ss += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(ss), 0x121, 0xF, 0xF, false));
+    return __builtin_amdgcn_rsqf(fmaxf(ss, 1e-24f));   // 1 / max(||x||, 1e-12)
+}
+
 // Rows of the staged tiles a thread loads: k and q rows tid/16 and tid/16 + 32 (16-byte
 // segment tid%16); v row tid/8 (4-byte piece tid%8); g, beta row tid%64.  Every thread
 // loads and commits the same amount, with no branch around a load or an LDS write,
@@ -253,26 +295,56 @@ __device__ __forceinline__ int prefetch_tok(const Work &wk, int c, int nchunks) 
 }
 
 template <typename IO>
-__device__ __forceinline__ void stage_commit(const Stage &st, Smem<IO> &s, int buf, int tid) {
+__device__ __forceinline__ void stage_commit(const Stage &st, Smem<IO> &s, int buf, int tid, unsigned pro) {
     const int seg = tid & 15;
     *reinterpret_cast<u32x4 *>(&s.K[buf][(tid >> 4) * KS + seg * 8]) = st.k0;
     *reinterpret_cast<u32x4 *>(&s.K[buf][((tid + THREADS) >> 4) * KS + seg * 8]) = st.k1;
     *reinterpret_cast<unsigned *>(&s.V[buf][(tid >> 3) * VS + (tid & 7) * 2]) = st.v;
+#if GDN_PIPE_PROLOGUE
+    const bool norm = pro & GDN_PROLOGUE_QK_L2NORM;
+    const float r0 = norm ? row_rnorm<IO>(st.k0) : 1.f, r1 = norm ? row_rnorm<IO>(st.k1) : 1.f;
+    if (seg == 0) {
+        s.gate[buf].rn[0][tid >> 4] = r0;
+        s.gate[buf].rn[0][(tid + THREADS) >> 4] = r1;
+    }
+#else
+    (void)pro;
+#endif
 }
 
 template <typename IO>
-__device__ __forceinline__ void stage_commit_q(const StageQ &st, Smem<IO> &s, int tid) {
+__device__ __forceinline__ void stage_commit_q(const StageQ &st, Smem<IO> &s, int buf, int tid, unsigned pro) {
     const int seg = tid & 15;
     *reinterpret_cast<u32x4 *>(&s.Q[(tid >> 4) * KS + seg * 8]) = st.q0;
     *reinterpret_cast<u32x4 *>(&s.Q[((tid + THREADS) >> 4) * KS + seg * 8]) = st.q1;
+#if GDN_PIPE_PROLOGUE
+    const bool norm = pro & GDN_PROLOGUE_QK_L2NORM;
+    const float r0 = norm ? row_rnorm<IO>(st.q0) : 1.f, r1 = norm ? row_rnorm<IO>(st.q1) : 1.f;
+    if (seg == 0) {
+        s.gate[buf].rn[1][tid >> 4] = r0;
+        s.gate[buf].rn[1][(tid + THREADS) >> 4] = r1;
+    }
+#else
+    (void)buf;
+    (void)pro;
+#endif
 }
 
 // #1 Gate for the chunk staged in buffer buf, by map wave 3 (lane = token): the
 // inclusive scan of g and every decay factor the grams and the chain need.
 template <typename IO>
-__device__ __forceinline__ void gate_scan(const Stage &st, Smem<IO> &s, int buf, int lane) {
+__device__ __forceinline__ void gate_scan(const Stage &st, Smem<IO> &s, int buf, int lane, unsigned pro) {
     const bool valid = lane < st.nval;
-    const float x2 = wave_inclusive_scan(valid ? st.g : 0.f, lane) * LOG2E;
+    float g = st.g, beta = st.b;
+    if constexpr (PRO) {
+        // beta = sigmoid(x); g = -softplus(x) = -(max(x, 0) + log(1 + e^-|x|))
+        if (pro & GDN_PROLOGUE_BETA_SIGMOID) beta = 1.f / (1.f + __builtin_amdgcn_exp2f(-beta * LOG2E));
+        if (pro & GDN_PROLOGUE_G_SOFTPLUS)
+            g = -(fmaxf(g, 0.f) + __builtin_amdgcn_logf(1.f + __builtin_amdgcn_exp2f(-fabsf(g) * LOG2E)) / LOG2E);
+    } else {
+        (void)pro;
+    }
+    const float x2 = wave_inclusive_scan(valid ? g : 0.f, lane) * LOG2E;
     const float last2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x2), 63));
     const float b16 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x2), 16));
     const float b32 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x2), 32));
@@ -281,7 +353,7 @@ __device__ __forceinline__ void gate_scan(const Stage &st, Smem<IO> &s, int buf,
     const int blk = lane >> 4;
     const float start = blk == 0 ? b0 : blk == 1 ? b16 : blk == 2 ? b32 : b48;
     Gate &gt = s.gate[buf];
-    gt.beta[lane] = valid ? st.b : 0.f;
+    gt.beta[lane] = valid ? beta : 0.f;
     gt.g2[lane] = x2;
     gt.gam[lane] = __builtin_amdgcn_exp2f(x2);
     gt.lam[lane] = __builtin_amdgcn_exp2f(last2 - x2);
@@ -328,6 +400,14 @@ __device__ __forceinline__ f32x4 gram_scale(const Smem<IO> &s, int nb, int bi, i
 #pragma unroll
         for (int r = 0; r < 4; ++r) d[r] *= br;
     }
+#if GDN_PIPE_PROLOGUE
+    {
+        const float rrow = s.gate[nb].rn[ISQ ? 1 : 0][rr];
+        const f32x4 rcol = *reinterpret_cast<const f32x4 *>(&s.gate[nb].rn[0][c0]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) d[r] *= rrow * rcol[r];
+    }
+#endif
     return d;
 }
 
@@ -548,6 +628,10 @@ __device__ __forceinline__ void chain_R(Smem<IO> &s, int buf, int W, int l16, in
         bv[i] = b[i] * Cvt<IO>::to_f32(s.V[buf][(t0 + i) * VS + l16]);
         bg[i] = b[i] * gm[i];
     }
+#if GDN_PIPE_PROLOGUE
+    const f32x4 rk = *reinterpret_cast<const f32x4 *>(&s.gate[buf].rn[0][t0]);
+    bg *= rk;
+#endif
     f32x4 ks = zero4();
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
@@ -582,7 +666,12 @@ __device__ __forceinline__ f32x4 chain_QS(const Smem<IO> &s, int W, int l16, int
 template <typename IO>
 __device__ __forceinline__ void chain_v(Smem<IO> &s, int buf, int W, int l16, int g4) {
     const int t0 = 16 * W + 4 * g4;
+#if GDN_PIPE_PROLOGUE
+    const f32x4 lm = *reinterpret_cast<const f32x4 *>(&s.gate[buf].lam[t0]) *
+                     *reinterpret_cast<const f32x4 *>(&s.gate[buf].rn[0][t0]);
+#else
     const f32x4 lm = *reinterpret_cast<const f32x4 *>(&s.gate[buf].lam[t0]);
+#endif
     f32x4 acc = zero4();
     const hf *trow = s.T + (16 * W + l16) * TS + 8 * g4;
     for (int kb = 0; kb <= (W >> 1); ++kb) {
@@ -608,7 +697,11 @@ __device__ __forceinline__ void chain_out_update(Smem<IO> &s, const PrefillArgs 
                                                  int g4, const f32x4 &qs, f32x4 (&st)[2], int h,
                                                  int dv0, int tok0, int nval) {
     const int t = 16 * W + l16;
+#if GDN_PIPE_PROLOGUE
+    const float gm = s.gate[buf].gam[t] * s.gate[buf].rn[1][t];
+#else
     const float gm = s.gate[buf].gam[t];
+#endif
     const float glast = s.gate[buf].gam[CH - 1];
     {
         // O^T = S Q^T diag(gamma) + v^T P^T: lane = token 16W + l16, rows = value
@@ -716,15 +809,15 @@ __global__ __launch_bounds__(THREADS) void gdn_prefill_pipe_kernel(const Prefill
         StageQ stq;
         stage_load(stg, a, wk, wk.bos, min(CH, len), tid);
         stage_load_q(stq, a, wk, wk.bos, min(CH, len), tid);
-        stage_commit(stg, s, 0, tid);
-        stage_commit_q(stq, s, tid);
-        if (wave == 2) gate_scan(stg, s, 0, lane);
+        stage_commit(stg, s, 0, tid, a.prologue);
+        stage_commit_q(stq, s, 0, tid, a.prologue);
+        if (wave == 2) gate_scan(stg, s, 0, lane, a.prologue);
         {
             const int t1 = prefetch_tok(wk, 1, nchunks), n1 = min(CH, wk.eos - t1);
             stage_load(stg, a, wk, t1, n1, tid);
             stage_load_q(stq, a, wk, t1, n1, tid);
-            stage_commit(stg, s, 1, tid);
-            if (wave == 2) gate_scan(stg, s, 1, lane);
+            stage_commit(stg, s, 1, tid, a.prologue);
+            if (wave == 2) gate_scan(stg, s, 1, lane, a.prologue);
             const int t2 = prefetch_tok(wk, 2, nchunks), n2 = min(CH, wk.eos - t2);
             stage_load(stg, a, wk, t2, n2, tid);
         }
@@ -769,8 +862,8 @@ __global__ __launch_bounds__(THREADS) void gdn_prefill_pipe_kernel(const Prefill
                         if (has_next) gram_tiles<false, 0, 5, 10, -1>(s, b1, l16, g4);
                         break;
                 }
-                stage_commit(stg, s, b2, tid);
-                if (wave == 1) gate_scan(stg, s, b2, lane);
+                stage_commit(stg, s, b2, tid, a.prologue);
+                if (wave == 1) gate_scan(stg, s, b2, lane, a.prologue);
                 stage_load(stg, a, wk, t3, n3, tid);
                 __syncthreads();
                 // phase 2: A(c+1) below the diagonal; first half of its diagonal solve
@@ -778,7 +871,7 @@ __global__ __launch_bounds__(THREADS) void gdn_prefill_pipe_kernel(const Prefill
                     if (W == 3) diag_solve_first(s, l16, g4, xd);
                     else map_gram_kk_below(s, b1, W, l16, g4);
                 }
-                stage_commit_q(stq, s, tid);
+                stage_commit_q(stq, s, b1, tid, a.prologue);
                 stage_load_q(stq, a, wk, tq, nq, tid);
                 __syncthreads();
                 // phase 3: P(c+1); second half of the diagonal solve of T(c+1)
@@ -797,7 +890,7 @@ __global__ __launch_bounds__(THREADS) void gdn_prefill_pipe_kernel(const Prefill
             __syncthreads();
             __syncthreads();
             auto step = [&](auto bufc, int c) {
-                constexpr int b0 = decltype(bufc)::value, b2 = (b0 + 2) % NBUF;
+                constexpr int b0 = decltype(bufc)::value, b1 = (b0 + 1) % NBUF, b2 = (b0 + 2) % NBUF;
                 const int tok0 = wk.bos + c * CH;
                 const int nval = min(CH, wk.eos - tok0);
                 const int tq = prefetch_tok(wk, c + 2, nchunks), nq = min(CH, wk.eos - tq);
@@ -806,12 +899,12 @@ __global__ __launch_bounds__(THREADS) void gdn_prefill_pipe_kernel(const Prefill
                 Frag<IO> fs[4];
                 chain_R(s, b0, W, l16, g4, fs);
                 const f32x4 qs = chain_QS(s, W, l16, g4, fs);
-                stage_commit(stg, s, b2, tid);
+                stage_commit(stg, s, b2, tid, a.prologue);
                 stage_load(stg, a, wk, t3, n3, tid);
                 __syncthreads();
                 // phase 2
                 chain_v(s, b0, W, l16, g4);
-                stage_commit_q(stq, s, tid);
+                stage_commit_q(stq, s, b1, tid, a.prologue);
                 stage_load_q(stq, a, wk, tq, nq, tid);
                 __syncthreads();
                 // phase 3
@@ -835,8 +928,21 @@ __global__ __launch_bounds__(THREADS) void gdn_prefill_pipe_kernel(const Prefill
     }
 }
 
-}  // namespace pipe
+}  // namespace pipe / pipe_pro
 
+#if GDN_PIPE_PROLOGUE
+hipError_t launch_prefill_pipe_prologue(const PrefillArgs &a, bool f16, int grid, hipStream_t stream) {
+    if (f16)
+        hipLaunchKernelGGL(pipe_pro::gdn_prefill_pipe_kernel<pipe_pro::hf>, dim3(grid), dim3(pipe_pro::THREADS), 0,
+                           stream, a);
+    else
+        hipLaunchKernelGGL(pipe_pro::gdn_prefill_pipe_kernel<pipe_pro::bf>, dim3(grid), dim3(pipe_pro::THREADS), 0,
+                           stream, a);
+    return hipGetLastError();
+}
+
+int prefill_pipe_prologue_lds_bytes() { return (int)sizeof(pipe_pro::Smem<pipe_pro::bf>); }
+#else
 hipError_t launch_prefill_pipe(const PrefillArgs &a, bool f16, int grid, hipStream_t stream) {
     if (f16)
         hipLaunchKernelGGL(pipe::gdn_prefill_pipe_kernel<pipe::hf>, dim3(grid), dim3(pipe::THREADS), 0, stream, a);
@@ -848,5 +954,6 @@ hipError_t launch_prefill_pipe(const PrefillArgs &a, bool f16, int grid, hipStre
 int prefill_pipe_lds_bytes() { return (int)sizeof(pipe::Smem<pipe::bf>); }
 
 int prefill_pipe_threads() { return pipe::THREADS; }
+#endif
 
 }  // namespace gdn

@@ -21,6 +21,11 @@ from .build import LIB_PATH
 GDN_F32 = 0
 GDN_BF16 = 1
 GDN_F16 = 2
+# input prologue flags (gdn_prologue_flags)
+PROLOGUE_QK_L2NORM = 1
+PROLOGUE_BETA_SIGMOID = 2
+PROLOGUE_G_SOFTPLUS = 4
+PROLOGUE_ALL = 7
 D = 128
 CHUNK = 64
 
@@ -51,6 +56,12 @@ def load_library(path: str = LIB_PATH):
     p32 = ctypes.POINTER(ctypes.c_int32)
     lib.gdn_prefill_plan.argtypes = [i32, i32, i32, ctypes.c_int, p32, p32, p32, p32]
     lib.gdn_prefill_plan.restype = ctypes.c_int
+    lib.gdn_prefill_fused.argtypes = [vp, vp, vp, fp, fp, fp, ip, i32, i32, i32, i32, i32, i32, i32,
+                                      ctypes.c_int, ctypes.c_uint32, vp, fp, vp]
+    lib.gdn_prefill_fused.restype = ctypes.c_int
+    lib.gdn_decode_step_fused.argtypes = [vp, vp, vp, fp, fp, fp, i32, i32, i32, i32, i32, ctypes.c_int,
+                                          ctypes.c_uint32, vp, vp]
+    lib.gdn_decode_step_fused.restype = ctypes.c_int
     lib.gdn_kda_workspace_size.argtypes = [i32, i32, i32, i32, ctypes.POINTER(ctypes.c_size_t)]
     lib.gdn_kda_workspace_size.restype = ctypes.c_int
     lib.gdn_kda_prefill.argtypes = [vp, vp, vp, fp, fp, fp, ip, i32, i32, i32, i32, i32, i32, i32,
@@ -105,12 +116,14 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
             beta: torch.Tensor, initial_state: Optional[torch.Tensor] = None,
             cu_seqlens: Optional[torch.Tensor] = None, chunk_size: int = CHUNK,
             output_final_state: bool = True, out: Optional[torch.Tensor] = None,
-            final_state: Optional[torch.Tensor] = None, lib=None
+            final_state: Optional[torch.Tensor] = None, prologue: int = 0, lib=None
             ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Packed chunked prefill.  q, k: [T, Hk, 128]; v: [T, Hv, 128] (bf16, fp16 or fp32,
     all the same); g, beta: [T, Hv] fp32; initial_state: [N, Hv, 128, 128] fp32 or None;
     cu_seqlens: [N+1] int32 on the device, or None for one sequence.  Returns
-    (o [T, Hv, 128], final_state [N, Hv, 128, 128] fp32 or None)."""
+    (o [T, Hv, 128], final_state [N, Hv, 128, 128] fp32 or None).  A nonzero
+    ``prologue`` (PROLOGUE_* flags) calls gdn_prefill_fused: q, k, g, beta are then the
+    values before those steps."""
     lib = lib or load_library()
     dev = q.device
     if dev.type != "cuda":
@@ -137,18 +150,24 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
         _need(final_state, "final_state", torch.float32, (N, Hv, Dv, Dk), dev)
     with torch.cuda.device(dev):
         stream = torch.cuda.current_stream(dev).cuda_stream
-        st = lib.gdn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
-                             _ptr(cu_seqlens), N, T, Hk, Hv, Dk, Dv, chunk_size, io, _ptr(out),
-                             _ptr(final_state), ctypes.c_void_p(stream))
-    _check(lib, st, "gdn_prefill")
+        if prologue:
+            st = lib.gdn_prefill_fused(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
+                                       _ptr(cu_seqlens), N, T, Hk, Hv, Dk, Dv, chunk_size, io, prologue,
+                                       _ptr(out), _ptr(final_state), ctypes.c_void_p(stream))
+        else:
+            st = lib.gdn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
+                                 _ptr(cu_seqlens), N, T, Hk, Hv, Dk, Dv, chunk_size, io, _ptr(out),
+                                 _ptr(final_state), ctypes.c_void_p(stream))
+    _check(lib, st, "gdn_prefill_fused" if prologue else "gdn_prefill")
     return out, final_state
 
 
 def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
                 beta: torch.Tensor, state: torch.Tensor, out: Optional[torch.Tensor] = None,
-                lib=None) -> torch.Tensor:
+                prologue: int = 0, lib=None) -> torch.Tensor:
     """One token per sequence; ``state`` [B, Hv, 128, 128] fp32 is updated in place.
-    q, k: [B, Hk, 128]; v: [B, Hv, 128]; g, beta: [B, Hv].  Returns o [B, Hv, 128]."""
+    q, k: [B, Hk, 128]; v: [B, Hv, 128]; g, beta: [B, Hv].  Returns o [B, Hv, 128].
+    A nonzero ``prologue`` calls gdn_decode_step_fused."""
     lib = lib or load_library()
     dev = q.device
     if dev.type != "cuda":
@@ -166,9 +185,13 @@ def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tens
     _need(out, "out", q.dtype, (B, Hv, Dv), dev)
     with torch.cuda.device(dev):
         stream = torch.cuda.current_stream(dev).cuda_stream
-        st = lib.gdn_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state),
-                                 B, Hk, Hv, Dk, Dv, io, _ptr(out), ctypes.c_void_p(stream))
-    _check(lib, st, "gdn_decode_step")
+        if prologue:
+            st = lib.gdn_decode_step_fused(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state),
+                                           B, Hk, Hv, Dk, Dv, io, prologue, _ptr(out), ctypes.c_void_p(stream))
+        else:
+            st = lib.gdn_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state),
+                                     B, Hk, Hv, Dk, Dv, io, _ptr(out), ctypes.c_void_p(stream))
+    _check(lib, st, "gdn_decode_step_fused" if prologue else "gdn_decode_step")
     return out
 
 

@@ -184,14 +184,15 @@ WORKLOADS = {
 
 
 def make_workload(i: int, decode_steps: Optional[int] = None, io: Optional[str] = None,
-                  per_channel: bool = False) -> GDNInputs:
+                  per_channel: bool = False, raw: bool = False) -> GDNInputs:
     """Build workload i (0..4) from its seed.  Draw order is fixed per workload.
 
     io overrides the storage type of q, k, v, o (default: the workload's own, fp32 for
     workload 0 and bf16 for the rest); the draws are the same, only the rounding
     differs, and the name then carries the new type.  per_channel draws one gate per
     key channel (the KDA variant; g-logits [T, Hv, Dk] in place of [T, Hv], so the later
-    draws differ too) and prefixes the name with "kda_"."""
+    draws differ too) and prefixes the name with "kda_".  raw returns the draws before
+    the input prologue (as draw_tokens) and prefixes the name with "raw_"."""
     rng = np.random.default_rng(SEED_BASE + i)
     own = "f32" if i == 0 else "bf16"
     name = WORKLOADS[i]["name"]
@@ -199,8 +200,15 @@ def make_workload(i: int, decode_steps: Optional[int] = None, io: Optional[str] 
         name = name.replace(own, io)
     if per_channel:
         name = "kda_" + name
+    if raw:
+        name = "raw_" + name
     io = io or own
     pc = per_channel
+    if raw:
+        def draw_tokens(*args, **kw):   # noqa: E306 -- the same draws, before the prologue
+            return _draw_tokens(*args, raw=True, **kw)
+    else:
+        draw_tokens = _draw_tokens
     D = 128
     if i == 0:
         q, k, v, g, beta = draw_tokens(rng, 256, 1, 1, D, D, io, per_channel=pc)
@@ -227,6 +235,9 @@ def make_workload(i: int, decode_steps: Optional[int] = None, io: Optional[str] 
         dec = dict(q=dq, k=dk_, v=dv, g=dg, beta=db, steps=steps)
         return GDNInputs(name, io, q, k, v, g, beta, np.array([0, 65536], np.int32), None, dec)
     raise KeyError(i)
+
+
+_draw_tokens = draw_tokens
 
 
 def select_heads(x: GDNInputs, heads) -> GDNInputs:

@@ -30,7 +30,8 @@ def lib():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted(
         ["gdn_prefill", "gdn_decode_step", "gdn_prefill_plan", "gdn_status_string", "gdn_last_error",
-         "gdn_kda_workspace_size", "gdn_kda_prefill", "gdn_kda_decode_step"])
+         "gdn_kda_workspace_size", "gdn_kda_prefill", "gdn_kda_decode_step", "gdn_prefill_fused",
+         "gdn_decode_step_fused"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -169,3 +170,31 @@ def test_kda_decode_rejects(lib):
     st = lib.gdn_kda_decode_step(p(0x1000), p(0x2000), p(0x3000), p(0x4000), p(0x5000), p(0x4100),
                                  1, 1, 1, 128, 128, 1, p(0x60000), None)
     assert st == 1 and b"state overlaps g" in lib.gdn_last_error()
+
+
+def _fused(lib, **over):
+    a = dict(q=0x10000, k=0x20000, v=0x30000, g=0x40000, beta=0x50000, s0=None, cu=None,
+             N=1, T=10, Hk=2, Hv=4, Dk=128, Dv=128, C=64, io=1, pro=7, o=0x60000, fs=None)
+    a.update(over)
+    p = lambda x: None if x is None else ctypes.c_void_p(x)  # noqa: E731
+    return lib.gdn_prefill_fused(p(a["q"]), p(a["k"]), p(a["v"]), p(a["g"]), p(a["beta"]), p(a["s0"]),
+                                 p(a["cu"]), a["N"], a["T"], a["Hk"], a["Hv"], a["Dk"], a["Dv"], a["C"],
+                                 a["io"], a["pro"], p(a["o"]), p(a["fs"]), None)
+
+
+@pytest.mark.parametrize("over,status,msg", [
+    (dict(pro=8), 1, "unknown bits"),
+    (dict(io=0), 2, "bf16 or fp16"),
+    (dict(C=32), 2, "chunk_size"),
+    (dict(o=0x30000), 1, "overlaps"),
+])
+def test_prefill_fused_rejects(lib, over, status, msg):
+    assert _fused(lib, **over) == status
+    assert msg in lib.gdn_last_error().decode()
+
+
+def test_decode_fused_rejects_unknown_flags(lib):
+    p = ctypes.c_void_p
+    st = lib.gdn_decode_step_fused(p(0x1000), p(0x2000), p(0x3000), p(0x4000), p(0x5000), p(0x10000),
+                                   1, 1, 1, 128, 128, 1, 16, p(0x60000), None)
+    assert st == 1 and b"unknown bits" in lib.gdn_last_error()
