@@ -175,3 +175,13 @@ def test_kda_rejects_fp32_io():
     d = to_device(x, DEV)
     with pytest.raises(gdn.GDNError):
         gdn.kda_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"])
+
+
+def test_kda_many_tiny_sequences_and_many_heads():
+    # 3000 packed sequences of 0-5 tokens: 3000 + T/64 chunk slots, most unused, found by
+    # the map kernel's binary search over cu_seqlens; and a 64-head shape
+    rng = np.random.default_rng(4343)
+    lengths = rng.integers(0, 6, size=3000)
+    _check_all(inputs.make_custom(4400, lengths, 1, 2, io="bf16", init_std=0.2, per_channel=True,
+                                  name="kda_tiny3000"))
+    _check_all(inputs.make_custom(4401, [130], 8, 64, io="f16", per_channel=True, name="kda_H64"))

@@ -208,3 +208,20 @@ def test_phase_by_phase_kernel_bf16(monkeypatch, dvs):
         ro, rf = _oracle(x)
         check("o", to_f64(o), ro, x.io)
         check("final_state", to_f64(fs), rf, x.io)
+
+
+def test_many_tiny_sequences_and_many_heads():
+    # 3000 packed sequences of 0-5 tokens (a grid of 3000 x Hv x 8 workgroups, most of
+    # them one short chunk), and a 64-head shape
+    rng = np.random.default_rng(4242)
+    lengths = rng.integers(0, 6, size=3000)
+    x = inputs.make_custom(4300, lengths, 1, 2, io="bf16", init_std=0.2)
+    o, fs = _run(x)
+    ro, rf = _oracle(x)
+    check("o", to_f64(o), ro, x.io)
+    check("final_state", to_f64(fs), rf, x.io)
+    x = inputs.make_custom(4301, [130], 8, 64, io="f16")
+    o, fs = _run(x)
+    ro, rf = _oracle(x)
+    check("o (64 heads)", to_f64(o), ro, x.io)
+    check("final_state (64 heads)", to_f64(fs), rf, x.io)
