@@ -111,13 +111,14 @@ def _counter_median(path: str, counter: str, kernel_substr: str) -> float:
     return statistics.median(per_dispatch.values())
 
 
-def summarize_pmc(directory: str, workload: int, calib_mib: int, io=None, kda=False) -> dict:
+def summarize_pmc(directory: str, workload: int, calib_mib: int, io=None, kda=False, prologue=False) -> dict:
     """Scale the FETCH_SIZE / WRITE_SIZE counters (KiB per dispatch) of the prefill kernel by
     what the same counters read for a copy of known size; rocprofv3 runs of bench.py wrote
     fetch_, write_, copyfetch_ and copywrite_counter_collection.csv into `directory`.  With
-    kda the step's two kernels are added (bytes per step)."""
+    kda the step's two kernels are added (bytes per step); with prologue the counters are
+    those of a `bench.py --prologue` run."""
     from linear_attention_chunked_gdn_amd import gdn, inputs
-    x = inputs.make_workload(workload, io=io, per_channel=kda)
+    x = inputs.make_workload(workload, io=io, per_channel=kda, raw=prologue)
     if kda:
         kernel = "kda_map_kernel+kda_chain_kernel"
     else:
@@ -127,7 +128,9 @@ def summarize_pmc(directory: str, workload: int, calib_mib: int, io=None, kda=Fa
     f = lambda n, c, k: _counter_median(os.path.join(directory, f"{n}_counter_collection.csv"), c, k)  # noqa: E731
     fscale = true_kib / f("copyfetch", "FETCH_SIZE", "")
     wscale = true_kib / f("copywrite", "WRITE_SIZE", "")
-    parts = kernel.split("+")
+    if prologue:
+        kernel += "(prologue)"
+    parts = [p.split("(")[0] for p in kernel.split("+")]
     fetch = sum(f("fetch", "FETCH_SIZE", k) for k in parts) * fscale * 1024
     write = sum(f("write", "WRITE_SIZE", k) for k in parts) * wscale * 1024
     return {f"{kernel}@{x.name}": {
@@ -319,7 +322,8 @@ def main() -> int:
         print("bench.py: this build runs on one GPU only; --gpus must be 1", file=sys.stderr)
         return 2
     if args.summarize_pmc:
-        entry = summarize_pmc(args.summarize_pmc, args.workload, args.calibrate_copy or 256, args.io, args.kda)
+        entry = summarize_pmc(args.summarize_pmc, args.workload, args.calibrate_copy or 256, args.io, args.kda,
+                              args.prologue)
         try:
             with open(TRAFFIC_FILE) as f:
                 table = json.load(f)
