@@ -1,17 +1,22 @@
 """Throughput of the chunked gated delta-rule prefill on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload I] [--io bf16|f16|f32]
-                    [--kda] [--prologue] [--no-cpu-baseline]
+                    [--path auto|pipe|split] [--kda] [--prologue] [--no-cpu-baseline]
 
-A step is one gdn_prefill call over the whole workload (all heads, all chunks) with
-inputs resident in HBM.  The default workload is the headline one: one sequence of
+A step is one prefill call over the whole workload (all heads, all chunks) with inputs
+resident in HBM: gdn_prefill (one launch), or gdn_prefill_split (a chunk-parallel map
+kernel, then the chain kernel, over a workspace allocated once outside the timed
+region).  --path auto (the default) takes the split path when the one-launch kernel's
+workgroups -- sequences x value heads x 8 value-channel slices, one per CU -- would
+occupy at most half of the 256 CUs (the headline shape), else gdn_prefill.  The default workload is the headline one: one sequence of
 T=4096 tokens, 16 heads, d=128, bf16 q/k/v/o, fp32 g/beta/state, chunk 64.  Input
 sets are rotated across steps (more bytes than the 256 MB Infinity Cache) so that
 every step streams from HBM.  Prints ONE JSON line.
 
 roofline.achieved = algorithmic bytes of one launch / mean launch time, where the
 mean launch time comes from HIP events recorded on the launch stream around the
-timed steps (one kernel per step).  Algorithmic bytes per launch:
+timed steps (one call per step; for the two-launch paths the step's two kernels together).
+Algorithmic bytes per launch:
     T*(Hk*2*Dk*s + Hv*(2*Dv*s + 8)) + N*Hv*Dv*Dk*4*(2 if an initial state else 1)
 with s = 2 (bf16, fp16) or 4 (fp32): q, k read once per key head, v read and o written once
 per value head, g and beta (fp32) read, the fp32 state read (if given) and written.
@@ -74,7 +79,10 @@ KERNEL_SOURCES = {
     "gdn_prefill_kernel": ["gdn_prefill.hip", "gdn_device.h", "gdn_launch.h"],
     "gdn_prefill_pipe_kernel(prologue)": ["gdn_prefill_pipe.hip", "gdn_prefill_pipe_prologue.hip",
                                           "gdn_device.h", "gdn_launch.h"],
-    "kda_map_kernel+kda_chain_kernel": ["kda_map.hip", "kda_chain.hip", "gdn_device.h", "gdn_launch.h"],
+    "kda_map_kernel+kda_chain_kernel": ["kda_map.hip", "kda_chain.hip", "gdn_wy.h", "gdn_device.h",
+                                        "gdn_launch.h"],
+    "gdn_map_kernel+kda_chain_kernel": ["gdn_map.hip", "kda_chain.hip", "gdn_wy.h", "gdn_device.h",
+                                        "gdn_launch.h"],
 }
 
 
@@ -111,7 +119,17 @@ def _counter_median(path: str, counter: str, kernel_substr: str) -> float:
     return statistics.median(per_dispatch.values())
 
 
-def summarize_pmc(directory: str, workload: int, calib_mib: int, io=None, kda=False, prologue=False) -> dict:
+def choose_path(x, path: str, prologue: bool) -> str:
+    """pipe (gdn_prefill) or split (gdn_prefill_split) for this workload: auto takes the split
+    path for 16-bit I/O without the prologue when the one-launch kernel's workgroups (one per
+    CU) would leave at least half of the 256 CUs idle."""
+    if path != "auto":
+        return path
+    return "split" if (x.io != "f32" and not prologue and x.N * x.Hv * 8 <= 128) else "pipe"
+
+
+def summarize_pmc(directory: str, workload: int, calib_mib: int, io=None, kda=False, prologue=False,
+                  path: str = "auto") -> dict:
     """Scale the FETCH_SIZE / WRITE_SIZE counters (KiB per dispatch) of the prefill kernel by
     what the same counters read for a copy of known size; rocprofv3 runs of bench.py wrote
     fetch_, write_, copyfetch_ and copywrite_counter_collection.csv into `directory`.  With
@@ -121,6 +139,8 @@ def summarize_pmc(directory: str, workload: int, calib_mib: int, io=None, kda=Fa
     x = inputs.make_workload(workload, io=io, per_channel=kda, raw=prologue)
     if kda:
         kernel = "kda_map_kernel+kda_chain_kernel"
+    elif choose_path(x, path, prologue) == "split":
+        kernel = "gdn_map_kernel+kda_chain_kernel"
     else:
         plan = gdn.prefill_plan(x.N, x.Hv, IO_CODE[x.io])
         kernel = "gdn_prefill_pipe_kernel" if plan["threads_per_workgroup"] == 512 else "gdn_prefill_kernel"
@@ -303,6 +323,9 @@ def main() -> int:
     ap.add_argument("--workload", type=int, default=1)
     ap.add_argument("--io", choices=sorted(IO_CODE), default=None,
                     help="storage type of q, k, v, o (default: the workload's own)")
+    ap.add_argument("--path", choices=["auto", "pipe", "split"], default="auto",
+                    help="scalar-gate prefill entry point: gdn_prefill (pipe), gdn_prefill_split, "
+                         "or by shape (auto)")
     ap.add_argument("--kda", action="store_true",
                     help="one decay per key channel (gdn_kda_prefill) on the same workload")
     ap.add_argument("--prologue", action="store_true",
@@ -323,7 +346,7 @@ def main() -> int:
         return 2
     if args.summarize_pmc:
         entry = summarize_pmc(args.summarize_pmc, args.workload, args.calibrate_copy or 256, args.io, args.kda,
-                              args.prologue)
+                              args.prologue, args.path)
         try:
             with open(TRAFFIC_FILE) as f:
                 table = json.load(f)
@@ -363,14 +386,22 @@ def main() -> int:
                          o=torch.empty((x.T_tot, x.Hv, x.Dv), dtype=io, device=dev),
                          fs=torch.empty((x.N, x.Hv, x.Dv, x.Dk), dtype=torch.float32, device=dev)))
 
-    ws = (torch.empty(gdn.kda_workspace_size(x.N, x.T_tot, x.Hv), dtype=torch.uint8, device=dev)
-          if args.kda else None)
+    path = "kda" if args.kda else choose_path(x, args.path, args.prologue)
+    if path == "split" and (x.io == "f32" or pro):
+        print("bench.py: --path split takes bf16 or fp16 I/O without the prologue", file=sys.stderr)
+        return 2
+    ws_bytes = {"kda": gdn.kda_workspace_size, "split": gdn.prefill_split_workspace_size}
+    ws = (torch.empty(ws_bytes[path](x.N, x.T_tot, x.Hv), dtype=torch.uint8, device=dev)
+          if path in ws_bytes else None)
 
     def step(i):
         s = sets[i % copies]
-        if args.kda:
+        if path == "kda":
             gdn.kda_prefill(s["q"], s["k"], s["v"], s["g"], s["beta"], s["init"], s["cu"],
                             out=s["o"], final_state=s["fs"], workspace=ws)
+        elif path == "split":
+            gdn.prefill_split(s["q"], s["k"], s["v"], s["g"], s["beta"], s["init"], s["cu"],
+                              out=s["o"], final_state=s["fs"], workspace=ws)
         else:
             gdn.prefill(s["q"], s["k"], s["v"], s["g"], s["beta"], s["init"], s["cu"],
                         out=s["o"], final_state=s["fs"], prologue=pro)
@@ -415,9 +446,9 @@ def main() -> int:
     nbytes = algorithmic_bytes(x)
     flops = algorithmic_flops(x)
     sec = ms_per_step / 1e3
-    if args.kda:
-        kernel = "kda_map_kernel+kda_chain_kernel"
-        launch = {"kernel": kernel, "map_workgroups": (x.T_tot // 64 + x.N) * x.Hv,
+    if path in ("kda", "split"):
+        kernel = ("kda_map_kernel" if path == "kda" else "gdn_map_kernel") + "+kda_chain_kernel"
+        launch = {"path": path, "kernel": kernel, "map_workgroups": (x.T_tot // 64 + x.N) * x.Hv,
                   "chain_workgroups": x.N * x.Hv * 8, "workspace_bytes": int(ws.numel()),
                   "input_copies_rotated": copies}
     else:
@@ -425,7 +456,7 @@ def main() -> int:
         kernel = "gdn_prefill_pipe_kernel" if plan["threads_per_workgroup"] == 512 else "gdn_prefill_kernel"
         if pro:
             kernel += "(prologue)"
-        launch = {"kernel": kernel, "prologue_flags": pro,
+        launch = {"path": path, "kernel": kernel, "prologue_flags": pro,
                   "dv_per_workgroup": plan["dv_per_workgroup"], "workgroups": plan["workgroups"],
                   "lds_bytes": plan["lds_bytes"], "threads": plan["threads_per_workgroup"],
                   "input_copies_rotated": copies}

@@ -206,6 +206,37 @@ gdn_status gdn_kda_decode_step(const void *q, const void *k, const void *v,
                                gdn_dtype io_dtype, void *o, void *stream);
 
 /*
+ * gdn_prefill_split -- gdn_prefill in two launches, with a caller-owned workspace: the
+ * state-independent Map phases of every chunk of every value head first, all at once
+ * (#1 Gate, #2 KKT and the Q K^T gram, #3 Solve: "Empowering Hybrid Attention Models on
+ * NPUs", section 2.1, Figure 1(b)), then the chunk-by-chunk state recurrence that reads
+ * their results.  Same results as gdn_prefill up to rounding; the faster of the two when
+ * the (sequence, value head) pairs times 8 value-channel slices are fewer than the GPU's
+ * compute units (gdn_prefill repeats the map work for each slice on the recurrence's
+ * critical path).  Arguments as for gdn_prefill, plus:
+ *
+ *   io_dtype       GDN_BF16 or GDN_F16 (GDN_F32 returns GDN_ERR_UNSUPPORTED)
+ *   workspace      device scratch owned by the caller, at least
+ *                  gdn_prefill_split_workspace_size(...) bytes, 256-byte aligned,
+ *                  overlapping no other argument; contents on entry ignored, on return
+ *                  unspecified; may be NULL when T_tot == 0; not shared by two calls
+ *                  in flight at once.
+ *   workspace_bytes  its size in bytes
+ *
+ * gdn_prefill_split_workspace_size -- the workspace bytes for these sizes (the same
+ * tiles as gdn_kda_workspace_size).  Host pointer `bytes`.
+ */
+gdn_status gdn_prefill_split_workspace_size(int32_t N, int32_t T_tot, int32_t Hv,
+                                            int32_t chunk_size, size_t *bytes);
+gdn_status gdn_prefill_split(const void *q, const void *k, const void *v,
+                             const float *g, const float *beta,
+                             const float *initial_state, const int32_t *cu_seqlens,
+                             int32_t N, int32_t T_tot, int32_t Hk, int32_t Hv,
+                             int32_t Dk, int32_t Dv, int32_t chunk_size, gdn_dtype io_dtype,
+                             void *workspace, size_t workspace_bytes,
+                             void *o, float *final_state, void *stream);
+
+/*
  * gdn_prefill_plan -- the launch shape gdn_prefill would use for these sizes,
  * without launching anything: the width of the value-channel slice each workgroup
  * owns (the column-wise split of S, "Empowering Hybrid Attention Models on NPUs",

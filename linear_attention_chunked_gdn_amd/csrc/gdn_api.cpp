@@ -246,7 +246,7 @@ gdn_status gdn_kda_workspace_size(int32_t N, int32_t T_tot, int32_t Hv, int32_t 
         return fail(GDN_ERR_INVALID_ARGUMENT, "N=%d, T_tot=%d, Hv=%d out of range", N, T_tot, Hv);
     if (chunk_size != kChunk)
         return fail(GDN_ERR_UNSUPPORTED, "chunk_size=%d (only 64 is implemented)", chunk_size);
-    *bytes = kda_slots(N, T_tot) * (size_t)Hv * gdn::KDA_TILE_BYTES;
+    *bytes = kda_slots(N, T_tot) * (size_t)Hv * gdn::WS_TILE_BYTES;
     return ok();
 }
 
@@ -284,6 +284,54 @@ gdn_status gdn_kda_prefill(const void *q, const void *k, const void *v, const fl
     if (e == hipSuccess) e = gdn::launch_kda_chain(a, f16, hs);
     if (e != hipSuccess)
         return fail(GDN_ERR_DEVICE, "kda prefill launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+gdn_status gdn_prefill_split_workspace_size(int32_t N, int32_t T_tot, int32_t Hv, int32_t chunk_size,
+                                            size_t *bytes) {
+    if (!bytes) return fail(GDN_ERR_INVALID_ARGUMENT, "bytes must be non-null");
+    if (N < 1 || T_tot < 0 || Hv < 1)
+        return fail(GDN_ERR_INVALID_ARGUMENT, "N=%d, T_tot=%d, Hv=%d out of range", N, T_tot, Hv);
+    if (chunk_size != kChunk)
+        return fail(GDN_ERR_UNSUPPORTED, "chunk_size=%d (only 64 is implemented)", chunk_size);
+    *bytes = kda_slots(N, T_tot) * (size_t)Hv * gdn::WS_TILE_BYTES;
+    return ok();
+}
+
+gdn_status gdn_prefill_split(const void *q, const void *k, const void *v, const float *g,
+                             const float *beta, const float *initial_state, const int32_t *cu_seqlens,
+                             int32_t N, int32_t T_tot, int32_t Hk, int32_t Hv, int32_t Dk, int32_t Dv,
+                             int32_t chunk_size, gdn_dtype io_dtype, void *workspace, size_t workspace_bytes,
+                             void *o, float *final_state, void *stream) {
+    const gdn_status cs = check_prefill(q, k, v, g, beta, initial_state, cu_seqlens, N, T_tot, Hk, Hv, Dk,
+                                        Dv, chunk_size, io_dtype, o, final_state, 1, workspace,
+                                        workspace_bytes);
+    if (cs != GDN_OK) return cs;
+    if (io_dtype == GDN_F32)
+        return fail(GDN_ERR_UNSUPPORTED, "gdn_prefill_split takes bf16 or fp16 q, k, v, o");
+    size_t need = 0;
+    gdn_prefill_split_workspace_size(N, T_tot, Hv, chunk_size, &need);
+    if (T_tot > 0 && (!workspace || workspace_bytes < need))
+        return fail(GDN_ERR_INVALID_ARGUMENT, "workspace of %zu bytes is smaller than the %zu required",
+                    workspace ? workspace_bytes : (size_t)0, need);
+    if (!aligned(workspace, 256)) return fail(GDN_ERR_INVALID_ARGUMENT, "workspace is not 256-byte aligned");
+    if ((long long)kda_slots(N, T_tot) * Hv > 0x7fffffffLL || (long long)N * Hv * 8 > 0x7fffffffLL)
+        return fail(GDN_ERR_UNSUPPORTED, "too many chunks or heads for one launch");
+    if (T_tot == 0 && !final_state) return ok();
+
+    gdn::KdaArgs a;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
+    a.s0 = initial_state; a.cu = cu_seqlens; a.o = o; a.sN = final_state;
+    a.ws = static_cast<char *>(workspace);
+    a.N = N; a.T_tot = T_tot; a.Hk = Hk; a.Hv = Hv;
+    a.nslots = (int32_t)kda_slots(N, T_tot);
+    const hipStream_t hs = static_cast<hipStream_t>(stream);
+    const bool f16 = io_dtype == GDN_F16;
+    (void)hipGetLastError();
+    hipError_t e = T_tot > 0 ? gdn::launch_gdn_map(a, f16, hs) : hipSuccess;
+    if (e == hipSuccess) e = gdn::launch_kda_chain(a, f16, hs);
+    if (e != hipSuccess)
+        return fail(GDN_ERR_DEVICE, "split prefill launch failed: %s", hipGetErrorString(e));
     return ok();
 }
 

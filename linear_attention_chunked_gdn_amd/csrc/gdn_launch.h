@@ -32,35 +32,45 @@ struct DecodeArgs {
     uint32_t prologue;      // GDN_PROLOGUE_* flags
 };
 
-// Per-key-channel decay (KDA): g is [T_tot, Hv, 128].  The map kernel writes one
-// workspace tile per (chunk slot, value head); chunk j of sequence n uses slot
-// cu[n] / 64 + n + j, so T_tot / 64 + N slots cover every packing of the batch.
+// Chunked prefill in two launches (the per-key-channel decay, KDA, with g [T_tot, Hv, 128];
+// the scalar gate, with g [T_tot, Hv]).  A map kernel writes one workspace tile per (chunk
+// slot, value head); chunk j of sequence n uses slot cu[n] / 64 + n + j, so T_tot / 64 + N
+// slots cover every packing of the batch.  The chain kernel reads them.
 struct KdaArgs {
     const void *q, *k, *v;  // [T_tot, Hk, 128], [T_tot, Hk, 128], [T_tot, Hv, 128]
-    const float *g;         // [T_tot, Hv, 128]
+    const float *g;         // [T_tot, Hv, 128] (KDA) or [T_tot, Hv] (scalar gate)
     const float *beta;      // [T_tot, Hv]
     const float *s0;        // [N, Hv, 128, 128] or null
     const int32_t *cu;      // [N+1] or null (single sequence)
     void *o;                // [T_tot, Hv, 128]
     float *sN;              // [N, Hv, 128, 128] or null
-    char *ws;               // nslots * Hv tiles of KDA_TILE_BYTES
+    char *ws;               // nslots * Hv tiles of WS_TILE_BYTES
     int32_t N, T_tot, Hk, Hv;
     int32_t nslots;
 };
-// Workspace tile of one chunk and value head (byte offsets): T = (I + A)^-1 and
-// P = tril(Q K^T (.) decays), 64 x 64 fp16 each; K (.) exp(Gamma), Q (.) exp(Gamma) and
-// K (.) exp(Gamma_last - Gamma), 64 x 128 fp16 each; exp(Gamma_last), 128 fp32.
-constexpr int KDA_OFF_T = 0;
-constexpr int KDA_OFF_P = 8192;
-constexpr int KDA_OFF_KG = 16384;
-constexpr int KDA_OFF_QG = 32768;
-constexpr int KDA_OFF_KL = 49152;
-constexpr int KDA_OFF_GL = 65536;
-constexpr size_t KDA_TILE_BYTES = 66048;
+// Workspace tile of one chunk and value head (byte offsets; fp16 except gl), with
+// T = (I + A)^-1 and the decays of the chunk:
+//   P  = lower-incl-diagonal(Q K^T (.) decays)       64 x 64
+//   W  = T diag(beta) (K (.) exp(Gamma))               64 x 128 (key channels)
+//   Qg = Q (.) exp(Gamma)                              64 x 128
+//   Kl = K (.) exp(Gamma_last - Gamma)                 64 x 128
+//   U  = T diag(beta) V                                64 x 128 (value channels)
+//   gl = exp(Gamma_last)                               128 fp32
+constexpr int WS_OFF_P = 0;
+constexpr int WS_OFF_W = 8192;
+constexpr int WS_OFF_QG = 24576;
+constexpr int WS_OFF_KL = 40960;
+constexpr int WS_OFF_U = 57344;
+constexpr int WS_OFF_GL = 73728;
+constexpr size_t WS_TILE_BYTES = 74240;
 hipError_t launch_kda_map(const KdaArgs &a, bool f16, hipStream_t stream);
 hipError_t launch_kda_chain(const KdaArgs &a, bool f16, hipStream_t stream);
 int kda_map_lds_bytes();
 int kda_chain_lds_bytes();
+// The scalar-gate map (KdaArgs::g is [T_tot, Hv]) into the same workspace tiles, read by
+// launch_kda_chain.
+hipError_t launch_gdn_map(const KdaArgs &a, bool f16, hipStream_t stream);
+int gdn_map_lds_bytes();
 // one token with a per-key-channel gate: DecodeArgs::g is [B, Hv, 128]
 hipError_t launch_kda_decode(const DecodeArgs &a, int io, hipStream_t stream);
 

@@ -1,0 +1,90 @@
+// The WY products of the two-launch prefill's map kernels (gdn_map.hip, kda_map.hip):
+// with T = (I + A)^-1 of one chunk,
+//
+//   W = T diag(beta) Kg   (64 tokens x 128 key channels),
+//   U = T diag(beta) V    (64 tokens x 128 value channels),
+//
+// so that the chain only forms v = U - W S^T.  This is the solve applied to the two
+// right-hand sides that do not depend on the state (the W/U form of op #4, "Empowering
+// Hybrid Attention Models on NPUs", section 2.1).
+#pragma once
+
+#include "gdn_device.h"
+#include "gdn_launch.h"
+
+namespace gdn {
+
+// fp16 row stride of the right-hand sides [token][channel] (288 B)
+constexpr int WY_S = 128 + 16;
+
+// Operand^T as an MFMA A operand from a token-major fp16 tile x (row stride WY_S): row =
+// channel c0 + l16, slots 4hh..4hh+3 of group G = tokens 32kb + 8G + 4hh .. +3, by
+// ds_read_b64_tr_b16 (source lane a of a 16-lane group addresses 4 channels of token
+// t + a / 4; result lane m then holds channel c0 + m of tokens t .. t + 3).
+__device__ __forceinline__ Frag<_Float16> wy_frag_t(const _Float16 *x, int c0, int kb, int l16, int g4) {
+    typedef __fp16 fp16x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) fp16x4 lds_fp16x4;
+    Frag<_Float16> f;
+    const int a_tok = l16 >> 2, a_ch = c0 + 4 * (l16 & 3);
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+        const int t = 32 * kb + 8 * g4 + 4 * hh;
+        const f16x4 v = __builtin_bit_cast(
+            f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4 *)&x[(t + a_tok) * WY_S + a_ch]));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) f.v[4 * hh + e] = v[e];
+    }
+    return f;
+}
+
+// T: fp32, row stride `as`, lower triangular (zeros above the diagonal).  kg, vb:
+// diag(beta) Kg and diag(beta) V, fp16 [token][channel] with row stride WY_S, in LDS.
+// Wave `wave` (0..3) forms channel tiles 2 wave and 2 wave + 1 of both products and
+// writes them to the workspace (wout, uout: 64 x 128 fp16, row-major).  The products are taken transposed (operand^T T^T),
+// so a lane holds token 16I + l16 and four consecutive channels: one 8-byte store.
+__device__ __forceinline__ void wy_products(const float *T, int as, const _Float16 *kg, const _Float16 *vb,
+                                            char *wout, char *uout, int wave, int l16, int g4) {
+    typedef _Float16 hf;
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
+        f32x4 acc[2][2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[j][0] = acc[j][1] = zero4();
+#pragma unroll
+        for (int kb = 0; kb <= (I >> 1); ++kb) {
+            // T^T as the B operand: column = token 16I + l16, slots = tokens 32kb + 8G + e
+            const float *tr = T + (16 * I + l16) * as + 32 * kb + 8 * g4;
+            const f32x4 t0 = *reinterpret_cast<const f32x4 *>(tr);
+            const f32x4 t1 = *reinterpret_cast<const f32x4 *>(tr + 4);
+            Frag<hf> ft;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                ft.v[e] = (hf)t0[e];
+                ft.v[4 + e] = (hf)t1[e];
+            }
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int c0 = 16 * (2 * wave + j);
+                const Frag<hf> fk = wy_frag_t(kg, c0, kb, l16, g4);
+                const Frag<hf> fv = wy_frag_t(vb, c0, kb, l16, g4);
+                mma(acc[j][0], fk, ft);
+                mma(acc[j][1], fv, ft);
+            }
+        }
+        const int r = 16 * I + l16;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int c = 16 * (2 * wave + j) + 4 * g4;
+            f16x4 w, u;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                w[i] = (hf)acc[j][0][i];
+                u[i] = (hf)acc[j][1][i];
+            }
+            *reinterpret_cast<f16x4 *>(wout + (r * 128 + c) * 2) = w;
+            *reinterpret_cast<f16x4 *>(uout + (r * 128 + c) * 2) = u;
+        }
+    }
+}
+
+}  // namespace gdn

@@ -1,26 +1,29 @@
-// Chain half of the chunked prefill with a per-key-channel decay (KDA) for gfx950.
+// Chain half of the two-launch chunked prefill for gfx950 (per-key-channel decay, and the
+// scalar gate of gdn_prefill_split).
 //
-// The map kernel (kda_map.hip) has left, per chunk and value head, T = (I + A)^-1, P,
-// Kg = K (.) exp(Gamma), Qg = Q (.) exp(Gamma), Kl = K (.) exp(Gamma_last - Gamma) and
-// exp(Gamma_last) in a workspace tile.  What remains depends on the state S (Dv x Dk) and
-// runs chunk after chunk, as ops #4-#6 of the Map-Reduce-Map pipeline ("Empowering
-// Hybrid Attention Models on NPUs", section 2.1; the chunk-first order of section 5):
+// The map kernels (kda_map.hip, gdn_map.hip) have left, per chunk and value head, the
+// products that do not depend on the state: with T = (I + A)^-1,
+//   W = T diag(beta) Kg,  U = T diag(beta) V,  P,  Qg,  Kl,  gl = exp(Gamma_last)
+// (Kg = K (.) exp(Gamma), Qg = Q (.) exp(Gamma), Kl = K (.) exp(Gamma_last - Gamma)).  What
+// remains depends on the state S (Dv x Dk) and runs chunk after chunk, as ops #5-#6 of the
+// Map-Reduce-Map pipeline ("Empowering Hybrid Attention Models on NPUs", section 2.1; the
+// chunk-first order of section 5):
 //
-//   R = diag(beta) (V - Kg S^T),   v = T R,
+//   v = U - W S^T            (= T diag(beta) (V - Kg S^T), the WY form of the solve)
 //   O = Qg S^T + P v,
-//   S <- S Diag(exp(Gamma_last)) + v^T Kl.
+//   S <- S Diag(gl) + v^T Kl.
 //
-// With the per-channel decays folded into Kg, Qg and Kl this is the gated delta rule's
-// chain with no per-token scaling left, so the chain waves follow gdn_prefill_pipe.hip
-// (the state slice in registers, K S^T and Q S^T from a 16-bit copy of it in LDS, the
-// update in place) with every product in fp16.  The column-wise split of S is the same:
-// one workgroup per (sequence, value head, 16 value channels).
+// With the inverse applied in the map, v is one product with S away from the state, and a
+// chunk needs two dependent stages on the chain's critical path instead of three.  The
+// chain waves follow gdn_prefill_pipe.hip (the state slice in registers, W S^T and Q S^T
+// from a 16-bit copy of it in LDS, the update in place) with every product in fp16.  The
+// column-wise split of S is the same: one workgroup per (sequence, value head, 16 value
+// channels).
 //
 // Roles: waves 0-3 load the workspace tiles one chunk ahead and commit them to LDS;
-// waves 4-7 run the chain.  A chunk takes three barrier-separated phases:
-//   phase 1: chain R(c), Q S^T(c)     | loaders: commit T, P, Kl, exp(Gamma_last) of c
-//   phase 2: chain v(c) = T R         | loaders: commit Kg, Qg, V, beta of c + 1
-//   phase 3: chain O(c), S update     |
+// waves 4-7 run the chain.  A chunk takes two barrier-separated phases:
+//   phase 1: chain v(c), Q S^T(c)   | loaders: commit P, Kl, gl of c
+//   phase 2: chain O(c), S update   | loaders: commit W, Qg, U of c + 1
 // Each tile is committed after its last reader of the previous chunk and before its
 // first reader, so one LDS copy of every tile suffices.
 #include "gdn_device.h"
@@ -38,22 +41,18 @@ constexpr int DK = 128;
 constexpr int DV = 128;
 constexpr int DVS = 16;        // value channels per workgroup
 constexpr int THREADS = 512;   // 4 loader + 4 chain waves
-constexpr int KS = DK + 16;    // fp16 row stride of Kg, Qg, Kl and the state copy (288 B)
-constexpr int TS = CH + 16;    // fp16 row stride of T, R^T and v^T (160 B)
+constexpr int KS = DK + 16;    // fp16 row stride of W, Qg, Kl and the state copy (288 B)
+constexpr int TS = CH + 16;    // fp16 row stride of v^T (160 B)
 constexpr int TP = CH + 8;     // fp16 row stride of P (144 B)
-constexpr int VS = DVS;
+constexpr int US = DVS;        // fp16 row stride of the U slice
 
-template <typename IO>
 struct __align__(16) Smem {
-    hf T[CH * TS];
     hf S[DVS * KS];            // fp16 copy of the state slice [value ch][key ch]
-    hf Rh[DVS * TS];           // R^T
     hf Vh[DVS * TS];           // v^T
-    IO V[CH * VS];
-    float beta[CH];
+    hf U[CH * US];             // U slice [token][value ch]
     float gl[DK];              // exp(Gamma_last) per key channel
     hf P[CH * TP];
-    hf Kg[CH * KS];
+    hf W[CH * KS];
     hf Qg[CH * KS];
     hf Kl[CH * KS];
 };
@@ -61,12 +60,11 @@ struct __align__(16) Smem {
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 // Loader registers: the tiles of one chunk between their load and their commit.
-struct StageA {       // T, P, Kl, exp(Gamma_last): read in phases 2 and 3
-    u32x4 t[2], p[2], kl[4], gl;
+struct StageA {       // P, Kl, gl: read in phase 2
+    u32x4 p[2], kl[4], gl;
 };
-struct StageB {       // Kg, Qg, V, beta: read in phase 1
-    u32x4 kg[4], qg[4], v;
-    float b;
+struct StageB {       // W, Qg, U: read in phase 1
+    u32x4 w[4], qg[4], u;
 };
 
 struct Work {
@@ -77,28 +75,22 @@ struct Work {
 
 __device__ __forceinline__ int chunk_clamp(const Work &wk, int c) { return min(c, wk.nchunks - 1); }
 
-// Loader thread ld (0..255).  Rows past a short chunk's end read the last valid row
-// (their beta is 0, so they contribute nothing).
+// Loader thread ld (0..255).
 __device__ __forceinline__ void load_a(StageA &st, const Work &wk, int c, int ld) {
     const char *tile = wk.ws + (size_t)chunk_clamp(wk, c) * wk.slot_stride;
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-        const int idx = ld + 256 * p;   // 64 rows x 8 segments of 16 B
-        st.t[p] = *reinterpret_cast<const u32x4 *>(tile + KDA_OFF_T + idx * 16);
-        st.p[p] = *reinterpret_cast<const u32x4 *>(tile + KDA_OFF_P + idx * 16);
-    }
+    for (int p = 0; p < 2; ++p)       // 64 rows x 8 segments of 16 B
+        st.p[p] = *reinterpret_cast<const u32x4 *>(tile + WS_OFF_P + (ld + 256 * p) * 16);
 #pragma unroll
     for (int p = 0; p < 4; ++p)       // 64 rows x 16 segments
-        st.kl[p] = *reinterpret_cast<const u32x4 *>(tile + KDA_OFF_KL + (ld + 256 * p) * 16);
-    st.gl = *reinterpret_cast<const u32x4 *>(tile + KDA_OFF_GL + (ld & 31) * 16);
+        st.kl[p] = *reinterpret_cast<const u32x4 *>(tile + WS_OFF_KL + (ld + 256 * p) * 16);
+    st.gl = *reinterpret_cast<const u32x4 *>(tile + WS_OFF_GL + (ld & 31) * 16);
 }
 
-template <typename IO>
-__device__ __forceinline__ void commit_a(const StageA &st, Smem<IO> &s, int ld) {
+__device__ __forceinline__ void commit_a(const StageA &st, Smem &s, int ld) {
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
         const int idx = ld + 256 * p, row = idx >> 3, seg = idx & 7;
-        *reinterpret_cast<u32x4 *>(&s.T[row * TS + seg * 8]) = st.t[p];
         *reinterpret_cast<u32x4 *>(&s.P[row * TP + seg * 8]) = st.p[p];
     }
 #pragma unroll
@@ -109,62 +101,48 @@ __device__ __forceinline__ void commit_a(const StageA &st, Smem<IO> &s, int ld) 
     if (ld < 32) *reinterpret_cast<u32x4 *>(&s.gl[ld * 4]) = st.gl;
 }
 
-template <typename IO>
-__device__ __forceinline__ void load_b(StageB &st, const KdaArgs &a, const Work &wk, int c, int ld) {
-    const int cc = chunk_clamp(wk, c);
-    const char *tile = wk.ws + (size_t)cc * wk.slot_stride;
+__device__ __forceinline__ void load_b(StageB &st, const Work &wk, int c, int ld) {
+    const char *tile = wk.ws + (size_t)chunk_clamp(wk, c) * wk.slot_stride;
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-        st.kg[p] = *reinterpret_cast<const u32x4 *>(tile + KDA_OFF_KG + (ld + 256 * p) * 16);
-        st.qg[p] = *reinterpret_cast<const u32x4 *>(tile + KDA_OFF_QG + (ld + 256 * p) * 16);
+        st.w[p] = *reinterpret_cast<const u32x4 *>(tile + WS_OFF_W + (ld + 256 * p) * 16);
+        st.qg[p] = *reinterpret_cast<const u32x4 *>(tile + WS_OFF_QG + (ld + 256 * p) * 16);
     }
-    const int tok0 = wk.bos + CH * cc, nval = min(CH, wk.eos - tok0);
-    // v: 64 rows x 2 segments of 8 values (threads 0-127; the rest repeat them)
-    const int vr = min((ld & 127) >> 1, nval - 1), vs = ld & 1;
-    st.v = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const IO *>(a.v) +
-                                            ((size_t)(tok0 + vr) * a.Hv + wk.h) * DV + wk.dv0 + 8 * vs);
-    const int br = ld & (CH - 1);
-    const float bv = a.beta[(size_t)(tok0 + min(br, nval - 1)) * a.Hv + wk.h];
-    st.b = br < nval ? bv : 0.f;
+    // U slice: 64 rows x 2 segments of 8 value channels (threads 0-127; the rest repeat them)
+    const int ur = (ld & 127) >> 1, us = ld & 1;
+    st.u = *reinterpret_cast<const u32x4 *>(tile + WS_OFF_U + (ur * DV + wk.dv0 + 8 * us) * 2);
 }
 
-template <typename IO>
-__device__ __forceinline__ void commit_b(const StageB &st, Smem<IO> &s, int ld) {
+__device__ __forceinline__ void commit_b(const StageB &st, Smem &s, int ld) {
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
         const int idx = ld + 256 * p, row = idx >> 4, seg = idx & 15;
-        *reinterpret_cast<u32x4 *>(&s.Kg[row * KS + seg * 8]) = st.kg[p];
+        *reinterpret_cast<u32x4 *>(&s.W[row * KS + seg * 8]) = st.w[p];
         *reinterpret_cast<u32x4 *>(&s.Qg[row * KS + seg * 8]) = st.qg[p];
     }
-    if (ld < 128) *reinterpret_cast<u32x4 *>(&s.V[(ld >> 1) * VS + 8 * (ld & 1)]) = st.v;
-    if (ld < CH) s.beta[ld] = st.b;
+    if (ld < 128) *reinterpret_cast<u32x4 *>(&s.U[(ld >> 1) * US + 8 * (ld & 1)]) = st.u;
 }
 
-// Phase 1: R = beta (V - Kg S^T) for tokens [16W, 16W + 16) (lane = value channel,
-// rows = tokens), then (Q S^T)^T = S Qg^T from the same S fragments.
-template <typename IO>
-__device__ __forceinline__ f32x4 chain_R_QS(Smem<IO> &s, int W, int l16, int g4) {
-    const hf *krow = s.Kg + (16 * W + l16) * KS + 8 * g4;
+// Phase 1: v = U - W S^T for tokens [16W, 16W + 16) (lane = value channel, rows =
+// tokens), stored transposed; then (Q S^T)^T = S Qg^T from the same S fragments.
+__device__ __forceinline__ f32x4 chain_v_QS(Smem &s, int W, int l16, int g4) {
+    const hf *wrow = s.W + (16 * W + l16) * KS + 8 * g4;
     const hf *qrow = s.Qg + (16 * W + l16) * KS + 8 * g4;
     const hf *srow = s.S + l16 * KS + 8 * g4;
     const int t0 = 16 * W + 4 * g4;
-    const f32x4 b = *reinterpret_cast<const f32x4 *>(&s.beta[t0]);
-    f32x4 vv;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) vv[i] = Cvt<IO>::to_f32(s.V[(t0 + i) * VS + l16]);
     Frag<hf> fs[4];
-    f32x4 ks = zero4();
+    f32x4 ws = zero4();
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-        Frag<hf> fk;
+        Frag<hf> fw;
         fs[kb].load8(srow + 32 * kb);
-        fk.load8(krow + 32 * kb);
-        mma(ks, fk, fs[kb]);
+        fw.load8(wrow + 32 * kb);
+        mma(ws, fw, fs[kb]);
     }
-    f16x4 r;
+    f16x4 x;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) r[i] = (hf)(b[i] * (vv[i] - ks[i]));
-    *reinterpret_cast<f16x4 *>(&s.Rh[l16 * TS + t0]) = r;
+    for (int i = 0; i < 4; ++i) x[i] = (hf)((float)s.U[(t0 + i) * US + l16] - ws[i]);
+    *reinterpret_cast<f16x4 *>(&s.Vh[l16 * TS + t0]) = x;
     f32x4 qs = zero4();
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
@@ -175,29 +153,10 @@ __device__ __forceinline__ f32x4 chain_R_QS(Smem<IO> &s, int W, int l16, int g4)
     return qs;
 }
 
-// Phase 2: v = T R for tokens [16W, 16W + 16); T is lower triangular, so only the
-// first W/2 + 1 blocks of 32 columns contribute.
-template <typename IO>
-__device__ __forceinline__ void chain_v(Smem<IO> &s, int W, int l16, int g4) {
-    const int t0 = 16 * W + 4 * g4;
-    f32x4 acc = zero4();
-    const hf *trow = s.T + (16 * W + l16) * TS + 8 * g4;
-    for (int kb = 0; kb <= (W >> 1); ++kb) {
-        Frag<hf> fa, fr;
-        fa.load8(trow + 32 * kb);
-        fr.load8(s.Rh + l16 * TS + 32 * kb + 8 * g4);
-        mma(acc, fa, fr);
-    }
-    f16x4 x;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) x[i] = (hf)acc[i];
-    *reinterpret_cast<f16x4 *>(&s.Vh[l16 * TS + t0]) = x;
-}
-
-// Phase 3: output rows of wave W, then the update of key channels [32W, 32W + 32) of
+// Phase 2: output rows of wave W, then the update of key channels [32W, 32W + 32) of
 // the state slice: S^T rows (key channels) 32W + 16mt + 4G + r, column = value channel.
 template <typename IO>
-__device__ __forceinline__ void chain_out_update(Smem<IO> &s, const KdaArgs &a, int W, int l16, int g4,
+__device__ __forceinline__ void chain_out_update(Smem &s, const KdaArgs &a, int W, int l16, int g4,
                                                  const f32x4 &qs, f32x4 (&st)[2], int h, int dv0,
                                                  int tok0, int nval) {
     const int t = 16 * W + l16;
@@ -256,7 +215,7 @@ __device__ __forceinline__ void chain_out_update(Smem<IO> &s, const KdaArgs &a, 
 
 template <typename IO>
 __global__ __launch_bounds__(THREADS) void kda_chain_kernel(const KdaArgs a) {
-    __shared__ Smem<IO> s;
+    __shared__ Smem s;
     const int tid = threadIdx.x;
     const int lane = tid & 63, l16 = lane & 15, g4 = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -277,8 +236,8 @@ __global__ __launch_bounds__(THREADS) void kda_chain_kernel(const KdaArgs a) {
     wk.eos = a.cu ? a.cu[n + 1] : a.T_tot;
     const int len = wk.eos > wk.bos ? wk.eos - wk.bos : 0;
     wk.nchunks = (len + CH - 1) / CH;
-    wk.slot_stride = (size_t)a.Hv * KDA_TILE_BYTES;
-    wk.ws = a.ws + ((size_t)(wk.bos / CH + n) * a.Hv + h) * KDA_TILE_BYTES;
+    wk.slot_stride = (size_t)a.Hv * WS_TILE_BYTES;
+    wk.ws = a.ws + ((size_t)(wk.bos / CH + n) * a.Hv + h) * WS_TILE_BYTES;
 
     f32x4 st[2];
     const size_t sbase = ((size_t)n * a.Hv + h) * (size_t)DV * DK;
@@ -300,10 +259,10 @@ __global__ __launch_bounds__(THREADS) void kda_chain_kernel(const KdaArgs a) {
         StageA sa;
         StageB sb;
         if (is_loader) {
-            load_b<IO>(sb, a, wk, 0, tid);
+            load_b(sb, wk, 0, tid);
             commit_b(sb, s, tid);
             load_a(sa, wk, 0, tid);
-            load_b<IO>(sb, a, wk, 1, tid);
+            load_b(sb, wk, 1, tid);
         }
         __syncthreads();
         if (is_loader) {
@@ -312,19 +271,16 @@ __global__ __launch_bounds__(THREADS) void kda_chain_kernel(const KdaArgs a) {
                 load_a(sa, wk, c + 1, tid);
                 __syncthreads();
                 commit_b(sb, s, tid);
-                load_b<IO>(sb, a, wk, c + 2, tid);
-                __syncthreads();
+                load_b(sb, wk, c + 2, tid);
                 __syncthreads();
             }
         } else {
             for (int c = 0; c < wk.nchunks; ++c) {
                 const int tok0 = wk.bos + c * CH;
                 const int nval = min(CH, wk.eos - tok0);
-                const f32x4 qs = chain_R_QS(s, W, l16, g4);
+                const f32x4 qs = chain_v_QS(s, W, l16, g4);
                 __syncthreads();
-                chain_v(s, W, l16, g4);
-                __syncthreads();
-                chain_out_update(s, a, W, l16, g4, qs, st, h, wk.dv0, tok0, nval);
+                chain_out_update<IO>(s, a, W, l16, g4, qs, st, h, wk.dv0, tok0, nval);
                 __syncthreads();
             }
         }
@@ -350,6 +306,6 @@ hipError_t launch_kda_chain(const KdaArgs &a, bool f16, hipStream_t stream) {
     return hipGetLastError();
 }
 
-int kda_chain_lds_bytes() { return (int)sizeof(kdachain::Smem<__bf16>); }
+int kda_chain_lds_bytes() { return (int)sizeof(kdachain::Smem); }
 
 }  // namespace gdn

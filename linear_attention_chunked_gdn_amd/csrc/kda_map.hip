@@ -10,13 +10,13 @@
 //   A[r, s] = beta_r sum_j k_rj k_sj exp(Gamma_rj - Gamma_sj)   (r > s),
 //   P[r, s] = sum_j q_rj k_sj exp(Gamma_rj - Gamma_sj)          (r >= s),
 //   T = (I + A)^-1,
-// and the S-dependent half (kda_chain.hip) needs K (.) exp(Gamma), Q (.) exp(Gamma),
-// K (.) exp(Gamma_last - Gamma) and exp(Gamma_last).  None of this depends on the
-// state, so every chunk of every head is one independent workgroup here (the Map
-// phases #1-#3 of the page's Map-Reduce-Map pipeline), and the results go to a
-// workspace tile the chain kernel reads: with a per-channel gate this map is several
-// times the chain's work, and doing it once per chunk instead of once per value-channel
-// slice of the chain is what makes the split pay.
+// and the S-dependent half (kda_chain.hip) needs W = T diag(beta) (K (.) exp(Gamma)),
+// U = T diag(beta) V, Q (.) exp(Gamma), K (.) exp(Gamma_last - Gamma) and
+// exp(Gamma_last).  None of this depends on the state, so every chunk of every head is
+// one independent workgroup here (the Map phases #1-#4 of the page's Map-Reduce-Map
+// pipeline), and the results go to a workspace tile the chain kernel reads: with a
+// per-channel gate this map is several times the chain's work, and doing it once per
+// chunk instead of once per value-channel slice of the chain is what makes the split pay.
 //
 // Decays without overflow.  exp(Gamma_rj - Gamma_sj) is rank one per channel,
 // f_rj * f'_sj, for any reference point between s and r: with f_rj = prod of a over
@@ -35,6 +35,7 @@
 // share a CU and hide each other's load and barrier latency.
 #include "gdn_device.h"
 #include "gdn_launch.h"
+#include "gdn_wy.h"
 
 #include <type_traits>
 
@@ -53,8 +54,16 @@ constexpr float LOG2E = 1.4426950408889634f;
 
 template <typename IO>
 struct __align__(16) Smem {
-    IO K[CH * XS];            // raw k rows of the chunk (rows past its end repeat the last)
-    IO Q[CH * XS];
+    union {
+        struct {
+            IO K[CH * XS];    // raw k rows of the chunk (rows past its end repeat the last)
+            IO Q[CH * XS];
+        } kq;
+        struct {              // once the grams are done: diag(beta) Kg, diag(beta) V
+            hf Kb[CH * WY_S];
+            hf Vb[CH * WY_S];
+        } wy;
+    };
     union {
         hf F[2][CH * XS];     // decay factors of two reference levels (grams)
         struct {
@@ -124,7 +133,7 @@ __device__ __forceinline__ void store_p(char *tile, int r, int c, const f32x4 &x
     f16x4 v;
 #pragma unroll
     for (int i = 0; i < 4; ++i) v[i] = (hf)x[i];
-    *reinterpret_cast<f16x4 *>(tile + KDA_OFF_P + (r * CH + c) * 2) = v;
+    *reinterpret_cast<f16x4 *>(tile + WS_OFF_P + (r * CH + c) * 2) = v;
 }
 
 // Tile (I, J), I > J, of A and P at one reference level, whole.  The product is taken
@@ -137,9 +146,9 @@ __device__ __forceinline__ f32x4 offdiag_tile(const Smem<IO> &s, char *tile, int
     f32x4 accA = zero4(), accP = zero4();
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-        const Frag<hf> kj = frag_scaled(s.K, f, J, kb, l16, g4);
-        const Frag<hf> ki = frag_scaled(s.K, f, I, kb, l16, g4);
-        const Frag<hf> qi = frag_scaled(s.Q, f, I, kb, l16, g4);
+        const Frag<hf> kj = frag_scaled(s.kq.K, f, J, kb, l16, g4);
+        const Frag<hf> ki = frag_scaled(s.kq.K, f, I, kb, l16, g4);
+        const Frag<hf> qi = frag_scaled(s.kq.Q, f, I, kb, l16, g4);
         mma(accA, kj, ki);
         mma(accP, kj, qi);
     }
@@ -156,8 +165,8 @@ __device__ __forceinline__ void diag_level(const Smem<IO> &s, int X, const hf *f
     f32x4 accA = zero4(), accP = zero4();
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-        const Frag<hf> kx = frag_scaled(s.K, f, X, kb, l16, g4);
-        const Frag<hf> qx = frag_scaled(s.Q, f, X, kb, l16, g4);
+        const Frag<hf> kx = frag_scaled(s.kq.K, f, X, kb, l16, g4);
+        const Frag<hf> qx = frag_scaled(s.kq.Q, f, X, kb, l16, g4);
         mma(accA, kx, kx);
         mma(accP, kx, qx);
     }
@@ -194,7 +203,7 @@ __global__ __launch_bounds__(THREADS, 2) void kda_map_kernel(const KdaArgs a) {
     const int tok0 = bos + CH * (slot - (bos / CH + n));
     if (tok0 >= eos) return;   // a slot no chunk uses (the whole workgroup leaves)
     const int nval = min(CH, eos - tok0);
-    char *tile = a.ws + ((size_t)slot * a.Hv + h) * KDA_TILE_BYTES;
+    char *tile = a.ws + ((size_t)slot * a.Hv + h) * WS_TILE_BYTES;
 
     if (tid < CH) s.beta[tid] = tid < nval ? a.beta[(size_t)(tok0 + tid) * a.Hv + h] : 0.f;
 
@@ -212,8 +221,8 @@ __global__ __launch_bounds__(THREADS, 2) void kda_map_kernel(const KdaArgs a) {
         a0[i] = ok ? exp2f(gg[0] * LOG2E) : 1.f;
         a1[i] = ok ? exp2f(gg[1] * LOG2E) : 1.f;
         const size_t kq = (tok * a.Hk + hk) * DK + ch;
-        *reinterpret_cast<v2 *>(&s.K[t * XS + ch]) = *reinterpret_cast<const v2 *>(reinterpret_cast<const IO *>(a.k) + kq);
-        *reinterpret_cast<v2 *>(&s.Q[t * XS + ch]) = *reinterpret_cast<const v2 *>(reinterpret_cast<const IO *>(a.q) + kq);
+        *reinterpret_cast<v2 *>(&s.kq.K[t * XS + ch]) = *reinterpret_cast<const v2 *>(reinterpret_cast<const IO *>(a.k) + kq);
+        *reinterpret_cast<v2 *>(&s.kq.Q[t * XS + ch]) = *reinterpret_cast<const v2 *>(reinterpret_cast<const IO *>(a.q) + kq);
     }
     // products inside the block: F inclusive from the block start, B exclusive to its end
     float F0[16], F1[16], B0[16], B1[16];
@@ -240,22 +249,24 @@ __global__ __launch_bounds__(THREADS, 2) void kda_map_kernel(const KdaArgs a) {
         if (bb < b) { pre0 *= x0; pre1 *= x1; }
         if (bb > b) { post0 *= x0; post1 *= x1; }
     }
-    // operands of the chain: K (.) exp(Gamma), Q (.) exp(Gamma), K (.) exp(Gamma_last - Gamma)
+    // operands of the chain: Q (.) exp(Gamma), K (.) exp(Gamma_last - Gamma); and
+    // diag(beta) (K (.) exp(Gamma)) kept for the WY products
+    f16x2 kgb[16];
     {
-        hf *kg = reinterpret_cast<hf *>(tile + KDA_OFF_KG);
-        hf *qg = reinterpret_cast<hf *>(tile + KDA_OFF_QG);
-        hf *kl = reinterpret_cast<hf *>(tile + KDA_OFF_KL);
+        hf *qg = reinterpret_cast<hf *>(tile + WS_OFF_QG);
+        hf *kl = reinterpret_cast<hf *>(tile + WS_OFF_KL);
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int t = 16 * b + i;
-            const v2 kv = *reinterpret_cast<const v2 *>(&s.K[t * XS + ch]);
-            const v2 qv = *reinterpret_cast<const v2 *>(&s.Q[t * XS + ch]);
+            const v2 kv = *reinterpret_cast<const v2 *>(&s.kq.K[t * XS + ch]);
+            const v2 qv = *reinterpret_cast<const v2 *>(&s.kq.Q[t * XS + ch]);
             const float k0 = Cvt<IO>::to_f32(kv[0]), k1 = Cvt<IO>::to_f32(kv[1]);
             const float e0 = pre0 * F0[i], e1 = pre1 * F1[i];
             const float l0 = B0[i] * post0, l1 = B1[i] * post1;
+            const float bt = s.beta[t];
+            kgb[i][0] = (hf)(k0 * e0 * bt);
+            kgb[i][1] = (hf)(k1 * e1 * bt);
             f16x2 x;
-            x[0] = (hf)(k0 * e0); x[1] = (hf)(k1 * e1);
-            *reinterpret_cast<f16x2 *>(&kg[t * DK + ch]) = x;
             x[0] = (hf)(Cvt<IO>::to_f32(qv[0]) * e0); x[1] = (hf)(Cvt<IO>::to_f32(qv[1]) * e1);
             *reinterpret_cast<f16x2 *>(&qg[t * DK + ch]) = x;
             x[0] = (hf)(k0 * l0); x[1] = (hf)(k1 * l1);
@@ -265,7 +276,7 @@ __global__ __launch_bounds__(THREADS, 2) void kda_map_kernel(const KdaArgs a) {
             f32x2 gl;
             gl[0] = F0[15] * post0;
             gl[1] = F1[15] * post1;
-            *reinterpret_cast<f32x2 *>(tile + KDA_OFF_GL + ch * 4) = gl;
+            *reinterpret_cast<f32x2 *>(tile + WS_OFF_GL + ch * 4) = gl;
         }
     }
 
@@ -317,7 +328,14 @@ __global__ __launch_bounds__(THREADS, 2) void kda_map_kernel(const KdaArgs a) {
     diag_level<3>(s, wave, s.F[0], l16, g4, selA, selP);
     diag_level<2>(s, wave, s.F[1], l16, g4, selA, selP);
     __syncthreads();
-    // round 3: levels 2 and 1, and the diagonal of P itself
+    // round 3: levels 2 and 1, and the diagonal of P itself; v of this thread's tokens and
+    // channels is fetched here for the WY products
+    v2 vp[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const size_t tok = (size_t)(tok0 + min(16 * b + i, nval - 1));
+        vp[i] = *reinterpret_cast<const v2 *>(reinterpret_cast<const IO *>(a.v) + (tok * a.Hv + h) * DK + ch);
+    }
     {
         float f0[16], f1[16], h0[16], h1[16];
         level_factors<2>(a0, f0);
@@ -337,12 +355,23 @@ __global__ __launch_bounds__(THREADS, 2) void kda_map_kernel(const KdaArgs a) {
     {
         f32x4 acc = zero4();
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) mma(acc, frag_raw(s.K, wave, kb, l16, g4), frag_raw(s.Q, wave, kb, l16, g4));
+        for (int kb = 0; kb < 4; ++kb) mma(acc, frag_raw(s.kq.K, wave, kb, l16, g4), frag_raw(s.kq.Q, wave, kb, l16, g4));
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             if (l16 == 4 * g4 + i) selP[i] = acc[i];
     }
-    __syncthreads();   // the factor tiles are dead; A and T overlay them from here
+    __syncthreads();   // the factor tiles and k, q are dead; A and T overlay the former,
+                       // the WY right-hand sides the latter
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int t = 16 * b + i;
+        const float bt = s.beta[t];
+        f16x2 x;
+        x[0] = (hf)(Cvt<IO>::to_f32(vp[i][0]) * bt);
+        x[1] = (hf)(Cvt<IO>::to_f32(vp[i][1]) * bt);
+        *reinterpret_cast<f16x2 *>(&s.wy.Kb[t * WY_S + ch]) = kgb[i];
+        *reinterpret_cast<f16x2 *>(&s.wy.Vb[t * WY_S + ch]) = x;
+    }
     {
         // A: this wave's diagonal tile, its tiles below the diagonal, zeros right of the
         // diagonal; P: the diagonal tile and the zeros (the tiles below went out above)
@@ -415,18 +444,8 @@ __global__ __launch_bounds__(THREADS, 2) void kda_map_kernel(const KdaArgs a) {
         }
         __syncthreads();
     }
-    {
-        // T to the workspace in fp16, 16 values per thread
-        const int r = tid >> 2, c0 = (tid & 3) * 16;
-        f16x8 lo, hi;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            lo[e] = (hf)T[r * AS + c0 + e];
-            hi[e] = (hf)T[r * AS + c0 + 8 + e];
-        }
-        *reinterpret_cast<f16x8 *>(tile + KDA_OFF_T + (r * CH + c0) * 2) = lo;
-        *reinterpret_cast<f16x8 *>(tile + KDA_OFF_T + (r * CH + c0 + 8) * 2) = hi;
-    }
+    // #4 W = T diag(beta) Kg and U = T diag(beta) V to the workspace
+    wy_products(s.sv.T, AS, s.wy.Kb, s.wy.Vb, tile + WS_OFF_W, tile + WS_OFF_U, wave, l16, g4);
 }
 
 }  // namespace kdamap

@@ -67,6 +67,10 @@ def load_library(path: str = LIB_PATH):
     lib.gdn_kda_prefill.argtypes = [vp, vp, vp, fp, fp, fp, ip, i32, i32, i32, i32, i32, i32, i32,
                                     ctypes.c_int, vp, ctypes.c_size_t, vp, fp, vp]
     lib.gdn_kda_prefill.restype = ctypes.c_int
+    lib.gdn_prefill_split_workspace_size.argtypes = lib.gdn_kda_workspace_size.argtypes
+    lib.gdn_prefill_split_workspace_size.restype = ctypes.c_int
+    lib.gdn_prefill_split.argtypes = lib.gdn_kda_prefill.argtypes
+    lib.gdn_prefill_split.restype = ctypes.c_int
     lib.gdn_kda_decode_step.argtypes = lib.gdn_decode_step.argtypes
     lib.gdn_kda_decode_step.restype = ctypes.c_int
     lib.gdn_status_string.argtypes = [ctypes.c_int]
@@ -212,10 +216,17 @@ def kda_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tens
     """Packed chunked prefill with one decay per key channel: as ``prefill`` except
     g: [T, Hv, 128] fp32 and q, k, v bf16 or fp16.  ``workspace`` (a uint8 device tensor
     of at least ``kda_workspace_size`` bytes) is allocated here when not given."""
+    return _prefill_ws("gdn_kda_prefill", kda_workspace_size, True, q, k, v, g, beta, initial_state,
+                       cu_seqlens, chunk_size, output_final_state, out, final_state, workspace, lib)
+
+
+def _prefill_ws(fn: str, size_fn, per_channel: bool, q, k, v, g, beta, initial_state, cu_seqlens,
+                chunk_size, output_final_state, out, final_state, workspace, lib):
+    """The entry points that take a caller-owned workspace (gdn_kda_prefill, gdn_prefill_split)."""
     lib = lib or load_library()
     dev = q.device
     if dev.type != "cuda":
-        raise ValueError("gdn.kda_prefill runs on the GPU only; q is on " + str(dev))
+        raise ValueError(f"{fn} runs on the GPU only; q is on " + str(dev))
     io = _io_code(q)
     T, Hk, Dk = q.shape
     Hv, Dv = v.shape[1], v.shape[2]
@@ -223,7 +234,7 @@ def kda_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tens
     _need(q, "q", q.dtype, (T, Hk, Dk), dev)
     _need(k, "k", q.dtype, (T, Hk, Dk), dev)
     _need(v, "v", q.dtype, (T, Hv, Dv), dev)
-    _need(g, "g", torch.float32, (T, Hv, Dk), dev)
+    _need(g, "g", torch.float32, (T, Hv, Dk) if per_channel else (T, Hv), dev)
     _need(beta, "beta", torch.float32, (T, Hv), dev)
     if cu_seqlens is not None:
         _need(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,), dev)
@@ -236,18 +247,41 @@ def kda_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tens
         final_state = torch.empty((N, Hv, Dv, Dk), dtype=torch.float32, device=dev)
     if final_state is not None:
         _need(final_state, "final_state", torch.float32, (N, Hv, Dv, Dk), dev)
-    need = kda_workspace_size(N, T, Hv, chunk_size, lib=lib)
+    need = size_fn(N, T, Hv, chunk_size, lib=lib)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     if workspace.device != dev or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous uint8 tensor on " + str(dev))
     with torch.cuda.device(dev):
         stream = torch.cuda.current_stream(dev).cuda_stream
-        st = lib.gdn_kda_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
-                                 _ptr(cu_seqlens), N, T, Hk, Hv, Dk, Dv, chunk_size, io, _ptr(workspace),
-                                 workspace.numel(), _ptr(out), _ptr(final_state), ctypes.c_void_p(stream))
-    _check(lib, st, "gdn_kda_prefill")
+        st = getattr(lib, fn)(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
+                              _ptr(cu_seqlens), N, T, Hk, Hv, Dk, Dv, chunk_size, io, _ptr(workspace),
+                              workspace.numel(), _ptr(out), _ptr(final_state), ctypes.c_void_p(stream))
+    _check(lib, st, fn)
     return out, final_state
+
+
+def prefill_split_workspace_size(N: int, T: int, Hv: int, chunk_size: int = CHUNK, lib=None) -> int:
+    """Workspace bytes gdn_prefill_split needs for N sequences, T packed tokens, Hv heads."""
+    lib = lib or load_library()
+    n = ctypes.c_size_t()
+    _check(lib, lib.gdn_prefill_split_workspace_size(N, T, Hv, chunk_size, ctypes.byref(n)),
+           "gdn_prefill_split_workspace_size")
+    return int(n.value)
+
+
+def prefill_split(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                  beta: torch.Tensor, initial_state: Optional[torch.Tensor] = None,
+                  cu_seqlens: Optional[torch.Tensor] = None, chunk_size: int = CHUNK,
+                  output_final_state: bool = True, out: Optional[torch.Tensor] = None,
+                  final_state: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                  lib=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """``prefill`` in two launches (gdn_prefill_split): q, k, v bf16 or fp16; ``workspace``
+    (a uint8 device tensor of at least ``prefill_split_workspace_size`` bytes) is allocated
+    here when not given."""
+    return _prefill_ws("gdn_prefill_split", prefill_split_workspace_size, False, q, k, v, g, beta,
+                       initial_state, cu_seqlens, chunk_size, output_final_state, out, final_state,
+                       workspace, lib)
 
 
 def kda_decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,

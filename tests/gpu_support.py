@@ -70,6 +70,23 @@ def error_stats(got: np.ndarray, ref: np.ndarray, storage=None) -> dict:
                 finite=bool(np.all(np.isfinite(got))))
 
 
+def check_pair(name: str, a: np.ndarray, b: np.ndarray, io: str, stored=True) -> float:
+    """Two kernels' results for the same inputs: each is within the tolerance of the exact
+    result, so they differ by at most twice the tolerance, beside both storage roundings
+    (stored: whether a and b were stored in io)."""
+    st = io if (stored and io != "f32") else None
+    diff = np.abs(a - b) - storage_allowance(a, st) - storage_allowance(b, st)
+    rms = float(np.sqrt(np.mean(b ** 2))) if b.size else 0.0
+    err = float(max(diff.max(), 0.0)) if diff.size else 0.0
+    print(f"  {name}: (|a - b| - roundings) max={err:.3e} rms={rms:.3e}", flush=True)
+    assert np.all(np.isfinite(a)) and np.all(np.isfinite(b)), f"{name}: non-finite values"
+    if io == "f32":
+        assert err <= 2 * TOL_F32_ABS, f"{name}: {err:.3e} > 2 x {TOL_F32_ABS}"
+    else:
+        assert err <= 2 * TOL_BF16_REL_RMS * rms, f"{name}: {err / rms:.3e} of rms > 2 x {TOL_BF16_REL_RMS}"
+    return err
+
+
 def check(name: str, got: np.ndarray, ref: np.ndarray, io: str, stored=None) -> dict:
     """stored: the 16-bit type `got` was stored in, or None / False (default: io
     when io is 16-bit and the name does not mention a state)."""

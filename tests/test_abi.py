@@ -31,7 +31,7 @@ def test_header_declares_the_boundary():
     assert declared_functions() == sorted(
         ["gdn_prefill", "gdn_decode_step", "gdn_prefill_plan", "gdn_status_string", "gdn_last_error",
          "gdn_kda_workspace_size", "gdn_kda_prefill", "gdn_kda_decode_step", "gdn_prefill_fused",
-         "gdn_decode_step_fused"])
+         "gdn_decode_step_fused", "gdn_prefill_split", "gdn_prefill_split_workspace_size"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -120,24 +120,30 @@ def test_plan(lib):
         gdn.prefill_plan(1, 16, 3, lib=lib)
 
 
-def test_kda_workspace_size(lib):
-    # one 66,048-byte tile per value head and chunk slot, T_tot / 64 + N slots
-    assert gdn.kda_workspace_size(1, 4096, 16, lib=lib) == (64 + 1) * 16 * 66048
-    assert gdn.kda_workspace_size(3, 100, 2, lib=lib) == (1 + 3) * 2 * 66048
+@pytest.mark.parametrize("size_fn", ["kda_workspace_size", "prefill_split_workspace_size"])
+def test_workspace_size(lib, size_fn):
+    # one 74,240-byte tile per value head and chunk slot, T_tot / 64 + N slots
+    f = getattr(gdn, size_fn)
+    assert f(1, 4096, 16, lib=lib) == (64 + 1) * 16 * 74240
+    assert f(3, 100, 2, lib=lib) == (1 + 3) * 2 * 74240
     with pytest.raises(gdn.GDNError):
-        gdn.kda_workspace_size(1, 10, 1, chunk_size=32, lib=lib)
+        f(1, 10, 1, chunk_size=32, lib=lib)
 
 
-def _kda_prefill(lib, **over):
+def _ws_prefill(lib, fn, **over):
     # fake, aligned, never-dereferenced addresses: validation fails before any use
     a = dict(q=0x100000, k=0x200000, v=0x300000, g=0x400000, beta=0x500000, s0=None, cu=None,
              N=1, T=10, Hk=2, Hv=4, Dk=128, Dv=128, C=64, io=1, ws=0x1000000, wsb=1 << 24,
              o=0x600000, fs=None)
     a.update(over)
     p = lambda x: None if x is None else ctypes.c_void_p(x)  # noqa: E731
-    return lib.gdn_kda_prefill(p(a["q"]), p(a["k"]), p(a["v"]), p(a["g"]), p(a["beta"]), p(a["s0"]),
-                               p(a["cu"]), a["N"], a["T"], a["Hk"], a["Hv"], a["Dk"], a["Dv"], a["C"],
-                               a["io"], p(a["ws"]), a["wsb"], p(a["o"]), p(a["fs"]), None)
+    return getattr(lib, fn)(p(a["q"]), p(a["k"]), p(a["v"]), p(a["g"]), p(a["beta"]), p(a["s0"]),
+                            p(a["cu"]), a["N"], a["T"], a["Hk"], a["Hv"], a["Dk"], a["Dv"], a["C"],
+                            a["io"], p(a["ws"]), a["wsb"], p(a["o"]), p(a["fs"]), None)
+
+
+def _kda_prefill(lib, **over):
+    return _ws_prefill(lib, "gdn_kda_prefill", **over)
 
 
 @pytest.mark.parametrize("over,status,msg", [
@@ -158,6 +164,28 @@ def test_kda_prefill_rejects(lib, over, status, msg):
 
 def test_kda_prefill_nothing_to_do_is_ok(lib):
     assert _kda_prefill(lib, q=None, k=None, v=None, g=None, beta=None, o=None, ws=None, wsb=0, T=0) == 0
+
+
+@pytest.mark.parametrize("over,status,msg", [
+    (dict(io=0), 2, "bf16 or fp16"),
+    (dict(C=32), 2, "chunk_size"),
+    (dict(wsb=1000), 1, "smaller than"),
+    (dict(ws=None), 1, "smaller than"),
+    (dict(ws=0x1000080), 1, "256-byte aligned"),
+    (dict(g=0x400002), 1, "g must be 4-byte aligned"),
+    (dict(ws=0x500000), 1, "workspace overlaps beta"),
+    (dict(fs=0x1000000), 1, "workspace overlaps an output"),
+    (dict(N=2), 1, "cu_seqlens is required"),
+])
+def test_split_prefill_rejects(lib, over, status, msg):
+    # the scalar gate's g is [T_tot, Hv] (4-byte aligned), as for gdn_prefill
+    assert _ws_prefill(lib, "gdn_prefill_split", **over) == status
+    assert msg in lib.gdn_last_error().decode()
+
+
+def test_split_prefill_nothing_to_do_is_ok(lib):
+    assert _ws_prefill(lib, "gdn_prefill_split", q=None, k=None, v=None, g=None, beta=None, o=None, ws=None,
+                       wsb=0, T=0) == 0
 
 
 def test_kda_decode_rejects(lib):

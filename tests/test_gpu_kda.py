@@ -11,7 +11,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_support import TORCH_IO, check, to_device, to_f64
+from gpu_support import TORCH_IO, check, check_pair, to_device, to_f64
 from linear_attention_chunked_gdn_amd import gdn, inputs
 
 pytestmark = pytest.mark.gpu
@@ -88,7 +88,7 @@ def test_kda_mixed_channels():
 
 def test_kda_uniform_gate_matches_scalar_gate_path():
     # a per-channel gate equal on every channel is the scalar gate: both paths meet the
-    # bar against the oracle and agree with each other to the same tolerance
+    # bar against the oracle, so they agree with each other within twice the tolerance
     x = inputs.make_custom(2300, [150, 70], 2, 2, io="bf16", init_std=0.2, name="uniform")
     xk = inputs.GDNInputs("kda_uniform", x.io, x.q, x.k, x.v, np.repeat(x.g[:, :, None], 128, axis=2),
                           x.beta, x.cu_seqlens, x.initial_state)
@@ -96,8 +96,8 @@ def test_kda_uniform_gate_matches_scalar_gate_path():
     d = to_device(x, DEV)
     og, fg = gdn.prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["initial_state"], d["cu_seqlens"])
     torch.cuda.synchronize()
-    check("kda vs scalar-gate o", to_f64(ok_), to_f64(og), "bf16")
-    check("kda vs scalar-gate state", to_f64(fk), to_f64(fg), "bf16")
+    check_pair("kda vs scalar-gate o", to_f64(ok_), to_f64(og), "bf16")
+    check_pair("kda vs scalar-gate state", to_f64(fk), to_f64(fg), "bf16", stored=False)
 
 
 @pytest.mark.parametrize("wid,io", [(1, "bf16"), (1, "f16"), (2, "bf16"), (3, "bf16")])
