@@ -122,3 +122,33 @@ def test_split_many_tiny_sequences_and_many_heads():
     lengths = rng.integers(0, 6, size=3000)
     _check_all(inputs.make_custom(5500, lengths, 1, 2, io="bf16", init_std=0.2, name="split_tiny3000"))
     _check_all(inputs.make_custom(5501, [130], 8, 64, io="f16", name="split_H64"))
+
+
+def test_split_in_a_hip_graph():
+    # both kernels captured from one call; every replay, with eager work and
+    # synchronisations between replays, gives the eager call's bits
+    x = inputs.make_workload(1)
+    d = to_device(x, DEV)
+    ws = torch.empty(gdn.prefill_split_workspace_size(x.N, x.T_tot, x.Hv), dtype=torch.uint8, device=DEV)
+    o = torch.empty((x.T_tot, x.Hv, x.Dv), dtype=torch.bfloat16, device=DEV)
+    fs = torch.empty((x.N, x.Hv, x.Dv, x.Dk), dtype=torch.float32, device=DEV)
+    call = lambda: gdn.prefill_split(*_args(d), out=o, final_state=fs, workspace=ws)  # noqa: E731
+    call()
+    torch.cuda.synchronize()
+    o_ref, f_ref = o.clone(), fs.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    for i in range(3):
+        o.zero_()
+        fs.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_ref) and torch.equal(fs, f_ref), f"replay {i} differs"
