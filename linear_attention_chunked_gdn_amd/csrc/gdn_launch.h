@@ -48,19 +48,20 @@ struct KdaArgs {
     int32_t N, T_tot, Hk, Hv;
     int32_t nslots;
 };
-// Workspace tile of one chunk and value head (byte offsets; fp16 except gl), with
-// T = (I + A)^-1 and the decays of the chunk:
-//   P  = lower-incl-diagonal(Q K^T (.) decays)       64 x 64
-//   W  = T diag(beta) (K (.) exp(Gamma))               64 x 128 (key channels)
-//   Qg = Q (.) exp(Gamma)                              64 x 128
-//   Kl = K (.) exp(Gamma_last - Gamma)                 64 x 128
-//   U  = T diag(beta) V                                64 x 128 (value channels)
-//   gl = exp(Gamma_last)                               128 fp32
+// Workspace tile of one chunk and value head (byte offsets; fp16 except gl; row-major),
+// with T = (I + A)^-1 and the decays of the chunk:
+//   P   = lower-incl-diagonal(Q K^T (.) decays)      [64 tokens][64 tokens]
+//   W   = T diag(beta) (K (.) exp(Gamma))             [64 tokens][128 key channels]
+//   Qg  = Q (.) exp(Gamma)                            [64 tokens][128 key channels]
+//   KlT = (K (.) exp(Gamma_last - Gamma))^T           [128 key channels][64 tokens]
+//   UT  = (T diag(beta) V)^T                          [128 value channels][64 tokens]
+//   gl  = exp(Gamma_last)                             [128 key channels] fp32
+// Each is laid out so that one chain wave's MFMA fragments are 16-byte row segments.
 constexpr int WS_OFF_P = 0;
 constexpr int WS_OFF_W = 8192;
 constexpr int WS_OFF_QG = 24576;
-constexpr int WS_OFF_KL = 40960;
-constexpr int WS_OFF_U = 57344;
+constexpr int WS_OFF_KLT = 40960;
+constexpr int WS_OFF_UT = 57344;
 constexpr int WS_OFF_GL = 73728;
 constexpr size_t WS_TILE_BYTES = 74240;
 hipError_t launch_kda_map(const KdaArgs &a, bool f16, hipStream_t stream);

@@ -8,8 +8,8 @@
 //
 //   A = strictly-lower(diag(beta) K K^T .* D),   T = (I + A)^-1,
 //   P = lower-incl-diagonal(Q K^T .* D),
-//   W = T diag(beta gamma) K,  U = T diag(beta) V,
-//   Qg = diag(gamma) Q,  Kl = diag(lambda) K,  gl = gamma_last,
+//   W = T diag(beta gamma) K,  U = T diag(beta) V (stored transposed),
+//   Qg = diag(gamma) Q,  Kl = diag(lambda) K (stored transposed),  gl = gamma_last,
 //
 // so that the chain's v = U - W S^T (= T diag(beta) (V - diag(gamma) K S^T)),
 // O = Qg S^T + P v and S <- gl S + v^T Kl are the scalar-gate chunk formulas with the
@@ -155,22 +155,36 @@ __global__ __launch_bounds__(THREADS, 2) void gdn_map_kernel(const KdaArgs a) {
     for (int i = tid; i < CH * AS; i += THREADS) s.T[i] = 0.f;
     __syncthreads();
 
-    // the decayed operands of the chain, fp16
+    // the decayed operands of the chain, fp16: Qg token-major from the registers; Kl
+    // transposed from the k tile in LDS (wave b: tokens 16b .. 16b + 15, lane: channels
+    // 2 lane and 2 lane + 1, two 16-byte row segments of Kl^T per channel)
     {
         hf *qg = reinterpret_cast<hf *>(tile + WS_OFF_QG);
-        hf *kl = reinterpret_cast<hf *>(tile + WS_OFF_KL);
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
             const int idx = tid + THREADS * p, row = idx >> 4;
-            const float gm = s.gam[row], lm = s.lam[row];
-            f16x8 xq, xl;
+            const float gm = s.gam[row];
+            f16x8 xq;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                xq[e] = (hf)(Cvt<IO>::to_f32(qv[p][e]) * gm);
-                xl[e] = (hf)(Cvt<IO>::to_f32(kv[p][e]) * lm);
-            }
+            for (int e = 0; e < 8; ++e) xq[e] = (hf)(Cvt<IO>::to_f32(qv[p][e]) * gm);
             *reinterpret_cast<f16x8 *>(qg + 8 * idx) = xq;
-            *reinterpret_cast<f16x8 *>(kl + 8 * idx) = xl;
+        }
+        typedef IO v2 __attribute__((ext_vector_type(2)));
+        const int ch = 2 * lane;
+        f16x8 kl[2][2];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int t = 16 * wave + i;
+            const v2 kk = *reinterpret_cast<const v2 *>(&s.kq.K[t * XS + ch]);
+            const float lm = s.lam[t];
+            kl[0][i >> 3][i & 7] = (hf)(Cvt<IO>::to_f32(kk[0]) * lm);
+            kl[1][i >> 3][i & 7] = (hf)(Cvt<IO>::to_f32(kk[1]) * lm);
+        }
+        hf *klt = reinterpret_cast<hf *>(tile + WS_OFF_KLT);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            *reinterpret_cast<f16x8 *>(klt + (ch + j) * CH + 16 * wave) = kl[j][0];
+            *reinterpret_cast<f16x8 *>(klt + (ch + j) * CH + 16 * wave + 8) = kl[j][1];
         }
     }
 
@@ -253,7 +267,7 @@ __global__ __launch_bounds__(THREADS, 2) void gdn_map_kernel(const KdaArgs a) {
         __syncthreads();
     }
     // #4 W = T diag(beta gamma) K and U = T diag(beta) V to the workspace
-    wy_products(s.T, AS, s.wy.Kb, s.wy.Vb, tile + WS_OFF_W, tile + WS_OFF_U, wave, l16, g4);
+    wy_products(s.T, AS, s.wy.Kb, s.wy.Vb, tile + WS_OFF_W, tile + WS_OFF_UT, wave, l16, g4);
 }
 
 }  // namespace gdnmap

@@ -40,10 +40,12 @@ __device__ __forceinline__ Frag<_Float16> wy_frag_t(const _Float16 *x, int c0, i
 // T: fp32, row stride `as`, lower triangular (zeros above the diagonal).  kg, vb:
 // diag(beta) Kg and diag(beta) V, fp16 [token][channel] with row stride WY_S, in LDS.
 // Wave `wave` (0..3) forms channel tiles 2 wave and 2 wave + 1 of both products and
-// writes them to the workspace (wout, uout: 64 x 128 fp16, row-major).  The products are taken transposed (operand^T T^T),
-// so a lane holds token 16I + l16 and four consecutive channels: one 8-byte store.
+// writes them to the workspace: W row-major [token][channel] (wout), U transposed
+// [channel][token] (utout).  The products are taken transposed (operand^T T^T), so a lane
+// holds token 16I + l16 and four consecutive channels: one 8-byte store of W, four 2-byte
+// stores of U^T.
 __device__ __forceinline__ void wy_products(const float *T, int as, const _Float16 *kg, const _Float16 *vb,
-                                            char *wout, char *uout, int wave, int l16, int g4) {
+                                            char *wout, char *utout, int wave, int l16, int g4) {
     typedef _Float16 hf;
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
@@ -75,14 +77,13 @@ __device__ __forceinline__ void wy_products(const float *T, int as, const _Float
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const int c = 16 * (2 * wave + j) + 4 * g4;
-            f16x4 w, u;
+            f16x4 w;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 w[i] = (hf)acc[j][0][i];
-                u[i] = (hf)acc[j][1][i];
+                reinterpret_cast<hf *>(utout)[(c + i) * 64 + r] = (hf)acc[j][1][i];
             }
             *reinterpret_cast<f16x4 *>(wout + (r * 128 + c) * 2) = w;
-            *reinterpret_cast<f16x4 *>(uout + (r * 128 + c) * 2) = u;
         }
     }
 }

@@ -20,6 +20,9 @@
 // column-wise split of S is the same: one workgroup per (sequence, value head, 16 value
 // channels).
 //
+// Kl and U come from the map transposed (Kl^T [key][token], U^T [value ch][token]), so
+// the update's Kl^T operand and the U term of v are plain row segments in LDS.
+//
 // Roles: waves 0-3 load the workspace tiles one chunk ahead and commit them to LDS;
 // waves 4-7 run the chain.  A chunk takes two barrier-separated phases:
 //   phase 1: chain v(c), Q S^T(c)   | loaders: commit P, Kl, gl of c
@@ -41,20 +44,19 @@ constexpr int DK = 128;
 constexpr int DV = 128;
 constexpr int DVS = 16;        // value channels per workgroup
 constexpr int THREADS = 512;   // 4 loader + 4 chain waves
-constexpr int KS = DK + 16;    // fp16 row stride of W, Qg, Kl and the state copy (288 B)
+constexpr int KS = DK + 16;    // fp16 row stride of W, Qg and the state copy (288 B)
 constexpr int TS = CH + 16;    // fp16 row stride of v^T (160 B)
-constexpr int TP = CH + 8;     // fp16 row stride of P (144 B)
-constexpr int US = DVS;        // fp16 row stride of the U slice
+constexpr int TP = CH + 8;     // fp16 row stride of P, Kl^T and U^T (144 B)
 
 struct __align__(16) Smem {
     hf S[DVS * KS];            // fp16 copy of the state slice [value ch][key ch]
     hf Vh[DVS * TS];           // v^T
-    hf U[CH * US];             // U slice [token][value ch]
+    hf U[DVS * TP];            // U^T slice [value ch][token]
     float gl[DK];              // exp(Gamma_last) per key channel
     hf P[CH * TP];
     hf W[CH * KS];
     hf Qg[CH * KS];
-    hf Kl[CH * KS];
+    hf Kl[DK * TP];            // Kl^T [key ch][token]
 };
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
@@ -82,8 +84,8 @@ __device__ __forceinline__ void load_a(StageA &st, const Work &wk, int c, int ld
     for (int p = 0; p < 2; ++p)       // 64 rows x 8 segments of 16 B
         st.p[p] = *reinterpret_cast<const u32x4 *>(tile + WS_OFF_P + (ld + 256 * p) * 16);
 #pragma unroll
-    for (int p = 0; p < 4; ++p)       // 64 rows x 16 segments
-        st.kl[p] = *reinterpret_cast<const u32x4 *>(tile + WS_OFF_KL + (ld + 256 * p) * 16);
+    for (int p = 0; p < 4; ++p)       // 128 rows x 8 segments
+        st.kl[p] = *reinterpret_cast<const u32x4 *>(tile + WS_OFF_KLT + (ld + 256 * p) * 16);
     st.gl = *reinterpret_cast<const u32x4 *>(tile + WS_OFF_GL + (ld & 31) * 16);
 }
 
@@ -95,8 +97,8 @@ __device__ __forceinline__ void commit_a(const StageA &st, Smem &s, int ld) {
     }
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-        const int idx = ld + 256 * p, row = idx >> 4, seg = idx & 15;
-        *reinterpret_cast<u32x4 *>(&s.Kl[row * KS + seg * 8]) = st.kl[p];
+        const int idx = ld + 256 * p, row = idx >> 3, seg = idx & 7;
+        *reinterpret_cast<u32x4 *>(&s.Kl[row * TP + seg * 8]) = st.kl[p];
     }
     if (ld < 32) *reinterpret_cast<u32x4 *>(&s.gl[ld * 4]) = st.gl;
 }
@@ -108,9 +110,10 @@ __device__ __forceinline__ void load_b(StageB &st, const Work &wk, int c, int ld
         st.w[p] = *reinterpret_cast<const u32x4 *>(tile + WS_OFF_W + (ld + 256 * p) * 16);
         st.qg[p] = *reinterpret_cast<const u32x4 *>(tile + WS_OFF_QG + (ld + 256 * p) * 16);
     }
-    // U slice: 64 rows x 2 segments of 8 value channels (threads 0-127; the rest repeat them)
-    const int ur = (ld & 127) >> 1, us = ld & 1;
-    st.u = *reinterpret_cast<const u32x4 *>(tile + WS_OFF_U + (ur * DV + wk.dv0 + 8 * us) * 2);
+    // U^T slice: 16 rows (value channels) x 8 segments of 8 tokens (threads 0-127; the rest
+    // repeat them)
+    const int ur = (ld & 127) >> 3, us = ld & 7;
+    st.u = *reinterpret_cast<const u32x4 *>(tile + WS_OFF_UT + ((wk.dv0 + ur) * CH + 8 * us) * 2);
 }
 
 __device__ __forceinline__ void commit_b(const StageB &st, Smem &s, int ld) {
@@ -120,7 +123,7 @@ __device__ __forceinline__ void commit_b(const StageB &st, Smem &s, int ld) {
         *reinterpret_cast<u32x4 *>(&s.W[row * KS + seg * 8]) = st.w[p];
         *reinterpret_cast<u32x4 *>(&s.Qg[row * KS + seg * 8]) = st.qg[p];
     }
-    if (ld < 128) *reinterpret_cast<u32x4 *>(&s.U[(ld >> 1) * US + 8 * (ld & 1)]) = st.u;
+    if (ld < 128) *reinterpret_cast<u32x4 *>(&s.U[(ld >> 3) * TP + 8 * (ld & 7)]) = st.u;
 }
 
 // Phase 1: v = U - W S^T for tokens [16W, 16W + 16) (lane = value channel, rows =
@@ -139,9 +142,10 @@ __device__ __forceinline__ f32x4 chain_v_QS(Smem &s, int W, int l16, int g4) {
         fw.load8(wrow + 32 * kb);
         mma(ws, fw, fs[kb]);
     }
+    const f16x4 u = *reinterpret_cast<const f16x4 *>(&s.U[l16 * TP + t0]);
     f16x4 x;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) x[i] = (hf)((float)s.U[(t0 + i) * US + l16] - ws[i]);
+    for (int i = 0; i < 4; ++i) x[i] = (hf)((float)u[i] - ws[i]);
     *reinterpret_cast<f16x4 *>(&s.Vh[l16 * TS + t0]) = x;
     f32x4 qs = zero4();
 #pragma unroll
@@ -159,17 +163,20 @@ template <typename IO>
 __device__ __forceinline__ void chain_out_update(Smem &s, const KdaArgs &a, int W, int l16, int g4,
                                                  const f32x4 &qs, f32x4 (&st)[2], int h, int dv0,
                                                  int tok0, int nval) {
-    const int t = 16 * W + l16;
+    Frag<hf> fv[2];   // v^T rows (value channel l16), tokens 32kb + 8g4 .. + 7
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) fv[kb].load8(s.Vh + l16 * TS + 32 * kb + 8 * g4);
     {
         // O^T = S Qg^T + v^T P^T: lane = token 16W + l16, rows = value channels 4G..4G+3
         f32x4 acc = qs;
         const hf *ph = s.P + (16 * W + l16) * TP + 8 * g4;
-        for (int kb = 0; kb <= (W >> 1); ++kb) {
-            Frag<hf> fp, fv;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            Frag<hf> fp;
             fp.load8(ph + 32 * kb);
-            fv.load8(s.Vh + l16 * TS + 32 * kb + 8 * g4);
-            mma(acc, fv, fp);
+            mma(acc, fv[kb], fp);   // P is zero above the diagonal (kb = 1 for W < 2)
         }
+        const int t = 16 * W + l16;
         if (t < nval) {
             typename Vec4<IO>::type y;
 #pragma unroll
@@ -180,30 +187,16 @@ __device__ __forceinline__ void chain_out_update(Smem &s, const KdaArgs &a, int 
     }
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
-        // Kl^T fragments by ds_read_b64_tr_b16 (slot e of group G = token 32kb + 8G + e,
-        // row = key channel 32W + 16mt + l16), as in gdn_prefill_pipe.hip
-        Frag<hf> ka[2];
-        const int a_tok = l16 >> 2, a_ch = 32 * W + 16 * mt + 4 * (l16 & 3);
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-                const int t0 = 32 * kb + 8 * g4 + 4 * hh;
-                typedef __fp16 fp16x4 __attribute__((ext_vector_type(4)));
-                typedef __attribute__((address_space(3))) fp16x4 lds_fp16x4;
-                const f16x4 v = __builtin_bit_cast(
-                    f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4 *)&s.Kl[(t0 + a_tok) * KS + a_ch]));
-#pragma unroll
-                for (int e = 0; e < 4; ++e) ka[kb].set_raw(4 * hh + e, v[e]);
-            }
+        // Kl^T rows 32W + 16mt + l16 (key channels), tokens 32kb + 8g4 .. + 7
+        const hf *kr = s.Kl + (32 * W + 16 * mt + l16) * TP + 8 * g4;
         const int kc = 32 * W + 16 * mt + 4 * g4;
         const f32x4 gl = *reinterpret_cast<const f32x4 *>(&s.gl[kc]);
         f32x4 acc = st[mt] * gl;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-            Frag<hf> fv;
-            fv.load8(s.Vh + l16 * TS + 32 * kb + 8 * g4);
-            mma(acc, ka[kb], fv);
+            Frag<hf> fk;
+            fk.load8(kr + 32 * kb);
+            mma(acc, fk, fv[kb]);
         }
         st[mt] = acc;
         f16x4 x;

@@ -12,7 +12,7 @@
 //   T = (I + A)^-1,
 // and the S-dependent half (kda_chain.hip) needs W = T diag(beta) (K (.) exp(Gamma)),
 // U = T diag(beta) V, Q (.) exp(Gamma), K (.) exp(Gamma_last - Gamma) and
-// exp(Gamma_last).  None of this depends on the state, so every chunk of every head is
+// exp(Gamma_last) (U and the last K transposed, in the layouts the chain reads).  None of this depends on the state, so every chunk of every head is
 // one independent workgroup here (the Map phases #1-#4 of the page's Map-Reduce-Map
 // pipeline), and the results go to a workspace tile the chain kernel reads: with a
 // per-channel gate this map is several times the chain's work, and doing it once per
@@ -254,7 +254,7 @@ __global__ __launch_bounds__(THREADS, 2) void kda_map_kernel(const KdaArgs a) {
     f16x2 kgb[16];
     {
         hf *qg = reinterpret_cast<hf *>(tile + WS_OFF_QG);
-        hf *kl = reinterpret_cast<hf *>(tile + WS_OFF_KL);
+        f16x8 kl[2][2];   // Kl^T rows ch, ch + 1 over this block's 16 tokens
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int t = 16 * b + i;
@@ -269,8 +269,14 @@ __global__ __launch_bounds__(THREADS, 2) void kda_map_kernel(const KdaArgs a) {
             f16x2 x;
             x[0] = (hf)(Cvt<IO>::to_f32(qv[0]) * e0); x[1] = (hf)(Cvt<IO>::to_f32(qv[1]) * e1);
             *reinterpret_cast<f16x2 *>(&qg[t * DK + ch]) = x;
-            x[0] = (hf)(k0 * l0); x[1] = (hf)(k1 * l1);
-            *reinterpret_cast<f16x2 *>(&kl[t * DK + ch]) = x;
+            kl[0][i >> 3][i & 7] = (hf)(k0 * l0);
+            kl[1][i >> 3][i & 7] = (hf)(k1 * l1);
+        }
+        hf *klt = reinterpret_cast<hf *>(tile + WS_OFF_KLT);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            *reinterpret_cast<f16x8 *>(klt + (ch + j) * CH + 16 * b) = kl[j][0];
+            *reinterpret_cast<f16x8 *>(klt + (ch + j) * CH + 16 * b + 8) = kl[j][1];
         }
         if (b == 0) {
             f32x2 gl;
@@ -445,7 +451,7 @@ __global__ __launch_bounds__(THREADS, 2) void kda_map_kernel(const KdaArgs a) {
         __syncthreads();
     }
     // #4 W = T diag(beta) Kg and U = T diag(beta) V to the workspace
-    wy_products(s.sv.T, AS, s.wy.Kb, s.wy.Vb, tile + WS_OFF_W, tile + WS_OFF_U, wave, l16, g4);
+    wy_products(s.sv.T, AS, s.wy.Kb, s.wy.Vb, tile + WS_OFF_W, tile + WS_OFF_UT, wave, l16, g4);
 }
 
 }  // namespace kdamap
