@@ -23,10 +23,11 @@
 // Kl and U come from the map transposed (Kl^T [key][token], U^T [value ch][token]), so
 // the update's Kl^T operand and the U term of v are plain row segments in LDS.
 //
-// Roles: waves 0-3 load the workspace tiles one chunk ahead and commit them to LDS;
-// waves 4-7 run the chain.  A chunk takes two barrier-separated phases:
-//   phase 1: chain v(c), Q S^T(c)   | loaders: commit P, Kl, gl of c
-//   phase 2: chain O(c), S update   | loaders: commit W, Qg, U of c + 1
+// Roles: waves 0-3 load the workspace tiles one chunk ahead and commit them to LDS, and
+// form the outputs, which nothing downstream in the chunk waits for; waves 4-7 run only
+// the recurrence.  A chunk takes two barrier-separated phases:
+//   phase 1: chain v(c)        | loaders: commit P, Kl, gl of c; Q S^T(c) from the state copy
+//   phase 2: chain S update    | loaders: commit W, Qg, U of c + 1; O(c) = Q S^T + P v
 // Each tile is committed after its last reader of the previous chunk and before its
 // first reader, so one LDS copy of every tile suffices.
 #include "gdn_device.h"
@@ -126,65 +127,73 @@ __device__ __forceinline__ void commit_b(const StageB &st, Smem &s, int ld) {
     if (ld < 128) *reinterpret_cast<u32x4 *>(&s.U[(ld >> 3) * TP + 8 * (ld & 7)]) = st.u;
 }
 
-// Phase 1: v = U - W S^T for tokens [16W, 16W + 16) (lane = value channel, rows =
-// tokens), stored transposed; then (Q S^T)^T = S Qg^T from the same S fragments.
-__device__ __forceinline__ f32x4 chain_v_QS(Smem &s, int W, int l16, int g4) {
+// Phase 1, chain wave W: v = U - W S^T for tokens [16W, 16W + 16) (lane = value channel,
+// rows = tokens), stored transposed.
+__device__ __forceinline__ void chain_v(Smem &s, int W, int l16, int g4) {
     const hf *wrow = s.W + (16 * W + l16) * KS + 8 * g4;
-    const hf *qrow = s.Qg + (16 * W + l16) * KS + 8 * g4;
     const hf *srow = s.S + l16 * KS + 8 * g4;
     const int t0 = 16 * W + 4 * g4;
-    Frag<hf> fs[4];
     f32x4 ws = zero4();
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-        Frag<hf> fw;
-        fs[kb].load8(srow + 32 * kb);
+        Frag<hf> fs, fw;
+        fs.load8(srow + 32 * kb);
         fw.load8(wrow + 32 * kb);
-        mma(ws, fw, fs[kb]);
+        mma(ws, fw, fs);
     }
     const f16x4 u = *reinterpret_cast<const f16x4 *>(&s.U[l16 * TP + t0]);
     f16x4 x;
 #pragma unroll
     for (int i = 0; i < 4; ++i) x[i] = (hf)((float)u[i] - ws[i]);
     *reinterpret_cast<f16x4 *>(&s.Vh[l16 * TS + t0]) = x;
+}
+
+// Phase 1, loader wave W (off the chain's critical path): (Q S^T)^T = S Qg^T for tokens
+// [16W, 16W + 16) (lane = token, rows = value channels 4G..4G+3), from the state copy,
+// which holds the chunk's starting state until phase 2.
+__device__ __forceinline__ f32x4 loader_QS(const Smem &s, int W, int l16, int g4) {
+    const hf *qrow = s.Qg + (16 * W + l16) * KS + 8 * g4;
+    const hf *srow = s.S + l16 * KS + 8 * g4;
     f32x4 qs = zero4();
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-        Frag<hf> fq;
+        Frag<hf> fs, fq;
+        fs.load8(srow + 32 * kb);
         fq.load8(qrow + 32 * kb);
-        mma(qs, fs[kb], fq);
+        mma(qs, fs, fq);
     }
     return qs;
 }
 
-// Phase 2: output rows of wave W, then the update of key channels [32W, 32W + 32) of
-// the state slice: S^T rows (key channels) 32W + 16mt + 4G + r, column = value channel.
+// Phase 2, loader wave W: O^T = S Qg^T + v^T P^T for tokens [16W, 16W + 16), stored.
 template <typename IO>
-__device__ __forceinline__ void chain_out_update(Smem &s, const KdaArgs &a, int W, int l16, int g4,
-                                                 const f32x4 &qs, f32x4 (&st)[2], int h, int dv0,
-                                                 int tok0, int nval) {
+__device__ __forceinline__ void loader_O(const Smem &s, const KdaArgs &a, int W, int l16, int g4, const f32x4 &qs,
+                                         int h, int dv0, int tok0, int nval) {
+    f32x4 acc = qs;
+    const hf *ph = s.P + (16 * W + l16) * TP + 8 * g4;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+        Frag<hf> fp, fv;
+        fp.load8(ph + 32 * kb);
+        fv.load8(s.Vh + l16 * TS + 32 * kb + 8 * g4);
+        mma(acc, fv, fp);   // P is zero above the diagonal (kb = 1 for W < 2)
+    }
+    const int t = 16 * W + l16;
+    if (t < nval) {
+        typename Vec4<IO>::type y;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) y[i] = Cvt<IO>::from_f32(acc[i]);
+        *reinterpret_cast<typename Vec4<IO>::type *>(reinterpret_cast<IO *>(a.o) +
+                                                     ((size_t)(tok0 + t) * a.Hv + h) * DV + dv0 + 4 * g4) = y;
+    }
+}
+
+// Phase 2, chain wave W: the update of key channels [32W, 32W + 32) of the state slice:
+// S^T rows (key channels) 32W + 16mt + 4G + r, column = value channel.
+__device__ __forceinline__ void chain_update(Smem &s, int W, int l16, int g4, f32x4 (&st)[2]) {
     Frag<hf> fv[2];   // v^T rows (value channel l16), tokens 32kb + 8g4 .. + 7
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) fv[kb].load8(s.Vh + l16 * TS + 32 * kb + 8 * g4);
-    {
-        // O^T = S Qg^T + v^T P^T: lane = token 16W + l16, rows = value channels 4G..4G+3
-        f32x4 acc = qs;
-        const hf *ph = s.P + (16 * W + l16) * TP + 8 * g4;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            Frag<hf> fp;
-            fp.load8(ph + 32 * kb);
-            mma(acc, fv[kb], fp);   // P is zero above the diagonal (kb = 1 for W < 2)
-        }
-        const int t = 16 * W + l16;
-        if (t < nval) {
-            typename Vec4<IO>::type y;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) y[i] = Cvt<IO>::from_f32(acc[i]);
-            *reinterpret_cast<typename Vec4<IO>::type *>(reinterpret_cast<IO *>(a.o) +
-                                                         ((size_t)(tok0 + t) * a.Hv + h) * DV + dv0 + 4 * g4) = y;
-        }
-    }
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
         // Kl^T rows 32W + 16mt + l16 (key channels), tokens 32kb + 8g4 .. + 7
@@ -260,20 +269,22 @@ __global__ __launch_bounds__(THREADS) void kda_chain_kernel(const KdaArgs a) {
         __syncthreads();
         if (is_loader) {
             for (int c = 0; c < wk.nchunks; ++c) {
+                const int tok0 = wk.bos + c * CH;
+                const int nval = min(CH, wk.eos - tok0);
                 commit_a(sa, s, tid);
                 load_a(sa, wk, c + 1, tid);
+                const f32x4 qs = loader_QS(s, W, l16, g4);
                 __syncthreads();
                 commit_b(sb, s, tid);
                 load_b(sb, wk, c + 2, tid);
+                loader_O<IO>(s, a, W, l16, g4, qs, h, wk.dv0, tok0, nval);
                 __syncthreads();
             }
         } else {
             for (int c = 0; c < wk.nchunks; ++c) {
-                const int tok0 = wk.bos + c * CH;
-                const int nval = min(CH, wk.eos - tok0);
-                const f32x4 qs = chain_v_QS(s, W, l16, g4);
+                chain_v(s, W, l16, g4);
                 __syncthreads();
-                chain_out_update<IO>(s, a, W, l16, g4, qs, st, h, wk.dv0, tok0, nval);
+                chain_update(s, W, l16, g4, st);
                 __syncthreads();
             }
         }
