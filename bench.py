@@ -1,14 +1,16 @@
 """Throughput of the chunked gated delta-rule prefill on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload I] [--io bf16|f16|f32]
-                    [--path auto|pipe|split] [--kda] [--prologue] [--no-cpu-baseline]
+                    [--path auto|pipe|split] [--chunk 32|64|128] [--kda] [--prologue]
+                    [--no-cpu-baseline]
 
 A step is one prefill call over the whole workload (all heads, all chunks) with inputs
 resident in HBM: gdn_prefill (one launch), or gdn_prefill_split (a chunk-parallel map
 kernel, then the chain kernel, over a workspace allocated once outside the timed
 region).  --path auto (the default) takes the split path when the one-launch kernel's
 workgroups -- sequences x value heads x 8 value-channel slices, one per CU -- would
-occupy at most half of the 256 CUs (the headline shape), else gdn_prefill.  The default workload is the headline one: one sequence of
+occupy at most half of the 256 CUs (the headline shape), else gdn_prefill.  --chunk sets
+the split path's chunk length (64 by default; the one-launch and KDA paths run 64).  The default workload is the headline one: one sequence of
 T=4096 tokens, 16 heads, d=128, bf16 q/k/v/o, fp32 g/beta/state, chunk 64.  Input
 sets are rotated across steps (more bytes than the 256 MB Infinity Cache) so that
 every step streams from HBM.  Prints ONE JSON line.
@@ -326,6 +328,8 @@ def main() -> int:
     ap.add_argument("--path", choices=["auto", "pipe", "split"], default="auto",
                     help="scalar-gate prefill entry point: gdn_prefill (pipe), gdn_prefill_split, "
                          "or by shape (auto)")
+    ap.add_argument("--chunk", type=int, choices=[32, 64, 128], default=64,
+                    help="chunk length of the split path (gdn_prefill_split)")
     ap.add_argument("--kda", action="store_true",
                     help="one decay per key channel (gdn_kda_prefill) on the same workload")
     ap.add_argument("--prologue", action="store_true",
@@ -390,8 +394,12 @@ def main() -> int:
     if path == "split" and (x.io == "f32" or pro):
         print("bench.py: --path split takes bf16 or fp16 I/O without the prologue", file=sys.stderr)
         return 2
+    chunk = args.chunk if path == "split" else 64
+    if args.chunk != 64 and path != "split":
+        print("bench.py: --chunk applies to the split path only", file=sys.stderr)
+        return 2
     ws_bytes = {"kda": gdn.kda_workspace_size, "split": gdn.prefill_split_workspace_size}
-    ws = (torch.empty(ws_bytes[path](x.N, x.T_tot, x.Hv), dtype=torch.uint8, device=dev)
+    ws = (torch.empty(ws_bytes[path](x.N, x.T_tot, x.Hv, chunk), dtype=torch.uint8, device=dev)
           if path in ws_bytes else None)
 
     def step(i):
@@ -400,7 +408,7 @@ def main() -> int:
             gdn.kda_prefill(s["q"], s["k"], s["v"], s["g"], s["beta"], s["init"], s["cu"],
                             out=s["o"], final_state=s["fs"], workspace=ws)
         elif path == "split":
-            gdn.prefill_split(s["q"], s["k"], s["v"], s["g"], s["beta"], s["init"], s["cu"],
+            gdn.prefill_split(s["q"], s["k"], s["v"], s["g"], s["beta"], s["init"], s["cu"], chunk_size=chunk,
                               out=s["o"], final_state=s["fs"], workspace=ws)
         else:
             gdn.prefill(s["q"], s["k"], s["v"], s["g"], s["beta"], s["init"], s["cu"],
@@ -444,7 +452,7 @@ def main() -> int:
                   "within_tolerance": ok}
 
     nbytes = algorithmic_bytes(x)
-    flops = algorithmic_flops(x)
+    flops = algorithmic_flops(x, chunk)
     sec = ms_per_step / 1e3
     if path in ("kda", "split"):
         kernel = ("kda_map_kernel" if path == "kda" else "gdn_map_kernel") + "+kda_chain_kernel"
@@ -475,11 +483,11 @@ def main() -> int:
         "dtype": x.io,
         "data": "synthetic",
         "config": {"workload": x.name, "sequences": x.N, "tokens": x.T_tot, "Hk": x.Hk, "Hv": x.Hv,
-                   "d": x.Dk, "chunk": 64, "io": x.io, "state": "fp32",
+                   "d": x.Dk, "chunk": chunk, "io": x.io, "state": "fp32",
                    "initial_state": x.initial_state is not None},
         "roofline": {"bound": "hbm", "achieved": nbytes / sec / 1e9, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": nbytes / sec / 1e9 / HBM_PEAK_GBS,
-                     "traffic": recorded_traffic(kernel, x.name)},
+                     "traffic": recorded_traffic(kernel, x.name) if chunk == 64 else None},
         "mfma": {"achieved": flops / sec / 1e12, "peak": mfma_peak, "unit": "TFLOP/s",
                  "frac": flops / sec / 1e12 / mfma_peak, "algorithmic_flops": flops},
         "algorithmic_bytes": nbytes,

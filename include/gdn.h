@@ -215,6 +215,10 @@ gdn_status gdn_kda_decode_step(const void *q, const void *k, const void *v,
  * compute units (gdn_prefill repeats the map work for each slice on the recurrence's
  * critical path).  Arguments as for gdn_prefill, plus:
  *
+ *   chunk_size     32, 64 or 128 tokens per chunk (others return GDN_ERR_UNSUPPORTED);
+ *                  the result does not depend on it beyond rounding.  64 is the fastest
+ *                  on MI355X: 32 doubles the chain's serial steps, 128 quadruples the
+ *                  intra-chunk products and the map's solve.
  *   io_dtype       GDN_BF16 or GDN_F16 (GDN_F32 returns GDN_ERR_UNSUPPORTED)
  *   workspace      device scratch owned by the caller, at least
  *                  gdn_prefill_split_workspace_size(...) bytes, 256-byte aligned,
@@ -223,8 +227,10 @@ gdn_status gdn_kda_decode_step(const void *q, const void *k, const void *v,
  *                  in flight at once.
  *   workspace_bytes  its size in bytes
  *
- * gdn_prefill_split_workspace_size -- the workspace bytes for these sizes (the same
- * tiles as gdn_kda_workspace_size).  Host pointer `bytes`.
+ * gdn_prefill_split_workspace_size -- the workspace bytes for these sizes and chunk length:
+ * one tile per value head and chunk slot (T_tot / chunk_size + N slots) of
+ * C^2 * 2 + C * 1024 + 512 bytes for C = chunk_size (74,240 at C = 64, as for
+ * gdn_kda_workspace_size).  Host pointer `bytes`.
  */
 gdn_status gdn_prefill_split_workspace_size(int32_t N, int32_t T_tot, int32_t Hv,
                                             int32_t chunk_size, size_t *bytes);

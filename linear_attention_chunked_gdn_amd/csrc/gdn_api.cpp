@@ -117,12 +117,20 @@ gdn_status gdn_prefill_plan(int32_t N, int32_t Hv, int32_t Dv, gdn_dtype io_dtyp
 
 namespace {
 
-// Host-side checks shared by the two prefill entry points: g holds g_width values per
+// Chunk lengths of the scalar-gate two-launch prefill.
+bool split_chunk_ok(int32_t c) { return c == 32 || c == 64 || c == 128; }
+
+size_t tile_bytes(int32_t c) {
+    return c == 32 ? gdn::Tile<32>::BYTES : c == 128 ? gdn::Tile<128>::BYTES : gdn::Tile<64>::BYTES;
+}
+
+// Host-side checks shared by the prefill entry points (any_chunk: the chunk lengths of
+// split_chunk_ok, else 64 only): g holds g_width values per
 // (token, value head) (1, or Dk for a per-key-channel gate); ws / ws_bytes is the
 // workspace (none for the scalar gate).
 gdn_status check_prefill(const void *q, const void *k, const void *v, const float *g, const float *beta,
                          const float *initial_state, const int32_t *cu_seqlens, int32_t N, int32_t T_tot,
-                         int32_t Hk, int32_t Hv, int32_t Dk, int32_t Dv, int32_t chunk_size,
+                         int32_t Hk, int32_t Hv, int32_t Dk, int32_t Dv, int32_t chunk_size, bool any_chunk,
                          gdn_dtype io_dtype, const void *o, const float *final_state, size_t g_width,
                          const void *ws, size_t ws_bytes) {
     if (!valid_dtype(io_dtype))
@@ -134,8 +142,9 @@ gdn_status check_prefill(const void *q, const void *k, const void *v, const floa
         return fail(GDN_ERR_INVALID_ARGUMENT, "Hv=%d is not a multiple of Hk=%d", Hv, Hk);
     if (Dk != kD || Dv != kD)
         return fail(GDN_ERR_UNSUPPORTED, "Dk=%d, Dv=%d (only 128 is implemented)", Dk, Dv);
-    if (chunk_size != kChunk)
-        return fail(GDN_ERR_UNSUPPORTED, "chunk_size=%d (only 64 is implemented)", chunk_size);
+    if (any_chunk ? !split_chunk_ok(chunk_size) : chunk_size != kChunk)
+        return fail(GDN_ERR_UNSUPPORTED, "chunk_size=%d (%s)", chunk_size,
+                    any_chunk ? "32, 64 or 128 are implemented" : "only 64 is implemented");
     if (N > 1 && !cu_seqlens)
         return fail(GDN_ERR_INVALID_ARGUMENT, "cu_seqlens is required when N=%d > 1", N);
     if (T_tot > 0 && (!q || !k || !v || !g || !beta || !o))
@@ -174,7 +183,7 @@ gdn_status check_prefill(const void *q, const void *k, const void *v, const floa
 
 // Chunk slots of the per-key-channel prefill: chunk j of sequence n uses slot
 // cu[n] / 64 + n + j, and these never exceed T_tot / 64 + N.
-size_t kda_slots(int32_t N, int32_t T_tot) { return (size_t)T_tot / kChunk + (size_t)N; }
+size_t kda_slots(int32_t N, int32_t T_tot, int32_t C = kChunk) { return (size_t)T_tot / C + (size_t)N; }
 
 }  // namespace
 
@@ -186,7 +195,7 @@ gdn_status gdn_prefill(const void *q, const void *k, const void *v, const float 
                        int32_t chunk_size, gdn_dtype io_dtype, void *o, float *final_state,
                        void *stream) {
     const gdn_status cs = check_prefill(q, k, v, g, beta, initial_state, cu_seqlens, N, T_tot, Hk, Hv, Dk,
-                                        Dv, chunk_size, io_dtype, o, final_state, 1, nullptr, 0);
+                                        Dv, chunk_size, false, io_dtype, o, final_state, 1, nullptr, 0);
     if (cs != GDN_OK) return cs;
 
     int32_t dvs = 0, wg = 0;
@@ -216,7 +225,7 @@ gdn_status gdn_prefill_fused(const void *q, const void *k, const void *v, const 
                              int32_t chunk_size, gdn_dtype io_dtype, uint32_t prologue, void *o,
                              float *final_state, void *stream) {
     const gdn_status cs = check_prefill(q, k, v, g, beta, initial_state, cu_seqlens, N, T_tot, Hk, Hv, Dk,
-                                        Dv, chunk_size, io_dtype, o, final_state, 1, nullptr, 0);
+                                        Dv, chunk_size, false, io_dtype, o, final_state, 1, nullptr, 0);
     if (cs != GDN_OK) return cs;
     if (prologue & ~kPrologueAll)
         return fail(GDN_ERR_INVALID_ARGUMENT, "prologue flags 0x%x include unknown bits", prologue);
@@ -256,7 +265,7 @@ gdn_status gdn_kda_prefill(const void *q, const void *k, const void *v, const fl
                            int32_t chunk_size, gdn_dtype io_dtype, void *workspace, size_t workspace_bytes,
                            void *o, float *final_state, void *stream) {
     const gdn_status cs = check_prefill(q, k, v, g, beta, initial_state, cu_seqlens, N, T_tot, Hk, Hv, Dk,
-                                        Dv, chunk_size, io_dtype, o, final_state, kD, workspace,
+                                        Dv, chunk_size, false, io_dtype, o, final_state, kD, workspace,
                                         workspace_bytes);
     if (cs != GDN_OK) return cs;
     if (io_dtype == GDN_F32)
@@ -281,7 +290,7 @@ gdn_status gdn_kda_prefill(const void *q, const void *k, const void *v, const fl
     const bool f16 = io_dtype == GDN_F16;
     (void)hipGetLastError();
     hipError_t e = T_tot > 0 ? gdn::launch_kda_map(a, f16, hs) : hipSuccess;
-    if (e == hipSuccess) e = gdn::launch_kda_chain(a, f16, hs);
+    if (e == hipSuccess) e = gdn::launch_kda_chain(a, f16, kChunk, hs);
     if (e != hipSuccess)
         return fail(GDN_ERR_DEVICE, "kda prefill launch failed: %s", hipGetErrorString(e));
     return ok();
@@ -292,9 +301,9 @@ gdn_status gdn_prefill_split_workspace_size(int32_t N, int32_t T_tot, int32_t Hv
     if (!bytes) return fail(GDN_ERR_INVALID_ARGUMENT, "bytes must be non-null");
     if (N < 1 || T_tot < 0 || Hv < 1)
         return fail(GDN_ERR_INVALID_ARGUMENT, "N=%d, T_tot=%d, Hv=%d out of range", N, T_tot, Hv);
-    if (chunk_size != kChunk)
-        return fail(GDN_ERR_UNSUPPORTED, "chunk_size=%d (only 64 is implemented)", chunk_size);
-    *bytes = kda_slots(N, T_tot) * (size_t)Hv * gdn::WS_TILE_BYTES;
+    if (!split_chunk_ok(chunk_size))
+        return fail(GDN_ERR_UNSUPPORTED, "chunk_size=%d (32, 64 or 128 are implemented)", chunk_size);
+    *bytes = kda_slots(N, T_tot, chunk_size) * (size_t)Hv * tile_bytes(chunk_size);
     return ok();
 }
 
@@ -304,7 +313,7 @@ gdn_status gdn_prefill_split(const void *q, const void *k, const void *v, const 
                              int32_t chunk_size, gdn_dtype io_dtype, void *workspace, size_t workspace_bytes,
                              void *o, float *final_state, void *stream) {
     const gdn_status cs = check_prefill(q, k, v, g, beta, initial_state, cu_seqlens, N, T_tot, Hk, Hv, Dk,
-                                        Dv, chunk_size, io_dtype, o, final_state, 1, workspace,
+                                        Dv, chunk_size, true, io_dtype, o, final_state, 1, workspace,
                                         workspace_bytes);
     if (cs != GDN_OK) return cs;
     if (io_dtype == GDN_F32)
@@ -315,7 +324,7 @@ gdn_status gdn_prefill_split(const void *q, const void *k, const void *v, const 
         return fail(GDN_ERR_INVALID_ARGUMENT, "workspace of %zu bytes is smaller than the %zu required",
                     workspace ? workspace_bytes : (size_t)0, need);
     if (!aligned(workspace, 256)) return fail(GDN_ERR_INVALID_ARGUMENT, "workspace is not 256-byte aligned");
-    if ((long long)kda_slots(N, T_tot) * Hv > 0x7fffffffLL || (long long)N * Hv * 8 > 0x7fffffffLL)
+    if ((long long)kda_slots(N, T_tot, chunk_size) * Hv > 0x7fffffffLL || (long long)N * Hv * 8 > 0x7fffffffLL)
         return fail(GDN_ERR_UNSUPPORTED, "too many chunks or heads for one launch");
     if (T_tot == 0 && !final_state) return ok();
 
@@ -324,12 +333,12 @@ gdn_status gdn_prefill_split(const void *q, const void *k, const void *v, const 
     a.s0 = initial_state; a.cu = cu_seqlens; a.o = o; a.sN = final_state;
     a.ws = static_cast<char *>(workspace);
     a.N = N; a.T_tot = T_tot; a.Hk = Hk; a.Hv = Hv;
-    a.nslots = (int32_t)kda_slots(N, T_tot);
+    a.nslots = (int32_t)kda_slots(N, T_tot, chunk_size);
     const hipStream_t hs = static_cast<hipStream_t>(stream);
     const bool f16 = io_dtype == GDN_F16;
     (void)hipGetLastError();
-    hipError_t e = T_tot > 0 ? gdn::launch_gdn_map(a, f16, hs) : hipSuccess;
-    if (e == hipSuccess) e = gdn::launch_kda_chain(a, f16, hs);
+    hipError_t e = T_tot > 0 ? gdn::launch_gdn_map(a, f16, chunk_size, hs) : hipSuccess;
+    if (e == hipSuccess) e = gdn::launch_kda_chain(a, f16, chunk_size, hs);
     if (e != hipSuccess)
         return fail(GDN_ERR_DEVICE, "split prefill launch failed: %s", hipGetErrorString(e));
     return ok();

@@ -44,34 +44,46 @@ struct KdaArgs {
     const int32_t *cu;      // [N+1] or null (single sequence)
     void *o;                // [T_tot, Hv, 128]
     float *sN;              // [N, Hv, 128, 128] or null
-    char *ws;               // nslots * Hv tiles of WS_TILE_BYTES
+    char *ws;               // nslots * Hv tiles of Tile<C>::BYTES
     int32_t N, T_tot, Hk, Hv;
-    int32_t nslots;
+    int32_t nslots;         // T_tot / C + N (chunk j of sequence n: slot cu[n] / C + n + j)
 };
-// Workspace tile of one chunk and value head (byte offsets; fp16 except gl; row-major),
-// with T = (I + A)^-1 and the decays of the chunk:
-//   P   = lower-incl-diagonal(Q K^T (.) decays)      [64 tokens][64 tokens]
-//   W   = T diag(beta) (K (.) exp(Gamma))             [64 tokens][128 key channels]
-//   Qg  = Q (.) exp(Gamma)                            [64 tokens][128 key channels]
-//   KlT = (K (.) exp(Gamma_last - Gamma))^T           [128 key channels][64 tokens]
-//   UT  = (T diag(beta) V)^T                          [128 value channels][64 tokens]
+// Workspace tile of one chunk of C tokens and one value head (byte offsets; fp16 except
+// gl; row-major), with T = (I + A)^-1 and the decays of the chunk:
+//   P   = lower-incl-diagonal(Q K^T (.) decays)      [C tokens][C tokens]
+//   W   = T diag(beta) (K (.) exp(Gamma))             [C tokens][128 key channels]
+//   Qg  = Q (.) exp(Gamma)                            [C tokens][128 key channels]
+//   KlT = (K (.) exp(Gamma_last - Gamma))^T           [128 key channels][C tokens]
+//   UT  = (T diag(beta) V)^T                          [128 value channels][C tokens]
 //   gl  = exp(Gamma_last)                             [128 key channels] fp32
 // Each is laid out so that one chain wave's MFMA fragments are 16-byte row segments.
-constexpr int WS_OFF_P = 0;
-constexpr int WS_OFF_W = 8192;
-constexpr int WS_OFF_QG = 24576;
-constexpr int WS_OFF_KLT = 40960;
-constexpr int WS_OFF_UT = 57344;
-constexpr int WS_OFF_GL = 73728;
-constexpr size_t WS_TILE_BYTES = 74240;
+template <int C> struct Tile {
+    static constexpr int P = 0;
+    static constexpr int W = C * C * 2;
+    static constexpr int QG = W + C * 256;
+    static constexpr int KLT = QG + C * 256;
+    static constexpr int UT = KLT + C * 256;
+    static constexpr int GL = UT + C * 256;
+    static constexpr size_t BYTES = (size_t)GL + 512;
+};
+static_assert(Tile<32>::BYTES % 256 == 0 && Tile<64>::BYTES % 256 == 0 && Tile<128>::BYTES % 256 == 0,
+              "tiles keep the workspace's 256-byte alignment");
+// The per-key-channel path runs 64-token chunks.
+constexpr int WS_OFF_P = Tile<64>::P;
+constexpr int WS_OFF_W = Tile<64>::W;
+constexpr int WS_OFF_QG = Tile<64>::QG;
+constexpr int WS_OFF_KLT = Tile<64>::KLT;
+constexpr int WS_OFF_UT = Tile<64>::UT;
+constexpr int WS_OFF_GL = Tile<64>::GL;
+constexpr size_t WS_TILE_BYTES = Tile<64>::BYTES;
 hipError_t launch_kda_map(const KdaArgs &a, bool f16, hipStream_t stream);
-hipError_t launch_kda_chain(const KdaArgs &a, bool f16, hipStream_t stream);
+// The chain over tiles of `chunk` tokens (32, 64 or 128).
+hipError_t launch_kda_chain(const KdaArgs &a, bool f16, int chunk, hipStream_t stream);
 int kda_map_lds_bytes();
 int kda_chain_lds_bytes();
 // The scalar-gate map (KdaArgs::g is [T_tot, Hv]) into the same workspace tiles, read by
 // launch_kda_chain.
-hipError_t launch_gdn_map(const KdaArgs &a, bool f16, hipStream_t stream);
-int gdn_map_lds_bytes();
+hipError_t launch_gdn_map(const KdaArgs &a, bool f16, int chunk, hipStream_t stream);
 // one token with a per-key-channel gate: DecodeArgs::g is [B, Hv, 128]
 hipError_t launch_kda_decode(const DecodeArgs &a, int io, hipStream_t stream);
 

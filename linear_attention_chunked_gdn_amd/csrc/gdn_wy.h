@@ -1,8 +1,8 @@
 // The WY products of the two-launch prefill's map kernels (gdn_map.hip, kda_map.hip):
-// with T = (I + A)^-1 of one chunk,
+// with T = (I + A)^-1 of one chunk of C tokens,
 //
-//   W = T diag(beta) Kg   (64 tokens x 128 key channels),
-//   U = T diag(beta) V    (64 tokens x 128 value channels),
+//   W = T diag(beta) Kg   (C tokens x 128 key channels),
+//   U = T diag(beta) V    (C tokens x 128 value channels),
 //
 // so that the chain only forms v = U - W S^T.  This is the solve applied to the two
 // right-hand sides that do not depend on the state (the W/U form of op #4, "Empowering
@@ -44,11 +44,12 @@ __device__ __forceinline__ Frag<_Float16> wy_frag_t(const _Float16 *x, int c0, i
 // [channel][token] (utout).  The products are taken transposed (operand^T T^T), so a lane
 // holds token 16I + l16 and four consecutive channels: one 8-byte store of W, four 2-byte
 // stores of U^T.
+template <int C>
 __device__ __forceinline__ void wy_products(const float *T, int as, const _Float16 *kg, const _Float16 *vb,
                                             char *wout, char *utout, int wave, int l16, int g4) {
     typedef _Float16 hf;
 #pragma unroll
-    for (int I = 0; I < 4; ++I) {
+    for (int I = 0; I < C / 16; ++I) {
         f32x4 acc[2][2];
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[j][0] = acc[j][1] = zero4();
@@ -81,7 +82,7 @@ __device__ __forceinline__ void wy_products(const float *T, int as, const _Float
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 w[i] = (hf)acc[j][0][i];
-                reinterpret_cast<hf *>(utout)[(c + i) * 64 + r] = (hf)acc[j][1][i];
+                reinterpret_cast<hf *>(utout)[(c + i) * C + r] = (hf)acc[j][1][i];
             }
             *reinterpret_cast<f16x4 *>(wout + (r * 128 + c) * 2) = w;
         }

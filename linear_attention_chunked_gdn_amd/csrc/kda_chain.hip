@@ -1,5 +1,5 @@
 // Chain half of the two-launch chunked prefill for gfx950 (per-key-channel decay, and the
-// scalar gate of gdn_prefill_split).
+// scalar gate of gdn_prefill_split), over chunks of C = 32, 64 or 128 tokens.
 //
 // The map kernels (kda_map.hip, gdn_map.hip) have left, per chunk and value head, the
 // products that do not depend on the state: with T = (I + A)^-1,
@@ -25,11 +25,14 @@
 //
 // Roles: waves 0-3 load the workspace tiles one chunk ahead and commit them to LDS, and
 // form the outputs, which nothing downstream in the chunk waits for; waves 4-7 run only
-// the recurrence.  A chunk takes two barrier-separated phases:
+// the recurrence.  Wave W (of either group) owns the 16-token tiles W and W + 4 of the
+// chunk (those that exist) for v, Q S^T and O, and key channels [32W, 32W + 32) for the
+// update.  A chunk takes two barrier-separated phases:
 //   phase 1: chain v(c)        | loaders: commit P, Kl, gl of c; Q S^T(c) from the state copy
 //   phase 2: chain S update    | loaders: commit W, Qg, U of c + 1; O(c) = Q S^T + P v
 // Each tile is committed after its last reader of the previous chunk and before its
-// first reader, so one LDS copy of every tile suffices.
+// first reader, so one LDS copy of every tile suffices.  LDS is 74 KB at C = 64 and
+// 154 KB at C = 128.
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
@@ -40,34 +43,52 @@ namespace kdachain {
 
 typedef _Float16 hf;
 
-constexpr int CH = 64;
 constexpr int DK = 128;
 constexpr int DV = 128;
 constexpr int DVS = 16;        // value channels per workgroup
 constexpr int THREADS = 512;   // 4 loader + 4 chain waves
 constexpr int KS = DK + 16;    // fp16 row stride of W, Qg and the state copy (288 B)
-constexpr int TS = CH + 16;    // fp16 row stride of v^T (160 B)
-constexpr int TP = CH + 8;     // fp16 row stride of P, Kl^T and U^T (144 B)
 
+template <int C>
+struct Cfg {
+    static constexpr int NT = C / 16;          // 16-token tiles
+    static constexpr int TPW = (NT + 3) / 4;   // tiles per wave (0 for waves 2, 3 at C = 32)
+    // (ownership tests are written so that the compiler drops them wherever every wave owns
+    // its tiles: a branch around the loaders' loads or stores makes the compiler's count of
+    // outstanding vector-memory operations conservative)
+    static constexpr int TS = C + 16;          // fp16 row stride of v^T
+    static constexpr int TP = C + 8;           // fp16 row stride of P, Kl^T and U^T
+    static constexpr int SEGS = C / 8;         // 16-byte segments per C-token row
+    static constexpr int KL_N = 128 * SEGS / 256;           // Kl^T segments per loader thread
+    static constexpr int P_SEGS = C * SEGS;                 // P segments (128 at C = 32)
+    static constexpr int P_N = (P_SEGS + 255) / 256;
+    static constexpr int W_N = C * 16 / 256;                // W, Qg segments per loader thread
+    static constexpr int U_SEGS = 16 * SEGS;                // the U^T slice's segments
+};
+
+template <int C>
 struct __align__(16) Smem {
+    using F = Cfg<C>;
     hf S[DVS * KS];            // fp16 copy of the state slice [value ch][key ch]
-    hf Vh[DVS * TS];           // v^T
-    hf U[DVS * TP];            // U^T slice [value ch][token]
+    hf Vh[DVS * F::TS];        // v^T
+    hf U[DVS * F::TP];         // U^T slice [value ch][token]
     float gl[DK];              // exp(Gamma_last) per key channel
-    hf P[CH * TP];
-    hf W[CH * KS];
-    hf Qg[CH * KS];
-    hf Kl[DK * TP];            // Kl^T [key ch][token]
+    hf P[C * F::TP];
+    hf W[C * KS];
+    hf Qg[C * KS];
+    hf Kl[DK * F::TP];         // Kl^T [key ch][token]
 };
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 // Loader registers: the tiles of one chunk between their load and their commit.
-struct StageA {       // P, Kl, gl: read in phase 2
-    u32x4 p[2], kl[4], gl;
+template <int C>
+struct StageA {       // P, Kl^T, gl: read in phase 2
+    u32x4 p[Cfg<C>::P_N], kl[Cfg<C>::KL_N], gl;
 };
-struct StageB {       // W, Qg, U: read in phase 1
-    u32x4 w[4], qg[4], u;
+template <int C>
+struct StageB {       // W, Qg, U^T: read in phase 1
+    u32x4 w[Cfg<C>::W_N], qg[Cfg<C>::W_N], u;
 };
 
 struct Work {
@@ -78,131 +99,174 @@ struct Work {
 
 __device__ __forceinline__ int chunk_clamp(const Work &wk, int c) { return min(c, wk.nchunks - 1); }
 
-// Loader thread ld (0..255).
-__device__ __forceinline__ void load_a(StageA &st, const Work &wk, int c, int ld) {
+// Loader thread ld (0..255).  Where a tile has fewer segments than threads, the rest read
+// its last segment again and do not commit.
+template <int C>
+__device__ __forceinline__ void load_a(StageA<C> &st, const Work &wk, int c, int ld) {
+    using F = Cfg<C>;
     const char *tile = wk.ws + (size_t)chunk_clamp(wk, c) * wk.slot_stride;
 #pragma unroll
-    for (int p = 0; p < 2; ++p)       // 64 rows x 8 segments of 16 B
-        st.p[p] = *reinterpret_cast<const u32x4 *>(tile + WS_OFF_P + (ld + 256 * p) * 16);
+    for (int p = 0; p < F::P_N; ++p)
+        st.p[p] = *reinterpret_cast<const u32x4 *>(
+            tile + Tile<C>::P + (F::P_SEGS % 256 != 0 ? min(ld + 256 * p, F::P_SEGS - 1) : ld + 256 * p) * 16);
 #pragma unroll
-    for (int p = 0; p < 4; ++p)       // 128 rows x 8 segments
-        st.kl[p] = *reinterpret_cast<const u32x4 *>(tile + WS_OFF_KLT + (ld + 256 * p) * 16);
-    st.gl = *reinterpret_cast<const u32x4 *>(tile + WS_OFF_GL + (ld & 31) * 16);
+    for (int p = 0; p < F::KL_N; ++p)
+        st.kl[p] = *reinterpret_cast<const u32x4 *>(tile + Tile<C>::KLT + (ld + 256 * p) * 16);
+    st.gl = *reinterpret_cast<const u32x4 *>(tile + Tile<C>::GL + (ld & 31) * 16);
 }
 
-__device__ __forceinline__ void commit_a(const StageA &st, Smem &s, int ld) {
+template <int C>
+__device__ __forceinline__ void commit_a(const StageA<C> &st, Smem<C> &s, int ld) {
+    using F = Cfg<C>;
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-        const int idx = ld + 256 * p, row = idx >> 3, seg = idx & 7;
-        *reinterpret_cast<u32x4 *>(&s.P[row * TP + seg * 8]) = st.p[p];
+    for (int p = 0; p < F::P_N; ++p) {
+        const int idx = ld + 256 * p, row = idx / F::SEGS, seg = idx % F::SEGS;
+        // a guard only where P has fewer segments than threads (C = 32): a branch here
+        // would make the compiler's count of outstanding loads conservative
+        if constexpr (F::P_SEGS % 256 != 0) {
+            if (idx < F::P_SEGS) *reinterpret_cast<u32x4 *>(&s.P[row * F::TP + seg * 8]) = st.p[p];
+        } else {
+            *reinterpret_cast<u32x4 *>(&s.P[row * F::TP + seg * 8]) = st.p[p];
+        }
     }
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        const int idx = ld + 256 * p, row = idx >> 3, seg = idx & 7;
-        *reinterpret_cast<u32x4 *>(&s.Kl[row * TP + seg * 8]) = st.kl[p];
+    for (int p = 0; p < F::KL_N; ++p) {
+        const int idx = ld + 256 * p, row = idx / F::SEGS, seg = idx % F::SEGS;
+        *reinterpret_cast<u32x4 *>(&s.Kl[row * F::TP + seg * 8]) = st.kl[p];
     }
     if (ld < 32) *reinterpret_cast<u32x4 *>(&s.gl[ld * 4]) = st.gl;
 }
 
-__device__ __forceinline__ void load_b(StageB &st, const Work &wk, int c, int ld) {
+template <int C>
+__device__ __forceinline__ void load_b(StageB<C> &st, const Work &wk, int c, int ld) {
+    using F = Cfg<C>;
     const char *tile = wk.ws + (size_t)chunk_clamp(wk, c) * wk.slot_stride;
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        st.w[p] = *reinterpret_cast<const u32x4 *>(tile + WS_OFF_W + (ld + 256 * p) * 16);
-        st.qg[p] = *reinterpret_cast<const u32x4 *>(tile + WS_OFF_QG + (ld + 256 * p) * 16);
+    for (int p = 0; p < F::W_N; ++p) {
+        st.w[p] = *reinterpret_cast<const u32x4 *>(tile + Tile<C>::W + (ld + 256 * p) * 16);
+        st.qg[p] = *reinterpret_cast<const u32x4 *>(tile + Tile<C>::QG + (ld + 256 * p) * 16);
     }
-    // U^T slice: 16 rows (value channels) x 8 segments of 8 tokens (threads 0-127; the rest
-    // repeat them)
-    const int ur = (ld & 127) >> 3, us = ld & 7;
-    st.u = *reinterpret_cast<const u32x4 *>(tile + WS_OFF_UT + ((wk.dv0 + ur) * CH + 8 * us) * 2);
+    // U^T slice: 16 rows (value channels dv0 ..) x C / 8 segments
+    const int ui = F::U_SEGS >= 256 ? ld : (ld & (F::U_SEGS - 1)), ur = ui / F::SEGS, us = ui % F::SEGS;
+    st.u = *reinterpret_cast<const u32x4 *>(tile + Tile<C>::UT + ((wk.dv0 + ur) * C + 8 * us) * 2);
 }
 
-__device__ __forceinline__ void commit_b(const StageB &st, Smem &s, int ld) {
+template <int C>
+__device__ __forceinline__ void commit_b(const StageB<C> &st, Smem<C> &s, int ld) {
+    using F = Cfg<C>;
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
+    for (int p = 0; p < F::W_N; ++p) {
         const int idx = ld + 256 * p, row = idx >> 4, seg = idx & 15;
         *reinterpret_cast<u32x4 *>(&s.W[row * KS + seg * 8]) = st.w[p];
         *reinterpret_cast<u32x4 *>(&s.Qg[row * KS + seg * 8]) = st.qg[p];
     }
-    if (ld < 128) *reinterpret_cast<u32x4 *>(&s.U[(ld >> 3) * TP + 8 * (ld & 7)]) = st.u;
+    if (ld < F::U_SEGS) *reinterpret_cast<u32x4 *>(&s.U[(ld / F::SEGS) * F::TP + 8 * (ld % F::SEGS)]) = st.u;
 }
 
-// Phase 1, chain wave W: v = U - W S^T for tokens [16W, 16W + 16) (lane = value channel,
-// rows = tokens), stored transposed.
-__device__ __forceinline__ void chain_v(Smem &s, int W, int l16, int g4) {
-    const hf *wrow = s.W + (16 * W + l16) * KS + 8 * g4;
+// Phase 1, chain wave W: v = U - W S^T for its token tiles (lane = value channel, rows =
+// tokens), stored transposed.
+template <int C>
+__device__ __forceinline__ void chain_v(Smem<C> &s, int W, int l16, int g4) {
+    using F = Cfg<C>;
     const hf *srow = s.S + l16 * KS + 8 * g4;
-    const int t0 = 16 * W + 4 * g4;
-    f32x4 ws = zero4();
+    Frag<hf> fs[4];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-        Frag<hf> fs, fw;
-        fs.load8(srow + 32 * kb);
-        fw.load8(wrow + 32 * kb);
-        mma(ws, fw, fs);
+    for (int k = 0; k < F::TPW; ++k) {
+        const int t = W + 4 * k;
+        if (F::NT >= 4 * (k + 1) || t < F::NT) {   // compile-time true unless C = 32
+            const hf *wrow = s.W + (16 * t + l16) * KS + 8 * g4;
+            f32x4 ws = zero4();
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                if (k == 0) fs[kb].load8(srow + 32 * kb);   // interleaved with the first tile's
+                Frag<hf> fw;
+                fw.load8(wrow + 32 * kb);
+                mma(ws, fw, fs[kb]);
+            }
+            const int t0 = 16 * t + 4 * g4;
+            const f16x4 u = *reinterpret_cast<const f16x4 *>(&s.U[l16 * F::TP + t0]);
+            f16x4 x;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x[i] = (hf)((float)u[i] - ws[i]);
+            *reinterpret_cast<f16x4 *>(&s.Vh[l16 * F::TS + t0]) = x;
+        }
     }
-    const f16x4 u = *reinterpret_cast<const f16x4 *>(&s.U[l16 * TP + t0]);
-    f16x4 x;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) x[i] = (hf)((float)u[i] - ws[i]);
-    *reinterpret_cast<f16x4 *>(&s.Vh[l16 * TS + t0]) = x;
 }
 
-// Phase 1, loader wave W (off the chain's critical path): (Q S^T)^T = S Qg^T for tokens
-// [16W, 16W + 16) (lane = token, rows = value channels 4G..4G+3), from the state copy,
-// which holds the chunk's starting state until phase 2.
-__device__ __forceinline__ f32x4 loader_QS(const Smem &s, int W, int l16, int g4) {
-    const hf *qrow = s.Qg + (16 * W + l16) * KS + 8 * g4;
+// Phase 1, loader wave W (off the chain's critical path): (Q S^T)^T = S Qg^T for its
+// token tiles (lane = token, rows = value channels 4G..4G+3), from the state copy, which
+// holds the chunk's starting state until phase 2.
+template <int C>
+__device__ __forceinline__ void loader_QS(const Smem<C> &s, int W, int l16, int g4, f32x4 (&qs)[Cfg<C>::TPW]) {
+    using F = Cfg<C>;
     const hf *srow = s.S + l16 * KS + 8 * g4;
-    f32x4 qs = zero4();
+    Frag<hf> fs[4];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-        Frag<hf> fs, fq;
-        fs.load8(srow + 32 * kb);
-        fq.load8(qrow + 32 * kb);
-        mma(qs, fs, fq);
+    for (int k = 0; k < F::TPW; ++k) {
+        const int t = W + 4 * k;
+        qs[k] = zero4();
+        if (F::NT >= 4 * (k + 1) || t < F::NT) {   // compile-time true unless C = 32
+            const hf *qrow = s.Qg + (16 * t + l16) * KS + 8 * g4;
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                if (k == 0) fs[kb].load8(srow + 32 * kb);
+                Frag<hf> fq;
+                fq.load8(qrow + 32 * kb);
+                mma(qs[k], fs[kb], fq);
+            }
+        }
     }
-    return qs;
 }
 
-// Phase 2, loader wave W: O^T = S Qg^T + v^T P^T for tokens [16W, 16W + 16), stored.
-template <typename IO>
-__device__ __forceinline__ void loader_O(const Smem &s, const KdaArgs &a, int W, int l16, int g4, const f32x4 &qs,
-                                         int h, int dv0, int tok0, int nval) {
-    f32x4 acc = qs;
-    const hf *ph = s.P + (16 * W + l16) * TP + 8 * g4;
+// Phase 2, loader wave W: O^T = S Qg^T + v^T P^T for its token tiles, stored.
+template <typename IO, int C>
+__device__ __forceinline__ void loader_O(const Smem<C> &s, const KdaArgs &a, int W, int l16, int g4,
+                                         const f32x4 (&qs)[Cfg<C>::TPW], int h, int dv0, int tok0, int nval) {
+    using F = Cfg<C>;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-        Frag<hf> fp, fv;
-        fp.load8(ph + 32 * kb);
-        fv.load8(s.Vh + l16 * TS + 32 * kb + 8 * g4);
-        mma(acc, fv, fp);   // P is zero above the diagonal (kb = 1 for W < 2)
-    }
-    const int t = 16 * W + l16;
-    if (t < nval) {
-        typename Vec4<IO>::type y;
+    for (int k = 0; k < F::TPW; ++k) {
+        const int t = W + 4 * k;
+        if (F::NT >= 4 * (k + 1) || t < F::NT) {   // compile-time true unless C = 32
+            f32x4 acc = qs[k];
+            const hf *ph = s.P + (16 * t + l16) * F::TP + 8 * g4;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) y[i] = Cvt<IO>::from_f32(acc[i]);
-        *reinterpret_cast<typename Vec4<IO>::type *>(reinterpret_cast<IO *>(a.o) +
-                                                     ((size_t)(tok0 + t) * a.Hv + h) * DV + dv0 + 4 * g4) = y;
+            for (int kb = 0; kb < (C >= 64 ? 2 : 1) + 2 * k; ++kb) {
+                // tokens 32kb ..: past the diagonal P is zero (tiles W < 2 at C = 64 take
+                // the zero block rather than a branch)
+                Frag<hf> fp, fv;
+                fp.load8(ph + 32 * kb);
+                fv.load8(s.Vh + l16 * F::TS + 32 * kb + 8 * g4);
+                mma(acc, fv, fp);
+            }
+            const int tok = 16 * t + l16;
+            if (tok < nval) {
+                typename Vec4<IO>::type y;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) y[i] = Cvt<IO>::from_f32(acc[i]);
+                *reinterpret_cast<typename Vec4<IO>::type *>(reinterpret_cast<IO *>(a.o) +
+                                                             ((size_t)(tok0 + tok) * a.Hv + h) * DV + dv0 + 4 * g4) = y;
+            }
+        }
     }
 }
 
 // Phase 2, chain wave W: the update of key channels [32W, 32W + 32) of the state slice:
 // S^T rows (key channels) 32W + 16mt + 4G + r, column = value channel.
-__device__ __forceinline__ void chain_update(Smem &s, int W, int l16, int g4, f32x4 (&st)[2]) {
-    Frag<hf> fv[2];   // v^T rows (value channel l16), tokens 32kb + 8g4 .. + 7
+template <int C>
+__device__ __forceinline__ void chain_update(Smem<C> &s, int W, int l16, int g4, f32x4 (&st)[2]) {
+    using F = Cfg<C>;
+    Frag<hf> fv[C / 32];   // v^T rows (value channel l16), tokens 32kb + 8g4 .. + 7
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) fv[kb].load8(s.Vh + l16 * TS + 32 * kb + 8 * g4);
+    for (int kb = 0; kb < C / 32; ++kb) fv[kb].load8(s.Vh + l16 * F::TS + 32 * kb + 8 * g4);
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
         // Kl^T rows 32W + 16mt + l16 (key channels), tokens 32kb + 8g4 .. + 7
-        const hf *kr = s.Kl + (32 * W + 16 * mt + l16) * TP + 8 * g4;
+        const hf *kr = s.Kl + (32 * W + 16 * mt + l16) * F::TP + 8 * g4;
         const int kc = 32 * W + 16 * mt + 4 * g4;
         const f32x4 gl = *reinterpret_cast<const f32x4 *>(&s.gl[kc]);
         f32x4 acc = st[mt] * gl;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < C / 32; ++kb) {
             Frag<hf> fk;
             fk.load8(kr + 32 * kb);
             mma(acc, fk, fv[kb]);
@@ -215,9 +279,10 @@ __device__ __forceinline__ void chain_update(Smem &s, int W, int l16, int g4, f3
     }
 }
 
-template <typename IO>
+template <typename IO, int C>
 __global__ __launch_bounds__(THREADS) void kda_chain_kernel(const KdaArgs a) {
-    __shared__ Smem s;
+    using F = Cfg<C>;
+    __shared__ Smem<C> s;
     const int tid = threadIdx.x;
     const int lane = tid & 63, l16 = lane & 15, g4 = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -237,9 +302,9 @@ __global__ __launch_bounds__(THREADS) void kda_chain_kernel(const KdaArgs a) {
     wk.bos = a.cu ? a.cu[n] : 0;
     wk.eos = a.cu ? a.cu[n + 1] : a.T_tot;
     const int len = wk.eos > wk.bos ? wk.eos - wk.bos : 0;
-    wk.nchunks = (len + CH - 1) / CH;
-    wk.slot_stride = (size_t)a.Hv * WS_TILE_BYTES;
-    wk.ws = a.ws + ((size_t)(wk.bos / CH + n) * a.Hv + h) * WS_TILE_BYTES;
+    wk.nchunks = (len + C - 1) / C;
+    wk.slot_stride = (size_t)a.Hv * Tile<C>::BYTES;
+    wk.ws = a.ws + ((size_t)(wk.bos / C + n) * a.Hv + h) * Tile<C>::BYTES;
 
     f32x4 st[2];
     const size_t sbase = ((size_t)n * a.Hv + h) * (size_t)DV * DK;
@@ -258,8 +323,8 @@ __global__ __launch_bounds__(THREADS) void kda_chain_kernel(const KdaArgs a) {
     }
 
     if (wk.nchunks > 0) {
-        StageA sa;
-        StageB sb;
+        StageA<C> sa;
+        StageB<C> sb;
         if (is_loader) {
             load_b(sb, wk, 0, tid);
             commit_b(sb, s, tid);
@@ -269,11 +334,12 @@ __global__ __launch_bounds__(THREADS) void kda_chain_kernel(const KdaArgs a) {
         __syncthreads();
         if (is_loader) {
             for (int c = 0; c < wk.nchunks; ++c) {
-                const int tok0 = wk.bos + c * CH;
-                const int nval = min(CH, wk.eos - tok0);
+                const int tok0 = wk.bos + c * C;
+                const int nval = min(C, wk.eos - tok0);
                 commit_a(sa, s, tid);
                 load_a(sa, wk, c + 1, tid);
-                const f32x4 qs = loader_QS(s, W, l16, g4);
+                f32x4 qs[F::TPW];
+                loader_QS(s, W, l16, g4, qs);
                 __syncthreads();
                 commit_b(sb, s, tid);
                 load_b(sb, wk, c + 2, tid);
@@ -301,15 +367,23 @@ __global__ __launch_bounds__(THREADS) void kda_chain_kernel(const KdaArgs a) {
 
 }  // namespace kdachain
 
-hipError_t launch_kda_chain(const KdaArgs &a, bool f16, hipStream_t stream) {
+hipError_t launch_kda_chain(const KdaArgs &a, bool f16, int chunk, hipStream_t stream) {
     const dim3 grid((unsigned)a.N * (unsigned)a.Hv * (kdachain::DV / kdachain::DVS)), block(kdachain::THREADS);
-    if (f16)
-        hipLaunchKernelGGL(kdachain::kda_chain_kernel<_Float16>, grid, block, 0, stream, a);
-    else
-        hipLaunchKernelGGL(kdachain::kda_chain_kernel<__bf16>, grid, block, 0, stream, a);
+#define KDA_CHAIN_LAUNCH(C)                                                                              \
+    do {                                                                                                 \
+        if (f16) hipLaunchKernelGGL((kdachain::kda_chain_kernel<_Float16, C>), grid, block, 0, stream, a); \
+        else hipLaunchKernelGGL((kdachain::kda_chain_kernel<__bf16, C>), grid, block, 0, stream, a);      \
+    } while (0)
+    switch (chunk) {
+        case 32: KDA_CHAIN_LAUNCH(32); break;
+        case 64: KDA_CHAIN_LAUNCH(64); break;
+        case 128: KDA_CHAIN_LAUNCH(128); break;
+        default: return hipErrorInvalidValue;
+    }
+#undef KDA_CHAIN_LAUNCH
     return hipGetLastError();
 }
 
-int kda_chain_lds_bytes() { return (int)sizeof(kdachain::Smem); }
+int kda_chain_lds_bytes() { return (int)sizeof(kdachain::Smem<64>); }
 
 }  // namespace gdn

@@ -451,7 +451,7 @@ __global__ __launch_bounds__(THREADS, 2) void kda_map_kernel(const KdaArgs a) {
         __syncthreads();
     }
     // #4 W = T diag(beta) Kg and U = T diag(beta) V to the workspace
-    wy_products(s.sv.T, AS, s.wy.Kb, s.wy.Vb, tile + WS_OFF_W, tile + WS_OFF_UT, wave, l16, g4);
+    wy_products<CH>(s.sv.T, AS, s.wy.Kb, s.wy.Vb, tile + WS_OFF_W, tile + WS_OFF_UT, wave, l16, g4);
 }
 
 }  // namespace kdamap

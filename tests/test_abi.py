@@ -120,6 +120,16 @@ def test_plan(lib):
         gdn.prefill_plan(1, 16, 3, lib=lib)
 
 
+@pytest.mark.parametrize("C", [32, 128])
+def test_split_workspace_size_other_chunks(lib, C):
+    # T_tot / C + N slots of C^2 * 2 + C * 1024 + 512 bytes
+    tile = C * C * 2 + C * 1024 + 512
+    assert gdn.prefill_split_workspace_size(1, 4096, 16, C, lib=lib) == (4096 // C + 1) * 16 * tile
+    assert gdn.prefill_split_workspace_size(3, 100, 2, C, lib=lib) == (100 // C + 3) * 2 * tile
+    with pytest.raises(gdn.GDNError):
+        gdn.kda_workspace_size(1, 10, 1, chunk_size=C, lib=lib)
+
+
 @pytest.mark.parametrize("size_fn", ["kda_workspace_size", "prefill_split_workspace_size"])
 def test_workspace_size(lib, size_fn):
     # one 74,240-byte tile per value head and chunk slot, T_tot / 64 + N slots
@@ -127,7 +137,7 @@ def test_workspace_size(lib, size_fn):
     assert f(1, 4096, 16, lib=lib) == (64 + 1) * 16 * 74240
     assert f(3, 100, 2, lib=lib) == (1 + 3) * 2 * 74240
     with pytest.raises(gdn.GDNError):
-        f(1, 10, 1, chunk_size=32, lib=lib)
+        f(1, 10, 1, chunk_size=48, lib=lib)
 
 
 def _ws_prefill(lib, fn, **over):
@@ -168,7 +178,9 @@ def test_kda_prefill_nothing_to_do_is_ok(lib):
 
 @pytest.mark.parametrize("over,status,msg", [
     (dict(io=0), 2, "bf16 or fp16"),
-    (dict(C=32), 2, "chunk_size"),
+    (dict(C=16), 2, "chunk_size"),
+    (dict(C=256), 2, "chunk_size"),
+    (dict(C=128, wsb=1 << 16), 1, "smaller than"),
     (dict(wsb=1000), 1, "smaller than"),
     (dict(ws=None), 1, "smaller than"),
     (dict(ws=0x1000080), 1, "256-byte aligned"),

@@ -29,10 +29,11 @@ def _args(d):
     return d["q"], d["k"], d["v"], d["g"], d["beta"], d["initial_state"], d["cu_seqlens"]
 
 
-def _check_all(x):
-    print(f"\n{x.name}: lengths={x.seq_lengths().tolist()[:10]} Hk={x.Hk} Hv={x.Hv} io={x.io}", flush=True)
+def _check_all(x, chunk=64):
+    print(f"\n{x.name}: lengths={x.seq_lengths().tolist()[:10]} Hk={x.Hk} Hv={x.Hv} io={x.io} chunk={chunk}",
+          flush=True)
     d = to_device(x, DEV)
-    o, fs = gdn.prefill_split(*_args(d))
+    o, fs = gdn.prefill_split(*_args(d), chunk_size=chunk)
     torch.cuda.synchronize()
     ro, rf = oracle.recurrent(x.q, x.k, x.v, x.g, x.beta, x.initial_state, x.cu_seqlens)
     check("o", to_f64(o), ro, x.io)
@@ -152,3 +153,29 @@ def test_split_in_a_hip_graph():
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(o, o_ref) and torch.equal(fs, f_ref), f"replay {i} differs"
+
+
+@pytest.mark.parametrize("chunk", [32, 128])
+@pytest.mark.parametrize("io", ["bf16", "f16"])
+@pytest.mark.parametrize("case", range(len(SMALL)))
+def test_split_other_chunk_sizes_small(chunk, io, case):
+    lengths, Hk, Hv, init_std = SMALL[case]
+    _check_all(inputs.make_custom(5700 + case, lengths, Hk, Hv, io=io, init_std=init_std,
+                                  g_shift=0.5 * (case % 3), name=f"split_c{chunk}_small{case}"), chunk)
+
+
+@pytest.mark.parametrize("chunk", [32, 128])
+def test_split_other_chunk_sizes_ragged_decay_and_workloads(chunk):
+    # lengths around the chunk boundaries of every size, strong decay, and the headline and
+    # varlen workloads; the three chunk sizes agree within twice the bar
+    _check_all(inputs.make_custom(5800, [31, 32, 33, 127, 128, 129, 255, 0, 1], 2, 4, io="bf16", init_std=0.2,
+                                  g_shift=1.0, name=f"split_c{chunk}_ragged"), chunk)
+    _check_all(inputs.make_custom(5801, [300, 5], 1, 2, io="bf16", g_shift=4.0, init_std=0.5,
+                                  name=f"split_c{chunk}_decay"), chunk)
+    for wid in (1, 3):
+        x = inputs.make_workload(wid)
+        d, o, fs = _check_all(x, chunk)
+        o64, f64 = gdn.prefill_split(*_args(d), chunk_size=64)
+        torch.cuda.synchronize()
+        check_pair(f"chunk {chunk} vs 64 o", to_f64(o), to_f64(o64), x.io)
+        check_pair(f"chunk {chunk} vs 64 state", to_f64(fs), to_f64(f64), x.io, stored=False)
