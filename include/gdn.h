@@ -160,7 +160,7 @@ gdn_status gdn_decode_step_fused(const void *q, const void *k, const void *v,
  * With every channel's g equal this is the gated delta rule above.
  *
  * gdn_kda_workspace_size -- device bytes gdn_kda_prefill needs as workspace for these
- * sizes: one 66,048-byte tile per value head and chunk slot, with T_tot / 64 + N slots
+ * sizes: one 74,240-byte tile per value head and chunk slot, with T_tot / 64 + N slots
  * (enough for any packing of N sequences into T_tot tokens).  Host pointer `bytes`.
  */
 gdn_status gdn_kda_workspace_size(int32_t N, int32_t T_tot, int32_t Hv, int32_t chunk_size,
@@ -184,8 +184,9 @@ gdn_status gdn_kda_workspace_size(int32_t N, int32_t T_tot, int32_t Hv, int32_t 
  *   workspace_bytes  its size in bytes
  *
  * Two kernels run in order on `stream`: one per (chunk, value head) that forms the
- * chunk's decay-weighted grams, (I + A)^-1 and decayed keys/queries into the workspace,
- * then the chunk-by-chunk state recurrence that reads them.
+ * chunk's decay-weighted grams, T = (I + A)^-1, the products W = T diag(beta) K_decayed
+ * and U = T diag(beta) V, and the decayed keys/queries into the workspace, then the
+ * chunk-by-chunk state recurrence that reads them.
  */
 gdn_status gdn_kda_prefill(const void *q, const void *k, const void *v,
                            const float *g, const float *beta,
