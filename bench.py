@@ -85,6 +85,8 @@ KERNEL_SOURCES = {
                                         "gdn_launch.h"],
     "gdn_map_kernel+kda_chain_kernel": ["gdn_map.hip", "kda_chain.hip", "gdn_wy.h", "gdn_device.h",
                                         "gdn_launch.h"],
+    "gdn_map_kernel+kda_chain_kernel+gdn_seg_fix_kernel": ["gdn_map.hip", "kda_chain.hip", "gdn_seg.hip",
+                                                           "gdn_wy.h", "gdn_device.h", "gdn_launch.h"],
 }
 
 
@@ -121,26 +123,32 @@ def _counter_median(path: str, counter: str, kernel_substr: str) -> float:
     return statistics.median(per_dispatch.values())
 
 
-def choose_path(x, path: str, prologue: bool) -> str:
-    """pipe (gdn_prefill) or split (gdn_prefill_split) for this workload: auto takes the split
-    path for 16-bit I/O without the prologue when the one-launch kernel's workgroups (one per
-    CU) would leave at least half of the 256 CUs idle."""
+def choose_path(x, path: str, prologue: bool, segments: int = 1) -> str:
+    """pipe (gdn_prefill), split (gdn_prefill_split) or seg (gdn_prefill_seg) for this
+    workload: auto takes the two-launch paths for 16-bit I/O without the prologue when the
+    one-launch kernel's workgroups (one per CU) would leave at least half of the 256 CUs
+    idle, and the segmented one among them when gdn_prefill_seg_choose gave more than one
+    segment."""
     if path != "auto":
         return path
-    return "split" if (x.io != "f32" and not prologue and x.N * x.Hv * 8 <= 128) else "pipe"
+    if x.io != "f32" and not prologue and x.N * x.Hv * 8 <= 128:
+        return "seg" if segments > 1 else "split"
+    return "pipe"
 
 
 def summarize_pmc(directory: str, workload: int, calib_mib: int, io=None, kda=False, prologue=False,
-                  path: str = "auto") -> dict:
+                  path: str = "auto", shard: int = 1) -> dict:
     """Scale the FETCH_SIZE / WRITE_SIZE counters (KiB per dispatch) of the prefill kernel by
     what the same counters read for a copy of known size; rocprofv3 runs of bench.py wrote
     fetch_, write_, copyfetch_ and copywrite_counter_collection.csv into `directory`.  With
     kda the step's two kernels are added (bytes per step); with prologue the counters are
     those of a `bench.py --prologue` run."""
     from linear_attention_chunked_gdn_amd import gdn, inputs
-    x = inputs.make_workload(workload, io=io, per_channel=kda, raw=prologue)
+    x = inputs.head_shard(inputs.make_workload(workload, io=io, per_channel=kda, raw=prologue), shard)
     if kda:
         kernel = "kda_map_kernel+kda_chain_kernel"
+    elif choose_path(x, path, prologue) == "seg":
+        kernel = "gdn_map_kernel+kda_chain_kernel+gdn_seg_fix_kernel"
     elif choose_path(x, path, prologue) == "split":
         kernel = "gdn_map_kernel+kda_chain_kernel"
     else:
@@ -325,11 +333,15 @@ def main() -> int:
     ap.add_argument("--workload", type=int, default=1)
     ap.add_argument("--io", choices=sorted(IO_CODE), default=None,
                     help="storage type of q, k, v, o (default: the workload's own)")
-    ap.add_argument("--path", choices=["auto", "pipe", "split"], default="auto",
+    ap.add_argument("--path", choices=["auto", "pipe", "split", "seg"], default="auto",
                     help="scalar-gate prefill entry point: gdn_prefill (pipe), gdn_prefill_split, "
-                         "or by shape (auto)")
+                         "gdn_prefill_seg, or by shape (auto)")
     ap.add_argument("--chunk", type=int, choices=[32, 64, 128], default=64,
-                    help="chunk length of the split path (gdn_prefill_split)")
+                    help="chunk length of the two-launch paths (gdn_prefill_split, gdn_prefill_seg)")
+    ap.add_argument("--segments", type=int, default=0,
+                    help="segments per sequence of gdn_prefill_seg (0: gdn_prefill_seg_choose's count)")
+    ap.add_argument("--head-shard", type=int, default=1, metavar="G",
+                    help="run one GPU's share of the workload's heads when they are split over G GPUs")
     ap.add_argument("--kda", action="store_true",
                     help="one decay per key channel (gdn_kda_prefill) on the same workload")
     ap.add_argument("--prologue", action="store_true",
@@ -350,7 +362,7 @@ def main() -> int:
         return 2
     if args.summarize_pmc:
         entry = summarize_pmc(args.summarize_pmc, args.workload, args.calibrate_copy or 256, args.io, args.kda,
-                              args.prologue, args.path)
+                              args.prologue, args.path, args.head_shard)
         try:
             with open(TRAFFIC_FILE) as f:
                 table = json.load(f)
@@ -374,7 +386,8 @@ def main() -> int:
     if args.prologue and args.kda:
         print("bench.py: --prologue applies to the scalar-gate prefill only", file=sys.stderr)
         return 2
-    x = inputs.make_workload(args.workload, io=args.io, per_channel=args.kda, raw=args.prologue)
+    x = inputs.head_shard(inputs.make_workload(args.workload, io=args.io, per_channel=args.kda,
+                                               raw=args.prologue), args.head_shard)
     pro = gdn.PROLOGUE_ALL if args.prologue else 0
     io = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[x.io]
 
@@ -390,15 +403,17 @@ def main() -> int:
                          o=torch.empty((x.T_tot, x.Hv, x.Dv), dtype=io, device=dev),
                          fs=torch.empty((x.N, x.Hv, x.Dv, x.Dk), dtype=torch.float32, device=dev)))
 
-    path = "kda" if args.kda else choose_path(x, args.path, args.prologue)
-    if path == "split" and (x.io == "f32" or pro):
-        print("bench.py: --path split takes bf16 or fp16 I/O without the prologue", file=sys.stderr)
+    segments = args.segments or gdn.prefill_seg_choose(x.N, x.T_tot, x.Hv, args.chunk)
+    path = "kda" if args.kda else choose_path(x, args.path, args.prologue, segments)
+    if path in ("split", "seg") and (x.io == "f32" or pro):
+        print(f"bench.py: --path {path} takes bf16 or fp16 I/O without the prologue", file=sys.stderr)
         return 2
-    chunk = args.chunk if path == "split" else 64
-    if args.chunk != 64 and path != "split":
-        print("bench.py: --chunk applies to the split path only", file=sys.stderr)
+    chunk = args.chunk if path in ("split", "seg") else 64
+    if args.chunk != 64 and path not in ("split", "seg"):
+        print("bench.py: --chunk applies to the two-launch paths only", file=sys.stderr)
         return 2
-    ws_bytes = {"kda": gdn.kda_workspace_size, "split": gdn.prefill_split_workspace_size}
+    ws_bytes = {"kda": gdn.kda_workspace_size, "split": gdn.prefill_split_workspace_size,
+                "seg": lambda N, T, Hv, C: gdn.prefill_seg_workspace_size(N, T, Hv, C, segments)}
     ws = (torch.empty(ws_bytes[path](x.N, x.T_tot, x.Hv, chunk), dtype=torch.uint8, device=dev)
           if path in ws_bytes else None)
 
@@ -410,6 +425,9 @@ def main() -> int:
         elif path == "split":
             gdn.prefill_split(s["q"], s["k"], s["v"], s["g"], s["beta"], s["init"], s["cu"], chunk_size=chunk,
                               out=s["o"], final_state=s["fs"], workspace=ws)
+        elif path == "seg":
+            gdn.prefill_seg(s["q"], s["k"], s["v"], s["g"], s["beta"], s["init"], s["cu"], chunk_size=chunk,
+                            segments=segments, out=s["o"], final_state=s["fs"], workspace=ws)
         else:
             gdn.prefill(s["q"], s["k"], s["v"], s["g"], s["beta"], s["init"], s["cu"],
                         out=s["o"], final_state=s["fs"], prologue=pro)
@@ -454,11 +472,15 @@ def main() -> int:
     nbytes = algorithmic_bytes(x)
     flops = algorithmic_flops(x, chunk)
     sec = ms_per_step / 1e3
-    if path in ("kda", "split"):
+    if path in ("kda", "split", "seg"):
         kernel = ("kda_map_kernel" if path == "kda" else "gdn_map_kernel") + "+kda_chain_kernel"
-        launch = {"path": path, "kernel": kernel, "map_workgroups": (x.T_tot // 64 + x.N) * x.Hv,
-                  "chain_workgroups": x.N * x.Hv * 8, "workspace_bytes": int(ws.numel()),
+        nseg = segments if path == "seg" else 1
+        launch = {"path": path, "kernel": kernel, "map_workgroups": (x.T_tot // chunk + x.N) * x.Hv,
+                  "chain_workgroups": x.N * x.Hv * 8 * (2 * nseg - 1), "workspace_bytes": int(ws.numel()),
                   "input_copies_rotated": copies}
+        if path == "seg":
+            kernel += "+gdn_seg_fix_kernel"
+            launch.update(kernel=kernel, segments=nseg, fix_workgroups=(x.T_tot // chunk + 2 * x.N) * x.Hv * 8)
     else:
         plan = gdn.prefill_plan(x.N, x.Hv, IO_CODE[x.io])
         kernel = "gdn_prefill_pipe_kernel" if plan["threads_per_workgroup"] == 512 else "gdn_prefill_kernel"
@@ -482,7 +504,7 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": x.io,
         "data": "synthetic",
-        "config": {"workload": x.name, "sequences": x.N, "tokens": x.T_tot, "Hk": x.Hk, "Hv": x.Hv,
+        "config": {"workload": x.name, "head_shard_of_gpus": args.head_shard, "sequences": x.N, "tokens": x.T_tot, "Hk": x.Hk, "Hv": x.Hv,
                    "d": x.Dk, "chunk": chunk, "io": x.io, "state": "fp32",
                    "initial_state": x.initial_state is not None},
         "roofline": {"bound": "hbm", "achieved": nbytes / sec / 1e9, "peak": HBM_PEAK_GBS,

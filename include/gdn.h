@@ -244,6 +244,47 @@ gdn_status gdn_prefill_split(const void *q, const void *k, const void *v,
                              void *o, float *final_state, void *stream);
 
 /*
+ * gdn_prefill_seg -- gdn_prefill_split with each sequence's state recurrence split into
+ * `segments` runs of whole chunks that execute at the same time: the Chunk-Seg-Seg
+ * mapping ("Empowering Hybrid Attention Models on NPUs", section 4, Figure 7), in which
+ * extra pre-computation lets the Reduce run over segments concurrently.  The chunk state
+ * map is affine (S -> S M + B), so each later segment runs twice side by side, from a zero
+ * state and from the identity, and a third launch joins them: the start state of segment
+ * s + 1 is S_in(s) X_s + S0(s), with X_s the segment's product of M, and its outputs gain
+ * E S_in(s)^T.  Same results as gdn_prefill_split up to rounding (bit-identical with
+ * segments = 1); the faster one when few (sequence, head) pairs leave compute units idle
+ * during the recurrence, since the serial chain shortens by the factor `segments` at
+ * 2 segments - 1 times the recurrence's workgroups.  Arguments as for gdn_prefill_split,
+ * plus:
+ *
+ *   segments       1 .. 256 segments per sequence (chunks [s nc / segments,
+ *                  (s + 1) nc / segments) of a sequence of nc chunks form segment s; a
+ *                  segment may be empty)
+ *   workspace      at least gdn_prefill_seg_workspace_size(...) bytes, with the same
+ *                  rules as gdn_prefill_split's
+ *
+ * gdn_prefill_seg_workspace_size -- gdn_prefill_split_workspace_size plus two fp32
+ * [T_tot, Hv, Dv] output buffers and N * Hv * segments * 2 fp32 Dk x Dk states.
+ *
+ * gdn_prefill_seg_choose -- a segment count for these sizes on the current device: the
+ * largest with one recurrence workgroup per compute unit, N * Hv * 8 * (2 segments - 1)
+ * <= compute units, and at least 4 chunks per segment on average; 1 means "use
+ * gdn_prefill_split".  Reads the device's compute-unit count (GDN_ERR_DEVICE if that
+ * fails).  Host pointer `segments`.
+ */
+gdn_status gdn_prefill_seg_workspace_size(int32_t N, int32_t T_tot, int32_t Hv,
+                                          int32_t chunk_size, int32_t segments, size_t *bytes);
+gdn_status gdn_prefill_seg_choose(int32_t N, int32_t T_tot, int32_t Hv, int32_t chunk_size,
+                                  int32_t *segments);
+gdn_status gdn_prefill_seg(const void *q, const void *k, const void *v,
+                           const float *g, const float *beta,
+                           const float *initial_state, const int32_t *cu_seqlens,
+                           int32_t N, int32_t T_tot, int32_t Hk, int32_t Hv,
+                           int32_t Dk, int32_t Dv, int32_t chunk_size, int32_t segments,
+                           gdn_dtype io_dtype, void *workspace, size_t workspace_bytes,
+                           void *o, float *final_state, void *stream);
+
+/*
  * gdn_prefill_plan -- the launch shape gdn_prefill would use for these sizes,
  * without launching anything: the width of the value-channel slice each workgroup
  * owns (the column-wise split of S, "Empowering Hybrid Attention Models on NPUs",

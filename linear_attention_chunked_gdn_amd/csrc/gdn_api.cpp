@@ -7,6 +7,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -280,7 +281,7 @@ gdn_status gdn_kda_prefill(const void *q, const void *k, const void *v, const fl
         return fail(GDN_ERR_UNSUPPORTED, "too many chunks or heads for one launch");
     if (T_tot == 0 && !final_state) return ok();
 
-    gdn::KdaArgs a;
+    gdn::KdaArgs a{};
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
     a.s0 = initial_state; a.cu = cu_seqlens; a.o = o; a.sN = final_state;
     a.ws = static_cast<char *>(workspace);
@@ -328,7 +329,7 @@ gdn_status gdn_prefill_split(const void *q, const void *k, const void *v, const 
         return fail(GDN_ERR_UNSUPPORTED, "too many chunks or heads for one launch");
     if (T_tot == 0 && !final_state) return ok();
 
-    gdn::KdaArgs a;
+    gdn::KdaArgs a{};
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
     a.s0 = initial_state; a.cu = cu_seqlens; a.o = o; a.sN = final_state;
     a.ws = static_cast<char *>(workspace);
@@ -341,6 +342,96 @@ gdn_status gdn_prefill_split(const void *q, const void *k, const void *v, const 
     if (e == hipSuccess) e = gdn::launch_kda_chain(a, f16, chunk_size, hs);
     if (e != hipSuccess)
         return fail(GDN_ERR_DEVICE, "split prefill launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+// Segmented prefill: the split path's map, the chain in segments, the fix-up.
+constexpr int32_t kMaxSegments = 256;
+
+gdn_status gdn_prefill_seg_workspace_size(int32_t N, int32_t T_tot, int32_t Hv, int32_t chunk_size,
+                                          int32_t segments, size_t *bytes) {
+    if (segments < 1 || segments > kMaxSegments)
+        return fail(GDN_ERR_INVALID_ARGUMENT, "segments=%d is outside 1..%d", segments, kMaxSegments);
+    size_t tiles = 0;
+    const gdn_status st = gdn_prefill_split_workspace_size(N, T_tot, Hv, chunk_size, &tiles);
+    if (st != GDN_OK) return st;
+    const size_t per_token = (size_t)Hv * kD * sizeof(float);        // o0 and e rows
+    const size_t states = (size_t)N * Hv * segments * 2 * kD * kD * sizeof(float);
+    *bytes = tiles + 2 * (size_t)T_tot * per_token + states;
+    return ok();
+}
+
+gdn_status gdn_prefill_seg_choose(int32_t N, int32_t T_tot, int32_t Hv, int32_t chunk_size,
+                                  int32_t *segments) {
+    if (!segments) return fail(GDN_ERR_INVALID_ARGUMENT, "segments must be non-null");
+    if (N < 1 || T_tot < 0 || Hv < 1)
+        return fail(GDN_ERR_INVALID_ARGUMENT, "N=%d, T_tot=%d, Hv=%d out of range", N, T_tot, Hv);
+    if (!split_chunk_ok(chunk_size))
+        return fail(GDN_ERR_UNSUPPORTED, "chunk_size=%d (32, 64 or 128 are implemented)", chunk_size);
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+        return fail(GDN_ERR_DEVICE, "cannot read the current device's compute-unit count");
+    // one chain workgroup per compute unit: 8 (2K - 1) per (sequence, head) for K segments
+    const long long pairs = (long long)N * Hv;
+    long long k = ((long long)cus / (8 * pairs) + 1) / 2;
+    // and at least 4 chunks per segment on average
+    const long long chunks = (long long)T_tot / chunk_size / N;
+    k = std::min(k, std::max(1LL, chunks / 4));
+    *segments = (int32_t)std::max(1LL, std::min<long long>(k, kMaxSegments));
+    return ok();
+}
+
+gdn_status gdn_prefill_seg(const void *q, const void *k, const void *v, const float *g,
+                           const float *beta, const float *initial_state, const int32_t *cu_seqlens,
+                           int32_t N, int32_t T_tot, int32_t Hk, int32_t Hv, int32_t Dk, int32_t Dv,
+                           int32_t chunk_size, int32_t segments, gdn_dtype io_dtype, void *workspace,
+                           size_t workspace_bytes, void *o, float *final_state, void *stream) {
+    const gdn_status cs = check_prefill(q, k, v, g, beta, initial_state, cu_seqlens, N, T_tot, Hk, Hv, Dk,
+                                        Dv, chunk_size, true, io_dtype, o, final_state, 1, workspace,
+                                        workspace_bytes);
+    if (cs != GDN_OK) return cs;
+    if (io_dtype == GDN_F32)
+        return fail(GDN_ERR_UNSUPPORTED, "gdn_prefill_seg takes bf16 or fp16 q, k, v, o");
+    size_t need = 0;
+    const gdn_status ws_st = gdn_prefill_seg_workspace_size(N, T_tot, Hv, chunk_size, segments, &need);
+    if (ws_st != GDN_OK) return ws_st;
+    if (T_tot > 0 && (!workspace || workspace_bytes < need))
+        return fail(GDN_ERR_INVALID_ARGUMENT, "workspace of %zu bytes is smaller than the %zu required",
+                    workspace ? workspace_bytes : (size_t)0, need);
+    if (!aligned(workspace, 256)) return fail(GDN_ERR_INVALID_ARGUMENT, "workspace is not 256-byte aligned");
+    const long long slots = (long long)kda_slots(N, T_tot, chunk_size);
+    if ((slots + N) * Hv * 8 > 0x7fffffffLL || (long long)N * Hv * 8 * (2 * segments - 1) > 0x7fffffffLL)
+        return fail(GDN_ERR_UNSUPPORTED, "too many chunks, heads or segments for one launch");
+    if (T_tot == 0 && !final_state) return ok();
+
+    gdn::KdaArgs a{};
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
+    a.s0 = initial_state; a.cu = cu_seqlens; a.o = o; a.sN = final_state;
+    a.ws = static_cast<char *>(workspace);
+    a.N = N; a.T_tot = T_tot; a.Hk = Hk; a.Hv = Hv;
+    a.nslots = (int32_t)slots;
+    a.nseg = segments;
+    const hipStream_t hs = static_cast<hipStream_t>(stream);
+    const bool f16 = io_dtype == GDN_F16;
+    (void)hipGetLastError();
+    hipError_t e;
+    if (T_tot == 0) {
+        // no tokens: the final state is the initial state (the plain chain copies it)
+        e = gdn::launch_kda_chain(a, f16, chunk_size, hs);
+    } else {
+        size_t off = (size_t)slots * Hv * tile_bytes(chunk_size);
+        a.o0 = reinterpret_cast<float *>(a.ws + off);
+        off += (size_t)T_tot * Hv * kD * sizeof(float);
+        a.e = reinterpret_cast<float *>(a.ws + off);
+        off += (size_t)T_tot * Hv * kD * sizeof(float);
+        a.sseg = reinterpret_cast<float *>(a.ws + off);
+        e = gdn::launch_gdn_map(a, f16, chunk_size, hs);
+        if (e == hipSuccess) e = gdn::launch_seg_chain(a, f16, chunk_size, hs);
+        if (e == hipSuccess) e = gdn::launch_seg_fix(a, f16, chunk_size, hs);
+    }
+    if (e != hipSuccess)
+        return fail(GDN_ERR_DEVICE, "segmented prefill launch failed: %s", hipGetErrorString(e));
     return ok();
 }
 

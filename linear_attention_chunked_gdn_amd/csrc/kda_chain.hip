@@ -163,10 +163,10 @@ __device__ __forceinline__ void commit_b(const StageB<C> &st, Smem<C> &s, int ld
     if (ld < F::U_SEGS) *reinterpret_cast<u32x4 *>(&s.U[(ld / F::SEGS) * F::TP + 8 * (ld % F::SEGS)]) = st.u;
 }
 
-// Phase 1, chain wave W: v = U - W S^T for its token tiles (lane = value channel, rows =
-// tokens), stored transposed.
+// Phase 1, chain wave W: v = ukeep U - W S^T for its token tiles (lane = value channel, rows
+// = tokens), stored transposed.  ukeep is 1, or 0 for the identity rows of a segment.
 template <int C>
-__device__ __forceinline__ void chain_v(Smem<C> &s, int W, int l16, int g4) {
+__device__ __forceinline__ void chain_v(Smem<C> &s, int W, int l16, int g4, float ukeep) {
     using F = Cfg<C>;
     const hf *srow = s.S + l16 * KS + 8 * g4;
     Frag<hf> fs[4];
@@ -187,7 +187,7 @@ __device__ __forceinline__ void chain_v(Smem<C> &s, int W, int l16, int g4) {
             const f16x4 u = *reinterpret_cast<const f16x4 *>(&s.U[l16 * F::TP + t0]);
             f16x4 x;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) x[i] = (hf)((float)u[i] - ws[i]);
+            for (int i = 0; i < 4; ++i) x[i] = (hf)(ukeep * (float)u[i] - ws[i]);
             *reinterpret_cast<f16x4 *>(&s.Vh[l16 * F::TS + t0]) = x;
         }
     }
@@ -218,10 +218,12 @@ __device__ __forceinline__ void loader_QS(const Smem<C> &s, int W, int l16, int 
     }
 }
 
-// Phase 2, loader wave W: O^T = S Qg^T + v^T P^T for its token tiles, stored.
-template <typename IO, int C>
+// Phase 2, loader wave W: O^T = S Qg^T + v^T P^T for its token tiles, stored (as IO to o;
+// in the segment mode as fp32 to obase, of the same [token][head][channel] shape).
+template <typename IO, int C, bool SEG>
 __device__ __forceinline__ void loader_O(const Smem<C> &s, const KdaArgs &a, int W, int l16, int g4,
-                                         const f32x4 (&qs)[Cfg<C>::TPW], int h, int dv0, int tok0, int nval) {
+                                         const f32x4 (&qs)[Cfg<C>::TPW], int h, int dv0, int tok0, int nval,
+                                         float *obase) {
     using F = Cfg<C>;
 #pragma unroll
     for (int k = 0; k < F::TPW; ++k) {
@@ -239,7 +241,10 @@ __device__ __forceinline__ void loader_O(const Smem<C> &s, const KdaArgs &a, int
                 mma(acc, fv, fp);
             }
             const int tok = 16 * t + l16;
-            if (tok < nval) {
+            if constexpr (SEG) {
+                if (tok < nval)
+                    *reinterpret_cast<f32x4 *>(obase + ((size_t)(tok0 + tok) * a.Hv + h) * DV + dv0 + 4 * g4) = acc;
+            } else if (tok < nval) {
                 typename Vec4<IO>::type y;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) y[i] = Cvt<IO>::from_f32(acc[i]);
@@ -279,7 +284,14 @@ __device__ __forceinline__ void chain_update(Smem<C> &s, int W, int l16, int g4,
     }
 }
 
-template <typename IO, int C>
+// SEG: the segment mode of the Chunk-Seg-Seg mapping ("Empowering Hybrid Attention Models on
+// NPUs", section 4, Figure 7): each sequence's chunks split into a.nseg runs.  Per
+// (sequence, head), segment 0 has the 8 value slices, from the initial state; every later
+// segment has 8 value slices from a zero state and 8 slices of identity rows (state X = I
+// and no U term), whose outputs E and end state X carry the segment's dependence on its
+// real start state.  Outputs go as fp32 to a.o0 (value rows) or a.e (identity rows), end
+// states to a.sseg (X transposed); gdn_seg.hip joins them.
+template <typename IO, int C, bool SEG>
 __global__ __launch_bounds__(THREADS) void kda_chain_kernel(const KdaArgs a) {
     using F = Cfg<C>;
     __shared__ Smem<C> s;
@@ -293,18 +305,41 @@ __global__ __launch_bounds__(THREADS) void kda_chain_kernel(const KdaArgs a) {
     const int G = gridDim.x;
     int item = blockIdx.x;
     if ((G & 7) == 0) item = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
-    const int slice = item % NSL;
-    const int h = (item / NSL) % a.Hv;
-    const int n = item / (NSL * a.Hv);
+    int slice, h, n, seg = 0;
+    bool ident = false;
+    if constexpr (SEG) {
+        const int per = NSL * (2 * a.nseg - 1);   // workgroups per (sequence, head)
+        const int i = item % per;
+        h = (item / per) % a.Hv;
+        n = item / (per * a.Hv);
+        if (i < NSL) {
+            slice = i;
+        } else {
+            seg = 1 + (i - NSL) / (2 * NSL);
+            ident = (i - NSL) % (2 * NSL) >= NSL;
+            slice = (i - NSL) % NSL;
+        }
+    } else {
+        slice = item % NSL;
+        h = (item / NSL) % a.Hv;
+        n = item / (NSL * a.Hv);
+    }
     Work wk;
     wk.h = h;
     wk.dv0 = slice * DVS;
-    wk.bos = a.cu ? a.cu[n] : 0;
-    wk.eos = a.cu ? a.cu[n + 1] : a.T_tot;
-    const int len = wk.eos > wk.bos ? wk.eos - wk.bos : 0;
-    wk.nchunks = (len + C - 1) / C;
+    const int bos = a.cu ? a.cu[n] : 0, eos = a.cu ? a.cu[n + 1] : a.T_tot;
+    const int len = eos > bos ? eos - bos : 0;
+    const int nc = (len + C - 1) / C;
+    // segment `seg`: chunks [seg nc / nseg, (seg + 1) nc / nseg) of the sequence
+    const int c0 = SEG ? (int)((long long)seg * nc / a.nseg) : 0;
+    const int c1 = SEG ? (int)((long long)(seg + 1) * nc / a.nseg) : nc;
+    wk.bos = bos + c0 * C;
+    wk.eos = SEG ? min(eos, bos + c1 * C) : eos;
+    wk.nchunks = c1 - c0;
     wk.slot_stride = (size_t)a.Hv * Tile<C>::BYTES;
-    wk.ws = a.ws + ((size_t)(wk.bos / C + n) * a.Hv + h) * Tile<C>::BYTES;
+    wk.ws = a.ws + ((size_t)(bos / C + n + c0) * a.Hv + h) * Tile<C>::BYTES;
+    float *const obase = ident ? a.e : a.o0;
+    const float ukeep = ident ? 0.f : 1.f;
 
     f32x4 st[2];
     const size_t sbase = ((size_t)n * a.Hv + h) * (size_t)DV * DK;
@@ -313,7 +348,11 @@ __global__ __launch_bounds__(THREADS) void kda_chain_kernel(const KdaArgs a) {
         for (int mt = 0; mt < 2; ++mt) {
             const int dk = 32 * W + 16 * mt + 4 * g4;
             f32x4 x = zero4();
-            if (a.s0) x = *reinterpret_cast<const f32x4 *>(a.s0 + sbase + (size_t)(wk.dv0 + l16) * DK + dk);
+            if (seg == 0 && a.s0) x = *reinterpret_cast<const f32x4 *>(a.s0 + sbase + (size_t)(wk.dv0 + l16) * DK + dk);
+            if (ident) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) x[i] = dk + i == wk.dv0 + l16 ? 1.f : 0.f;
+            }
             st[mt] = x;
             f16x4 y;
 #pragma unroll
@@ -343,12 +382,12 @@ __global__ __launch_bounds__(THREADS) void kda_chain_kernel(const KdaArgs a) {
                 __syncthreads();
                 commit_b(sb, s, tid);
                 load_b(sb, wk, c + 2, tid);
-                loader_O<IO>(s, a, W, l16, g4, qs, h, wk.dv0, tok0, nval);
+                loader_O<IO, C, SEG>(s, a, W, l16, g4, qs, h, wk.dv0, tok0, nval, obase);
                 __syncthreads();
             }
         } else {
             for (int c = 0; c < wk.nchunks; ++c) {
-                chain_v(s, W, l16, g4);
+                chain_v(s, W, l16, g4, SEG ? ukeep : 1.f);
                 __syncthreads();
                 chain_update(s, W, l16, g4, st);
                 __syncthreads();
@@ -356,7 +395,21 @@ __global__ __launch_bounds__(THREADS) void kda_chain_kernel(const KdaArgs a) {
         }
     }
 
-    if (a.sN && !is_loader) {
+    if constexpr (SEG) {
+        if (!is_loader) {
+            float *sb = a.sseg + ((((size_t)n * a.Hv + h) * a.nseg + seg) * 2 + (ident ? 1 : 0)) * DV * DK;
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) {
+                const int dk = 32 * W + 16 * mt + 4 * g4, r = wk.dv0 + l16;
+                if (ident) {   // X^T [key][row]
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) sb[(size_t)(dk + i) * DV + r] = st[mt][i];
+                } else {
+                    *reinterpret_cast<f32x4 *>(sb + (size_t)r * DK + dk) = st[mt];
+                }
+            }
+        }
+    } else if (a.sN && !is_loader) {
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
             const int dk = 32 * W + 16 * mt + 4 * g4;
@@ -367,12 +420,17 @@ __global__ __launch_bounds__(THREADS) void kda_chain_kernel(const KdaArgs a) {
 
 }  // namespace kdachain
 
-hipError_t launch_kda_chain(const KdaArgs &a, bool f16, int chunk, hipStream_t stream) {
-    const dim3 grid((unsigned)a.N * (unsigned)a.Hv * (kdachain::DV / kdachain::DVS)), block(kdachain::THREADS);
-#define KDA_CHAIN_LAUNCH(C)                                                                              \
-    do {                                                                                                 \
-        if (f16) hipLaunchKernelGGL((kdachain::kda_chain_kernel<_Float16, C>), grid, block, 0, stream, a); \
-        else hipLaunchKernelGGL((kdachain::kda_chain_kernel<__bf16, C>), grid, block, 0, stream, a);      \
+namespace {
+
+template <bool SEG>
+hipError_t chain_launch(const KdaArgs &a, bool f16, int chunk, hipStream_t stream) {
+    constexpr unsigned NSL = kdachain::DV / kdachain::DVS;
+    const dim3 grid((unsigned)a.N * (unsigned)a.Hv * NSL * (SEG ? 2u * (unsigned)a.nseg - 1u : 1u)),
+        block(kdachain::THREADS);
+#define KDA_CHAIN_LAUNCH(C)                                                                                   \
+    do {                                                                                                      \
+        if (f16) hipLaunchKernelGGL((kdachain::kda_chain_kernel<_Float16, C, SEG>), grid, block, 0, stream, a); \
+        else hipLaunchKernelGGL((kdachain::kda_chain_kernel<__bf16, C, SEG>), grid, block, 0, stream, a);      \
     } while (0)
     switch (chunk) {
         case 32: KDA_CHAIN_LAUNCH(32); break;
@@ -382,6 +440,17 @@ hipError_t launch_kda_chain(const KdaArgs &a, bool f16, int chunk, hipStream_t s
     }
 #undef KDA_CHAIN_LAUNCH
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_kda_chain(const KdaArgs &a, bool f16, int chunk, hipStream_t stream) {
+    return chain_launch<false>(a, f16, chunk, stream);
+}
+
+hipError_t launch_seg_chain(const KdaArgs &a, bool f16, int chunk, hipStream_t stream) {
+    if (a.nseg < 1) return hipErrorInvalidValue;
+    return chain_launch<true>(a, f16, chunk, stream);
 }
 
 int kda_chain_lds_bytes() { return (int)sizeof(kdachain::Smem<64>); }

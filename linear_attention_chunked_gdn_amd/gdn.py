@@ -71,6 +71,13 @@ def load_library(path: str = LIB_PATH):
     lib.gdn_prefill_split_workspace_size.restype = ctypes.c_int
     lib.gdn_prefill_split.argtypes = lib.gdn_kda_prefill.argtypes
     lib.gdn_prefill_split.restype = ctypes.c_int
+    lib.gdn_prefill_seg_workspace_size.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(ctypes.c_size_t)]
+    lib.gdn_prefill_seg_workspace_size.restype = ctypes.c_int
+    lib.gdn_prefill_seg_choose.argtypes = [i32, i32, i32, i32, p32]
+    lib.gdn_prefill_seg_choose.restype = ctypes.c_int
+    lib.gdn_prefill_seg.argtypes = [vp, vp, vp, fp, fp, fp, ip, i32, i32, i32, i32, i32, i32, i32, i32,
+                                    ctypes.c_int, vp, ctypes.c_size_t, vp, fp, vp]
+    lib.gdn_prefill_seg.restype = ctypes.c_int
     lib.gdn_kda_decode_step.argtypes = lib.gdn_decode_step.argtypes
     lib.gdn_kda_decode_step.restype = ctypes.c_int
     lib.gdn_status_string.argtypes = [ctypes.c_int]
@@ -221,8 +228,10 @@ def kda_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tens
 
 
 def _prefill_ws(fn: str, size_fn, per_channel: bool, q, k, v, g, beta, initial_state, cu_seqlens,
-                chunk_size, output_final_state, out, final_state, workspace, lib):
-    """The entry points that take a caller-owned workspace (gdn_kda_prefill, gdn_prefill_split)."""
+                chunk_size, output_final_state, out, final_state, workspace, lib, extra=()):
+    """The entry points that take a caller-owned workspace (gdn_kda_prefill, gdn_prefill_split,
+    gdn_prefill_seg); ``extra`` holds the integer arguments after chunk_size (the segment
+    count), which size_fn takes too."""
     lib = lib or load_library()
     dev = q.device
     if dev.type != "cuda":
@@ -247,7 +256,7 @@ def _prefill_ws(fn: str, size_fn, per_channel: bool, q, k, v, g, beta, initial_s
         final_state = torch.empty((N, Hv, Dv, Dk), dtype=torch.float32, device=dev)
     if final_state is not None:
         _need(final_state, "final_state", torch.float32, (N, Hv, Dv, Dk), dev)
-    need = size_fn(N, T, Hv, chunk_size, lib=lib)
+    need = size_fn(N, T, Hv, chunk_size, *extra, lib=lib)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     if workspace.device != dev or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
@@ -255,7 +264,7 @@ def _prefill_ws(fn: str, size_fn, per_channel: bool, q, k, v, g, beta, initial_s
     with torch.cuda.device(dev):
         stream = torch.cuda.current_stream(dev).cuda_stream
         st = getattr(lib, fn)(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
-                              _ptr(cu_seqlens), N, T, Hk, Hv, Dk, Dv, chunk_size, io, _ptr(workspace),
+                              _ptr(cu_seqlens), N, T, Hk, Hv, Dk, Dv, chunk_size, *extra, io, _ptr(workspace),
                               workspace.numel(), _ptr(out), _ptr(final_state), ctypes.c_void_p(stream))
     _check(lib, st, fn)
     return out, final_state
@@ -282,6 +291,43 @@ def prefill_split(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
     return _prefill_ws("gdn_prefill_split", prefill_split_workspace_size, False, q, k, v, g, beta,
                        initial_state, cu_seqlens, chunk_size, output_final_state, out, final_state,
                        workspace, lib)
+
+
+def prefill_seg_workspace_size(N: int, T: int, Hv: int, chunk_size: int = CHUNK, segments: int = 1,
+                               lib=None) -> int:
+    """Workspace bytes gdn_prefill_seg needs for N sequences, T packed tokens, Hv heads and
+    ``segments`` segments per sequence."""
+    lib = lib or load_library()
+    n = ctypes.c_size_t()
+    _check(lib, lib.gdn_prefill_seg_workspace_size(N, T, Hv, chunk_size, segments, ctypes.byref(n)),
+           "gdn_prefill_seg_workspace_size")
+    return int(n.value)
+
+
+def prefill_seg_choose(N: int, T: int, Hv: int, chunk_size: int = CHUNK, lib=None) -> int:
+    """gdn_prefill_seg_choose: the segment count for these sizes on the current device."""
+    lib = lib or load_library()
+    n = ctypes.c_int32()
+    _check(lib, lib.gdn_prefill_seg_choose(N, T, Hv, chunk_size, ctypes.byref(n)), "gdn_prefill_seg_choose")
+    return int(n.value)
+
+
+def prefill_seg(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                beta: torch.Tensor, initial_state: Optional[torch.Tensor] = None,
+                cu_seqlens: Optional[torch.Tensor] = None, chunk_size: int = CHUNK,
+                segments: Optional[int] = None, output_final_state: bool = True,
+                out: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None,
+                workspace: Optional[torch.Tensor] = None, lib=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """``prefill_split`` with each sequence's recurrence run as ``segments`` concurrent
+    segments (gdn_prefill_seg); ``segments`` defaults to ``prefill_seg_choose``'s count."""
+    lib = lib or load_library()
+    if segments is None:
+        N = 1 if cu_seqlens is None else cu_seqlens.shape[0] - 1
+        with torch.cuda.device(q.device):
+            segments = prefill_seg_choose(N, q.shape[0], v.shape[1], chunk_size, lib=lib)
+    return _prefill_ws("gdn_prefill_seg", prefill_seg_workspace_size, False, q, k, v, g, beta,
+                       initial_state, cu_seqlens, chunk_size, output_final_state, out, final_state,
+                       workspace, lib, extra=(int(segments),))
 
 
 def kda_decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,

@@ -170,6 +170,23 @@ def make_custom(seed: int, lengths, Hk: int, Hv: int, Dk: int = 128, Dv: int = 1
     return GDNInputs(name, io, q, k, v, g, beta, cu, s0)
 
 
+def head_shard(x: GDNInputs, gpus: int) -> GDNInputs:
+    """One GPU's share of x when its heads are split over `gpus` GPUs (tensor parallel over
+    heads): key heads [0, Hk / gpus) and the value heads that read them, renumbered so that
+    value head h' still reads key head h' % (Hk / gpus).  The decode steps are dropped."""
+    if gpus == 1:
+        return x
+    if x.Hk % gpus:
+        raise ValueError(f"Hk={x.Hk} heads do not split over {gpus} GPUs")
+    hk = x.Hk // gpus
+    vheads = [j + x.Hk * m for m in range(x.Hv // x.Hk) for j in range(hk)]
+    take = lambda a: None if a is None else np.ascontiguousarray(a[:, vheads])  # noqa: E731
+    s0 = None if x.initial_state is None else np.ascontiguousarray(x.initial_state[:, vheads])
+    return GDNInputs(f"{x.name}_shard{gpus}", x.io, np.ascontiguousarray(x.q[:, :hk]),
+                     np.ascontiguousarray(x.k[:, :hk]), take(x.v), take(x.g), take(x.beta),
+                     x.cu_seqlens, s0)
+
+
 # The five workloads.  Index i uses seed SEED_BASE + i.
 WORKLOADS = {
     0: dict(name="tiny_f32_H1_T256", desc="B=1, H=1, T=256, d=128, fp32 I/O, zero initial state"),

@@ -7,6 +7,7 @@ import re
 import subprocess
 
 import pytest
+import torch
 
 from linear_attention_chunked_gdn_amd import build, gdn
 
@@ -31,7 +32,8 @@ def test_header_declares_the_boundary():
     assert declared_functions() == sorted(
         ["gdn_prefill", "gdn_decode_step", "gdn_prefill_plan", "gdn_status_string", "gdn_last_error",
          "gdn_kda_workspace_size", "gdn_kda_prefill", "gdn_kda_decode_step", "gdn_prefill_fused",
-         "gdn_decode_step_fused", "gdn_prefill_split", "gdn_prefill_split_workspace_size"])
+         "gdn_decode_step_fused", "gdn_prefill_split", "gdn_prefill_split_workspace_size",
+         "gdn_prefill_seg", "gdn_prefill_seg_workspace_size", "gdn_prefill_seg_choose"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -238,3 +240,62 @@ def test_decode_fused_rejects_unknown_flags(lib):
     st = lib.gdn_decode_step_fused(p(0x1000), p(0x2000), p(0x3000), p(0x4000), p(0x5000), p(0x10000),
                                    1, 1, 1, 128, 128, 1, 16, p(0x60000), None)
     assert st == 1 and b"unknown bits" in lib.gdn_last_error()
+
+
+@pytest.mark.parametrize("C,K", [(64, 1), (64, 3), (32, 2), (128, 5)])
+def test_seg_workspace_size(lib, C, K):
+    # the split path's tiles, then fp32 o0 and e rows [T_tot, Hv, 128], then per (sequence,
+    # head, segment) two fp32 128 x 128 states
+    for N, T, Hv in ((1, 4096, 16), (3, 100, 2), (2, 0, 1)):
+        tiles = gdn.prefill_split_workspace_size(N, T, Hv, C, lib=lib)
+        want = tiles + 2 * T * Hv * 128 * 4 + N * Hv * K * 2 * 128 * 128 * 4
+        assert gdn.prefill_seg_workspace_size(N, T, Hv, C, K, lib=lib) == want
+    for bad in (0, 257, -1):
+        with pytest.raises(gdn.GDNError):
+            gdn.prefill_seg_workspace_size(1, 10, 1, 64, bad, lib=lib)
+    with pytest.raises(gdn.GDNError):
+        gdn.prefill_seg_workspace_size(1, 10, 1, 48, 1, lib=lib)
+
+
+def _seg_prefill(lib, K=2, **over):
+    a = dict(q=0x100000, k=0x200000, v=0x300000, g=0x400000, beta=0x500000, s0=None, cu=None,
+             N=1, T=10, Hk=2, Hv=4, Dk=128, Dv=128, C=64, io=1, ws=0x1000000, wsb=1 << 24,
+             o=0x600000, fs=None)
+    a.update(over)
+    p = lambda x: None if x is None else ctypes.c_void_p(x)  # noqa: E731
+    return lib.gdn_prefill_seg(p(a["q"]), p(a["k"]), p(a["v"]), p(a["g"]), p(a["beta"]), p(a["s0"]),
+                               p(a["cu"]), a["N"], a["T"], a["Hk"], a["Hv"], a["Dk"], a["Dv"], a["C"], K,
+                               a["io"], p(a["ws"]), a["wsb"], p(a["o"]), p(a["fs"]), None)
+
+
+@pytest.mark.parametrize("K,over,status,msg", [
+    (0, {}, 1, "segments=0"),
+    (300, {}, 1, "segments=300"),
+    (2, dict(io=0), 2, "bf16 or fp16"),
+    (2, dict(C=16), 2, "chunk_size"),
+    (2, dict(wsb=1 << 18), 1, "smaller than"),
+    (2, dict(ws=None), 1, "smaller than"),
+    (2, dict(ws=0x1000080), 1, "256-byte aligned"),
+    (2, dict(ws=0x500000), 1, "workspace overlaps beta"),
+    (2, dict(fs=0x1000000), 1, "workspace overlaps an output"),
+    (2, dict(N=2), 1, "cu_seqlens is required"),
+])
+def test_seg_prefill_rejects(lib, K, over, status, msg):
+    assert _seg_prefill(lib, K, **over) == status
+    assert msg in lib.gdn_last_error().decode()
+
+
+def test_seg_prefill_nothing_to_do_is_ok(lib):
+    assert _seg_prefill(lib, 3, q=None, k=None, v=None, g=None, beta=None, o=None, ws=None, wsb=0, T=0) == 0
+
+
+def test_seg_choose_needs_a_device(lib):
+    # the count depends on the device's compute units; without a GPU it is a device error
+    K = ctypes.c_int32(-1)
+    assert lib.gdn_prefill_seg_choose(1, 4096, 4, 64, None) == 1
+    assert lib.gdn_prefill_seg_choose(1, 4096, 4, 48, ctypes.byref(K)) == 2
+    st = lib.gdn_prefill_seg_choose(1, 4096, 4, 64, ctypes.byref(K))
+    if torch.cuda.is_available():
+        assert st == 0 and K.value >= 1
+    else:
+        assert st == 3 and b"compute-unit" in lib.gdn_last_error()
