@@ -249,13 +249,13 @@ gdn_status gdn_prefill_split(const void *q, const void *k, const void *v,
  * mapping ("Empowering Hybrid Attention Models on NPUs", section 4, Figure 7), in which
  * extra pre-computation lets the Reduce run over segments concurrently.  The chunk state
  * map is affine (S -> S M + B), so each later segment runs twice side by side, from a zero
- * state and from the identity, and a third launch joins them: the start state of segment
- * s + 1 is S_in(s) X_s + S0(s), with X_s the segment's product of M, and its outputs gain
- * E S_in(s)^T.  Same results as gdn_prefill_split up to rounding (bit-identical with
- * segments = 1); the faster one when few (sequence, head) pairs leave compute units idle
- * during the recurrence, since the serial chain shortens by the factor `segments` at
- * 2 segments - 1 times the recurrence's workgroups.  Arguments as for gdn_prefill_split,
- * plus:
+ * state and from the identity, and two more launches join them: the start state of
+ * segment s + 1 is S_in(s) X_s + S0(s), with X_s the segment's product of M, and its
+ * outputs gain E S_in(s)^T.  Same results as gdn_prefill_split up to rounding
+ * (bit-identical with segments = 1); the faster one when few (sequence, head) pairs leave
+ * compute units idle during the recurrence, since the serial chain shortens by the factor
+ * `segments` at 2 segments - 1 times the recurrence's workgroups.  Arguments as for
+ * gdn_prefill_split, plus:
  *
  *   segments       1 .. 256 segments per sequence (chunks [s nc / segments,
  *                  (s + 1) nc / segments) of a sequence of nc chunks form segment s; a
@@ -263,8 +263,9 @@ gdn_status gdn_prefill_split(const void *q, const void *k, const void *v,
  *   workspace      at least gdn_prefill_seg_workspace_size(...) bytes, with the same
  *                  rules as gdn_prefill_split's
  *
- * gdn_prefill_seg_workspace_size -- gdn_prefill_split_workspace_size plus two fp32
- * [T_tot, Hv, Dv] output buffers and N * Hv * segments * 2 fp32 Dk x Dk states.
+ * gdn_prefill_seg_workspace_size -- gdn_prefill_split_workspace_size plus two fp16
+ * [T_tot, Hv, Dv] output buffers and, per (sequence, head, segment), two fp32 and one
+ * fp16 Dk x Dk states.
  *
  * gdn_prefill_seg_choose -- a segment count for these sizes on the current device: the
  * largest with one recurrence workgroup per compute unit, N * Hv * 8 * (2 segments - 1)

@@ -355,9 +355,10 @@ gdn_status gdn_prefill_seg_workspace_size(int32_t N, int32_t T_tot, int32_t Hv, 
     size_t tiles = 0;
     const gdn_status st = gdn_prefill_split_workspace_size(N, T_tot, Hv, chunk_size, &tiles);
     if (st != GDN_OK) return st;
-    const size_t per_token = (size_t)Hv * kD * sizeof(float);        // o0 and e rows
-    const size_t states = (size_t)N * Hv * segments * 2 * kD * kD * sizeof(float);
-    *bytes = tiles + 2 * (size_t)T_tot * per_token + states;
+    const size_t per_token = (size_t)Hv * kD * 2 * 2;   // o0 and e rows, fp16
+    // fp32 end states (S and X^T) and fp16 start states per (sequence, head, segment)
+    const size_t states = (size_t)N * Hv * segments * kD * kD * (2 * sizeof(float) + 2);
+    *bytes = tiles + (size_t)T_tot * per_token + states;
     return ok();
 }
 
@@ -421,13 +422,16 @@ gdn_status gdn_prefill_seg(const void *q, const void *k, const void *v, const fl
         e = gdn::launch_kda_chain(a, f16, chunk_size, hs);
     } else {
         size_t off = (size_t)slots * Hv * tile_bytes(chunk_size);
-        a.o0 = reinterpret_cast<float *>(a.ws + off);
-        off += (size_t)T_tot * Hv * kD * sizeof(float);
-        a.e = reinterpret_cast<float *>(a.ws + off);
-        off += (size_t)T_tot * Hv * kD * sizeof(float);
+        a.o0 = reinterpret_cast<_Float16 *>(a.ws + off);
+        off += (size_t)T_tot * Hv * kD * 2;
+        a.e = reinterpret_cast<_Float16 *>(a.ws + off);
+        off += (size_t)T_tot * Hv * kD * 2;
         a.sseg = reinterpret_cast<float *>(a.ws + off);
+        off += (size_t)N * Hv * segments * 2 * kD * kD * sizeof(float);
+        a.sin16 = reinterpret_cast<_Float16 *>(a.ws + off);
         e = gdn::launch_gdn_map(a, f16, chunk_size, hs);
         if (e == hipSuccess) e = gdn::launch_seg_chain(a, f16, chunk_size, hs);
+        if (e == hipSuccess) e = gdn::launch_seg_join(a, hs);
         if (e == hipSuccess) e = gdn::launch_seg_fix(a, f16, chunk_size, hs);
     }
     if (e != hipSuccess)

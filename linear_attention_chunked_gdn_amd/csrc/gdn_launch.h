@@ -50,9 +50,10 @@ struct KdaArgs {
     // Segmented chain only (launch_seg_chain, launch_seg_fix): every sequence runs as nseg
     // segments of whole chunks, each from its own start state (see gdn_seg.hip).
     int32_t nseg;
-    float *o0;              // [T_tot, Hv, 128] outputs of each segment from a zero start
-    float *e;               // [T_tot, Hv, 128] outputs of the identity-state rows
+    _Float16 *o0;           // [T_tot, Hv, 128] outputs of segments >= 1 from a zero start
+    _Float16 *e;            // [T_tot, Hv, 128] outputs of the identity-state rows
     float *sseg;            // [N, Hv, nseg, 2, 128, 128] segment end states (S and X^T)
+    _Float16 *sin16;        // [N, Hv, nseg, 128, 128] start states of segments 1 .. nseg - 1
 };
 // Workspace tile of one chunk of C tokens and one value head (byte offsets; fp16 except
 // gl; row-major), with T = (I + A)^-1 and the decays of the chunk:
@@ -90,9 +91,10 @@ int kda_chain_lds_bytes();
 // The scalar-gate map (KdaArgs::g is [T_tot, Hv]) into the same workspace tiles, read by
 // launch_kda_chain.
 hipError_t launch_gdn_map(const KdaArgs &a, bool f16, int chunk, hipStream_t stream);
-// The segmented chain (the chain kernel in its segment mode) and the fix-up that joins the
-// segments (gdn_seg.hip), both over tiles of `chunk` tokens.
+// The segmented chain (the chain kernel in its segment mode), then the two kernels that join
+// the segments (gdn_seg.hip): the segments' start states, and the outputs' corrections.
 hipError_t launch_seg_chain(const KdaArgs &a, bool f16, int chunk, hipStream_t stream);
+hipError_t launch_seg_join(const KdaArgs &a, hipStream_t stream);
 hipError_t launch_seg_fix(const KdaArgs &a, bool f16, int chunk, hipStream_t stream);
 // one token with a per-key-channel gate: DecodeArgs::g is [B, Hv, 128]
 hipError_t launch_kda_decode(const DecodeArgs &a, int io, hipStream_t stream);

@@ -1,6 +1,6 @@
-// Fix-up of the segmented chain (the Chunk-Seg-Seg mapping of "Empowering Hybrid Attention
-// Models on NPUs", section 4, Figure 7): the state recurrence of one sequence split into
-// segments that run at the same time, each from its own start state, then joined here.
+// Joining the segments of the segmented chain (the Chunk-Seg-Seg mapping of "Empowering
+// Hybrid Attention Models on NPUs", section 4, Figure 7): the state recurrence of one
+// sequence split into segments that run at the same time, each from its own start state.
 //
 // Per chunk the state map is affine, S -> S M + B (M = Diag(gl) - W^T Kl, B = U^T Kl), so a
 // segment run from a zero state and from the identity (in place of S, with no B term)
@@ -10,13 +10,16 @@
 //   O0, E      outputs of the value rows from zero, and of the identity rows, per token,
 // and then, exactly up to rounding,
 //   S_end = S_in X + S0_end,      O = O0 + E S_in^T.
-// The chain kernel's segment mode writes O0, E, S0_end and X^T; this kernel composes the
-// start state of every segment (S_in of segment 0 is the initial state, so its end state
-// is the first S_in) and writes o and the final state.
+// The chain kernel's segment mode writes O0 and E (fp16), S0_end and X^T; segment 0
+// starts from the real initial state and writes its outputs directly.
 //
-// One 256-thread workgroup per (chunk slot, value head, 16 value channels) corrects that
-// chunk's outputs; N * Hv * 8 more compose the final state.  Each composes the 16 rows of
-// S_in it needs in LDS, one fp32 MFMA product per earlier segment.
+// gdn_seg_join_kernel: one 256-thread workgroup per (sequence, value head, 16 value
+// channels) walks the segments in order, S_in(s + 1) = S_in(s) X_s + S0_end(s) with one
+// fp32 MFMA product each, stores every S_in as fp16 (a.sin16) and the last one as the
+// final state.
+// gdn_seg_fix_kernel: one 512-thread workgroup per (chunk slot, value head) of segments
+// >= 1 stages the chunk's E rows in LDS; wave w forms O = O0 + E S_in^T for value channels
+// [16w, 16w + 16) (fp16 MFMA, fp32 accumulation) and stores it.
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
@@ -28,64 +31,36 @@ constexpr int ROWS = 16;        // value channels per workgroup
 constexpr int RS = D + 4;       // fp32 row stride of the S_in rows in LDS
 constexpr int THREADS = 256;
 
-template <typename IO, int C>
-__global__ __launch_bounds__(THREADS) void gdn_seg_fix_kernel(const KdaArgs a) {
+// S_in(s + 1) = S_in(s) X_s + S0_end(s) for the workgroup's 16 rows, held in LDS
+__global__ __launch_bounds__(THREADS) void gdn_seg_join_kernel(const KdaArgs a) {
     __shared__ __align__(16) float R[ROWS * RS];
     const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, g4 = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     constexpr int NSL = D / ROWS;
-    const long long nout = (long long)a.nslots * a.Hv * NSL;
-    const bool final_item = (long long)blockIdx.x >= nout;
-
-    int n, h, slice, upto, tok0 = 0, eos = 0;
-    if (!final_item) {
-        const int slot = blockIdx.x / (a.Hv * NSL), rem = blockIdx.x % (a.Hv * NSL);
-        h = rem / NSL;
-        slice = rem % NSL;
-        // the sequence of this slot: the last n with cu[n] / C + n <= slot
-        n = 0;
-        if (a.cu) {
-            int lo = 0, hi = a.N - 1;
-            while (lo < hi) {
-                const int mid = (lo + hi + 1) >> 1;
-                if (a.cu[mid] / C + mid <= slot) lo = mid;
-                else hi = mid - 1;
-            }
-            n = lo;
-        }
-        const int bos = a.cu ? a.cu[n] : 0;
-        eos = a.cu ? a.cu[n + 1] : a.T_tot;
-        const int j = slot - (bos / C + n);
-        tok0 = bos + C * j;
-        if (tok0 >= eos) return;   // a slot no chunk uses
-        const int nc = (eos - bos + C - 1) / C;
-        // the segment holding chunk j: the largest s with s nc / nseg <= j
-        upto = (int)(((long long)(j + 1) * a.nseg + nc - 1) / nc) - 1;
-    } else {
-        const int b = (int)((long long)blockIdx.x - nout);
-        slice = b % NSL;
-        h = (b / NSL) % a.Hv;
-        n = b / (NSL * a.Hv);
-        upto = a.nseg;   // through every segment
-    }
+    const int slice = blockIdx.x % NSL, h = (blockIdx.x / NSL) % a.Hv, n = blockIdx.x / (NSL * a.Hv);
     const int dv0 = slice * ROWS;
-    const float *sb = a.sseg + ((size_t)n * a.Hv + h) * a.nseg * 2 * D * D;
+    float *sb = a.sseg + ((size_t)n * a.Hv + h) * a.nseg * 2 * D * D;
 
-    // S_in of segment 1 = the end state of segment 0, rows dv0 .. dv0 + 15
-    for (int i = tid; i < ROWS * D / 4; i += THREADS) {
+    // fp16 copies of S_in(1) .. S_in(nseg - 1), [nseg][128][128] per (sequence, head)
+    _Float16 *s16 = a.sin16 + ((size_t)n * a.Hv + h) * a.nseg * D * D;
+    for (int i = tid; i < ROWS * D / 4; i += THREADS) {   // S_in(1): segment 0's end state
         const int r = i / (D / 4), c = 4 * (i % (D / 4));
-        *reinterpret_cast<f32x4 *>(&R[r * RS + c]) =
-            *reinterpret_cast<const f32x4 *>(sb + (size_t)(dv0 + r) * D + c);
+        const f32x4 x = *reinterpret_cast<const f32x4 *>(sb + (size_t)(dv0 + r) * D + c);
+        *reinterpret_cast<f32x4 *>(&R[r * RS + c]) = x;
+        f16x4 y;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] = (_Float16)x[e];
+        *reinterpret_cast<f16x4 *>(s16 + (size_t)(dv0 + r) * D + c) = y;
     }
     __syncthreads();
-    // S_in of segment s + 1 = S_in(s) X_s + S0_end(s); wave w forms key columns [32w, 32w + 32)
-    for (int s = 1; s < upto; ++s) {
-        const float *s0e = sb + (size_t)s * 2 * D * D, *xt = s0e + D * D;
+    for (int s = 1; s < a.nseg; ++s) {
+        float *s0e = sb + (size_t)s * 2 * D * D;
+        const float *xt = s0e + D * D;
+        // wave w: key columns [32w, 32w + 32); lane: rows dv0 + 4 g4 + i, key column col
         f32x4 acc[2];
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) {
             const int col = 32 * wave + 16 * ct + l16;
-            // lane: rows dv0 + 4 g4 + i, key column col
 #pragma unroll
             for (int i = 0; i < 4; ++i) acc[ct][i] = s0e[(size_t)(dv0 + 4 * g4 + i) * D + col];
 #pragma unroll
@@ -97,58 +72,119 @@ __global__ __launch_bounds__(THREADS) void gdn_seg_fix_kernel(const KdaArgs a) {
                 mma(acc[ct], fa, fb);
             }
         }
-        __syncthreads();
+        __syncthreads();   // every wave has read R and its S0_end(s) elements
+        // S_in(s + 1) as fp16 for the fix-up, or the final state after the last segment
+        const bool last = s + 1 == a.nseg;
+        float *fin = last && a.sN ? a.sN + ((size_t)n * a.Hv + h) * D * D : nullptr;
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct)
+        for (int ct = 0; ct < 2; ++ct) {
+            const int col = 32 * wave + 16 * ct + l16;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) R[(4 * g4 + i) * RS + 32 * wave + 16 * ct + l16] = acc[ct][i];
-        __syncthreads();
-    }
-
-    if (final_item) {
-        if (a.sN) {
-            float *dst = a.sN + ((size_t)n * a.Hv + h) * D * D;
-            for (int i = tid; i < ROWS * D / 4; i += THREADS) {
-                const int r = i / (D / 4), c = 4 * (i % (D / 4));
-                *reinterpret_cast<f32x4 *>(dst + (size_t)(dv0 + r) * D + c) =
-                    *reinterpret_cast<const f32x4 *>(&R[r * RS + c]);
+            for (int i = 0; i < 4; ++i) {
+                const size_t at = (size_t)(dv0 + 4 * g4 + i) * D + col;
+                R[(4 * g4 + i) * RS + col] = acc[ct][i];
+                if (!last) s16[(size_t)s * D * D + at] = (_Float16)acc[ct][i];
+                if (fin) fin[at] = acc[ct][i];
             }
         }
-        return;
+        __syncthreads();
     }
-
-    // O^T (value channels x tokens) = O0^T + S_in E^T for the chunk's 16-token tiles
-    for (int t = wave; t < C / 16; t += 4) {
-        const int tok = tok0 + 16 * t + l16;
-        const int tc = min(tok, eos - 1);   // rows past the sequence are read in bounds, not stored
-        const size_t row = ((size_t)tc * a.Hv + h) * D;
-        f32x4 acc = *reinterpret_cast<const f32x4 *>(a.o0 + row + dv0 + 4 * g4);
-        if (upto > 0) {
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                Frag<float> fa, fb;
-                fa.load8(&R[l16 * RS + 32 * kb + 8 * g4]);
-                fb.load8(a.e + row + 32 * kb + 8 * g4);
-                mma(acc, fa, fb);
-            }
+    if (a.nseg == 1 && a.sN) {   // one segment: its end state is the final state
+        float *dst = a.sN + ((size_t)n * a.Hv + h) * D * D;
+        for (int i = tid; i < ROWS * D / 4; i += THREADS) {
+            const int r = i / (D / 4), c = 4 * (i % (D / 4));
+            *reinterpret_cast<f32x4 *>(dst + (size_t)(dv0 + r) * D + c) = *reinterpret_cast<const f32x4 *>(&R[r * RS + c]);
         }
-        if (tok < eos) {
+    }
+}
+
+constexpr int FIX_THREADS = 512;   // 8 waves: one per 16 value channels
+
+template <typename IO, int C>
+__global__ __launch_bounds__(FIX_THREADS) void gdn_seg_fix_kernel(const KdaArgs a) {
+    constexpr int ES = D + 8;   // fp16 row stride of the staged E rows
+    __shared__ __align__(16) _Float16 Es[C * ES];
+    const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, g4 = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int slot = blockIdx.x / a.Hv, h = blockIdx.x % a.Hv;
+    // the sequence of this slot: the last n with cu[n] / C + n <= slot
+    int n = 0;
+    if (a.cu) {
+        int lo = 0, hi = a.N - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (a.cu[mid] / C + mid <= slot) lo = mid;
+            else hi = mid - 1;
+        }
+        n = lo;
+    }
+    const int bos = a.cu ? a.cu[n] : 0, eos = a.cu ? a.cu[n + 1] : a.T_tot;
+    const int j = slot - (bos / C + n);
+    const int tok0 = bos + C * j;
+    if (tok0 >= eos) return;   // a slot no chunk uses
+    const int nc = (eos - bos + C - 1) / C;
+    // the segment holding chunk j: the largest s with s nc / nseg <= j
+    const int seg = (int)(((long long)(j + 1) * a.nseg + nc - 1) / nc) - 1;
+    if (seg == 0) return;      // segment 0 stored its outputs itself
+    const int dv0 = ROWS * wave;
+    const int nval = min(C, eos - tok0);
+
+    // E rows of the chunk (rows past the sequence are zero) into LDS
+    for (int i = tid; i < C * D / 8; i += FIX_THREADS) {
+        const int t = i / (D / 8), c = 8 * (i % (D / 8));
+        f16x8 x = {};
+        if (t < nval) x = *reinterpret_cast<const f16x8 *>(a.e + ((size_t)(tok0 + t) * a.Hv + h) * D + c);
+        *reinterpret_cast<f16x8 *>(&Es[t * ES + c]) = x;
+    }
+    // S_in(seg) rows dv0 + l16 as A operands (slots = identity rows 32 kb + 8 g4 + e), and O0
+    const _Float16 *sin = a.sin16 + (((size_t)n * a.Hv + h) * a.nseg + (seg - 1)) * D * D;
+    Frag<_Float16> fs[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) fs[kb].load8(sin + (size_t)(dv0 + l16) * D + 32 * kb + 8 * g4);
+    f32x4 acc[C / 16];
+#pragma unroll
+    for (int t = 0; t < C / 16; ++t) {
+        const int tc = min(16 * t + l16, nval - 1);   // rows past the sequence: read in bounds, not stored
+        const f16x4 o0 = *reinterpret_cast<const f16x4 *>(a.o0 + ((size_t)(tok0 + tc) * a.Hv + h) * D + dv0 + 4 * g4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[t][i] = (float)o0[i];
+    }
+    __syncthreads();
+
+    // O^T (value channels x tokens) = O0^T + S_in E^T, one 16-token tile at a time
+#pragma unroll
+    for (int t = 0; t < C / 16; ++t) {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            Frag<_Float16> fe;
+            fe.load8(&Es[(16 * t + l16) * ES + 32 * kb + 8 * g4]);
+            mma(acc[t], fs[kb], fe);
+        }
+        if (16 * t + l16 < nval) {
             typename Vec4<IO>::type y;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) y[i] = Cvt<IO>::from_f32(acc[i]);
-            *reinterpret_cast<typename Vec4<IO>::type *>(reinterpret_cast<IO *>(a.o) + ((size_t)tok * a.Hv + h) * D +
-                                                         dv0 + 4 * g4) = y;
+            for (int i = 0; i < 4; ++i) y[i] = Cvt<IO>::from_f32(acc[t][i]);
+            *reinterpret_cast<typename Vec4<IO>::type *>(reinterpret_cast<IO *>(a.o) +
+                                                         ((size_t)(tok0 + 16 * t + l16) * a.Hv + h) * D + dv0 + 4 * g4) = y;
         }
     }
 }
 
 }  // namespace gdnseg
 
-hipError_t launch_seg_fix(const KdaArgs &a, bool f16, int chunk, hipStream_t stream) {
+hipError_t launch_seg_join(const KdaArgs &a, hipStream_t stream) {
     constexpr unsigned NSL = gdnseg::D / gdnseg::ROWS;
-    const unsigned long long items = ((unsigned long long)a.nslots + (unsigned long long)a.N) * a.Hv * NSL;
+    const unsigned long long items = (unsigned long long)a.N * a.Hv * NSL;
     if (a.nseg < 1 || items > 0x7fffffffULL) return hipErrorInvalidValue;
-    const dim3 grid((unsigned)items), block(gdnseg::THREADS);
+    hipLaunchKernelGGL(gdnseg::gdn_seg_join_kernel, dim3((unsigned)items), dim3(gdnseg::THREADS), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_seg_fix(const KdaArgs &a, bool f16, int chunk, hipStream_t stream) {
+    const unsigned long long items = (unsigned long long)a.nslots * a.Hv;
+    if (a.nseg < 1 || items > 0x7fffffffULL) return hipErrorInvalidValue;
+    if (items == 0) return hipSuccess;
+    const dim3 grid((unsigned)items), block(gdnseg::FIX_THREADS);
 #define SEG_FIX_LAUNCH(C)                                                                                \
     do {                                                                                                 \
         if (f16) hipLaunchKernelGGL((gdnseg::gdn_seg_fix_kernel<_Float16, C>), grid, block, 0, stream, a); \

@@ -218,12 +218,16 @@ __device__ __forceinline__ void loader_QS(const Smem<C> &s, int W, int l16, int 
     }
 }
 
-// Phase 2, loader wave W: O^T = S Qg^T + v^T P^T for its token tiles, stored (as IO to o;
-// in the segment mode as fp32 to obase, of the same [token][head][channel] shape).
+// Phase 2, loader wave W: O^T = S Qg^T + v^T P^T for its token tiles, stored as IO to o.
+// In the segment mode `kind` picks the destination, all [token][head][channel]: 0 IO to o
+// (segment 0), 1 fp16 to a.o0 (value rows of later segments), 2 fp16 to a.e (identity
+// rows); one 8-byte store for each, with no branch between them (a branch around stores
+// here would make the compiler's count of outstanding vector-memory operations
+// conservative).
 template <typename IO, int C, bool SEG>
 __device__ __forceinline__ void loader_O(const Smem<C> &s, const KdaArgs &a, int W, int l16, int g4,
                                          const f32x4 (&qs)[Cfg<C>::TPW], int h, int dv0, int tok0, int nval,
-                                         float *obase) {
+                                         int kind) {
     using F = Cfg<C>;
 #pragma unroll
     for (int k = 0; k < F::TPW; ++k) {
@@ -241,15 +245,24 @@ __device__ __forceinline__ void loader_O(const Smem<C> &s, const KdaArgs &a, int
                 mma(acc, fv, fp);
             }
             const int tok = 16 * t + l16;
+            const size_t at = ((size_t)(tok0 + tok) * a.Hv + h) * DV + dv0 + 4 * g4;
             if constexpr (SEG) {
-                if (tok < nval)
-                    *reinterpret_cast<f32x4 *>(obase + ((size_t)(tok0 + tok) * a.Hv + h) * DV + dv0 + 4 * g4) = acc;
+                typename Vec4<IO>::type yio;
+                f16x4 yh;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    yio[i] = Cvt<IO>::from_f32(acc[i]);
+                    yh[i] = (hf)acc[i];
+                }
+                typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+                const u32x2 bits = kind == 0 ? __builtin_bit_cast(u32x2, yio) : __builtin_bit_cast(u32x2, yh);
+                char *base = kind == 0 ? (char *)a.o : kind == 1 ? (char *)a.o0 : (char *)a.e;
+                if (tok < nval) *reinterpret_cast<u32x2 *>(base + at * 2) = bits;
             } else if (tok < nval) {
                 typename Vec4<IO>::type y;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) y[i] = Cvt<IO>::from_f32(acc[i]);
-                *reinterpret_cast<typename Vec4<IO>::type *>(reinterpret_cast<IO *>(a.o) +
-                                                             ((size_t)(tok0 + tok) * a.Hv + h) * DV + dv0 + 4 * g4) = y;
+                *reinterpret_cast<typename Vec4<IO>::type *>(reinterpret_cast<IO *>(a.o) + at) = y;
             }
         }
     }
@@ -289,8 +302,9 @@ __device__ __forceinline__ void chain_update(Smem<C> &s, int W, int l16, int g4,
 // (sequence, head), segment 0 has the 8 value slices, from the initial state; every later
 // segment has 8 value slices from a zero state and 8 slices of identity rows (state X = I
 // and no U term), whose outputs E and end state X carry the segment's dependence on its
-// real start state.  Outputs go as fp32 to a.o0 (value rows) or a.e (identity rows), end
-// states to a.sseg (X transposed); gdn_seg.hip joins them.
+// real start state.  Segment 0 stores its outputs to o; later segments store theirs as
+// fp32 to a.o0 (value rows) or fp16 to a.e (identity rows); end states go to a.sseg (X
+// transposed).  gdn_seg.hip joins them.
 template <typename IO, int C, bool SEG>
 __global__ __launch_bounds__(THREADS) void kda_chain_kernel(const KdaArgs a) {
     using F = Cfg<C>;
@@ -338,7 +352,7 @@ __global__ __launch_bounds__(THREADS) void kda_chain_kernel(const KdaArgs a) {
     wk.nchunks = c1 - c0;
     wk.slot_stride = (size_t)a.Hv * Tile<C>::BYTES;
     wk.ws = a.ws + ((size_t)(bos / C + n + c0) * a.Hv + h) * Tile<C>::BYTES;
-    float *const obase = ident ? a.e : a.o0;
+    const int kind = seg == 0 ? 0 : ident ? 2 : 1;
     const float ukeep = ident ? 0.f : 1.f;
 
     f32x4 st[2];
@@ -382,7 +396,7 @@ __global__ __launch_bounds__(THREADS) void kda_chain_kernel(const KdaArgs a) {
                 __syncthreads();
                 commit_b(sb, s, tid);
                 load_b(sb, wk, c + 2, tid);
-                loader_O<IO, C, SEG>(s, a, W, l16, g4, qs, h, wk.dv0, tok0, nval, obase);
+                loader_O<IO, C, SEG>(s, a, W, l16, g4, qs, h, wk.dv0, tok0, nval, kind);
                 __syncthreads();
             }
         } else {

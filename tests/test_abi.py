@@ -244,11 +244,11 @@ def test_decode_fused_rejects_unknown_flags(lib):
 
 @pytest.mark.parametrize("C,K", [(64, 1), (64, 3), (32, 2), (128, 5)])
 def test_seg_workspace_size(lib, C, K):
-    # the split path's tiles, then fp32 o0 and e rows [T_tot, Hv, 128], then per (sequence,
-    # head, segment) two fp32 128 x 128 states
+    # the split path's tiles, then o0 and e rows [T_tot, Hv, 128] (fp16), then per
+    # (sequence, head, segment) two fp32 and one fp16 128 x 128 states
     for N, T, Hv in ((1, 4096, 16), (3, 100, 2), (2, 0, 1)):
         tiles = gdn.prefill_split_workspace_size(N, T, Hv, C, lib=lib)
-        want = tiles + 2 * T * Hv * 128 * 4 + N * Hv * K * 2 * 128 * 128 * 4
+        want = tiles + T * Hv * 128 * 2 * 2 + N * Hv * K * 128 * 128 * (2 * 4 + 2)
         assert gdn.prefill_seg_workspace_size(N, T, Hv, C, K, lib=lib) == want
     for bad in (0, 257, -1):
         with pytest.raises(gdn.GDNError):
