@@ -277,7 +277,7 @@ gdn_status gdn_kda_prefill(const void *q, const void *k, const void *v, const fl
         return fail(GDN_ERR_INVALID_ARGUMENT, "workspace of %zu bytes is smaller than the %zu required",
                     workspace ? workspace_bytes : (size_t)0, need);
     if (!aligned(workspace, 256)) return fail(GDN_ERR_INVALID_ARGUMENT, "workspace is not 256-byte aligned");
-    if ((long long)kda_slots(N, T_tot) * Hv > 0x7fffffffLL || (long long)N * Hv * 8 > 0x7fffffffLL)
+    if ((long long)kda_slots(N, T_tot) * Hv > 0x7fffffffLL || (long long)N * Hv * 8 + 64 > 0x7fffffffLL)
         return fail(GDN_ERR_UNSUPPORTED, "too many chunks or heads for one launch");
     if (T_tot == 0 && !final_state) return ok();
 
@@ -325,7 +325,7 @@ gdn_status gdn_prefill_split(const void *q, const void *k, const void *v, const 
         return fail(GDN_ERR_INVALID_ARGUMENT, "workspace of %zu bytes is smaller than the %zu required",
                     workspace ? workspace_bytes : (size_t)0, need);
     if (!aligned(workspace, 256)) return fail(GDN_ERR_INVALID_ARGUMENT, "workspace is not 256-byte aligned");
-    if ((long long)kda_slots(N, T_tot, chunk_size) * Hv > 0x7fffffffLL || (long long)N * Hv * 8 > 0x7fffffffLL)
+    if ((long long)kda_slots(N, T_tot, chunk_size) * Hv > 0x7fffffffLL || (long long)N * Hv * 8 + 64 > 0x7fffffffLL)
         return fail(GDN_ERR_UNSUPPORTED, "too many chunks or heads for one launch");
     if (T_tot == 0 && !final_state) return ok();
 
@@ -402,7 +402,7 @@ gdn_status gdn_prefill_seg(const void *q, const void *k, const void *v, const fl
                     workspace ? workspace_bytes : (size_t)0, need);
     if (!aligned(workspace, 256)) return fail(GDN_ERR_INVALID_ARGUMENT, "workspace is not 256-byte aligned");
     const long long slots = (long long)kda_slots(N, T_tot, chunk_size);
-    if ((slots + N) * Hv * 8 > 0x7fffffffLL || (long long)N * Hv * 8 * (2 * segments - 1) > 0x7fffffffLL)
+    if ((slots + N) * Hv * 8 > 0x7fffffffLL || (long long)N * Hv * 16 * (segments + 8) > 0x7fffffffLL)
         return fail(GDN_ERR_UNSUPPORTED, "too many chunks, heads or segments for one launch");
     if (T_tot == 0 && !final_state) return ok();
 

@@ -316,23 +316,26 @@ __global__ __launch_bounds__(THREADS) void kda_chain_kernel(const KdaArgs a) {
     const int W = wave & 3;
 
     constexpr int NSL = DV / DVS;
-    const int G = gridDim.x;
-    int item = blockIdx.x;
-    if ((G & 7) == 0) item = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
+    // XCD-aware mapping.  Workgroups are dispatched to the 8 XCDs in turn (blockIdx % 8).
+    // The GS workgroups that read the same tiles (a head's 8 slices; in the segment mode a
+    // segment's value and identity slices) form a group, and group g runs on XCD g % 8, so
+    // its tiles are fetched into one L2.  The grid is padded to whole rounds of 8 groups;
+    // the padding workgroups leave at once.
+    constexpr int GS = SEG ? 2 * NSL : NSL;
+    const int xcd = blockIdx.x & 7, kx = blockIdx.x >> 3;
+    const int item = GS * (xcd + 8 * (kx / GS)) + kx % GS;
+    if (item >= a.N * a.Hv * (SEG ? GS * a.nseg : NSL)) return;
     int slice, h, n, seg = 0;
     bool ident = false;
     if constexpr (SEG) {
-        const int per = NSL * (2 * a.nseg - 1);   // workgroups per (sequence, head)
+        const int per = GS * a.nseg;   // item slots per (sequence, head)
         const int i = item % per;
         h = (item / per) % a.Hv;
         n = item / (per * a.Hv);
-        if (i < NSL) {
-            slice = i;
-        } else {
-            seg = 1 + (i - NSL) / (2 * NSL);
-            ident = (i - NSL) % (2 * NSL) >= NSL;
-            slice = (i - NSL) % NSL;
-        }
+        seg = i / GS;
+        ident = i % GS >= NSL;
+        slice = i % NSL;
+        if (seg == 0 && ident) return;   // segment 0 runs from the real state: no identity rows
     } else {
         slice = item % NSL;
         h = (item / NSL) % a.Hv;
@@ -438,9 +441,12 @@ namespace {
 
 template <bool SEG>
 hipError_t chain_launch(const KdaArgs &a, bool f16, int chunk, hipStream_t stream) {
-    constexpr unsigned NSL = kdachain::DV / kdachain::DVS;
-    const dim3 grid((unsigned)a.N * (unsigned)a.Hv * NSL * (SEG ? 2u * (unsigned)a.nseg - 1u : 1u)),
-        block(kdachain::THREADS);
+    // groups of GS workgroups (see the kernel), padded to whole rounds of 8 groups
+    constexpr unsigned long long GS = (kdachain::DV / kdachain::DVS) * (SEG ? 2 : 1);
+    const unsigned long long groups = (unsigned long long)a.N * a.Hv * (SEG ? (unsigned long long)a.nseg : 1ull);
+    const unsigned long long wgs = 8 * GS * ((groups + 7) / 8);
+    if (wgs > 0x7fffffffULL) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)wgs), block(kdachain::THREADS);
 #define KDA_CHAIN_LAUNCH(C)                                                                                   \
     do {                                                                                                      \
         if (f16) hipLaunchKernelGGL((kdachain::kda_chain_kernel<_Float16, C, SEG>), grid, block, 0, stream, a); \
