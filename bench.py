@@ -125,13 +125,14 @@ def _counter_median(path: str, counter: str, kernel_substr: str) -> float:
 
 def choose_path(x, path: str, prologue: bool, segments: int = 1) -> str:
     """pipe (gdn_prefill), split (gdn_prefill_split) or seg (gdn_prefill_seg) for this
-    workload: auto takes the two-launch paths for 16-bit I/O without the prologue when the
+    workload.  auto takes a two-launch path for 16-bit I/O without the prologue when the
     one-launch kernel's workgroups (one per CU) would leave at least half of the 256 CUs
-    idle, and the segmented one among them when gdn_prefill_seg_choose gave more than one
-    segment."""
+    idle, or for a packed batch of several sequences (where the one-launch kernel's
+    longest sequences set its time); among them the segmented one when
+    gdn_prefill_seg_choose gave more than one segment."""
     if path != "auto":
         return path
-    if x.io != "f32" and not prologue and x.N * x.Hv * 8 <= 128:
+    if x.io != "f32" and not prologue and (x.N * x.Hv * 8 <= 128 or x.N > 1):
         return "seg" if segments > 1 else "split"
     return "pipe"
 
@@ -480,7 +481,8 @@ def main() -> int:
                   "input_copies_rotated": copies}
         if path == "seg":
             kernel += "+gdn_seg_fix_kernel"
-            launch.update(kernel=kernel, segments=nseg, fix_workgroups=(x.T_tot // chunk + 2 * x.N) * x.Hv * 8)
+            launch.update(kernel=kernel, segments=nseg, join_workgroups=x.N * x.Hv * 8,
+                          fix_workgroups=(x.T_tot // chunk + x.N) * x.Hv)
     else:
         plan = gdn.prefill_plan(x.N, x.Hv, IO_CODE[x.io])
         kernel = "gdn_prefill_pipe_kernel" if plan["threads_per_workgroup"] == 512 else "gdn_prefill_kernel"

@@ -36,3 +36,21 @@ def test_workload_io_override_keeps_draws(io):
     if io == "f16":
         assert "f16" in b.name
         assert np.array_equal(b.v.astype(np.float16).astype(np.float32), b.v)
+
+
+def test_head_shard_keeps_the_key_head_of_every_value_head():
+    # one GPU's share of a GQA batch: key heads [0, Hk / G) and the value heads reading them,
+    # renumbered so that value head h' reads key head h' % (Hk / G)
+    x = inputs.make_custom(3, [40, 0, 25], 4, 8, io="bf16", init_std=0.1)
+    y = inputs.head_shard(x, 2)
+    assert (y.Hk, y.Hv, y.N, y.T_tot) == (2, 4, 3, 65)
+    picked = [0, 1, 4, 5]   # value heads j + 4 m for j < 2, m < 2
+    for hp, h in enumerate(picked):
+        assert np.array_equal(y.v[:, hp], x.v[:, h]) and np.array_equal(y.g[:, hp], x.g[:, h])
+        assert np.array_equal(y.beta[:, hp], x.beta[:, h])
+        assert np.array_equal(y.initial_state[:, hp], x.initial_state[:, h])
+        assert np.array_equal(y.k[:, hp % y.Hk], x.k[:, h % x.Hk])
+        assert np.array_equal(y.q[:, hp % y.Hk], x.q[:, h % x.Hk])
+    assert inputs.head_shard(x, 1) is x
+    with pytest.raises(ValueError):
+        inputs.head_shard(x, 3)
