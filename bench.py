@@ -85,8 +85,8 @@ KERNEL_SOURCES = {
                                         "gdn_launch.h"],
     "gdn_map_kernel+kda_chain_kernel": ["gdn_map.hip", "kda_chain.hip", "gdn_wy.h", "gdn_device.h",
                                         "gdn_launch.h"],
-    "gdn_map_kernel+kda_chain_kernel+gdn_seg_fix_kernel": ["gdn_map.hip", "kda_chain.hip", "gdn_seg.hip",
-                                                           "gdn_wy.h", "gdn_device.h", "gdn_launch.h"],
+    "gdn_map_kernel+kda_chain_kernel+gdn_seg_join_kernel+gdn_seg_fix_kernel": [
+        "gdn_map.hip", "kda_chain.hip", "gdn_seg.hip", "gdn_wy.h", "gdn_device.h", "gdn_launch.h"],
 }
 
 
@@ -149,7 +149,7 @@ def summarize_pmc(directory: str, workload: int, calib_mib: int, io=None, kda=Fa
     if kda:
         kernel = "kda_map_kernel+kda_chain_kernel"
     elif choose_path(x, path, prologue) == "seg":
-        kernel = "gdn_map_kernel+kda_chain_kernel+gdn_seg_fix_kernel"
+        kernel = "gdn_map_kernel+kda_chain_kernel+gdn_seg_join_kernel+gdn_seg_fix_kernel"
     elif choose_path(x, path, prologue) == "split":
         kernel = "gdn_map_kernel+kda_chain_kernel"
     else:
@@ -480,7 +480,7 @@ def main() -> int:
                   "chain_workgroups": x.N * x.Hv * 8 * (2 * nseg - 1), "workspace_bytes": int(ws.numel()),
                   "input_copies_rotated": copies}
         if path == "seg":
-            kernel += "+gdn_seg_fix_kernel"
+            kernel += "+gdn_seg_join_kernel+gdn_seg_fix_kernel"
             launch.update(kernel=kernel, segments=nseg, join_workgroups=x.N * x.Hv * 8,
                           fix_workgroups=(x.T_tot // chunk + x.N) * x.Hv)
     else:
