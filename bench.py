@@ -85,6 +85,8 @@ KERNEL_SOURCES = {
                                         "gdn_launch.h"],
     "gdn_map_kernel+kda_chain_kernel": ["gdn_map.hip", "kda_chain.hip", "gdn_wy.h", "gdn_device.h",
                                         "gdn_launch.h"],
+    "gdn_map_kernel+kda_chain_kernel(prologue)": ["gdn_map.hip", "kda_chain.hip", "gdn_wy.h", "gdn_device.h",
+                                                  "gdn_launch.h"],
     "gdn_map_kernel+kda_chain_kernel+gdn_seg_join_kernel+gdn_seg_fix_kernel": [
         "gdn_map.hip", "kda_chain.hip", "gdn_seg.hip", "gdn_wy.h", "gdn_device.h", "gdn_launch.h"],
 }
@@ -124,16 +126,16 @@ def _counter_median(path: str, counter: str, kernel_substr: str) -> float:
 
 
 def choose_path(x, path: str, prologue: bool, segments: int = 1) -> str:
-    """pipe (gdn_prefill), split (gdn_prefill_split) or seg (gdn_prefill_seg) for this
-    workload.  auto takes a two-launch path for 16-bit I/O without the prologue when the
-    one-launch kernel's workgroups (one per CU) would leave at least half of the 256 CUs
+    """pipe (gdn_prefill / gdn_prefill_fused), split (gdn_prefill_split / _fused) or seg
+    (gdn_prefill_seg) for this workload.  auto takes a two-launch path for 16-bit I/O when
+    the one-launch kernel's workgroups (one per CU) would leave at least half of the 256 CUs
     idle, or for a packed batch of several sequences (where the one-launch kernel's
     longest sequences set its time); among them the segmented one when
-    gdn_prefill_seg_choose gave more than one segment."""
+    gdn_prefill_seg_choose gave more than one segment (not with the prologue)."""
     if path != "auto":
         return path
-    if x.io != "f32" and not prologue and (x.N * x.Hv * 8 <= 128 or x.N > 1):
-        return "seg" if segments > 1 else "split"
+    if x.io != "f32" and (x.N * x.Hv * 8 <= 128 or x.N > 1):
+        return "seg" if segments > 1 and not prologue else "split"
     return "pipe"
 
 
@@ -406,8 +408,11 @@ def main() -> int:
 
     segments = args.segments or gdn.prefill_seg_choose(x.N, x.T_tot, x.Hv, args.chunk)
     path = "kda" if args.kda else choose_path(x, args.path, args.prologue, segments)
-    if path in ("split", "seg") and (x.io == "f32" or pro):
-        print(f"bench.py: --path {path} takes bf16 or fp16 I/O without the prologue", file=sys.stderr)
+    if path in ("split", "seg") and x.io == "f32":
+        print(f"bench.py: --path {path} takes bf16 or fp16 I/O", file=sys.stderr)
+        return 2
+    if path == "seg" and pro:
+        print("bench.py: --path seg runs without the prologue", file=sys.stderr)
         return 2
     chunk = args.chunk if path in ("split", "seg") else 64
     if args.chunk != 64 and path not in ("split", "seg"):
@@ -425,7 +430,7 @@ def main() -> int:
                             out=s["o"], final_state=s["fs"], workspace=ws)
         elif path == "split":
             gdn.prefill_split(s["q"], s["k"], s["v"], s["g"], s["beta"], s["init"], s["cu"], chunk_size=chunk,
-                              out=s["o"], final_state=s["fs"], workspace=ws)
+                              out=s["o"], final_state=s["fs"], workspace=ws, prologue=pro)
         elif path == "seg":
             gdn.prefill_seg(s["q"], s["k"], s["v"], s["g"], s["beta"], s["init"], s["cu"], chunk_size=chunk,
                             segments=segments, out=s["o"], final_state=s["fs"], workspace=ws)
@@ -483,6 +488,9 @@ def main() -> int:
             kernel += "+gdn_seg_join_kernel+gdn_seg_fix_kernel"
             launch.update(kernel=kernel, segments=nseg, join_workgroups=x.N * x.Hv * 8,
                           fix_workgroups=(x.T_tot // chunk + x.N) * x.Hv)
+        if pro:
+            kernel += "(prologue)"
+            launch.update(kernel=kernel, prologue_flags=pro)
     else:
         plan = gdn.prefill_plan(x.N, x.Hv, IO_CODE[x.io])
         kernel = "gdn_prefill_pipe_kernel" if plan["threads_per_workgroup"] == 512 else "gdn_prefill_kernel"

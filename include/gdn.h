@@ -244,6 +244,21 @@ gdn_status gdn_prefill_split(const void *q, const void *k, const void *v,
                              void *o, float *final_state, void *stream);
 
 /*
+ * gdn_prefill_split_fused -- gdn_prefill_split with the input prologue applied in the map
+ * kernel's load path, as gdn_prefill_fused does for gdn_prefill: `prologue` is a bitwise
+ * or of gdn_prologue_flags (unknown bits return GDN_ERR_INVALID_ARGUMENT), and q, k, g,
+ * beta are then the raw inputs of the selected steps.  Workspace as for
+ * gdn_prefill_split.  With prologue = 0 it is gdn_prefill_split.
+ */
+gdn_status gdn_prefill_split_fused(const void *q, const void *k, const void *v,
+                                   const float *g, const float *beta,
+                                   const float *initial_state, const int32_t *cu_seqlens,
+                                   int32_t N, int32_t T_tot, int32_t Hk, int32_t Hv,
+                                   int32_t Dk, int32_t Dv, int32_t chunk_size, gdn_dtype io_dtype,
+                                   uint32_t prologue, void *workspace, size_t workspace_bytes,
+                                   void *o, float *final_state, void *stream);
+
+/*
  * gdn_prefill_seg -- gdn_prefill_split with each sequence's state recurrence split into
  * `segments` runs of whole chunks that execute at the same time: the Chunk-Seg-Seg
  * mapping ("Empowering Hybrid Attention Models on NPUs", section 4, Figure 7), in which

@@ -308,11 +308,17 @@ gdn_status gdn_prefill_split_workspace_size(int32_t N, int32_t T_tot, int32_t Hv
     return ok();
 }
 
-gdn_status gdn_prefill_split(const void *q, const void *k, const void *v, const float *g,
-                             const float *beta, const float *initial_state, const int32_t *cu_seqlens,
-                             int32_t N, int32_t T_tot, int32_t Hk, int32_t Hv, int32_t Dk, int32_t Dv,
-                             int32_t chunk_size, gdn_dtype io_dtype, void *workspace, size_t workspace_bytes,
-                             void *o, float *final_state, void *stream) {
+}  // extern "C"
+
+namespace {
+
+gdn_status split_impl(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                      const float *initial_state, const int32_t *cu_seqlens, int32_t N, int32_t T_tot, int32_t Hk,
+                      int32_t Hv, int32_t Dk, int32_t Dv, int32_t chunk_size, gdn_dtype io_dtype,
+                      uint32_t prologue, void *workspace, size_t workspace_bytes, void *o, float *final_state,
+                      void *stream) {
+    if (prologue & ~kPrologueAll)
+        return fail(GDN_ERR_INVALID_ARGUMENT, "prologue flags 0x%x include unknown bits", prologue);
     const gdn_status cs = check_prefill(q, k, v, g, beta, initial_state, cu_seqlens, N, T_tot, Hk, Hv, Dk,
                                         Dv, chunk_size, true, io_dtype, o, final_state, 1, workspace,
                                         workspace_bytes);
@@ -335,6 +341,7 @@ gdn_status gdn_prefill_split(const void *q, const void *k, const void *v, const 
     a.ws = static_cast<char *>(workspace);
     a.N = N; a.T_tot = T_tot; a.Hk = Hk; a.Hv = Hv;
     a.nslots = (int32_t)kda_slots(N, T_tot, chunk_size);
+    a.prologue = prologue;
     const hipStream_t hs = static_cast<hipStream_t>(stream);
     const bool f16 = io_dtype == GDN_F16;
     (void)hipGetLastError();
@@ -343,6 +350,28 @@ gdn_status gdn_prefill_split(const void *q, const void *k, const void *v, const 
     if (e != hipSuccess)
         return fail(GDN_ERR_DEVICE, "split prefill launch failed: %s", hipGetErrorString(e));
     return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+gdn_status gdn_prefill_split(const void *q, const void *k, const void *v, const float *g,
+                             const float *beta, const float *initial_state, const int32_t *cu_seqlens,
+                             int32_t N, int32_t T_tot, int32_t Hk, int32_t Hv, int32_t Dk, int32_t Dv,
+                             int32_t chunk_size, gdn_dtype io_dtype, void *workspace, size_t workspace_bytes,
+                             void *o, float *final_state, void *stream) {
+    return split_impl(q, k, v, g, beta, initial_state, cu_seqlens, N, T_tot, Hk, Hv, Dk, Dv, chunk_size, io_dtype, 0,
+                      workspace, workspace_bytes, o, final_state, stream);
+}
+
+gdn_status gdn_prefill_split_fused(const void *q, const void *k, const void *v, const float *g,
+                                   const float *beta, const float *initial_state, const int32_t *cu_seqlens,
+                                   int32_t N, int32_t T_tot, int32_t Hk, int32_t Hv, int32_t Dk, int32_t Dv,
+                                   int32_t chunk_size, gdn_dtype io_dtype, uint32_t prologue, void *workspace,
+                                   size_t workspace_bytes, void *o, float *final_state, void *stream) {
+    return split_impl(q, k, v, g, beta, initial_state, cu_seqlens, N, T_tot, Hk, Hv, Dk, Dv, chunk_size, io_dtype,
+                      prologue, workspace, workspace_bytes, o, final_state, stream);
 }
 
 // Segmented prefill: the split path's map, the chain in segments, the fix-up.

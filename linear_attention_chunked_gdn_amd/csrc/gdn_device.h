@@ -128,4 +128,34 @@ __device__ __forceinline__ void mma(f32x4 &acc, const Frag<float> &a, const Frag
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
+// Steps of the fused input prologue (GDN_PROLOGUE_* flags).
+constexpr float kLog2e = 1.4426950408889634f;
+// beta = sigmoid(x)
+__device__ __forceinline__ float prologue_sigmoid(float x) { return 1.f / (1.f + __builtin_amdgcn_exp2f(-x * kLog2e)); }
+// g = -softplus(x) = -(max(x, 0) + log(1 + e^-|x|))
+__device__ __forceinline__ float prologue_neg_softplus(float x) {
+    return -(fmaxf(x, 0.f) + __builtin_amdgcn_logf(1.f + __builtin_amdgcn_exp2f(-fabsf(x) * kLog2e)) / kLog2e);
+}
+// 1 / max(||x||_2, 1e-12) for the row whose 16-byte pieces (8 values each) the 16 lanes
+// of this lane's DPP row hold; every lane of the row gets the result (row rotations).
+// (`piece`: any 16-byte vector holding 8 values of type IO)
+template <typename IO, typename V>
+__device__ __forceinline__ float row_rnorm(const V &piece) {
+    typedef IO v8 __attribute__((ext_vector_type(8)));
+    static_assert(sizeof(V) == sizeof(v8), "a row piece is 8 values");
+    const v8 x = __builtin_bit_cast(v8, piece);
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float f = Cvt<IO>::to_f32(x[e]);
+        ss += f * f;
+    }
+    // row_ror:8, 4, 2, 1 (dpp_ctrl 0x120 + n)
+    ss += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(ss), 0x128, 0xF, 0xF, false));
+    ss += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(ss), 0x124, 0xF, 0xF, false));
+    ss += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(ss), 0x122, 0xF, 0xF, false));
+    ss += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(ss), 0x121, 0xF, 0xF, false));
+    return __builtin_amdgcn_rsqf(fmaxf(ss, 1e-24f));   // 1 / max(||x||, 1e-12)
+}
+
 }  // namespace gdn

@@ -54,6 +54,7 @@ struct KdaArgs {
     _Float16 *e;            // [T_tot, Hv, 128] outputs of the identity-state rows
     float *sseg;            // [N, Hv, nseg, 2, 128, 128] segment end states (S and X^T)
     _Float16 *sin16;        // [N, Hv, nseg, 128, 128] start states of segments 1 .. nseg - 1
+    uint32_t prologue;      // GDN_PROLOGUE_* flags of the scalar-gate map (0: none)
 };
 // Workspace tile of one chunk of C tokens and one value head (byte offsets; fp16 except
 // gl; row-major), with T = (I + A)^-1 and the decays of the chunk:

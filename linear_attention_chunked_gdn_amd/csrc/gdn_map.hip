@@ -26,6 +26,13 @@
 // exp(Gamma_r) * exp(-Gamma_s).  gamma and lambda are <= 1 for g <= 0, so the decayed
 // fp16 operands underflow only where the decay really is negligible.
 //
+// Fused input prologue (PRO, with the GDN_PROLOGUE_* flags of the call): q and k arrive
+// unnormalised and beta, g as logits.  The 16 lanes holding a q or k row reduce its L2
+// norm in fp32 from the registers it was loaded into; 1 / ||row|| is kept per token and
+// folded into the per-row factors applied anyway (the grams' decays, gamma on Qg and in
+// W's right-hand side, lambda on Kl), so q and k stay exact 16-bit MFMA operands.  The
+// gate scan applies beta = sigmoid(x) and g = -softplus(x).
+//
 // One workgroup = 4 wave64s per (chunk slot, value head).  One LDS region holds, in
 // turn, the k and q tiles (grams) and the right-hand sides diag(beta gamma) K and
 // diag(beta) V of the W/U products (from the k and v rows each thread keeps in registers
@@ -57,7 +64,7 @@ struct Cfg {
                                                  : (A_BYTES > RHS_BYTES ? A_BYTES : RHS_BYTES);
 };
 
-template <typename IO, int C>
+template <typename IO, int C, bool PRO>
 struct __align__(16) Smem {
     using F = Cfg<IO, C>;
     union {
@@ -79,14 +86,15 @@ struct __align__(16) Smem {
     float gam[C];             // exp(Gamma)
     float lam[C];             // exp(Gamma_last - Gamma)
     float beta[C];            // 0 past the chunk's end
+    float rn[PRO ? 2 : 1][PRO ? C : 1];   // prologue: 1 / ||k_t||, 1 / ||q_t|| (1 without the norm)
 };
 
 // Tile (I, J), I >= J, of A and P.  The product is taken transposed (K_J X_I^T), so the
 // lane holds row r = 16I + l16 and columns 16J + 4g4 .. 16J + 4g4 + 3; P goes to the
 // workspace as fp16, the beta-scaled A is returned (it goes to LDS once every wave is done
 // reading the k and q tiles it would overlay).
-template <typename IO, int C>
-__device__ __forceinline__ f32x4 gram_tile(const Smem<IO, C> &s, char *tile, int I, int J, int l16, int g4) {
+template <typename IO, int C, bool PRO>
+__device__ __forceinline__ f32x4 gram_tile(const Smem<IO, C, PRO> &s, char *tile, int I, int J, int l16, int g4) {
     f32x4 accA = zero4(), accP = zero4();
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
@@ -105,8 +113,13 @@ __device__ __forceinline__ f32x4 gram_tile(const Smem<IO, C> &s, char *tile, int
     for (int i = 0; i < 4; ++i) {
         const int c = c0 + i;
         const float d = c <= r ? __expf(gr - s.gcum[c]) : 0.f;
-        va[i] = c < r ? br * accA[i] * d : 0.f;
-        hp[i] = (hf)(accP[i] * d);
+        float da = d, dp = d;
+        if constexpr (PRO) {   // the rows' and columns' reciprocal norms
+            da *= s.rn[0][r] * s.rn[0][c];
+            dp *= s.rn[1][r] * s.rn[0][c];
+        }
+        va[i] = c < r ? br * accA[i] * da : 0.f;
+        hp[i] = (hf)(accP[i] * dp);
     }
     *reinterpret_cast<f16x4 *>(tile + Tile<C>::P + (r * C + c0) * 2) = hp;
     return va;
@@ -119,13 +132,13 @@ __device__ __forceinline__ void tile_of_job(int j, int &I, int &J) {
     J = j - I * (I + 1) / 2;
 }
 
-template <typename IO, int C>
+template <typename IO, int C, bool PRO>
 __global__ __launch_bounds__(THREADS) void gdn_map_kernel(const KdaArgs a) {
     using F = Cfg<IO, C>;
     constexpr int NT = F::NT, AS = F::AS;
     constexpr int NJOBS = NT * (NT + 1) / 2;
     constexpr int JPW = (NJOBS + 3) / 4;   // gram jobs per wave
-    __shared__ Smem<IO, C> s;
+    __shared__ Smem<IO, C, PRO> s;
     const int tid = threadIdx.x;
     const int lane = tid & 63, l16 = lane & 15, g4 = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -162,6 +175,18 @@ __global__ __launch_bounds__(THREADS) void gdn_map_kernel(const KdaArgs a) {
         *reinterpret_cast<v8 *>(&s.kq.K[row * XS + 8 * seg]) = kv[p];
         *reinterpret_cast<v8 *>(&s.kq.Q[row * XS + 8 * seg]) = qv[p];
     }
+    if constexpr (PRO) {   // the 16 lanes of a DPP row hold one token's k (q) row
+        const bool norm = a.prologue & GDN_PROLOGUE_QK_L2NORM;
+#pragma unroll
+        for (int p = 0; p < C / 16; ++p) {
+            const int idx = tid + THREADS * p, row = idx >> 4;
+            const float rk = norm ? row_rnorm<IO>(kv[p]) : 1.f, rq = norm ? row_rnorm<IO>(qv[p]) : 1.f;
+            if ((idx & 15) == 0) {
+                s.rn[0][row] = rk;
+                s.rn[1][row] = rq;
+            }
+        }
+    }
     float *const A = F::A_OWN ? s.Aown : s.Aov;
     // #1 Gate on wave 0, lane = token (64 at a time): inclusive prefix sum, flat past the
     // chunk's end
@@ -173,7 +198,11 @@ __global__ __launch_bounds__(THREADS) void gdn_map_kernel(const KdaArgs a) {
             const bool ok = t < nval;
             const size_t gi = (size_t)(tok0 + min(t, nval - 1)) * a.Hv + h;
             float x = ok ? a.g[gi] : 0.f;
-            const float b = ok ? a.beta[gi] : 0.f;
+            float b = ok ? a.beta[gi] : 0.f;
+            if constexpr (PRO) {
+                if (ok && (a.prologue & GDN_PROLOGUE_BETA_SIGMOID)) b = prologue_sigmoid(b);
+                if (ok && (a.prologue & GDN_PROLOGUE_G_SOFTPLUS)) x = prologue_neg_softplus(x);
+            }
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) {
                 const float y = __shfl_up(x, off, 64);
@@ -214,7 +243,7 @@ __global__ __launch_bounds__(THREADS) void gdn_map_kernel(const KdaArgs a) {
 #pragma unroll
         for (int p = 0; p < C / 16; ++p) {
             const int idx = tid + THREADS * p, row = idx >> 4;
-            const float gm = s.gam[row];
+            const float gm = PRO ? s.gam[row] * s.rn[1][row] : s.gam[row];
             f16x8 xq;
 #pragma unroll
             for (int e = 0; e < 8; ++e) xq[e] = (hf)(Cvt<IO>::to_f32(qv[p][e]) * gm);
@@ -229,7 +258,7 @@ __global__ __launch_bounds__(THREADS) void gdn_map_kernel(const KdaArgs a) {
             for (int i = 0; i < 16; ++i) {
                 const int t = 16 * tb + i;
                 const v2 kk = *reinterpret_cast<const v2 *>(&s.kq.K[t * XS + ch]);
-                const float lm = s.lam[t];
+                const float lm = PRO ? s.lam[t] * s.rn[0][t] : s.lam[t];
                 kl[0][i >> 3][i & 7] = (hf)(Cvt<IO>::to_f32(kk[0]) * lm);
                 kl[1][i >> 3][i & 7] = (hf)(Cvt<IO>::to_f32(kk[1]) * lm);
             }
@@ -283,7 +312,7 @@ __global__ __launch_bounds__(THREADS) void gdn_map_kernel(const KdaArgs a) {
 #pragma unroll
         for (int p = 0; p < C / 16; ++p) {
             const int idx = tid + THREADS * p, row = idx >> 4, seg = idx & 15;
-            const float bk = s.beta[row] * s.gam[row], bv = s.beta[row];
+            const float bk = s.beta[row] * s.gam[row] * (PRO ? s.rn[0][row] : 1.f), bv = s.beta[row];
             f16x8 xk, xv;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
@@ -342,7 +371,7 @@ __global__ __launch_bounds__(THREADS) void gdn_map_kernel(const KdaArgs a) {
 #pragma unroll
     for (int p = 0; p < C / 16; ++p) {
         const int idx = tid + THREADS * p, row = idx >> 4, seg = idx & 15;
-        const float bk = s.beta[row] * s.gam[row], bv = s.beta[row];
+        const float bk = s.beta[row] * s.gam[row] * (PRO ? s.rn[0][row] : 1.f), bv = s.beta[row];
         f16x8 xk, xv;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -363,10 +392,15 @@ __global__ __launch_bounds__(THREADS) void gdn_map_kernel(const KdaArgs a) {
 
 hipError_t launch_gdn_map(const KdaArgs &a, bool f16, int chunk, hipStream_t stream) {
     const dim3 grid((unsigned)a.nslots * (unsigned)a.Hv), block(gdnmap::THREADS);
-#define GDN_MAP_LAUNCH(C)                                                                          \
-    do {                                                                                           \
-        if (f16) hipLaunchKernelGGL((gdnmap::gdn_map_kernel<_Float16, C>), grid, block, 0, stream, a); \
-        else hipLaunchKernelGGL((gdnmap::gdn_map_kernel<__bf16, C>), grid, block, 0, stream, a);      \
+#define GDN_MAP_LAUNCH(C)                                                                                    \
+    do {                                                                                                     \
+        if (a.prologue) {                                                                                    \
+            if (f16) hipLaunchKernelGGL((gdnmap::gdn_map_kernel<_Float16, C, true>), grid, block, 0, stream, a); \
+            else hipLaunchKernelGGL((gdnmap::gdn_map_kernel<__bf16, C, true>), grid, block, 0, stream, a);      \
+        } else {                                                                                             \
+            if (f16) hipLaunchKernelGGL((gdnmap::gdn_map_kernel<_Float16, C, false>), grid, block, 0, stream, a); \
+            else hipLaunchKernelGGL((gdnmap::gdn_map_kernel<__bf16, C, false>), grid, block, 0, stream, a);      \
+        }                                                                                                    \
     } while (0)
     switch (chunk) {
         case 32: GDN_MAP_LAUNCH(32); break;

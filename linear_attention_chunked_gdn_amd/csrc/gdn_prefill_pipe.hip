@@ -224,26 +224,6 @@ struct StageQ {
     u32x4 q0, q1;
 };
 
-// 1 / max(||x||_2, 1e-12) for the row whose 16-byte pieces (8 values each) the 16 lanes
-// of this lane's DPP row hold; every lane of the row gets the result (row rotations).
-template <typename IO>
-__device__ __forceinline__ float row_rnorm(const u32x4 &piece) {
-    typedef IO v8 __attribute__((ext_vector_type(8)));
-    const v8 x = __builtin_bit_cast(v8, piece);
-    float ss = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const float f = Cvt<IO>::to_f32(x[e]);
-        ss += f * f;
-    }
-    // row_ror:8, 4, 2, 1 (dpp_ctrl 0x120 + n)
-    ss += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(ss), 0x128, 0xF, 0xF, false));
-    ss += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(ss), 0x124, 0xF, 0xF, false));
-    ss += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(ss), 0x122, 0xF, 0xF, false));
-    ss += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(ss), 0x121, 0xF, 0xF, false));
-    return __builtin_amdgcn_rsqf(fmaxf(ss, 1e-24f));   // 1 / max(||x||, 1e-12)
-}
-
 // Rows of the staged tiles a thread loads: k and q rows tid/16 and tid/16 + 32 (16-byte
 // segment tid%16); v row tid/8 (4-byte piece tid%8); g, beta row tid%64.  Every thread
 // loads and commits the same amount, with no branch around a load or an LDS write,
@@ -338,9 +318,8 @@ __device__ __forceinline__ void gate_scan(const Stage &st, Smem<IO> &s, int buf,
     float g = st.g, beta = st.b;
     if constexpr (PRO) {
         // beta = sigmoid(x); g = -softplus(x) = -(max(x, 0) + log(1 + e^-|x|))
-        if (pro & GDN_PROLOGUE_BETA_SIGMOID) beta = 1.f / (1.f + __builtin_amdgcn_exp2f(-beta * LOG2E));
-        if (pro & GDN_PROLOGUE_G_SOFTPLUS)
-            g = -(fmaxf(g, 0.f) + __builtin_amdgcn_logf(1.f + __builtin_amdgcn_exp2f(-fabsf(g) * LOG2E)) / LOG2E);
+        if (pro & GDN_PROLOGUE_BETA_SIGMOID) beta = prologue_sigmoid(beta);
+        if (pro & GDN_PROLOGUE_G_SOFTPLUS) g = prologue_neg_softplus(g);
     } else {
         (void)pro;
     }

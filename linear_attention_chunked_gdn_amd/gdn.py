@@ -71,6 +71,9 @@ def load_library(path: str = LIB_PATH):
     lib.gdn_prefill_split_workspace_size.restype = ctypes.c_int
     lib.gdn_prefill_split.argtypes = lib.gdn_kda_prefill.argtypes
     lib.gdn_prefill_split.restype = ctypes.c_int
+    lib.gdn_prefill_split_fused.argtypes = [vp, vp, vp, fp, fp, fp, ip, i32, i32, i32, i32, i32, i32, i32,
+                                            ctypes.c_int, ctypes.c_uint32, vp, ctypes.c_size_t, vp, fp, vp]
+    lib.gdn_prefill_split_fused.restype = ctypes.c_int
     lib.gdn_prefill_seg_workspace_size.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(ctypes.c_size_t)]
     lib.gdn_prefill_seg_workspace_size.restype = ctypes.c_int
     lib.gdn_prefill_seg_choose.argtypes = [i32, i32, i32, i32, p32]
@@ -228,10 +231,12 @@ def kda_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tens
 
 
 def _prefill_ws(fn: str, size_fn, per_channel: bool, q, k, v, g, beta, initial_state, cu_seqlens,
-                chunk_size, output_final_state, out, final_state, workspace, lib, extra=()):
+                chunk_size, output_final_state, out, final_state, workspace, lib, extra=(),
+                extra_after_io: bool = False):
     """The entry points that take a caller-owned workspace (gdn_kda_prefill, gdn_prefill_split,
-    gdn_prefill_seg); ``extra`` holds the integer arguments after chunk_size (the segment
-    count), which size_fn takes too."""
+    gdn_prefill_split_fused, gdn_prefill_seg); ``extra`` holds further integer arguments,
+    which size_fn takes too: after chunk_size (the segment count), or after io_dtype with
+    extra_after_io (the prologue flags)."""
     lib = lib or load_library()
     dev = q.device
     if dev.type != "cuda":
@@ -263,8 +268,9 @@ def _prefill_ws(fn: str, size_fn, per_channel: bool, q, k, v, g, beta, initial_s
         raise ValueError("workspace must be a contiguous uint8 tensor on " + str(dev))
     with torch.cuda.device(dev):
         stream = torch.cuda.current_stream(dev).cuda_stream
+        pre, post = ((), extra) if extra_after_io else (extra, ())
         st = getattr(lib, fn)(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
-                              _ptr(cu_seqlens), N, T, Hk, Hv, Dk, Dv, chunk_size, *extra, io, _ptr(workspace),
+                              _ptr(cu_seqlens), N, T, Hk, Hv, Dk, Dv, chunk_size, *pre, io, *post, _ptr(workspace),
                               workspace.numel(), _ptr(out), _ptr(final_state), ctypes.c_void_p(stream))
     _check(lib, st, fn)
     return out, final_state
@@ -284,10 +290,16 @@ def prefill_split(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
                   cu_seqlens: Optional[torch.Tensor] = None, chunk_size: int = CHUNK,
                   output_final_state: bool = True, out: Optional[torch.Tensor] = None,
                   final_state: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-                  lib=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+                  prologue: int = 0, lib=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """``prefill`` in two launches (gdn_prefill_split): q, k, v bf16 or fp16; ``workspace``
     (a uint8 device tensor of at least ``prefill_split_workspace_size`` bytes) is allocated
-    here when not given."""
+    here when not given.  A nonzero ``prologue`` (PROLOGUE_* flags) calls
+    gdn_prefill_split_fused: q, k, g, beta are then the raw inputs of those steps."""
+    if prologue:
+        size_fn = lambda N, T, Hv, C, _p, lib=None: prefill_split_workspace_size(N, T, Hv, C, lib=lib)  # noqa: E731
+        return _prefill_ws("gdn_prefill_split_fused", size_fn, False, q, k, v, g, beta, initial_state,
+                           cu_seqlens, chunk_size, output_final_state, out, final_state, workspace, lib,
+                           extra=(int(prologue),), extra_after_io=True)
     return _prefill_ws("gdn_prefill_split", prefill_split_workspace_size, False, q, k, v, g, beta,
                        initial_state, cu_seqlens, chunk_size, output_final_state, out, final_state,
                        workspace, lib)

@@ -33,7 +33,8 @@ def test_header_declares_the_boundary():
         ["gdn_prefill", "gdn_decode_step", "gdn_prefill_plan", "gdn_status_string", "gdn_last_error",
          "gdn_kda_workspace_size", "gdn_kda_prefill", "gdn_kda_decode_step", "gdn_prefill_fused",
          "gdn_decode_step_fused", "gdn_prefill_split", "gdn_prefill_split_workspace_size",
-         "gdn_prefill_seg", "gdn_prefill_seg_workspace_size", "gdn_prefill_seg_choose"])
+         "gdn_prefill_seg", "gdn_prefill_seg_workspace_size", "gdn_prefill_seg_choose",
+         "gdn_prefill_split_fused"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -299,3 +300,30 @@ def test_seg_choose_needs_a_device(lib):
         assert st == 0 and K.value >= 1
     else:
         assert st == 3 and b"compute-unit" in lib.gdn_last_error()
+
+
+def _split_fused(lib, pro, **over):
+    a = dict(q=0x100000, k=0x200000, v=0x300000, g=0x400000, beta=0x500000, s0=None, cu=None,
+             N=1, T=10, Hk=2, Hv=4, Dk=128, Dv=128, C=64, io=1, ws=0x1000000, wsb=1 << 24,
+             o=0x600000, fs=None)
+    a.update(over)
+    p = lambda x: None if x is None else ctypes.c_void_p(x)  # noqa: E731
+    return lib.gdn_prefill_split_fused(p(a["q"]), p(a["k"]), p(a["v"]), p(a["g"]), p(a["beta"]), p(a["s0"]),
+                                       p(a["cu"]), a["N"], a["T"], a["Hk"], a["Hv"], a["Dk"], a["Dv"], a["C"],
+                                       a["io"], pro, p(a["ws"]), a["wsb"], p(a["o"]), p(a["fs"]), None)
+
+
+@pytest.mark.parametrize("pro,over,status,msg", [
+    (8, {}, 1, "unknown bits"),
+    (7, dict(io=0), 2, "bf16 or fp16"),
+    (7, dict(C=16), 2, "chunk_size"),
+    (7, dict(wsb=1000), 1, "smaller than"),
+    (7, dict(o=0x300000), 1, "overlaps"),
+])
+def test_split_fused_rejects(lib, pro, over, status, msg):
+    assert _split_fused(lib, pro, **over) == status
+    assert msg in lib.gdn_last_error().decode()
+
+
+def test_split_fused_nothing_to_do_is_ok(lib):
+    assert _split_fused(lib, 7, q=None, k=None, v=None, g=None, beta=None, o=None, ws=None, wsb=0, T=0) == 0

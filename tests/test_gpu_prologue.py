@@ -46,10 +46,10 @@ def _oracle(x, flags):
     return oracle.recurrent(q, k, x.v, g, b, x.initial_state, x.cu_seqlens)
 
 
-def _run(x, flags):
+def _run(x, flags, split=False):
     d = to_device(x, DEV)
-    o, fs = gdn.prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["initial_state"], d["cu_seqlens"],
-                        prologue=flags)
+    fn = gdn.prefill_split if split else gdn.prefill
+    o, fs = fn(d["q"], d["k"], d["v"], d["g"], d["beta"], d["initial_state"], d["cu_seqlens"], prologue=flags)
     torch.cuda.synchronize()
     return o, fs
 
@@ -119,3 +119,66 @@ def test_decode_prologue(io):
     ro, rs = oracle.decode_step(q, k, x.v, g, b, x.initial_state)
     check(f"decode o ({io})", to_f64(o), ro, io)
     check(f"decode state ({io})", to_f64(st), rs, io)
+
+
+# the same steps in the two-launch path's map kernel (gdn_prefill_split_fused)
+
+@pytest.mark.parametrize("io", ["bf16", "f16"])
+@pytest.mark.parametrize("case", range(len(SMALL)))
+def test_split_prologue_all_steps_small_shapes(io, case):
+    lengths, Hk, Hv, init_std = SMALL[case]
+    x = inputs.make_custom(3400 + case, lengths, Hk, Hv, io=io, init_std=init_std, g_shift=0.5, raw=True)
+    print(f"\nsplit: lengths={lengths} Hk={Hk} Hv={Hv} io={io}", flush=True)
+    o, fs = _run(x, gdn.PROLOGUE_ALL, split=True)
+    ro, rf = _oracle(x, gdn.PROLOGUE_ALL)
+    check("o", to_f64(o), ro, io)
+    check("final_state", to_f64(fs), rf, io)
+
+
+@pytest.mark.parametrize("flags", [1, 2, 4, 3, 6])
+def test_split_prologue_flag_subsets(flags):
+    raw = inputs.make_custom(3500 + flags, [150, 70], 2, 2, io="bf16", init_std=0.2, g_shift=1.0, raw=True)
+    x = _host_steps(raw, flags)
+    o, fs = _run(x, flags, split=True)
+    ro, rf = _oracle(x, flags)
+    check("o", to_f64(o), ro, "bf16")
+    check("final_state", to_f64(fs), rf, "bf16")
+
+
+@pytest.mark.parametrize("chunk", [32, 128])
+def test_split_prologue_other_chunk_sizes(chunk):
+    x = inputs.make_custom(3600 + chunk, [200, 0, 129], 2, 4, io="bf16", init_std=0.1, g_shift=0.5, raw=True)
+    d = to_device(x, DEV)
+    o, fs = gdn.prefill_split(d["q"], d["k"], d["v"], d["g"], d["beta"], d["initial_state"], d["cu_seqlens"],
+                              chunk_size=chunk, prologue=gdn.PROLOGUE_ALL)
+    torch.cuda.synchronize()
+    ro, rf = _oracle(x, gdn.PROLOGUE_ALL)
+    check("o", to_f64(o), ro, "bf16")
+    check("final_state", to_f64(fs), rf, "bf16")
+
+
+def test_split_prologue_headline_workload():
+    x = inputs.make_workload(1, raw=True)
+    o, fs = _run(x, gdn.PROLOGUE_ALL, split=True)
+    ro, rf = _oracle(x, gdn.PROLOGUE_ALL)
+    check("o", to_f64(o), ro, x.io)
+    check("final_state", to_f64(fs), rf, x.io)
+
+
+def test_split_prologue_unnormalised_scale_and_strong_decay():
+    x = inputs.make_custom(3700, [300, 5], 1, 2, io="bf16", init_std=0.5, g_shift=4.0, raw=True)
+    x.q = inputs.round_to_bf16(x.q * np.float32(40.0))
+    x.k = inputs.round_to_bf16(x.k * np.float32(0.05))
+    o, fs = _run(x, gdn.PROLOGUE_ALL, split=True)
+    ro, rf = _oracle(x, gdn.PROLOGUE_ALL)
+    check("o", to_f64(o), ro, "bf16")
+    check("final_state", to_f64(fs), rf, "bf16")
+
+
+def test_split_prologue_off_is_the_split_path():
+    x = inputs.make_custom(3800, [129], 1, 2, io="bf16", init_std=0.1)
+    d = to_device(x, DEV)
+    a = gdn.prefill_split(d["q"], d["k"], d["v"], d["g"], d["beta"], d["initial_state"])
+    b = gdn.prefill_split(d["q"], d["k"], d["v"], d["g"], d["beta"], d["initial_state"], prologue=0)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
