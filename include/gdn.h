@@ -301,6 +301,21 @@ gdn_status gdn_prefill_seg(const void *q, const void *k, const void *v,
                            void *o, float *final_state, void *stream);
 
 /*
+ * gdn_kda_prefill_seg -- gdn_kda_prefill with each sequence's recurrence run as
+ * `segments` concurrent segments, as gdn_prefill_seg does for the scalar gate (the chunk
+ * state map with a per-key-channel decay is affine too, S -> S (Diag(gl) - W^T Kl) +
+ * U^T Kl).  Arguments as for gdn_kda_prefill plus `segments`; chunk_size 64; workspace at
+ * least gdn_prefill_seg_workspace_size(N, T_tot, Hv, 64, segments) bytes.
+ */
+gdn_status gdn_kda_prefill_seg(const void *q, const void *k, const void *v,
+                               const float *g, const float *beta,
+                               const float *initial_state, const int32_t *cu_seqlens,
+                               int32_t N, int32_t T_tot, int32_t Hk, int32_t Hv,
+                               int32_t Dk, int32_t Dv, int32_t chunk_size, int32_t segments,
+                               gdn_dtype io_dtype, void *workspace, size_t workspace_bytes,
+                               void *o, float *final_state, void *stream);
+
+/*
  * gdn_prefill_plan -- the launch shape gdn_prefill would use for these sizes,
  * without launching anything: the width of the value-channel slice each workgroup
  * owns (the column-wise split of S, "Empowering Hybrid Attention Models on NPUs",

@@ -412,17 +412,23 @@ gdn_status gdn_prefill_seg_choose(int32_t N, int32_t T_tot, int32_t Hv, int32_t 
     return ok();
 }
 
-gdn_status gdn_prefill_seg(const void *q, const void *k, const void *v, const float *g,
-                           const float *beta, const float *initial_state, const int32_t *cu_seqlens,
-                           int32_t N, int32_t T_tot, int32_t Hk, int32_t Hv, int32_t Dk, int32_t Dv,
-                           int32_t chunk_size, int32_t segments, gdn_dtype io_dtype, void *workspace,
-                           size_t workspace_bytes, void *o, float *final_state, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// The segmented prefill with the scalar gate (g [T_tot, Hv]) or a per-key-channel one
+// (g [T_tot, Hv, Dk], 64-token chunks): the two differ only in the map kernel.
+gdn_status seg_impl(const char *fn, bool per_channel, const void *q, const void *k, const void *v, const float *g,
+                    const float *beta, const float *initial_state, const int32_t *cu_seqlens, int32_t N,
+                    int32_t T_tot, int32_t Hk, int32_t Hv, int32_t Dk, int32_t Dv, int32_t chunk_size,
+                    int32_t segments, gdn_dtype io_dtype, void *workspace, size_t workspace_bytes, void *o,
+                    float *final_state, void *stream) {
     const gdn_status cs = check_prefill(q, k, v, g, beta, initial_state, cu_seqlens, N, T_tot, Hk, Hv, Dk,
-                                        Dv, chunk_size, true, io_dtype, o, final_state, 1, workspace,
-                                        workspace_bytes);
+                                        Dv, chunk_size, !per_channel, io_dtype, o, final_state,
+                                        per_channel ? (size_t)kD : 1, workspace, workspace_bytes);
     if (cs != GDN_OK) return cs;
     if (io_dtype == GDN_F32)
-        return fail(GDN_ERR_UNSUPPORTED, "gdn_prefill_seg takes bf16 or fp16 q, k, v, o");
+        return fail(GDN_ERR_UNSUPPORTED, "%s takes bf16 or fp16 q, k, v, o", fn);
     size_t need = 0;
     const gdn_status ws_st = gdn_prefill_seg_workspace_size(N, T_tot, Hv, chunk_size, segments, &need);
     if (ws_st != GDN_OK) return ws_st;
@@ -458,7 +464,7 @@ gdn_status gdn_prefill_seg(const void *q, const void *k, const void *v, const fl
         a.sseg = reinterpret_cast<float *>(a.ws + off);
         off += (size_t)N * Hv * segments * 2 * kD * kD * sizeof(float);
         a.sin16 = reinterpret_cast<_Float16 *>(a.ws + off);
-        e = gdn::launch_gdn_map(a, f16, chunk_size, hs);
+        e = per_channel ? gdn::launch_kda_map(a, f16, hs) : gdn::launch_gdn_map(a, f16, chunk_size, hs);
         if (e == hipSuccess) e = gdn::launch_seg_chain(a, f16, chunk_size, hs);
         if (e == hipSuccess) e = gdn::launch_seg_join(a, hs);
         if (e == hipSuccess) e = gdn::launch_seg_fix(a, f16, chunk_size, hs);
@@ -466,6 +472,28 @@ gdn_status gdn_prefill_seg(const void *q, const void *k, const void *v, const fl
     if (e != hipSuccess)
         return fail(GDN_ERR_DEVICE, "segmented prefill launch failed: %s", hipGetErrorString(e));
     return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+gdn_status gdn_prefill_seg(const void *q, const void *k, const void *v, const float *g,
+                           const float *beta, const float *initial_state, const int32_t *cu_seqlens,
+                           int32_t N, int32_t T_tot, int32_t Hk, int32_t Hv, int32_t Dk, int32_t Dv,
+                           int32_t chunk_size, int32_t segments, gdn_dtype io_dtype, void *workspace,
+                           size_t workspace_bytes, void *o, float *final_state, void *stream) {
+    return seg_impl("gdn_prefill_seg", false, q, k, v, g, beta, initial_state, cu_seqlens, N, T_tot, Hk, Hv, Dk,
+                    Dv, chunk_size, segments, io_dtype, workspace, workspace_bytes, o, final_state, stream);
+}
+
+gdn_status gdn_kda_prefill_seg(const void *q, const void *k, const void *v, const float *g,
+                               const float *beta, const float *initial_state, const int32_t *cu_seqlens,
+                               int32_t N, int32_t T_tot, int32_t Hk, int32_t Hv, int32_t Dk, int32_t Dv,
+                               int32_t chunk_size, int32_t segments, gdn_dtype io_dtype, void *workspace,
+                               size_t workspace_bytes, void *o, float *final_state, void *stream) {
+    return seg_impl("gdn_kda_prefill_seg", true, q, k, v, g, beta, initial_state, cu_seqlens, N, T_tot, Hk, Hv,
+                    Dk, Dv, chunk_size, segments, io_dtype, workspace, workspace_bytes, o, final_state, stream);
 }
 
 }  // extern "C"

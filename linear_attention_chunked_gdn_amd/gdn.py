@@ -81,6 +81,8 @@ def load_library(path: str = LIB_PATH):
     lib.gdn_prefill_seg.argtypes = [vp, vp, vp, fp, fp, fp, ip, i32, i32, i32, i32, i32, i32, i32, i32,
                                     ctypes.c_int, vp, ctypes.c_size_t, vp, fp, vp]
     lib.gdn_prefill_seg.restype = ctypes.c_int
+    lib.gdn_kda_prefill_seg.argtypes = lib.gdn_prefill_seg.argtypes
+    lib.gdn_kda_prefill_seg.restype = ctypes.c_int
     lib.gdn_kda_decode_step.argtypes = lib.gdn_decode_step.argtypes
     lib.gdn_kda_decode_step.restype = ctypes.c_int
     lib.gdn_status_string.argtypes = [ctypes.c_int]
@@ -339,6 +341,25 @@ def prefill_seg(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tens
             segments = prefill_seg_choose(N, q.shape[0], v.shape[1], chunk_size, lib=lib)
     return _prefill_ws("gdn_prefill_seg", prefill_seg_workspace_size, False, q, k, v, g, beta,
                        initial_state, cu_seqlens, chunk_size, output_final_state, out, final_state,
+                       workspace, lib, extra=(int(segments),))
+
+
+def kda_prefill_seg(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                    beta: torch.Tensor, initial_state: Optional[torch.Tensor] = None,
+                    cu_seqlens: Optional[torch.Tensor] = None, segments: Optional[int] = None,
+                    output_final_state: bool = True, out: Optional[torch.Tensor] = None,
+                    final_state: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                    lib=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """``kda_prefill`` with each sequence's recurrence run as ``segments`` concurrent
+    segments (gdn_kda_prefill_seg; g: [T, Hv, 128]); ``segments`` defaults to
+    ``prefill_seg_choose``'s count."""
+    lib = lib or load_library()
+    if segments is None:
+        N = 1 if cu_seqlens is None else cu_seqlens.shape[0] - 1
+        with torch.cuda.device(q.device):
+            segments = prefill_seg_choose(N, q.shape[0], v.shape[1], CHUNK, lib=lib)
+    return _prefill_ws("gdn_kda_prefill_seg", prefill_seg_workspace_size, True, q, k, v, g, beta,
+                       initial_state, cu_seqlens, CHUNK, output_final_state, out, final_state,
                        workspace, lib, extra=(int(segments),))
 
 

@@ -34,7 +34,7 @@ def test_header_declares_the_boundary():
          "gdn_kda_workspace_size", "gdn_kda_prefill", "gdn_kda_decode_step", "gdn_prefill_fused",
          "gdn_decode_step_fused", "gdn_prefill_split", "gdn_prefill_split_workspace_size",
          "gdn_prefill_seg", "gdn_prefill_seg_workspace_size", "gdn_prefill_seg_choose",
-         "gdn_prefill_split_fused"])
+         "gdn_prefill_split_fused", "gdn_kda_prefill_seg"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -327,3 +327,22 @@ def test_split_fused_rejects(lib, pro, over, status, msg):
 
 def test_split_fused_nothing_to_do_is_ok(lib):
     assert _split_fused(lib, 7, q=None, k=None, v=None, g=None, beta=None, o=None, ws=None, wsb=0, T=0) == 0
+
+
+@pytest.mark.parametrize("over,status,msg", [
+    (dict(C=32), 2, "chunk_size"),
+    (dict(g=0x400008), 1, "g must be 16-byte aligned"),
+    (dict(io=0), 2, "bf16 or fp16"),
+    (dict(wsb=1 << 18), 1, "smaller than"),
+])
+def test_kda_seg_rejects(lib, over, status, msg):
+    a = dict(q=0x100000, k=0x200000, v=0x300000, g=0x400000, beta=0x500000, s0=None, cu=None,
+             N=1, T=10, Hk=2, Hv=4, Dk=128, Dv=128, C=64, io=1, ws=0x1000000, wsb=1 << 24,
+             o=0x600000, fs=None)
+    a.update(over)
+    p = lambda x: None if x is None else ctypes.c_void_p(x)  # noqa: E731
+    st = lib.gdn_kda_prefill_seg(p(a["q"]), p(a["k"]), p(a["v"]), p(a["g"]), p(a["beta"]), p(a["s0"]),
+                                 p(a["cu"]), a["N"], a["T"], a["Hk"], a["Hv"], a["Dk"], a["Dv"], a["C"], 2,
+                                 a["io"], p(a["ws"]), a["wsb"], p(a["o"]), p(a["fs"]), None)
+    assert st == status
+    assert msg in lib.gdn_last_error().decode()

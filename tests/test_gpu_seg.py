@@ -168,3 +168,29 @@ def test_seg_in_a_hip_graph():
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(o, o_ref) and torch.equal(fs, f_ref), f"replay {i} differs"
+
+
+@pytest.mark.parametrize("K", [2, 4])
+@pytest.mark.parametrize("io", ["bf16", "f16"])
+def test_kda_seg_shapes(K, io):
+    # the per-key-channel decay through the same segments
+    for case, (lengths, Hk, Hv, init_std) in enumerate([([700], 1, 2, 0.2), ([0, 130, 1, 64, 77], 1, 2, 0.1),
+                                                          ([300, 5], 2, 2, 0.5)]):
+        x = inputs.make_custom(6800 + case, lengths, Hk, Hv, io=io, init_std=init_std, per_channel=True,
+                               g_shift=0.5 * case, name=f"kda_seg{case}")
+        print(f"\n{x.name}: lengths={lengths} Hk={Hk} Hv={Hv} io={io} segments={K}", flush=True)
+        d = to_device(x, DEV)
+        o, fs = gdn.kda_prefill_seg(*_args(d), segments=K)
+        torch.cuda.synchronize()
+        ro, rf = oracle.recurrent(x.q, x.k, x.v, x.g, x.beta, x.initial_state, x.cu_seqlens)
+        check("o", to_f64(o), ro, x.io)
+        check("final_state", to_f64(fs), rf, x.io)
+
+
+def test_kda_seg_one_segment_is_kda_prefill():
+    x = inputs.make_custom(6900, [333, 0, 90], 2, 4, io="bf16", init_std=0.2, per_channel=True)
+    d = to_device(x, DEV)
+    o1, f1 = gdn.kda_prefill_seg(*_args(d), segments=1)
+    o2, f2 = gdn.kda_prefill(*_args(d))
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(f1, f2)
