@@ -52,6 +52,7 @@ T*Hv*Dk*4 bytes and the grams are per value head (see `algorithmic_bytes`,
 from __future__ import annotations
 
 import argparse
+import gc
 import csv
 import hashlib
 import json
@@ -443,6 +444,10 @@ def main() -> int:
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # no Python garbage collection inside the timed region: a collection pass while the
+    # GPU has no queued work (right after the synchronisation) would be timed as GPU time
+    gc.collect()
+    gc.disable()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0.record(stream)
@@ -451,6 +456,7 @@ def main() -> int:
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    gc.enable()
     gpu_ms = ev0.elapsed_time(ev1)
     ms_per_step = gpu_ms / args.steps
     tokens = x.T_tot
