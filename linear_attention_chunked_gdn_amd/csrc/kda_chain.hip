@@ -297,13 +297,26 @@ __device__ __forceinline__ void chain_update(Smem<C> &s, int W, int l16, int g4,
     }
 }
 
+// The sequence of rank r when the N <= 64 sequences of cu are ordered by decreasing length
+// (ties by index), by one wave: lane i counts the sequences ahead of sequence i.
+__device__ __forceinline__ int longest_first(const int32_t *cu, int N, int r, int lane) {
+    const int len = lane < N ? cu[lane + 1] - cu[lane] : -1;
+    int rank = 0;
+    for (int j = 0; j < N; ++j) {
+        const int lj = __shfl(len, j, 64);
+        rank += (lj > len || (lj == len && j < lane)) ? 1 : 0;
+    }
+    const unsigned long long hit = __ballot(lane < N && rank == r);
+    return hit ? __builtin_ctzll(hit) : r;
+}
+
 // SEG: the segment mode of the Chunk-Seg-Seg mapping ("Empowering Hybrid Attention Models on
 // NPUs", section 4, Figure 7): each sequence's chunks split into a.nseg runs.  Per
 // (sequence, head), segment 0 has the 8 value slices, from the initial state; every later
 // segment has 8 value slices from a zero state and 8 slices of identity rows (state X = I
 // and no U term), whose outputs E and end state X carry the segment's dependence on its
 // real start state.  Segment 0 stores its outputs to o; later segments store theirs as
-// fp32 to a.o0 (value rows) or fp16 to a.e (identity rows); end states go to a.sseg (X
+// fp16 to a.o0 (value rows) or a.e (identity rows); end states go to a.sseg (X
 // transposed).  gdn_seg.hip joins them.
 template <typename IO, int C, bool SEG>
 __global__ __launch_bounds__(THREADS) void kda_chain_kernel(const KdaArgs a) {
@@ -340,6 +353,10 @@ __global__ __launch_bounds__(THREADS) void kda_chain_kernel(const KdaArgs a) {
         slice = item % NSL;
         h = (item / NSL) % a.Hv;
         n = item / (NSL * a.Hv);
+        // A packed batch of up to 64 sequences runs longest first, so that the longest
+        // chains start in the first round of workgroups: item rank n takes the sequence
+        // with the n-th most tokens (ties by index).
+        if (a.cu && a.N > 1 && a.N <= 64) n = longest_first(a.cu, a.N, n, lane);
     }
     Work wk;
     wk.h = h;
