@@ -33,12 +33,15 @@
 // W's right-hand side, lambda on Kl), so q and k stay exact 16-bit MFMA operands.  The
 // gate scan applies beta = sigmoid(x) and g = -softplus(x).
 //
-// One workgroup = 4 wave64s per (chunk slot, value head).  One LDS region holds, in
-// turn, the k and q tiles (grams) and the right-hand sides diag(beta gamma) K and
-// diag(beta) V of the W/U products (from the k and v rows each thread keeps in registers
-// since its first load); A and T have their own.  At C = 128 that does not fit, and A
-// goes over the k and q tiles too, held in registers until every wave is done with them.
-// LDS is 77 KB at C = 64 (two workgroups per CU) and 146 KB at C = 128.
+// One workgroup = 4 wave64s per (chunk slot, value head).  One LDS region is reused
+// three times: the k and q tiles (grams); then M, T in its lower triangle and A^T in its
+// strict upper one (A is held in registers until every wave is done with k and q); then
+// T in fp16 and the right-hand sides diag(beta gamma) K and diag(beta) V of the W/U
+// products, from the k and v rows each thread keeps in registers since its first load.
+// The map moves 122 KB per item and waits mostly on memory, so the item count per CU
+// decides its time: at C = 64 (37.9 KB, the right-hand sides one after the other, at
+// most 128 VGPRs) four workgroups fit on a CU, one round for 1,024 items on 256 CUs.
+// C = 32 takes 19 KB, C = 128 105 KB.
 #include "gdn_device.h"
 #include "gdn_launch.h"
 #include "gdn_wy.h"
@@ -55,38 +58,48 @@ constexpr int XS = DK + 16;   // 16-bit row stride of the k and q tiles (288 B)
 template <typename IO, int C>
 struct Cfg {
     static constexpr int NT = C / 16;            // 16-token tiles
-    static constexpr int AS = C + 8;             // fp32 row stride of A and T
+    static constexpr int AS = C + 8;             // fp32 row stride of M (T and A^T)
+    static constexpr int TS = C + 8;             // fp16 row stride of T for the W/U products
     static constexpr int KQ_BYTES = 2 * C * XS * (int)sizeof(IO);
-    static constexpr int A_BYTES = C * AS * 4;
-    static constexpr int RHS_BYTES = 2 * C * WY_S * 2;
-    static constexpr bool A_OWN = C <= 64;       // A in its own region (else over k, q)
-    static constexpr int R1 = KQ_BYTES > A_BYTES ? (KQ_BYTES > RHS_BYTES ? KQ_BYTES : RHS_BYTES)
-                                                 : (A_BYTES > RHS_BYTES ? A_BYTES : RHS_BYTES);
+    static constexpr int M_BYTES = C * AS * 4;
+    static constexpr int Y_OFF = M_BYTES;                 // after M
+    static constexpr int RHS_BYTES = C * WY_S * 2;
+    // At C = 64 the right-hand sides take turns in one buffer, which keeps the workgroup
+    // under a quarter of the CU's LDS (four per CU); elsewhere that gains no workgroup
+    // and both are staged at once.
+    static constexpr bool TWO_PASS = C == 64;
+    static constexpr int RHS_ALL = TWO_PASS ? RHS_BYTES : 2 * RHS_BYTES;
+    static constexpr int T16_OFF = RHS_ALL > M_BYTES ? RHS_ALL : M_BYTES;   // past M and the RHS
+    static constexpr int T16_BYTES = C * TS * 2;
+    static constexpr int R0 = KQ_BYTES > Y_OFF + 4096 ? (KQ_BYTES > T16_OFF + T16_BYTES ? KQ_BYTES : T16_OFF + T16_BYTES)
+                                                      : (Y_OFF + 4096 > T16_OFF + T16_BYTES ? Y_OFF + 4096 : T16_OFF + T16_BYTES);
 };
 
+// One LDS region, overlaid in turn by
+//   the k and q tiles (grams);
+//   M, fp32: T = (I + A)^-1 in its lower triangle (diagonal included) and the beta-scaled
+//     A transposed in its strict upper triangle (A is strictly lower, so the two never
+//     meet), then the solve's per-wave partial products Y;
+//   T in fp16, placed past M so that it is written while M is read, and the right-hand
+//     sides of the W/U products, diag(beta gamma) K and diag(beta) V (at C = 64 one at a
+//     time).
 template <typename IO, int C, bool PRO>
 struct __align__(16) Smem {
     using F = Cfg<IO, C>;
-    union {
-        struct {
-            IO K[C * XS];     // k rows of the chunk (rows past its end repeat the last)
-            IO Q[C * XS];
-        } kq;
-        float Aov[C * F::AS]; // A over k, q (C = 128, once the grams are done)
-        struct {              // once the solve is done: diag(beta gamma) K, diag(beta) V
-            hf Kb[C * WY_S];
-            hf Vb[C * WY_S];
-        } wy;
-        char bytes[F::R1];
-    };
-    float Aown[F::A_OWN ? C * F::AS : 1];   // beta-scaled, strictly lower (C <= 64)
-    float T[C * F::AS];       // (I + A)^-1
-    float Y[4][16 * 16];      // partial products of the block solve, one per wave
+    __align__(16) char r0[F::R0];
     float gcum[C];            // Gamma (flat past the chunk's end)
     float gam[C];             // exp(Gamma)
     float lam[C];             // exp(Gamma_last - Gamma)
     float beta[C];            // 0 past the chunk's end
     float rn[PRO ? 2 : 1][PRO ? C : 1];   // prologue: 1 / ||k_t||, 1 / ||q_t|| (1 without the norm)
+    __device__ IO *K() { return reinterpret_cast<IO *>(r0); }
+    __device__ IO *Q() { return reinterpret_cast<IO *>(r0) + C * XS; }
+    __device__ const IO *K() const { return reinterpret_cast<const IO *>(r0); }
+    __device__ const IO *Q() const { return reinterpret_cast<const IO *>(r0) + C * XS; }
+    __device__ float *M() { return reinterpret_cast<float *>(r0); }
+    __device__ float *Y(int w) { return reinterpret_cast<float *>(r0 + F::Y_OFF) + 256 * w; }
+    __device__ hf *T16() { return reinterpret_cast<hf *>(r0 + F::T16_OFF); }
+    __device__ hf *RHS() { return reinterpret_cast<hf *>(r0); }
 };
 
 // Tile (I, J), I >= J, of A and P.  The product is taken transposed (K_J X_I^T), so the
@@ -99,9 +112,9 @@ __device__ __forceinline__ f32x4 gram_tile(const Smem<IO, C, PRO> &s, char *tile
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
         Frag<IO> kj, ki, qi;
-        kj.load8(s.kq.K + (16 * J + l16) * XS + 32 * kb + 8 * g4);
-        ki.load8(s.kq.K + (16 * I + l16) * XS + 32 * kb + 8 * g4);
-        qi.load8(s.kq.Q + (16 * I + l16) * XS + 32 * kb + 8 * g4);
+        kj.load8(s.K() + (16 * J + l16) * XS + 32 * kb + 8 * g4);
+        ki.load8(s.K() + (16 * I + l16) * XS + 32 * kb + 8 * g4);
+        qi.load8(s.Q() + (16 * I + l16) * XS + 32 * kb + 8 * g4);
         mma(accA, kj, ki);
         mma(accP, kj, qi);
     }
@@ -133,7 +146,7 @@ __device__ __forceinline__ void tile_of_job(int j, int &I, int &J) {
 }
 
 template <typename IO, int C, bool PRO>
-__global__ __launch_bounds__(THREADS) void gdn_map_kernel(const KdaArgs a) {
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(C <= 64 ? 4 : 1))) void gdn_map_kernel(const KdaArgs a) {
     using F = Cfg<IO, C>;
     constexpr int NT = F::NT, AS = F::AS;
     constexpr int NJOBS = NT * (NT + 1) / 2;
@@ -172,8 +185,8 @@ __global__ __launch_bounds__(THREADS) void gdn_map_kernel(const KdaArgs a) {
         kv[p] = *reinterpret_cast<const v8 *>(reinterpret_cast<const IO *>(a.k) + off);
         qv[p] = *reinterpret_cast<const v8 *>(reinterpret_cast<const IO *>(a.q) + off);
         vv[p] = *reinterpret_cast<const v8 *>(reinterpret_cast<const IO *>(a.v) + (tr * a.Hv + h) * DK + 8 * seg);
-        *reinterpret_cast<v8 *>(&s.kq.K[row * XS + 8 * seg]) = kv[p];
-        *reinterpret_cast<v8 *>(&s.kq.Q[row * XS + 8 * seg]) = qv[p];
+        *reinterpret_cast<v8 *>(&s.K()[row * XS + 8 * seg]) = kv[p];
+        *reinterpret_cast<v8 *>(&s.Q()[row * XS + 8 * seg]) = qv[p];
     }
     if constexpr (PRO) {   // the 16 lanes of a DPP row hold one token's k (q) row
         const bool norm = a.prologue & GDN_PROLOGUE_QK_L2NORM;
@@ -187,7 +200,6 @@ __global__ __launch_bounds__(THREADS) void gdn_map_kernel(const KdaArgs a) {
             }
         }
     }
-    float *const A = F::A_OWN ? s.Aown : s.Aov;
     // #1 Gate on wave 0, lane = token (64 at a time): inclusive prefix sum, flat past the
     // chunk's end
     if (wave == 0) {
@@ -232,7 +244,6 @@ __global__ __launch_bounds__(THREADS) void gdn_map_kernel(const KdaArgs a) {
         const float gl = __expf(carry);
         *reinterpret_cast<float2 *>(tile + Tile<C>::GL + 8 * lane) = make_float2(gl, gl);
     }
-    for (int i = tid; i < C * AS; i += THREADS) s.T[i] = 0.f;
     __syncthreads();
 
     // the decayed operands of the chain, fp16, from the tiles in LDS: Qg token-major; Kl
@@ -257,7 +268,7 @@ __global__ __launch_bounds__(THREADS) void gdn_map_kernel(const KdaArgs a) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const int t = 16 * tb + i;
-                const v2 kk = *reinterpret_cast<const v2 *>(&s.kq.K[t * XS + ch]);
+                const v2 kk = *reinterpret_cast<const v2 *>(&s.K()[t * XS + ch]);
                 const float lm = PRO ? s.lam[t] * s.rn[0][t] : s.lam[t];
                 kl[0][i >> 3][i & 7] = (hf)(Cvt<IO>::to_f32(kk[0]) * lm);
                 kl[1][i >> 3][i & 7] = (hf)(Cvt<IO>::to_f32(kk[1]) * lm);
@@ -271,8 +282,7 @@ __global__ __launch_bounds__(THREADS) void gdn_map_kernel(const KdaArgs a) {
     }
 
     // #2 the lower 16x16 tiles of A and P, round-robin over the waves; zeros for P's tiles
-    // above the diagonal.  Over k and q (C = 128), A stays in registers until every wave
-    // is done with them.
+    // above the diagonal.  A stays in registers until every wave is done with k and q.
     f32x4 av[JPW];
 #pragma unroll
     for (int k = 0; k < JPW; ++k) {
@@ -281,7 +291,6 @@ __global__ __launch_bounds__(THREADS) void gdn_map_kernel(const KdaArgs a) {
             int I, J;
             tile_of_job(j, I, J);
             av[k] = gram_tile(s, tile, I, J, l16, g4);
-            if constexpr (F::A_OWN) *reinterpret_cast<f32x4 *>(&A[(16 * I + l16) * AS + 16 * J + 4 * g4]) = av[k];
         }
     }
     {
@@ -295,34 +304,21 @@ __global__ __launch_bounds__(THREADS) void gdn_map_kernel(const KdaArgs a) {
                 *reinterpret_cast<f16x8 *>(tile + Tile<C>::P + (r * C + 8 * sg) * 2) = z;
         }
     }
-    __syncthreads();   // k and q are dead (over them, A at C = 128)
-    if constexpr (!F::A_OWN) {
+    __syncthreads();   // k and q are dead: A and T go over them
+    // A^T into M's upper triangle: the lane's A[r][c0 + i] to M[c0 + i][r] (a diagonal
+    // tile's zeros land on the lower half, which the solve then fills)
+    float *const M = s.M();
 #pragma unroll
-        for (int k = 0; k < JPW; ++k) {
-            const int j = wave + 4 * k;
-            if (j < NJOBS) {
-                int I, J;
-                tile_of_job(j, I, J);
-                *reinterpret_cast<f32x4 *>(&A[(16 * I + l16) * AS + 16 * J + 4 * g4]) = av[k];
-            }
-        }
-        __syncthreads();
-    } else {
-        // the right-hand sides of the W/U products go over k and q now (A has its own region)
+    for (int k = 0; k < JPW; ++k) {
+        const int j = wave + 4 * k;
+        if (j < NJOBS) {
+            int I, J;
+            tile_of_job(j, I, J);
 #pragma unroll
-        for (int p = 0; p < C / 16; ++p) {
-            const int idx = tid + THREADS * p, row = idx >> 4, seg = idx & 15;
-            const float bk = s.beta[row] * s.gam[row] * (PRO ? s.rn[0][row] : 1.f), bv = s.beta[row];
-            f16x8 xk, xv;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                xk[e] = (hf)(Cvt<IO>::to_f32(kv[p][e]) * bk);
-                xv[e] = (hf)(Cvt<IO>::to_f32(vv[p][e]) * bv);
-            }
-            *reinterpret_cast<f16x8 *>(&s.wy.Kb[row * WY_S + 8 * seg]) = xk;
-            *reinterpret_cast<f16x8 *>(&s.wy.Vb[row * WY_S + 8 * seg]) = xv;
+            for (int i = 0; i < 4; ++i) M[(16 * J + 4 * g4 + i) * AS + 16 * I + l16] = av[k][i];
         }
     }
+    __syncthreads();
 
     // #3 Solve, T = (I + A)^-1: the diagonal 16x16 blocks by substitution (lane l16 one
     // column), then the blocks below them by distance d from the diagonal,
@@ -331,18 +327,22 @@ __global__ __launch_bounds__(THREADS) void gdn_map_kernel(const KdaArgs a) {
     // blocks of smaller distance; each wave keeps its partial product in its own Y.
     for (int X = wave; X < NT; X += 4) {
         const int c = l16;
-        const float *arow = &A[16 * X * AS + 16 * X];
+        const float *blk = &M[16 * X * AS + 16 * X];   // A[16X + r][16X + q] = blk[q AS + r]
         float x[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             float acc = r == c ? 1.f : 0.f;
 #pragma unroll
-            for (int q = 0; q < r; ++q) acc -= arow[r * AS + q] * x[q];
+            for (int q = 0; q < r; ++q) acc -= blk[q * AS + r] * x[q];
             x[r] = acc;
         }
-        if (g4 == 0) {
+        if (g4 == 0) {   // the lower half with the diagonal; rows above it (x[r] = 0, over A^T)
+                         // go to the wave's Y block, unused until the levels below
 #pragma unroll
-            for (int r = 0; r < 16; ++r) s.T[(16 * X + r) * AS + 16 * X + c] = x[r];
+            for (int r = 0; r < 16; ++r) {
+                float *dst = r >= c ? &M[(16 * X + r) * AS + 16 * X + c] : s.Y(wave) + c;
+                *dst = x[r];
+            }
         }
     }
     __syncthreads();
@@ -351,41 +351,69 @@ __global__ __launch_bounds__(THREADS) void gdn_map_kernel(const KdaArgs a) {
             const int I = J + d;
             f32x4 y = zero4();
             for (int kk = 16 * J; kk < 16 * I; kk += 4)
-                y = __builtin_amdgcn_mfma_f32_16x16x4f32(A[(16 * I + l16) * AS + kk + g4],
-                                                         s.T[(kk + g4) * AS + 16 * J + l16], y, 0, 0, 0);
+                y = __builtin_amdgcn_mfma_f32_16x16x4f32(M[(kk + g4) * AS + 16 * I + l16],
+                                                         kk + g4 >= 16 * J + l16 ? M[(kk + g4) * AS + 16 * J + l16] : 0.f,
+                                                         y, 0, 0, 0);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) s.Y[wave][(4 * g4 + i) * 16 + l16] = y[i];
+            for (int i = 0; i < 4; ++i) s.Y(wave)[(4 * g4 + i) * 16 + l16] = y[i];
             f32x4 t = zero4();
 #pragma unroll
             for (int v = 0; v < 16; v += 4)
-                t = __builtin_amdgcn_mfma_f32_16x16x4f32(s.T[(16 * I + l16) * AS + 16 * I + v + g4],
-                                                         s.Y[wave][(v + g4) * 16 + l16], t, 0, 0, 0);
+                t = __builtin_amdgcn_mfma_f32_16x16x4f32(v + g4 <= l16 ? M[(16 * I + l16) * AS + 16 * I + v + g4] : 0.f,
+                                                         s.Y(wave)[(v + g4) * 16 + l16], t, 0, 0, 0);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) s.T[(16 * I + 4 * g4 + i) * AS + 16 * J + l16] = -t[i];
+            for (int i = 0; i < 4; ++i) M[(16 * I + 4 * g4 + i) * AS + 16 * J + l16] = -t[i];
         }
         __syncthreads();
     }
 
-    // at C = 128, A is dead: diag(beta gamma) K and diag(beta) V go over it
-    if constexpr (!F::A_OWN) {
+    // T to fp16 for the products (the MFMA operand type), zeros above the diagonal
+    constexpr int TS = F::TS;
+    for (int i = tid; i < C * C / 8; i += THREADS) {
+        const int r = i / (C / 8), c = 8 * (i % (C / 8));
+        const f32x4 t0 = *reinterpret_cast<const f32x4 *>(&M[r * AS + c]);
+        const f32x4 t1 = *reinterpret_cast<const f32x4 *>(&M[r * AS + c + 4]);
+        f16x8 y;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            y[e] = (hf)(c + e <= r ? t0[e] : 0.f);
+            y[4 + e] = (hf)(c + 4 + e <= r ? t1[e] : 0.f);
+        }
+        *reinterpret_cast<f16x8 *>(&s.T16()[r * TS + c]) = y;
+    }
+    __syncthreads();   // M is dead: the right-hand sides go over it, one at a time
+
+    // #4 W = T diag(beta gamma) K and U = T diag(beta) V to the workspace
+    hf *const rhs = s.RHS();
 #pragma unroll
     for (int p = 0; p < C / 16; ++p) {
         const int idx = tid + THREADS * p, row = idx >> 4, seg = idx & 15;
-        const float bk = s.beta[row] * s.gam[row] * (PRO ? s.rn[0][row] : 1.f), bv = s.beta[row];
-        f16x8 xk, xv;
+        const float bk = s.beta[row] * s.gam[row] * (PRO ? s.rn[0][row] : 1.f);
+        f16x8 xk;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            xk[e] = (hf)(Cvt<IO>::to_f32(kv[p][e]) * bk);
-            xv[e] = (hf)(Cvt<IO>::to_f32(vv[p][e]) * bv);
-        }
-        *reinterpret_cast<f16x8 *>(&s.wy.Kb[row * WY_S + 8 * seg]) = xk;
-        *reinterpret_cast<f16x8 *>(&s.wy.Vb[row * WY_S + 8 * seg]) = xv;
+        for (int e = 0; e < 8; ++e) xk[e] = (hf)(Cvt<IO>::to_f32(kv[p][e]) * bk);
+        *reinterpret_cast<f16x8 *>(&rhs[row * WY_S + 8 * seg]) = xk;
+    }
+    hf *const vb = F::TWO_PASS ? rhs : rhs + C * WY_S;
+    if constexpr (F::TWO_PASS) {
+        __syncthreads();
+        wy_products<C, hf, true, false>(s.T16(), TS, rhs, nullptr, tile + Tile<C>::W, nullptr, wave, l16, g4);
+        __syncthreads();
+    }
+#pragma unroll
+    for (int p = 0; p < C / 16; ++p) {
+        const int idx = tid + THREADS * p, row = idx >> 4, seg = idx & 15;
+        const float bv = s.beta[row];
+        f16x8 xv;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) xv[e] = (hf)(Cvt<IO>::to_f32(vv[p][e]) * bv);
+        *reinterpret_cast<f16x8 *>(&vb[row * WY_S + 8 * seg]) = xv;
     }
     __syncthreads();
-    }
-
-    // #4 W = T diag(beta gamma) K and U = T diag(beta) V to the workspace
-    wy_products<C>(s.T, AS, s.wy.Kb, s.wy.Vb, tile + Tile<C>::W, tile + Tile<C>::UT, wave, l16, g4);
+    if constexpr (F::TWO_PASS)
+        wy_products<C, hf, false, true>(s.T16(), TS, nullptr, vb, nullptr, tile + Tile<C>::UT, wave, l16, g4);
+    else
+        wy_products<C, hf, true, true>(s.T16(), TS, rhs, vb, tile + Tile<C>::W, tile + Tile<C>::UT, wave, l16, g4);
 }
 
 }  // namespace gdnmap

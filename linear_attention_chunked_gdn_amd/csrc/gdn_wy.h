@@ -37,15 +37,17 @@ __device__ __forceinline__ Frag<_Float16> wy_frag_t(const _Float16 *x, int c0, i
     return f;
 }
 
-// T: fp32, row stride `as`, lower triangular (zeros above the diagonal).  kg, vb:
-// diag(beta) Kg and diag(beta) V, fp16 [token][channel] with row stride WY_S, in LDS.
-// Wave `wave` (0..3) forms channel tiles 2 wave and 2 wave + 1 of both products and
-// writes them to the workspace: W row-major [token][channel] (wout), U transposed
-// [channel][token] (utout).  The products are taken transposed (operand^T T^T), so a lane
-// holds token 16I + l16 and four consecutive channels: one 8-byte store of W, four 2-byte
-// stores of U^T.
-template <int C>
-__device__ __forceinline__ void wy_products(const float *T, int as, const _Float16 *kg, const _Float16 *vb,
+// T: fp32 or fp16 (TT), row stride `as`, lower triangular (zeros above the diagonal),
+// rounded to fp16 as an MFMA operand.  kg, vb: diag(beta) Kg and diag(beta) V, fp16
+// [token][channel] with row stride WY_S, in LDS.  Wave `wave` (0..3) forms channel tiles
+// 2 wave and 2 wave + 1 of both products and writes them to the workspace: W row-major
+// [token][channel] (wout), U transposed [channel][token] (utout).  The products are
+// taken transposed (operand^T T^T), so a lane holds token 16I + l16 and four consecutive
+// channels: one 8-byte store of W, four 2-byte stores of U^T.  (U^T rows stored 8 bytes
+// at a time from the untransposed product measured slower.)  DW / DU select the products
+// formed (kg or vb may be null for the other).
+template <int C, typename TT = float, bool DW = true, bool DU = true>
+__device__ __forceinline__ void wy_products(const TT *T, int as, const _Float16 *kg, const _Float16 *vb,
                                             char *wout, char *utout, int wave, int l16, int g4) {
     typedef _Float16 hf;
 #pragma unroll
@@ -56,35 +58,41 @@ __device__ __forceinline__ void wy_products(const float *T, int as, const _Float
 #pragma unroll
         for (int kb = 0; kb <= (I >> 1); ++kb) {
             // T^T as the B operand: column = token 16I + l16, slots = tokens 32kb + 8G + e
-            const float *tr = T + (16 * I + l16) * as + 32 * kb + 8 * g4;
-            const f32x4 t0 = *reinterpret_cast<const f32x4 *>(tr);
-            const f32x4 t1 = *reinterpret_cast<const f32x4 *>(tr + 4);
+            const TT *tr = T + (16 * I + l16) * as + 32 * kb + 8 * g4;
             Frag<hf> ft;
+            if constexpr (sizeof(TT) == 2) {
+                ft.load8(reinterpret_cast<const hf *>(tr));
+            } else {
+                const f32x4 t0 = *reinterpret_cast<const f32x4 *>(tr);
+                const f32x4 t1 = *reinterpret_cast<const f32x4 *>(tr + 4);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                ft.v[e] = (hf)t0[e];
-                ft.v[4 + e] = (hf)t1[e];
+                for (int e = 0; e < 4; ++e) {
+                    ft.v[e] = (hf)t0[e];
+                    ft.v[4 + e] = (hf)t1[e];
+                }
             }
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 const int c0 = 16 * (2 * wave + j);
-                const Frag<hf> fk = wy_frag_t(kg, c0, kb, l16, g4);
-                const Frag<hf> fv = wy_frag_t(vb, c0, kb, l16, g4);
-                mma(acc[j][0], fk, ft);
-                mma(acc[j][1], fv, ft);
+                if constexpr (DW) mma(acc[j][0], wy_frag_t(kg, c0, kb, l16, g4), ft);
+                if constexpr (DU) mma(acc[j][1], wy_frag_t(vb, c0, kb, l16, g4), ft);
             }
         }
         const int r = 16 * I + l16;
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const int c = 16 * (2 * wave + j) + 4 * g4;
-            f16x4 w;
+            f16x4 w, u;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 w[i] = (hf)acc[j][0][i];
-                reinterpret_cast<hf *>(utout)[(c + i) * C + r] = (hf)acc[j][1][i];
+                u[i] = (hf)acc[j][1][i];
             }
-            *reinterpret_cast<f16x4 *>(wout + (r * 128 + c) * 2) = w;
+            if constexpr (DW) *reinterpret_cast<f16x4 *>(wout + (r * 128 + c) * 2) = w;
+            if constexpr (DU) {   // token r of U^T rows c .. c + 3
+#pragma unroll
+                for (int i = 0; i < 4; ++i) reinterpret_cast<hf *>(utout)[(c + i) * C + r] = u[i];
+            }
         }
     }
 }
