@@ -174,6 +174,19 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(C <= 64
     const int nval = min(C, eos - tok0);
     char *tile = a.ws + ((size_t)slot * a.Hv + h) * Tile<C>::BYTES;
 
+    // wave 0's gate operands first (lane = token, clamped into the chunk), so that their
+    // round trip overlaps the k, q, v loads instead of following them
+    constexpr int GB = C > 64 ? C / 64 : 1;
+    float graw[GB], braw[GB];
+    if (wave == 0) {
+#pragma unroll
+        for (int b = 0; b < GB; ++b) {
+            const size_t gi = (size_t)(tok0 + min(64 * b + lane, nval - 1)) * a.Hv + h;
+            graw[b] = a.g[gi];
+            braw[b] = a.beta[gi];
+        }
+    }
+
     // k, q rows to LDS, and kept in registers with the v rows: C rows x 16 segments of 8
     typedef IO v8 __attribute__((ext_vector_type(8)));
     v8 kv[C / 16], qv[C / 16], vv[C / 16];
@@ -208,9 +221,8 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(C <= 64
         for (int base = 0; base < C; base += 64) {
             const int t = base + lane;
             const bool ok = t < nval;
-            const size_t gi = (size_t)(tok0 + min(t, nval - 1)) * a.Hv + h;
-            float x = ok ? a.g[gi] : 0.f;
-            float b = ok ? a.beta[gi] : 0.f;
+            float x = ok ? graw[base / 64] : 0.f;
+            float b = ok ? braw[base / 64] : 0.f;
             if constexpr (PRO) {
                 if (ok && (a.prologue & GDN_PROLOGUE_BETA_SIGMOID)) b = prologue_sigmoid(b);
                 if (ok && (a.prologue & GDN_PROLOGUE_G_SOFTPLUS)) x = prologue_neg_softplus(x);
