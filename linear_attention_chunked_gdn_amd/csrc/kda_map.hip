@@ -205,7 +205,11 @@ __global__ __launch_bounds__(THREADS, 2) void kda_map_kernel(const KdaArgs a) {
     const int nval = min(CH, eos - tok0);
     char *tile = a.ws + ((size_t)slot * a.Hv + h) * WS_TILE_BYTES;
 
-    if (tid < CH) s.beta[tid] = tid < nval ? a.beta[(size_t)(tok0 + tid) * a.Hv + h] : 0.f;
+    // beta for wave 0 (lane = token, clamped into the chunk) before the gate's loads, to
+    // LDS after them: its round trip overlaps theirs
+    static_assert(CH == 64, "one wave holds the chunk's beta");
+    float braw = 0.f;
+    if (wave == 0) braw = a.beta[(size_t)(tok0 + min(lane, nval - 1)) * a.Hv + h];
 
     // #1 Gate, per channel: a = exp(g) for this lane's two channels and 16 tokens; k and
     // q go straight to LDS
@@ -224,6 +228,7 @@ __global__ __launch_bounds__(THREADS, 2) void kda_map_kernel(const KdaArgs a) {
         *reinterpret_cast<v2 *>(&s.kq.K[t * XS + ch]) = *reinterpret_cast<const v2 *>(reinterpret_cast<const IO *>(a.k) + kq);
         *reinterpret_cast<v2 *>(&s.kq.Q[t * XS + ch]) = *reinterpret_cast<const v2 *>(reinterpret_cast<const IO *>(a.q) + kq);
     }
+    if (wave == 0) s.beta[lane] = lane < nval ? braw : 0.f;
     // products inside the block: F inclusive from the block start, B exclusive to its end
     float F0[16], F1[16], B0[16], B1[16];
     F0[0] = a0[0];
