@@ -102,6 +102,13 @@ struct __align__(16) Smem {
     __device__ hf *RHS() { return reinterpret_cast<hf *>(r0); }
 };
 
+static_assert(Cfg<__bf16, 64>::T16_OFF >= Cfg<__bf16, 64>::M_BYTES &&
+                  Cfg<__bf16, 128>::T16_OFF >= Cfg<__bf16, 128>::M_BYTES &&
+                  Cfg<__bf16, 32>::T16_OFF >= Cfg<__bf16, 32>::M_BYTES,
+              "T's fp16 copy is written while M is read");
+static_assert(sizeof(Smem<__bf16, 64, true>) <= 160 * 1024 / 4 && sizeof(Smem<_Float16, 64, true>) <= 160 * 1024 / 4,
+              "four chunk-64 workgroups share a CU's LDS");
+
 // Tile (I, J), I >= J, of A and P.  The product is taken transposed (K_J X_I^T), so the
 // lane holds row r = 16I + l16 and columns 16J + 4g4 .. 16J + 4g4 + 3; P goes to the
 // workspace as fp16, the beta-scaled A is returned (it goes to LDS once every wave is done
