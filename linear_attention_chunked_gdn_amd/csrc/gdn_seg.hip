@@ -18,8 +18,9 @@
 // fp32 MFMA product each, stores every S_in as fp16 (a.sin16) and the last one as the
 // final state.
 // gdn_seg_fix_kernel: one 512-thread workgroup per (chunk slot, value head) of segments
-// >= 1 stages the chunk's E rows in LDS; wave w forms O = O0 + E S_in^T for value channels
-// [16w, 16w + 16) (fp16 MFMA, fp32 accumulation) and stores it.
+// >= 1 issues all its loads at once (E rows, S_in fragments, O0), stages the chunk's E
+// rows in LDS; wave w forms O = O0 + E S_in^T for value channels [16w, 16w + 16) (fp16
+// MFMA, fp32 accumulation) and stores it.
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
@@ -129,12 +130,15 @@ __global__ __launch_bounds__(FIX_THREADS) void gdn_seg_fix_kernel(const KdaArgs 
     const int dv0 = ROWS * wave;
     const int nval = min(C, eos - tok0);
 
-    // E rows of the chunk (rows past the sequence are zero) into LDS
-    for (int i = tid; i < C * D / 8; i += FIX_THREADS) {
-        const int t = i / (D / 8), c = 8 * (i % (D / 8));
-        f16x8 x = {};
-        if (t < nval) x = *reinterpret_cast<const f16x8 *>(a.e + ((size_t)(tok0 + t) * a.Hv + h) * D + c);
-        *reinterpret_cast<f16x8 *>(&Es[t * ES + c]) = x;
+    // E rows of the chunk (clamped into the sequence; rows past it become zero in LDS),
+    // loaded with S_in and O0 below before any of them is waited for
+    constexpr int EPT = C * D / 8 / FIX_THREADS;   // 16-byte E segments per thread
+    static_assert(EPT * FIX_THREADS * 8 == C * D, "E segments split evenly over the threads");
+    f16x8 ev[EPT];
+#pragma unroll
+    for (int p = 0; p < EPT; ++p) {
+        const int i = tid + FIX_THREADS * p, t = i / (D / 8), c = 8 * (i % (D / 8));
+        ev[p] = *reinterpret_cast<const f16x8 *>(a.e + ((size_t)(tok0 + min(t, nval - 1)) * a.Hv + h) * D + c);
     }
     // S_in(seg) rows dv0 + l16 as A operands (slots = identity rows 32 kb + 8 g4 + e), and O0
     const _Float16 *sin = a.sin16 + (((size_t)n * a.Hv + h) * a.nseg + (seg - 1)) * D * D;
@@ -148,6 +152,12 @@ __global__ __launch_bounds__(FIX_THREADS) void gdn_seg_fix_kernel(const KdaArgs 
         const f16x4 o0 = *reinterpret_cast<const f16x4 *>(a.o0 + ((size_t)(tok0 + tc) * a.Hv + h) * D + dv0 + 4 * g4);
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc[t][i] = (float)o0[i];
+    }
+#pragma unroll
+    for (int p = 0; p < EPT; ++p) {
+        const int i = tid + FIX_THREADS * p, t = i / (D / 8), c = 8 * (i % (D / 8));
+        const f16x8 zero = {};
+        *reinterpret_cast<f16x8 *>(&Es[t * ES + c]) = t < nval ? ev[p] : zero;
     }
     __syncthreads();
 
