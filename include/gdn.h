@@ -160,7 +160,7 @@ gdn_status gdn_decode_step_fused(const void *q, const void *k, const void *v,
  * With every channel's g equal this is the gated delta rule above.
  *
  * gdn_kda_workspace_size -- device bytes gdn_kda_prefill needs as workspace for these
- * sizes: one 74,240-byte tile per value head and chunk slot, with T_tot / 64 + N slots
+ * sizes: one 72,192-byte tile per value head and chunk slot, with T_tot / 64 + N slots
  * (enough for any packing of N sequences into T_tot tokens).  Host pointer `bytes`.
  */
 gdn_status gdn_kda_workspace_size(int32_t N, int32_t T_tot, int32_t Hv, int32_t chunk_size,
@@ -230,8 +230,8 @@ gdn_status gdn_kda_decode_step(const void *q, const void *k, const void *v,
  *
  * gdn_prefill_split_workspace_size -- the workspace bytes for these sizes and chunk length:
  * one tile per value head and chunk slot (T_tot / chunk_size + N slots) of
- * C^2 * 2 + C * 1024 + 512 bytes for C = chunk_size (74,240 at C = 64, as for
- * gdn_kda_workspace_size).  Host pointer `bytes`.
+ * C * 1024 + (C / 32) (C / 32 + 1) * 1024 + 512 bytes for C = chunk_size (72,192 at
+ * C = 64, as for gdn_kda_workspace_size).  Host pointer `bytes`.
  */
 gdn_status gdn_prefill_split_workspace_size(int32_t N, int32_t T_tot, int32_t Hv,
                                             int32_t chunk_size, size_t *bytes);

@@ -291,7 +291,7 @@ gdn_status gdn_kda_prefill(const void *q, const void *k, const void *v, const fl
     const bool f16 = io_dtype == GDN_F16;
     (void)hipGetLastError();
     hipError_t e = T_tot > 0 ? gdn::launch_kda_map(a, f16, hs) : hipSuccess;
-    if (e == hipSuccess) e = gdn::launch_kda_chain(a, f16, kChunk, hs);
+    if (e == hipSuccess) e = gdn::launch_kda_chain(a, f16, kChunk, true, hs);
     if (e != hipSuccess)
         return fail(GDN_ERR_DEVICE, "kda prefill launch failed: %s", hipGetErrorString(e));
     return ok();
@@ -346,7 +346,7 @@ gdn_status split_impl(const void *q, const void *k, const void *v, const float *
     const bool f16 = io_dtype == GDN_F16;
     (void)hipGetLastError();
     hipError_t e = T_tot > 0 ? gdn::launch_gdn_map(a, f16, chunk_size, hs) : hipSuccess;
-    if (e == hipSuccess) e = gdn::launch_kda_chain(a, f16, chunk_size, hs);
+    if (e == hipSuccess) e = gdn::launch_kda_chain(a, f16, chunk_size, false, hs);
     if (e != hipSuccess)
         return fail(GDN_ERR_DEVICE, "split prefill launch failed: %s", hipGetErrorString(e));
     return ok();
@@ -454,7 +454,7 @@ gdn_status seg_impl(const char *fn, bool per_channel, const void *q, const void 
     hipError_t e;
     if (T_tot == 0) {
         // no tokens: the final state is the initial state (the plain chain copies it)
-        e = gdn::launch_kda_chain(a, f16, chunk_size, hs);
+        e = gdn::launch_kda_chain(a, f16, chunk_size, per_channel, hs);
     } else {
         size_t off = (size_t)slots * Hv * tile_bytes(chunk_size);
         a.o0 = reinterpret_cast<_Float16 *>(a.ws + off);
@@ -465,7 +465,7 @@ gdn_status seg_impl(const char *fn, bool per_channel, const void *q, const void 
         off += (size_t)N * Hv * segments * 2 * kD * kD * sizeof(float);
         a.sin16 = reinterpret_cast<_Float16 *>(a.ws + off);
         e = per_channel ? gdn::launch_kda_map(a, f16, hs) : gdn::launch_gdn_map(a, f16, chunk_size, hs);
-        if (e == hipSuccess) e = gdn::launch_seg_chain(a, f16, chunk_size, hs);
+        if (e == hipSuccess) e = gdn::launch_seg_chain(a, f16, chunk_size, per_channel, hs);
         if (e == hipSuccess) e = gdn::launch_seg_join(a, hs);
         if (e == hipSuccess) e = gdn::launch_seg_fix(a, f16, chunk_size, hs);
     }

@@ -56,37 +56,60 @@ struct KdaArgs {
     _Float16 *sin16;        // [N, Hv, nseg, 128, 128] start states of segments 1 .. nseg - 1
     uint32_t prologue;      // GDN_PROLOGUE_* flags of the scalar-gate map (0: none)
 };
-// Workspace tile of one chunk of C tokens and one value head (byte offsets; fp16 except
-// gl; row-major), with T = (I + A)^-1 and the decays of the chunk:
-//   P   = lower-incl-diagonal(Q K^T (.) decays)      [C tokens][C tokens]
-//   W   = T diag(beta) (K (.) exp(Gamma))             [C tokens][128 key channels]
-//   Qg  = Q (.) exp(Gamma)                            [C tokens][128 key channels]
-//   KlT = (K (.) exp(Gamma_last - Gamma))^T           [128 key channels][C tokens]
-//   UT  = (T diag(beta) V)^T                          [128 value channels][C tokens]
-//   gl  = exp(Gamma_last)                             [128 key channels] fp32
-// Each is laid out so that one chain wave's MFMA fragments are 16-byte row segments.
+// Workspace tile of one chunk of C tokens and one value head, with T = (I + A)^-1 and the
+// decays of the chunk:
+//   WN = -T diag(beta) (K (.) exp(Gamma))            C tokens x 128 key channels
+//   QG = Q (.) exp(Gamma)                            C tokens x 128 key channels
+//   KL = K (.) exp(Gamma_last - Gamma)               C tokens x 128 key channels
+//   P  = lower-incl-diagonal(Q K^T (.) decays)       C tokens x C tokens
+//   U  = T diag(beta) V                              C tokens x 128 value channels
+//   GL = exp(Gamma_last)                             128 key channels, fp32
+// Everything but GL is fp16 and stored as MFMA operand fragments, so that the chain reads
+// every operand with one coalesced 16-byte load per lane.  A fragment is 64 lanes x 16
+// bytes: lane l = 16 G + m holds, for row m of a 16-row block, the eight entries of a
+// 32-wide block kb of the reduction index j = 32 kb + pi(G, e), e = 0..7, with
+//   pi(G, e) = 4 G + e (e < 4),   16 + 4 G + (e - 4) (e >= 4),
+// the order in which a 16x16 fp32 accumulator pair holds its rows, so that results feed
+// the next product without leaving registers.  Fragments:
+//   WN, QG: (t, kb), t < C/16 token tiles, kb < 4: row = token 16 t + m, j = key channel
+//   KL:     (i, kb), i < 8 key tiles, kb < C/32: row = key channel 16 i + m, j = token
+//   P:      (t, kb) for kb <= t/2 only (the rest is zero): row = token 16 t + m, j = token
+// and U in the fp32 accumulator order of the value rows: per value slice sl (16 channels)
+// and token tile t, lane 16 G + m holds U[16 t + 4 G + r][16 sl + m], r = 0..3 (8 bytes).
 template <int C> struct Tile {
-    static constexpr int P = 0;
-    static constexpr int W = C * C * 2;
-    static constexpr int QG = W + C * 256;
-    static constexpr int KLT = QG + C * 256;
-    static constexpr int UT = KLT + C * 256;
-    static constexpr int GL = UT + C * 256;
+    static constexpr int NT = C / 16;
+    static constexpr int KB = C / 32;
+    static constexpr int FRAG = 1024;
+    // P fragments before token tile t: sum over t' < t of (t' / 2 + 1)
+    static constexpr int pstart(int t) { return (t / 2) * (t / 2 + 1) + (t % 2) * (t / 2 + 1); }
+    static constexpr int NPF = pstart(NT);
+    static constexpr int WN = 0;
+    static constexpr int QG = WN + NT * 4 * FRAG;
+    static constexpr int KL = QG + NT * 4 * FRAG;
+    static constexpr int P = KL + 8 * KB * FRAG;
+    static constexpr int U = P + NPF * FRAG;
+    static constexpr int GL = U + 8 * NT * 512;
     static constexpr size_t BYTES = (size_t)GL + 512;
+    static constexpr int wn(int t, int kb) { return WN + (t * 4 + kb) * FRAG; }
+    static constexpr int qg(int t, int kb) { return QG + (t * 4 + kb) * FRAG; }
+    static constexpr int kl(int i, int kb) { return KL + (i * KB + kb) * FRAG; }
+    static constexpr int p(int t, int kb) { return P + (pstart(t) + kb) * FRAG; }
+    static constexpr int u(int sl, int t) { return U + (sl * NT + t) * 512; }
 };
 static_assert(Tile<32>::BYTES % 256 == 0 && Tile<64>::BYTES % 256 == 0 && Tile<128>::BYTES % 256 == 0,
               "tiles keep the workspace's 256-byte alignment");
+static_assert(Tile<64>::NPF == 6 && Tile<32>::NPF == 2 && Tile<128>::NPF == 20, "P fragments of the lower triangle");
+static_assert(Tile<64>::BYTES == 72192, "the documented tile size at C = 64");
+// Byte offset inside a lane's 16-byte fragment piece, and the lane, of reduction index j of
+// a 32-wide block (row m): the inverse of pi.
+__host__ __device__ constexpr int frag_lane(int j, int m) { return 16 * ((j & 15) >> 2) + m; }
+__host__ __device__ constexpr int frag_byte(int j) { return 2 * ((j & 3) + ((j & 16) >> 2)); }
 // The per-key-channel path runs 64-token chunks.
-constexpr int WS_OFF_P = Tile<64>::P;
-constexpr int WS_OFF_W = Tile<64>::W;
-constexpr int WS_OFF_QG = Tile<64>::QG;
-constexpr int WS_OFF_KLT = Tile<64>::KLT;
-constexpr int WS_OFF_UT = Tile<64>::UT;
-constexpr int WS_OFF_GL = Tile<64>::GL;
 constexpr size_t WS_TILE_BYTES = Tile<64>::BYTES;
 hipError_t launch_kda_map(const KdaArgs &a, bool f16, hipStream_t stream);
-// The chain over tiles of `chunk` tokens (32, 64 or 128).
-hipError_t launch_kda_chain(const KdaArgs &a, bool f16, int chunk, hipStream_t stream);
+// The chain over tiles of `chunk` tokens (32, 64 or 128); per_channel: GL differs per key
+// channel (the KDA map), else one decay per chunk (the scalar-gate map).
+hipError_t launch_kda_chain(const KdaArgs &a, bool f16, int chunk, bool per_channel, hipStream_t stream);
 int kda_map_lds_bytes();
 int kda_chain_lds_bytes();
 // The scalar-gate map (KdaArgs::g is [T_tot, Hv]) into the same workspace tiles, read by
@@ -94,7 +117,7 @@ int kda_chain_lds_bytes();
 hipError_t launch_gdn_map(const KdaArgs &a, bool f16, int chunk, hipStream_t stream);
 // The segmented chain (the chain kernel in its segment mode), then the two kernels that join
 // the segments (gdn_seg.hip): the segments' start states, and the outputs' corrections.
-hipError_t launch_seg_chain(const KdaArgs &a, bool f16, int chunk, hipStream_t stream);
+hipError_t launch_seg_chain(const KdaArgs &a, bool f16, int chunk, bool per_channel, hipStream_t stream);
 hipError_t launch_seg_join(const KdaArgs &a, hipStream_t stream);
 hipError_t launch_seg_fix(const KdaArgs &a, bool f16, int chunk, hipStream_t stream);
 // one token with a per-key-channel gate: DecodeArgs::g is [B, Hv, 128]

@@ -8,10 +8,11 @@
 //
 //   A = strictly-lower(diag(beta) K K^T .* D),   T = (I + A)^-1,
 //   P = lower-incl-diagonal(Q K^T .* D),
-//   W = T diag(beta gamma) K,  U = T diag(beta) V (stored transposed),
-//   Qg = diag(gamma) Q,  Kl = diag(lambda) K (stored transposed),  gl = gamma_last,
+//   W = T diag(beta gamma) K (stored negated),  U = T diag(beta) V,
+//   Qg = diag(gamma) Q,  Kl = diag(lambda) K,  gl = gamma_last,
 //
-// so that the chain's v = U - W S^T (= T diag(beta) (V - diag(gamma) K S^T)),
+// all as the chain's MFMA operand fragments (gdn_launch.h, Tile), so that the chain's
+// v = U - W S^T (= T diag(beta) (V - diag(gamma) K S^T)),
 // O = Qg S^T + P v and S <- gl S + v^T Kl are the scalar-gate chunk formulas with the
 // decays and the inverse already in the operands (the per-key-channel gate of
 // kda_map.hip with every channel's decay equal).
@@ -111,8 +112,8 @@ static_assert(sizeof(Smem<__bf16, 64, true>) <= 160 * 1024 / 4 && sizeof(Smem<_F
 
 // Tile (I, J), I >= J, of A and P.  The product is taken transposed (K_J X_I^T), so the
 // lane holds row r = 16I + l16 and columns 16J + 4g4 .. 16J + 4g4 + 3; P goes to the
-// workspace as fp16, the beta-scaled A is returned (it goes to LDS once every wave is done
-// reading the k and q tiles it would overlay).
+// workspace as fp16 (its half of fragment P(I, J / 2)), the beta-scaled A is returned (it
+// goes to LDS once every wave is done reading the k and q tiles it would overlay).
 template <typename IO, int C, bool PRO>
 __device__ __forceinline__ f32x4 gram_tile(const Smem<IO, C, PRO> &s, char *tile, int I, int J, int l16, int g4) {
     f32x4 accA = zero4(), accP = zero4();
@@ -141,7 +142,7 @@ __device__ __forceinline__ f32x4 gram_tile(const Smem<IO, C, PRO> &s, char *tile
         va[i] = c < r ? br * accA[i] * da : 0.f;
         hp[i] = (hf)(accP[i] * dp);
     }
-    *reinterpret_cast<f16x4 *>(tile + Tile<C>::P + (r * C + c0) * 2) = hp;
+    store_p_frag<C>(tile, I, J, l16, g4, hp);
     return va;
 }
 
@@ -265,37 +266,45 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(C <= 64
     }
     __syncthreads();
 
-    // the decayed operands of the chain, fp16, from the tiles in LDS: Qg token-major; Kl
-    // transposed (token block tb: tokens 16tb .. 16tb + 15; lane: channels 2 lane and
-    // 2 lane + 1, two 16-byte row segments of Kl^T per channel)
+    // the decayed operands of the chain, fp16, from the rows in registers and LDS, as operand
+    // fragments (gdn_launch.h, Tile): Qg by the thread that loaded the row (8 channels: two
+    // lanes' 8-byte halves); Kl by key channel (lane: channels 2 lane and 2 lane + 1), four
+    // tokens 16 tb + 4 G .. + 3 at a time, the half of lane (G, channel) in fragment
+    // KL(channel / 16, tb / 2)
     {
-        hf *qg = reinterpret_cast<hf *>(tile + Tile<C>::QG);
 #pragma unroll
         for (int p = 0; p < C / 16; ++p) {
-            const int idx = tid + THREADS * p, row = idx >> 4;
+            const int idx = tid + THREADS * p, row = idx >> 4, seg = idx & 15;
             const float gm = PRO ? s.gam[row] * s.rn[1][row] : s.gam[row];
-            f16x8 xq;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) xq[e] = (hf)(Cvt<IO>::to_f32(qv[p][e]) * gm);
-            *reinterpret_cast<f16x8 *>(qg + 8 * idx) = xq;
+            for (int h2 = 0; h2 < 2; ++h2) {
+                const int j = 8 * seg + 4 * h2;
+                f16x4 xq;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) xq[e] = (hf)(Cvt<IO>::to_f32(qv[p][4 * h2 + e]) * gm);
+                *reinterpret_cast<f16x4 *>(tile + Tile<C>::qg(row >> 4, j >> 5) + 16 * frag_lane(j, row & 15) +
+                                           frag_byte(j)) = xq;
+            }
         }
         typedef IO v2 __attribute__((ext_vector_type(2)));
         const int ch = 2 * lane;
-        hf *klt = reinterpret_cast<hf *>(tile + Tile<C>::KLT);
         for (int tb = wave; tb < NT; tb += 4) {
-            f16x8 kl[2][2];
+            f16x4 kl[2][4];
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const int t = 16 * tb + i;
                 const v2 kk = *reinterpret_cast<const v2 *>(&s.K()[t * XS + ch]);
                 const float lm = PRO ? s.lam[t] * s.rn[0][t] : s.lam[t];
-                kl[0][i >> 3][i & 7] = (hf)(Cvt<IO>::to_f32(kk[0]) * lm);
-                kl[1][i >> 3][i & 7] = (hf)(Cvt<IO>::to_f32(kk[1]) * lm);
+                kl[0][i >> 2][i & 3] = (hf)(Cvt<IO>::to_f32(kk[0]) * lm);
+                kl[1][i >> 2][i & 3] = (hf)(Cvt<IO>::to_f32(kk[1]) * lm);
             }
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
-                *reinterpret_cast<f16x8 *>(klt + (ch + j) * C + 16 * tb) = kl[j][0];
-                *reinterpret_cast<f16x8 *>(klt + (ch + j) * C + 16 * tb + 8) = kl[j][1];
+                const int c = ch + j;
+#pragma unroll
+                for (int G = 0; G < 4; ++G)
+                    *reinterpret_cast<f16x4 *>(tile + Tile<C>::kl(c >> 4, tb >> 1) + 16 * (16 * G + (c & 15)) +
+                                               8 * (tb & 1)) = kl[j][G];
             }
         }
     }
@@ -310,17 +319,6 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(C <= 64
             int I, J;
             tile_of_job(j, I, J);
             av[k] = gram_tile(s, tile, I, J, l16, g4);
-        }
-    }
-    {
-        f16x8 z;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) z[e] = (hf)0.f;
-        // upper tiles: row r, segment of 8 columns 8sg, for columns past the diagonal tile
-        for (int i = tid; i < C * (C / 8); i += THREADS) {
-            const int r = i / (C / 8), sg = i % (C / 8);
-            if (8 * sg >= 16 * (r / 16 + 1))
-                *reinterpret_cast<f16x8 *>(tile + Tile<C>::P + (r * C + 8 * sg) * 2) = z;
         }
     }
     __syncthreads();   // k and q are dead: A and T go over them
@@ -416,7 +414,7 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(C <= 64
     hf *const vb = F::TWO_PASS ? rhs : rhs + C * WY_S;
     if constexpr (F::TWO_PASS) {
         __syncthreads();
-        wy_products<C, hf, true, false>(s.T16(), TS, rhs, nullptr, tile + Tile<C>::W, nullptr, wave, l16, g4);
+        wy_products<C, hf, true, false>(s.T16(), TS, rhs, nullptr, tile, wave, l16, g4);
         __syncthreads();
     }
 #pragma unroll
@@ -430,9 +428,9 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(C <= 64
     }
     __syncthreads();
     if constexpr (F::TWO_PASS)
-        wy_products<C, hf, false, true>(s.T16(), TS, nullptr, vb, nullptr, tile + Tile<C>::UT, wave, l16, g4);
+        wy_products<C, hf, false, true>(s.T16(), TS, nullptr, vb, tile, wave, l16, g4);
     else
-        wy_products<C, hf, true, true>(s.T16(), TS, rhs, vb, tile + Tile<C>::W, tile + Tile<C>::UT, wave, l16, g4);
+        wy_products<C, hf, true, true>(s.T16(), TS, rhs, vb, tile, wave, l16, g4);
 }
 
 }  // namespace gdnmap

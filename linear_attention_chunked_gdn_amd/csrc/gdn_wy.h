@@ -40,16 +40,18 @@ __device__ __forceinline__ Frag<_Float16> wy_frag_t(const _Float16 *x, int c0, i
 // T: fp32 or fp16 (TT), row stride `as`, lower triangular (zeros above the diagonal),
 // rounded to fp16 as an MFMA operand.  kg, vb: diag(beta) Kg and diag(beta) V, fp16
 // [token][channel] with row stride WY_S, in LDS.  Wave `wave` (0..3) forms channel tiles
-// 2 wave and 2 wave + 1 of both products and writes them to the workspace: W row-major
-// [token][channel] (wout), U transposed [channel][token] (utout).  The products are
-// taken transposed (operand^T T^T), so a lane holds token 16I + l16 and four consecutive
-// channels: one 8-byte store of W, four 2-byte stores of U^T.  (U^T rows stored 8 bytes
-// at a time from the untransposed product measured slower.)  DW / DU select the products
-// formed (kg or vb may be null for the other).
+// 2 wave and 2 wave + 1 of both products and writes them to the workspace tile in the
+// chain's operand layout (gdn_launch.h, Tile): W is taken transposed (Kg^T T^T), so a
+// lane holds token 16 I + l16 and four consecutive key channels of each of the two
+// channel tiles, which together are its 16-byte piece of fragment WN(I, wave) (stored
+// negated); U is taken as it stands (T (diag(beta) V)), so a lane holds four consecutive
+// tokens of one value channel, its 8-byte piece of U(slice, I).  DW / DU select the
+// products formed (kg or vb may be null for the other).
 template <int C, typename TT = float, bool DW = true, bool DU = true>
 __device__ __forceinline__ void wy_products(const TT *T, int as, const _Float16 *kg, const _Float16 *vb,
-                                            char *wout, char *utout, int wave, int l16, int g4) {
+                                            char *tile, int wave, int l16, int g4) {
     typedef _Float16 hf;
+    const int lane = 16 * g4 + l16;
 #pragma unroll
     for (int I = 0; I < C / 16; ++I) {
         f32x4 acc[2][2];
@@ -57,7 +59,8 @@ __device__ __forceinline__ void wy_products(const TT *T, int as, const _Float16 
         for (int j = 0; j < 2; ++j) acc[j][0] = acc[j][1] = zero4();
 #pragma unroll
         for (int kb = 0; kb <= (I >> 1); ++kb) {
-            // T^T as the B operand: column = token 16I + l16, slots = tokens 32kb + 8G + e
+            // T's row 16I + l16 as an A operand, or T^T's column as a B operand: slots =
+            // tokens 32kb + 8G + e
             const TT *tr = T + (16 * I + l16) * as + 32 * kb + 8 * g4;
             Frag<hf> ft;
             if constexpr (sizeof(TT) == 2) {
@@ -75,26 +78,38 @@ __device__ __forceinline__ void wy_products(const TT *T, int as, const _Float16 
             for (int j = 0; j < 2; ++j) {
                 const int c0 = 16 * (2 * wave + j);
                 if constexpr (DW) mma(acc[j][0], wy_frag_t(kg, c0, kb, l16, g4), ft);
-                if constexpr (DU) mma(acc[j][1], wy_frag_t(vb, c0, kb, l16, g4), ft);
+                if constexpr (DU) mma(acc[j][1], ft, wy_frag_t(vb, c0, kb, l16, g4));
             }
         }
-        const int r = 16 * I + l16;
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int c = 16 * (2 * wave + j) + 4 * g4;
-            f16x4 w, u;
+        if constexpr (DW) {   // -W[16I + l16][32 wave + 4 g4 + e] (e < 4), [32 wave + 16 + 4 g4 + e - 4]
+            f16x8 w;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                w[i] = (hf)acc[j][0][i];
-                u[i] = (hf)acc[j][1][i];
+                w[i] = (hf)(-acc[0][0][i]);
+                w[4 + i] = (hf)(-acc[1][0][i]);
             }
-            if constexpr (DW) *reinterpret_cast<f16x4 *>(wout + (r * 128 + c) * 2) = w;
-            if constexpr (DU) {   // token r of U^T rows c .. c + 3
+            *reinterpret_cast<f16x8 *>(tile + Tile<C>::wn(I, wave) + 16 * lane) = w;
+        }
+        if constexpr (DU) {   // U[16I + 4 g4 + i][16 (2 wave + j) + l16]
 #pragma unroll
-                for (int i = 0; i < 4; ++i) reinterpret_cast<hf *>(utout)[(c + i) * C + r] = u[i];
+            for (int j = 0; j < 2; ++j) {
+                f16x4 u;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) u[i] = (hf)acc[j][1][i];
+                *reinterpret_cast<f16x4 *>(tile + Tile<C>::u(2 * wave + j, I) + 8 * lane) = u;
             }
         }
     }
+}
+
+// P[16I + l16][16J + 4 g4 + i], i = 0..3 (a 16x16 gram tile taken transposed) into the
+// lane's half of fragment P(I, J / 2).  J <= I; for even I the diagonal tile's fragment
+// also covers tile (I, I + 1), above the diagonal, whose half is zeroed with it.
+template <int C>
+__device__ __forceinline__ void store_p_frag(char *tile, int I, int J, int l16, int g4, const f16x4 &x) {
+    char *pf = tile + Tile<C>::p(I, J >> 1) + 16 * (16 * g4 + l16) + 8 * (J & 1);
+    *reinterpret_cast<f16x4 *>(pf) = x;
+    if (J == I && (I & 1) == 0) *reinterpret_cast<f16x4 *>(pf + 8) = f16x4{};
 }
 
 }  // namespace gdn

@@ -3,299 +3,396 @@
 //
 // The map kernels (kda_map.hip, gdn_map.hip) have left, per chunk and value head, the
 // products that do not depend on the state: with T = (I + A)^-1,
-//   W = T diag(beta) Kg,  U = T diag(beta) V,  P,  Qg,  Kl,  gl = exp(Gamma_last)
-// (Kg = K (.) exp(Gamma), Qg = Q (.) exp(Gamma), Kl = K (.) exp(Gamma_last - Gamma)).  What
-// remains depends on the state S (Dv x Dk) and runs chunk after chunk, as ops #5-#6 of the
-// Map-Reduce-Map pipeline ("Empowering Hybrid Attention Models on NPUs", section 2.1; the
-// chunk-first order of section 5):
+//   WN = -T diag(beta) Kg,  U = T diag(beta) V,  P,  Qg,  Kl,  gl = exp(Gamma_last)
+// (Kg = K (.) exp(Gamma), Qg = Q (.) exp(Gamma), Kl = K (.) exp(Gamma_last - Gamma)), as
+// MFMA operand fragments (gdn_launch.h, Tile).  What remains depends on the state S
+// (Dv x Dk) and runs chunk after chunk, as ops #5-#6 of the Map-Reduce-Map pipeline
+// ("Empowering Hybrid Attention Models on NPUs", section 2.1; the chunk-first order of
+// section 5):
 //
-//   v = U - W S^T            (= T diag(beta) (V - Kg S^T), the WY form of the solve)
+//   v = U + WN S^T           (= T diag(beta) (V - Kg S^T), the WY form of the solve)
 //   O = Qg S^T + P v,
 //   S <- S Diag(gl) + v^T Kl.
 //
-// With the inverse applied in the map, v is one product with S away from the state, and a
-// chunk needs two dependent stages on the chain's critical path instead of three.  The
-// chain waves follow gdn_prefill_pipe.hip (the state slice in registers, W S^T and Q S^T
-// from a 16-bit copy of it in LDS, the update in place) with every product in fp16.  The
-// column-wise split of S is the same: one workgroup per (sequence, value head, 16 value
-// channels).
+// Value channels are independent in all three (S's rows never mix), so one workgroup
+// owns 16 of them for one (sequence, value head) and needs nothing from the others.
 //
-// Kl and U come from the map transposed (Kl^T [key][token], U^T [value ch][token]), so
-// the update's Kl^T operand and the U term of v are plain row segments in LDS.
+// The recurrence runs on ONE wave and never leaves its registers.  It holds S^T (128 key
+// x 16 value channels) as eight fp32 16x16 accumulators; read in pairs, an accumulator's
+// rows are the eight reduction slots of an MFMA operand (the slot order pi of the tile
+// layout), so fp16 copies of S^T are the B operands of v = U + WN S^T as they stand, and
+// v's token tiles are likewise the B operands of the update S^T <- gl S^T + Kl^T v.  A
+// chunk is 4 x C/16 + 8 x C/32 MFMAs (32 at C = 64) on one SIMD with no barrier between
+// them.  Their A operands (WN, Kl, U, gl: 34.5 KB at C = 64) come from LDS: a wave64
+// 16-byte global load holds the issuing wave ~16 cycles in the address unit, so the
+// recurrence issues none.  Two loader waves (operand halves A: WN, U, gl and B: Kl)
+// stream each chunk's tiles from L2 into a two-buffer LDS ring, issued two chunks ahead
+// into a second register set.  (Each of a head's 8 workgroups reads the same tiles; a
+// head's workgroups share one XCD and so one L2.)
 //
-// Roles: waves 0-3 load the workspace tiles one chunk ahead and commit them to LDS, and
-// form the outputs, which nothing downstream in the chunk waits for; waves 4-7 run only
-// the recurrence.  Wave W (of either group) owns the 16-token tiles W and W + 4 of the
-// chunk (those that exist) for v, Q S^T and O, and key channels [32W, 32W + 32) for the
-// update.  A chunk takes two barrier-separated phases:
-//   phase 1: chain v(c)        | loaders: commit P, Kl, gl of c; Q S^T(c) from the state copy
-//   phase 2: chain S update    | loaders: commit W, Qg, U of c + 1; O(c) = Q S^T + P v
-// Each tile is committed after its last reader of the previous chunk and before its
-// first reader, so one LDS copy of every tile suffices.  LDS is 74 KB at C = 64 and
-// 154 KB at C = 128.
+// Two output waves form O^T = S Qg^T + v^T P^T, half of the token tiles each, from the
+// fp16 state and v fragments the recurrence wave leaves in one of two LDS exchange slots
+// per chunk, their Qg and P fragments loaded a chunk ahead from L2.  O^T puts four
+// consecutive value channels of one token in a lane: one 8-byte store.
+//
+// One barrier per chunk orders the roles.  Between barriers c - 1 and c (barrier -1 ends
+// the loaders' prologue, which puts chunk 0 in the ring): the recurrence wave reads ring
+// buffer c % 2 and fills exchange slot c % 2; the loaders put chunk c + 1 into buffer
+// (c + 1) % 2, which the recurrence wave last read before barrier c - 1; the output waves
+// read exchange slot (c - 1) % 2, filled before barrier c - 1 and refilled after barrier c.
+//
+// Measured and not kept (H16 T4096): three ring buffers with the next chunk's operands
+// read in the shadow of the update products; progress counters in LDS instead of
+// barriers; loaders and output waves split by chunk parity; the recurrence split over
+// two waves by key halves with a partial-v exchange.  Each was slower: the operand
+// stream, not the recurrence's issue, sets the chunk period (the tiles come from the
+// Infinity Cache or HBM, whose round trip the two-chunk prefetch barely covers).
 #include "gdn_device.h"
 #include "gdn_launch.h"
-
-#include <type_traits>
 
 namespace gdn {
 namespace kdachain {
 
 typedef _Float16 hf;
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int DK = 128;
 constexpr int DV = 128;
-constexpr int DVS = 16;        // value channels per workgroup
-constexpr int THREADS = 512;   // 4 loader + 4 chain waves
-constexpr int KS = DK + 16;    // fp16 row stride of W, Qg and the state copy (288 B)
+constexpr int DVS = 16;         // value channels per workgroup
+constexpr int NSL = DV / DVS;   // workgroups per (sequence, head)
+// wave 0: the recurrence; 1, 2: the outputs; 3, 4: the loaders (operand halves A, B)
+constexpr int THREADS = 320;
 
 template <int C>
 struct Cfg {
-    static constexpr int NT = C / 16;          // 16-token tiles
-    static constexpr int TPW = (NT + 3) / 4;   // tiles per wave (0 for waves 2, 3 at C = 32)
-    // (ownership tests are written so that the compiler drops them wherever every wave owns
-    // its tiles: a branch around the loaders' loads or stores makes the compiler's count of
-    // outstanding vector-memory operations conservative)
-    static constexpr int TS = C + 16;          // fp16 row stride of v^T
-    static constexpr int TP = C + 8;           // fp16 row stride of P, Kl^T and U^T
-    static constexpr int SEGS = C / 8;         // 16-byte segments per C-token row
-    static constexpr int KL_N = 128 * SEGS / 256;           // Kl^T segments per loader thread
-    static constexpr int P_SEGS = C * SEGS;                 // P segments (128 at C = 32)
-    static constexpr int P_N = (P_SEGS + 255) / 256;
-    static constexpr int W_N = C * 16 / 256;                // W, Qg segments per loader thread
-    static constexpr int U_SEGS = 16 * SEGS;                // the U^T slice's segments
+    static constexpr int NT = C / 16;             // 16-token tiles
+    static constexpr int KB = C / 32;             // 32-token reduction blocks
+    static constexpr int OT = NT / 2;             // token tiles per output wave
+    // loaders and output waves keep a second register set (loads issued two chunks
+    // ahead) up to C = 64; at C = 128 one chunk's operands are already 128 registers
+    static constexpr bool DB = C <= 64;
+    // output wave o's k-th tile (the two waves take tiles 0, 3, 4, 7 and 1, 2, 5, 6, which
+    // gives both the same number of P fragments) and its P fragment count
+    __device__ static constexpr int tile(int k, int o) { return 4 * (k >> 1) + ((k & 1) ? 3 - o : o); }
+    static constexpr int npf(int k) { return 2 * (k >> 1) + (k & 1) + 1; }
+    static constexpr int NPO = OT == 1 ? 1 : OT == 2 ? 3 : 10;   // P fragments per output wave
 };
+static_assert(Cfg<64>::npf(0) + Cfg<64>::npf(1) == Cfg<64>::NPO, "");
+static_assert(Cfg<128>::npf(0) + Cfg<128>::npf(1) + Cfg<128>::npf(2) + Cfg<128>::npf(3) == Cfg<128>::NPO, "");
 
+__device__ __forceinline__ f32x4 mfma(const f16x8 &a, const f16x8 &b, const f32x4 &c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// LDS: the exchange slots and the operand ring (81 KB at C = 64, 153 KB at C = 128).
 template <int C>
 struct __align__(16) Smem {
     using F = Cfg<C>;
-    hf S[DVS * KS];            // fp16 copy of the state slice [value ch][key ch]
-    hf Vh[DVS * F::TS];        // v^T
-    hf U[DVS * F::TP];         // U^T slice [value ch][token]
-    float gl[DK];              // exp(Gamma_last) per key channel
-    hf P[C * F::TP];
-    hf W[C * KS];
-    hf Qg[C * KS];
-    hf Kl[DK * F::TP];         // Kl^T [key ch][token]
+    f16x8 xs[2][(4 + F::KB) * 64];   // S^T (4) and v (KB) fragments, lane-major
+    struct Ops {
+        f16x8 w[F::NT * 4 * 64];  // WN fragments (t, kb), lane-major
+        f16x8 kl[8 * F::KB * 64]; // Kl fragments (i, kb)
+        u32x2 u[F::NT * 64];      // the workgroup's U slice, per token tile
+        f32x4 gl[32];             // exp(Gamma_last) per key channel
+    } ob[2];
 };
-
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-
-// Loader registers: the tiles of one chunk between their load and their commit.
-template <int C>
-struct StageA {       // P, Kl^T, gl: read in phase 2
-    u32x4 p[Cfg<C>::P_N], kl[Cfg<C>::KL_N], gl;
-};
-template <int C>
-struct StageB {       // W, Qg, U^T: read in phase 1
-    u32x4 w[Cfg<C>::W_N], qg[Cfg<C>::W_N], u;
-};
+static_assert(sizeof(Smem<128>) <= 160 * 1024 && sizeof(Smem<64>) <= 160 * 1024, "the LDS holds the ring");
 
 struct Work {
     const char *ws;       // workspace tile of this (sequence, head) at its first chunk
     size_t slot_stride;   // bytes from one chunk's tile to the next (Hv tiles)
-    int bos, eos, nchunks, h, dv0;
+    int bos, eos, nchunks, h, dv0, slice;
 };
 
-__device__ __forceinline__ int chunk_clamp(const Work &wk, int c) { return min(c, wk.nchunks - 1); }
-
-// Loader thread ld (0..255).  Where a tile has fewer segments than threads, the rest read
-// its last segment again and do not commit.
+// The workspace tile of chunk c as a buffer (clamped to the last chunk: prefetches past the
+// end read it again).  Operands are read with buffer loads: a lane's byte offset is one
+// VGPR for every load, the tile and the fragment offsets are scalars, so no load needs a
+// 64-bit address computed in vector registers, and every access is bounded by the tile.
 template <int C>
-__device__ __forceinline__ void load_a(StageA<C> &st, const Work &wk, int c, int ld) {
-    using F = Cfg<C>;
-    const char *tile = wk.ws + (size_t)chunk_clamp(wk, c) * wk.slot_stride;
-#pragma unroll
-    for (int p = 0; p < F::P_N; ++p)
-        st.p[p] = *reinterpret_cast<const u32x4 *>(
-            tile + Tile<C>::P + (F::P_SEGS % 256 != 0 ? min(ld + 256 * p, F::P_SEGS - 1) : ld + 256 * p) * 16);
-#pragma unroll
-    for (int p = 0; p < F::KL_N; ++p)
-        st.kl[p] = *reinterpret_cast<const u32x4 *>(tile + Tile<C>::KLT + (ld + 256 * p) * 16);
-    st.gl = *reinterpret_cast<const u32x4 *>(tile + Tile<C>::GL + (ld & 31) * 16);
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const Work &wk, int c) {
+    const char *tile = wk.ws + (size_t)min(c, wk.nchunks - 1) * wk.slot_stride;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(tile), 0, (int)Tile<C>::BYTES, 0x00020000);
 }
 
+__device__ __forceinline__ f16x8 ld_frag(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+    return __builtin_bit_cast(f16x8, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
+// ---- loaders ------------------------------------------------------------------------
+
+// The loaders' registers for one chunk: A takes gl, U and WN, B takes Kl.
+template <int C, bool A>
+struct LoadRegs;
 template <int C>
-__device__ __forceinline__ void commit_a(const StageA<C> &st, Smem<C> &s, int ld) {
+struct LoadRegs<C, true> {
+    f16x8 w[Cfg<C>::NT * 4];
+    u32x2 u[Cfg<C>::NT];
+    f32x4 gl;                 // lanes 0..31: 4 key channels each
+};
+template <int C>
+struct LoadRegs<C, false> {
+    f16x8 kl[8 * Cfg<C>::KB];
+};
+
+template <int C, bool A>
+__device__ __forceinline__ void load_ops(LoadRegs<C, A> &rg, const Work &wk, int c, int lane) {
     using F = Cfg<C>;
+    using TL = Tile<C>;
+    const __amdgpu_buffer_rsrc_t r = tile_rsrc<C>(wk, c);
+    if constexpr (A) {
+        rg.gl = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, 16 * (lane & 31), TL::GL, 0));
 #pragma unroll
-    for (int p = 0; p < F::P_N; ++p) {
-        const int idx = ld + 256 * p, row = idx / F::SEGS, seg = idx % F::SEGS;
-        // a guard only where P has fewer segments than threads (C = 32): a branch here
-        // would make the compiler's count of outstanding loads conservative
-        if constexpr (F::P_SEGS % 256 != 0) {
-            if (idx < F::P_SEGS) *reinterpret_cast<u32x4 *>(&s.P[row * F::TP + seg * 8]) = st.p[p];
-        } else {
-            *reinterpret_cast<u32x4 *>(&s.P[row * F::TP + seg * 8]) = st.p[p];
+        for (int t = 0; t < F::NT; ++t)
+            rg.u[t] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, 8 * lane, TL::u(wk.slice, t), 0));
+#pragma unroll
+        for (int t = 0; t < F::NT; ++t)
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) rg.w[t * 4 + kb] = ld_frag(r, 16 * lane, TL::wn(t, kb));
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int kb = 0; kb < F::KB; ++kb) rg.kl[i * F::KB + kb] = ld_frag(r, 16 * lane, TL::kl(i, kb));
+    }
+}
+
+template <int C, bool A>
+__device__ __forceinline__ void store_ops(const LoadRegs<C, A> &rg, typename Smem<C>::Ops &ob, int lane) {
+    using F = Cfg<C>;
+    if constexpr (A) {
+        if (lane < 32) ob.gl[lane] = rg.gl;
+#pragma unroll
+        for (int t = 0; t < F::NT; ++t) ob.u[t * 64 + lane] = rg.u[t];
+#pragma unroll
+        for (int j = 0; j < F::NT * 4; ++j) ob.w[j * 64 + lane] = rg.w[j];
+    } else {
+#pragma unroll
+        for (int j = 0; j < 8 * F::KB; ++j) ob.kl[j * 64 + lane] = rg.kl[j];
+    }
+}
+
+// A loader wave's run: before barrier c it puts chunk c + 1 into buffer (c + 1) % 2 from
+// registers loaded two chunks earlier, and issues the loads of chunk c + 3 into them (one
+// register set at C = 128: chunk c + 2, loaded right after).
+template <int C, bool A>
+__device__ __forceinline__ void loader_run(Smem<C> &sm, const Work &wk, int lane) {
+    const int n = wk.nchunks;
+    if constexpr (Cfg<C>::DB) {
+        LoadRegs<C, A> r0, r1;
+        load_ops(r0, wk, 0, lane);
+        load_ops(r1, wk, 1, lane);
+        store_ops(r0, sm.ob[0], lane);
+        load_ops(r0, wk, 2, lane);
+        __syncthreads();
+        for (int c = 0; c < n; c += 2) {
+            store_ops(r1, sm.ob[1], lane);
+            load_ops(r1, wk, c + 3, lane);
+            __syncthreads();
+            if (c + 1 >= n) break;
+            store_ops(r0, sm.ob[0], lane);
+            load_ops(r0, wk, c + 4, lane);
+            __syncthreads();
         }
-    }
-#pragma unroll
-    for (int p = 0; p < F::KL_N; ++p) {
-        const int idx = ld + 256 * p, row = idx / F::SEGS, seg = idx % F::SEGS;
-        *reinterpret_cast<u32x4 *>(&s.Kl[row * F::TP + seg * 8]) = st.kl[p];
-    }
-    if (ld < 32) *reinterpret_cast<u32x4 *>(&s.gl[ld * 4]) = st.gl;
-}
-
-template <int C>
-__device__ __forceinline__ void load_b(StageB<C> &st, const Work &wk, int c, int ld) {
-    using F = Cfg<C>;
-    const char *tile = wk.ws + (size_t)chunk_clamp(wk, c) * wk.slot_stride;
-#pragma unroll
-    for (int p = 0; p < F::W_N; ++p) {
-        st.w[p] = *reinterpret_cast<const u32x4 *>(tile + Tile<C>::W + (ld + 256 * p) * 16);
-        st.qg[p] = *reinterpret_cast<const u32x4 *>(tile + Tile<C>::QG + (ld + 256 * p) * 16);
-    }
-    // U^T slice: 16 rows (value channels dv0 ..) x C / 8 segments
-    const int ui = F::U_SEGS >= 256 ? ld : (ld & (F::U_SEGS - 1)), ur = ui / F::SEGS, us = ui % F::SEGS;
-    st.u = *reinterpret_cast<const u32x4 *>(tile + Tile<C>::UT + ((wk.dv0 + ur) * C + 8 * us) * 2);
-}
-
-template <int C>
-__device__ __forceinline__ void commit_b(const StageB<C> &st, Smem<C> &s, int ld) {
-    using F = Cfg<C>;
-#pragma unroll
-    for (int p = 0; p < F::W_N; ++p) {
-        const int idx = ld + 256 * p, row = idx >> 4, seg = idx & 15;
-        *reinterpret_cast<u32x4 *>(&s.W[row * KS + seg * 8]) = st.w[p];
-        *reinterpret_cast<u32x4 *>(&s.Qg[row * KS + seg * 8]) = st.qg[p];
-    }
-    if (ld < F::U_SEGS) *reinterpret_cast<u32x4 *>(&s.U[(ld / F::SEGS) * F::TP + 8 * (ld % F::SEGS)]) = st.u;
-}
-
-// Phase 1, chain wave W: v = ukeep U - W S^T for its token tiles (lane = value channel, rows
-// = tokens), stored transposed.  ukeep is 1, or 0 for the identity rows of a segment.
-template <int C>
-__device__ __forceinline__ void chain_v(Smem<C> &s, int W, int l16, int g4, float ukeep) {
-    using F = Cfg<C>;
-    const hf *srow = s.S + l16 * KS + 8 * g4;
-    Frag<hf> fs[4];
-#pragma unroll
-    for (int k = 0; k < F::TPW; ++k) {
-        const int t = W + 4 * k;
-        if (F::NT >= 4 * (k + 1) || t < F::NT) {   // compile-time true unless C = 32
-            const hf *wrow = s.W + (16 * t + l16) * KS + 8 * g4;
-            f32x4 ws = zero4();
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                if (k == 0) fs[kb].load8(srow + 32 * kb);   // interleaved with the first tile's
-                Frag<hf> fw;
-                fw.load8(wrow + 32 * kb);
-                mma(ws, fw, fs[kb]);
-            }
-            const int t0 = 16 * t + 4 * g4;
-            const f16x4 u = *reinterpret_cast<const f16x4 *>(&s.U[l16 * F::TP + t0]);
-            f16x4 x;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) x[i] = (hf)(ukeep * (float)u[i] - ws[i]);
-            *reinterpret_cast<f16x4 *>(&s.Vh[l16 * F::TS + t0]) = x;
-        }
-    }
-}
-
-// Phase 1, loader wave W (off the chain's critical path): (Q S^T)^T = S Qg^T for its
-// token tiles (lane = token, rows = value channels 4G..4G+3), from the state copy, which
-// holds the chunk's starting state until phase 2.
-template <int C>
-__device__ __forceinline__ void loader_QS(const Smem<C> &s, int W, int l16, int g4, f32x4 (&qs)[Cfg<C>::TPW]) {
-    using F = Cfg<C>;
-    const hf *srow = s.S + l16 * KS + 8 * g4;
-    Frag<hf> fs[4];
-#pragma unroll
-    for (int k = 0; k < F::TPW; ++k) {
-        const int t = W + 4 * k;
-        qs[k] = zero4();
-        if (F::NT >= 4 * (k + 1) || t < F::NT) {   // compile-time true unless C = 32
-            const hf *qrow = s.Qg + (16 * t + l16) * KS + 8 * g4;
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                if (k == 0) fs[kb].load8(srow + 32 * kb);
-                Frag<hf> fq;
-                fq.load8(qrow + 32 * kb);
-                mma(qs[k], fs[kb], fq);
-            }
+    } else {
+        LoadRegs<C, A> r0;
+        load_ops(r0, wk, 0, lane);
+        store_ops(r0, sm.ob[0], lane);
+        load_ops(r0, wk, 1, lane);
+        __syncthreads();
+        for (int c = 0; c < n; ++c) {
+            store_ops(r0, sm.ob[(c + 1) & 1], lane);
+            load_ops(r0, wk, c + 2, lane);
+            __syncthreads();
         }
     }
 }
 
-// Phase 2, loader wave W: O^T = S Qg^T + v^T P^T for its token tiles, stored as IO to o.
-// In the segment mode `kind` picks the destination, all [token][head][channel]: 0 IO to o
-// (segment 0), 1 fp16 to a.o0 (value rows of later segments), 2 fp16 to a.e (identity
-// rows); one 8-byte store for each, with no branch between them (a branch around stores
-// here would make the compiler's count of outstanding vector-memory operations
-// conservative).
+// ---- the recurrence -------------------------------------------------------------------
+
+// One chunk c of the recurrence: v = ukeep U + WN S^T, then S^T <- gl S^T + Kl^T v, with
+// the operands from ring buffer c % 2.  The fp16 S^T and v fragments go to exchange slot
+// c % 2.  ukeep is 1, or 0 for the identity rows of a segment (no U term).
+template <int C, bool PERCH>
+__device__ __forceinline__ void chain_step(f32x4 (&st)[8], Smem<C> &sm, int c, int lane, bool ukeep) {
+    using F = Cfg<C>;
+    const typename Smem<C>::Ops &ob = sm.ob[c & 1];
+    const int g4 = lane >> 4;
+    // the v phase's operands first, then the update's (LDS returns them in order)
+    f16x8 w[F::NT][4];
+    u32x2 u[F::NT];
+#pragma unroll
+    for (int t = 0; t < F::NT; ++t) u[t] = ob.u[t * 64 + lane];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int t = 0; t < F::NT; ++t) w[t][kb] = ob.w[(t * 4 + kb) * 64 + lane];
+    f32x4 gl[PERCH ? 8 : 1];
+    if constexpr (PERCH) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) gl[i] = ob.gl[4 * i + g4];
+    } else {
+        gl[0] = ob.gl[0];
+    }
+    f16x8 kl[8][F::KB];
+#pragma unroll
+    for (int kb = 0; kb < F::KB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) kl[i][kb] = ob.kl[(i * F::KB + kb) * 64 + lane];
+
+    f16x8 *xs = sm.xs[c & 1];
+    f16x8 sb[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            sb[kb][e] = (hf)st[2 * kb][e];
+            sb[kb][4 + e] = (hf)st[2 * kb + 1][e];
+        }
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) xs[kb * 64 + lane] = sb[kb];
+    f32x4 v[F::NT];
+#pragma unroll
+    for (int t = 0; t < F::NT; ++t) {
+        const f16x4 uu = __builtin_bit_cast(f16x4, u[t]);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[t][q] = ukeep ? (float)uu[q] : 0.f;
+    }
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int t = 0; t < F::NT; ++t) v[t] = mfma(w[t][kb], sb[kb], v[t]);
+    // the decay of the state (off the v products' path)
+    if constexpr (PERCH) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) st[i] *= gl[i];
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) st[i] *= gl[0][0];
+    }
+    f16x8 vb[F::KB];
+#pragma unroll
+    for (int kb = 0; kb < F::KB; ++kb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            vb[kb][e] = (hf)v[2 * kb][e];
+            vb[kb][4 + e] = (hf)v[2 * kb + 1][e];
+        }
+#pragma unroll
+    for (int kb = 0; kb < F::KB; ++kb) xs[(4 + kb) * 64 + lane] = vb[kb];
+#pragma unroll
+    for (int kb = 0; kb < F::KB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) st[i] = mfma(kl[i][kb], vb[kb], st[i]);
+}
+
+// ---- the outputs ----------------------------------------------------------------------
+
+template <int C>
+struct OutOps {
+    using F = Cfg<C>;
+    f16x8 qg[F::OT][4];
+    f16x8 p[F::NPO];
+};
+
+template <int C>
+__device__ __forceinline__ void load_out(OutOps<C> &op, const Work &wk, int c, int o, int lane) {
+    using F = Cfg<C>;
+    using TL = Tile<C>;
+    const __amdgpu_buffer_rsrc_t r = tile_rsrc<C>(wk, c);
+    int pi = 0;
+#pragma unroll
+    for (int k = 0; k < F::OT; ++k) {
+        const int t = F::tile(k, o);
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) op.qg[k][kb] = ld_frag(r, 16 * lane, TL::qg(t, kb));
+#pragma unroll
+        for (int j = 0; j < F::npf(k); ++j) op.p[pi++] = ld_frag(r, 16 * lane, TL::p(t, j));
+    }
+}
+
+// Chunk c's outputs on output wave o: O^T = S Qg^T + v^T P^T for its token tiles, from the
+// exchange slot.  In the segment mode `kind` picks the destination, all
+// [token][head][channel]: 0 IO to o (segment 0), 1 fp16 to a.o0 (value rows of later
+// segments), 2 fp16 to a.e (identity rows); one 8-byte store for each, with no branch
+// between them.
 template <typename IO, int C, bool SEG>
-__device__ __forceinline__ void loader_O(const Smem<C> &s, const KdaArgs &a, int W, int l16, int g4,
-                                         const f32x4 (&qs)[Cfg<C>::TPW], int h, int dv0, int tok0, int nval,
-                                         int kind) {
+__device__ __forceinline__ void out_step(const OutOps<C> &op, const Smem<C> &sm, int c, const KdaArgs &a, int o,
+                                         int lane, int h, int dv0, int tok0, int nval, int kind) {
     using F = Cfg<C>;
+    const int l16 = lane & 15, g4 = lane >> 4;
+    const f16x8 *xs = sm.xs[c & 1];
+    f16x8 sb[4], vb[F::KB];
 #pragma unroll
-    for (int k = 0; k < F::TPW; ++k) {
-        const int t = W + 4 * k;
-        if (F::NT >= 4 * (k + 1) || t < F::NT) {   // compile-time true unless C = 32
-            f32x4 acc = qs[k];
-            const hf *ph = s.P + (16 * t + l16) * F::TP + 8 * g4;
+    for (int kb = 0; kb < 4; ++kb) sb[kb] = xs[kb * 64 + lane];
 #pragma unroll
-            for (int kb = 0; kb < (C >= 64 ? 2 : 1) + 2 * k; ++kb) {
-                // tokens 32kb ..: past the diagonal P is zero (tiles W < 2 at C = 64 take
-                // the zero block rather than a branch)
-                Frag<hf> fp, fv;
-                fp.load8(ph + 32 * kb);
-                fv.load8(s.Vh + l16 * F::TS + 32 * kb + 8 * g4);
-                mma(acc, fv, fp);
+    for (int kb = 0; kb < F::KB; ++kb) vb[kb] = xs[(4 + kb) * 64 + lane];
+    int pi = 0;
+#pragma unroll
+    for (int k = 0; k < F::OT; ++k) {
+        const int t = F::tile(k, o);
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) acc = mfma(sb[kb], op.qg[k][kb], acc);
+#pragma unroll
+        for (int j = 0; j < F::npf(k); ++j) acc = mfma(vb[j], op.p[pi++], acc);
+        const int tok = 16 * t + l16;
+        const size_t at = ((size_t)(tok0 + tok) * a.Hv + h) * DV + dv0 + 4 * g4;
+        if constexpr (SEG) {
+            typename Vec4<IO>::type yio;
+            f16x4 yh;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                yio[i] = Cvt<IO>::from_f32(acc[i]);
+                yh[i] = (hf)acc[i];
             }
-            const int tok = 16 * t + l16;
-            const size_t at = ((size_t)(tok0 + tok) * a.Hv + h) * DV + dv0 + 4 * g4;
-            if constexpr (SEG) {
-                typename Vec4<IO>::type yio;
-                f16x4 yh;
+            const u32x2 bits = kind == 0 ? __builtin_bit_cast(u32x2, yio) : __builtin_bit_cast(u32x2, yh);
+            char *base = kind == 0 ? (char *)a.o : kind == 1 ? (char *)a.o0 : (char *)a.e;
+            if (tok < nval) *reinterpret_cast<u32x2 *>(base + at * 2) = bits;
+        } else if (tok < nval) {
+            typename Vec4<IO>::type y;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    yio[i] = Cvt<IO>::from_f32(acc[i]);
-                    yh[i] = (hf)acc[i];
-                }
-                typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-                const u32x2 bits = kind == 0 ? __builtin_bit_cast(u32x2, yio) : __builtin_bit_cast(u32x2, yh);
-                char *base = kind == 0 ? (char *)a.o : kind == 1 ? (char *)a.o0 : (char *)a.e;
-                if (tok < nval) *reinterpret_cast<u32x2 *>(base + at * 2) = bits;
-            } else if (tok < nval) {
-                typename Vec4<IO>::type y;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) y[i] = Cvt<IO>::from_f32(acc[i]);
-                *reinterpret_cast<typename Vec4<IO>::type *>(reinterpret_cast<IO *>(a.o) + at) = y;
-            }
+            for (int i = 0; i < 4; ++i) y[i] = Cvt<IO>::from_f32(acc[i]);
+            *reinterpret_cast<typename Vec4<IO>::type *>(reinterpret_cast<IO *>(a.o) + at) = y;
         }
     }
 }
 
-// Phase 2, chain wave W: the update of key channels [32W, 32W + 32) of the state slice:
-// S^T rows (key channels) 32W + 16mt + 4G + r, column = value channel.
-template <int C>
-__device__ __forceinline__ void chain_update(Smem<C> &s, int W, int l16, int g4, f32x4 (&st)[2]) {
+// Output wave o's run: after barrier c it forms chunk c's outputs; before barrier c it
+// issues the loads of chunk c + 1 into its other register set (one set at C = 128).
+template <typename IO, int C, bool SEG>
+__device__ __forceinline__ void output_run(const Smem<C> &sm, const KdaArgs &a, const Work &wk, int o, int lane,
+                                           int kind) {
     using F = Cfg<C>;
-    Frag<hf> fv[C / 32];   // v^T rows (value channel l16), tokens 32kb + 8g4 .. + 7
-#pragma unroll
-    for (int kb = 0; kb < C / 32; ++kb) fv[kb].load8(s.Vh + l16 * F::TS + 32 * kb + 8 * g4);
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-        // Kl^T rows 32W + 16mt + l16 (key channels), tokens 32kb + 8g4 .. + 7
-        const hf *kr = s.Kl + (32 * W + 16 * mt + l16) * F::TP + 8 * g4;
-        const int kc = 32 * W + 16 * mt + 4 * g4;
-        const f32x4 gl = *reinterpret_cast<const f32x4 *>(&s.gl[kc]);
-        f32x4 acc = st[mt] * gl;
-#pragma unroll
-        for (int kb = 0; kb < C / 32; ++kb) {
-            Frag<hf> fk;
-            fk.load8(kr + 32 * kb);
-            mma(acc, fk, fv[kb]);
+    const int n = wk.nchunks;
+    auto step = [&](const OutOps<C> &op, int c) {
+        const int tok0 = wk.bos + c * C;
+        out_step<IO, C, SEG>(op, sm, c, a, o, lane, wk.h, wk.dv0, tok0, min(C, wk.eos - tok0), kind);
+    };
+    if constexpr (F::DB) {
+        OutOps<C> op0, op1;
+        load_out(op0, wk, 0, o, lane);
+        __syncthreads();
+        for (int c = 0; c < n; c += 2) {
+            load_out(op1, wk, c + 1, o, lane);
+            __syncthreads();
+            step(op0, c);
+            if (c + 1 >= n) break;
+            load_out(op0, wk, c + 2, o, lane);
+            __syncthreads();
+            step(op1, c + 1);
         }
-        st[mt] = acc;
-        f16x4 x;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) x[i] = (hf)acc[i];
-        *reinterpret_cast<f16x4 *>(&s.S[l16 * KS + kc]) = x;
+    } else {
+        OutOps<C> op0;
+        __syncthreads();
+        for (int c = 0; c < n; ++c) {
+            load_out(op0, wk, c, o, lane);
+            __syncthreads();
+            step(op0, c);
+        }
     }
 }
+
+// ---- the kernel ------------------------------------------------------------------------
 
 // The sequence of rank r when the N <= 64 sequences of cu are ordered by decreasing length
 // (ties by index), by one wave: lane i counts the sequences ahead of sequence i.
@@ -318,17 +415,13 @@ __device__ __forceinline__ int longest_first(const int32_t *cu, int N, int r, in
 // real start state.  Segment 0 stores its outputs to o; later segments store theirs as
 // fp16 to a.o0 (value rows) or a.e (identity rows); end states go to a.sseg (X
 // transposed).  gdn_seg.hip joins them.
-template <typename IO, int C, bool SEG>
-__global__ __launch_bounds__(THREADS) void kda_chain_kernel(const KdaArgs a) {
-    using F = Cfg<C>;
-    __shared__ Smem<C> s;
+template <typename IO, int C, bool SEG, bool PERCH>
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2))) void kda_chain_kernel(const KdaArgs a) {
+    __shared__ Smem<C> sm;
     const int tid = threadIdx.x;
-    const int lane = tid & 63, l16 = lane & 15, g4 = lane >> 4;
+    const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const bool is_loader = wave < 4;
-    const int W = wave & 3;
 
-    constexpr int NSL = DV / DVS;
     // XCD-aware mapping.  Workgroups are dispatched to the 8 XCDs in turn (blockIdx % 8).
     // The GS workgroups that read the same tiles (a head's 8 slices; in the segment mode a
     // segment's value and identity slices) form a group, and group g runs on XCD g % 8, so
@@ -360,6 +453,7 @@ __global__ __launch_bounds__(THREADS) void kda_chain_kernel(const KdaArgs a) {
     }
     Work wk;
     wk.h = h;
+    wk.slice = slice;
     wk.dv0 = slice * DVS;
     const int bos = a.cu ? a.cu[n] : 0, eos = a.cu ? a.cu[n + 1] : a.T_tot;
     const int len = eos > bos ? eos - bos : 0;
@@ -373,82 +467,52 @@ __global__ __launch_bounds__(THREADS) void kda_chain_kernel(const KdaArgs a) {
     wk.slot_stride = (size_t)a.Hv * Tile<C>::BYTES;
     wk.ws = a.ws + ((size_t)(bos / C + n + c0) * a.Hv + h) * Tile<C>::BYTES;
     const int kind = seg == 0 ? 0 : ident ? 2 : 1;
-    const float ukeep = ident ? 0.f : 1.f;
-
-    f32x4 st[2];
     const size_t sbase = ((size_t)n * a.Hv + h) * (size_t)DV * DK;
-    if (!is_loader) {
+    const int l16 = lane & 15, g4 = lane >> 4;
+
+    if (wave == 0) {
+        // S^T rows (key channels) 16 i + 4 G + q, column = value channel dv0 + m
+        f32x4 st[8];
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-            const int dk = 32 * W + 16 * mt + 4 * g4;
+        for (int i = 0; i < 8; ++i) {
+            const int dk = 16 * i + 4 * g4;
             f32x4 x = zero4();
             if (seg == 0 && a.s0) x = *reinterpret_cast<const f32x4 *>(a.s0 + sbase + (size_t)(wk.dv0 + l16) * DK + dk);
             if (ident) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) x[i] = dk + i == wk.dv0 + l16 ? 1.f : 0.f;
+                for (int q = 0; q < 4; ++q) x[q] = dk + q == wk.dv0 + l16 ? 1.f : 0.f;
             }
-            st[mt] = x;
-            f16x4 y;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) y[i] = (hf)x[i];
-            *reinterpret_cast<f16x4 *>(&s.S[l16 * KS + dk]) = y;
+            st[i] = x;
         }
-    }
-
-    if (wk.nchunks > 0) {
-        StageA<C> sa;
-        StageB<C> sb;
-        if (is_loader) {
-            load_b(sb, wk, 0, tid);
-            commit_b(sb, s, tid);
-            load_a(sa, wk, 0, tid);
-            load_b(sb, wk, 1, tid);
-        }
-        __syncthreads();
-        if (is_loader) {
+        if (wk.nchunks > 0) {
+            __syncthreads();   // the loaders' prologue: chunk 0 is in the ring
             for (int c = 0; c < wk.nchunks; ++c) {
-                const int tok0 = wk.bos + c * C;
-                const int nval = min(C, wk.eos - tok0);
-                commit_a(sa, s, tid);
-                load_a(sa, wk, c + 1, tid);
-                f32x4 qs[F::TPW];
-                loader_QS(s, W, l16, g4, qs);
-                __syncthreads();
-                commit_b(sb, s, tid);
-                load_b(sb, wk, c + 2, tid);
-                loader_O<IO, C, SEG>(s, a, W, l16, g4, qs, h, wk.dv0, tok0, nval, kind);
-                __syncthreads();
-            }
-        } else {
-            for (int c = 0; c < wk.nchunks; ++c) {
-                chain_v(s, W, l16, g4, SEG ? ukeep : 1.f);
-                __syncthreads();
-                chain_update(s, W, l16, g4, st);
+                chain_step<C, PERCH>(st, sm, c, lane, !ident);
                 __syncthreads();
             }
         }
-    }
-
-    if constexpr (SEG) {
-        if (!is_loader) {
+        if constexpr (SEG) {
             float *sb = a.sseg + ((((size_t)n * a.Hv + h) * a.nseg + seg) * 2 + (ident ? 1 : 0)) * DV * DK;
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt) {
-                const int dk = 32 * W + 16 * mt + 4 * g4, r = wk.dv0 + l16;
+            for (int i = 0; i < 8; ++i) {
+                const int dk = 16 * i + 4 * g4, r = wk.dv0 + l16;
                 if (ident) {   // X^T [key][row]
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) sb[(size_t)(dk + i) * DV + r] = st[mt][i];
+                    for (int q = 0; q < 4; ++q) sb[(size_t)(dk + q) * DV + r] = st[i][q];
                 } else {
-                    *reinterpret_cast<f32x4 *>(sb + (size_t)r * DK + dk) = st[mt];
+                    *reinterpret_cast<f32x4 *>(sb + (size_t)r * DK + dk) = st[i];
                 }
             }
-        }
-    } else if (a.sN && !is_loader) {
+        } else if (a.sN) {
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-            const int dk = 32 * W + 16 * mt + 4 * g4;
-            *reinterpret_cast<f32x4 *>(a.sN + sbase + (size_t)(wk.dv0 + l16) * DK + dk) = st[mt];
+            for (int i = 0; i < 8; ++i)
+                *reinterpret_cast<f32x4 *>(a.sN + sbase + (size_t)(wk.dv0 + l16) * DK + 16 * i + 4 * g4) = st[i];
         }
+    } else if (wk.nchunks > 0 && wave < 3) {
+        output_run<IO, C, SEG>(sm, a, wk, wave - 1, lane, kind);
+    } else if (wk.nchunks > 0) {
+        if (wave == 3) loader_run<C, true>(sm, wk, lane);
+        else loader_run<C, false>(sm, wk, lane);
     }
 }
 
@@ -456,18 +520,18 @@ __global__ __launch_bounds__(THREADS) void kda_chain_kernel(const KdaArgs a) {
 
 namespace {
 
-template <bool SEG>
+template <bool SEG, bool PERCH>
 hipError_t chain_launch(const KdaArgs &a, bool f16, int chunk, hipStream_t stream) {
     // groups of GS workgroups (see the kernel), padded to whole rounds of 8 groups
-    constexpr unsigned long long GS = (kdachain::DV / kdachain::DVS) * (SEG ? 2 : 1);
+    constexpr unsigned long long GS = kdachain::NSL * (SEG ? 2 : 1);
     const unsigned long long groups = (unsigned long long)a.N * a.Hv * (SEG ? (unsigned long long)a.nseg : 1ull);
     const unsigned long long wgs = 8 * GS * ((groups + 7) / 8);
     if (wgs > 0x7fffffffULL) return hipErrorInvalidValue;
     const dim3 grid((unsigned)wgs), block(kdachain::THREADS);
-#define KDA_CHAIN_LAUNCH(C)                                                                                   \
-    do {                                                                                                      \
-        if (f16) hipLaunchKernelGGL((kdachain::kda_chain_kernel<_Float16, C, SEG>), grid, block, 0, stream, a); \
-        else hipLaunchKernelGGL((kdachain::kda_chain_kernel<__bf16, C, SEG>), grid, block, 0, stream, a);      \
+#define KDA_CHAIN_LAUNCH(C)                                                                                           \
+    do {                                                                                                              \
+        if (f16) hipLaunchKernelGGL((kdachain::kda_chain_kernel<_Float16, C, SEG, PERCH>), grid, block, 0, stream, a); \
+        else hipLaunchKernelGGL((kdachain::kda_chain_kernel<__bf16, C, SEG, PERCH>), grid, block, 0, stream, a);      \
     } while (0)
     switch (chunk) {
         case 32: KDA_CHAIN_LAUNCH(32); break;
@@ -481,13 +545,13 @@ hipError_t chain_launch(const KdaArgs &a, bool f16, int chunk, hipStream_t strea
 
 }  // namespace
 
-hipError_t launch_kda_chain(const KdaArgs &a, bool f16, int chunk, hipStream_t stream) {
-    return chain_launch<false>(a, f16, chunk, stream);
+hipError_t launch_kda_chain(const KdaArgs &a, bool f16, int chunk, bool per_channel, hipStream_t stream) {
+    return per_channel ? chain_launch<false, true>(a, f16, chunk, stream) : chain_launch<false, false>(a, f16, chunk, stream);
 }
 
-hipError_t launch_seg_chain(const KdaArgs &a, bool f16, int chunk, hipStream_t stream) {
+hipError_t launch_seg_chain(const KdaArgs &a, bool f16, int chunk, bool per_channel, hipStream_t stream) {
     if (a.nseg < 1) return hipErrorInvalidValue;
-    return chain_launch<true>(a, f16, chunk, stream);
+    return per_channel ? chain_launch<true, true>(a, f16, chunk, stream) : chain_launch<true, false>(a, f16, chunk, stream);
 }
 
 int kda_chain_lds_bytes() { return (int)sizeof(kdachain::Smem<64>); }

@@ -12,7 +12,7 @@
 //   T = (I + A)^-1,
 // and the S-dependent half (kda_chain.hip) needs W = T diag(beta) (K (.) exp(Gamma)),
 // U = T diag(beta) V, Q (.) exp(Gamma), K (.) exp(Gamma_last - Gamma) and
-// exp(Gamma_last) (U and the last K transposed, in the layouts the chain reads).  None of this depends on the state, so every chunk of every head is
+// exp(Gamma_last), stored as its MFMA operand fragments (gdn_launch.h, Tile).  None of this depends on the state, so every chunk of every head is
 // one independent workgroup here (the Map phases #1-#4 of the page's Map-Reduce-Map
 // pipeline), and the results go to a workspace tile the chain kernel reads: with a
 // per-channel gate this map is several times the chain's work, and doing it once per
@@ -129,11 +129,12 @@ __device__ __forceinline__ Frag<hf> frag_raw(const IO *x, int X, int kb, int l16
     return r;
 }
 
-__device__ __forceinline__ void store_p(char *tile, int r, int c, const f32x4 &x) {
+// P tile (I, J), J <= I, as the lane holds it (row 16I + l16, columns 16J + 4g4 + i)
+__device__ __forceinline__ void store_p(char *tile, int I, int J, int l16, int g4, const f32x4 &x) {
     f16x4 v;
 #pragma unroll
     for (int i = 0; i < 4; ++i) v[i] = (hf)x[i];
-    *reinterpret_cast<f16x4 *>(tile + WS_OFF_P + (r * CH + c) * 2) = v;
+    store_p_frag<CH>(tile, I, J, l16, g4, v);
 }
 
 // Tile (I, J), I > J, of A and P at one reference level, whole.  The product is taken
@@ -152,9 +153,8 @@ __device__ __forceinline__ f32x4 offdiag_tile(const Smem<IO> &s, char *tile, int
         mma(accA, kj, ki);
         mma(accP, kj, qi);
     }
-    const int r = 16 * I + l16, c = 16 * J + 4 * g4;
-    store_p(tile, r, c, accP);
-    return accA * s.beta[r];
+    store_p(tile, I, J, l16, g4, accP);
+    return accA * s.beta[16 * I + l16];
 }
 
 // Diagonal tile X at level 2^LB: the full 16x16 products, of which this level keeps the
@@ -258,8 +258,7 @@ __global__ __launch_bounds__(THREADS, 2) void kda_map_kernel(const KdaArgs a) {
     // diag(beta) (K (.) exp(Gamma)) kept for the WY products
     f16x2 kgb[16];
     {
-        hf *qg = reinterpret_cast<hf *>(tile + WS_OFF_QG);
-        f16x8 kl[2][2];   // Kl^T rows ch, ch + 1 over this block's 16 tokens
+        f16x4 kl[2][4];   // Kl of channels ch, ch + 1 over this block's 16 tokens, 4 at a time
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int t = 16 * b + i;
@@ -273,21 +272,26 @@ __global__ __launch_bounds__(THREADS, 2) void kda_map_kernel(const KdaArgs a) {
             kgb[i][1] = (hf)(k1 * e1 * bt);
             f16x2 x;
             x[0] = (hf)(Cvt<IO>::to_f32(qv[0]) * e0); x[1] = (hf)(Cvt<IO>::to_f32(qv[1]) * e1);
-            *reinterpret_cast<f16x2 *>(&qg[t * DK + ch]) = x;
-            kl[0][i >> 3][i & 7] = (hf)(k0 * l0);
-            kl[1][i >> 3][i & 7] = (hf)(k1 * l1);
+            // Qg(token tile b, channel block ch / 32): channels ch, ch + 1 share a lane's slots
+            const int j = ch & 31;
+            *reinterpret_cast<f16x2 *>(tile + Tile<CH>::qg(b, ch >> 5) + 16 * frag_lane(j, i) + frag_byte(j)) = x;
+            kl[0][i >> 2][i & 3] = (hf)(k0 * l0);
+            kl[1][i >> 2][i & 3] = (hf)(k1 * l1);
         }
-        hf *klt = reinterpret_cast<hf *>(tile + WS_OFF_KLT);
+        // Kl(key tile c / 16, token block b / 2): lane (G, c % 16), half b % 2
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            *reinterpret_cast<f16x8 *>(klt + (ch + j) * CH + 16 * b) = kl[j][0];
-            *reinterpret_cast<f16x8 *>(klt + (ch + j) * CH + 16 * b + 8) = kl[j][1];
+            const int c = ch + j;
+#pragma unroll
+            for (int G = 0; G < 4; ++G)
+                *reinterpret_cast<f16x4 *>(tile + Tile<CH>::kl(c >> 4, b >> 1) + 16 * (16 * G + (c & 15)) + 8 * (b & 1)) =
+                    kl[j][G];
         }
         if (b == 0) {
             f32x2 gl;
             gl[0] = F0[15] * post0;
             gl[1] = F1[15] * post1;
-            *reinterpret_cast<f32x2 *>(tile + WS_OFF_GL + ch * 4) = gl;
+            *reinterpret_cast<f32x2 *>(tile + Tile<CH>::GL + ch * 4) = gl;
         }
     }
 
@@ -389,11 +393,8 @@ __global__ __launch_bounds__(THREADS, 2) void kda_map_kernel(const KdaArgs a) {
         float *A = s.sv.A;
         const int r = 16 * wave + l16;
         *reinterpret_cast<f32x4 *>(&A[r * AS + 16 * wave + 4 * g4]) = selA * s.beta[r];
-        store_p(tile, r, 16 * wave + 4 * g4, selP);
-        for (int J = wave + 1; J < 4; ++J) {
-            *reinterpret_cast<f32x4 *>(&A[r * AS + 16 * J + 4 * g4]) = zero4();
-            store_p(tile, r, 16 * J + 4 * g4, zero4());
-        }
+        store_p(tile, wave, wave, l16, g4, selP);   // (and the zero half of an even diagonal's fragment)
+        for (int J = wave + 1; J < 4; ++J) *reinterpret_cast<f32x4 *>(&A[r * AS + 16 * J + 4 * g4]) = zero4();
         switch (wave) {
             case 0: *reinterpret_cast<f32x4 *>(&A[(16 + l16) * AS + 4 * g4]) = offA0; break;
             case 1:
@@ -456,7 +457,7 @@ __global__ __launch_bounds__(THREADS, 2) void kda_map_kernel(const KdaArgs a) {
         __syncthreads();
     }
     // #4 W = T diag(beta) Kg and U = T diag(beta) V to the workspace
-    wy_products<CH>(s.sv.T, AS, s.wy.Kb, s.wy.Vb, tile + WS_OFF_W, tile + WS_OFF_UT, wave, l16, g4);
+    wy_products<CH>(s.sv.T, AS, s.wy.Kb, s.wy.Vb, tile, wave, l16, g4);
 }
 
 }  // namespace kdamap

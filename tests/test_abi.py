@@ -125,8 +125,9 @@ def test_plan(lib):
 
 @pytest.mark.parametrize("C", [32, 128])
 def test_split_workspace_size_other_chunks(lib, C):
-    # T_tot / C + N slots of C^2 * 2 + C * 1024 + 512 bytes
-    tile = C * C * 2 + C * 1024 + 512
+    # T_tot / C + N slots of C * 1024 + (C / 32) (C / 32 + 1) * 1024 + 512 bytes (the lower
+    # triangle of P as 16x32 fragments)
+    tile = C * 1024 + (C // 32) * (C // 32 + 1) * 1024 + 512
     assert gdn.prefill_split_workspace_size(1, 4096, 16, C, lib=lib) == (4096 // C + 1) * 16 * tile
     assert gdn.prefill_split_workspace_size(3, 100, 2, C, lib=lib) == (100 // C + 3) * 2 * tile
     with pytest.raises(gdn.GDNError):
@@ -135,10 +136,10 @@ def test_split_workspace_size_other_chunks(lib, C):
 
 @pytest.mark.parametrize("size_fn", ["kda_workspace_size", "prefill_split_workspace_size"])
 def test_workspace_size(lib, size_fn):
-    # one 74,240-byte tile per value head and chunk slot, T_tot / 64 + N slots
+    # one 72,192-byte tile per value head and chunk slot, T_tot / 64 + N slots
     f = getattr(gdn, size_fn)
-    assert f(1, 4096, 16, lib=lib) == (64 + 1) * 16 * 74240
-    assert f(3, 100, 2, lib=lib) == (1 + 3) * 2 * 74240
+    assert f(1, 4096, 16, lib=lib) == (64 + 1) * 16 * 72192
+    assert f(3, 100, 2, lib=lib) == (1 + 3) * 2 * 72192
     with pytest.raises(gdn.GDNError):
         f(1, 10, 1, chunk_size=48, lib=lib)
 
