@@ -244,6 +244,30 @@ gdn_status gdn_prefill_split(const void *q, const void *k, const void *v,
                              void *o, float *final_state, void *stream);
 
 /*
+ * gdn_prefill_split_noalloc -- gdn_prefill_split for callers that cannot allocate device
+ * memory or pass a workspace (code under HIP graph capture, tight serving loops, hosts
+ * that forbid allocation): the same kernels and results, with the workspace taken from a
+ * static array of GDN_NOALLOC_SCRATCH_BYTES in the library, one per GPU, held from the
+ * library's first use on that GPU until the process ends.  The call allocates nothing.
+ * Arguments as for gdn_prefill_split without workspace / workspace_bytes.
+ *
+ *   Sizes whose gdn_prefill_split_workspace_size exceeds GDN_NOALLOC_SCRATCH_BYTES
+ *   (96 MiB: e.g. 64-token chunks of up to 1394 (chunk slot, value head) pairs, which
+ *   holds T_tot = 4096 at Hv = 16) return GDN_ERR_UNSUPPORTED before anything runs.
+ *   Every call on one GPU uses that GPU's one array: two calls that overlap in time on
+ *   the same GPU (different streams, or host threads without ordering) race and give
+ *   undefined results.  Calls ordered on one stream are safe; nothing needs clearing
+ *   between them.
+ */
+#define GDN_NOALLOC_SCRATCH_BYTES ((size_t)96 << 20)
+gdn_status gdn_prefill_split_noalloc(const void *q, const void *k, const void *v,
+                                     const float *g, const float *beta,
+                                     const float *initial_state, const int32_t *cu_seqlens,
+                                     int32_t N, int32_t T_tot, int32_t Hk, int32_t Hv,
+                                     int32_t Dk, int32_t Dv, int32_t chunk_size, gdn_dtype io_dtype,
+                                     void *o, float *final_state, void *stream);
+
+/*
  * gdn_prefill_split_fused -- gdn_prefill_split with the input prologue applied in the map
  * kernel's load path, as gdn_prefill_fused does for gdn_prefill: `prologue` is a bitwise
  * or of gdn_prologue_flags (unknown bits return GDN_ERR_INVALID_ARGUMENT), and q, k, g,

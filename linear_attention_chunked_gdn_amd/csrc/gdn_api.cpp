@@ -12,6 +12,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 namespace {
@@ -372,6 +373,73 @@ gdn_status gdn_prefill_split_fused(const void *q, const void *k, const void *v, 
                                    size_t workspace_bytes, void *o, float *final_state, void *stream) {
     return split_impl(q, k, v, g, beta, initial_state, cu_seqlens, N, T_tot, Hk, Hv, Dk, Dv, chunk_size, io_dtype,
                       prologue, workspace, workspace_bytes, o, final_state, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// gdn_prefill_split_noalloc's workspace: a static array in the library's code object, so
+// each GPU the library is loaded on holds its own copy until the process ends.  In host
+// code `scratch` names a host-side stand-in, not device memory: the kernels get the
+// device address that hipGetSymbolAddress returns for the current device, looked up once
+// per device and kept.  The split kernels write every workspace byte they read, so the
+// array needs no clearing between calls.
+static __device__ __align__(256) char scratch[GDN_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxDevices];
+
+gdn_status scratch_on_current_device(void **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(GDN_ERR_DEVICE, "hipGetDevice failed: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(GDN_ERR_UNSUPPORTED, "device %d: static scratch is tracked for devices 0..%d", dev,
+                    kMaxDevices - 1);
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(GDN_ERR_DEVICE, "hipGetSymbolAddress(scratch) on device %d failed: %s", dev,
+                        hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+gdn_status gdn_prefill_split_noalloc(const void *q, const void *k, const void *v, const float *g,
+                                     const float *beta, const float *initial_state, const int32_t *cu_seqlens,
+                                     int32_t N, int32_t T_tot, int32_t Hk, int32_t Hv, int32_t Dk, int32_t Dv,
+                                     int32_t chunk_size, gdn_dtype io_dtype, void *o, float *final_state,
+                                     void *stream) {
+    // every argument is checked before the device is touched
+    gdn_status st = check_prefill(q, k, v, g, beta, initial_state, cu_seqlens, N, T_tot, Hk, Hv, Dk, Dv,
+                                  chunk_size, true, io_dtype, o, final_state, 1, nullptr, 0);
+    if (st != GDN_OK) return st;
+    if (io_dtype == GDN_F32)
+        return fail(GDN_ERR_UNSUPPORTED, "gdn_prefill_split_noalloc takes bf16 or fp16 q, k, v, o");
+    size_t need = 0;
+    st = gdn_prefill_split_workspace_size(N, T_tot, Hv, chunk_size, &need);
+    if (st != GDN_OK) return st;
+    if (need > (size_t)GDN_NOALLOC_SCRATCH_BYTES)
+        return fail(GDN_ERR_UNSUPPORTED,
+                    "gdn_prefill_split_noalloc: N=%d, T_tot=%d, Hv=%d, chunk_size=%d need %zu workspace bytes, "
+                    "more than the %zu of its static scratch (gdn_prefill_split takes a caller workspace)",
+                    N, T_tot, Hv, chunk_size, need, (size_t)GDN_NOALLOC_SCRATCH_BYTES);
+    if (T_tot == 0 && !final_state) return ok();
+    void *ws = nullptr;
+    st = scratch_on_current_device(&ws);
+    if (st != GDN_OK) return st;
+    return split_impl(q, k, v, g, beta, initial_state, cu_seqlens, N, T_tot, Hk, Hv, Dk, Dv, chunk_size, io_dtype, 0,
+                      ws, (size_t)GDN_NOALLOC_SCRATCH_BYTES, o, final_state, stream);
 }
 
 // Segmented prefill: the split path's map, the chain in segments, the fix-up.

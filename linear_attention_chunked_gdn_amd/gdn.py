@@ -71,6 +71,8 @@ def load_library(path: str = LIB_PATH):
     lib.gdn_prefill_split_workspace_size.restype = ctypes.c_int
     lib.gdn_prefill_split.argtypes = lib.gdn_kda_prefill.argtypes
     lib.gdn_prefill_split.restype = ctypes.c_int
+    lib.gdn_prefill_split_noalloc.argtypes = lib.gdn_prefill.argtypes
+    lib.gdn_prefill_split_noalloc.restype = ctypes.c_int
     lib.gdn_prefill_split_fused.argtypes = [vp, vp, vp, fp, fp, fp, ip, i32, i32, i32, i32, i32, i32, i32,
                                             ctypes.c_int, ctypes.c_uint32, vp, ctypes.c_size_t, vp, fp, vp]
     lib.gdn_prefill_split_fused.restype = ctypes.c_int
@@ -305,6 +307,52 @@ def prefill_split(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
     return _prefill_ws("gdn_prefill_split", prefill_split_workspace_size, False, q, k, v, g, beta,
                        initial_state, cu_seqlens, chunk_size, output_final_state, out, final_state,
                        workspace, lib)
+
+
+NOALLOC_SCRATCH_BYTES = 96 << 20   # GDN_NOALLOC_SCRATCH_BYTES
+
+
+def prefill_split_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                          beta: torch.Tensor, initial_state: Optional[torch.Tensor] = None,
+                          cu_seqlens: Optional[torch.Tensor] = None, chunk_size: int = CHUNK,
+                          output_final_state: bool = True, out: Optional[torch.Tensor] = None,
+                          final_state: Optional[torch.Tensor] = None, lib=None
+                          ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """``prefill_split`` without a workspace (gdn_prefill_split_noalloc): the library's
+    static per-GPU scratch stands in for it.  Pass ``out`` (and ``final_state``) to make
+    the call allocate nothing at all; sizes beyond NOALLOC_SCRATCH_BYTES of workspace
+    raise GDNError."""
+    lib = lib or load_library()
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("gdn_prefill_split_noalloc runs on the GPU only; q is on " + str(dev))
+    io = _io_code(q)
+    T, Hk, Dk = q.shape
+    Hv, Dv = v.shape[1], v.shape[2]
+    N = 1 if cu_seqlens is None else cu_seqlens.shape[0] - 1
+    _need(q, "q", q.dtype, (T, Hk, Dk), dev)
+    _need(k, "k", q.dtype, (T, Hk, Dk), dev)
+    _need(v, "v", q.dtype, (T, Hv, Dv), dev)
+    _need(g, "g", torch.float32, (T, Hv), dev)
+    _need(beta, "beta", torch.float32, (T, Hv), dev)
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,), dev)
+    if initial_state is not None:
+        _need(initial_state, "initial_state", torch.float32, (N, Hv, Dv, Dk), dev)
+    if out is None:
+        out = torch.empty((T, Hv, Dv), dtype=q.dtype, device=dev)
+    _need(out, "out", q.dtype, (T, Hv, Dv), dev)
+    if output_final_state and final_state is None:
+        final_state = torch.empty((N, Hv, Dv, Dk), dtype=torch.float32, device=dev)
+    if final_state is not None:
+        _need(final_state, "final_state", torch.float32, (N, Hv, Dv, Dk), dev)
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        st = lib.gdn_prefill_split_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
+                                           _ptr(cu_seqlens), N, T, Hk, Hv, Dk, Dv, chunk_size, io, _ptr(out),
+                                           _ptr(final_state), ctypes.c_void_p(stream))
+    _check(lib, st, "gdn_prefill_split_noalloc")
+    return out, final_state
 
 
 def prefill_seg_workspace_size(N: int, T: int, Hv: int, chunk_size: int = CHUNK, segments: int = 1,

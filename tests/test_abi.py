@@ -34,7 +34,7 @@ def test_header_declares_the_boundary():
          "gdn_kda_workspace_size", "gdn_kda_prefill", "gdn_kda_decode_step", "gdn_prefill_fused",
          "gdn_decode_step_fused", "gdn_prefill_split", "gdn_prefill_split_workspace_size",
          "gdn_prefill_seg", "gdn_prefill_seg_workspace_size", "gdn_prefill_seg_choose",
-         "gdn_prefill_split_fused", "gdn_kda_prefill_seg"])
+         "gdn_prefill_split_fused", "gdn_kda_prefill_seg", "gdn_prefill_split_noalloc"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -202,6 +202,50 @@ def test_split_prefill_rejects(lib, over, status, msg):
 def test_split_prefill_nothing_to_do_is_ok(lib):
     assert _ws_prefill(lib, "gdn_prefill_split", q=None, k=None, v=None, g=None, beta=None, o=None, ws=None,
                        wsb=0, T=0) == 0
+
+
+def _noalloc(lib, **over):
+    # fake, widely spaced, never-dereferenced addresses: validation fails before any use
+    t = 1 << 40
+    a = dict(q=t, k=2 * t, v=3 * t, g=4 * t, beta=5 * t, s0=None, cu=None, N=1, T=10, Hk=2, Hv=4,
+             Dk=128, Dv=128, C=64, io=1, o=6 * t, fs=None)
+    a.update(over)
+    p = lambda x: None if x is None else ctypes.c_void_p(x)  # noqa: E731
+    return lib.gdn_prefill_split_noalloc(p(a["q"]), p(a["k"]), p(a["v"]), p(a["g"]), p(a["beta"]),
+                                         p(a["s0"]), p(a["cu"]), a["N"], a["T"], a["Hk"], a["Hv"], a["Dk"],
+                                         a["Dv"], a["C"], a["io"], p(a["o"]), p(a["fs"]), None)
+
+
+def _split_ws(lib, N, T, Hv, C):
+    n = ctypes.c_size_t()
+    assert lib.gdn_prefill_split_workspace_size(N, T, Hv, C, ctypes.byref(n)) == 0
+    return n.value
+
+
+@pytest.mark.parametrize("over,status,msg", [
+    (dict(io=0), 2, "bf16 or fp16"),
+    (dict(C=16), 2, "chunk_size"),
+    (dict(g=4 * (1 << 40) + 2), 1, "g must be 4-byte aligned"),
+    (dict(N=2), 1, "cu_seqlens is required"),
+    # 64-token chunks: 1394 (slot, head) tiles fit in the 96 MiB scratch, 1395 do not
+    (dict(T=(1395 - 1) * 64, Hv=1, Hk=1), 2, "static scratch"),
+    (dict(T=1 << 20, Hv=16, Hk=16), 2, "static scratch"),
+])
+def test_split_noalloc_rejects(lib, over, status, msg):
+    assert _noalloc(lib, **over) == status
+    assert msg in lib.gdn_last_error().decode()
+
+
+def test_split_noalloc_limit(lib):
+    assert gdn.NOALLOC_SCRATCH_BYTES == 96 << 20
+    # the largest single-head sequence that fits, and the H16 T4096 prefill
+    assert _split_ws(lib, 1, (1394 - 1) * 64, 1, 64) <= gdn.NOALLOC_SCRATCH_BYTES
+    assert _split_ws(lib, 1, 1394 * 64, 1, 64) > gdn.NOALLOC_SCRATCH_BYTES
+    assert _split_ws(lib, 1, 4096, 16, 64) <= gdn.NOALLOC_SCRATCH_BYTES
+
+
+def test_split_noalloc_nothing_to_do_is_ok(lib):
+    assert _noalloc(lib, q=None, k=None, v=None, g=None, beta=None, o=None, T=0) == 0
 
 
 def test_kda_decode_rejects(lib):
