@@ -14,6 +14,7 @@ from __future__ import annotations
 
 import json
 import os
+import re
 
 import numpy as np
 
@@ -418,4 +419,35 @@ def pin_prologue_matches_generator(_rec=None):
         _close(raw.v, ref.v, 0.0, "v is drawn the same")
 
 
-PROLOGUE_PINS = [pin_prologue_values, pin_prologue_matches_generator]
+# P3. each flag bit selects its own step and nothing else: flags = 0 is the identity, and
+#     for every subset of the bits exactly the selected tensors change, to the generator's
+#     recipe, while the others come back as drawn.  The bit values are the ones the C
+#     header gives gdn_prologue_flags.
+def pin_prologue_flag_subsets(_rec=None):
+    from linear_attention_chunked_gdn_amd import inputs
+    header = os.path.join(os.path.dirname(GOLDEN), os.pardir, "include", "gdn.h")
+    with open(header) as f:
+        bits = {n: int(b) for n, b in re.findall(r"GDN_PROLOGUE_(\w+)\s*=\s*(\d+)", f.read())}
+    assert bits == {"QK_L2NORM": 1, "BETA_SIGMOID": 2, "G_SOFTPLUS": 4}, bits
+    assert (oracle.PROLOGUE_QK_L2NORM, oracle.PROLOGUE_BETA_SIGMOID, oracle.PROLOGUE_G_SOFTPLUS) == \
+        (bits["QK_L2NORM"], bits["BETA_SIGMOID"], bits["G_SOFTPLUS"]), "oracle flag values"
+    for per_channel in (False, True):
+        raw = inputs.make_custom(52, [33, 7], 2, 4, Dk=16, Dv=8, io="f32", g_shift=1.0,
+                                 per_channel=per_channel, raw=True)
+        ref = inputs.make_custom(52, [33, 7], 2, 4, Dk=16, Dv=8, io="f32", g_shift=1.0,
+                                 per_channel=per_channel)
+        # every step changes its tensors by far more than the tolerances below
+        for a, b in ((raw.q, ref.q), (raw.k, ref.k), (raw.g, ref.g), (raw.beta, ref.beta)):
+            assert np.min(np.abs(np.asarray(a, np.float64) - b)) > 1e-3 or np.max(np.abs(a - b)) > 0.1
+        for flags in range(8):
+            q, k, g, b = oracle.prologue(raw.q, raw.k, raw.g, raw.beta, flags)
+            norm = bool(flags & bits["QK_L2NORM"])
+            sig = bool(flags & bits["BETA_SIGMOID"])
+            sp = bool(flags & bits["G_SOFTPLUS"])
+            _close(q, ref.q if norm else raw.q, 2e-7 if norm else 0.0, f"flags={flags}: q")
+            _close(k, ref.k if norm else raw.k, 2e-7 if norm else 0.0, f"flags={flags}: k")
+            _close(b, ref.beta if sig else raw.beta, 1e-7 if sig else 0.0, f"flags={flags}: beta")
+            _close(g, ref.g if sp else raw.g, 1e-6 if sp else 0.0, f"flags={flags}: g")
+
+
+PROLOGUE_PINS = [pin_prologue_values, pin_prologue_matches_generator, pin_prologue_flag_subsets]

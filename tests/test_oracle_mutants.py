@@ -204,6 +204,14 @@ PROLOGUE_MUTANTS = [
      "norm = np.sqrt(np.sum(x * x, axis=-2, keepdims=True))"),
     ("g = +softplus", "prologue", "g = -softplus(g)", "g = softplus(g)"),
     ("beta flag ignored", "prologue", "beta = sigmoid(beta)", "beta = beta"),
+    # the bit-to-step mapping: a step keyed to another step's bit, or run whatever the bits
+    ("softplus keyed to the sigmoid bit", "prologue", "if flags & PROLOGUE_G_SOFTPLUS:",
+     "if flags & PROLOGUE_BETA_SIGMOID:"),
+    ("sigmoid keyed to the norm bit", "prologue", "if flags & PROLOGUE_BETA_SIGMOID:",
+     "if flags & PROLOGUE_QK_L2NORM:"),
+    ("norm on any flag", "prologue", "if flags & PROLOGUE_QK_L2NORM:", "if flags:"),
+    ("sigmoid always", "prologue", "if flags & PROLOGUE_BETA_SIGMOID:", "if True:"),
+    ("norm of q only", "prologue", "q, k = l2_normalize(q), l2_normalize(k)", "q = l2_normalize(q)"),
 ]
 
 
