@@ -200,24 +200,48 @@ def algorithmic_flops(x, C: int = 64) -> int:
     return total
 
 
-def cpu_baseline(x, min_repeats: int = 3, min_seconds: float = 5.0, prologue: int = 0) -> dict:
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(x, min_repeats: int = 3, min_seconds: float = 5.0, prologue: int = 0,
+                 single_thread: bool = False) -> dict:
     """Median wall time of whole-workload oracle runs (with the input prologue's steps
-    when given): at least min_repeats runs and at least min_seconds of CPU work in total."""
+    when given): at least min_repeats runs and at least min_seconds of CPU work in total,
+    on every OpenMP thread; with single_thread, also one run on one thread."""
     import oracle
     oracle.load_library()
-    times = []
-    while len(times) < min_repeats or sum(times) < min_seconds:
+    cores = oracle.max_threads()
+
+    def run(nthreads):
         t0 = time.perf_counter()
         q, k, g, b = oracle.prologue(x.q, x.k, x.g, x.beta, prologue)
-        oracle.recurrent(q, k, x.v, g, b, x.initial_state, x.cu_seqlens)
-        times.append(time.perf_counter() - t0)
+        oracle.recurrent(q, k, x.v, g, b, x.initial_state, x.cu_seqlens, nthreads=nthreads)
+        return time.perf_counter() - t0
+
+    times = []
+    while len(times) < min_repeats or sum(times) < min_seconds:
+        times.append(run(cores))
     repeats = len(times)
     dt = float(np.median(times))
-    return {"value": x.T_tot / dt, "unit": "tokens/s", "cores": oracle.max_threads(),
-            "kind": "oracle",
-            "sample": f"the whole workload ({x.T_tot} tokens x {x.Hv} heads), fp64 token-by-token "
-                      f"recurrence, OpenMP over (sequence, head); median of {repeats} runs, "
-                      f"{dt:.3f} s each"}
+    threads_used = min(cores, x.N * x.Hv)   # OpenMP over (sequence, head) pairs
+    rec = {"value": x.T_tot / dt, "unit": "tokens/s", "cores": threads_used,
+           "kind": "oracle", "cpu_model": cpu_model(), "omp_threads": cores,
+           "sample": f"the whole workload ({x.T_tot} tokens x {x.Hv} heads), fp64 token-by-token "
+                     f"recurrence, OpenMP over (sequence, head); median of {repeats} runs, "
+                     f"{dt:.3f} s each"}
+    if single_thread:   # last: the oracle keeps the thread count it was last given
+        t1 = run(1)
+        rec["single_thread"] = {"value": x.T_tot / t1, "unit": "tokens/s", "cores": 1,
+                                "sample": f"the whole workload on one thread, one run of {t1:.3f} s"}
+    return rec
 
 
 def decode_bench(x, dev, state0) -> dict:
@@ -407,8 +431,15 @@ def main() -> int:
                          o=torch.empty((x.T_tot, x.Hv, x.Dv), dtype=io, device=dev),
                          fs=torch.empty((x.N, x.Hv, x.Dv, x.Dk), dtype=torch.float32, device=dev)))
 
-    segments = args.segments or gdn.prefill_seg_choose(x.N, x.T_tot, x.Hv, args.chunk)
-    path = "kda" if args.kda else choose_path(x, args.path, args.prologue, segments)
+    auto = None
+    if args.path == "auto" and not args.kda and args.chunk == 64 and not args.segments:
+        # the library's own choice (gdn_prefill_auto_plan), run through gdn_prefill_auto
+        auto = gdn.prefill_auto_plan(x.N, x.T_tot, x.Hv, IO_CODE[x.io], pro)
+        segments = auto["segments"]
+        path = {"one_launch": "pipe", "split": "split", "seg": "seg"}[auto["path"]]
+    else:
+        segments = args.segments or gdn.prefill_seg_choose(x.N, x.T_tot, x.Hv, args.chunk)
+        path = "kda" if args.kda else choose_path(x, args.path, args.prologue, segments)
     if path in ("split", "seg") and x.io == "f32":
         print(f"bench.py: --path {path} takes bf16 or fp16 I/O", file=sys.stderr)
         return 2
@@ -423,10 +454,15 @@ def main() -> int:
                 "seg": lambda N, T, Hv, C: gdn.prefill_seg_workspace_size(N, T, Hv, C, segments)}
     ws = (torch.empty(ws_bytes[path](x.N, x.T_tot, x.Hv, chunk), dtype=torch.uint8, device=dev)
           if path in ws_bytes else None)
+    if auto is not None:
+        ws = torch.empty(max(1, auto["workspace_bytes"]), dtype=torch.uint8, device=dev)
 
     def step(i):
         s = sets[i % copies]
-        if path == "kda":
+        if auto is not None:
+            gdn.prefill_auto(s["q"], s["k"], s["v"], s["g"], s["beta"], s["init"], s["cu"],
+                             out=s["o"], final_state=s["fs"], workspace=ws, prologue=pro)
+        elif path == "kda":
             gdn.kda_prefill(s["q"], s["k"], s["v"], s["g"], s["beta"], s["init"], s["cu"],
                             out=s["o"], final_state=s["fs"], workspace=ws)
         elif path == "split":
@@ -448,38 +484,47 @@ def main() -> int:
     # GPU has no queued work (right after the synchronisation) would be timed as GPU time
     gc.collect()
     gc.disable()
+    # an event between consecutive steps as well: per-step times for the median and minimum
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps - 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0.record(stream)
     for i in range(args.steps):
         step(i)
+        if i < args.steps - 1:
+            evs[i].record(stream)
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     gc.enable()
     gpu_ms = ev0.elapsed_time(ev1)
     ms_per_step = gpu_ms / args.steps
+    marks = [ev0] + evs + [ev1]
+    per_step = [marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)]
     tokens = x.T_tot
 
-    # parity of the timed launches' last output against the oracle (headline sizes only)
-    parity = None
-    if x.T_tot * x.Hv <= (1 << 17):
-        import oracle
-        sys.path.insert(0, os.path.join(ROOT, "tests"))
-        from gpu_support import error_stats
-        s = sets[(args.steps - 1) % copies]
-        q_, k_, g_, b_ = oracle.prologue(x.q, x.k, x.g, x.beta, pro)
-        ro, rf = oracle.recurrent(q_, k_, x.v, g_, b_, x.initial_state, x.cu_seqlens)
-        from gpu_support import TOL_BF16_REL_RMS, TOL_F32_ABS
-        half = x.io != "f32"
-        eo = error_stats(s["o"].double().cpu().numpy(), ro, storage=x.io if half else None)
-        ef = error_stats(s["fs"].double().cpu().numpy(), rf)
-        # 16-bit I/O: kernel error / rms beside the stored outputs' rounding (the tests' bar)
-        ok = (max(eo["kernel_rel_rms"], ef["kernel_rel_rms"]) <= TOL_BF16_REL_RMS if half
-              else max(eo["max_abs"], ef["max_abs"]) <= TOL_F32_ABS)
-        parity = {"o_kernel_err_over_rms": eo["kernel_rel_rms"], "o_max_err_over_rms": eo["rel_rms"],
-                  "state_err_over_rms": ef["rel_rms"], "o_nmse": eo["nmse"], "state_nmse": ef["nmse"],
-                  "within_tolerance": ok}
+    # parity of the timed launches' last output against the oracle: every value head up to
+    # 2^17 (token, head) pairs, else three value heads at the full length (first, middle,
+    # last; the oracle's heads are independent, so a subset is exact)
+    import oracle
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from gpu_support import TOL_BF16_REL_RMS, TOL_F32_ABS, error_stats
+    s = sets[(args.steps - 1) % copies]
+    heads = list(range(x.Hv)) if x.T_tot * x.Hv <= (1 << 17) else sorted({0, x.Hv // 2, x.Hv - 1})
+    xs = x if len(heads) == x.Hv else inputs.select_heads(x, heads)
+    q_, k_, g_, b_ = oracle.prologue(xs.q, xs.k, xs.g, xs.beta, pro)
+    ro, rf = oracle.recurrent(q_, k_, xs.v, g_, b_, xs.initial_state, xs.cu_seqlens)
+    half = x.io != "f32"
+    hsel = torch.tensor(heads, device=dev)
+    eo = error_stats(s["o"].index_select(1, hsel).double().cpu().numpy(), ro, storage=x.io if half else None)
+    ef = error_stats(s["fs"].index_select(1, hsel).double().cpu().numpy(), rf)
+    # 16-bit I/O: kernel error / rms beside the stored outputs' rounding (the tests' bar)
+    ok = (max(eo["kernel_rel_rms"], ef["kernel_rel_rms"]) <= TOL_BF16_REL_RMS if half
+          else max(eo["max_abs"], ef["max_abs"]) <= TOL_F32_ABS)
+    parity = {"value_heads": "all" if len(heads) == x.Hv else heads,
+              "o_kernel_err_over_rms": eo["kernel_rel_rms"], "o_max_err_over_rms": eo["rel_rms"],
+              "state_err_over_rms": ef["rel_rms"], "o_nmse": eo["nmse"], "state_nmse": ef["nmse"],
+              "within_tolerance": ok}
 
     nbytes = algorithmic_bytes(x)
     flops = algorithmic_flops(x, chunk)
@@ -506,6 +551,11 @@ def main() -> int:
                   "dv_per_workgroup": plan["dv_per_workgroup"], "workgroups": plan["workgroups"],
                   "lds_bytes": plan["lds_bytes"], "threads": plan["threads_per_workgroup"],
                   "input_copies_rotated": copies}
+    launch["entry_point"] = "gdn_prefill_auto" if auto is not None else {
+        "kda": "gdn_kda_prefill", "split": "gdn_prefill_split_fused" if pro else "gdn_prefill_split",
+        "seg": "gdn_prefill_seg", "pipe": "gdn_prefill_fused" if pro else "gdn_prefill"}[path]
+    if auto is not None:
+        launch["auto_plan"] = auto
     mfma_peak = FP32_MFMA_PEAK_TFLOPS if x.io == "f32" else BF16_MFMA_PEAK_TFLOPS  # fp16 = bf16 rate
     rec = {
         "metric": KDA_METRIC.format(H=x.Hv, T=x.T_tot) if args.kda else METRIC,
@@ -515,6 +565,8 @@ def main() -> int:
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_per_step,
+        "ms_per_step_median": float(np.median(per_step)),
+        "ms_per_step_min": float(min(per_step)),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -537,7 +589,8 @@ def main() -> int:
         rec["decode"] = decode_bench(x, dev, sets[(args.steps - 1) % copies]["fs"])
     rec["measured_peaks"] = measured_peaks(dev)
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(x, prologue=pro)
+        rec["cpu_baseline"] = cpu_baseline(x, prologue=pro,
+                                           single_thread=args.workload in (0, 1) and args.head_shard == 1)
     print(json.dumps(rec), flush=True)
     return 0
 

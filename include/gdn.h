@@ -19,16 +19,34 @@
  *
  * Conventions for every entry point
  *   - All tensor arguments are DEVICE pointers owned by the caller, row-major and
- *     contiguous, 16-byte aligned.  The library never allocates, frees or retains
- *     device memory and keeps no pointer after the call returns.
+ *     contiguous.  q, k, v, o and the states are 16-byte aligned (the decode steps
+ *     take v and o 4-byte aligned); g and beta 4-byte aligned, except a per-key-channel
+ *     g (16-byte); cu_seqlens 4-byte; workspaces 256-byte.  The library allocates and
+ *     frees no device memory and keeps no pointer after the call returns; the one
+ *     device memory it holds is the static scratch of gdn_prefill_split_noalloc.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and the
  *     call returns without synchronising.  Inputs are never written.
  *   - Argument errors are detected on the host before anything is enqueued; the
  *     call then returns a non-OK status, launches nothing and records a message
  *     retrievable with gdn_last_error() (thread-local).  A failed kernel launch
  *     returns GDN_ERR_DEVICE.  No C++ exception crosses this interface.
- *   - Supported shapes: Dk = Dv = 128 and chunk_size = 64; anything else returns
- *     GDN_ERR_UNSUPPORTED.
+ *   - The contents of cu_seqlens (device memory) are a precondition the kernels do
+ *     not check: with the environment variable GDN_CHECK set (to anything but "" or
+ *     "0"), every prefill entry point first reads cu_seqlens back (ordered after the
+ *     work already on `stream`, then waiting for it) and returns
+ *     GDN_ERR_INVALID_ARGUMENT unless cu[0] = 0, cu is nondecreasing and
+ *     cu[N] = T_tot; not for use under stream capture.
+ *   - Supported shapes: Dk = Dv = 128; chunk_size 64, and also 32 and 128 for the
+ *     scalar-gate two-launch paths (gdn_prefill_split*, gdn_prefill_seg); anything
+ *     else returns GDN_ERR_UNSUPPORTED.
+ *   - Value range with bf16 or fp16 I/O (every prefill entry point): the per-chunk
+ *     products (v = U - W S^T, P, U, W and the decayed keys and queries) and the
+ *     state's 16-bit copy that the recurrence multiplies with are fp16, whose largest
+ *     finite value is 65504.  Results are within tolerance while the entries of v,
+ *     of the states (initial, final and in between) and of o stay below about 6e4 in
+ *     magnitude and g <= 0 (a decay: alpha = exp(g) in (0, 1], as the pages define
+ *     it).  Beyond that the outputs may hold inf or NaN; no error is reported.  fp32
+ *     I/O (gdn_prefill) and the decode steps keep fp32 throughout.
  */
 #ifndef GDN_MI355X_GDN_H
 #define GDN_MI355X_GDN_H
@@ -81,13 +99,13 @@ typedef enum gdn_prologue_flags {
  *   q, k           [T_tot, Hk, Dk]  io_dtype      queries / keys, per key head
  *   v              [T_tot, Hv, Dv]  io_dtype      values, per value head
  *   g              [T_tot, Hv]      fp32          natural log of the decay alpha
- *                                                 (finite; normally <= 0)
+ *                                                 (finite, <= 0; see the value range)
  *   beta           [T_tot, Hv]      fp32          delta-rule write strength
  *   initial_state  [N, Hv, Dv, Dk]  fp32 or NULL  NULL means zero states
  *   cu_seqlens     [N+1]            int32 device  cu[0] = 0, nondecreasing,
- *                                                 cu[N] = T_tot (precondition, not
- *                                                 checked on the device); may be
- *                                                 NULL only when N == 1
+ *                                                 cu[N] = T_tot (precondition,
+ *                                                 checked only under GDN_CHECK); may
+ *                                                 be NULL only when N == 1
  *   N, T_tot       number of sequences (>= 1) and packed tokens (>= 0)
  *   Hk, Hv         key and value head counts, Hv % Hk == 0
  *   Dk, Dv         head dimensions (128)
@@ -351,6 +369,46 @@ gdn_status gdn_prefill_plan(int32_t N, int32_t Hv, int32_t Dv, gdn_dtype io_dtyp
                             int32_t *lds_bytes, int32_t *threads_per_workgroup);
 
 /* Static English name of a status code. */
+/*
+ * gdn_prefill_auto_plan / gdn_prefill_auto -- the prefill (with the input prologue when
+ * `prologue` is nonzero) through whichever of this library's prefill paths is fastest
+ * for these sizes on the current device, with 64-token chunks: the one-launch kernel of
+ * gdn_prefill / gdn_prefill_fused, the two launches of gdn_prefill_split /
+ * gdn_prefill_split_fused, or the segmented gdn_prefill_seg ("Empowering Hybrid
+ * Attention Models on NPUs", section 4: the Chunk-Seg-Seg mapping for few heads and long
+ * sequences).  Same results as gdn_prefill up to rounding.
+ *
+ * gdn_prefill_auto_plan reads the device's compute-unit count and returns, through the
+ * non-NULL pointers, the path (gdn_prefill_path), the segment count (1 unless
+ * GDN_PATH_SEG) and the workspace bytes gdn_prefill_auto needs for these sizes (0 for
+ * GDN_PATH_ONE_LAUNCH; workspace_bytes must be non-NULL).  fp32 I/O always takes the
+ * one-launch path; 16-bit I/O takes a two-launch path when the one-launch kernel's
+ * N * Hv * 8 workgroups would fill at most half of the compute units, or when N > 1,
+ * and the segmented one when gdn_prefill_seg_choose gives more than one segment and
+ * prologue is 0.
+ *
+ * gdn_prefill_auto takes gdn_prefill_fused's arguments (chunk_size is 64) plus a
+ * caller-owned workspace of at least the planned bytes on the same device (256-byte
+ * aligned, overlapping no other argument, not shared by two calls in flight; NULL when
+ * the plan needs none); it plans again and runs the chosen entry point, which checks its
+ * arguments and returns their statuses.
+ */
+typedef enum gdn_prefill_path {
+    GDN_PATH_ONE_LAUNCH = 0,   /* gdn_prefill / gdn_prefill_fused          */
+    GDN_PATH_SPLIT = 1,        /* gdn_prefill_split / gdn_prefill_split_fused */
+    GDN_PATH_SEG = 2           /* gdn_prefill_seg                          */
+} gdn_prefill_path;
+gdn_status gdn_prefill_auto_plan(int32_t N, int32_t T_tot, int32_t Hv, gdn_dtype io_dtype,
+                                 uint32_t prologue, int32_t *path, int32_t *segments,
+                                 size_t *workspace_bytes);
+gdn_status gdn_prefill_auto(const void *q, const void *k, const void *v,
+                            const float *g, const float *beta,
+                            const float *initial_state, const int32_t *cu_seqlens,
+                            int32_t N, int32_t T_tot, int32_t Hk, int32_t Hv,
+                            int32_t Dk, int32_t Dv, gdn_dtype io_dtype, uint32_t prologue,
+                            void *workspace, size_t workspace_bytes,
+                            void *o, float *final_state, void *stream);
+
 const char *gdn_status_string(gdn_status s);
 
 /* Detail of the last non-OK return on the calling thread ("" if none). */

@@ -14,6 +14,7 @@
 #include <cstring>
 #include <mutex>
 #include <string>
+#include <vector>
 
 namespace {
 
@@ -126,6 +127,33 @@ size_t tile_bytes(int32_t c) {
     return c == 32 ? gdn::Tile<32>::BYTES : c == 128 ? gdn::Tile<128>::BYTES : gdn::Tile<64>::BYTES;
 }
 
+// GDN_CHECK set to anything but "" or "0" turns on the checks of device-resident
+// arguments, which cost a device-to-host copy and a wait on the stream per call.
+bool check_enabled() {
+    const char *e = std::getenv("GDN_CHECK");
+    return e && *e && std::strcmp(e, "0") != 0;
+}
+
+// cu_seqlens, read back after the work already queued on `stream` (which may write it),
+// must be a packing of T_tot tokens: cu[0] = 0, nondecreasing, cu[N] = T_tot.  The kernels
+// index q, k, v, o and the workspace with it unchecked.
+gdn_status check_cu_seqlens(const int32_t *cu, int32_t N, int32_t T_tot, void *stream) {
+    std::vector<int32_t> h((size_t)N + 1);
+    const hipStream_t hs = static_cast<hipStream_t>(stream);
+    hipError_t e = hipMemcpyAsync(h.data(), cu, h.size() * sizeof(int32_t), hipMemcpyDeviceToHost, hs);
+    if (e == hipSuccess) e = hipStreamSynchronize(hs);
+    if (e != hipSuccess)
+        return fail(GDN_ERR_DEVICE, "GDN_CHECK: reading cu_seqlens back failed: %s", hipGetErrorString(e));
+    if (h[0] != 0) return fail(GDN_ERR_INVALID_ARGUMENT, "GDN_CHECK: cu_seqlens[0] = %d, not 0", h[0]);
+    for (int32_t n = 0; n < N; ++n)
+        if (h[n + 1] < h[n])
+            return fail(GDN_ERR_INVALID_ARGUMENT, "GDN_CHECK: cu_seqlens decreases at %d (%d, then %d)", n + 1,
+                        h[n], h[n + 1]);
+    if (h[N] != T_tot)
+        return fail(GDN_ERR_INVALID_ARGUMENT, "GDN_CHECK: cu_seqlens[%d] = %d, not T_tot = %d", N, h[N], T_tot);
+    return GDN_OK;
+}
+
 // Host-side checks shared by the prefill entry points (any_chunk: the chunk lengths of
 // split_chunk_ok, else 64 only): g holds g_width values per
 // (token, value head) (1, or Dk for a per-key-channel gate); ws / ws_bytes is the
@@ -134,7 +162,7 @@ gdn_status check_prefill(const void *q, const void *k, const void *v, const floa
                          const float *initial_state, const int32_t *cu_seqlens, int32_t N, int32_t T_tot,
                          int32_t Hk, int32_t Hv, int32_t Dk, int32_t Dv, int32_t chunk_size, bool any_chunk,
                          gdn_dtype io_dtype, const void *o, const float *final_state, size_t g_width,
-                         const void *ws, size_t ws_bytes) {
+                         const void *ws, size_t ws_bytes, void *stream) {
     if (!valid_dtype(io_dtype))
         return fail(GDN_ERR_INVALID_ARGUMENT, "io_dtype %d is not GDN_F32, GDN_BF16 or GDN_F16", (int)io_dtype);
     if (N < 1) return fail(GDN_ERR_INVALID_ARGUMENT, "N=%d must be >= 1", N);
@@ -180,7 +208,7 @@ gdn_status check_prefill(const void *q, const void *k, const void *v, const floa
     if (overlap(ro, rf)) return fail(GDN_ERR_INVALID_ARGUMENT, "o overlaps final_state");
     if (overlap(rw, ro) || overlap(rw, rf))
         return fail(GDN_ERR_INVALID_ARGUMENT, "workspace overlaps an output");
-    return GDN_OK;
+    return check_enabled() && cu_seqlens ? check_cu_seqlens(cu_seqlens, N, T_tot, stream) : GDN_OK;
 }
 
 // Chunk slots of the per-key-channel prefill: chunk j of sequence n uses slot
@@ -197,7 +225,7 @@ gdn_status gdn_prefill(const void *q, const void *k, const void *v, const float 
                        int32_t chunk_size, gdn_dtype io_dtype, void *o, float *final_state,
                        void *stream) {
     const gdn_status cs = check_prefill(q, k, v, g, beta, initial_state, cu_seqlens, N, T_tot, Hk, Hv, Dk,
-                                        Dv, chunk_size, false, io_dtype, o, final_state, 1, nullptr, 0);
+                                        Dv, chunk_size, false, io_dtype, o, final_state, 1, nullptr, 0, stream);
     if (cs != GDN_OK) return cs;
 
     int32_t dvs = 0, wg = 0;
@@ -227,7 +255,7 @@ gdn_status gdn_prefill_fused(const void *q, const void *k, const void *v, const 
                              int32_t chunk_size, gdn_dtype io_dtype, uint32_t prologue, void *o,
                              float *final_state, void *stream) {
     const gdn_status cs = check_prefill(q, k, v, g, beta, initial_state, cu_seqlens, N, T_tot, Hk, Hv, Dk,
-                                        Dv, chunk_size, false, io_dtype, o, final_state, 1, nullptr, 0);
+                                        Dv, chunk_size, false, io_dtype, o, final_state, 1, nullptr, 0, stream);
     if (cs != GDN_OK) return cs;
     if (prologue & ~kPrologueAll)
         return fail(GDN_ERR_INVALID_ARGUMENT, "prologue flags 0x%x include unknown bits", prologue);
@@ -268,7 +296,7 @@ gdn_status gdn_kda_prefill(const void *q, const void *k, const void *v, const fl
                            void *o, float *final_state, void *stream) {
     const gdn_status cs = check_prefill(q, k, v, g, beta, initial_state, cu_seqlens, N, T_tot, Hk, Hv, Dk,
                                         Dv, chunk_size, false, io_dtype, o, final_state, kD, workspace,
-                                        workspace_bytes);
+                                        workspace_bytes, stream);
     if (cs != GDN_OK) return cs;
     if (io_dtype == GDN_F32)
         return fail(GDN_ERR_UNSUPPORTED, "gdn_kda_prefill takes bf16 or fp16 q, k, v, o");
@@ -322,7 +350,7 @@ gdn_status split_impl(const void *q, const void *k, const void *v, const float *
         return fail(GDN_ERR_INVALID_ARGUMENT, "prologue flags 0x%x include unknown bits", prologue);
     const gdn_status cs = check_prefill(q, k, v, g, beta, initial_state, cu_seqlens, N, T_tot, Hk, Hv, Dk,
                                         Dv, chunk_size, true, io_dtype, o, final_state, 1, workspace,
-                                        workspace_bytes);
+                                        workspace_bytes, stream);
     if (cs != GDN_OK) return cs;
     if (io_dtype == GDN_F32)
         return fail(GDN_ERR_UNSUPPORTED, "gdn_prefill_split takes bf16 or fp16 q, k, v, o");
@@ -422,7 +450,7 @@ gdn_status gdn_prefill_split_noalloc(const void *q, const void *k, const void *v
                                      void *stream) {
     // every argument is checked before the device is touched
     gdn_status st = check_prefill(q, k, v, g, beta, initial_state, cu_seqlens, N, T_tot, Hk, Hv, Dk, Dv,
-                                  chunk_size, true, io_dtype, o, final_state, 1, nullptr, 0);
+                                  chunk_size, true, io_dtype, o, final_state, 1, nullptr, 0, stream);
     if (st != GDN_OK) return st;
     if (io_dtype == GDN_F32)
         return fail(GDN_ERR_UNSUPPORTED, "gdn_prefill_split_noalloc takes bf16 or fp16 q, k, v, o");
@@ -493,7 +521,7 @@ gdn_status seg_impl(const char *fn, bool per_channel, const void *q, const void 
                     float *final_state, void *stream) {
     const gdn_status cs = check_prefill(q, k, v, g, beta, initial_state, cu_seqlens, N, T_tot, Hk, Hv, Dk,
                                         Dv, chunk_size, !per_channel, io_dtype, o, final_state,
-                                        per_channel ? (size_t)kD : 1, workspace, workspace_bytes);
+                                        per_channel ? (size_t)kD : 1, workspace, workspace_bytes, stream);
     if (cs != GDN_OK) return cs;
     if (io_dtype == GDN_F32)
         return fail(GDN_ERR_UNSUPPORTED, "%s takes bf16 or fp16 q, k, v, o", fn);
@@ -636,6 +664,90 @@ gdn_status gdn_kda_decode_step(const void *q, const void *k, const void *v, cons
                                const float *beta, float *state, int32_t B, int32_t Hk, int32_t Hv,
                                int32_t Dk, int32_t Dv, gdn_dtype io_dtype, void *o, void *stream) {
     return decode_impl(q, k, v, g, beta, state, B, Hk, Hv, Dk, Dv, io_dtype, o, stream, true, 0);
+}
+
+}  // extern "C"
+
+namespace {
+
+// The path gdn_prefill_auto takes.  fp32 I/O has only the one-launch path.  With 16-bit
+// I/O the two-launch paths win when the one-launch kernel (one workgroup per (sequence,
+// head, 16 value channels), each redoing the state-independent products of its chunks on
+// its own critical path) would leave at least half of the compute units idle, and for
+// packed batches of several sequences (whose longest sequence sets the one-launch
+// kernel's time, while the two-launch map covers all chunks at once).  Among the two, the
+// segmented one when gdn_prefill_seg_choose gives more than one segment (it has no
+// prologue).
+struct AutoPlan {
+    int32_t path, segments;
+    size_t workspace;
+};
+
+gdn_status auto_plan(int32_t N, int32_t T_tot, int32_t Hv, gdn_dtype io_dtype, uint32_t prologue, AutoPlan *p) {
+    if (!valid_dtype(io_dtype))
+        return fail(GDN_ERR_INVALID_ARGUMENT, "io_dtype %d is not GDN_F32, GDN_BF16 or GDN_F16", (int)io_dtype);
+    if (N < 1 || T_tot < 0 || Hv < 1)
+        return fail(GDN_ERR_INVALID_ARGUMENT, "N=%d, T_tot=%d, Hv=%d out of range", N, T_tot, Hv);
+    if (prologue & ~kPrologueAll)
+        return fail(GDN_ERR_INVALID_ARGUMENT, "prologue flags 0x%x include unknown bits", prologue);
+    *p = AutoPlan{GDN_PATH_ONE_LAUNCH, 1, 0};
+    if (io_dtype == GDN_F32) return GDN_OK;
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+        return fail(GDN_ERR_DEVICE, "cannot read the current device's compute-unit count");
+    if (!(2LL * N * Hv * (kD / 16) <= cus || N > 1)) return GDN_OK;
+    int32_t K = 1;
+    if (!prologue) {
+        const gdn_status st = gdn_prefill_seg_choose(N, T_tot, Hv, kChunk, &K);
+        if (st != GDN_OK) return st;
+    }
+    if (K > 1) {
+        *p = AutoPlan{GDN_PATH_SEG, K, 0};
+        return gdn_prefill_seg_workspace_size(N, T_tot, Hv, kChunk, K, &p->workspace);
+    }
+    *p = AutoPlan{GDN_PATH_SPLIT, 1, 0};
+    return gdn_prefill_split_workspace_size(N, T_tot, Hv, kChunk, &p->workspace);
+}
+
+}  // namespace
+
+extern "C" {
+
+gdn_status gdn_prefill_auto_plan(int32_t N, int32_t T_tot, int32_t Hv, gdn_dtype io_dtype, uint32_t prologue,
+                                 int32_t *path, int32_t *segments, size_t *workspace_bytes) {
+    if (!workspace_bytes) return fail(GDN_ERR_INVALID_ARGUMENT, "workspace_bytes must be non-null");
+    AutoPlan p{};
+    const gdn_status st = auto_plan(N, T_tot, Hv, io_dtype, prologue, &p);
+    if (st != GDN_OK) return st;
+    if (path) *path = p.path;
+    if (segments) *segments = p.segments;
+    *workspace_bytes = p.workspace;
+    return ok();
+}
+
+gdn_status gdn_prefill_auto(const void *q, const void *k, const void *v, const float *g,
+                            const float *beta, const float *initial_state, const int32_t *cu_seqlens,
+                            int32_t N, int32_t T_tot, int32_t Hk, int32_t Hv, int32_t Dk, int32_t Dv,
+                            gdn_dtype io_dtype, uint32_t prologue, void *workspace, size_t workspace_bytes,
+                            void *o, float *final_state, void *stream) {
+    AutoPlan p{};
+    const gdn_status st = auto_plan(N, T_tot, Hv, io_dtype, prologue, &p);
+    if (st != GDN_OK) return st;
+    switch (p.path) {
+        case GDN_PATH_SEG:
+            return seg_impl("gdn_prefill_auto", false, q, k, v, g, beta, initial_state, cu_seqlens, N, T_tot, Hk,
+                            Hv, Dk, Dv, kChunk, p.segments, io_dtype, workspace, workspace_bytes, o, final_state,
+                            stream);
+        case GDN_PATH_SPLIT:
+            return split_impl(q, k, v, g, beta, initial_state, cu_seqlens, N, T_tot, Hk, Hv, Dk, Dv, kChunk,
+                              io_dtype, prologue, workspace, workspace_bytes, o, final_state, stream);
+        default:
+            return prologue ? gdn_prefill_fused(q, k, v, g, beta, initial_state, cu_seqlens, N, T_tot, Hk, Hv, Dk,
+                                                Dv, kChunk, io_dtype, prologue, o, final_state, stream)
+                            : gdn_prefill(q, k, v, g, beta, initial_state, cu_seqlens, N, T_tot, Hk, Hv, Dk, Dv,
+                                          kChunk, io_dtype, o, final_state, stream);
+    }
 }
 
 }  // extern "C"

@@ -87,6 +87,12 @@ def load_library(path: str = LIB_PATH):
     lib.gdn_kda_prefill_seg.restype = ctypes.c_int
     lib.gdn_kda_decode_step.argtypes = lib.gdn_decode_step.argtypes
     lib.gdn_kda_decode_step.restype = ctypes.c_int
+    lib.gdn_prefill_auto_plan.argtypes = [i32, i32, i32, ctypes.c_int, ctypes.c_uint32, p32, p32,
+                                          ctypes.POINTER(ctypes.c_size_t)]
+    lib.gdn_prefill_auto_plan.restype = ctypes.c_int
+    lib.gdn_prefill_auto.argtypes = [vp, vp, vp, fp, fp, fp, ip, i32, i32, i32, i32, i32, i32,
+                                     ctypes.c_int, ctypes.c_uint32, vp, ctypes.c_size_t, vp, fp, vp]
+    lib.gdn_prefill_auto.restype = ctypes.c_int
     lib.gdn_status_string.argtypes = [ctypes.c_int]
     lib.gdn_status_string.restype = ctypes.c_char_p
     lib.gdn_last_error.argtypes = []
@@ -238,7 +244,8 @@ def _prefill_ws(fn: str, size_fn, per_channel: bool, q, k, v, g, beta, initial_s
                 chunk_size, output_final_state, out, final_state, workspace, lib, extra=(),
                 extra_after_io: bool = False):
     """The entry points that take a caller-owned workspace (gdn_kda_prefill, gdn_prefill_split,
-    gdn_prefill_split_fused, gdn_prefill_seg); ``extra`` holds further integer arguments,
+    gdn_prefill_split_fused, gdn_prefill_seg, gdn_prefill_auto: chunk_size None, it has no
+    such argument); ``extra`` holds further integer arguments,
     which size_fn takes too: after chunk_size (the segment count), or after io_dtype with
     extra_after_io (the prologue flags)."""
     lib = lib or load_library()
@@ -273,8 +280,9 @@ def _prefill_ws(fn: str, size_fn, per_channel: bool, q, k, v, g, beta, initial_s
     with torch.cuda.device(dev):
         stream = torch.cuda.current_stream(dev).cuda_stream
         pre, post = ((), extra) if extra_after_io else (extra, ())
+        chunk = () if chunk_size is None else (chunk_size,)   # gdn_prefill_auto has none
         st = getattr(lib, fn)(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
-                              _ptr(cu_seqlens), N, T, Hk, Hv, Dk, Dv, chunk_size, *pre, io, *post, _ptr(workspace),
+                              _ptr(cu_seqlens), N, T, Hk, Hv, Dk, Dv, *chunk, *pre, io, *post, _ptr(workspace),
                               workspace.numel(), _ptr(out), _ptr(final_state), ctypes.c_void_p(stream))
     _check(lib, st, fn)
     return out, final_state
@@ -437,6 +445,43 @@ def kda_decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.
                                      B, Hk, Hv, Dk, Dv, io, _ptr(out), ctypes.c_void_p(stream))
     _check(lib, st, "gdn_kda_decode_step")
     return out
+
+
+PATH_ONE_LAUNCH, PATH_SPLIT, PATH_SEG = 0, 1, 2
+PATH_NAMES = {PATH_ONE_LAUNCH: "one_launch", PATH_SPLIT: "split", PATH_SEG: "seg"}
+
+
+def prefill_auto_plan(N: int, T: int, Hv: int, io_dtype: int = GDN_BF16, prologue: int = 0, lib=None) -> dict:
+    """gdn_prefill_auto_plan: the path gdn_prefill_auto takes on the current device for these
+    sizes ("one_launch", "split" or "seg"), its segment count and workspace bytes."""
+    lib = lib or load_library()
+    path, seg, n = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_size_t()
+    _check(lib, lib.gdn_prefill_auto_plan(N, T, Hv, io_dtype, prologue, ctypes.byref(path), ctypes.byref(seg),
+                                          ctypes.byref(n)), "gdn_prefill_auto_plan")
+    return {"path": PATH_NAMES[path.value], "segments": seg.value, "workspace_bytes": int(n.value)}
+
+
+def prefill_auto(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                 beta: torch.Tensor, initial_state: Optional[torch.Tensor] = None,
+                 cu_seqlens: Optional[torch.Tensor] = None, output_final_state: bool = True,
+                 out: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None,
+                 workspace: Optional[torch.Tensor] = None, prologue: int = 0, lib=None
+                 ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """``prefill`` through the fastest path for these sizes (gdn_prefill_auto).  A workspace
+    of ``prefill_auto_plan(...)["workspace_bytes"]`` bytes is allocated here when not
+    given."""
+    lib = lib or load_library()
+    if q.device.type != "cuda":
+        raise ValueError("gdn_prefill_auto runs on the GPU only; q is on " + str(q.device))
+    if workspace is None:   # the library checks a given workspace's size itself
+        N = 1 if cu_seqlens is None else cu_seqlens.shape[0] - 1
+        with torch.cuda.device(q.device):
+            need = prefill_auto_plan(N, q.shape[0], v.shape[1], _io_code(q), prologue, lib=lib)["workspace_bytes"]
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    size_fn = lambda N, T, Hv, C, _p, lib=None: 0  # noqa: E731
+    return _prefill_ws("gdn_prefill_auto", size_fn, False, q, k, v, g, beta, initial_state, cu_seqlens,
+                       None, output_final_state, out, final_state, workspace, lib, extra=(int(prologue),),
+                       extra_after_io=True)
 
 
 def prefill_plan(N: int, Hv: int, io_dtype: int = GDN_BF16, lib=None) -> dict:

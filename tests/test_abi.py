@@ -34,7 +34,8 @@ def test_header_declares_the_boundary():
          "gdn_kda_workspace_size", "gdn_kda_prefill", "gdn_kda_decode_step", "gdn_prefill_fused",
          "gdn_decode_step_fused", "gdn_prefill_split", "gdn_prefill_split_workspace_size",
          "gdn_prefill_seg", "gdn_prefill_seg_workspace_size", "gdn_prefill_seg_choose",
-         "gdn_prefill_split_fused", "gdn_kda_prefill_seg", "gdn_prefill_split_noalloc"])
+         "gdn_prefill_split_fused", "gdn_kda_prefill_seg", "gdn_prefill_split_noalloc",
+         "gdn_prefill_auto_plan", "gdn_prefill_auto"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -391,3 +392,57 @@ def test_kda_seg_rejects(lib, over, status, msg):
                                  a["io"], p(a["ws"]), a["wsb"], p(a["o"]), p(a["fs"]), None)
     assert st == status
     assert msg in lib.gdn_last_error().decode()
+
+
+def _auto_plan(lib, N=1, T=4096, Hv=16, io=1, pro=0, want_bytes=True):
+    path, seg, n = ctypes.c_int32(-1), ctypes.c_int32(-1), ctypes.c_size_t(7)
+    st = lib.gdn_prefill_auto_plan(N, T, Hv, io, pro, ctypes.byref(path), ctypes.byref(seg),
+                                   ctypes.byref(n) if want_bytes else None)
+    return st, path.value, seg.value, n.value
+
+
+def test_auto_plan_fp32_is_the_one_launch_path(lib):
+    # fp32 I/O has one path, chosen without asking the device
+    assert _auto_plan(lib, io=0) == (0, gdn.PATH_ONE_LAUNCH, 1, 0)
+
+
+@pytest.mark.parametrize("over,status,msg", [
+    (dict(io=5), 1, "io_dtype"),
+    (dict(N=0), 1, "out of range"),
+    (dict(T=-1), 1, "out of range"),
+    (dict(pro=8), 1, "unknown bits"),
+    (dict(want_bytes=False), 1, "workspace_bytes must be non-null"),
+])
+def test_auto_plan_rejects(lib, over, status, msg):
+    assert _auto_plan(lib, **over)[0] == status
+    assert msg in lib.gdn_last_error().decode()
+
+
+def test_auto_plan_needs_a_device_for_16_bit_io(lib):
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert _auto_plan(lib)[0] == 3
+    assert "compute-unit count" in lib.gdn_last_error().decode()
+
+
+def test_auto_rejects_before_planning_nothing(lib):
+    p = lambda x: None if x is None else ctypes.c_void_p(x)  # noqa: E731
+    st = lib.gdn_prefill_auto(p(0x100000), p(0x200000), p(0x300000), p(0x400000), p(0x500000), None, None,
+                              1, 10, 2, 4, 128, 128, 0, 9, None, 0, p(0x600000), None, None)
+    assert st == 1 and "unknown bits" in lib.gdn_last_error().decode()
+
+
+def test_gdn_check_reads_cu_seqlens_before_any_launch(lib, monkeypatch):
+    # without a GPU the read-back itself fails: the check runs first, after the host
+    # checks and before any launch, and says so
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present (the GPU tests cover malformed cu_seqlens)")
+    p = lambda x: None if x is None else ctypes.c_void_p(x)  # noqa: E731
+    args = lambda: (p(0x100000), p(0x200000), p(0x300000), p(0x400000), p(0x500000), None, p(0x700000),  # noqa: E731
+                    2, 10, 2, 4, 128, 128, 64, 1, p(0x600000), None, None)
+    monkeypatch.setenv("GDN_CHECK", "1")
+    assert lib.gdn_prefill(*args()) == 3
+    assert "GDN_CHECK: reading cu_seqlens back failed" in lib.gdn_last_error().decode()
+    monkeypatch.setenv("GDN_CHECK", "0")
+    lib.gdn_prefill(*args())
+    assert "GDN_CHECK" not in lib.gdn_last_error().decode()

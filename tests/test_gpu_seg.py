@@ -103,6 +103,15 @@ def test_seg_few_heads_long_sequence():
     check_pair("seg vs split state", to_f64(fs), to_f64(f1), x.io, stored=False)
 
 
+def test_seg_benched_shard_H4_T65536():
+    # the shape the segmented path is measured on: one GPU's 4-head share of the H32
+    # T65536 prefill, at the segment count gdn_prefill_seg_choose picks for it
+    x = inputs.head_shard(inputs.make_workload(4), 8)
+    K = gdn.prefill_seg_choose(x.N, x.T_tot, x.Hv)
+    assert K > 1
+    _check_seg(x, K)
+
+
 @pytest.mark.parametrize("wid,K", [(1, 2), (3, 2), (3, 3)])
 def test_seg_workloads(wid, K):
     _check_seg(inputs.make_workload(wid), K)
