@@ -17,36 +17,35 @@
 // Value channels are independent in all three (S's rows never mix), so one workgroup
 // owns 16 of them for one (sequence, value head) and needs nothing from the others.
 //
-// The recurrence runs on ONE wave and never leaves its registers.  It holds S^T (128 key
-// x 16 value channels) as eight fp32 16x16 accumulators; read in pairs, an accumulator's
-// rows are the eight reduction slots of an MFMA operand (the slot order pi of the tile
-// layout), so fp16 copies of S^T are the B operands of v = U + WN S^T as they stand, and
-// v's token tiles are likewise the B operands of the update S^T <- gl S^T + Kl^T v.  A
-// chunk is 4 x C/16 + 8 x C/32 MFMAs (32 at C = 64) on one SIMD with no barrier between
-// them.  Their A operands (WN, Kl, U, gl: 34.5 KB at C = 64) come from LDS: a wave64
-// 16-byte global load holds the issuing wave ~16 cycles in the address unit, so the
-// recurrence issues none.  Two loader waves (operand halves A: WN, U, gl and B: Kl)
-// stream each chunk's tiles from L2 into a two-buffer LDS ring, issued two chunks ahead
-// into a second register set.  (Each of a head's 8 workgroups reads the same tiles; a
-// head's workgroups share one XCD and so one L2.)
+// The recurrence runs on two waves, one per half of the key channels, and never leaves
+// their registers.  Wave h holds rows 64 h .. 64 h + 63 of S^T (its key half x 16 value
+// channels) as four fp32 16x16 accumulators; read in pairs, an accumulator's rows are the
+// eight reduction slots of an MFMA operand (the slot order pi of the tile layout), so
+// fp16 copies of S^T are B operands as they stand.  Per chunk, wave h forms the partial
+// p_h = [U] + WN[:, half h] S^T[half h] (U on wave 0 only), both waves exchange their
+// partials as fp16 through LDS, and each forms v = p_0 + p_1 (the same fp16 values on
+// every wave) and updates its half, S^T[half h] <- gl S^T[half h] + Kl[half h]^T v, with
+// v's token tiles as the B operands.  A wave's operands per chunk (its halves of WN and
+// Kl, gl, U: 17 KB at C = 64) come straight from L2 into registers with buffer loads, one
+// chunk ahead: a wave receives LDS reads at ~22 B per clock, a third of the rate at
+// which it issues 16-byte global loads, so the operands do not pass through LDS.  (Each
+// of a head's 8 workgroups reads the same tiles; they share one XCD and so one L2.)
 //
 // Two output waves form O^T = S Qg^T + v^T P^T, half of the token tiles each, from the
-// fp16 state and v fragments the recurrence wave leaves in one of two LDS exchange slots
-// per chunk, their Qg and P fragments loaded a chunk ahead from L2.  O^T puts four
-// consecutive value channels of one token in a lane: one 8-byte store.
+// fp16 state halves and the two partials the recurrence waves leave in one of two LDS
+// exchange slots per chunk, their Qg and P fragments loaded a chunk ahead.  O^T puts
+// four consecutive value channels of one token in a lane: one 8-byte store.
 //
-// One barrier per chunk orders the roles.  Between barriers c - 1 and c (barrier -1 ends
-// the loaders' prologue, which puts chunk 0 in the ring): the recurrence wave reads ring
-// buffer c % 2 and fills exchange slot c % 2; the loaders put chunk c + 1 into buffer
-// (c + 1) % 2, which the recurrence wave last read before barrier c - 1; the output waves
-// read exchange slot (c - 1) % 2, filled before barrier c - 1 and refilled after barrier c.
+// One barrier per chunk orders everything.  Before barrier c the recurrence waves write
+// S^T(c) and their partials of chunk c into slot c % 2; after it each reads the other's
+// partial, and the output waves read the slot, before barrier c + 1, after which slot
+// c % 2 is written again (chunk c + 2).
 //
-// Measured and not kept (H16 T4096): three ring buffers with the next chunk's operands
-// read in the shadow of the update products; progress counters in LDS instead of
-// barriers; loaders and output waves split by chunk parity; the recurrence split over
-// two waves by key halves with a partial-v exchange.  Each was slower: the operand
-// stream, not the recurrence's issue, sets the chunk period (the tiles come from the
-// Infinity Cache or HBM, whose round trip the two-chunk prefetch barely covers).
+// Measured and not kept (H16 T4096): one recurrence wave fed from an LDS ring by loader
+// waves (47 us: the wave's LDS reads of 34.5 KB per chunk set the period); the same with
+// three ring buffers, with LDS progress counters instead of barriers, or with loaders
+// and output waves split by chunk parity; a two-wave split with loader waves and two
+// barriers per chunk (65 us: every role waited for the slowest at each barrier).
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
@@ -60,43 +59,45 @@ constexpr int DK = 128;
 constexpr int DV = 128;
 constexpr int DVS = 16;         // value channels per workgroup
 constexpr int NSL = DV / DVS;   // workgroups per (sequence, head)
-// wave 0: the recurrence; 1, 2: the outputs; 3, 4: the loaders (operand halves A, B)
-constexpr int THREADS = 320;
+// waves 0, 1: the recurrence (key halves); 2 .. 5: the outputs (token tiles t = 4 k + o);
+// 6, 7: the loaders (WN, Kl)
+constexpr int THREADS = 512;
 
 template <int C>
 struct Cfg {
     static constexpr int NT = C / 16;             // 16-token tiles
     static constexpr int KB = C / 32;             // 32-token reduction blocks
-    static constexpr int OT = NT / 2;             // token tiles per output wave
-    // loaders and output waves keep a second register set (loads issued two chunks
-    // ahead) up to C = 64; at C = 128 one chunk's operands are already 128 registers
-    static constexpr bool DB = C <= 64;
-    // output wave o's k-th tile (the two waves take tiles 0, 3, 4, 7 and 1, 2, 5, 6, which
-    // gives both the same number of P fragments) and its P fragment count
-    __device__ static constexpr int tile(int k, int o) { return 4 * (k >> 1) + ((k & 1) ? 3 - o : o); }
-    static constexpr int npf(int k) { return 2 * (k >> 1) + (k & 1) + 1; }
-    static constexpr int NPO = OT == 1 ? 1 : OT == 2 ? 3 : 10;   // P fragments per output wave
+    static constexpr int NW = NT * 4;             // WN fragments per chunk
+    static constexpr int NK = 8 * KB;             // Kl fragments per chunk
+    // operand ring depth: chunk c + NB - 1 is loaded while chunk c runs
+    static constexpr int NB = C == 32 ? 4 : C == 64 ? 3 : 2;
+    static constexpr int OT = NT >= 4 ? NT / 4 : 1;   // token tiles per output wave
+    // P fragments of token tile t (its 32-token blocks up to its own), and of output wave o
+    static constexpr int npf(int t) { return t / 2 + 1; }
+    static constexpr int npo(int o) {
+        int n = 0;
+        for (int k = 0; k < OT; ++k)
+            if (4 * k + o < NT) n += npf(4 * k + o);
+        return n;
+    }
 };
-static_assert(Cfg<64>::npf(0) + Cfg<64>::npf(1) == Cfg<64>::NPO, "");
-static_assert(Cfg<128>::npf(0) + Cfg<128>::npf(1) + Cfg<128>::npf(2) + Cfg<128>::npf(3) == Cfg<128>::NPO, "");
 
 __device__ __forceinline__ f32x4 mfma(const f16x8 &a, const f16x8 &b, const f32x4 &c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
-// LDS: the exchange slots and the operand ring (81 KB at C = 64, 153 KB at C = 128).
+// LDS: the operand ring and two exchange slots (112 KB at C = 64, 152 KB at C = 128).
 template <int C>
 struct __align__(16) Smem {
-    using F = Cfg<C>;
-    f16x8 xs[2][(4 + F::KB) * 64];   // S^T (4) and v (KB) fragments, lane-major
     struct Ops {
-        f16x8 w[F::NT * 4 * 64];  // WN fragments (t, kb), lane-major
-        f16x8 kl[8 * F::KB * 64]; // Kl fragments (i, kb)
-        u32x2 u[F::NT * 64];      // the workgroup's U slice, per token tile
-        f32x4 gl[32];             // exp(Gamma_last) per key channel
-    } ob[2];
+        f16x8 w[Cfg<C>::NW * 64];   // WN fragments (t, kb), lane-major, as in the tile
+        f16x8 kl[Cfg<C>::NK * 64];  // Kl fragments (i, kb)
+    } ob[Cfg<C>::NB];
+    f16x8 xs[2][4 * 64];                 // S^T fragments (key blocks 0..3)
+    u32x2 pv[2][2][Cfg<C>::NT * 64];     // the recurrence waves' partials, fp16, per token tile
 };
-static_assert(sizeof(Smem<128>) <= 160 * 1024 && sizeof(Smem<64>) <= 160 * 1024, "the LDS holds the ring");
+static_assert(sizeof(Smem<32>) <= 160 * 1024 && sizeof(Smem<64>) <= 160 * 1024 && sizeof(Smem<128>) <= 160 * 1024,
+              "the LDS holds the ring");
 
 struct Work {
     const char *ws;       // workspace tile of this (sequence, head) at its first chunk
@@ -118,223 +119,244 @@ __device__ __forceinline__ f16x8 ld_frag(__amdgpu_buffer_rsrc_t r, int voff, int
     return __builtin_bit_cast(f16x8, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
 
-// ---- loaders ------------------------------------------------------------------------
+// ---- the loaders ---------------------------------------------------------------------
 
-// The loaders' registers for one chunk: A takes gl, U and WN, B takes Kl.
-template <int C, bool A>
-struct LoadRegs;
-template <int C>
-struct LoadRegs<C, true> {
-    f16x8 w[Cfg<C>::NT * 4];
-    u32x2 u[Cfg<C>::NT];
-    f32x4 gl;                 // lanes 0..31: 4 key channels each
-};
-template <int C>
-struct LoadRegs<C, false> {
-    f16x8 kl[8 * Cfg<C>::KB];
-};
+typedef __attribute__((address_space(3))) void lds_void;
 
-template <int C, bool A>
-__device__ __forceinline__ void load_ops(LoadRegs<C, A> &rg, const Work &wk, int c, int lane) {
+// vmcnt(N) alone (gfx9 encoding: expcnt and lgkmcnt at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt holds 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Chunk c's WN (KL false) or Kl fragments into ring buffer c % NB, one 1 KB fragment per
+// instruction, global to LDS directly (lane l's 16 bytes land at 16 l: the fragment
+// layout of the tile is kept).
+template <int C, bool KL>
+__device__ __forceinline__ void dma_chunk(Smem<C> &sm, const Work &wk, int c, int lane) {
     using F = Cfg<C>;
     using TL = Tile<C>;
     const __amdgpu_buffer_rsrc_t r = tile_rsrc<C>(wk, c);
-    if constexpr (A) {
-        rg.gl = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, 16 * (lane & 31), TL::GL, 0));
+    typename Smem<C>::Ops &ob = sm.ob[c % F::NB];
+    f16x8 *dst = KL ? ob.kl : ob.w;
+    constexpr int NF = KL ? F::NK : F::NW;
+    constexpr int SRC = KL ? TL::KL : TL::WN;
 #pragma unroll
-        for (int t = 0; t < F::NT; ++t)
-            rg.u[t] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, 8 * lane, TL::u(wk.slice, t), 0));
-#pragma unroll
-        for (int t = 0; t < F::NT; ++t)
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb) rg.w[t * 4 + kb] = ld_frag(r, 16 * lane, TL::wn(t, kb));
-    } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-#pragma unroll
-            for (int kb = 0; kb < F::KB; ++kb) rg.kl[i * F::KB + kb] = ld_frag(r, 16 * lane, TL::kl(i, kb));
-    }
+    for (int f = 0; f < NF; ++f)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(dst + 64 * f), 16, 16 * lane, SRC + 1024 * f, 0, 0);
 }
 
-template <int C, bool A>
-__device__ __forceinline__ void store_ops(const LoadRegs<C, A> &rg, typename Smem<C>::Ops &ob, int lane) {
-    using F = Cfg<C>;
-    if constexpr (A) {
-        if (lane < 32) ob.gl[lane] = rg.gl;
-#pragma unroll
-        for (int t = 0; t < F::NT; ++t) ob.u[t * 64 + lane] = rg.u[t];
-#pragma unroll
-        for (int j = 0; j < F::NT * 4; ++j) ob.w[j * 64 + lane] = rg.w[j];
-    } else {
-#pragma unroll
-        for (int j = 0; j < 8 * F::KB; ++j) ob.kl[j * 64 + lane] = rg.kl[j];
-    }
-}
-
-// A loader wave's run: before barrier c it puts chunk c + 1 into buffer (c + 1) % 2 from
-// registers loaded two chunks earlier, and issues the loads of chunk c + 3 into them (one
-// register set at C = 128: chunk c + 2, loaded right after).
-template <int C, bool A>
+// A loader wave's run.  Chunk c's operands are read by the recurrence waves between
+// barriers c - 1 and c, so chunk c + NB goes into buffer c % NB after barrier c, and
+// chunk c + 1 must have landed before barrier c: the loads have NB - 1 chunks to land.
+// Plain s_barrier: the waits on this wave's own loads are explicit (vmcnt counts them in
+// issue order); it writes LDS only through the loads.
+template <int C, bool KL>
 __device__ __forceinline__ void loader_run(Smem<C> &sm, const Work &wk, int lane) {
-    const int n = wk.nchunks;
-    if constexpr (Cfg<C>::DB) {
-        LoadRegs<C, A> r0, r1;
-        load_ops(r0, wk, 0, lane);
-        load_ops(r1, wk, 1, lane);
-        store_ops(r0, sm.ob[0], lane);
-        load_ops(r0, wk, 2, lane);
-        __syncthreads();
-        for (int c = 0; c < n; c += 2) {
-            store_ops(r1, sm.ob[1], lane);
-            load_ops(r1, wk, c + 3, lane);
-            __syncthreads();
-            if (c + 1 >= n) break;
-            store_ops(r0, sm.ob[0], lane);
-            load_ops(r0, wk, c + 4, lane);
-            __syncthreads();
-        }
-    } else {
-        LoadRegs<C, A> r0;
-        load_ops(r0, wk, 0, lane);
-        store_ops(r0, sm.ob[0], lane);
-        load_ops(r0, wk, 1, lane);
-        __syncthreads();
-        for (int c = 0; c < n; ++c) {
-            store_ops(r0, sm.ob[(c + 1) & 1], lane);
-            load_ops(r0, wk, c + 2, lane);
-            __syncthreads();
-        }
+    using F = Cfg<C>;
+    constexpr int NF = KL ? F::NK : F::NW;
+#pragma unroll
+    for (int j = 0; j < F::NB; ++j) dma_chunk<C, KL>(sm, wk, j, lane);
+    wait_vmcnt<(F::NB - 1) * NF>();   // chunk 0
+    __builtin_amdgcn_s_barrier();
+    for (int c = 0; c < wk.nchunks; ++c) {
+        wait_vmcnt<(F::NB - 2) * NF>();   // chunk c + 1
+        __builtin_amdgcn_s_barrier();
+        dma_chunk<C, KL>(sm, wk, c + F::NB, lane);
     }
+    wait_vmcnt<0>();   // nothing in flight into the LDS when the workgroup ends
 }
 
 // ---- the recurrence -------------------------------------------------------------------
 
-// One chunk c of the recurrence: v = ukeep U + WN S^T, then S^T <- gl S^T + Kl^T v, with
-// the operands from ring buffer c % 2.  The fp16 S^T and v fragments go to exchange slot
-// c % 2.  ukeep is 1, or 0 for the identity rows of a segment (no U term).
+// Recurrence wave h's global operands for one chunk: half of the workgroup's slice of U
+// (token tiles h NT / 2 .. (h + 1) NT / 2 - 1, which its partial adds) and its keys'
+// decays gl (one value for the scalar gate).  WN and Kl come from the ring.
 template <int C, bool PERCH>
-__device__ __forceinline__ void chain_step(f32x4 (&st)[8], Smem<C> &sm, int c, int lane, bool ukeep) {
+struct RecRegs {
+    u32x2 u[Cfg<C>::NT / 2];
+    f32x4 gl[PERCH ? 4 : 1];
+};
+
+template <int C, bool PERCH>
+__device__ __forceinline__ void load_rec(RecRegs<C, PERCH> &rg, const Work &wk, int c, int h, int lane) {
     using F = Cfg<C>;
-    const typename Smem<C>::Ops &ob = sm.ob[c & 1];
-    const int g4 = lane >> 4;
-    // the v phase's operands first, then the update's (LDS returns them in order)
-    f16x8 w[F::NT][4];
-    u32x2 u[F::NT];
+    using TL = Tile<C>;
+    const __amdgpu_buffer_rsrc_t r = tile_rsrc<C>(wk, c);
 #pragma unroll
-    for (int t = 0; t < F::NT; ++t) u[t] = ob.u[t * 64 + lane];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int t = 0; t < F::NT; ++t) w[t][kb] = ob.w[(t * 4 + kb) * 64 + lane];
-    f32x4 gl[PERCH ? 8 : 1];
+    for (int t = 0; t < F::NT / 2; ++t)
+        rg.u[t] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, 8 * lane,
+                                                                                 TL::u(wk.slice, h * F::NT / 2 + t), 0));
     if constexpr (PERCH) {
+        // keys 64 h + 16 i + 4 G + q: 16 bytes at GL + 4 (16 (4 h + i) + 4 G)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) gl[i] = ob.gl[4 * i + g4];
+        for (int i = 0; i < 4; ++i)
+            rg.gl[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, 16 * (lane >> 4),
+                                                                                       TL::GL + 64 * (4 * h + i), 0));
     } else {
-        gl[0] = ob.gl[0];
+        rg.gl[0][0] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, 0, TL::GL, 0));
     }
-    f16x8 kl[8][F::KB];
+}
+
+// Chunk c on recurrence wave h, around barrier c: its halves of WN and Kl from ring buffer
+// c % NB, the partial, the exchange, the update.  with_u is 0 for the identity rows of a
+// segment (no U term).
+template <int C, bool PERCH>
+__device__ __forceinline__ void rec_step(f32x4 (&st)[4], const RecRegs<C, PERCH> &rg, Smem<C> &sm, int c, int h,
+                                         int lane, bool with_u) {
+    using F = Cfg<C>;
+    const typename Smem<C>::Ops &ob = sm.ob[c % F::NB];
+    f16x8 w[F::NT][2], kl[4][F::KB];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int t = 0; t < F::NT; ++t) w[t][j] = ob.w[(4 * t + 2 * h + j) * 64 + lane];
 #pragma unroll
     for (int kb = 0; kb < F::KB; ++kb)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) kl[i][kb] = ob.kl[(i * F::KB + kb) * 64 + lane];
-
-    f16x8 *xs = sm.xs[c & 1];
-    f16x8 sb[4];
+        for (int i = 0; i < 4; ++i) kl[i][kb] = ob.kl[((4 * h + i) * F::KB + kb) * 64 + lane];
+    f16x8 sb[2];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            sb[kb][e] = (hf)st[2 * kb][e];
-            sb[kb][4 + e] = (hf)st[2 * kb + 1][e];
+            sb[j][e] = (hf)st[2 * j][e];
+            sb[j][4 + e] = (hf)st[2 * j + 1][e];
         }
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) xs[kb * 64 + lane] = sb[kb];
-    f32x4 v[F::NT];
+    // U on this wave's half of the token tiles
+    f32x4 p[F::NT];
 #pragma unroll
     for (int t = 0; t < F::NT; ++t) {
-        const f16x4 uu = __builtin_bit_cast(f16x4, u[t]);
+        const f16x4 uu = __builtin_bit_cast(f16x4, rg.u[t % (F::NT / 2)]);
+        const bool add = with_u && t / (F::NT / 2) == h;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) v[t][q] = ukeep ? (float)uu[q] : 0.f;
+        for (int q = 0; q < 4; ++q) p[t][q] = add ? (float)uu[q] : 0.f;
     }
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int t = 0; t < F::NT; ++t) v[t] = mfma(w[t][kb], sb[kb], v[t]);
-    // the decay of the state (off the v products' path)
+        for (int t = 0; t < F::NT; ++t) p[t] = mfma(w[t][j], sb[j], p[t]);
+    f16x8 *xs = sm.xs[c & 1];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) xs[(2 * h + j) * 64 + lane] = sb[j];
+    // the decay of the state (off the partial's path)
     if constexpr (PERCH) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) st[i] *= gl[i];
+        for (int i = 0; i < 4; ++i) st[i] *= rg.gl[i];
     } else {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) st[i] *= gl[0][0];
+        for (int i = 0; i < 4; ++i) st[i] *= rg.gl[0][0];
     }
+    f16x4 ph[F::NT];
+#pragma unroll
+    for (int t = 0; t < F::NT; ++t)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) ph[t][q] = (hf)p[t][q];
+    u32x2 *mine = sm.pv[c & 1][h];
+#pragma unroll
+    for (int t = 0; t < F::NT; ++t) mine[t * 64 + lane] = __builtin_bit_cast(u32x2, ph[t]);
+    __syncthreads();
+    const u32x2 *other = sm.pv[c & 1][h ^ 1];
+    f16x4 po[F::NT];
+#pragma unroll
+    for (int t = 0; t < F::NT; ++t) po[t] = __builtin_bit_cast(f16x4, other[t * 64 + lane]);
+    // v = p_0 + p_1 from the fp16 partials (addition commutes exactly: every wave that
+    // forms v gets the same values)
     f16x8 vb[F::KB];
 #pragma unroll
     for (int kb = 0; kb < F::KB; ++kb)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            vb[kb][e] = (hf)v[2 * kb][e];
-            vb[kb][4 + e] = (hf)v[2 * kb + 1][e];
+            vb[kb][e] = (hf)((float)ph[2 * kb][e] + (float)po[2 * kb][e]);
+            vb[kb][4 + e] = (hf)((float)ph[2 * kb + 1][e] + (float)po[2 * kb + 1][e]);
         }
-#pragma unroll
-    for (int kb = 0; kb < F::KB; ++kb) xs[(4 + kb) * 64 + lane] = vb[kb];
 #pragma unroll
     for (int kb = 0; kb < F::KB; ++kb)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) st[i] = mfma(kl[i][kb], vb[kb], st[i]);
+        for (int i = 0; i < 4; ++i) st[i] = mfma(kl[i][kb], vb[kb], st[i]);
+}
+
+// Recurrence wave h's run: barrier -1 (chunk 0 in the ring), then a barrier per chunk;
+// U and gl of chunk c + 1 are loaded while chunk c runs.
+template <int C, bool PERCH>
+__device__ __forceinline__ void rec_run(f32x4 (&st)[4], Smem<C> &sm, const Work &wk, int h, int lane, bool with_u) {
+    const int n = wk.nchunks;
+    RecRegs<C, PERCH> r0, r1;
+    load_rec(r0, wk, 0, h, lane);
+    __syncthreads();
+    for (int c = 0; c < n; c += 2) {
+        load_rec(r1, wk, c + 1, h, lane);
+        rec_step(st, r0, sm, c, h, lane, with_u);
+        if (c + 1 >= n) break;
+        load_rec(r0, wk, c + 2, h, lane);
+        rec_step(st, r1, sm, c + 1, h, lane, with_u);
+    }
 }
 
 // ---- the outputs ----------------------------------------------------------------------
 
-template <int C>
+// Output wave O's operands for one chunk: Qg and P fragments of its token tiles 4 k + O.
+template <int C, int O>
 struct OutOps {
     using F = Cfg<C>;
     f16x8 qg[F::OT][4];
-    f16x8 p[F::NPO];
+    f16x8 p[F::npo(O) > 0 ? F::npo(O) : 1];
 };
 
-template <int C>
-__device__ __forceinline__ void load_out(OutOps<C> &op, const Work &wk, int c, int o, int lane) {
+template <int C, int O>
+__device__ __forceinline__ void load_out(OutOps<C, O> &op, const Work &wk, int c, int lane) {
     using F = Cfg<C>;
     using TL = Tile<C>;
     const __amdgpu_buffer_rsrc_t r = tile_rsrc<C>(wk, c);
     int pi = 0;
 #pragma unroll
     for (int k = 0; k < F::OT; ++k) {
-        const int t = F::tile(k, o);
+        const int t = 4 * k + O;
+        if (t >= F::NT) continue;
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) op.qg[k][kb] = ld_frag(r, 16 * lane, TL::qg(t, kb));
 #pragma unroll
-        for (int j = 0; j < F::npf(k); ++j) op.p[pi++] = ld_frag(r, 16 * lane, TL::p(t, j));
+        for (int j = 0; j < F::npf(t); ++j) op.p[pi++] = ld_frag(r, 16 * lane, TL::p(t, j));
     }
 }
 
-// Chunk c's outputs on output wave o: O^T = S Qg^T + v^T P^T for its token tiles, from the
-// exchange slot.  In the segment mode `kind` picks the destination, all
-// [token][head][channel]: 0 IO to o (segment 0), 1 fp16 to a.o0 (value rows of later
-// segments), 2 fp16 to a.e (identity rows); one 8-byte store for each, with no branch
-// between them.
-template <typename IO, int C, bool SEG>
-__device__ __forceinline__ void out_step(const OutOps<C> &op, const Smem<C> &sm, int c, const KdaArgs &a, int o,
+// Chunk c's outputs on output wave O: O^T = S Qg^T + v^T P^T for its token tiles, from the
+// exchange slot (S^T and the two partials of v).  In the segment mode `kind` picks the
+// destination, all [token][head][channel]: 0 IO to o (segment 0), 1 fp16 to a.o0 (value
+// rows of later segments), 2 fp16 to a.e (identity rows); one 8-byte store for each,
+// with no branch between them.
+template <typename IO, int C, bool SEG, int O>
+__device__ __forceinline__ void out_step(const OutOps<C, O> &op, const Smem<C> &sm, int c, const KdaArgs &a,
                                          int lane, int h, int dv0, int tok0, int nval, int kind) {
     using F = Cfg<C>;
     const int l16 = lane & 15, g4 = lane >> 4;
+    constexpr int TMAX = 4 * (F::OT - 1) + O;                   // its last token tile
+    constexpr int VB = (TMAX < F::NT ? TMAX : F::NT - 1) / 2 + 1;  // v blocks it needs
     const f16x8 *xs = sm.xs[c & 1];
-    f16x8 sb[4], vb[F::KB];
+    f16x8 sb[4], vb[VB];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) sb[kb] = xs[kb * 64 + lane];
+    // v = p_0 + p_1, as the recurrence waves form it
 #pragma unroll
-    for (int kb = 0; kb < F::KB; ++kb) vb[kb] = xs[(4 + kb) * 64 + lane];
+    for (int kb = 0; kb < VB; ++kb)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const f16x4 a0 = __builtin_bit_cast(f16x4, sm.pv[c & 1][0][(2 * kb + j) * 64 + lane]);
+            const f16x4 a1 = __builtin_bit_cast(f16x4, sm.pv[c & 1][1][(2 * kb + j) * 64 + lane]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) vb[kb][4 * j + e] = (hf)((float)a0[e] + (float)a1[e]);
+        }
     int pi = 0;
 #pragma unroll
     for (int k = 0; k < F::OT; ++k) {
-        const int t = F::tile(k, o);
+        const int t = 4 * k + O;
+        if (t >= F::NT) continue;
         f32x4 acc = zero4();
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) acc = mfma(sb[kb], op.qg[k][kb], acc);
 #pragma unroll
-        for (int j = 0; j < F::npf(k); ++j) acc = mfma(vb[j], op.p[pi++], acc);
+        for (int j = 0; j < F::npf(t); ++j) acc = mfma(vb[j], op.p[pi++], acc);
         const int tok = 16 * t + l16;
         const size_t at = ((size_t)(tok0 + tok) * a.Hv + h) * DV + dv0 + 4 * g4;
         if constexpr (SEG) {
@@ -357,38 +379,34 @@ __device__ __forceinline__ void out_step(const OutOps<C> &op, const Smem<C> &sm,
     }
 }
 
-// Output wave o's run: after barrier c it forms chunk c's outputs; before barrier c it
-// issues the loads of chunk c + 1 into its other register set (one set at C = 128).
-template <typename IO, int C, bool SEG>
-__device__ __forceinline__ void output_run(const Smem<C> &sm, const KdaArgs &a, const Work &wk, int o, int lane,
-                                           int kind) {
+// Output wave O's run: barrier -1, then after barrier c it forms chunk c's outputs; the
+// loads of chunk c + 1 are issued before barrier c.  A wave with no token tile (O >= NT,
+// at C = 32) takes part in the barriers only.
+template <typename IO, int C, bool SEG, int O>
+__device__ __forceinline__ void output_run(const Smem<C> &sm, const KdaArgs &a, const Work &wk, int lane, int kind) {
     using F = Cfg<C>;
     const int n = wk.nchunks;
-    auto step = [&](const OutOps<C> &op, int c) {
+    if constexpr (O >= F::NT) {
+        for (int c = 0; c <= n; ++c) __syncthreads();
+        return;
+    }
+    auto step = [&](const OutOps<C, O> &op, int c) {
         const int tok0 = wk.bos + c * C;
-        out_step<IO, C, SEG>(op, sm, c, a, o, lane, wk.h, wk.dv0, tok0, min(C, wk.eos - tok0), kind);
+        out_step<IO, C, SEG, O>(op, sm, c, a, lane, wk.h, wk.dv0, tok0, min(C, wk.eos - tok0), kind);
     };
-    if constexpr (F::DB) {
-        OutOps<C> op0, op1;
-        load_out(op0, wk, 0, o, lane);
+    OutOps<C, O> op0, op1;
+    load_out(op0, wk, 0, lane);
+    __syncthreads();
+    for (int c = 0; c < n; c += 2) {
+        load_out(op1, wk, c + 1, lane);
+        __builtin_amdgcn_sched_barrier(0);
         __syncthreads();
-        for (int c = 0; c < n; c += 2) {
-            load_out(op1, wk, c + 1, o, lane);
-            __syncthreads();
-            step(op0, c);
-            if (c + 1 >= n) break;
-            load_out(op0, wk, c + 2, o, lane);
-            __syncthreads();
-            step(op1, c + 1);
-        }
-    } else {
-        OutOps<C> op0;
+        step(op0, c);
+        if (c + 1 >= n) break;
+        load_out(op0, wk, c + 2, lane);
+        __builtin_amdgcn_sched_barrier(0);
         __syncthreads();
-        for (int c = 0; c < n; ++c) {
-            load_out(op0, wk, c, o, lane);
-            __syncthreads();
-            step(op0, c);
-        }
+        step(op1, c + 1);
     }
 }
 
@@ -470,12 +488,13 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const size_t sbase = ((size_t)n * a.Hv + h) * (size_t)DV * DK;
     const int l16 = lane & 15, g4 = lane >> 4;
 
-    if (wave == 0) {
-        // S^T rows (key channels) 16 i + 4 G + q, column = value channel dv0 + m
-        f32x4 st[8];
+    if (wave < 2) {
+        const int kh = wave;   // key half
+        // S^T rows (key channels) 64 kh + 16 i + 4 G + q, column = value channel dv0 + m
+        f32x4 st[4];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int dk = 16 * i + 4 * g4;
+        for (int i = 0; i < 4; ++i) {
+            const int dk = 64 * kh + 16 * i + 4 * g4;
             f32x4 x = zero4();
             if (seg == 0 && a.s0) x = *reinterpret_cast<const f32x4 *>(a.s0 + sbase + (size_t)(wk.dv0 + l16) * DK + dk);
             if (ident) {
@@ -484,18 +503,12 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
             }
             st[i] = x;
         }
-        if (wk.nchunks > 0) {
-            __syncthreads();   // the loaders' prologue: chunk 0 is in the ring
-            for (int c = 0; c < wk.nchunks; ++c) {
-                chain_step<C, PERCH>(st, sm, c, lane, !ident);
-                __syncthreads();
-            }
-        }
+        if (wk.nchunks > 0) rec_run<C, PERCH>(st, sm, wk, kh, lane, !ident);
         if constexpr (SEG) {
             float *sb = a.sseg + ((((size_t)n * a.Hv + h) * a.nseg + seg) * 2 + (ident ? 1 : 0)) * DV * DK;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int dk = 16 * i + 4 * g4, r = wk.dv0 + l16;
+            for (int i = 0; i < 4; ++i) {
+                const int dk = 64 * kh + 16 * i + 4 * g4, r = wk.dv0 + l16;
                 if (ident) {   // X^T [key][row]
 #pragma unroll
                     for (int q = 0; q < 4; ++q) sb[(size_t)(dk + q) * DV + r] = st[i][q];
@@ -505,14 +518,19 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
             }
         } else if (a.sN) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
-                *reinterpret_cast<f32x4 *>(a.sN + sbase + (size_t)(wk.dv0 + l16) * DK + 16 * i + 4 * g4) = st[i];
+            for (int i = 0; i < 4; ++i)
+                *reinterpret_cast<f32x4 *>(a.sN + sbase + (size_t)(wk.dv0 + l16) * DK + 64 * kh + 16 * i + 4 * g4) = st[i];
         }
-    } else if (wk.nchunks > 0 && wave < 3) {
-        output_run<IO, C, SEG>(sm, a, wk, wave - 1, lane, kind);
+    } else if (wk.nchunks > 0 && wave < 6) {
+        switch (wave) {
+            case 2: output_run<IO, C, SEG, 0>(sm, a, wk, lane, kind); break;
+            case 3: output_run<IO, C, SEG, 1>(sm, a, wk, lane, kind); break;
+            case 4: output_run<IO, C, SEG, 2>(sm, a, wk, lane, kind); break;
+            default: output_run<IO, C, SEG, 3>(sm, a, wk, lane, kind); break;
+        }
     } else if (wk.nchunks > 0) {
-        if (wave == 3) loader_run<C, true>(sm, wk, lane);
-        else loader_run<C, false>(sm, wk, lane);
+        if (wave == 6) loader_run<C, false>(sm, wk, lane);
+        else loader_run<C, true>(sm, wk, lane);
     }
 }
 
