@@ -199,23 +199,43 @@ __device__ __forceinline__ void load_rec(RecRegs<C, PERCH> &rg, const Work &wk, 
     }
 }
 
-// Chunk c on recurrence wave h, around barrier c: its halves of WN and Kl from ring buffer
-// c % NB, the partial, the exchange, the update.  with_u is 0 for the identity rows of a
-// segment (no U term).
-template <int C, bool PERCH>
-__device__ __forceinline__ void rec_step(f32x4 (&st)[4], const RecRegs<C, PERCH> &rg, Smem<C> &sm, int c, int h,
-                                         int lane, bool with_u) {
+// Recurrence wave h's halves of WN and Kl for one chunk, from its ring buffer.
+template <int C>
+struct RingRegs {
+    f16x8 w[Cfg<C>::NT][2];
+    f16x8 kl[4][Cfg<C>::KB];
+};
+
+template <int C>
+__device__ __forceinline__ void read_ring_w(RingRegs<C> &rr, const Smem<C> &sm, int c, int h, int lane) {
     using F = Cfg<C>;
     const typename Smem<C>::Ops &ob = sm.ob[c % F::NB];
-    f16x8 w[F::NT][2], kl[4][F::KB];
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int t = 0; t < F::NT; ++t) w[t][j] = ob.w[(4 * t + 2 * h + j) * 64 + lane];
+        for (int t = 0; t < F::NT; ++t) rr.w[t][j] = ob.w[(4 * t + 2 * h + j) * 64 + lane];
+}
+
+template <int C>
+__device__ __forceinline__ void read_ring_kl(RingRegs<C> &rr, const Smem<C> &sm, int c, int h, int lane) {
+    using F = Cfg<C>;
+    const typename Smem<C>::Ops &ob = sm.ob[c % F::NB];
 #pragma unroll
     for (int kb = 0; kb < F::KB; ++kb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) kl[i][kb] = ob.kl[((4 * h + i) * F::KB + kb) * 64 + lane];
+        for (int i = 0; i < 4; ++i) rr.kl[i][kb] = ob.kl[((4 * h + i) * F::KB + kb) * 64 + lane];
+}
+
+// Chunk c on recurrence wave h, around barrier c: the partial, the exchange, the update,
+// with chunk c's operands in cur.  Chunk c + 1's buffer is complete before barrier c, so
+// its reads into nxt are issued right after it and land during this chunk's exchange and
+// update (WN first, needed first).  with_u is 0 for the identity rows of a segment (no U
+// term).
+template <int C, bool PERCH>
+__device__ __forceinline__ void rec_step(f32x4 (&st)[4], const RecRegs<C, PERCH> &rg, const RingRegs<C> &cur,
+                                         RingRegs<C> &nxt, Smem<C> &sm, int c, bool more, int h, int lane,
+                                         bool with_u) {
+    using F = Cfg<C>;
     f16x8 sb[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j)
@@ -236,7 +256,7 @@ __device__ __forceinline__ void rec_step(f32x4 (&st)[4], const RecRegs<C, PERCH>
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int t = 0; t < F::NT; ++t) p[t] = mfma(w[t][j], sb[j], p[t]);
+        for (int t = 0; t < F::NT; ++t) p[t] = mfma(cur.w[t][j], sb[j], p[t]);
     f16x8 *xs = sm.xs[c & 1];
 #pragma unroll
     for (int j = 0; j < 2; ++j) xs[(2 * h + j) * 64 + lane] = sb[j];
@@ -261,6 +281,7 @@ __device__ __forceinline__ void rec_step(f32x4 (&st)[4], const RecRegs<C, PERCH>
     f16x4 po[F::NT];
 #pragma unroll
     for (int t = 0; t < F::NT; ++t) po[t] = __builtin_bit_cast(f16x4, other[t * 64 + lane]);
+    if (more) read_ring_w(nxt, sm, c + 1, h, lane);
     // v = p_0 + p_1 from the fp16 partials (addition commutes exactly: every wave that
     // forms v gets the same values)
     f16x8 vb[F::KB];
@@ -274,23 +295,44 @@ __device__ __forceinline__ void rec_step(f32x4 (&st)[4], const RecRegs<C, PERCH>
 #pragma unroll
     for (int kb = 0; kb < F::KB; ++kb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) st[i] = mfma(kl[i][kb], vb[kb], st[i]);
+        for (int i = 0; i < 4; ++i) st[i] = mfma(cur.kl[i][kb], vb[kb], st[i]);
+    if (more) read_ring_kl(nxt, sm, c + 1, h, lane);
 }
 
 // Recurrence wave h's run: barrier -1 (chunk 0 in the ring), then a barrier per chunk;
-// U and gl of chunk c + 1 are loaded while chunk c runs.
+// U and gl of chunk c + 1 are loaded, and its ring operands read, while chunk c runs.
 template <int C, bool PERCH>
 __device__ __forceinline__ void rec_run(f32x4 (&st)[4], Smem<C> &sm, const Work &wk, int h, int lane, bool with_u) {
     const int n = wk.nchunks;
     RecRegs<C, PERCH> r0, r1;
+    if constexpr (C >= 128) {   // a chunk's ring operands are 128 registers: one set, read at its start
+        RingRegs<C> q;
+        load_rec(r0, wk, 0, h, lane);
+        __syncthreads();
+        for (int c = 0; c < n; c += 2) {
+            load_rec(r1, wk, c + 1, h, lane);
+            read_ring_w(q, sm, c, h, lane);
+            read_ring_kl(q, sm, c, h, lane);
+            rec_step(st, r0, q, q, sm, c, false, h, lane, with_u);
+            if (c + 1 >= n) break;
+            load_rec(r0, wk, c + 2, h, lane);
+            read_ring_w(q, sm, c + 1, h, lane);
+            read_ring_kl(q, sm, c + 1, h, lane);
+            rec_step(st, r1, q, q, sm, c + 1, false, h, lane, with_u);
+        }
+        return;
+    }
+    RingRegs<C> q0, q1;
     load_rec(r0, wk, 0, h, lane);
     __syncthreads();
+    read_ring_w(q0, sm, 0, h, lane);
+    read_ring_kl(q0, sm, 0, h, lane);
     for (int c = 0; c < n; c += 2) {
         load_rec(r1, wk, c + 1, h, lane);
-        rec_step(st, r0, sm, c, h, lane, with_u);
+        rec_step(st, r0, q0, q1, sm, c, c + 1 < n, h, lane, with_u);
         if (c + 1 >= n) break;
         load_rec(r0, wk, c + 2, h, lane);
-        rec_step(st, r1, sm, c + 1, h, lane, with_u);
+        rec_step(st, r1, q1, q0, sm, c + 1, c + 2 < n, h, lane, with_u);
     }
 }
 
