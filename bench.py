@@ -128,32 +128,34 @@ def _counter_median(path: str, counter: str, kernel_substr: str) -> float:
 
 def choose_path(x, path: str, prologue: bool, segments: int = 1) -> str:
     """pipe (gdn_prefill / gdn_prefill_fused), split (gdn_prefill_split / _fused) or seg
-    (gdn_prefill_seg) for this workload.  auto takes a two-launch path for 16-bit I/O when
-    the one-launch kernel's workgroups (one per CU) would leave at least half of the 256 CUs
-    idle, or for a packed batch of several sequences (where the one-launch kernel's
-    longest sequences set its time); among them the segmented one when
-    gdn_prefill_seg_choose gave more than one segment (not with the prologue)."""
+    (gdn_prefill_seg) for this workload: the rule gdn_prefill_auto_plan applies on a
+    256-CU device (the timed run asks the library itself; this copy names the kernels
+    of a counter summary on a host without the GPU).  A two-launch path for 16-bit I/O
+    when its chain's N * Hv * 8 workgroups fit the 256 CUs in one round, or for a packed
+    batch of several sequences; among them the segmented one when gdn_prefill_seg_choose
+    gave more than one segment (not with the prologue)."""
     if path != "auto":
         return path
-    if x.io != "f32" and (x.N * x.Hv * 8 <= 128 or x.N > 1):
+    if x.io != "f32" and (x.N * x.Hv * 8 <= 256 or x.N > 1):
         return "seg" if segments > 1 and not prologue else "split"
     return "pipe"
 
 
 def summarize_pmc(directory: str, workload: int, calib_mib: int, io=None, kda=False, prologue=False,
-                  path: str = "auto", shard: int = 1) -> dict:
+                  path: str = "auto", shard: int = 1, segments: int = 1) -> dict:
     """Scale the FETCH_SIZE / WRITE_SIZE counters (KiB per dispatch) of the prefill kernel by
     what the same counters read for a copy of known size; rocprofv3 runs of bench.py wrote
     fetch_, write_, copyfetch_ and copywrite_counter_collection.csv into `directory`.  With
     kda the step's two kernels are added (bytes per step); with prologue the counters are
-    those of a `bench.py --prologue` run."""
+    those of a `bench.py --prologue` run; `segments` is the count the run's library chose
+    (the host has no device to ask)."""
     from linear_attention_chunked_gdn_amd import gdn, inputs
     x = inputs.head_shard(inputs.make_workload(workload, io=io, per_channel=kda, raw=prologue), shard)
     if kda:
         kernel = "kda_map_kernel+kda_chain_kernel"
-    elif choose_path(x, path, prologue) == "seg":
+    elif choose_path(x, path, prologue, segments) == "seg":
         kernel = "gdn_map_kernel+kda_chain_kernel+gdn_seg_join_kernel+gdn_seg_fix_kernel"
-    elif choose_path(x, path, prologue) == "split":
+    elif choose_path(x, path, prologue, segments) == "split":
         kernel = "gdn_map_kernel+kda_chain_kernel"
     else:
         plan = gdn.prefill_plan(x.N, x.Hv, IO_CODE[x.io])
@@ -390,7 +392,7 @@ def main() -> int:
         return 2
     if args.summarize_pmc:
         entry = summarize_pmc(args.summarize_pmc, args.workload, args.calibrate_copy or 256, args.io, args.kda,
-                              args.prologue, args.path, args.head_shard)
+                              args.prologue, args.path, args.head_shard, args.segments or 1)
         try:
             with open(TRAFFIC_FILE) as f:
                 table = json.load(f)

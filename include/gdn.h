@@ -382,8 +382,8 @@ gdn_status gdn_prefill_plan(int32_t N, int32_t Hv, int32_t Dv, gdn_dtype io_dtyp
  * non-NULL pointers, the path (gdn_prefill_path), the segment count (1 unless
  * GDN_PATH_SEG) and the workspace bytes gdn_prefill_auto needs for these sizes (0 for
  * GDN_PATH_ONE_LAUNCH; workspace_bytes must be non-NULL).  fp32 I/O always takes the
- * one-launch path; 16-bit I/O takes a two-launch path when the one-launch kernel's
- * N * Hv * 8 workgroups would fill at most half of the compute units, or when N > 1,
+ * one-launch path; 16-bit I/O takes a two-launch path when their chain's N * Hv * 8
+ * workgroups fit the compute units in one round, or when N > 1,
  * and the segmented one when gdn_prefill_seg_choose gives more than one segment and
  * prologue is 0.
  *

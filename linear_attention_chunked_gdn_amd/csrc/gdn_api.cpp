@@ -671,11 +671,11 @@ gdn_status gdn_kda_decode_step(const void *q, const void *k, const void *v, cons
 namespace {
 
 // The path gdn_prefill_auto takes.  fp32 I/O has only the one-launch path.  With 16-bit
-// I/O the two-launch paths win when the one-launch kernel (one workgroup per (sequence,
-// head, 16 value channels), each redoing the state-independent products of its chunks on
-// its own critical path) would leave at least half of the compute units idle, and for
-// packed batches of several sequences (whose longest sequence sets the one-launch
-// kernel's time, while the two-launch map covers all chunks at once).  Among the two, the
+// I/O the two-launch paths win whenever their chain kernel's workgroups (one per
+// (sequence, head, 16 value channels)) fit the compute units in one round, and for
+// packed batches of several sequences: the one-launch kernel has the same workgroups,
+// but each redoes the state-independent products of its chunks on its own critical
+// path, while the two-launch map does them once, on the whole chip.  Among the two, the
 // segmented one when gdn_prefill_seg_choose gives more than one segment (it has no
 // prologue).
 struct AutoPlan {
@@ -696,7 +696,7 @@ gdn_status auto_plan(int32_t N, int32_t T_tot, int32_t Hv, gdn_dtype io_dtype, u
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
         return fail(GDN_ERR_DEVICE, "cannot read the current device's compute-unit count");
-    if (!(2LL * N * Hv * (kD / 16) <= cus || N > 1)) return GDN_OK;
+    if (!((long long)N * Hv * (kD / 16) <= cus || N > 1)) return GDN_OK;
     int32_t K = 1;
     if (!prologue) {
         const gdn_status st = gdn_prefill_seg_choose(N, T_tot, Hv, kChunk, &K);
