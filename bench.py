@@ -136,9 +136,15 @@ def choose_path(x, path: str, prologue: bool, segments: int = 1) -> str:
     gave more than one segment (not with the prologue)."""
     if path != "auto":
         return path
-    if x.io != "f32" and (x.N * x.Hv * 8 <= 256 or x.N > 1):
-        return "seg" if segments > 1 and not prologue else "split"
+    if x.io != "f32" and (x.N * x.Hv * chain_workgroups_per_head(64, True) <= 256 or x.N > 1):
+        return "seg" if segments >= 3 and not prologue else "split"
     return "pipe"
+
+
+def chain_workgroups_per_head(chunk: int, wide: bool) -> int:
+    """The chain kernel's workgroups per (sequence, head): one per 16 value channels, or
+    with two slices per workgroup (chunks of up to 64 tokens) one per 32."""
+    return 4 if wide and chunk <= 64 else 8
 
 
 def summarize_pmc(directory: str, workload: int, calib_mib: int, io=None, kda=False, prologue=False,
@@ -535,7 +541,9 @@ def main() -> int:
         kernel = ("kda_map_kernel" if path == "kda" else "gdn_map_kernel") + "+kda_chain_kernel"
         nseg = segments if path == "seg" else 1
         launch = {"path": path, "kernel": kernel, "map_workgroups": (x.T_tot // chunk + x.N) * x.Hv,
-                  "chain_workgroups": x.N * x.Hv * 8 * (2 * nseg - 1), "workspace_bytes": int(ws.numel()),
+                  "chain_workgroups": x.N * x.Hv * (2 * nseg - 1) * chain_workgroups_per_head(
+                      chunk, path == "seg" or x.N * x.Hv * 8 > 256),
+                  "workspace_bytes": int(ws.numel()),
                   "input_copies_rotated": copies}
         if path == "seg":
             kernel += "+gdn_seg_join_kernel+gdn_seg_fix_kernel"

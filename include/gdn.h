@@ -325,9 +325,10 @@ gdn_status gdn_prefill_split_fused(const void *q, const void *k, const void *v,
  * fp16 Dk x Dk states.
  *
  * gdn_prefill_seg_choose -- a segment count for these sizes on the current device: the
- * largest with one recurrence workgroup per compute unit, N * Hv * 8 * (2 segments - 1)
- * <= compute units, and at least 4 chunks per segment on average; 1 means "use
- * gdn_prefill_split".  Reads the device's compute-unit count (GDN_ERR_DEVICE if that
+ * largest with one recurrence workgroup per compute unit, N * Hv * W * (2 segments - 1)
+ * <= compute units, where W is the recurrence's workgroups per (sequence, head): 4 (32
+ * value channels each) for chunk_size 32 or 64, 8 for 128; and at least 4 chunks per
+ * segment on average; 1 means "use gdn_prefill_split".  Reads the device's compute-unit count (GDN_ERR_DEVICE if that
  * fails).  Host pointer `segments`.
  */
 gdn_status gdn_prefill_seg_workspace_size(int32_t N, int32_t T_tot, int32_t Hv,
@@ -382,10 +383,10 @@ gdn_status gdn_prefill_plan(int32_t N, int32_t Hv, int32_t Dv, gdn_dtype io_dtyp
  * non-NULL pointers, the path (gdn_prefill_path), the segment count (1 unless
  * GDN_PATH_SEG) and the workspace bytes gdn_prefill_auto needs for these sizes (0 for
  * GDN_PATH_ONE_LAUNCH; workspace_bytes must be non-NULL).  fp32 I/O always takes the
- * one-launch path; 16-bit I/O takes a two-launch path when their chain's N * Hv * 8
- * workgroups fit the compute units in one round, or when N > 1,
- * and the segmented one when gdn_prefill_seg_choose gives more than one segment and
- * prologue is 0.
+ * one-launch path; 16-bit I/O takes a two-launch path when their chain's N * Hv * 4
+ * workgroups (two 16-channel slices each, 64-token chunks) fit the compute units in one
+ * round, or when N > 1, and the segmented one when gdn_prefill_seg_choose gives at least
+ * three segments and prologue is 0.
  *
  * gdn_prefill_auto takes gdn_prefill_fused's arguments (chunk_size is 64) plus a
  * caller-owned workspace of at least the planned bytes on the same device (256-byte

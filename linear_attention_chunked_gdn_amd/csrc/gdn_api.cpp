@@ -211,6 +211,23 @@ gdn_status check_prefill(const void *q, const void *k, const void *v, const floa
     return check_enabled() && cu_seqlens ? check_cu_seqlens(cu_seqlens, N, T_tot, stream) : GDN_OK;
 }
 
+// The current device's compute units, 0 if they cannot be read.
+int device_cus() {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 0;
+    return cus;
+}
+
+// Two 16-channel slices per chain workgroup (chunks of up to 64 tokens) when one slice per
+// workgroup would need more than one round of workgroups on the device: half the
+// workgroups, each about twice as long per chunk.  One slice otherwise (shorter chunks).
+bool wide_chain(int32_t N, int32_t Hv, int32_t chunk) {
+    const int cus = device_cus();
+    return chunk <= 64 && cus > 0 && (long long)N * Hv * gdn::chain_workgroups_per_head(chunk, false) > cus;
+}
+
 // Chunk slots of the per-key-channel prefill: chunk j of sequence n uses slot
 // cu[n] / 64 + n + j, and these never exceed T_tot / 64 + N.
 size_t kda_slots(int32_t N, int32_t T_tot, int32_t C = kChunk) { return (size_t)T_tot / C + (size_t)N; }
@@ -320,7 +337,7 @@ gdn_status gdn_kda_prefill(const void *q, const void *k, const void *v, const fl
     const bool f16 = io_dtype == GDN_F16;
     (void)hipGetLastError();
     hipError_t e = T_tot > 0 ? gdn::launch_kda_map(a, f16, hs) : hipSuccess;
-    if (e == hipSuccess) e = gdn::launch_kda_chain(a, f16, kChunk, true, hs);
+    if (e == hipSuccess) e = gdn::launch_kda_chain(a, f16, kChunk, true, wide_chain(N, Hv, kChunk), hs);
     if (e != hipSuccess)
         return fail(GDN_ERR_DEVICE, "kda prefill launch failed: %s", hipGetErrorString(e));
     return ok();
@@ -375,7 +392,7 @@ gdn_status split_impl(const void *q, const void *k, const void *v, const float *
     const bool f16 = io_dtype == GDN_F16;
     (void)hipGetLastError();
     hipError_t e = T_tot > 0 ? gdn::launch_gdn_map(a, f16, chunk_size, hs) : hipSuccess;
-    if (e == hipSuccess) e = gdn::launch_kda_chain(a, f16, chunk_size, false, hs);
+    if (e == hipSuccess) e = gdn::launch_kda_chain(a, f16, chunk_size, false, wide_chain(N, Hv, chunk_size), hs);
     if (e != hipSuccess)
         return fail(GDN_ERR_DEVICE, "split prefill launch failed: %s", hipGetErrorString(e));
     return ok();
@@ -498,9 +515,10 @@ gdn_status gdn_prefill_seg_choose(int32_t N, int32_t T_tot, int32_t Hv, int32_t 
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
         return fail(GDN_ERR_DEVICE, "cannot read the current device's compute-unit count");
-    // one chain workgroup per compute unit: 8 (2K - 1) per (sequence, head) for K segments
-    const long long pairs = (long long)N * Hv;
-    long long k = ((long long)cus / (8 * pairs) + 1) / 2;
+    // one chain workgroup per compute unit: W (2K - 1) per (sequence, head) for K segments,
+    // W the segmented chain's workgroups per head (two slices each up to 64-token chunks)
+    const long long pairs = (long long)N * Hv, W = gdn::chain_workgroups_per_head(chunk_size, chunk_size <= 64);
+    long long k = ((long long)cus / (W * pairs) + 1) / 2;
     // and at least 4 chunks per segment on average
     const long long chunks = (long long)T_tot / chunk_size / N;
     k = std::min(k, std::max(1LL, chunks / 4));
@@ -550,7 +568,7 @@ gdn_status seg_impl(const char *fn, bool per_channel, const void *q, const void 
     hipError_t e;
     if (T_tot == 0) {
         // no tokens: the final state is the initial state (the plain chain copies it)
-        e = gdn::launch_kda_chain(a, f16, chunk_size, per_channel, hs);
+        e = gdn::launch_kda_chain(a, f16, chunk_size, per_channel, chunk_size <= 64, hs);
     } else {
         size_t off = (size_t)slots * Hv * tile_bytes(chunk_size);
         a.o0 = reinterpret_cast<_Float16 *>(a.ws + off);
@@ -561,7 +579,7 @@ gdn_status seg_impl(const char *fn, bool per_channel, const void *q, const void 
         off += (size_t)N * Hv * segments * 2 * kD * kD * sizeof(float);
         a.sin16 = reinterpret_cast<_Float16 *>(a.ws + off);
         e = per_channel ? gdn::launch_kda_map(a, f16, hs) : gdn::launch_gdn_map(a, f16, chunk_size, hs);
-        if (e == hipSuccess) e = gdn::launch_seg_chain(a, f16, chunk_size, per_channel, hs);
+        if (e == hipSuccess) e = gdn::launch_seg_chain(a, f16, chunk_size, per_channel, chunk_size <= 64, hs);
         if (e == hipSuccess) e = gdn::launch_seg_join(a, hs);
         if (e == hipSuccess) e = gdn::launch_seg_fix(a, f16, chunk_size, hs);
     }
@@ -671,13 +689,14 @@ gdn_status gdn_kda_decode_step(const void *q, const void *k, const void *v, cons
 namespace {
 
 // The path gdn_prefill_auto takes.  fp32 I/O has only the one-launch path.  With 16-bit
-// I/O the two-launch paths win whenever their chain kernel's workgroups (one per
-// (sequence, head, 16 value channels)) fit the compute units in one round, and for
-// packed batches of several sequences: the one-launch kernel has the same workgroups,
-// but each redoes the state-independent products of its chunks on its own critical
-// path, while the two-launch map does them once, on the whole chip.  Among the two, the
-// segmented one when gdn_prefill_seg_choose gives more than one segment (it has no
-// prologue).
+// I/O the two-launch paths win whenever their chain kernel's workgroups (at most one per
+// (sequence, head, 32 value channels)) fit the compute units in one round, and for packed
+// batches of several sequences: the one-launch kernel's workgroups each redo the
+// state-independent products of their chunks on their own critical path, while the
+// two-launch map does them once, on the whole chip.  Among the two, the segmented one
+// when gdn_prefill_seg_choose gives at least three segments (it has no prologue): its
+// chain workgroups hold two slices and take about twice as long per chunk as the split
+// path's one-slice workgroups, so two segments only break even.
 struct AutoPlan {
     int32_t path, segments;
     size_t workspace;
@@ -696,13 +715,13 @@ gdn_status auto_plan(int32_t N, int32_t T_tot, int32_t Hv, gdn_dtype io_dtype, u
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
         return fail(GDN_ERR_DEVICE, "cannot read the current device's compute-unit count");
-    if (!((long long)N * Hv * (kD / 16) <= cus || N > 1)) return GDN_OK;
+    if (!((long long)N * Hv * gdn::chain_workgroups_per_head(kChunk, true) <= cus || N > 1)) return GDN_OK;
     int32_t K = 1;
     if (!prologue) {
         const gdn_status st = gdn_prefill_seg_choose(N, T_tot, Hv, kChunk, &K);
         if (st != GDN_OK) return st;
     }
-    if (K > 1) {
+    if (K >= 3) {
         *p = AutoPlan{GDN_PATH_SEG, K, 0};
         return gdn_prefill_seg_workspace_size(N, T_tot, Hv, kChunk, K, &p->workspace);
     }

@@ -108,16 +108,21 @@ __host__ __device__ constexpr int frag_byte(int j) { return 2 * ((j & 3) + ((j &
 constexpr size_t WS_TILE_BYTES = Tile<64>::BYTES;
 hipError_t launch_kda_map(const KdaArgs &a, bool f16, hipStream_t stream);
 // The chain over tiles of `chunk` tokens (32, 64 or 128); per_channel: GL differs per key
-// channel (the KDA map), else one decay per chunk (the scalar-gate map).
-hipError_t launch_kda_chain(const KdaArgs &a, bool f16, int chunk, bool per_channel, hipStream_t stream);
+// channel (the KDA map), else one decay per chunk (the scalar-gate map); wide: two 16-value-
+// channel slices per workgroup (chunks of up to 64 tokens), else one.
+hipError_t launch_kda_chain(const KdaArgs &a, bool f16, int chunk, bool per_channel, bool wide, hipStream_t stream);
 int kda_map_lds_bytes();
 int kda_chain_lds_bytes();
+// The chain kernel's workgroups per (sequence, head): one per 16 value channels, or with
+// `wide` (chunks of up to 64 tokens) one per 32, whose two slices share every operand
+// fragment (half the workgroups, each about twice as long per chunk).
+int chain_workgroups_per_head(int chunk, bool wide);
 // The scalar-gate map (KdaArgs::g is [T_tot, Hv]) into the same workspace tiles, read by
 // launch_kda_chain.
 hipError_t launch_gdn_map(const KdaArgs &a, bool f16, int chunk, hipStream_t stream);
 // The segmented chain (the chain kernel in its segment mode), then the two kernels that join
 // the segments (gdn_seg.hip): the segments' start states, and the outputs' corrections.
-hipError_t launch_seg_chain(const KdaArgs &a, bool f16, int chunk, bool per_channel, hipStream_t stream);
+hipError_t launch_seg_chain(const KdaArgs &a, bool f16, int chunk, bool per_channel, bool wide, hipStream_t stream);
 hipError_t launch_seg_join(const KdaArgs &a, hipStream_t stream);
 hipError_t launch_seg_fix(const KdaArgs &a, bool f16, int chunk, hipStream_t stream);
 // one token with a per-key-channel gate: DecodeArgs::g is [B, Hv, 128]

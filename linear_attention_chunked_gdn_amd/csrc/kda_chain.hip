@@ -57,16 +57,20 @@ typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int DK = 128;
 constexpr int DV = 128;
-constexpr int DVS = 16;         // value channels per workgroup
-constexpr int NSL = DV / DVS;   // workgroups per (sequence, head)
 // waves 0, 1: the recurrence (key halves); 2 .. 5: the outputs (token tiles t = 4 k + o);
 // 6, 7: the loaders (WN, Kl)
 constexpr int THREADS = 512;
 
-template <int C>
+template <int C, int SPW_ = 1>
 struct Cfg {
     static constexpr int NT = C / 16;             // 16-token tiles
     static constexpr int KB = C / 32;             // 32-token reduction blocks
+    // 16-value-channel slices per workgroup: one, or two (their WN, Kl, Qg and P operands
+    // shared in the same registers; up to C = 64, two would not fit the LDS at 128)
+    static constexpr int SPW = SPW_;
+    static_assert(SPW == 1 || (SPW == 2 && C <= 64), "two slices up to C = 64");
+    static constexpr int DVS = 16 * SPW;          // value channels per workgroup
+    static constexpr int NSL = DV / DVS;          // workgroups per (sequence, head)
     static constexpr int NW = NT * 4;             // WN fragments per chunk
     static constexpr int NK = 8 * KB;             // Kl fragments per chunk
     // operand ring depth: chunk c + NB - 1 is loaded while chunk c runs
@@ -86,17 +90,18 @@ __device__ __forceinline__ f32x4 mfma(const f16x8 &a, const f16x8 &b, const f32x
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
-// LDS: the operand ring and two exchange slots (112 KB at C = 64, 152 KB at C = 128).
-template <int C>
+// LDS: the operand ring and two exchange slots (128 KB at C = 64, 152 KB at C = 128).
+template <int C, int SPW>
 struct __align__(16) Smem {
+    using F = Cfg<C, SPW>;
     struct Ops {
-        f16x8 w[Cfg<C>::NW * 64];   // WN fragments (t, kb), lane-major, as in the tile
-        f16x8 kl[Cfg<C>::NK * 64];  // Kl fragments (i, kb)
-    } ob[Cfg<C>::NB];
-    f16x8 xs[2][4 * 64];                 // S^T fragments (key blocks 0..3)
-    u32x2 pv[2][2][Cfg<C>::NT * 64];     // the recurrence waves' partials, fp16, per token tile
+        f16x8 w[F::NW * 64];   // WN fragments (t, kb), lane-major, as in the tile
+        f16x8 kl[F::NK * 64];  // Kl fragments (i, kb)
+    } ob[F::NB];
+    f16x8 xs[2][F::SPW * 4 * 64];             // S^T fragments (slice, key block)
+    u32x2 pv[2][2][F::SPW][F::NT * 64];       // the recurrence waves' partials, fp16 (wave, slice, token tile)
 };
-static_assert(sizeof(Smem<32>) <= 160 * 1024 && sizeof(Smem<64>) <= 160 * 1024 && sizeof(Smem<128>) <= 160 * 1024,
+static_assert(sizeof(Smem<32, 2>) <= 160 * 1024 && sizeof(Smem<64, 2>) <= 160 * 1024 && sizeof(Smem<128, 1>) <= 160 * 1024,
               "the LDS holds the ring");
 
 struct Work {
@@ -109,7 +114,7 @@ struct Work {
 // end read it again).  Operands are read with buffer loads: a lane's byte offset is one
 // VGPR for every load, the tile and the fragment offsets are scalars, so no load needs a
 // 64-bit address computed in vector registers, and every access is bounded by the tile.
-template <int C>
+template <int C, int SPW>
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const Work &wk, int c) {
     const char *tile = wk.ws + (size_t)min(c, wk.nchunks - 1) * wk.slot_stride;
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(tile), 0, (int)Tile<C>::BYTES, 0x00020000);
@@ -133,12 +138,12 @@ __device__ __forceinline__ void wait_vmcnt() {
 // Chunk c's WN (KL false) or Kl fragments into ring buffer c % NB, one 1 KB fragment per
 // instruction, global to LDS directly (lane l's 16 bytes land at 16 l: the fragment
 // layout of the tile is kept).
-template <int C, bool KL>
-__device__ __forceinline__ void dma_chunk(Smem<C> &sm, const Work &wk, int c, int lane) {
-    using F = Cfg<C>;
+template <int C, int SPW, bool KL>
+__device__ __forceinline__ void dma_chunk(Smem<C, SPW> &sm, const Work &wk, int c, int lane) {
+    using F = Cfg<C, SPW>;
     using TL = Tile<C>;
-    const __amdgpu_buffer_rsrc_t r = tile_rsrc<C>(wk, c);
-    typename Smem<C>::Ops &ob = sm.ob[c % F::NB];
+    const __amdgpu_buffer_rsrc_t r = tile_rsrc<C, SPW>(wk, c);
+    typename Smem<C, SPW>::Ops &ob = sm.ob[c % F::NB];
     f16x8 *dst = KL ? ob.kl : ob.w;
     constexpr int NF = KL ? F::NK : F::NW;
     constexpr int SRC = KL ? TL::KL : TL::WN;
@@ -152,42 +157,45 @@ __device__ __forceinline__ void dma_chunk(Smem<C> &sm, const Work &wk, int c, in
 // chunk c + 1 must have landed before barrier c: the loads have NB - 1 chunks to land.
 // Plain s_barrier: the waits on this wave's own loads are explicit (vmcnt counts them in
 // issue order); it writes LDS only through the loads.
-template <int C, bool KL>
-__device__ __forceinline__ void loader_run(Smem<C> &sm, const Work &wk, int lane) {
-    using F = Cfg<C>;
+template <int C, int SPW, bool KL>
+__device__ __forceinline__ void loader_run(Smem<C, SPW> &sm, const Work &wk, int lane) {
+    using F = Cfg<C, SPW>;
     constexpr int NF = KL ? F::NK : F::NW;
 #pragma unroll
-    for (int j = 0; j < F::NB; ++j) dma_chunk<C, KL>(sm, wk, j, lane);
+    for (int j = 0; j < F::NB; ++j) dma_chunk<C, SPW, KL>(sm, wk, j, lane);
     wait_vmcnt<(F::NB - 1) * NF>();   // chunk 0
     __builtin_amdgcn_s_barrier();
     for (int c = 0; c < wk.nchunks; ++c) {
         wait_vmcnt<(F::NB - 2) * NF>();   // chunk c + 1
         __builtin_amdgcn_s_barrier();
-        dma_chunk<C, KL>(sm, wk, c + F::NB, lane);
+        dma_chunk<C, SPW, KL>(sm, wk, c + F::NB, lane);
     }
     wait_vmcnt<0>();   // nothing in flight into the LDS when the workgroup ends
 }
 
 // ---- the recurrence -------------------------------------------------------------------
 
-// Recurrence wave h's global operands for one chunk: half of the workgroup's slice of U
-// (token tiles h NT / 2 .. (h + 1) NT / 2 - 1, which its partial adds) and its keys'
+// Recurrence wave h's global operands for one chunk: half of the token tiles of the
+// workgroup's U slices (tiles h NT / 2 .. (h + 1) NT / 2 - 1, which its partials add; the
+// same loads on both waves, so that the compiler's load counts are exact) and its keys'
 // decays gl (one value for the scalar gate).  WN and Kl come from the ring.
-template <int C, bool PERCH>
+template <int C, int SPW, bool PERCH>
 struct RecRegs {
-    u32x2 u[Cfg<C>::NT / 2];
+    u32x2 u[Cfg<C, SPW>::SPW][Cfg<C, SPW>::NT / 2];
     f32x4 gl[PERCH ? 4 : 1];
 };
 
-template <int C, bool PERCH>
-__device__ __forceinline__ void load_rec(RecRegs<C, PERCH> &rg, const Work &wk, int c, int h, int lane) {
-    using F = Cfg<C>;
+template <int C, int SPW, bool PERCH>
+__device__ __forceinline__ void load_rec(RecRegs<C, SPW, PERCH> &rg, const Work &wk, int c, int h, int lane) {
+    using F = Cfg<C, SPW>;
     using TL = Tile<C>;
-    const __amdgpu_buffer_rsrc_t r = tile_rsrc<C>(wk, c);
+    const __amdgpu_buffer_rsrc_t r = tile_rsrc<C, SPW>(wk, c);
 #pragma unroll
-    for (int t = 0; t < F::NT / 2; ++t)
-        rg.u[t] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, 8 * lane,
-                                                                                 TL::u(wk.slice, h * F::NT / 2 + t), 0));
+    for (int s = 0; s < F::SPW; ++s)
+#pragma unroll
+        for (int t = 0; t < F::NT / 2; ++t)
+            rg.u[s][t] = __builtin_bit_cast(
+                u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, 8 * lane, TL::u(wk.slice * F::SPW + s, h * F::NT / 2 + t), 0));
     if constexpr (PERCH) {
         // keys 64 h + 16 i + 4 G + q: 16 bytes at GL + 4 (16 (4 h + i) + 4 G)
 #pragma unroll
@@ -200,157 +208,153 @@ __device__ __forceinline__ void load_rec(RecRegs<C, PERCH> &rg, const Work &wk, 
 }
 
 // Recurrence wave h's halves of WN and Kl for one chunk, from its ring buffer.
-template <int C>
+template <int C, int SPW>
 struct RingRegs {
-    f16x8 w[Cfg<C>::NT][2];
-    f16x8 kl[4][Cfg<C>::KB];
+    f16x8 w[Cfg<C, SPW>::NT][2];
+    f16x8 kl[4][Cfg<C, SPW>::KB];
 };
 
-template <int C>
-__device__ __forceinline__ void read_ring_w(RingRegs<C> &rr, const Smem<C> &sm, int c, int h, int lane) {
-    using F = Cfg<C>;
-    const typename Smem<C>::Ops &ob = sm.ob[c % F::NB];
+template <int C, int SPW>
+__device__ __forceinline__ void read_ring_w(RingRegs<C, SPW> &rr, const Smem<C, SPW> &sm, int c, int h, int lane) {
+    using F = Cfg<C, SPW>;
+    const typename Smem<C, SPW>::Ops &ob = sm.ob[c % F::NB];
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int t = 0; t < F::NT; ++t) rr.w[t][j] = ob.w[(4 * t + 2 * h + j) * 64 + lane];
 }
 
-template <int C>
-__device__ __forceinline__ void read_ring_kl(RingRegs<C> &rr, const Smem<C> &sm, int c, int h, int lane) {
-    using F = Cfg<C>;
-    const typename Smem<C>::Ops &ob = sm.ob[c % F::NB];
+template <int C, int SPW>
+__device__ __forceinline__ void read_ring_kl(RingRegs<C, SPW> &rr, const Smem<C, SPW> &sm, int c, int h, int lane) {
+    using F = Cfg<C, SPW>;
+    const typename Smem<C, SPW>::Ops &ob = sm.ob[c % F::NB];
 #pragma unroll
     for (int kb = 0; kb < F::KB; ++kb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) rr.kl[i][kb] = ob.kl[((4 * h + i) * F::KB + kb) * 64 + lane];
 }
 
-// Chunk c on recurrence wave h, around barrier c: the partial, the exchange, the update,
-// with chunk c's operands in cur.  Chunk c + 1's buffer is complete before barrier c, so
-// its reads into nxt are issued right after it and land during this chunk's exchange and
-// update (WN first, needed first).  with_u is 0 for the identity rows of a segment (no U
-// term).
-template <int C, bool PERCH>
-__device__ __forceinline__ void rec_step(f32x4 (&st)[4], const RecRegs<C, PERCH> &rg, const RingRegs<C> &cur,
-                                         RingRegs<C> &nxt, Smem<C> &sm, int c, bool more, int h, int lane,
-                                         bool with_u) {
-    using F = Cfg<C>;
-    f16x8 sb[2];
+// Chunk c on recurrence wave h, around barrier c: its halves of WN and Kl from ring buffer
+// c % NB, then per slice the partial, the exchange, the update; every WN and Kl fragment
+// serves all of the workgroup's slices.  with_u is 0 for the identity rows of a segment
+// (no U term).
+template <int C, int SPW, bool PERCH>
+__device__ __forceinline__ void rec_step(f32x4 (&st)[SPW][4], const RecRegs<C, SPW, PERCH> &rg, Smem<C, SPW> &sm,
+                                         int c, int h, int lane, bool with_u) {
+    using F = Cfg<C, SPW>;
+    RingRegs<C, SPW> cur;
+    read_ring_w(cur, sm, c, h, lane);
+    read_ring_kl(cur, sm, c, h, lane);
+    f16x8 sb[SPW][2];
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int s = 0; s < SPW; ++s)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            sb[j][e] = (hf)st[2 * j][e];
-            sb[j][4 + e] = (hf)st[2 * j + 1][e];
-        }
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                sb[s][j][e] = (hf)st[s][2 * j][e];
+                sb[s][j][4 + e] = (hf)st[s][2 * j + 1][e];
+            }
     // U on this wave's half of the token tiles
-    f32x4 p[F::NT];
+    f32x4 p[SPW][F::NT];
 #pragma unroll
-    for (int t = 0; t < F::NT; ++t) {
-        const f16x4 uu = __builtin_bit_cast(f16x4, rg.u[t % (F::NT / 2)]);
-        const bool add = with_u && t / (F::NT / 2) == h;
+    for (int s = 0; s < SPW; ++s)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) p[t][q] = add ? (float)uu[q] : 0.f;
-    }
+        for (int t = 0; t < F::NT; ++t) {
+            const f16x4 uu = __builtin_bit_cast(f16x4, rg.u[s][t % (F::NT / 2)]);
+            const bool add = with_u && t / (F::NT / 2) == h;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) p[s][t][q] = add ? (float)uu[q] : 0.f;
+        }
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int t = 0; t < F::NT; ++t) p[t] = mfma(cur.w[t][j], sb[j], p[t]);
+        for (int t = 0; t < F::NT; ++t)
+#pragma unroll
+            for (int s = 0; s < SPW; ++s) p[s][t] = mfma(cur.w[t][j], sb[s][j], p[s][t]);
     f16x8 *xs = sm.xs[c & 1];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) xs[(2 * h + j) * 64 + lane] = sb[j];
+    for (int s = 0; s < SPW; ++s)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) xs[(4 * s + 2 * h + j) * 64 + lane] = sb[s][j];
     // the decay of the state (off the partial's path)
-    if constexpr (PERCH) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) st[i] *= rg.gl[i];
-    } else {
+    for (int s = 0; s < SPW; ++s) {
+        if constexpr (PERCH) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) st[i] *= rg.gl[0][0];
-    }
-    f16x4 ph[F::NT];
+            for (int i = 0; i < 4; ++i) st[s][i] *= rg.gl[i];
+        } else {
 #pragma unroll
-    for (int t = 0; t < F::NT; ++t)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) ph[t][q] = (hf)p[t][q];
-    u32x2 *mine = sm.pv[c & 1][h];
-#pragma unroll
-    for (int t = 0; t < F::NT; ++t) mine[t * 64 + lane] = __builtin_bit_cast(u32x2, ph[t]);
-    __syncthreads();
-    const u32x2 *other = sm.pv[c & 1][h ^ 1];
-    f16x4 po[F::NT];
-#pragma unroll
-    for (int t = 0; t < F::NT; ++t) po[t] = __builtin_bit_cast(f16x4, other[t * 64 + lane]);
-    if (more) read_ring_w(nxt, sm, c + 1, h, lane);
-    // v = p_0 + p_1 from the fp16 partials (addition commutes exactly: every wave that
-    // forms v gets the same values)
-    f16x8 vb[F::KB];
-#pragma unroll
-    for (int kb = 0; kb < F::KB; ++kb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            vb[kb][e] = (hf)((float)ph[2 * kb][e] + (float)po[2 * kb][e]);
-            vb[kb][4 + e] = (hf)((float)ph[2 * kb + 1][e] + (float)po[2 * kb + 1][e]);
+            for (int i = 0; i < 4; ++i) st[s][i] *= rg.gl[0][0];
         }
+    }
+    f16x4 ph[SPW][F::NT];
 #pragma unroll
-    for (int kb = 0; kb < F::KB; ++kb)
+    for (int s = 0; s < SPW; ++s)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) st[i] = mfma(cur.kl[i][kb], vb[kb], st[i]);
-    if (more) read_ring_kl(nxt, sm, c + 1, h, lane);
+        for (int t = 0; t < F::NT; ++t)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) ph[s][t][q] = (hf)p[s][t][q];
+#pragma unroll
+    for (int s = 0; s < SPW; ++s)
+#pragma unroll
+        for (int t = 0; t < F::NT; ++t) sm.pv[c & 1][h][s][t * 64 + lane] = __builtin_bit_cast(u32x2, ph[s][t]);
+    __syncthreads();
+    // v = p_0 + p_1 from the fp16 partials (addition commutes exactly: every wave that
+    // forms v gets the same values), then the update
+#pragma unroll
+    for (int s = 0; s < SPW; ++s) {
+        f16x4 po[F::NT];
+#pragma unroll
+        for (int t = 0; t < F::NT; ++t) po[t] = __builtin_bit_cast(f16x4, sm.pv[c & 1][h ^ 1][s][t * 64 + lane]);
+        f16x8 vb[F::KB];
+#pragma unroll
+        for (int kb = 0; kb < F::KB; ++kb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                vb[kb][e] = (hf)((float)ph[s][2 * kb][e] + (float)po[2 * kb][e]);
+                vb[kb][4 + e] = (hf)((float)ph[s][2 * kb + 1][e] + (float)po[2 * kb + 1][e]);
+            }
+#pragma unroll
+        for (int kb = 0; kb < F::KB; ++kb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) st[s][i] = mfma(cur.kl[i][kb], vb[kb], st[s][i]);
+    }
 }
 
 // Recurrence wave h's run: barrier -1 (chunk 0 in the ring), then a barrier per chunk;
-// U and gl of chunk c + 1 are loaded, and its ring operands read, while chunk c runs.
-template <int C, bool PERCH>
-__device__ __forceinline__ void rec_run(f32x4 (&st)[4], Smem<C> &sm, const Work &wk, int h, int lane, bool with_u) {
+// U and gl of chunk c + 1 are loaded while chunk c runs.
+template <int C, int SPW, bool PERCH>
+__device__ __forceinline__ void rec_run(f32x4 (&st)[SPW][4], Smem<C, SPW> &sm, const Work &wk, int h, int lane,
+                                        bool with_u) {
     const int n = wk.nchunks;
-    RecRegs<C, PERCH> r0, r1;
-    if constexpr (C >= 128) {   // a chunk's ring operands are 128 registers: one set, read at its start
-        RingRegs<C> q;
-        load_rec(r0, wk, 0, h, lane);
-        __syncthreads();
-        for (int c = 0; c < n; c += 2) {
-            load_rec(r1, wk, c + 1, h, lane);
-            read_ring_w(q, sm, c, h, lane);
-            read_ring_kl(q, sm, c, h, lane);
-            rec_step(st, r0, q, q, sm, c, false, h, lane, with_u);
-            if (c + 1 >= n) break;
-            load_rec(r0, wk, c + 2, h, lane);
-            read_ring_w(q, sm, c + 1, h, lane);
-            read_ring_kl(q, sm, c + 1, h, lane);
-            rec_step(st, r1, q, q, sm, c + 1, false, h, lane, with_u);
-        }
-        return;
-    }
-    RingRegs<C> q0, q1;
+    RecRegs<C, SPW, PERCH> r0, r1;
     load_rec(r0, wk, 0, h, lane);
     __syncthreads();
-    read_ring_w(q0, sm, 0, h, lane);
-    read_ring_kl(q0, sm, 0, h, lane);
     for (int c = 0; c < n; c += 2) {
         load_rec(r1, wk, c + 1, h, lane);
-        rec_step(st, r0, q0, q1, sm, c, c + 1 < n, h, lane, with_u);
+        rec_step(st, r0, sm, c, h, lane, with_u);
         if (c + 1 >= n) break;
         load_rec(r0, wk, c + 2, h, lane);
-        rec_step(st, r1, q1, q0, sm, c + 1, c + 2 < n, h, lane, with_u);
+        rec_step(st, r1, sm, c + 1, h, lane, with_u);
     }
 }
 
 // ---- the outputs ----------------------------------------------------------------------
 
 // Output wave O's operands for one chunk: Qg and P fragments of its token tiles 4 k + O.
-template <int C, int O>
+template <int C, int SPW, int O>
 struct OutOps {
-    using F = Cfg<C>;
+    using F = Cfg<C, SPW>;
     f16x8 qg[F::OT][4];
     f16x8 p[F::npo(O) > 0 ? F::npo(O) : 1];
 };
 
-template <int C, int O>
-__device__ __forceinline__ void load_out(OutOps<C, O> &op, const Work &wk, int c, int lane) {
-    using F = Cfg<C>;
+template <int C, int SPW, int O>
+__device__ __forceinline__ void load_out(OutOps<C, SPW, O> &op, const Work &wk, int c, int lane) {
+    using F = Cfg<C, SPW>;
     using TL = Tile<C>;
-    const __amdgpu_buffer_rsrc_t r = tile_rsrc<C>(wk, c);
+    const __amdgpu_buffer_rsrc_t r = tile_rsrc<C, SPW>(wk, c);
     int pi = 0;
 #pragma unroll
     for (int k = 0; k < F::OT; ++k) {
@@ -368,39 +372,54 @@ __device__ __forceinline__ void load_out(OutOps<C, O> &op, const Work &wk, int c
 // destination, all [token][head][channel]: 0 IO to o (segment 0), 1 fp16 to a.o0 (value
 // rows of later segments), 2 fp16 to a.e (identity rows); one 8-byte store for each,
 // with no branch between them.
-template <typename IO, int C, bool SEG, int O>
-__device__ __forceinline__ void out_step(const OutOps<C, O> &op, const Smem<C> &sm, int c, const KdaArgs &a,
+template <typename IO, int C, int SPW, bool SEG, int O>
+__device__ __forceinline__ void out_step(const OutOps<C, SPW, O> &op, const Smem<C, SPW> &sm, int c, const KdaArgs &a,
                                          int lane, int h, int dv0, int tok0, int nval, int kind) {
-    using F = Cfg<C>;
+    using F = Cfg<C, SPW>;
     const int l16 = lane & 15, g4 = lane >> 4;
     constexpr int TMAX = 4 * (F::OT - 1) + O;                   // its last token tile
     constexpr int VB = (TMAX < F::NT ? TMAX : F::NT - 1) / 2 + 1;  // v blocks it needs
     const f16x8 *xs = sm.xs[c & 1];
-    f16x8 sb[4], vb[VB];
+    f16x8 sb[SPW][4], vb[SPW][VB];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) sb[kb] = xs[kb * 64 + lane];
+    for (int s = 0; s < SPW; ++s)
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) sb[s][kb] = xs[(4 * s + kb) * 64 + lane];
     // v = p_0 + p_1, as the recurrence waves form it
 #pragma unroll
-    for (int kb = 0; kb < VB; ++kb)
+    for (int s = 0; s < SPW; ++s)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const f16x4 a0 = __builtin_bit_cast(f16x4, sm.pv[c & 1][0][(2 * kb + j) * 64 + lane]);
-            const f16x4 a1 = __builtin_bit_cast(f16x4, sm.pv[c & 1][1][(2 * kb + j) * 64 + lane]);
+        for (int kb = 0; kb < VB; ++kb)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) vb[kb][4 * j + e] = (hf)((float)a0[e] + (float)a1[e]);
-        }
+            for (int j = 0; j < 2; ++j) {
+                const f16x4 a0 = __builtin_bit_cast(f16x4, sm.pv[c & 1][0][s][(2 * kb + j) * 64 + lane]);
+                const f16x4 a1 = __builtin_bit_cast(f16x4, sm.pv[c & 1][1][s][(2 * kb + j) * 64 + lane]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) vb[s][kb][4 * j + e] = (hf)((float)a0[e] + (float)a1[e]);
+            }
     int pi = 0;
 #pragma unroll
     for (int k = 0; k < F::OT; ++k) {
         const int t = 4 * k + O;
         if (t >= F::NT) continue;
-        f32x4 acc = zero4();
+        f32x4 accs[SPW];
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) acc = mfma(sb[kb], op.qg[k][kb], acc);
+        for (int s = 0; s < SPW; ++s) accs[s] = zero4();
 #pragma unroll
-        for (int j = 0; j < F::npf(t); ++j) acc = mfma(vb[j], op.p[pi++], acc);
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int s = 0; s < SPW; ++s) accs[s] = mfma(sb[s][kb], op.qg[k][kb], accs[s]);
+#pragma unroll
+        for (int j = 0; j < F::npf(t); ++j) {
+#pragma unroll
+            for (int s = 0; s < SPW; ++s) accs[s] = mfma(vb[s][j], op.p[pi], accs[s]);
+            ++pi;
+        }
         const int tok = 16 * t + l16;
-        const size_t at = ((size_t)(tok0 + tok) * a.Hv + h) * DV + dv0 + 4 * g4;
+#pragma unroll
+        for (int s = 0; s < SPW; ++s) {
+        const f32x4 &acc = accs[s];
+        const size_t at = ((size_t)(tok0 + tok) * a.Hv + h) * DV + dv0 + 16 * s + 4 * g4;
         if constexpr (SEG) {
             typename Vec4<IO>::type yio;
             f16x4 yh;
@@ -418,25 +437,26 @@ __device__ __forceinline__ void out_step(const OutOps<C, O> &op, const Smem<C> &
             for (int i = 0; i < 4; ++i) y[i] = Cvt<IO>::from_f32(acc[i]);
             *reinterpret_cast<typename Vec4<IO>::type *>(reinterpret_cast<IO *>(a.o) + at) = y;
         }
+        }
     }
 }
 
 // Output wave O's run: barrier -1, then after barrier c it forms chunk c's outputs; the
 // loads of chunk c + 1 are issued before barrier c.  A wave with no token tile (O >= NT,
 // at C = 32) takes part in the barriers only.
-template <typename IO, int C, bool SEG, int O>
-__device__ __forceinline__ void output_run(const Smem<C> &sm, const KdaArgs &a, const Work &wk, int lane, int kind) {
-    using F = Cfg<C>;
+template <typename IO, int C, int SPW, bool SEG, int O>
+__device__ __forceinline__ void output_run(const Smem<C, SPW> &sm, const KdaArgs &a, const Work &wk, int lane, int kind) {
+    using F = Cfg<C, SPW>;
     const int n = wk.nchunks;
     if constexpr (O >= F::NT) {
         for (int c = 0; c <= n; ++c) __syncthreads();
         return;
     }
-    auto step = [&](const OutOps<C, O> &op, int c) {
+    auto step = [&](const OutOps<C, SPW, O> &op, int c) {
         const int tok0 = wk.bos + c * C;
-        out_step<IO, C, SEG, O>(op, sm, c, a, lane, wk.h, wk.dv0, tok0, min(C, wk.eos - tok0), kind);
+        out_step<IO, C, SPW, SEG, O>(op, sm, c, a, lane, wk.h, wk.dv0, tok0, min(C, wk.eos - tok0), kind);
     };
-    OutOps<C, O> op0, op1;
+    OutOps<C, SPW, O> op0, op1;
     load_out(op0, wk, 0, lane);
     __syncthreads();
     for (int c = 0; c < n; c += 2) {
@@ -475,9 +495,9 @@ __device__ __forceinline__ int longest_first(const int32_t *cu, int N, int r, in
 // real start state.  Segment 0 stores its outputs to o; later segments store theirs as
 // fp16 to a.o0 (value rows) or a.e (identity rows); end states go to a.sseg (X
 // transposed).  gdn_seg.hip joins them.
-template <typename IO, int C, bool SEG, bool PERCH>
+template <typename IO, int C, int SPW, bool SEG, bool PERCH>
 __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2))) void kda_chain_kernel(const KdaArgs a) {
-    __shared__ Smem<C> sm;
+    __shared__ Smem<C, SPW> sm;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -487,6 +507,8 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
     // segment's value and identity slices) form a group, and group g runs on XCD g % 8, so
     // its tiles are fetched into one L2.  The grid is padded to whole rounds of 8 groups;
     // the padding workgroups leave at once.
+    using F = Cfg<C, SPW>;
+    constexpr int NSL = F::NSL, DVS = F::DVS;
     constexpr int GS = SEG ? 2 * NSL : NSL;
     const int xcd = blockIdx.x & 7, kx = blockIdx.x >> 3;
     const int item = GS * (xcd + 8 * (kx / GS)) + kx % GS;
@@ -532,47 +554,55 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
     if (wave < 2) {
         const int kh = wave;   // key half
-        // S^T rows (key channels) 64 kh + 16 i + 4 G + q, column = value channel dv0 + m
-        f32x4 st[4];
+        // slice s: S^T rows (key channels) 64 kh + 16 i + 4 G + q, column = value channel
+        // dv0 + 16 s + m
+        f32x4 st[SPW][4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int dk = 64 * kh + 16 * i + 4 * g4;
-            f32x4 x = zero4();
-            if (seg == 0 && a.s0) x = *reinterpret_cast<const f32x4 *>(a.s0 + sbase + (size_t)(wk.dv0 + l16) * DK + dk);
-            if (ident) {
+        for (int sl = 0; sl < SPW; ++sl)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) x[q] = dk + q == wk.dv0 + l16 ? 1.f : 0.f;
+            for (int i = 0; i < 4; ++i) {
+                const int dk = 64 * kh + 16 * i + 4 * g4, r = wk.dv0 + 16 * sl + l16;
+                f32x4 x = zero4();
+                if (seg == 0 && a.s0) x = *reinterpret_cast<const f32x4 *>(a.s0 + sbase + (size_t)r * DK + dk);
+                if (ident) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) x[q] = dk + q == r ? 1.f : 0.f;
+                }
+                st[sl][i] = x;
             }
-            st[i] = x;
-        }
-        if (wk.nchunks > 0) rec_run<C, PERCH>(st, sm, wk, kh, lane, !ident);
+        if (wk.nchunks > 0) rec_run<C, SPW, PERCH>(st, sm, wk, kh, lane, !ident);
         if constexpr (SEG) {
             float *sb = a.sseg + ((((size_t)n * a.Hv + h) * a.nseg + seg) * 2 + (ident ? 1 : 0)) * DV * DK;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int dk = 64 * kh + 16 * i + 4 * g4, r = wk.dv0 + l16;
-                if (ident) {   // X^T [key][row]
+            for (int sl = 0; sl < SPW; ++sl)
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) sb[(size_t)(dk + q) * DV + r] = st[i][q];
-                } else {
-                    *reinterpret_cast<f32x4 *>(sb + (size_t)r * DK + dk) = st[i];
+                for (int i = 0; i < 4; ++i) {
+                    const int dk = 64 * kh + 16 * i + 4 * g4, r = wk.dv0 + 16 * sl + l16;
+                    if (ident) {   // X^T [key][row]
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) sb[(size_t)(dk + q) * DV + r] = st[sl][i][q];
+                    } else {
+                        *reinterpret_cast<f32x4 *>(sb + (size_t)r * DK + dk) = st[sl][i];
+                    }
                 }
-            }
         } else if (a.sN) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                *reinterpret_cast<f32x4 *>(a.sN + sbase + (size_t)(wk.dv0 + l16) * DK + 64 * kh + 16 * i + 4 * g4) = st[i];
+            for (int sl = 0; sl < SPW; ++sl)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    *reinterpret_cast<f32x4 *>(a.sN + sbase + (size_t)(wk.dv0 + 16 * sl + l16) * DK + 64 * kh + 16 * i +
+                                               4 * g4) = st[sl][i];
         }
     } else if (wk.nchunks > 0 && wave < 6) {
         switch (wave) {
-            case 2: output_run<IO, C, SEG, 0>(sm, a, wk, lane, kind); break;
-            case 3: output_run<IO, C, SEG, 1>(sm, a, wk, lane, kind); break;
-            case 4: output_run<IO, C, SEG, 2>(sm, a, wk, lane, kind); break;
-            default: output_run<IO, C, SEG, 3>(sm, a, wk, lane, kind); break;
+            case 2: output_run<IO, C, SPW, SEG, 0>(sm, a, wk, lane, kind); break;
+            case 3: output_run<IO, C, SPW, SEG, 1>(sm, a, wk, lane, kind); break;
+            case 4: output_run<IO, C, SPW, SEG, 2>(sm, a, wk, lane, kind); break;
+            default: output_run<IO, C, SPW, SEG, 3>(sm, a, wk, lane, kind); break;
         }
     } else if (wk.nchunks > 0) {
-        if (wave == 6) loader_run<C, false>(sm, wk, lane);
-        else loader_run<C, true>(sm, wk, lane);
+        if (wave == 6) loader_run<C, SPW, false>(sm, wk, lane);
+        else loader_run<C, SPW, true>(sm, wk, lane);
     }
 }
 
@@ -580,40 +610,44 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
 namespace {
 
-template <bool SEG, bool PERCH>
-hipError_t chain_launch(const KdaArgs &a, bool f16, int chunk, hipStream_t stream) {
+template <int C, int SPW, bool SEG, bool PERCH>
+hipError_t chain_launch_c(const KdaArgs &a, bool f16, hipStream_t stream) {
     // groups of GS workgroups (see the kernel), padded to whole rounds of 8 groups
-    constexpr unsigned long long GS = kdachain::NSL * (SEG ? 2 : 1);
+    constexpr unsigned long long GS = kdachain::Cfg<C, SPW>::NSL * (SEG ? 2 : 1);
     const unsigned long long groups = (unsigned long long)a.N * a.Hv * (SEG ? (unsigned long long)a.nseg : 1ull);
     const unsigned long long wgs = 8 * GS * ((groups + 7) / 8);
     if (wgs > 0x7fffffffULL) return hipErrorInvalidValue;
     const dim3 grid((unsigned)wgs), block(kdachain::THREADS);
-#define KDA_CHAIN_LAUNCH(C)                                                                                           \
-    do {                                                                                                              \
-        if (f16) hipLaunchKernelGGL((kdachain::kda_chain_kernel<_Float16, C, SEG, PERCH>), grid, block, 0, stream, a); \
-        else hipLaunchKernelGGL((kdachain::kda_chain_kernel<__bf16, C, SEG, PERCH>), grid, block, 0, stream, a);      \
-    } while (0)
+    if (f16) hipLaunchKernelGGL((kdachain::kda_chain_kernel<_Float16, C, SPW, SEG, PERCH>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((kdachain::kda_chain_kernel<__bf16, C, SPW, SEG, PERCH>), grid, block, 0, stream, a);
+    return hipGetLastError();
+}
+
+template <bool SEG, bool PERCH>
+hipError_t chain_launch(const KdaArgs &a, bool f16, int chunk, bool wide, hipStream_t stream) {
     switch (chunk) {
-        case 32: KDA_CHAIN_LAUNCH(32); break;
-        case 64: KDA_CHAIN_LAUNCH(64); break;
-        case 128: KDA_CHAIN_LAUNCH(128); break;
+        case 32: return wide ? chain_launch_c<32, 2, SEG, PERCH>(a, f16, stream) : chain_launch_c<32, 1, SEG, PERCH>(a, f16, stream);
+        case 64: return wide ? chain_launch_c<64, 2, SEG, PERCH>(a, f16, stream) : chain_launch_c<64, 1, SEG, PERCH>(a, f16, stream);
+        case 128: return wide ? hipErrorInvalidValue : chain_launch_c<128, 1, SEG, PERCH>(a, f16, stream);
         default: return hipErrorInvalidValue;
     }
-#undef KDA_CHAIN_LAUNCH
-    return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_kda_chain(const KdaArgs &a, bool f16, int chunk, bool per_channel, hipStream_t stream) {
-    return per_channel ? chain_launch<false, true>(a, f16, chunk, stream) : chain_launch<false, false>(a, f16, chunk, stream);
+hipError_t launch_kda_chain(const KdaArgs &a, bool f16, int chunk, bool per_channel, bool wide, hipStream_t stream) {
+    return per_channel ? chain_launch<false, true>(a, f16, chunk, wide, stream)
+                       : chain_launch<false, false>(a, f16, chunk, wide, stream);
 }
 
-hipError_t launch_seg_chain(const KdaArgs &a, bool f16, int chunk, bool per_channel, hipStream_t stream) {
+hipError_t launch_seg_chain(const KdaArgs &a, bool f16, int chunk, bool per_channel, bool wide, hipStream_t stream) {
     if (a.nseg < 1) return hipErrorInvalidValue;
-    return per_channel ? chain_launch<true, true>(a, f16, chunk, stream) : chain_launch<true, false>(a, f16, chunk, stream);
+    return per_channel ? chain_launch<true, true>(a, f16, chunk, wide, stream)
+                       : chain_launch<true, false>(a, f16, chunk, wide, stream);
 }
 
-int kda_chain_lds_bytes() { return (int)sizeof(kdachain::Smem<64>); }
+int kda_chain_lds_bytes() { return (int)sizeof(kdachain::Smem<64, 1>); }
+
+int chain_workgroups_per_head(int chunk, bool wide) { return wide && chunk <= 64 ? 4 : 8; }
 
 }  // namespace gdn

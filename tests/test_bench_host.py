@@ -38,9 +38,9 @@ def test_headline_counts():
 
 
 @pytest.mark.parametrize("lengths,Hk,Hv,io,prologue,segments,want", [
-    ([4096], 16, 16, "bf16", False, 1, "split"),   # 128 chain workgroups: one round
-    ([4096], 16, 32, "bf16", False, 1, "split"),   # 256 chain workgroups: still one round
-    ([4096], 16, 48, "bf16", False, 1, "pipe"),    # 384: the one-launch kernel
+    ([4096], 16, 16, "bf16", False, 2, "split"),   # two segments only break even
+    ([4096], 16, 64, "bf16", False, 1, "split"),   # 256 chain workgroups: still one round
+    ([4096], 16, 80, "bf16", False, 1, "pipe"),    # 320: the one-launch kernel
     ([100, 200], 16, 16, "bf16", False, 1, "split"),   # a packed batch
     ([4096], 4, 4, "bf16", False, 4, "seg"),       # few heads, several segments chosen
     ([4096], 4, 4, "bf16", True, 4, "split"),      # the prologue runs on the split path, not in segments

@@ -30,14 +30,14 @@ def _args(d):
 # ---- gdn_prefill_auto ------------------------------------------------------------------
 
 AUTO = [
-    # (inputs, expected path): the two-launch recurrence while its workgroups fit the 256
-    # CUs in one round (16 and 32 heads); 4 heads of a long sequence take segments; 48
-    # heads take the one-launch kernel; packed batches take the two-launch map; fp32 has
-    # one path
+    # (inputs, expected path): the two-launch recurrence while its workgroups (at least 4
+    # per head) fit the 256 CUs in one round, segmented when three or more segments fit
+    # (4 heads of a long sequence; 16 heads fit only two); 80 heads take the one-launch
+    # kernel; packed batches take the two-launch map; fp32 has one path
     (lambda: inputs.make_workload(1), "split"),
     (lambda: inputs.make_custom(7700, [8192], 2, 4, io="bf16", init_std=0.1, name="auto_H4_T8192"), "seg"),
     (lambda: inputs.make_custom(7701, [1000], 16, 32, io="f16", name="auto_H32_T1000"), "split"),
-    (lambda: inputs.make_custom(7704, [300], 48, 48, io="bf16", name="auto_H48_T300"), "one_launch"),
+    (lambda: inputs.make_custom(7704, [300], 80, 80, io="bf16", name="auto_H80_T300"), "one_launch"),
     (lambda: inputs.make_custom(7702, [100, 0, 700, 65], 2, 16, io="bf16", init_std=0.2, name="auto_packed"),
      "split"),
     (lambda: inputs.make_workload(0), "one_launch"),
