@@ -172,3 +172,33 @@ def test_bf16_values_near_the_fp16_range(entry):
     assert torch.isfinite(o.float()).all() and torch.isfinite(fs).all()
     check("o", to_f64(o), ro, x.io)
     check("final_state", to_f64(fs), rf, x.io)
+
+
+# ---- HIP graph capture ---------------------------------------------------------------
+
+@pytest.mark.parametrize("wid,path", [(1, "split"), (4, "seg")])
+def test_graph_replays_match_eager(wid, path):
+    # a gdn_prefill_auto call captured in a HIP graph, replayed three times with eager calls
+    # on other inputs between the replays; every replay gives the eager call's bits
+    x = inputs.make_workload(1) if wid == 1 else inputs.head_shard(inputs.make_workload(4), 8)
+    io = gdn.GDN_BF16
+    plan = gdn.prefill_auto_plan(x.N, x.T_tot, x.Hv, io)
+    assert plan["path"] == path
+    d = to_device(x, DEV)
+    ws = torch.empty(plan["workspace_bytes"], dtype=torch.uint8, device=DEV)
+    o_ref, f_ref = gdn.prefill_auto(*_args(d), workspace=ws)
+    torch.cuda.synchronize()
+    out = torch.empty_like(o_ref)
+    fs = torch.empty_like(f_ref)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        gdn.prefill_auto(*_args(d), out=out, final_state=fs, workspace=ws)
+    y = inputs.make_custom(7950, [300, 77], 1, x.Hv, io="bf16", init_std=0.1)
+    dy = to_device(y, DEV)
+    for rep in range(3):
+        out.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, o_ref) and torch.equal(fs, f_ref), f"replay {rep}"
+        gdn.prefill_auto(*_args(dy))   # eager work between the replays, sharing the workspace's device
+        torch.cuda.synchronize()
