@@ -131,9 +131,10 @@ def choose_path(x, path: str, prologue: bool, segments: int = 1) -> str:
     (gdn_prefill_seg) for this workload: the rule gdn_prefill_auto_plan applies on a
     256-CU device (the timed run asks the library itself; this copy names the kernels
     of a counter summary on a host without the GPU).  A two-launch path for 16-bit I/O
-    when its chain's N * Hv * 8 workgroups fit the 256 CUs in one round, or for a packed
-    batch of several sequences; among them the segmented one when gdn_prefill_seg_choose
-    gave more than one segment (not with the prologue)."""
+    when its chain's N * Hv * 4 workgroups (two 16-channel slices each) fit the 256 CUs
+    in one round, or for a packed batch of several sequences; among them the segmented
+    one when gdn_prefill_seg_choose gave three segments or more (not with the
+    prologue)."""
     if path != "auto":
         return path
     if x.io != "f32" and (x.N * x.Hv * chain_workgroups_per_head(64, True) <= 256 or x.N > 1):
