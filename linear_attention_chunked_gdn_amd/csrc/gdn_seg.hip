@@ -15,8 +15,8 @@
 //
 // gdn_seg_join_kernel: one 256-thread workgroup per (sequence, value head, 16 value
 // channels) walks the segments in order, S_in(s + 1) = S_in(s) X_s + S0_end(s) with one
-// fp32 MFMA product each, stores every S_in as fp16 (a.sin16) and the last one as the
-// final state.
+// fp32 MFMA product each (X_{s+1} and S0_end(s + 1) loaded while segment s is joined),
+// stores every S_in as fp16 (a.sin16) and the last one as the final state.
 // gdn_seg_fix_kernel: one 512-thread workgroup per (chunk slot, value head) of segments
 // >= 1 issues all its loads at once (E rows, S_in fragments, O0), stages the chunk's E
 // rows in LDS; wave w forms O = O0 + E S_in^T for value channels [16w, 16w + 16) (fp16
@@ -54,26 +54,41 @@ __global__ __launch_bounds__(THREADS) void gdn_seg_join_kernel(const KdaArgs a) 
         *reinterpret_cast<f16x4 *>(s16 + (size_t)(dv0 + r) * D + c) = y;
     }
     __syncthreads();
-    for (int s = 1; s < a.nseg; ++s) {
-        float *s0e = sb + (size_t)s * 2 * D * D;
+    // Segment s's operands, loaded one segment ahead: wave w's key columns
+    // [32w, 32w + 32) of X_s^T (B fragments; slot (g4, e) = row r = 32 kb + 8 g4 + e of X)
+    // and of S0_end(s) (rows dv0 + 4 g4 + i).
+    struct StepOps {
+        Frag<float> fb[2][4];
+        f32x4 s0[2];
+    };
+    auto load_step = [&](StepOps &op, int s) {
+        const float *s0e = sb + (size_t)s * 2 * D * D;
         const float *xt = s0e + D * D;
-        // wave w: key columns [32w, 32w + 32); lane: rows dv0 + 4 g4 + i, key column col
-        f32x4 acc[2];
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) {
             const int col = 32 * wave + 16 * ct + l16;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[ct][i] = s0e[(size_t)(dv0 + 4 * g4 + i) * D + col];
+            for (int kb = 0; kb < 4; ++kb) op.fb[ct][kb].load8(xt + (size_t)col * D + 32 * kb + 8 * g4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) op.s0[ct][i] = s0e[(size_t)(dv0 + 4 * g4 + i) * D + col];
+        }
+    };
+    auto step = [&](const StepOps &op, int s) {
+        // lane: rows dv0 + 4 g4 + i, key column 32 wave + 16 ct + l16; the sum over a row of
+        // X in two halves (two accumulators) for a shorter dependent chain
+        f32x4 acc[2][2];
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+            acc[ct][0] = op.s0[ct];
+            acc[ct][1] = zero4();
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) {
-                // slot (g4, e) = row r = 32 kb + 8 g4 + e of X: R[.][r] and X^T[col][r]
-                Frag<float> fa, fb;
+                Frag<float> fa;
                 fa.load8(&R[l16 * RS + 32 * kb + 8 * g4]);
-                fb.load8(xt + (size_t)col * D + 32 * kb + 8 * g4);
-                mma(acc[ct], fa, fb);
+                mma(acc[ct][kb & 1], fa, op.fb[ct][kb]);
             }
         }
-        __syncthreads();   // every wave has read R and its S0_end(s) elements
+        __syncthreads();   // every wave has read R
         // S_in(s + 1) as fp16 for the fix-up, or the final state after the last segment
         const bool last = s + 1 == a.nseg;
         float *fin = last && a.sN ? a.sN + ((size_t)n * a.Hv + h) * D * D : nullptr;
@@ -82,13 +97,23 @@ __global__ __launch_bounds__(THREADS) void gdn_seg_join_kernel(const KdaArgs a) 
             const int col = 32 * wave + 16 * ct + l16;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
+                const float y = acc[ct][0][i] + acc[ct][1][i];
                 const size_t at = (size_t)(dv0 + 4 * g4 + i) * D + col;
-                R[(4 * g4 + i) * RS + col] = acc[ct][i];
-                if (!last) s16[(size_t)s * D * D + at] = (_Float16)acc[ct][i];
-                if (fin) fin[at] = acc[ct][i];
+                R[(4 * g4 + i) * RS + col] = y;
+                if (!last) s16[(size_t)s * D * D + at] = (_Float16)y;
+                if (fin) fin[at] = y;
             }
         }
         __syncthreads();
+    };
+    StepOps op0, op1;
+    if (a.nseg > 1) load_step(op0, 1);
+    for (int s = 1; s < a.nseg; s += 2) {
+        if (s + 1 < a.nseg) load_step(op1, s + 1);
+        step(op0, s);
+        if (s + 1 >= a.nseg) break;
+        if (s + 2 < a.nseg) load_step(op0, s + 2);
+        step(op1, s + 1);
     }
     if (a.nseg == 1 && a.sN) {   // one segment: its end state is the final state
         float *dst = a.sN + ((size_t)n * a.Hv + h) * D * D;

@@ -15,37 +15,41 @@
 //   S <- S Diag(gl) + v^T Kl.
 //
 // Value channels are independent in all three (S's rows never mix), so one workgroup
-// owns 16 of them for one (sequence, value head) and needs nothing from the others.
+// owns 16 of them (or 32, as two slices) for one (sequence, value head) and needs nothing
+// from the others.
 //
-// The recurrence runs on two waves, one per half of the key channels, and never leaves
-// their registers.  Wave h holds rows 64 h .. 64 h + 63 of S^T (its key half x 16 value
-// channels) as four fp32 16x16 accumulators; read in pairs, an accumulator's rows are the
-// eight reduction slots of an MFMA operand (the slot order pi of the tile layout), so
-// fp16 copies of S^T are B operands as they stand.  Per chunk, wave h forms the partial
-// p_h = [U] + WN[:, half h] S^T[half h] (U on wave 0 only), both waves exchange their
-// partials as fp16 through LDS, and each forms v = p_0 + p_1 (the same fp16 values on
-// every wave) and updates its half, S^T[half h] <- gl S^T[half h] + Kl[half h]^T v, with
-// v's token tiles as the B operands.  A wave's operands per chunk (its halves of WN and
-// Kl, gl, U: 17 KB at C = 64) come straight from L2 into registers with buffer loads, one
-// chunk ahead: a wave receives LDS reads at ~22 B per clock, a third of the rate at
-// which it issues 16-byte global loads, so the operands do not pass through LDS.  (Each
-// of a head's 8 workgroups reads the same tiles; they share one XCD and so one L2.)
+// Eight waves share a workgroup, one barrier per chunk:
 //
-// Two output waves form O^T = S Qg^T + v^T P^T, half of the token tiles each, from the
-// fp16 state halves and the two partials the recurrence waves leave in one of two LDS
-// exchange slots per chunk, their Qg and P fragments loaded a chunk ahead.  O^T puts
-// four consecutive value channels of one token in a lane: one 8-byte store.
+// * Waves 0, 1, the recurrence, one per half of the key channels.  Wave h holds rows
+//   64 h .. 64 h + 63 of S^T (its key half x 16 value channels, per slice) as four fp32
+//   16x16 accumulators that never leave its registers; read in pairs, an accumulator's
+//   rows are the eight reduction slots of an MFMA operand (the slot order pi of the tile
+//   layout), so fp16 copies of S^T are B operands as they stand.  Per chunk, wave h reads
+//   its halves of WN and Kl from the LDS ring, forms the partial
+//   p_h = WN[:, half h] S^T[half h], plus U on its half of the token tiles, and writes it
+//   and its fp16 copy of S^T into exchange slot c % 2; after the barrier it reads the
+//   other wave's partial, forms v = p_0 + p_1 in fp16 (addition commutes exactly, so
+//   every wave that forms v gets the same values) and updates its half,
+//   S^T[half h] <- gl S^T[half h] + Kl[half h]^T v, with v's token tiles as B operands.
+//   U and gl come from L2 into registers one chunk ahead.
+// * Waves 2 .. 5, the outputs, one 16-token tile each (two at C = 128).  After barrier c a
+//   wave reads slot c % 2 (S^T and both partials) and forms O^T = S Qg^T + v^T P^T, its
+//   Qg and P fragments loaded from L2 into registers a chunk ahead.  O^T puts four
+//   consecutive value channels of one token in a lane: one 8-byte store.
+// * Waves 6, 7, the loaders, stream WN and Kl into an NB-buffer LDS ring with direct
+//   global-to-LDS loads, chunk c + NB into buffer c % NB after barrier c.
 //
-// One barrier per chunk orders everything.  Before barrier c the recurrence waves write
-// S^T(c) and their partials of chunk c into slot c % 2; after it each reads the other's
-// partial, and the output waves read the slot, before barrier c + 1, after which slot
-// c % 2 is written again (chunk c + 2).
+// Each of a head's workgroups reads the same tiles; they run on one XCD and so share one
+// L2, from which a workgroup moves about 56 KB per chunk at C = 64.  With two slices per
+// workgroup every WN, Kl, Qg and P fragment serves both: about the same bytes per chunk
+// for twice the value channels, and twice the recurrence and output work.
 //
-// Measured and not kept (H16 T4096): one recurrence wave fed from an LDS ring by loader
-// waves (47 us: the wave's LDS reads of 34.5 KB per chunk set the period); the same with
-// three ring buffers, with LDS progress counters instead of barriers, or with loaders
-// and output waves split by chunk parity; a two-wave split with loader waves and two
-// barriers per chunk (65 us: every role waited for the slowest at each barrier).
+// Measured and not kept (chain kernel at H16 T4096, against 44 us): one recurrence wave
+// fed from the ring (47 us: its LDS reads of 34.5 KB per chunk set the period); the two
+// recurrence waves loading their own WN and Kl from L2 (47.8 us); two barriers per chunk
+// (65 us); Qg and P through a second LDS ring filled by two more loader waves (48-54 us);
+// Qg replaced by the raw q rows, the decay applied by the output waves (62.8 us: a load
+// instruction then touches 16 rows).
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
@@ -137,7 +141,9 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 // Chunk c's WN (KL false) or Kl fragments into ring buffer c % NB, one 1 KB fragment per
 // instruction, global to LDS directly (lane l's 16 bytes land at 16 l: the fragment
-// layout of the tile is kept).
+// layout of the tile is kept).  The workgroups reading one tile start at different
+// fragments (slice s at fragment 2 s), so that they do not all ask the L2 for the same
+// lines at once.
 template <int C, int SPW, bool KL>
 __device__ __forceinline__ void dma_chunk(Smem<C, SPW> &sm, const Work &wk, int c, int lane) {
     using F = Cfg<C, SPW>;
@@ -147,9 +153,12 @@ __device__ __forceinline__ void dma_chunk(Smem<C, SPW> &sm, const Work &wk, int 
     f16x8 *dst = KL ? ob.kl : ob.w;
     constexpr int NF = KL ? F::NK : F::NW;
     constexpr int SRC = KL ? TL::KL : TL::WN;
+    const int rot = __builtin_amdgcn_readfirstlane((2 * wk.slice) % NF);
 #pragma unroll
-    for (int f = 0; f < NF; ++f)
+    for (int f0 = 0; f0 < NF; ++f0) {
+        const int f = f0 + rot < NF ? f0 + rot : f0 + rot - NF;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(dst + 64 * f), 16, 16 * lane, SRC + 1024 * f, 0, 0);
+    }
 }
 
 // A loader wave's run.  Chunk c's operands are read by the recurrence waves between
