@@ -176,29 +176,47 @@ def test_bf16_values_near_the_fp16_range(entry):
 
 # ---- HIP graph capture ---------------------------------------------------------------
 
-@pytest.mark.parametrize("wid,path", [(1, "split"), (4, "seg")])
-def test_graph_replays_match_eager(wid, path):
-    # a gdn_prefill_auto call captured in a HIP graph, replayed three times with eager calls
-    # on other inputs between the replays; every replay gives the eager call's bits
-    x = inputs.make_workload(1) if wid == 1 else inputs.head_shard(inputs.make_workload(4), 8)
-    io = gdn.GDN_BF16
-    plan = gdn.prefill_auto_plan(x.N, x.T_tot, x.Hv, io)
-    assert plan["path"] == path
+GRAPH_CASES = [
+    # (inputs, entry point, expected gdn_prefill_auto path or None): the headline shape
+    # (split), one GPU's share of the long workload (segmented), 80 heads (the one-launch
+    # kernel, no workspace), and the per-key-channel prefill
+    (lambda: inputs.make_workload(1), "auto", "split"),
+    (lambda: inputs.head_shard(inputs.make_workload(4), 8), "auto", "seg"),
+    (lambda: inputs.make_custom(7951, [300], 80, 80, io="bf16", init_std=0.1), "auto", "one_launch"),
+    (lambda: inputs.make_custom(7952, [1000, 333], 8, 16, io="bf16", init_std=0.1, per_channel=True), "kda", None),
+]
+
+
+@pytest.mark.parametrize("case", range(len(GRAPH_CASES)))
+def test_graph_replays_match_eager(case):
+    # a prefill call captured in a HIP graph, replayed three times with eager calls on
+    # other inputs between the replays; every replay gives the eager call's bits
+    make, entry, path = GRAPH_CASES[case]
+    x = make()
     d = to_device(x, DEV)
-    ws = torch.empty(plan["workspace_bytes"], dtype=torch.uint8, device=DEV)
-    o_ref, f_ref = gdn.prefill_auto(*_args(d), workspace=ws)
+    if entry == "auto":
+        plan = gdn.prefill_auto_plan(x.N, x.T_tot, x.Hv, gdn.GDN_BF16)
+        assert plan["path"] == path
+        nbytes = plan["workspace_bytes"]
+        call = gdn.prefill_auto
+        y = inputs.make_custom(7950, [300, 77], 1, x.Hv, io="bf16", init_std=0.1)
+    else:
+        nbytes = gdn.kda_workspace_size(x.N, x.T_tot, x.Hv)
+        call = gdn.kda_prefill
+        y = inputs.make_custom(7953, [300, 77], 1, x.Hv, io="bf16", init_std=0.1, per_channel=True)
+    ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=DEV)
+    o_ref, f_ref = call(*_args(d), workspace=ws)
     torch.cuda.synchronize()
     out = torch.empty_like(o_ref)
     fs = torch.empty_like(f_ref)
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
-        gdn.prefill_auto(*_args(d), out=out, final_state=fs, workspace=ws)
-    y = inputs.make_custom(7950, [300, 77], 1, x.Hv, io="bf16", init_std=0.1)
+        call(*_args(d), out=out, final_state=fs, workspace=ws)
     dy = to_device(y, DEV)
     for rep in range(3):
         out.fill_(float("nan"))
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(out, o_ref) and torch.equal(fs, f_ref), f"replay {rep}"
-        gdn.prefill_auto(*_args(dy))   # eager work between the replays, sharing the workspace's device
+        call(*_args(dy))   # eager work between the replays, sharing the workspace's device
         torch.cuda.synchronize()
