@@ -1,19 +1,23 @@
 """Throughput of the chunked gated delta-rule prefill on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload I] [--io bf16|f16|f32]
-                    [--path auto|pipe|split] [--chunk 32|64|128] [--kda] [--prologue]
-                    [--no-cpu-baseline]
+                    [--path auto|pipe|split|seg] [--chunk 32|64|128] [--segments K]
+                    [--head-shard G] [--kda] [--prologue] [--eager] [--no-cpu-baseline]
 
 A step is one prefill call over the whole workload (all heads, all chunks) with inputs
-resident in HBM: gdn_prefill (one launch), or gdn_prefill_split (a chunk-parallel map
-kernel, then the chain kernel, over a workspace allocated once outside the timed
-region).  --path auto (the default) takes the split path when the one-launch kernel's
-workgroups -- sequences x value heads x 8 value-channel slices, one per CU -- would
-occupy at most half of the 256 CUs (the headline shape), else gdn_prefill.  --chunk sets
-the split path's chunk length (64 by default; the one-launch and KDA paths run 64).  The default workload is the headline one: one sequence of
-T=4096 tokens, 16 heads, d=128, bf16 q/k/v/o, fp32 g/beta/state, chunk 64.  Input
-sets are rotated across steps (more bytes than the 256 MB Infinity Cache) so that
-every step streams from HBM.  Prints ONE JSON line.
+resident in HBM.  --path auto (the default) calls gdn_prefill_auto, the library's own
+choice among the one-launch kernel (gdn_prefill), the two-launch path (gdn_prefill_split:
+a chunk-parallel map kernel, then the chain kernel) and the segmented one
+(gdn_prefill_seg); --path pipe|split|seg calls that entry point instead.  Workspaces are
+allocated once outside the timed region.  --chunk sets the two-launch paths' chunk length
+(64 by default; the one-launch and KDA paths run 64).  The default workload is the
+headline one: one sequence of T=4096 tokens, 16 heads, d=128, bf16 q/k/v/o, fp32
+g/beta/state, chunk 64.  Input sets are rotated across steps (more bytes than the 256 MB
+Infinity Cache) so that every step streams from HBM.  The W warm-up and K timed steps
+run as launches from Python (HIP events between them give the eager mean, median and
+minimum); the K steps are then captured in one HIP graph and replayed, and that replay
+is what ms_per_step and value time (--eager: the eager loop instead).  Prints ONE JSON
+line.
 
 roofline.achieved = algorithmic bytes of one launch / mean launch time, where the
 mean launch time comes from HIP events recorded on the launch stream around the
@@ -40,8 +44,9 @@ cpu_baseline: the fp64 CPU oracle (test infrastructure, untuned) timed on the ho
 cores over the same workload.
 
 --prologue: the same workload's draws before the input prologue (q, k unnormalised,
-beta and g logits), run through gdn_prefill_fused with all three prologue steps; the
-oracle applies the same steps for the parity block.
+beta and g logits), run with all three prologue steps applied in the kernels
+(gdn_prefill_auto with the prologue flags); the oracle applies the same steps for the
+parity block.
 
 --kda: the same workload with one decay per key channel (gdn_kda_prefill: a
 chunk-parallel map kernel, then the chain kernel, over a workspace allocated once
@@ -382,7 +387,9 @@ def main() -> int:
     ap.add_argument("--kda", action="store_true",
                     help="one decay per key channel (gdn_kda_prefill) on the same workload")
     ap.add_argument("--prologue", action="store_true",
-                    help="raw inputs through gdn_prefill_fused with the q/k norm, sigmoid and softplus steps")
+                    help="raw inputs, the q/k norm, sigmoid and softplus steps applied in the kernels "
+                         "(gdn_prefill_auto with all prologue flags; with --path, gdn_prefill_fused or "
+                         "gdn_prefill_split_fused)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true",
                     help="time the K steps as launches from Python instead of one HIP graph of the K steps")
