@@ -56,6 +56,7 @@ SMALL = [
     ([200], 2, 4, 0.1),
     ([0, 130, 1, 64, 77], 1, 2, 0.1),
     ([129, 0], 2, 2, 0.1),
+    ([300, 45], 1, 8, 0.1),
 ]
 
 

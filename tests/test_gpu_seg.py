@@ -52,6 +52,7 @@ SMALL = [
     ([0, 130, 1, 64, 77], 1, 2, 0.1),
     ([129, 0], 2, 2, 0.1),
     ([700], 1, 2, 0.2),
+    ([300, 45], 1, 8, 0.1),
 ]
 
 
