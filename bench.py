@@ -85,8 +85,7 @@ IO_CODE = {"f32": 0, "bf16": 1, "f16": 2}   # gdn_dtype
 KERNEL_SOURCES = {
     "gdn_prefill_pipe_kernel": ["gdn_prefill_pipe.hip", "gdn_device.h", "gdn_launch.h"],
     "gdn_prefill_kernel": ["gdn_prefill.hip", "gdn_device.h", "gdn_launch.h"],
-    "gdn_prefill_pipe_kernel(prologue)": ["gdn_prefill_pipe.hip", "gdn_prefill_pipe_prologue.hip",
-                                          "gdn_device.h", "gdn_launch.h"],
+    "gdn_prefill_pipe_kernel(prologue)": ["gdn_prefill_pipe.hip", "gdn_device.h", "gdn_launch.h"],
     "kda_map_kernel+kda_chain_kernel": ["kda_map.hip", "kda_chain.hip", "gdn_wy.h", "gdn_device.h",
                                         "gdn_launch.h"],
     "gdn_map_kernel+kda_chain_kernel": ["gdn_map.hip", "kda_chain.hip", "gdn_wy.h", "gdn_device.h",

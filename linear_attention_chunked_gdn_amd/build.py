@@ -22,8 +22,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libgdn_mi355x.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 SOURCES = ["gdn_api.cpp", "gdn_prefill.hip", "gdn_prefill_pipe.hip", "gdn_decode.hip",
-           "kda_map.hip", "kda_chain.hip", "gdn_prefill_pipe_prologue.hip", "gdn_map.hip",
-           "gdn_seg.hip"]
+           "kda_map.hip", "kda_chain.hip", "gdn_map.hip", "gdn_seg.hip"]
 ARCH = "gfx950"
 
 

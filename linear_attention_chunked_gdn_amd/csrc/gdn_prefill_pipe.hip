@@ -41,8 +41,8 @@
 // the blocks of A(c) below it, read in the same phase, are disjoint).
 // One workgroup = 8 wave64s = one (sequence, value head, 16 value channels).
 //
-// Fused input prologue (compiled when GDN_PIPE_PROLOGUE is 1, by
-// gdn_prefill_pipe_prologue.hip, as a kernel of its own): q and k arrive unnormalised and
+// Fused input prologue (the kernel's PRO template parameter; each setting is a kernel of
+// its own, with its own registers and LDS layout): q and k arrive unnormalised and
 // beta, g as their logits.  The gate scan applies beta = sigmoid(x) and g = -softplus(x).
 // The L2 norms of the q and k rows are reduced in fp32 while the rows are staged (the
 // 16 lanes that commit a row), and 1 / ||row|| is kept per token; q and k stay exact
@@ -54,18 +54,8 @@
 
 #include <type_traits>
 
-#ifndef GDN_PIPE_PROLOGUE
-#define GDN_PIPE_PROLOGUE 0
-#endif
-
 namespace gdn {
-#if GDN_PIPE_PROLOGUE
-namespace pipe_pro {
-#else
 namespace pipe {
-#endif
-
-constexpr bool PRO = GDN_PIPE_PROLOGUE != 0;
 
 constexpr int CH = 64;        // chunk length
 constexpr int DK = 128;
@@ -92,6 +82,7 @@ typedef _Float16 hf;
 // 16-token blocks (r in block i > block of s) they are formed as u_r * w[i-1]_s with
 // u_r = exp(Gamma_r - Gamma_16i') (i' the block of r) and w[i-1]_s = exp(Gamma_16i -
 // Gamma_s): both exponents are <= 0 when g <= 0, so neither factor can overflow.
+template <bool PRO>
 struct Gate {
     float beta[CH];   // beta (0 past the chunk's end)
     float gam[CH];    // gamma_t = exp(Gamma_t)
@@ -99,12 +90,10 @@ struct Gate {
     float g2[CH];     // Gamma_t * log2(e)
     float u[CH];      // exp(Gamma_t - Gamma at the first token of t's 16-token block)
     float w[3][CH];   // w[i-1][s] = exp(Gamma_16i - Gamma_s) for s < 16i, else 0
-#if GDN_PIPE_PROLOGUE
-    float rn[2][CH];  // 1 / ||k_t|| and 1 / ||q_t|| (input prologue)
-#endif
+    float rn[PRO ? 2 : 0][CH];  // 1 / ||k_t|| and 1 / ||q_t|| (input prologue only)
 };
 
-template <typename IO>
+template <typename IO, bool PRO>
 struct __align__(16) Smem {
     // The small tiles come first: a DS instruction's immediate offset reaches 64 KiB,
     // so these are addressed from one base register plus constants.
@@ -114,7 +103,7 @@ struct __align__(16) Smem {
     hf Rh[DVS * TS];               // R^T
     hf Vh[DVS * TS];               // v^T
     IO Wh[DVS * TS], Wl[DVS * TS];  // (diag(lambda) v)^T (hi + lo for bf16 I/O)
-    Gate gate[NBUF];
+    Gate<PRO> gate[NBUF];
     IO V[NBUF][CH * VS];
     IO K[NBUF][CH * KS];
     IO Q[CH * KS];
@@ -274,46 +263,46 @@ __device__ __forceinline__ int prefetch_tok(const Work &wk, int c, int nchunks) 
     return wk.bos + min(c, nchunks - 1) * CH;
 }
 
-template <typename IO>
-__device__ __forceinline__ void stage_commit(const Stage &st, Smem<IO> &s, int buf, int tid, unsigned pro) {
+template <typename IO, bool PRO>
+__device__ __forceinline__ void stage_commit(const Stage &st, Smem<IO, PRO> &s, int buf, int tid, unsigned pro) {
     const int seg = tid & 15;
     *reinterpret_cast<u32x4 *>(&s.K[buf][(tid >> 4) * KS + seg * 8]) = st.k0;
     *reinterpret_cast<u32x4 *>(&s.K[buf][((tid + THREADS) >> 4) * KS + seg * 8]) = st.k1;
     *reinterpret_cast<unsigned *>(&s.V[buf][(tid >> 3) * VS + (tid & 7) * 2]) = st.v;
-#if GDN_PIPE_PROLOGUE
-    const bool norm = pro & GDN_PROLOGUE_QK_L2NORM;
-    const float r0 = norm ? row_rnorm<IO>(st.k0) : 1.f, r1 = norm ? row_rnorm<IO>(st.k1) : 1.f;
-    if (seg == 0) {
-        s.gate[buf].rn[0][tid >> 4] = r0;
-        s.gate[buf].rn[0][(tid + THREADS) >> 4] = r1;
+    if constexpr (PRO) {
+        const bool norm = pro & GDN_PROLOGUE_QK_L2NORM;
+        const float r0 = norm ? row_rnorm<IO>(st.k0) : 1.f, r1 = norm ? row_rnorm<IO>(st.k1) : 1.f;
+        if (seg == 0) {
+            s.gate[buf].rn[0][tid >> 4] = r0;
+            s.gate[buf].rn[0][(tid + THREADS) >> 4] = r1;
+        }
+    } else {
+        (void)pro;
     }
-#else
-    (void)pro;
-#endif
 }
 
-template <typename IO>
-__device__ __forceinline__ void stage_commit_q(const StageQ &st, Smem<IO> &s, int buf, int tid, unsigned pro) {
+template <typename IO, bool PRO>
+__device__ __forceinline__ void stage_commit_q(const StageQ &st, Smem<IO, PRO> &s, int buf, int tid, unsigned pro) {
     const int seg = tid & 15;
     *reinterpret_cast<u32x4 *>(&s.Q[(tid >> 4) * KS + seg * 8]) = st.q0;
     *reinterpret_cast<u32x4 *>(&s.Q[((tid + THREADS) >> 4) * KS + seg * 8]) = st.q1;
-#if GDN_PIPE_PROLOGUE
-    const bool norm = pro & GDN_PROLOGUE_QK_L2NORM;
-    const float r0 = norm ? row_rnorm<IO>(st.q0) : 1.f, r1 = norm ? row_rnorm<IO>(st.q1) : 1.f;
-    if (seg == 0) {
-        s.gate[buf].rn[1][tid >> 4] = r0;
-        s.gate[buf].rn[1][(tid + THREADS) >> 4] = r1;
+    if constexpr (PRO) {
+        const bool norm = pro & GDN_PROLOGUE_QK_L2NORM;
+        const float r0 = norm ? row_rnorm<IO>(st.q0) : 1.f, r1 = norm ? row_rnorm<IO>(st.q1) : 1.f;
+        if (seg == 0) {
+            s.gate[buf].rn[1][tid >> 4] = r0;
+            s.gate[buf].rn[1][(tid + THREADS) >> 4] = r1;
+        }
+    } else {
+        (void)buf;
+        (void)pro;
     }
-#else
-    (void)buf;
-    (void)pro;
-#endif
 }
 
 // #1 Gate for the chunk staged in buffer buf, by map wave 3 (lane = token): the
 // inclusive scan of g and every decay factor the grams and the chain need.
-template <typename IO>
-__device__ __forceinline__ void gate_scan(const Stage &st, Smem<IO> &s, int buf, int lane, unsigned pro) {
+template <typename IO, bool PRO>
+__device__ __forceinline__ void gate_scan(const Stage &st, Smem<IO, PRO> &s, int buf, int lane, unsigned pro) {
     const bool valid = lane < st.nval;
     float g = st.g, beta = st.b;
     if constexpr (PRO) {
@@ -331,7 +320,7 @@ __device__ __forceinline__ void gate_scan(const Stage &st, Smem<IO> &s, int buf,
     const float b0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x2), 0));
     const int blk = lane >> 4;
     const float start = blk == 0 ? b0 : blk == 1 ? b16 : blk == 2 ? b32 : b48;
-    Gate &gt = s.gate[buf];
+    Gate<PRO> &gt = s.gate[buf];
     gt.beta[lane] = valid ? beta : 0.f;
     gt.g2[lane] = x2;
     gt.gam[lane] = __builtin_amdgcn_exp2f(x2);
@@ -353,9 +342,9 @@ __device__ __forceinline__ void gate_scan(const Stage &st, Smem<IO> &s, int buf,
 // Per-element factor of tile (bi, bj) for this lane's row and four columns: the decay,
 // times beta of the row for K K^T.  Computed before the tile's products so the gate
 // reads overlap the MFMAs.
-template <bool ISQ, typename IO>
-__device__ __forceinline__ f32x4 gram_scale(const Smem<IO> &s, int nb, int bi, int bj, int l16, int g4) {
-    const Gate &gt = s.gate[nb];
+template <bool ISQ, typename IO, bool PRO>
+__device__ __forceinline__ f32x4 gram_scale(const Smem<IO, PRO> &s, int nb, int bi, int bj, int l16, int g4) {
+    const Gate<PRO> &gt = s.gate[nb];
     const int rr = 16 * bi + l16;          // row of this lane
     const int c0 = 16 * bj + 4 * g4;       // first of its four columns
     f32x4 d;
@@ -379,20 +368,18 @@ __device__ __forceinline__ f32x4 gram_scale(const Smem<IO> &s, int nb, int bi, i
 #pragma unroll
         for (int r = 0; r < 4; ++r) d[r] *= br;
     }
-#if GDN_PIPE_PROLOGUE
-    {
+    if constexpr (PRO) {
         const float rrow = s.gate[nb].rn[ISQ ? 1 : 0][rr];
         const f32x4 rcol = *reinterpret_cast<const f32x4 *>(&s.gate[nb].rn[0][c0]);
 #pragma unroll
         for (int r = 0; r < 4; ++r) d[r] *= rrow * rcol[r];
     }
-#endif
     return d;
 }
 
 // A goes to s.A (fp32), P to s.Ph[nb] (fp16).
-template <bool ISQ, typename IO>
-__device__ __forceinline__ void gram_store(Smem<IO> &s, int nb, int bi, int bj, const f32x4 &acc, const f32x4 &d,
+template <bool ISQ, typename IO, bool PRO>
+__device__ __forceinline__ void gram_store(Smem<IO, PRO> &s, int nb, int bi, int bj, const f32x4 &acc, const f32x4 &d,
                                           int l16, int g4) {
     const int rr = 16 * bi + l16;
     const int c0 = 16 * bj + 4 * g4;
@@ -406,8 +393,8 @@ __device__ __forceinline__ void gram_store(Smem<IO> &s, int nb, int bi, int bj, 
 
 // Up to four tiles of one gram, each given as 4 * (row block) + (column block), -1 for
 // none.  Operand fragments shared by several tiles are read once per step.
-template <bool ISQ, int T0, int T1, int T2, int T3, typename IO>
-__device__ __forceinline__ void gram_tiles(Smem<IO> &s, int nb, int l16, int g4) {
+template <bool ISQ, int T0, int T1, int T2, int T3, typename IO, bool PRO>
+__device__ __forceinline__ void gram_tiles(Smem<IO, PRO> &s, int nb, int l16, int g4) {
     constexpr int tl[4] = {T0, T1, T2, T3};
     constexpr int NT = (T0 >= 0) + (T1 >= 0) + (T2 >= 0) + (T3 >= 0);
     f32x4 c[NT], d[NT];
@@ -433,8 +420,8 @@ __device__ __forceinline__ void gram_tiles(Smem<IO> &s, int nb, int l16, int g4)
 }
 
 // K K^T of the chunk in buffer nb, all ten tiles over the four map waves (first chunk).
-template <typename IO>
-__device__ __forceinline__ void map_gram_kk(Smem<IO> &s, int nb, int m, int l16, int g4) {
+template <typename IO, bool PRO>
+__device__ __forceinline__ void map_gram_kk(Smem<IO, PRO> &s, int nb, int m, int l16, int g4) {
     switch (m) {
         case 0: gram_tiles<false, 12, 13, -1, -1>(s, nb, l16, g4); break;   // (3,0) (3,1)
         case 1: gram_tiles<false, 14, 15, 0, -1>(s, nb, l16, g4); break;    // (3,2) (3,3) (0,0)
@@ -445,8 +432,8 @@ __device__ __forceinline__ void map_gram_kk(Smem<IO> &s, int nb, int m, int l16,
 
 // K K^T tiles below the diagonal, over map waves 0-2 (the diagonal tiles are computed
 // one phase earlier by wave 3, which then solves the diagonal blocks of T from them).
-template <typename IO>
-__device__ __forceinline__ void map_gram_kk_below(Smem<IO> &s, int nb, int m, int l16, int g4) {
+template <typename IO, bool PRO>
+__device__ __forceinline__ void map_gram_kk_below(Smem<IO, PRO> &s, int nb, int m, int l16, int g4) {
     switch (m) {
         case 0: gram_tiles<false, 12, 13, -1, -1>(s, nb, l16, g4); break;   // (3,0) (3,1)
         case 1: gram_tiles<false, 14, 8, -1, -1>(s, nb, l16, g4); break;    // (3,2) (2,0)
@@ -456,8 +443,8 @@ __device__ __forceinline__ void map_gram_kk_below(Smem<IO> &s, int nb, int m, in
 
 // Q K^T of the chunk in buffer nb (q in the single q buffer), ten tiles over three map
 // waves: m = 1..3 for the first chunk, m = 0..2 in the loop.
-template <typename IO>
-__device__ __forceinline__ void map_gram_qk(Smem<IO> &s, int nb, int m, int l16, int g4) {
+template <typename IO, bool PRO>
+__device__ __forceinline__ void map_gram_qk(Smem<IO, PRO> &s, int nb, int m, int l16, int g4) {
     switch (m) {
         case 0: gram_tiles<true, 12, 13, 14, 15>(s, nb, l16, g4); break;    // row block 3
         case 1: gram_tiles<true, 8, 9, 10, -1>(s, nb, l16, g4); break;      // row block 2
@@ -476,8 +463,8 @@ __device__ __forceinline__ void map_gram_qk(Smem<IO> &s, int nb, int m, int l16,
 // ---------------------------------------------------------------------------------
 // Rows 8+R0 .. 8+R1-1 of a diagonal block minus the lower-left 8x8 block times rows
 // 0-7 (the update between the two halves of the substitution).
-template <int R0, int R1, typename IO>
-__device__ __forceinline__ void diag_update_rows(const Smem<IO> &s, int g4, float (&x)[16]) {
+template <int R0, int R1, typename IO, bool PRO>
+__device__ __forceinline__ void diag_update_rows(const Smem<IO, PRO> &s, int g4, float (&x)[16]) {
     const float *bblk = &s.A[(16 * g4 + 8) * AS + 16 * g4];
     float b[8][8];
 #pragma unroll
@@ -497,8 +484,8 @@ __device__ __forceinline__ void diag_update_rows(const Smem<IO> &s, int g4, floa
 // rows of the update done in the first phase of the solve, the rest in the second
 constexpr int DIAG_SPLIT = 0;
 
-template <typename IO>
-__device__ __forceinline__ void diag_solve_first(const Smem<IO> &s, int l16, int g4, float (&x)[16]) {
+template <typename IO, bool PRO>
+__device__ __forceinline__ void diag_solve_first(const Smem<IO, PRO> &s, int l16, int g4, float (&x)[16]) {
     const float *ablk = &s.A[(16 * g4) * AS + 16 * g4];
 #pragma unroll
     for (int i = 0; i < 16; ++i) x[i] = (i == l16) ? 1.f : 0.f;
@@ -518,8 +505,8 @@ __device__ __forceinline__ void diag_solve_first(const Smem<IO> &s, int l16, int
     diag_update_rows<0, DIAG_SPLIT>(s, g4, x);
 }
 
-template <typename IO>
-__device__ __forceinline__ void diag_solve_second(Smem<IO> &s, int l16, int g4, float (&x)[16]) {
+template <typename IO, bool PRO>
+__device__ __forceinline__ void diag_solve_second(Smem<IO, PRO> &s, int l16, int g4, float (&x)[16]) {
     diag_update_rows<DIAG_SPLIT, 8>(s, g4, x);
     const float *ablk = &s.A[(16 * g4 + 8) * AS + 16 * g4 + 8];
     float a[8][8];
@@ -542,8 +529,8 @@ __device__ __forceinline__ void diag_solve_second(Smem<IO> &s, int l16, int g4, 
 // Map: blocks of column block CB below the diagonal, T_i,CB = -T_ii sum_j A_ij T_j,CB.
 // Results stay in registers (accumulator layout == B-operand layout) between steps.
 // ---------------------------------------------------------------------------------
-template <int CB, typename IO>
-__device__ __forceinline__ void map_merges(Smem<IO> &s, int l16, int g4) {
+template <int CB, typename IO, bool PRO>
+__device__ __forceinline__ void map_merges(Smem<IO, PRO> &s, int l16, int g4) {
     // every operand read from LDS up front, so the three dependent levels wait on one
     // round of loads instead of one per level
     f32x4 a[4][4];       // a[i][j]: A_ij, row 16i + l16, columns 16j + 4G..+3
@@ -593,8 +580,8 @@ __device__ __forceinline__ void map_merges(Smem<IO> &s, int l16, int g4) {
 // Chain, phase 1: R = beta V - beta gamma (K S^T) for tokens [16W, 16W+16).  The S
 // fragments are returned for Q S^T.
 // ---------------------------------------------------------------------------------
-template <typename IO>
-__device__ __forceinline__ void chain_R(Smem<IO> &s, int buf, int W, int l16, int g4, Frag<IO> (&fs)[4]) {
+template <typename IO, bool PRO>
+__device__ __forceinline__ void chain_R(Smem<IO, PRO> &s, int buf, int W, int l16, int g4, Frag<IO> (&fs)[4]) {
     const IO *krow = s.K[buf] + (16 * W + l16) * KS + 8 * g4;
     const IO *srow = s.S + l16 * KS + 8 * g4;
     // R = beta V - (beta gamma) (K S^T): the gate and V terms are read before the products
@@ -607,10 +594,7 @@ __device__ __forceinline__ void chain_R(Smem<IO> &s, int buf, int W, int l16, in
         bv[i] = b[i] * Cvt<IO>::to_f32(s.V[buf][(t0 + i) * VS + l16]);
         bg[i] = b[i] * gm[i];
     }
-#if GDN_PIPE_PROLOGUE
-    const f32x4 rk = *reinterpret_cast<const f32x4 *>(&s.gate[buf].rn[0][t0]);
-    bg *= rk;
-#endif
+    if constexpr (PRO) bg *= *reinterpret_cast<const f32x4 *>(&s.gate[buf].rn[0][t0]);
     f32x4 ks = zero4();
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
@@ -627,8 +611,8 @@ __device__ __forceinline__ void chain_R(Smem<IO> &s, int buf, int W, int l16, in
 
 // Chain, phase 1: (Q S^T)^T = S Q^T for tokens [16W, 16W+16) (lane = token, rows =
 // value channels), from the S fragments loaded by chain_R.
-template <typename IO>
-__device__ __forceinline__ f32x4 chain_QS(const Smem<IO> &s, int W, int l16, int g4, const Frag<IO> (&fs)[4]) {
+template <typename IO, bool PRO>
+__device__ __forceinline__ f32x4 chain_QS(const Smem<IO, PRO> &s, int W, int l16, int g4, const Frag<IO> (&fs)[4]) {
     const IO *qrow = s.Q + (16 * W + l16) * KS + 8 * g4;
     f32x4 qs = zero4();
 #pragma unroll
@@ -642,15 +626,11 @@ __device__ __forceinline__ f32x4 chain_QS(const Smem<IO> &s, int W, int l16, int
 
 // Chain, phase 2: v = T R for tokens [16W, 16W+16); T is lower triangular, so only
 // the first W/2 + 1 blocks of 32 columns contribute.
-template <typename IO>
-__device__ __forceinline__ void chain_v(Smem<IO> &s, int buf, int W, int l16, int g4) {
+template <typename IO, bool PRO>
+__device__ __forceinline__ void chain_v(Smem<IO, PRO> &s, int buf, int W, int l16, int g4) {
     const int t0 = 16 * W + 4 * g4;
-#if GDN_PIPE_PROLOGUE
-    const f32x4 lm = *reinterpret_cast<const f32x4 *>(&s.gate[buf].lam[t0]) *
-                     *reinterpret_cast<const f32x4 *>(&s.gate[buf].rn[0][t0]);
-#else
-    const f32x4 lm = *reinterpret_cast<const f32x4 *>(&s.gate[buf].lam[t0]);
-#endif
+    f32x4 lm = *reinterpret_cast<const f32x4 *>(&s.gate[buf].lam[t0]);
+    if constexpr (PRO) lm *= *reinterpret_cast<const f32x4 *>(&s.gate[buf].rn[0][t0]);
     f32x4 acc = zero4();
     const hf *trow = s.T + (16 * W + l16) * TS + 8 * g4;
     for (int kb = 0; kb <= (W >> 1); ++kb) {
@@ -671,16 +651,13 @@ __device__ __forceinline__ void chain_v(Smem<IO> &s, int buf, int W, int l16, in
 
 // Chain, phase 3: output rows of wave W, then the update of key channels
 // [32W, 32W+32) of the state slice.
-template <typename IO>
-__device__ __forceinline__ void chain_out_update(Smem<IO> &s, const PrefillArgs &a, int buf, int W, int l16,
+template <typename IO, bool PRO>
+__device__ __forceinline__ void chain_out_update(Smem<IO, PRO> &s, const PrefillArgs &a, int buf, int W, int l16,
                                                  int g4, const f32x4 &qs, f32x4 (&st)[2], int h,
                                                  int dv0, int tok0, int nval) {
     const int t = 16 * W + l16;
-#if GDN_PIPE_PROLOGUE
-    const float gm = s.gate[buf].gam[t] * s.gate[buf].rn[1][t];
-#else
-    const float gm = s.gate[buf].gam[t];
-#endif
+    float gm = s.gate[buf].gam[t];
+    if constexpr (PRO) gm *= s.gate[buf].rn[1][t];
     const float glast = s.gate[buf].gam[CH - 1];
     {
         // O^T = S Q^T diag(gamma) + v^T P^T: lane = token 16W + l16, rows = value
@@ -732,9 +709,9 @@ __device__ __forceinline__ void chain_out_update(Smem<IO> &s, const PrefillArgs 
     }
 }
 
-template <typename IO>
+template <typename IO, bool PRO>
 __global__ __launch_bounds__(THREADS) void gdn_prefill_pipe_kernel(const PrefillArgs a) {
-    __shared__ Smem<IO> s;
+    __shared__ Smem<IO, PRO> s;
     const int tid = threadIdx.x;
     const int lane = tid & 63, l16 = lane & 15, g4 = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -907,32 +884,28 @@ __global__ __launch_bounds__(THREADS) void gdn_prefill_pipe_kernel(const Prefill
     }
 }
 
-}  // namespace pipe / pipe_pro
+}  // namespace pipe
 
-#if GDN_PIPE_PROLOGUE
-hipError_t launch_prefill_pipe_prologue(const PrefillArgs &a, bool f16, int grid, hipStream_t stream) {
-    if (f16)
-        hipLaunchKernelGGL(pipe_pro::gdn_prefill_pipe_kernel<pipe_pro::hf>, dim3(grid), dim3(pipe_pro::THREADS), 0,
-                           stream, a);
-    else
-        hipLaunchKernelGGL(pipe_pro::gdn_prefill_pipe_kernel<pipe_pro::bf>, dim3(grid), dim3(pipe_pro::THREADS), 0,
-                           stream, a);
-    return hipGetLastError();
-}
-
-int prefill_pipe_prologue_lds_bytes() { return (int)sizeof(pipe_pro::Smem<pipe_pro::bf>); }
-#else
 hipError_t launch_prefill_pipe(const PrefillArgs &a, bool f16, int grid, hipStream_t stream) {
     if (f16)
-        hipLaunchKernelGGL(pipe::gdn_prefill_pipe_kernel<pipe::hf>, dim3(grid), dim3(pipe::THREADS), 0, stream, a);
+        hipLaunchKernelGGL((pipe::gdn_prefill_pipe_kernel<pipe::hf, false>), dim3(grid), dim3(pipe::THREADS), 0, stream, a);
     else
-        hipLaunchKernelGGL(pipe::gdn_prefill_pipe_kernel<pipe::bf>, dim3(grid), dim3(pipe::THREADS), 0, stream, a);
+        hipLaunchKernelGGL((pipe::gdn_prefill_pipe_kernel<pipe::bf, false>), dim3(grid), dim3(pipe::THREADS), 0, stream, a);
     return hipGetLastError();
 }
 
-int prefill_pipe_lds_bytes() { return (int)sizeof(pipe::Smem<pipe::bf>); }
+hipError_t launch_prefill_pipe_prologue(const PrefillArgs &a, bool f16, int grid, hipStream_t stream) {
+    if (f16)
+        hipLaunchKernelGGL((pipe::gdn_prefill_pipe_kernel<pipe::hf, true>), dim3(grid), dim3(pipe::THREADS), 0, stream, a);
+    else
+        hipLaunchKernelGGL((pipe::gdn_prefill_pipe_kernel<pipe::bf, true>), dim3(grid), dim3(pipe::THREADS), 0, stream, a);
+    return hipGetLastError();
+}
+
+int prefill_pipe_lds_bytes() { return (int)sizeof(pipe::Smem<pipe::bf, false>); }
+
+int prefill_pipe_prologue_lds_bytes() { return (int)sizeof(pipe::Smem<pipe::bf, true>); }
 
 int prefill_pipe_threads() { return pipe::THREADS; }
-#endif
 
 }  // namespace gdn
