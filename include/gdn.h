@@ -369,7 +369,6 @@ gdn_status gdn_prefill_plan(int32_t N, int32_t Hv, int32_t Dv, gdn_dtype io_dtyp
                             int32_t *dv_per_workgroup, int32_t *workgroups,
                             int32_t *lds_bytes, int32_t *threads_per_workgroup);
 
-/* Static English name of a status code. */
 /*
  * gdn_prefill_auto_plan / gdn_prefill_auto -- the prefill (with the input prologue when
  * `prologue` is nonzero) through whichever of this library's prefill paths is fastest
@@ -410,6 +409,7 @@ gdn_status gdn_prefill_auto(const void *q, const void *k, const void *v,
                             void *workspace, size_t workspace_bytes,
                             void *o, float *final_state, void *stream);
 
+/* Static English name of a status code. */
 const char *gdn_status_string(gdn_status s);
 
 /* Detail of the last non-OK return on the calling thread ("" if none). */
