@@ -136,6 +136,43 @@ def _need(t: torch.Tensor, name: str, dtype, shape, device):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _fits(t, dtype, shape, device) -> bool:
+    return (isinstance(t, torch.Tensor) and t.dtype == dtype and t.shape == shape and t.device == device
+            and t.is_contiguous())
+
+
+def _decode_call(lib, fn, name: str, q, k, v, g, g_shape, beta, state, out, extra=()):
+    """The decode steps' marshalling, kept short (a serving loop calls it once per token):
+    one combined check of every tensor (the detailed one only when it fails), raw
+    pointers as integers, and no device switch when q's device is already current."""
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError(f"gdn.{name} runs on the GPU only; q is on {dev}")
+    io = _io_code(q)
+    B, Hk, Dk = q.shape
+    Hv, Dv = v.shape[1], v.shape[2]
+    if out is None:
+        out = torch.empty((B, Hv, Dv), dtype=q.dtype, device=dev)
+    checks = ((k, "k", q.dtype, (B, Hk, Dk)), (v, "v", q.dtype, (B, Hv, Dv)),
+              (g, "g", torch.float32, g_shape(B, Hv, Dk)), (beta, "beta", torch.float32, (B, Hv)),
+              (state, "state", torch.float32, (B, Hv, Dv, Dk)), (out, "out", q.dtype, (B, Hv, Dv)))
+    if not (q.is_contiguous() and all(_fits(t, dt, sh, dev) for t, _, dt, sh in checks)):
+        if not q.is_contiguous():
+            raise ValueError("q must be contiguous")
+        for t, nm, dt, sh in checks:
+            _need(t, nm, dt, sh, dev)
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(), beta.data_ptr(), state.data_ptr(),
+            B, Hk, Hv, Dk, Dv, io) + tuple(extra)
+    if dev.index == torch.cuda.current_device():
+        st = fn(*args, out.data_ptr(), torch.cuda.current_stream(dev).cuda_stream)
+    else:
+        with torch.cuda.device(dev):
+            st = fn(*args, out.data_ptr(), torch.cuda.current_stream(dev).cuda_stream)
+    if st != 0:
+        _check(lib, st, name)
+    return out
+
+
 def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
             beta: torch.Tensor, initial_state: Optional[torch.Tensor] = None,
             cu_seqlens: Optional[torch.Tensor] = None, chunk_size: int = CHUNK,
@@ -193,30 +230,11 @@ def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tens
     q, k: [B, Hk, 128]; v: [B, Hv, 128]; g, beta: [B, Hv].  Returns o [B, Hv, 128].
     A nonzero ``prologue`` calls gdn_decode_step_fused."""
     lib = lib or load_library()
-    dev = q.device
-    if dev.type != "cuda":
-        raise ValueError("gdn.decode_step runs on the GPU only; q is on " + str(dev))
-    io = _io_code(q)
-    B, Hk, Dk = q.shape
-    Hv, Dv = v.shape[1], v.shape[2]
-    _need(k, "k", q.dtype, (B, Hk, Dk), dev)
-    _need(v, "v", q.dtype, (B, Hv, Dv), dev)
-    _need(g, "g", torch.float32, (B, Hv), dev)
-    _need(beta, "beta", torch.float32, (B, Hv), dev)
-    _need(state, "state", torch.float32, (B, Hv, Dv, Dk), dev)
-    if out is None:
-        out = torch.empty((B, Hv, Dv), dtype=q.dtype, device=dev)
-    _need(out, "out", q.dtype, (B, Hv, Dv), dev)
-    with torch.cuda.device(dev):
-        stream = torch.cuda.current_stream(dev).cuda_stream
-        if prologue:
-            st = lib.gdn_decode_step_fused(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state),
-                                           B, Hk, Hv, Dk, Dv, io, prologue, _ptr(out), ctypes.c_void_p(stream))
-        else:
-            st = lib.gdn_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state),
-                                     B, Hk, Hv, Dk, Dv, io, _ptr(out), ctypes.c_void_p(stream))
-    _check(lib, st, "gdn_decode_step_fused" if prologue else "gdn_decode_step")
-    return out
+    if prologue:
+        return _decode_call(lib, lib.gdn_decode_step_fused, "gdn_decode_step_fused", q, k, v, g,
+                            lambda B, Hv, Dk: (B, Hv), beta, state, out, extra=(int(prologue),))
+    return _decode_call(lib, lib.gdn_decode_step, "gdn_decode_step", q, k, v, g, lambda B, Hv, Dk: (B, Hv),
+                        beta, state, out)
 
 
 def kda_workspace_size(N: int, T: int, Hv: int, chunk_size: int = CHUNK, lib=None) -> int:
@@ -425,26 +443,8 @@ def kda_decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.
     """One token per sequence with one decay per key channel: as ``decode_step`` except
     g: [B, Hv, 128] fp32."""
     lib = lib or load_library()
-    dev = q.device
-    if dev.type != "cuda":
-        raise ValueError("gdn.kda_decode_step runs on the GPU only; q is on " + str(dev))
-    io = _io_code(q)
-    B, Hk, Dk = q.shape
-    Hv, Dv = v.shape[1], v.shape[2]
-    _need(k, "k", q.dtype, (B, Hk, Dk), dev)
-    _need(v, "v", q.dtype, (B, Hv, Dv), dev)
-    _need(g, "g", torch.float32, (B, Hv, Dk), dev)
-    _need(beta, "beta", torch.float32, (B, Hv), dev)
-    _need(state, "state", torch.float32, (B, Hv, Dv, Dk), dev)
-    if out is None:
-        out = torch.empty((B, Hv, Dv), dtype=q.dtype, device=dev)
-    _need(out, "out", q.dtype, (B, Hv, Dv), dev)
-    with torch.cuda.device(dev):
-        stream = torch.cuda.current_stream(dev).cuda_stream
-        st = lib.gdn_kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state),
-                                     B, Hk, Hv, Dk, Dv, io, _ptr(out), ctypes.c_void_p(stream))
-    _check(lib, st, "gdn_kda_decode_step")
-    return out
+    return _decode_call(lib, lib.gdn_kda_decode_step, "gdn_kda_decode_step", q, k, v, g,
+                        lambda B, Hv, Dk: (B, Hv, Dk), beta, state, out)
 
 
 PATH_ONE_LAUNCH, PATH_SPLIT, PATH_SEG = 0, 1, 2
