@@ -337,13 +337,15 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(C <= 64
     }
     __syncthreads();
 
-    // #3 Solve, T = (I + A)^-1: the diagonal 16x16 blocks by substitution (lane l16 one
-    // column), then the blocks below them by distance d from the diagonal,
+    // #3 Solve, T = (I + A)^-1: the diagonal 16x16 blocks by substitution, four at once on
+    // one wave (lane group g4 of wave w takes block 4 w + g4, lane l16 one column; the
+    // other waves wait at the barrier, leaving their SIMDs to the CU's other workgroups),
+    // then the blocks below them by distance d from the diagonal,
     // T_IJ = -T_II (sum_{J <= m < I} A_Im T_mJ), on fp32 MFMAs (16x16x4: lane l supplies
     // row / column l % 16 at k = l / 16).  One barrier per distance: the sums read only
     // blocks of smaller distance; each wave keeps its partial product in its own Y.
-    for (int X = wave; X < NT; X += 4) {
-        const int c = l16;
+    if (wave < (NT + 3) / 4 && 4 * wave + g4 < NT) {
+        const int X = 4 * wave + g4, c = l16;
         const float *blk = &M[16 * X * AS + 16 * X];   // A[16X + r][16X + q] = blk[q AS + r]
         float x[16];
 #pragma unroll
@@ -353,13 +355,12 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(C <= 64
             for (int q = 0; q < r; ++q) acc -= blk[q * AS + r] * x[q];
             x[r] = acc;
         }
-        if (g4 == 0) {   // the lower half with the diagonal; rows above it (x[r] = 0, over A^T)
-                         // go to the wave's Y block, unused until the levels below
+        // the lower half with the diagonal; rows above it (x[r] = 0, over A^T) go to a
+        // slot of Y, unused until the levels below
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float *dst = r >= c ? &M[(16 * X + r) * AS + 16 * X + c] : s.Y(wave) + c;
-                *dst = x[r];
-            }
+        for (int r = 0; r < 16; ++r) {
+            float *dst = r >= c ? &M[(16 * X + r) * AS + 16 * X + c] : s.Y(g4) + 16 * wave + c;
+            *dst = x[r];
         }
     }
     __syncthreads();

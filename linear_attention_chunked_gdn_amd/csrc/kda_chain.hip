@@ -153,10 +153,11 @@ __device__ __forceinline__ void dma_chunk(Smem<C, SPW> &sm, const Work &wk, int 
     f16x8 *dst = KL ? ob.kl : ob.w;
     constexpr int NF = KL ? F::NK : F::NW;
     constexpr int SRC = KL ? TL::KL : TL::WN;
-    const int rot = __builtin_amdgcn_readfirstlane((2 * wk.slice) % NF);
+    static_assert((NF & (NF - 1)) == 0, "fragment counts are powers of two");
+    const int rot = __builtin_amdgcn_readfirstlane(2 * wk.slice);
 #pragma unroll
     for (int f0 = 0; f0 < NF; ++f0) {
-        const int f = f0 + rot < NF ? f0 + rot : f0 + rot - NF;
+        const int f = (f0 + rot) & (NF - 1);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(dst + 64 * f), 16, 16 * lane, SRC + 1024 * f, 0, 0);
     }
 }

@@ -411,14 +411,14 @@ __global__ __launch_bounds__(THREADS, 2) void kda_map_kernel(const KdaArgs a) {
     }
     __syncthreads();
 
-    // #3 Solve, T = (I + A)^-1: the diagonal 16x16 blocks by substitution (wave X solves
-    // block X, lane l16 one column), then the blocks below them by distance from the
-    // diagonal, T_IJ = -T_II (sum_{J <= m < I} A_Im T_mJ), one block per wave on fp32
-    // MFMAs (16x16x4: lane l supplies row / column l % 16 at k = l / 16).
+    // #3 Solve, T = (I + A)^-1: the diagonal 16x16 blocks by substitution (all four on wave
+    // 0: lane group g4 solves block g4, lane l16 one column), then the blocks below them by
+    // distance from the diagonal, T_IJ = -T_II (sum_{J <= m < I} A_Im T_mJ), one block per
+    // wave on fp32 MFMAs (16x16x4: lane l supplies row / column l % 16 at k = l / 16).
     const float *A = s.sv.A;
     float *T = s.sv.T;
-    {
-        const int X = wave, c = l16;
+    if (wave == 0) {
+        const int X = g4, c = l16;
         const float *arow = &A[16 * X * AS + 16 * X];
         float x[16];
 #pragma unroll
@@ -428,10 +428,8 @@ __global__ __launch_bounds__(THREADS, 2) void kda_map_kernel(const KdaArgs a) {
             for (int q = 0; q < r; ++q) acc -= arow[r * AS + q] * x[q];
             x[r] = acc;
         }
-        if (g4 == 0) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) T[(16 * X + r) * AS + 16 * X + c] = x[r];
-        }
+        for (int r = 0; r < 16; ++r) T[(16 * X + r) * AS + 16 * X + c] = x[r];
     }
     __syncthreads();
     for (int d = 1; d < 4; ++d) {
