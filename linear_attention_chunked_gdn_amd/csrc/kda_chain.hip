@@ -31,13 +31,14 @@
 //   other wave's partial, forms v = p_0 + p_1 in fp16 (addition commutes exactly, so
 //   every wave that forms v gets the same values) and updates its half,
 //   S^T[half h] <- gl S^T[half h] + Kl[half h]^T v, with v's token tiles as B operands.
-//   U and gl come from L2 into registers one chunk ahead.
+//   U and gl come with WN and Kl through the ring (at C = 128 from L2 into registers, a
+//   chunk ahead).
 // * Waves 2 .. 5, the outputs, one 16-token tile each (two at C = 128).  After barrier c a
 //   wave reads slot c % 2 (S^T and both partials) and forms O^T = S Qg^T + v^T P^T, its
 //   Qg and P fragments loaded from L2 into registers a chunk ahead.  O^T puts four
 //   consecutive value channels of one token in a lane: one 8-byte store.
-// * Waves 6, 7, the loaders, stream WN and Kl into an NB-buffer LDS ring with direct
-//   global-to-LDS loads, chunk c + NB into buffer c % NB after barrier c.
+// * Waves 6, 7, the loaders, stream WN (with U) and Kl (with gl) into an NB-buffer LDS
+//   ring with direct global-to-LDS loads, chunk c + NB into buffer c % NB after barrier c.
 //
 // Each of a head's workgroups reads the same tiles; they run on one XCD and so share one
 // L2, from which a workgroup moves about 56 KB per chunk at C = 64.  With two slices per
@@ -77,6 +78,14 @@ struct Cfg {
     static constexpr int NSL = DV / DVS;          // workgroups per (sequence, head)
     static constexpr int NW = NT * 4;             // WN fragments per chunk
     static constexpr int NK = 8 * KB;             // Kl fragments per chunk
+    // U (the workgroup's slices) and gl travel with WN and Kl through the ring where the
+    // LDS holds them (C <= 64): NU 1 KB pieces of U and one of gl per chunk.  At C = 128
+    // the recurrence waves load them from L2 into registers.
+    static constexpr bool URING = C <= 64;
+    static constexpr int NU = URING ? SPW * NT / 2 : 0;
+    static constexpr int NG = URING ? 1 : 0;
+    // 1 KB direct-to-LDS loads per chunk of the WN loader (with U) and the Kl loader (with gl)
+    static constexpr int nload(bool kl) { return kl ? NK + NG : NW + NU; }
     // operand ring depth: chunk c + NB - 1 is loaded while chunk c runs
     static constexpr int NB = C == 32 ? 4 : C == 64 ? 3 : 2;
     static constexpr int OT = NT >= 4 ? NT / 4 : 1;   // token tiles per output wave
@@ -94,13 +103,16 @@ __device__ __forceinline__ f32x4 mfma(const f16x8 &a, const f16x8 &b, const f32x
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
-// LDS: the operand ring and two exchange slots (128 KB at C = 64, 152 KB at C = 128).
+// LDS: the operand ring and two exchange slots (123 KB at C = 64, 152 KB at C = 128).
 template <int C, int SPW>
 struct __align__(16) Smem {
     using F = Cfg<C, SPW>;
     struct Ops {
         f16x8 w[F::NW * 64];   // WN fragments (t, kb), lane-major, as in the tile
         f16x8 kl[F::NK * 64];  // Kl fragments (i, kb)
+        // the workgroup's U fragments (slice, token tile) as in the tile, then gl's 512
+        // bytes (in a 1 KB piece)
+        f16x8 ug[F::URING ? (F::NU + F::NG) * 64 : 1];
     } ob[F::NB];
     f16x8 xs[2][F::SPW * 4 * 64];             // S^T fragments (slice, key block)
     u32x2 pv[2][2][F::SPW][F::NT * 64];       // the recurrence waves' partials, fp16 (wave, slice, token tile)
@@ -160,6 +172,17 @@ __device__ __forceinline__ void dma_chunk(Smem<C, SPW> &sm, const Work &wk, int 
         const int f = (f0 + rot) & (NF - 1);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(dst + 64 * f), 16, 16 * lane, SRC + 1024 * f, 0, 0);
     }
+    if constexpr (F::URING) {
+        if constexpr (KL) {   // gl's 512 bytes, the tile's last: lanes 0 .. 31
+            if (lane < 32)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(ob.ug + 64 * F::NU), 16, TL::GL + 16 * lane, 0, 0, 0);
+        } else {              // U of the workgroup's slices, contiguous in the tile
+            const int u0 = __builtin_amdgcn_readfirstlane(TL::u(wk.slice * F::SPW, 0));
+#pragma unroll
+            for (int j = 0; j < F::NU; ++j)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(ob.ug + 64 * j), 16, 16 * lane, u0 + 1024 * j, 0, 0);
+        }
+    }
 }
 
 // A loader wave's run.  Chunk c's operands are read by the recurrence waves between
@@ -170,7 +193,7 @@ __device__ __forceinline__ void dma_chunk(Smem<C, SPW> &sm, const Work &wk, int 
 template <int C, int SPW, bool KL>
 __device__ __forceinline__ void loader_run(Smem<C, SPW> &sm, const Work &wk, int lane) {
     using F = Cfg<C, SPW>;
-    constexpr int NF = KL ? F::NK : F::NW;
+    constexpr int NF = F::nload(KL);
 #pragma unroll
     for (int j = 0; j < F::NB; ++j) dma_chunk<C, SPW, KL>(sm, wk, j, lane);
     wait_vmcnt<(F::NB - 1) * NF>();   // chunk 0
@@ -185,10 +208,13 @@ __device__ __forceinline__ void loader_run(Smem<C, SPW> &sm, const Work &wk, int
 
 // ---- the recurrence -------------------------------------------------------------------
 
-// Recurrence wave h's global operands for one chunk: half of the token tiles of the
-// workgroup's U slices (tiles h NT / 2 .. (h + 1) NT / 2 - 1, which its partials add; the
-// same loads on both waves, so that the compiler's load counts are exact) and its keys'
-// decays gl (one value for the scalar gate).  WN and Kl come from the ring.
+// Recurrence wave h's per-chunk operands besides WN and Kl: half of the token tiles of the
+// workgroup's U slices (tiles h NT / 2 .. (h + 1) NT / 2 - 1, which its partials add) and
+// its keys' decays gl (one value for the scalar gate).  From the ring where it carries
+// them (ring_rec); at C = 128 from L2 a chunk ahead (load_rec: the same loads on both
+// waves, so that the compiler's load counts are exact).  A vector-memory instruction
+// costs the CU's address and data path about as much whatever its width, and these small
+// loads on the recurrence waves took ~7 % of the chain's time at C = 64.
 template <int C, int SPW, bool PERCH>
 struct RecRegs {
     u32x2 u[Cfg<C, SPW>::SPW][Cfg<C, SPW>::NT / 2];
@@ -214,6 +240,24 @@ __device__ __forceinline__ void load_rec(RecRegs<C, SPW, PERCH> &rg, const Work 
                                                                                        TL::GL + 64 * (4 * h + i), 0));
     } else {
         rg.gl[0][0] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, 0, TL::GL, 0));
+    }
+}
+
+template <int C, int SPW, bool PERCH>
+__device__ __forceinline__ void ring_rec(RecRegs<C, SPW, PERCH> &rg, const Smem<C, SPW> &sm, int c, int h, int lane) {
+    using F = Cfg<C, SPW>;
+    const typename Smem<C, SPW>::Ops &ob = sm.ob[c % F::NB];
+    const u32x2 *u = reinterpret_cast<const u32x2 *>(ob.ug);
+#pragma unroll
+    for (int s = 0; s < F::SPW; ++s)
+#pragma unroll
+        for (int t = 0; t < F::NT / 2; ++t) rg.u[s][t] = u[(s * F::NT + h * F::NT / 2 + t) * 64 + lane];
+    if constexpr (PERCH) {
+        const f32x4 *g = reinterpret_cast<const f32x4 *>(ob.ug + 64 * F::NU);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) rg.gl[i] = g[4 * (4 * h + i) + (lane >> 4)];
+    } else {
+        rg.gl[0][0] = reinterpret_cast<const float *>(ob.ug + 64 * F::NU)[0];
     }
 }
 
@@ -333,11 +377,21 @@ __device__ __forceinline__ void rec_step(f32x4 (&st)[SPW][4], const RecRegs<C, S
 }
 
 // Recurrence wave h's run: barrier -1 (chunk 0 in the ring), then a barrier per chunk;
-// U and gl of chunk c + 1 are loaded while chunk c runs.
+// U and gl of chunk c come with its ring buffer, or (C = 128) those of chunk c + 1 are
+// loaded while chunk c runs.
 template <int C, int SPW, bool PERCH>
 __device__ __forceinline__ void rec_run(f32x4 (&st)[SPW][4], Smem<C, SPW> &sm, const Work &wk, int h, int lane,
                                         bool with_u) {
     const int n = wk.nchunks;
+    if constexpr (Cfg<C, SPW>::URING) {
+        __syncthreads();
+        for (int c = 0; c < n; ++c) {
+            RecRegs<C, SPW, PERCH> rg;
+            ring_rec(rg, sm, c, h, lane);
+            rec_step(st, rg, sm, c, h, lane, with_u);
+        }
+        return;
+    }
     RecRegs<C, SPW, PERCH> r0, r1;
     load_rec(r0, wk, 0, h, lane);
     __syncthreads();
