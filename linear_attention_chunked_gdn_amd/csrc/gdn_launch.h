@@ -52,7 +52,8 @@ struct KdaArgs {
     int32_t nseg;
     _Float16 *o0;           // [T_tot, Hv, 128] outputs of segments >= 1 from a zero start
     _Float16 *e;            // [T_tot, Hv, 128] outputs of the identity-state rows
-    float *sseg;            // [N, Hv, nseg, 2, 128, 128] segment end states (S and X^T)
+    float *sseg;            // [N, Hv, nseg, 2, 128, 128] segment end states: segment 0's S [row][key], later
+                            // segments' S from zero and X, both transposed [key][row]
     _Float16 *sin16;        // [N, Hv, nseg, 128, 128] start states of segments 1 .. nseg - 1
     uint32_t prologue;      // GDN_PROLOGUE_* flags of the scalar-gate map (0: none)
 };

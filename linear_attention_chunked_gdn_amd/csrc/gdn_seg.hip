@@ -13,7 +13,7 @@
 // The chain kernel's segment mode writes O0 and E (fp16), S0_end and X^T; segment 0
 // starts from the real initial state and writes its outputs directly.
 //
-// gdn_seg_join_kernel: one 256-thread workgroup per (sequence, value head, 16 value
+// gdn_seg_join_kernel: one 512-thread workgroup per (sequence, value head, 16 value
 // channels) walks the segments in order, S_in(s + 1) = S_in(s) X_s + S0_end(s) with one
 // fp32 MFMA product each (X_{s+1} and S0_end(s + 1) loaded while segment s is joined),
 // stores every S_in as fp16 (a.sin16) and the last one as the final state.
@@ -30,10 +30,11 @@ namespace gdnseg {
 constexpr int D = 128;
 constexpr int ROWS = 16;        // value channels per workgroup
 constexpr int RS = D + 4;       // fp32 row stride of the S_in rows in LDS
-constexpr int THREADS = 256;
+constexpr int JOIN_THREADS = 512;   // 8 waves: one per 16 key columns
 
-// S_in(s + 1) = S_in(s) X_s + S0_end(s) for the workgroup's 16 rows, held in LDS
-__global__ __launch_bounds__(THREADS) void gdn_seg_join_kernel(const KdaArgs a) {
+// S_in(s + 1) = S_in(s) X_s + S0_end(s) for the workgroup's 16 rows, held in LDS; wave w
+// forms key columns [16 w, 16 w + 16).
+__global__ __launch_bounds__(JOIN_THREADS) void gdn_seg_join_kernel(const KdaArgs a) {
     __shared__ __align__(16) float R[ROWS * RS];
     const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, g4 = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -44,8 +45,8 @@ __global__ __launch_bounds__(THREADS) void gdn_seg_join_kernel(const KdaArgs a) 
 
     // fp16 copies of S_in(1) .. S_in(nseg - 1), [nseg][128][128] per (sequence, head)
     _Float16 *s16 = a.sin16 + ((size_t)n * a.Hv + h) * a.nseg * D * D;
-    for (int i = tid; i < ROWS * D / 4; i += THREADS) {   // S_in(1): segment 0's end state
-        const int r = i / (D / 4), c = 4 * (i % (D / 4));
+    {   // S_in(1): segment 0's end state (thread t: row t / 32, keys 4 (t % 32) .. + 3)
+        const int r = tid >> 5, c = 4 * (tid & 31);
         const f32x4 x = *reinterpret_cast<const f32x4 *>(sb + (size_t)(dv0 + r) * D + c);
         *reinterpret_cast<f32x4 *>(&R[r * RS + c]) = x;
         f16x4 y;
@@ -54,57 +55,51 @@ __global__ __launch_bounds__(THREADS) void gdn_seg_join_kernel(const KdaArgs a) 
         *reinterpret_cast<f16x4 *>(s16 + (size_t)(dv0 + r) * D + c) = y;
     }
     __syncthreads();
-    // Segment s's operands, loaded one segment ahead: wave w's key columns
-    // [32w, 32w + 32) of X_s^T (B fragments; slot (g4, e) = row r = 32 kb + 8 g4 + e of X)
-    // and of S0_end(s) (rows dv0 + 4 g4 + i).
+    // Segment s's operands, loaded one segment ahead: the wave's 16 key columns of X_s^T (B
+    // fragments; slot (g4, e) = row r = 32 kb + 8 g4 + e of X) and of S0_end(s)^T (rows
+    // dv0 + 4 g4 .. + 3 of a column: 16 bytes).
+    const int col = 16 * wave + l16;
     struct StepOps {
-        Frag<float> fb[2][4];
-        f32x4 s0[2];
+        Frag<float> fb[4];
+        f32x4 s0;
     };
     auto load_step = [&](StepOps &op, int s) {
         const float *s0e = sb + (size_t)s * 2 * D * D;
         const float *xt = s0e + D * D;
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-            const int col = 32 * wave + 16 * ct + l16;
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb) op.fb[ct][kb].load8(xt + (size_t)col * D + 32 * kb + 8 * g4);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) op.s0[ct][i] = s0e[(size_t)(dv0 + 4 * g4 + i) * D + col];
-        }
+        for (int kb = 0; kb < 4; ++kb) op.fb[kb].load8(xt + (size_t)col * D + 32 * kb + 8 * g4);
+        op.s0 = *reinterpret_cast<const f32x4 *>(s0e + (size_t)col * D + dv0 + 4 * g4);
     };
     auto step = [&](const StepOps &op, int s) {
-        // lane: rows dv0 + 4 g4 + i, key column 32 wave + 16 ct + l16; the sum over a row of
-        // X in two halves (two accumulators) for a shorter dependent chain
-        f32x4 acc[2][2];
+        // lane: rows dv0 + 4 g4 + i, key column col; the sum over a row of X in two halves
+        // (two accumulators) for a shorter dependent chain
+        f32x4 acc[2];
+        acc[0] = op.s0;
+        acc[1] = zero4();
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-            acc[ct][0] = op.s0[ct];
-            acc[ct][1] = zero4();
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                Frag<float> fa;
-                fa.load8(&R[l16 * RS + 32 * kb + 8 * g4]);
-                mma(acc[ct][kb & 1], fa, op.fb[ct][kb]);
-            }
+        for (int kb = 0; kb < 4; ++kb) {
+            Frag<float> fa;
+            fa.load8(&R[l16 * RS + 32 * kb + 8 * g4]);
+            mma(acc[kb & 1], fa, op.fb[kb]);
         }
         __syncthreads();   // every wave has read R
-        // S_in(s + 1) as fp16 for the fix-up, or the final state after the last segment
-        const bool last = s + 1 == a.nseg;
-        float *fin = last && a.sN ? a.sN + ((size_t)n * a.Hv + h) * D * D : nullptr;
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-            const int col = 32 * wave + 16 * ct + l16;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float y = acc[ct][0][i] + acc[ct][1][i];
-                const size_t at = (size_t)(dv0 + 4 * g4 + i) * D + col;
-                R[(4 * g4 + i) * RS + col] = y;
-                if (!last) s16[(size_t)s * D * D + at] = (_Float16)y;
-                if (fin) fin[at] = y;
-            }
-        }
+        for (int i = 0; i < 4; ++i) R[(4 * g4 + i) * RS + col] = acc[0][i] + acc[1][i];
         __syncthreads();
+        // S_in(s + 1) from R, row-major (thread t: row t / 32, keys 4 (t % 32) .. + 3): as
+        // fp16 for the fix-up, or in fp32 as the final state after the last segment.  (The
+        // next step only reads R before its first barrier, as these reads do.)
+        const int r = tid >> 5, c = 4 * (tid & 31);
+        const f32x4 y = *reinterpret_cast<const f32x4 *>(&R[r * RS + c]);
+        const size_t at = (size_t)(dv0 + r) * D + c;
+        if (s + 1 < a.nseg) {
+            f16x4 yh;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) yh[e] = (_Float16)y[e];
+            *reinterpret_cast<f16x4 *>(s16 + (size_t)s * D * D + at) = yh;
+        } else if (a.sN) {
+            *reinterpret_cast<f32x4 *>(a.sN + ((size_t)n * a.Hv + h) * D * D + at) = y;
+        }
     };
     StepOps op0, op1;
     if (a.nseg > 1) load_step(op0, 1);
@@ -116,11 +111,9 @@ __global__ __launch_bounds__(THREADS) void gdn_seg_join_kernel(const KdaArgs a) 
         step(op1, s + 1);
     }
     if (a.nseg == 1 && a.sN) {   // one segment: its end state is the final state
-        float *dst = a.sN + ((size_t)n * a.Hv + h) * D * D;
-        for (int i = tid; i < ROWS * D / 4; i += THREADS) {
-            const int r = i / (D / 4), c = 4 * (i % (D / 4));
-            *reinterpret_cast<f32x4 *>(dst + (size_t)(dv0 + r) * D + c) = *reinterpret_cast<const f32x4 *>(&R[r * RS + c]);
-        }
+        const int r = tid >> 5, c = 4 * (tid & 31);
+        *reinterpret_cast<f32x4 *>(a.sN + ((size_t)n * a.Hv + h) * D * D + (size_t)(dv0 + r) * D + c) =
+            *reinterpret_cast<const f32x4 *>(&R[r * RS + c]);
     }
 }
 
@@ -211,7 +204,7 @@ hipError_t launch_seg_join(const KdaArgs &a, hipStream_t stream) {
     constexpr unsigned NSL = gdnseg::D / gdnseg::ROWS;
     const unsigned long long items = (unsigned long long)a.N * a.Hv * NSL;
     if (a.nseg < 1 || items > 0x7fffffffULL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(gdnseg::gdn_seg_join_kernel, dim3((unsigned)items), dim3(gdnseg::THREADS), 0, stream, a);
+    hipLaunchKernelGGL(gdnseg::gdn_seg_join_kernel, dim3((unsigned)items), dim3(gdnseg::JOIN_THREADS), 0, stream, a);
     return hipGetLastError();
 }
 

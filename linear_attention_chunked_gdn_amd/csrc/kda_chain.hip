@@ -636,13 +636,15 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
             }
         if (wk.nchunks > 0) rec_run<C, SPW, PERCH>(st, sm, wk, kh, lane, !ident);
         if constexpr (SEG) {
+            // segment 0's end state [row][key]; later segments' end states from zero and
+            // from the identity (X) transposed, [key][row], as the join reads them
             float *sb = a.sseg + ((((size_t)n * a.Hv + h) * a.nseg + seg) * 2 + (ident ? 1 : 0)) * DV * DK;
 #pragma unroll
             for (int sl = 0; sl < SPW; ++sl)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int dk = 64 * kh + 16 * i + 4 * g4, r = wk.dv0 + 16 * sl + l16;
-                    if (ident) {   // X^T [key][row]
+                    if (seg > 0) {
 #pragma unroll
                         for (int q = 0; q < 4; ++q) sb[(size_t)(dk + q) * DV + r] = st[sl][i][q];
                     } else {
