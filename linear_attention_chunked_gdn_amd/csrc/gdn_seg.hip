@@ -18,9 +18,10 @@
 // fp32 MFMA product each (X_{s+1} and S0_end(s + 1) loaded while segment s is joined),
 // stores every S_in as fp16 (a.sin16) and the last one as the final state.
 // gdn_seg_fix_kernel: one 512-thread workgroup per (chunk slot, value head) of segments
-// >= 1 issues all its loads at once (E rows, S_in fragments, O0), stages the chunk's E
-// rows in LDS; wave w forms O = O0 + E S_in^T for value channels [16w, 16w + 16) (fp16
-// MFMA, fp32 accumulation) and stores it.
+// >= 1 issues all its loads at once (E and O0 rows, 16 bytes per lane, and S_in
+// fragments), stages the chunk's E and O0 rows in LDS; wave w forms O = O0 + E S_in^T for
+// value channels [16w, 16w + 16) (fp16 MFMA, fp32 accumulation) into the O0 rows' place,
+// and the workgroup stores the o rows 16 bytes per lane.
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
@@ -121,8 +122,9 @@ constexpr int FIX_THREADS = 512;   // 8 waves: one per 16 value channels
 
 template <typename IO, int C>
 __global__ __launch_bounds__(FIX_THREADS) void gdn_seg_fix_kernel(const KdaArgs a) {
-    constexpr int ES = D + 8;   // fp16 row stride of the staged E rows
+    constexpr int ES = D + 8;   // 16-bit row stride of the staged E, O0 and o rows
     __shared__ __align__(16) _Float16 Es[C * ES];
+    __shared__ __align__(16) _Float16 Os[C * ES];   // O0 rows, then o's (IO) in place
     const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, g4 = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int slot = blockIdx.x / a.Hv, h = blockIdx.x % a.Hv;
@@ -148,53 +150,61 @@ __global__ __launch_bounds__(FIX_THREADS) void gdn_seg_fix_kernel(const KdaArgs 
     const int dv0 = ROWS * wave;
     const int nval = min(C, eos - tok0);
 
-    // E rows of the chunk (clamped into the sequence; rows past it become zero in LDS),
-    // loaded with S_in and O0 below before any of them is waited for
-    constexpr int EPT = C * D / 8 / FIX_THREADS;   // 16-byte E segments per thread
-    static_assert(EPT * FIX_THREADS * 8 == C * D, "E segments split evenly over the threads");
-    f16x8 ev[EPT];
+    // E and O0 rows of the chunk, 16 bytes per lane (rows clamped into the sequence: E's
+    // past it become zero in LDS, O0's are not stored), and S_in, all issued before any
+    // is waited for
+    constexpr int EPT = C * D / 8 / FIX_THREADS;   // 16-byte row segments per thread
+    static_assert(EPT * FIX_THREADS * 8 == C * D, "row segments split evenly over the threads");
+    f16x8 ev[EPT], ov[EPT];
 #pragma unroll
     for (int p = 0; p < EPT; ++p) {
         const int i = tid + FIX_THREADS * p, t = i / (D / 8), c = 8 * (i % (D / 8));
-        ev[p] = *reinterpret_cast<const f16x8 *>(a.e + ((size_t)(tok0 + min(t, nval - 1)) * a.Hv + h) * D + c);
+        const size_t at = ((size_t)(tok0 + min(t, nval - 1)) * a.Hv + h) * D + c;
+        ev[p] = *reinterpret_cast<const f16x8 *>(a.e + at);
+        ov[p] = *reinterpret_cast<const f16x8 *>(a.o0 + at);
     }
-    // S_in(seg) rows dv0 + l16 as A operands (slots = identity rows 32 kb + 8 g4 + e), and O0
+    // S_in(seg) rows dv0 + l16 as A operands (slots = identity rows 32 kb + 8 g4 + e)
     const _Float16 *sin = a.sin16 + (((size_t)n * a.Hv + h) * a.nseg + (seg - 1)) * D * D;
     Frag<_Float16> fs[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) fs[kb].load8(sin + (size_t)(dv0 + l16) * D + 32 * kb + 8 * g4);
-    f32x4 acc[C / 16];
-#pragma unroll
-    for (int t = 0; t < C / 16; ++t) {
-        const int tc = min(16 * t + l16, nval - 1);   // rows past the sequence: read in bounds, not stored
-        const f16x4 o0 = *reinterpret_cast<const f16x4 *>(a.o0 + ((size_t)(tok0 + tc) * a.Hv + h) * D + dv0 + 4 * g4);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[t][i] = (float)o0[i];
-    }
 #pragma unroll
     for (int p = 0; p < EPT; ++p) {
         const int i = tid + FIX_THREADS * p, t = i / (D / 8), c = 8 * (i % (D / 8));
         const f16x8 zero = {};
         *reinterpret_cast<f16x8 *>(&Es[t * ES + c]) = t < nval ? ev[p] : zero;
+        *reinterpret_cast<f16x8 *>(&Os[t * ES + c]) = ov[p];
     }
     __syncthreads();
 
-    // O^T (value channels x tokens) = O0^T + S_in E^T, one 16-token tile at a time
+    // O^T (value channels x tokens) = O0^T + S_in E^T, one 16-token tile at a time; o back
+    // into the wave's own columns of Os
 #pragma unroll
     for (int t = 0; t < C / 16; ++t) {
+        _Float16 *orow = &Os[(16 * t + l16) * ES + dv0 + 4 * g4];
+        const f16x4 o0 = *reinterpret_cast<const f16x4 *>(orow);
+        f32x4 acc;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] = (float)o0[i];
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
             Frag<_Float16> fe;
             fe.load8(&Es[(16 * t + l16) * ES + 32 * kb + 8 * g4]);
-            mma(acc[t], fs[kb], fe);
+            mma(acc, fs[kb], fe);
         }
-        if (16 * t + l16 < nval) {
-            typename Vec4<IO>::type y;
+        typename Vec4<IO>::type y;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) y[i] = Cvt<IO>::from_f32(acc[t][i]);
-            *reinterpret_cast<typename Vec4<IO>::type *>(reinterpret_cast<IO *>(a.o) +
-                                                         ((size_t)(tok0 + 16 * t + l16) * a.Hv + h) * D + dv0 + 4 * g4) = y;
-        }
+        for (int i = 0; i < 4; ++i) y[i] = Cvt<IO>::from_f32(acc[i]);
+        *reinterpret_cast<typename Vec4<IO>::type *>(orow) = y;
+    }
+    __syncthreads();
+    // o rows of the chunk's tokens, 16 bytes per lane
+#pragma unroll
+    for (int p = 0; p < EPT; ++p) {
+        const int i = tid + FIX_THREADS * p, t = i / (D / 8), c = 8 * (i % (D / 8));
+        if (t < nval)
+            *reinterpret_cast<f16x8 *>(reinterpret_cast<IO *>(a.o) + ((size_t)(tok0 + t) * a.Hv + h) * D + c) =
+                *reinterpret_cast<const f16x8 *>(&Os[t * ES + c]);
     }
 }
 
