@@ -36,7 +36,10 @@
 // * Waves 2 .. 5, the outputs, one 16-token tile each (two at C = 128).  After barrier c a
 //   wave reads slot c % 2 (S^T and both partials) and forms O^T = S Qg^T + v^T P^T, its
 //   Qg and P fragments loaded from L2 into registers a chunk ahead.  O^T puts four
-//   consecutive value channels of one token in a lane: one 8-byte store.
+//   consecutive value channels of one token in a lane; the tiles go out through LDS as
+//   16-byte stores (a vector-memory instruction costs the CU's address and data path
+//   about the same whatever its width): with two slices a wave's own tile (32 channels
+//   per token), with one slice at C = 64 two waves' tiles after the next barrier.
 // * Waves 6, 7, the loaders, stream WN (with U) and Kl (with gl) into an NB-buffer LDS
 //   ring with direct global-to-LDS loads, chunk c + NB into buffer c % NB after barrier c.
 //
@@ -116,6 +119,10 @@ struct __align__(16) Smem {
     } ob[F::NB];
     f16x8 xs[2][F::SPW * 4 * 64];             // S^T fragments (slice, key block)
     u32x2 pv[2][2][F::SPW][F::NT * 64];       // the recurrence waves' partials, fp16 (wave, slice, token tile)
+    // output tiles on their way to 16-byte stores: with two slices each output wave's tile
+    // (16 tokens x 32 channels, 1 KB); with one slice at C = 64 every wave's tile (16 x 16,
+    // 512 B) of chunk c in half c % 2, stored with its neighbour's after the next barrier
+    f16x8 ot[F::SPW == 2 || C == 64 ? 256 : 1];
 };
 static_assert(sizeof(Smem<32, 2>) <= 160 * 1024 && sizeof(Smem<64, 2>) <= 160 * 1024 && sizeof(Smem<128, 1>) <= 160 * 1024,
               "the LDS holds the ring");
@@ -434,12 +441,24 @@ __device__ __forceinline__ void load_out(OutOps<C, SPW, O> &op, const Work &wk, 
 // Chunk c's outputs on output wave O: O^T = S Qg^T + v^T P^T for its token tiles, from the
 // exchange slot (S^T and the two partials of v).  In the segment mode `kind` picks the
 // destination, all [token][head][channel]: 0 IO to o (segment 0), 1 fp16 to a.o0 (value
-// rows of later segments), 2 fp16 to a.e (identity rows); one 8-byte store for each,
-// with no branch between them.
+// rows of later segments), 2 fp16 to a.e (identity rows), with the same stores for each
+// (bits and base pointer selected, no branch between them).
 template <typename IO, int C, int SPW, bool SEG, int O>
-__device__ __forceinline__ void out_step(const OutOps<C, SPW, O> &op, const Smem<C, SPW> &sm, int c, const KdaArgs &a,
-                                         int lane, int h, int dv0, int tok0, int nval, int kind) {
+__device__ __forceinline__ void out_step(const OutOps<C, SPW, O> &op, Smem<C, SPW> &sm, int c, const KdaArgs &a,
+                                         int lane, int h, int dv0, int tok0, int nval, int kind, char *obase, bool last) {
     using F = Cfg<C, SPW>;
+    // one slice at C = 64: the even output waves store chunk c - 1's tiles O and O + 1 (a
+    // chunk before the last is whole), 16 bytes per lane: token 16 O + lane / 2, channels
+    // dv0 + 8 (lane % 2) ..
+    constexpr bool PAIR = SPW == 1 && C == 64;
+    char *const stg = reinterpret_cast<char *>(sm.ot);
+    if constexpr (PAIR) {
+        if (O % 2 == 0 && c > 0) {
+            const f16x8 row = *reinterpret_cast<const f16x8 *>(stg + ((c - 1) & 1) * 2048 + O * 512 + 16 * lane);
+            const int tk = 16 * O + (lane >> 1);
+            *reinterpret_cast<f16x8 *>(obase + (((size_t)(tok0 - C + tk) * a.Hv + h) * DV + dv0 + 8 * (lane & 1)) * 2) = row;
+        }
+    }
     const int l16 = lane & 15, g4 = lane >> 4;
     constexpr int TMAX = 4 * (F::OT - 1) + O;                   // its last token tile
     constexpr int VB = (TMAX < F::NT ? TMAX : F::NT - 1) / 2 + 1;  // v blocks it needs
@@ -480,6 +499,29 @@ __device__ __forceinline__ void out_step(const OutOps<C, SPW, O> &op, const Smem
             ++pi;
         }
         const int tok = 16 * t + l16;
+        if constexpr (SPW == 2) {
+            // the tile's 32 channels per token through the wave's staging rows (64 bytes per
+            // token): one 16-byte store per lane (token 16 t + lane / 4, channels
+            // dv0 + 8 (lane % 4) ..) instead of two 8-byte ones
+#pragma unroll
+            for (int s = 0; s < SPW; ++s) {
+                typename Vec4<IO>::type yio;
+                f16x4 yh;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    yio[i] = Cvt<IO>::from_f32(accs[s][i]);
+                    yh[i] = (hf)accs[s][i];
+                }
+                const u32x2 bits = !SEG || kind == 0 ? __builtin_bit_cast(u32x2, yio) : __builtin_bit_cast(u32x2, yh);
+                *reinterpret_cast<u32x2 *>(stg + 1024 * O + 64 * l16 + 32 * s + 8 * g4) = bits;
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            const f16x8 row = *reinterpret_cast<const f16x8 *>(stg + 1024 * O + 16 * lane);
+            const int tk = 16 * t + (lane >> 2);
+            if (tk < nval) *reinterpret_cast<f16x8 *>(obase + (((size_t)(tok0 + tk) * a.Hv + h) * DV + dv0 + 8 * (lane & 3)) * 2) = row;
+            continue;
+        }
 #pragma unroll
         for (int s = 0; s < SPW; ++s) {
         const f32x4 &acc = accs[s];
@@ -493,13 +535,15 @@ __device__ __forceinline__ void out_step(const OutOps<C, SPW, O> &op, const Smem
                 yh[i] = (hf)acc[i];
             }
             const u32x2 bits = kind == 0 ? __builtin_bit_cast(u32x2, yio) : __builtin_bit_cast(u32x2, yh);
-            char *base = kind == 0 ? (char *)a.o : kind == 1 ? (char *)a.o0 : (char *)a.e;
-            if (tok < nval) *reinterpret_cast<u32x2 *>(base + at * 2) = bits;
-        } else if (tok < nval) {
+            if (tok < nval) *reinterpret_cast<u32x2 *>(obase + at * 2) = bits;
+        } else {
             typename Vec4<IO>::type y;
 #pragma unroll
             for (int i = 0; i < 4; ++i) y[i] = Cvt<IO>::from_f32(acc[i]);
-            *reinterpret_cast<typename Vec4<IO>::type *>(reinterpret_cast<IO *>(a.o) + at) = y;
+            if (PAIR && !last)
+                *reinterpret_cast<typename Vec4<IO>::type *>(stg + (c & 1) * 2048 + O * 512 + 32 * l16 + 8 * g4) = y;
+            else if (tok < nval)
+                *reinterpret_cast<typename Vec4<IO>::type *>(reinterpret_cast<IO *>(a.o) + at) = y;
         }
         }
     }
@@ -509,16 +553,20 @@ __device__ __forceinline__ void out_step(const OutOps<C, SPW, O> &op, const Smem
 // loads of chunk c + 1 are issued before barrier c.  A wave with no token tile (O >= NT,
 // at C = 32) takes part in the barriers only.
 template <typename IO, int C, int SPW, bool SEG, int O>
-__device__ __forceinline__ void output_run(const Smem<C, SPW> &sm, const KdaArgs &a, const Work &wk, int lane, int kind) {
+__device__ __forceinline__ void output_run(Smem<C, SPW> &sm, const KdaArgs &a, const Work &wk, int lane, int kind) {
     using F = Cfg<C, SPW>;
     const int n = wk.nchunks;
     if constexpr (O >= F::NT) {
         for (int c = 0; c <= n; ++c) __syncthreads();
         return;
     }
+    // the destination (segment mode: o, a.o0 or a.e by the workgroup's kind), picked once
+    char *obase = (char *)a.o;
+    if constexpr (SEG) obase = kind == 1 ? (char *)a.o0 : kind == 2 ? (char *)a.e : obase;
     auto step = [&](const OutOps<C, SPW, O> &op, int c) {
         const int tok0 = wk.bos + c * C;
-        out_step<IO, C, SPW, SEG, O>(op, sm, c, a, lane, wk.h, wk.dv0, tok0, min(C, wk.eos - tok0), kind);
+        out_step<IO, C, SPW, SEG, O>(op, sm, c, a, lane, wk.h, wk.dv0, tok0, min(C, wk.eos - tok0), kind, obase,
+                                     c + 1 >= n);
     };
     OutOps<C, SPW, O> op0, op1;
     load_out(op0, wk, 0, lane);
