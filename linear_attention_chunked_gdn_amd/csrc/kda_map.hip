@@ -56,8 +56,8 @@ template <typename IO>
 struct __align__(16) Smem {
     union {
         struct {
-            IO K[CH * XS];    // raw k rows of the chunk (rows past its end repeat the last)
-            IO Q[CH * XS];
+            hf K[CH * XS];    // k rows of the chunk in fp16 (rows past its end repeat the last)
+            hf Q[CH * XS];
         } kq;
         struct {              // once the grams are done: diag(beta) Kg, diag(beta) V
             hf Kb[CH * WY_S];
@@ -106,26 +106,20 @@ __device__ __forceinline__ void put_pair(hf *tile, int t, int ch, float x0, floa
 }
 
 // MFMA operand: 16 tokens (rows 16X + l16) x 32 key channels (32kb + 8g4 + e) of x, times
-// the factor tile f (fp16 product).
-template <typename IO>
-__device__ __forceinline__ Frag<hf> frag_scaled(const IO *x, const hf *f, int X, int kb, int l16, int g4) {
-    typedef IO v8 __attribute__((ext_vector_type(8)));
+// the factor tile f: one fp16 multiply per element (packed two to an instruction).  x and
+// f are fp16, so their exact product fits fp32 and the fp16 multiply rounds it once, as
+// forming it in fp32 and converting would; k and q go to fp16 as they are staged, which is
+// exact for bf16 values within fp16's normal range.
+__device__ __forceinline__ Frag<hf> frag_scaled(const hf *x, const hf *f, int X, int kb, int l16, int g4) {
     const int off = (16 * X + l16) * XS + 32 * kb + 8 * g4;
-    const v8 xv = *reinterpret_cast<const v8 *>(x + off);
-    const f16x8 fv = *reinterpret_cast<const f16x8 *>(f + off);
     Frag<hf> r;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) r.v[e] = (hf)(Cvt<IO>::to_f32(xv[e]) * (float)fv[e]);
+    r.v = *reinterpret_cast<const f16x8 *>(x + off) * *reinterpret_cast<const f16x8 *>(f + off);
     return r;
 }
 
-template <typename IO>
-__device__ __forceinline__ Frag<hf> frag_raw(const IO *x, int X, int kb, int l16, int g4) {
-    typedef IO v8 __attribute__((ext_vector_type(8)));
-    const v8 xv = *reinterpret_cast<const v8 *>(x + (16 * X + l16) * XS + 32 * kb + 8 * g4);
+__device__ __forceinline__ Frag<hf> frag_raw(const hf *x, int X, int kb, int l16, int g4) {
     Frag<hf> r;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) r.v[e] = (hf)Cvt<IO>::to_f32(xv[e]);
+    r.v = *reinterpret_cast<const f16x8 *>(x + (16 * X + l16) * XS + 32 * kb + 8 * g4);
     return r;
 }
 
@@ -225,8 +219,15 @@ __global__ __launch_bounds__(THREADS, 2) void kda_map_kernel(const KdaArgs a) {
         a0[i] = ok ? exp2f(gg[0] * LOG2E) : 1.f;
         a1[i] = ok ? exp2f(gg[1] * LOG2E) : 1.f;
         const size_t kq = (tok * a.Hk + hk) * DK + ch;
-        *reinterpret_cast<v2 *>(&s.kq.K[t * XS + ch]) = *reinterpret_cast<const v2 *>(reinterpret_cast<const IO *>(a.k) + kq);
-        *reinterpret_cast<v2 *>(&s.kq.Q[t * XS + ch]) = *reinterpret_cast<const v2 *>(reinterpret_cast<const IO *>(a.q) + kq);
+        const v2 kk = *reinterpret_cast<const v2 *>(reinterpret_cast<const IO *>(a.k) + kq);
+        const v2 qq = *reinterpret_cast<const v2 *>(reinterpret_cast<const IO *>(a.q) + kq);
+        f16x2 kh, qh;
+        kh[0] = (hf)Cvt<IO>::to_f32(kk[0]);
+        kh[1] = (hf)Cvt<IO>::to_f32(kk[1]);
+        qh[0] = (hf)Cvt<IO>::to_f32(qq[0]);
+        qh[1] = (hf)Cvt<IO>::to_f32(qq[1]);
+        *reinterpret_cast<f16x2 *>(&s.kq.K[t * XS + ch]) = kh;
+        *reinterpret_cast<f16x2 *>(&s.kq.Q[t * XS + ch]) = qh;
     }
     if (wave == 0) s.beta[lane] = lane < nval ? braw : 0.f;
     // products inside the block: F inclusive from the block start, B exclusive to its end
@@ -262,16 +263,16 @@ __global__ __launch_bounds__(THREADS, 2) void kda_map_kernel(const KdaArgs a) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int t = 16 * b + i;
-            const v2 kv = *reinterpret_cast<const v2 *>(&s.kq.K[t * XS + ch]);
-            const v2 qv = *reinterpret_cast<const v2 *>(&s.kq.Q[t * XS + ch]);
-            const float k0 = Cvt<IO>::to_f32(kv[0]), k1 = Cvt<IO>::to_f32(kv[1]);
+            const f16x2 kv = *reinterpret_cast<const f16x2 *>(&s.kq.K[t * XS + ch]);
+            const f16x2 qv = *reinterpret_cast<const f16x2 *>(&s.kq.Q[t * XS + ch]);
+            const float k0 = (float)kv[0], k1 = (float)kv[1];
             const float e0 = pre0 * F0[i], e1 = pre1 * F1[i];
             const float l0 = B0[i] * post0, l1 = B1[i] * post1;
             const float bt = s.beta[t];
             kgb[i][0] = (hf)(k0 * e0 * bt);
             kgb[i][1] = (hf)(k1 * e1 * bt);
             f16x2 x;
-            x[0] = (hf)(Cvt<IO>::to_f32(qv[0]) * e0); x[1] = (hf)(Cvt<IO>::to_f32(qv[1]) * e1);
+            x[0] = (hf)((float)qv[0] * e0); x[1] = (hf)((float)qv[1] * e1);
             // Qg(token tile b, channel block ch / 32): channels ch, ch + 1 share a lane's slots
             const int j = ch & 31;
             *reinterpret_cast<f16x2 *>(tile + Tile<CH>::qg(b, ch >> 5) + 16 * frag_lane(j, i) + frag_byte(j)) = x;
