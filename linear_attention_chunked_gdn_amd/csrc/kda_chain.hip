@@ -106,7 +106,8 @@ __device__ __forceinline__ f32x4 mfma(const f16x8 &a, const f16x8 &b, const f32x
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
-// LDS: the operand ring and two exchange slots (123 KB at C = 64, 152 KB at C = 128).
+// LDS: the operand ring, two exchange slots and the output staging (125 KB at C = 64 with
+// one slice, 147 KB with two, 152 KB at C = 128).
 template <int C, int SPW>
 struct __align__(16) Smem {
     using F = Cfg<C, SPW>;
