@@ -50,3 +50,12 @@ def test_choose_path(lengths, Hk, Hv, io, prologue, segments, want):
     x = _shape(lengths, Hk, Hv, io=io)
     assert bench.choose_path(x, "auto", prologue, segments) == want
     assert bench.choose_path(x, "pipe", prologue, segments) == "pipe"
+
+
+def test_headline_traffic_record_matches_the_kernel_sources():
+    # bench.py reports roofline.traffic from profiles/hbm_traffic.json only while the
+    # sources it was measured on are unchanged: a kernel edit needs the counters retaken
+    # (or, for an edit that leaves the code as it was, the record re-keyed from them)
+    rec = bench.recorded_traffic("gdn_map_kernel+kda_chain_kernel", "prefill_bf16_H16_T4096")
+    assert rec is not None, "profiles/hbm_traffic.json has no current record for the headline's kernels"
+    assert 2 * bench.algorithmic_bytes(inputs.make_workload(1)) < rec < 4 * bench.algorithmic_bytes(inputs.make_workload(1))
