@@ -393,10 +393,13 @@ __device__ __forceinline__ void rec_run(f32x4 (&st)[SPW][4], Smem<C, SPW> &sm, c
     const int n = wk.nchunks;
     if constexpr (Cfg<C, SPW>::URING) {
         __syncthreads();
-        for (int c = 0; c < n; ++c) {
-            RecRegs<C, SPW, PERCH> rg;
-            ring_rec(rg, sm, c, h, lane);
-            rec_step(st, rg, sm, c, h, lane, with_u);
+        for (int c = 0; c < n; c += 2) {   // two chunks per trip, as below
+            RecRegs<C, SPW, PERCH> r0, r1;
+            ring_rec(r0, sm, c, h, lane);
+            rec_step(st, r0, sm, c, h, lane, with_u);
+            if (c + 1 >= n) break;
+            ring_rec(r1, sm, c + 1, h, lane);
+            rec_step(st, r1, sm, c + 1, h, lane, with_u);
         }
         return;
     }
