@@ -18,35 +18,36 @@
 // owns 16 of them (or 32, as two slices) for one (sequence, value head) and needs nothing
 // from the others.
 //
-// Eight waves share a workgroup, one barrier per chunk:
+// Eight waves share a workgroup (ten with two slices), one barrier per chunk:
 //
-// * Waves 0, 1, the recurrence, one per half of the key channels.  Wave h holds rows
-//   64 h .. 64 h + 63 of S^T (its key half x 16 value channels, per slice) as four fp32
-//   16x16 accumulators that never leave its registers; read in pairs, an accumulator's
-//   rows are the eight reduction slots of an MFMA operand (the slot order pi of the tile
-//   layout), so fp16 copies of S^T are B operands as they stand.  Per chunk, wave h reads
-//   its halves of WN and Kl from the LDS ring, forms the partial
-//   p_h = WN[:, half h] S^T[half h], plus U on its half of the token tiles, and writes it
-//   and its fp16 copy of S^T into exchange slot c % 2; after the barrier it reads the
-//   other wave's partial, forms v = p_0 + p_1 in fp16 (addition commutes exactly, so
-//   every wave that forms v gets the same values) and updates its half,
+// * Waves 0 .. 2 SPW - 1, the recurrence, two per slice of 16 value channels, one per half
+//   of the key channels.  The wave of slice s and key half h holds rows 64 h .. 64 h + 63
+//   of that slice's S^T as four fp32 16x16 accumulators that never leave its registers;
+//   read in pairs, an accumulator's rows are the eight reduction slots of an MFMA operand
+//   (the slot order pi of the tile layout), so fp16 copies of S^T are B operands as they
+//   stand.  Per chunk, the wave reads its key half of WN and Kl from the LDS ring, forms
+//   the partial p_h = WN[:, half h] S^T[half h], plus U on its half of the token tiles,
+//   and writes it and its fp16 copy of S^T into exchange slot c % 2; after the barrier it
+//   reads the other key half's partial, forms v = p_0 + p_1 in fp16 (addition commutes
+//   exactly, so every wave that forms v gets the same values) and updates its half,
 //   S^T[half h] <- gl S^T[half h] + Kl[half h]^T v, with v's token tiles as B operands.
 //   U and gl come with WN and Kl through the ring (at C = 128 from L2 into registers, a
 //   chunk ahead).
-// * Waves 2 .. 5, the outputs, one 16-token tile each (two at C = 128).  After barrier c a
-//   wave reads slot c % 2 (S^T and both partials) and forms O^T = S Qg^T + v^T P^T, its
-//   Qg and P fragments loaded from L2 into registers a chunk ahead.  O^T puts four
+// * The next four waves, the outputs, one 16-token tile each (two at C = 128).  After
+//   barrier c a wave reads slot c % 2 (S^T and both partials) and forms
+//   O^T = S Qg^T + v^T P^T, its Qg and P fragments loaded from L2 into registers a chunk
+//   ahead.  O^T puts four
 //   consecutive value channels of one token in a lane; the tiles go out through LDS as
 //   16-byte stores (a vector-memory instruction costs the CU's address and data path
 //   about the same whatever its width): with two slices a wave's own tile (32 channels
 //   per token), with one slice at C = 64 two waves' tiles after the next barrier.
-// * Waves 6, 7, the loaders, stream WN (with U) and Kl (with gl) into an NB-buffer LDS
-//   ring with direct global-to-LDS loads, chunk c + NB into buffer c % NB after barrier c.
+// * The last two waves, the loaders, stream WN (with U) and Kl (with gl) into an NB-buffer
+//   LDS ring with direct global-to-LDS loads, chunk c + NB into buffer c % NB after barrier c.
 //
 // Each of a head's workgroups reads the same tiles; they run on one XCD and so share one
 // L2, from which a workgroup moves about 56 KB per chunk at C = 64.  With two slices per
 // workgroup every WN, Kl, Qg and P fragment serves both: about the same bytes per chunk
-// for twice the value channels, and twice the recurrence and output work.
+// for twice the value channels, twice the output work, and two more recurrence waves.
 //
 // Measured and not kept (chain kernel at H16 T4096, against 44 us): one recurrence wave
 // fed from the ring (47 us: its LDS reads of 34.5 KB per chunk set the period); the two
@@ -65,9 +66,6 @@ typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int DK = 128;
 constexpr int DV = 128;
-// waves 0, 1: the recurrence (key halves); 2 .. 5: the outputs (token tiles t = 4 k + o);
-// 6, 7: the loaders (WN, Kl)
-constexpr int THREADS = 512;
 
 template <int C, int SPW_ = 1>
 struct Cfg {
@@ -78,6 +76,11 @@ struct Cfg {
     static constexpr int SPW = SPW_;
     static_assert(SPW == 1 || (SPW == 2 && C <= 64), "two slices up to C = 64");
     static constexpr int DVS = 16 * SPW;          // value channels per workgroup
+    // waves 0 .. NRW - 1: the recurrence (slice s = w / 2, key half w % 2); then four output
+    // waves (token tiles t = 4 k + o) and two loaders (WN, Kl)
+    static constexpr int NRW = 2 * SPW;
+    static constexpr int THREADS = 64 * (NRW + 6);
+    static constexpr int WPE = (NRW + 6 + 3) / 4;   // waves per SIMD
     static constexpr int NSL = DV / DVS;          // workgroups per (sequence, head)
     static constexpr int NW = NT * 4;             // WN fragments per chunk
     static constexpr int NK = 8 * KB;             // Kl fragments per chunk
@@ -216,30 +219,28 @@ __device__ __forceinline__ void loader_run(Smem<C, SPW> &sm, const Work &wk, int
 
 // ---- the recurrence -------------------------------------------------------------------
 
-// Recurrence wave h's per-chunk operands besides WN and Kl: half of the token tiles of the
-// workgroup's U slices (tiles h NT / 2 .. (h + 1) NT / 2 - 1, which its partials add) and
-// its keys' decays gl (one value for the scalar gate).  From the ring where it carries
+// The per-chunk operands besides WN and Kl of the recurrence wave of slice s and key half
+// h: half of the token tiles of U's slice s (tiles h NT / 2 .. (h + 1) NT / 2 - 1, which
+// its partials add) and its keys' decays gl (one value for the scalar gate).  From the ring where it carries
 // them (ring_rec); at C = 128 from L2 a chunk ahead (load_rec: the same loads on both
 // waves, so that the compiler's load counts are exact).  A vector-memory instruction
 // costs the CU's address and data path about as much whatever its width, and these small
 // loads on the recurrence waves took ~7 % of the chain's time at C = 64.
 template <int C, int SPW, bool PERCH>
 struct RecRegs {
-    u32x2 u[Cfg<C, SPW>::SPW][Cfg<C, SPW>::NT / 2];
+    u32x2 u[Cfg<C, SPW>::NT / 2];
     f32x4 gl[PERCH ? 4 : 1];
 };
 
 template <int C, int SPW, bool PERCH>
-__device__ __forceinline__ void load_rec(RecRegs<C, SPW, PERCH> &rg, const Work &wk, int c, int h, int lane) {
+__device__ __forceinline__ void load_rec(RecRegs<C, SPW, PERCH> &rg, const Work &wk, int c, int s, int h, int lane) {
     using F = Cfg<C, SPW>;
     using TL = Tile<C>;
     const __amdgpu_buffer_rsrc_t r = tile_rsrc<C, SPW>(wk, c);
 #pragma unroll
-    for (int s = 0; s < F::SPW; ++s)
-#pragma unroll
-        for (int t = 0; t < F::NT / 2; ++t)
-            rg.u[s][t] = __builtin_bit_cast(
-                u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, 8 * lane, TL::u(wk.slice * F::SPW + s, h * F::NT / 2 + t), 0));
+    for (int t = 0; t < F::NT / 2; ++t)
+        rg.u[t] = __builtin_bit_cast(
+            u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, 8 * lane, TL::u(wk.slice * F::SPW + s, h * F::NT / 2 + t), 0));
     if constexpr (PERCH) {
         // keys 64 h + 16 i + 4 G + q: 16 bytes at GL + 4 (16 (4 h + i) + 4 G)
 #pragma unroll
@@ -252,14 +253,13 @@ __device__ __forceinline__ void load_rec(RecRegs<C, SPW, PERCH> &rg, const Work 
 }
 
 template <int C, int SPW, bool PERCH>
-__device__ __forceinline__ void ring_rec(RecRegs<C, SPW, PERCH> &rg, const Smem<C, SPW> &sm, int c, int h, int lane) {
+__device__ __forceinline__ void ring_rec(RecRegs<C, SPW, PERCH> &rg, const Smem<C, SPW> &sm, int c, int s, int h,
+                                         int lane) {
     using F = Cfg<C, SPW>;
     const typename Smem<C, SPW>::Ops &ob = sm.ob[c % F::NB];
     const u32x2 *u = reinterpret_cast<const u32x2 *>(ob.ug);
 #pragma unroll
-    for (int s = 0; s < F::SPW; ++s)
-#pragma unroll
-        for (int t = 0; t < F::NT / 2; ++t) rg.u[s][t] = u[(s * F::NT + h * F::NT / 2 + t) * 64 + lane];
+    for (int t = 0; t < F::NT / 2; ++t) rg.u[t] = u[(s * F::NT + h * F::NT / 2 + t) * 64 + lane];
     if constexpr (PERCH) {
         const f32x4 *g = reinterpret_cast<const f32x4 *>(ob.ug + 64 * F::NU);
 #pragma unroll
@@ -269,7 +269,7 @@ __device__ __forceinline__ void ring_rec(RecRegs<C, SPW, PERCH> &rg, const Smem<
     }
 }
 
-// Recurrence wave h's halves of WN and Kl for one chunk, from its ring buffer.
+// Key half h of WN and Kl for one chunk, from its ring buffer.
 template <int C, int SPW>
 struct RingRegs {
     f16x8 w[Cfg<C, SPW>::NT][2];
@@ -296,122 +296,103 @@ __device__ __forceinline__ void read_ring_kl(RingRegs<C, SPW> &rr, const Smem<C,
         for (int i = 0; i < 4; ++i) rr.kl[i][kb] = ob.kl[((4 * h + i) * F::KB + kb) * 64 + lane];
 }
 
-// Chunk c on recurrence wave h, around barrier c: its halves of WN and Kl from ring buffer
-// c % NB, then per slice the partial, the exchange, the update; every WN and Kl fragment
-// serves all of the workgroup's slices.  with_u is 0 for the identity rows of a segment
-// (no U term).
+// Chunk c on the recurrence wave of slice s and key half h, around barrier c: its halves
+// of WN and Kl from ring buffer c % NB, then the partial, the exchange with the other key
+// half's wave, the update.  with_u is 0 for the identity rows of a segment (no U term).
 template <int C, int SPW, bool PERCH>
-__device__ __forceinline__ void rec_step(f32x4 (&st)[SPW][4], const RecRegs<C, SPW, PERCH> &rg, Smem<C, SPW> &sm,
-                                         int c, int h, int lane, bool with_u) {
+__device__ __forceinline__ void rec_step(f32x4 (&st)[4], const RecRegs<C, SPW, PERCH> &rg, Smem<C, SPW> &sm, int c,
+                                         int s, int h, int lane, bool with_u) {
     using F = Cfg<C, SPW>;
     RingRegs<C, SPW> cur;
     read_ring_w(cur, sm, c, h, lane);
     read_ring_kl(cur, sm, c, h, lane);
-    f16x8 sb[SPW][2];
-#pragma unroll
-    for (int s = 0; s < SPW; ++s)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                sb[s][j][e] = (hf)st[s][2 * j][e];
-                sb[s][j][4 + e] = (hf)st[s][2 * j + 1][e];
-            }
-    // U on this wave's half of the token tiles
-    f32x4 p[SPW][F::NT];
-#pragma unroll
-    for (int s = 0; s < SPW; ++s)
-#pragma unroll
-        for (int t = 0; t < F::NT; ++t) {
-            const f16x4 uu = __builtin_bit_cast(f16x4, rg.u[s][t % (F::NT / 2)]);
-            const bool add = with_u && t / (F::NT / 2) == h;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) p[s][t][q] = add ? (float)uu[q] : 0.f;
-        }
+    f16x8 sb[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int t = 0; t < F::NT; ++t)
+        for (int e = 0; e < 4; ++e) {
+            sb[j][e] = (hf)st[2 * j][e];
+            sb[j][4 + e] = (hf)st[2 * j + 1][e];
+        }
+    // U on this wave's half of the token tiles
+    f32x4 p[F::NT];
 #pragma unroll
-            for (int s = 0; s < SPW; ++s) p[s][t] = mfma(cur.w[t][j], sb[s][j], p[s][t]);
+    for (int t = 0; t < F::NT; ++t) {
+        const f16x4 uu = __builtin_bit_cast(f16x4, rg.u[t % (F::NT / 2)]);
+        const bool add = with_u && t / (F::NT / 2) == h;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) p[t][q] = add ? (float)uu[q] : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int t = 0; t < F::NT; ++t) p[t] = mfma(cur.w[t][j], sb[j], p[t]);
     f16x8 *xs = sm.xs[c & 1];
 #pragma unroll
-    for (int s = 0; s < SPW; ++s)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) xs[(4 * s + 2 * h + j) * 64 + lane] = sb[s][j];
+    for (int j = 0; j < 2; ++j) xs[(4 * s + 2 * h + j) * 64 + lane] = sb[j];
     // the decay of the state (off the partial's path)
+    if constexpr (PERCH) {
 #pragma unroll
-    for (int s = 0; s < SPW; ++s) {
-        if constexpr (PERCH) {
+        for (int i = 0; i < 4; ++i) st[i] *= rg.gl[i];
+    } else {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) st[s][i] *= rg.gl[i];
-        } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) st[s][i] *= rg.gl[0][0];
-        }
+        for (int i = 0; i < 4; ++i) st[i] *= rg.gl[0][0];
     }
-    f16x4 ph[SPW][F::NT];
+    f16x4 ph[F::NT];
 #pragma unroll
-    for (int s = 0; s < SPW; ++s)
+    for (int t = 0; t < F::NT; ++t)
 #pragma unroll
-        for (int t = 0; t < F::NT; ++t)
+        for (int q = 0; q < 4; ++q) ph[t][q] = (hf)p[t][q];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) ph[s][t][q] = (hf)p[s][t][q];
-#pragma unroll
-    for (int s = 0; s < SPW; ++s)
-#pragma unroll
-        for (int t = 0; t < F::NT; ++t) sm.pv[c & 1][h][s][t * 64 + lane] = __builtin_bit_cast(u32x2, ph[s][t]);
+    for (int t = 0; t < F::NT; ++t) sm.pv[c & 1][h][s][t * 64 + lane] = __builtin_bit_cast(u32x2, ph[t]);
     __syncthreads();
     // v = p_0 + p_1 from the fp16 partials (addition commutes exactly: every wave that
     // forms v gets the same values), then the update
+    f16x4 po[F::NT];
 #pragma unroll
-    for (int s = 0; s < SPW; ++s) {
-        f16x4 po[F::NT];
+    for (int t = 0; t < F::NT; ++t) po[t] = __builtin_bit_cast(f16x4, sm.pv[c & 1][h ^ 1][s][t * 64 + lane]);
+    f16x8 vb[F::KB];
 #pragma unroll
-        for (int t = 0; t < F::NT; ++t) po[t] = __builtin_bit_cast(f16x4, sm.pv[c & 1][h ^ 1][s][t * 64 + lane]);
-        f16x8 vb[F::KB];
+    for (int kb = 0; kb < F::KB; ++kb)
 #pragma unroll
-        for (int kb = 0; kb < F::KB; ++kb)
+        for (int e = 0; e < 4; ++e) {
+            vb[kb][e] = (hf)((float)ph[2 * kb][e] + (float)po[2 * kb][e]);
+            vb[kb][4 + e] = (hf)((float)ph[2 * kb + 1][e] + (float)po[2 * kb + 1][e]);
+        }
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                vb[kb][e] = (hf)((float)ph[s][2 * kb][e] + (float)po[2 * kb][e]);
-                vb[kb][4 + e] = (hf)((float)ph[s][2 * kb + 1][e] + (float)po[2 * kb + 1][e]);
-            }
+    for (int kb = 0; kb < F::KB; ++kb)
 #pragma unroll
-        for (int kb = 0; kb < F::KB; ++kb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) st[s][i] = mfma(cur.kl[i][kb], vb[kb], st[s][i]);
-    }
+        for (int i = 0; i < 4; ++i) st[i] = mfma(cur.kl[i][kb], vb[kb], st[i]);
 }
 
-// Recurrence wave h's run: barrier -1 (chunk 0 in the ring), then a barrier per chunk;
-// U and gl of chunk c come with its ring buffer, or (C = 128) those of chunk c + 1 are
-// loaded while chunk c runs.
+// The run of the recurrence wave of slice s and key half h: barrier -1 (chunk 0 in the
+// ring), then a barrier per chunk; U and gl of chunk c come with its ring buffer, or
+// (C = 128) those of chunk c + 1 are loaded while chunk c runs.
 template <int C, int SPW, bool PERCH>
-__device__ __forceinline__ void rec_run(f32x4 (&st)[SPW][4], Smem<C, SPW> &sm, const Work &wk, int h, int lane,
+__device__ __forceinline__ void rec_run(f32x4 (&st)[4], Smem<C, SPW> &sm, const Work &wk, int s, int h, int lane,
                                         bool with_u) {
     const int n = wk.nchunks;
     if constexpr (Cfg<C, SPW>::URING) {
         __syncthreads();
         for (int c = 0; c < n; c += 2) {   // two chunks per trip, as below
             RecRegs<C, SPW, PERCH> r0, r1;
-            ring_rec(r0, sm, c, h, lane);
-            rec_step(st, r0, sm, c, h, lane, with_u);
+            ring_rec(r0, sm, c, s, h, lane);
+            rec_step(st, r0, sm, c, s, h, lane, with_u);
             if (c + 1 >= n) break;
-            ring_rec(r1, sm, c + 1, h, lane);
-            rec_step(st, r1, sm, c + 1, h, lane, with_u);
+            ring_rec(r1, sm, c + 1, s, h, lane);
+            rec_step(st, r1, sm, c + 1, s, h, lane, with_u);
         }
         return;
     }
     RecRegs<C, SPW, PERCH> r0, r1;
-    load_rec(r0, wk, 0, h, lane);
+    load_rec(r0, wk, 0, s, h, lane);
     __syncthreads();
     for (int c = 0; c < n; c += 2) {
-        load_rec(r1, wk, c + 1, h, lane);
-        rec_step(st, r0, sm, c, h, lane, with_u);
+        load_rec(r1, wk, c + 1, s, h, lane);
+        rec_step(st, r0, sm, c, s, h, lane, with_u);
         if (c + 1 >= n) break;
-        load_rec(r0, wk, c + 2, h, lane);
-        rec_step(st, r1, sm, c + 1, h, lane, with_u);
+        load_rec(r0, wk, c + 2, s, h, lane);
+        rec_step(st, r1, sm, c + 1, s, h, lane, with_u);
     }
 }
 
@@ -612,7 +593,8 @@ __device__ __forceinline__ int longest_first(const int32_t *cu, int N, int r, in
 // fp16 to a.o0 (value rows) or a.e (identity rows); end states go to a.sseg (X
 // transposed).  gdn_seg.hip joins them.
 template <typename IO, int C, int SPW, bool SEG, bool PERCH>
-__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2))) void kda_chain_kernel(const KdaArgs a) {
+__global__ __launch_bounds__((Cfg<C, SPW>::THREADS))
+__attribute__((amdgpu_waves_per_eu(Cfg<C, SPW>::WPE, Cfg<C, SPW>::WPE))) void kda_chain_kernel(const KdaArgs a) {
     __shared__ Smem<C, SPW> sm;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -668,58 +650,51 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const size_t sbase = ((size_t)n * a.Hv + h) * (size_t)DV * DK;
     const int l16 = lane & 15, g4 = lane >> 4;
 
-    if (wave < 2) {
-        const int kh = wave;   // key half
-        // slice s: S^T rows (key channels) 64 kh + 16 i + 4 G + q, column = value channel
-        // dv0 + 16 s + m
-        f32x4 st[SPW][4];
+    if (wave < F::NRW) {
+        const int kh = wave & 1, sl = wave >> 1;   // key half, slice
+        // S^T rows (key channels) 64 kh + 16 i + 4 G + q, column = value channel r
+        const int r = wk.dv0 + 16 * sl + l16;
+        f32x4 st[4];
 #pragma unroll
-        for (int sl = 0; sl < SPW; ++sl)
+        for (int i = 0; i < 4; ++i) {
+            const int dk = 64 * kh + 16 * i + 4 * g4;
+            f32x4 x = zero4();
+            if (seg == 0 && a.s0) x = *reinterpret_cast<const f32x4 *>(a.s0 + sbase + (size_t)r * DK + dk);
+            if (ident) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int dk = 64 * kh + 16 * i + 4 * g4, r = wk.dv0 + 16 * sl + l16;
-                f32x4 x = zero4();
-                if (seg == 0 && a.s0) x = *reinterpret_cast<const f32x4 *>(a.s0 + sbase + (size_t)r * DK + dk);
-                if (ident) {
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) x[q] = dk + q == r ? 1.f : 0.f;
-                }
-                st[sl][i] = x;
+                for (int q = 0; q < 4; ++q) x[q] = dk + q == r ? 1.f : 0.f;
             }
-        if (wk.nchunks > 0) rec_run<C, SPW, PERCH>(st, sm, wk, kh, lane, !ident);
+            st[i] = x;
+        }
+        if (wk.nchunks > 0) rec_run<C, SPW, PERCH>(st, sm, wk, sl, kh, lane, !ident);
         if constexpr (SEG) {
             // segment 0's end state [row][key]; later segments' end states from zero and
             // from the identity (X) transposed, [key][row], as the join reads them
             float *sb = a.sseg + ((((size_t)n * a.Hv + h) * a.nseg + seg) * 2 + (ident ? 1 : 0)) * DV * DK;
 #pragma unroll
-            for (int sl = 0; sl < SPW; ++sl)
+            for (int i = 0; i < 4; ++i) {
+                const int dk = 64 * kh + 16 * i + 4 * g4;
+                if (seg > 0) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int dk = 64 * kh + 16 * i + 4 * g4, r = wk.dv0 + 16 * sl + l16;
-                    if (seg > 0) {
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) sb[(size_t)(dk + q) * DV + r] = st[sl][i][q];
-                    } else {
-                        *reinterpret_cast<f32x4 *>(sb + (size_t)r * DK + dk) = st[sl][i];
-                    }
+                    for (int q = 0; q < 4; ++q) sb[(size_t)(dk + q) * DV + r] = st[i][q];
+                } else {
+                    *reinterpret_cast<f32x4 *>(sb + (size_t)r * DK + dk) = st[i];
                 }
+            }
         } else if (a.sN) {
 #pragma unroll
-            for (int sl = 0; sl < SPW; ++sl)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    *reinterpret_cast<f32x4 *>(a.sN + sbase + (size_t)(wk.dv0 + 16 * sl + l16) * DK + 64 * kh + 16 * i +
-                                               4 * g4) = st[sl][i];
+            for (int i = 0; i < 4; ++i)
+                *reinterpret_cast<f32x4 *>(a.sN + sbase + (size_t)r * DK + 64 * kh + 16 * i + 4 * g4) = st[i];
         }
-    } else if (wk.nchunks > 0 && wave < 6) {
-        switch (wave) {
-            case 2: output_run<IO, C, SPW, SEG, 0>(sm, a, wk, lane, kind); break;
-            case 3: output_run<IO, C, SPW, SEG, 1>(sm, a, wk, lane, kind); break;
-            case 4: output_run<IO, C, SPW, SEG, 2>(sm, a, wk, lane, kind); break;
+    } else if (wk.nchunks > 0 && wave < F::NRW + 4) {
+        switch (wave - F::NRW) {
+            case 0: output_run<IO, C, SPW, SEG, 0>(sm, a, wk, lane, kind); break;
+            case 1: output_run<IO, C, SPW, SEG, 1>(sm, a, wk, lane, kind); break;
+            case 2: output_run<IO, C, SPW, SEG, 2>(sm, a, wk, lane, kind); break;
             default: output_run<IO, C, SPW, SEG, 3>(sm, a, wk, lane, kind); break;
         }
     } else if (wk.nchunks > 0) {
-        if (wave == 6) loader_run<C, SPW, false>(sm, wk, lane);
+        if (wave == F::NRW + 4) loader_run<C, SPW, false>(sm, wk, lane);
         else loader_run<C, SPW, true>(sm, wk, lane);
     }
 }
@@ -735,7 +710,7 @@ hipError_t chain_launch_c(const KdaArgs &a, bool f16, hipStream_t stream) {
     const unsigned long long groups = (unsigned long long)a.N * a.Hv * (SEG ? (unsigned long long)a.nseg : 1ull);
     const unsigned long long wgs = 8 * GS * ((groups + 7) / 8);
     if (wgs > 0x7fffffffULL) return hipErrorInvalidValue;
-    const dim3 grid((unsigned)wgs), block(kdachain::THREADS);
+    const dim3 grid((unsigned)wgs), block(kdachain::Cfg<C, SPW>::THREADS);
     if (f16) hipLaunchKernelGGL((kdachain::kda_chain_kernel<_Float16, C, SPW, SEG, PERCH>), grid, block, 0, stream, a);
     else hipLaunchKernelGGL((kdachain::kda_chain_kernel<__bf16, C, SPW, SEG, PERCH>), grid, block, 0, stream, a);
     return hipGetLastError();
