@@ -51,6 +51,7 @@ namespace gdn {
 namespace gdnmap {
 
 typedef _Float16 hf;
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int DK = 128;
 constexpr int THREADS = 256;
@@ -267,45 +268,47 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(C <= 64
     __syncthreads();
 
     // the decayed operands of the chain, fp16, from the rows in registers and LDS, as operand
-    // fragments (gdn_launch.h, Tile): Qg by the thread that loaded the row (8 channels: two
-    // lanes' 8-byte halves); Kl by key channel (lane: channels 2 lane and 2 lane + 1), four
-    // tokens 16 tb + 4 G .. + 3 at a time, the half of lane (G, channel) in fragment
-    // KL(channel / 16, tb / 2)
+    // fragments (gdn_launch.h, Tile), each as 16-byte pieces (one fragment lane's eight
+    // entries).  Qg by the threads that loaded the row: the piece of lane (G, row) holds
+    // channels 32 kb + 4 G .. + 3 and 32 kb + 16 + 4 G .. + 3, which row segments seg and
+    // seg ^ 2 (lanes l and l ^ 2) hold, so the two swap one half and each stores one piece.
+    // Kl by key channel (lane: channel 64 x + lane) and pair of token tiles kb: the piece of
+    // lane (G, channel) holds tokens 32 kb + 4 G .. + 3 and 32 kb + 16 + 4 G .. + 3.
     {
 #pragma unroll
         for (int p = 0; p < C / 16; ++p) {
             const int idx = tid + THREADS * p, row = idx >> 4, seg = idx & 15;
             const float gm = PRO ? s.gam[row] * s.rn[1][row] : s.gam[row];
+            f16x4 xq[2];
 #pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2) {
-                const int j = 8 * seg + 4 * h2;
-                f16x4 xq;
+            for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) xq[e] = (hf)(Cvt<IO>::to_f32(qv[p][4 * h2 + e]) * gm);
-                *reinterpret_cast<f16x4 *>(tile + Tile<C>::qg(row >> 4, j >> 5) + 16 * frag_lane(j, row & 15) +
-                                           frag_byte(j)) = xq;
-            }
+                for (int e = 0; e < 4; ++e) xq[h2][e] = (hf)(Cvt<IO>::to_f32(qv[p][4 * h2 + e]) * gm);
+            // channel j = 8 seg + 4 h2: G = 2 (seg & 1) + h2, upper half of the piece iff
+            // seg & 2, block kb = seg / 4
+            const int up = (seg >> 1) & 1;
+            const u32x2 send = __builtin_bit_cast(u32x2, up ? xq[0] : xq[1]);
+            u32x2 recv;
+            recv[0] = __shfl_xor(send[0], 2, 64);
+            recv[1] = __shfl_xor(send[1], 2, 64);
+            const f16x4 other = __builtin_bit_cast(f16x4, recv);
+            const f16x4 lo = up ? other : xq[0], hi = up ? xq[1] : other;
+            const f16x8 piece = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            const int G = 2 * (seg & 1) + up;
+            *reinterpret_cast<f16x8 *>(tile + Tile<C>::qg(row >> 4, seg >> 2) + 16 * (16 * G + (row & 15))) = piece;
         }
-        typedef IO v2 __attribute__((ext_vector_type(2)));
-        const int ch = 2 * lane;
-        for (int tb = wave; tb < NT; tb += 4) {
-            f16x4 kl[2][4];
+        for (int it = wave; it < 2 * (C / 32); it += 4) {
+            const int kb = it >> 1, ch = 64 * (it & 1) + lane;
+            f16x8 kl[4];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int t = 16 * tb + i;
-                const v2 kk = *reinterpret_cast<const v2 *>(&s.K()[t * XS + ch]);
+            for (int i = 0; i < 32; ++i) {
+                const int t = 32 * kb + i;
                 const float lm = PRO ? s.lam[t] * s.rn[0][t] : s.lam[t];
-                kl[0][i >> 2][i & 3] = (hf)(Cvt<IO>::to_f32(kk[0]) * lm);
-                kl[1][i >> 2][i & 3] = (hf)(Cvt<IO>::to_f32(kk[1]) * lm);
+                kl[(i & 15) >> 2][4 * (i >> 4) + (i & 3)] = (hf)(Cvt<IO>::to_f32(s.K()[t * XS + ch]) * lm);
             }
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int c = ch + j;
-#pragma unroll
-                for (int G = 0; G < 4; ++G)
-                    *reinterpret_cast<f16x4 *>(tile + Tile<C>::kl(c >> 4, tb >> 1) + 16 * (16 * G + (c & 15)) +
-                                               8 * (tb & 1)) = kl[j][G];
-            }
+            for (int G = 0; G < 4; ++G)
+                *reinterpret_cast<f16x8 *>(tile + Tile<C>::kl(ch >> 4, kb) + 16 * (16 * G + (ch & 15))) = kl[G];
         }
     }
 
