@@ -45,8 +45,10 @@ __device__ __forceinline__ Frag<_Float16> wy_frag_t(const _Float16 *x, int c0, i
 // lane holds token 16 I + l16 and four consecutive key channels of each of the two
 // channel tiles, which together are its 16-byte piece of fragment WN(I, wave) (stored
 // negated); U is taken as it stands (T (diag(beta) V)), so a lane holds four consecutive
-// tokens of one value channel, its 8-byte piece of U(slice, I).  DW / DU select the
-// products formed (kg or vb may be null for the other).
+// tokens of one value channel, its 8-byte piece of U(slice, I) for each of the wave's two
+// slices: lanes l and l ^ 1 swap one of them, so that the even lane stores both lanes'
+// pieces of the first slice and the odd lane both of the second, 16 bytes each.  DW / DU
+// select the products formed (kg or vb may be null for the other).
 template <int C, typename TT = float, bool DW = true, bool DU = true>
 __device__ __forceinline__ void wy_products(const TT *T, int as, const _Float16 *kg, const _Float16 *vb,
                                             char *tile, int wave, int l16, int g4) {
@@ -91,13 +93,21 @@ __device__ __forceinline__ void wy_products(const TT *T, int as, const _Float16 
             *reinterpret_cast<f16x8 *>(tile + Tile<C>::wn(I, wave) + 16 * lane) = w;
         }
         if constexpr (DU) {   // U[16I + 4 g4 + i][16 (2 wave + j) + l16]
+            typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+            f16x4 u[2];
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                f16x4 u;
+            for (int j = 0; j < 2; ++j)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) u[i] = (hf)acc[j][1][i];
-                *reinterpret_cast<f16x4 *>(tile + Tile<C>::u(2 * wave + j, I) + 8 * lane) = u;
-            }
+                for (int i = 0; i < 4; ++i) u[j][i] = (hf)acc[j][1][i];
+            const int odd = lane & 1;
+            const u32x2 send = __builtin_bit_cast(u32x2, odd ? u[0] : u[1]);
+            u32x2 recv;
+            recv[0] = __shfl_xor(send[0], 1, 64);
+            recv[1] = __shfl_xor(send[1], 1, 64);
+            const f16x4 other = __builtin_bit_cast(f16x4, recv);
+            const f16x4 lo = odd ? other : u[0], hi = odd ? u[1] : other;
+            const f16x8 piece = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            *reinterpret_cast<f16x8 *>(tile + Tile<C>::u(2 * wave + odd, I) + 8 * (lane & ~1)) = piece;
         }
     }
 }
@@ -108,8 +118,10 @@ __device__ __forceinline__ void wy_products(const TT *T, int as, const _Float16 
 template <int C>
 __device__ __forceinline__ void store_p_frag(char *tile, int I, int J, int l16, int g4, const f16x4 &x) {
     char *pf = tile + Tile<C>::p(I, J >> 1) + 16 * (16 * g4 + l16) + 8 * (J & 1);
-    *reinterpret_cast<f16x4 *>(pf) = x;
-    if (J == I && (I & 1) == 0) *reinterpret_cast<f16x4 *>(pf + 8) = f16x4{};
+    if (J == I && (I & 1) == 0)
+        *reinterpret_cast<f16x8 *>(pf) = f16x8{x[0], x[1], x[2], x[3], 0, 0, 0, 0};
+    else
+        *reinterpret_cast<f16x4 *>(pf) = x;
 }
 
 }  // namespace gdn
