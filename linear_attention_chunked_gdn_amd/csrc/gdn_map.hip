@@ -55,7 +55,7 @@ typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int DK = 128;
 constexpr int THREADS = 256;
-constexpr int XS = DK + 16;   // 16-bit row stride of the k and q tiles (288 B)
+constexpr int XS = DK + 8;   // 16-bit row stride of the k and q tiles (272 B)
 
 template <typename IO, int C>
 struct Cfg {
