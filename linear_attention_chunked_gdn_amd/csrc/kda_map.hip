@@ -273,9 +273,8 @@ __global__ __launch_bounds__(THREADS, 2) void kda_map_kernel(const KdaArgs a) {
             kgb[i][1] = (hf)(k1 * e1 * bt);
             f16x2 x;
             x[0] = (hf)((float)qv[0] * e0); x[1] = (hf)((float)qv[1] * e1);
-            // Qg(token tile b, channel block ch / 32): channels ch, ch + 1 share a lane's slots
-            const int j = ch & 31;
-            *reinterpret_cast<f16x2 *>(tile + Tile<CH>::qg(b, ch >> 5) + 16 * frag_lane(j, i) + frag_byte(j)) = x;
+            // Qg's rows of this wave, staged in F[0] (unused until the gram factors)
+            *reinterpret_cast<f16x2 *>(&s.F[0][t * XS + ch]) = x;
             kl[0][i >> 2][i & 3] = (hf)(k0 * l0);
             kl[1][i >> 2][i & 3] = (hf)(k1 * l1);
         }
@@ -288,6 +287,23 @@ __global__ __launch_bounds__(THREADS, 2) void kda_map_kernel(const KdaArgs a) {
                 *reinterpret_cast<f16x4 *>(tile + Tile<CH>::kl(c >> 4, b >> 1) + 16 * (16 * G + (c & 15)) + 8 * (b & 1)) =
                     kl[j][G];
         }
+        // Qg(b, kb) from the staged rows, one 16-byte store per fragment: lane (G, m) takes
+        // token 16 b + m, channels 32 kb + 4 G .. + 3 and 32 kb + 16 + 4 G .. + 3.  The rows
+        // are this wave's own, and only its own gram factors overwrite them after.
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        {
+            const hf *row = &s.F[0][(16 * b + l16) * XS];
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                const f16x4 lo = *reinterpret_cast<const f16x4 *>(row + 32 * kb + 4 * g4);
+                const f16x4 hi = *reinterpret_cast<const f16x4 *>(row + 32 * kb + 16 + 4 * g4);
+                *reinterpret_cast<f16x8 *>(tile + Tile<CH>::qg(b, kb) + 16 * lane) =
+                    f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         if (b == 0) {
             f32x2 gl;
             gl[0] = F0[15] * post0;
