@@ -205,10 +205,28 @@ __global__ __launch_bounds__(THREADS, 2) void kda_map_kernel(const KdaArgs a) {
     float braw = 0.f;
     if (wave == 0) braw = a.beta[(size_t)(tok0 + min(lane, nval - 1)) * a.Hv + h];
 
-    // #1 Gate, per channel: a = exp(g) for this lane's two channels and 16 tokens; k and
-    // q go straight to LDS
-    typedef IO v2 __attribute__((ext_vector_type(2)));
+    // k and q rows of this wave's 16-token block straight to LDS in fp16, four rows per load
+    // (lane: row 4 p + lane / 16 of the block, channels 8 (lane % 16) .. + 7)
     const int b = wave, ch = 2 * lane;
+    {
+        typedef IO v8 __attribute__((ext_vector_type(8)));
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const int t = 16 * b + 4 * p + (lane >> 4), c8 = 8 * (lane & 15);
+            const size_t kq = ((size_t)(tok0 + min(t, nval - 1)) * a.Hk + hk) * DK + c8;
+            const v8 kk = *reinterpret_cast<const v8 *>(reinterpret_cast<const IO *>(a.k) + kq);
+            const v8 qq = *reinterpret_cast<const v8 *>(reinterpret_cast<const IO *>(a.q) + kq);
+            f16x8 kh, qh;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                kh[e] = (hf)Cvt<IO>::to_f32(kk[e]);
+                qh[e] = (hf)Cvt<IO>::to_f32(qq[e]);
+            }
+            *reinterpret_cast<f16x8 *>(&s.kq.K[t * XS + c8]) = kh;
+            *reinterpret_cast<f16x8 *>(&s.kq.Q[t * XS + c8]) = qh;
+        }
+    }
+    // #1 Gate, per channel: a = exp(g) for this lane's two channels and 16 tokens
     float a0[16], a1[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -218,16 +236,6 @@ __global__ __launch_bounds__(THREADS, 2) void kda_map_kernel(const KdaArgs a) {
         const bool ok = t < nval;
         a0[i] = ok ? exp2f(gg[0] * LOG2E) : 1.f;
         a1[i] = ok ? exp2f(gg[1] * LOG2E) : 1.f;
-        const size_t kq = (tok * a.Hk + hk) * DK + ch;
-        const v2 kk = *reinterpret_cast<const v2 *>(reinterpret_cast<const IO *>(a.k) + kq);
-        const v2 qq = *reinterpret_cast<const v2 *>(reinterpret_cast<const IO *>(a.q) + kq);
-        f16x2 kh, qh;
-        kh[0] = (hf)Cvt<IO>::to_f32(kk[0]);
-        kh[1] = (hf)Cvt<IO>::to_f32(kk[1]);
-        qh[0] = (hf)Cvt<IO>::to_f32(qq[0]);
-        qh[1] = (hf)Cvt<IO>::to_f32(qq[1]);
-        *reinterpret_cast<f16x2 *>(&s.kq.K[t * XS + ch]) = kh;
-        *reinterpret_cast<f16x2 *>(&s.kq.Q[t * XS + ch]) = qh;
     }
     if (wave == 0) s.beta[lane] = lane < nval ? braw : 0.f;
     // products inside the block: F inclusive from the block start, B exclusive to its end
@@ -362,11 +370,13 @@ __global__ __launch_bounds__(THREADS, 2) void kda_map_kernel(const KdaArgs a) {
     __syncthreads();
     // round 3: levels 2 and 1, and the diagonal of P itself; v of this thread's tokens and
     // channels is fetched here for the WY products
-    v2 vp[16];
+    // (four rows per load: lane = row 4 p + lane / 16 of the block, channels 8 (lane % 16) ..)
+    typedef IO v8 __attribute__((ext_vector_type(8)));
+    v8 vp[4];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const size_t tok = (size_t)(tok0 + min(16 * b + i, nval - 1));
-        vp[i] = *reinterpret_cast<const v2 *>(reinterpret_cast<const IO *>(a.v) + (tok * a.Hv + h) * DK + ch);
+    for (int p = 0; p < 4; ++p) {
+        const size_t tok = (size_t)(tok0 + min(16 * b + 4 * p + (lane >> 4), nval - 1));
+        vp[p] = *reinterpret_cast<const v8 *>(reinterpret_cast<const IO *>(a.v) + (tok * a.Hv + h) * DK + 8 * (lane & 15));
     }
     {
         float f0[16], f1[16], h0[16], h1[16];
@@ -395,14 +405,15 @@ __global__ __launch_bounds__(THREADS, 2) void kda_map_kernel(const KdaArgs a) {
     __syncthreads();   // the factor tiles and k, q are dead; A and T overlay the former,
                        // the WY right-hand sides the latter
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int t = 16 * b + i;
+    for (int i = 0; i < 16; ++i) *reinterpret_cast<f16x2 *>(&s.wy.Kb[(16 * b + i) * WY_S + ch]) = kgb[i];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const int t = 16 * b + 4 * p + (lane >> 4);
         const float bt = s.beta[t];
-        f16x2 x;
-        x[0] = (hf)(Cvt<IO>::to_f32(vp[i][0]) * bt);
-        x[1] = (hf)(Cvt<IO>::to_f32(vp[i][1]) * bt);
-        *reinterpret_cast<f16x2 *>(&s.wy.Kb[t * WY_S + ch]) = kgb[i];
-        *reinterpret_cast<f16x2 *>(&s.wy.Vb[t * WY_S + ch]) = x;
+        f16x8 x;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = (hf)(Cvt<IO>::to_f32(vp[p][e]) * bt);
+        *reinterpret_cast<f16x8 *>(&s.wy.Vb[t * WY_S + 8 * (lane & 15)]) = x;
     }
     {
         // A: this wave's diagonal tile, its tiles below the diagonal, zeros right of the
