@@ -32,6 +32,15 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
+// A lane's value from lane l ^ 2 and from lane l ^ 1 of its group of four, by DPP quad
+// permutations (2, 3, 0, 1) and (1, 0, 3, 2): a VALU move, no LDS round trip.
+__device__ __forceinline__ unsigned from_lane_xor2(unsigned x) {
+    return (unsigned)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, false);
+}
+__device__ __forceinline__ unsigned from_lane_xor1(unsigned x) {
+    return (unsigned)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, false);
+}
+
 __device__ __forceinline__ float bf16_to_f32(__bf16 x) {
     return __uint_as_float(static_cast<uint32_t>(__builtin_bit_cast(uint16_t, x)) << 16);
 }

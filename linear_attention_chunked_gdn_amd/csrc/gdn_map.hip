@@ -289,8 +289,8 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(C <= 64
             const int up = (seg >> 1) & 1;
             const u32x2 send = __builtin_bit_cast(u32x2, up ? xq[0] : xq[1]);
             u32x2 recv;
-            recv[0] = __shfl_xor(send[0], 2, 64);
-            recv[1] = __shfl_xor(send[1], 2, 64);
+            recv[0] = from_lane_xor2(send[0]);
+            recv[1] = from_lane_xor2(send[1]);
             const f16x4 other = __builtin_bit_cast(f16x4, recv);
             const f16x4 lo = up ? other : xq[0], hi = up ? xq[1] : other;
             const f16x8 piece = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};

@@ -102,8 +102,8 @@ __device__ __forceinline__ void wy_products(const TT *T, int as, const _Float16 
             const int odd = lane & 1;
             const u32x2 send = __builtin_bit_cast(u32x2, odd ? u[0] : u[1]);
             u32x2 recv;
-            recv[0] = __shfl_xor(send[0], 1, 64);
-            recv[1] = __shfl_xor(send[1], 1, 64);
+            recv[0] = from_lane_xor1(send[0]);
+            recv[1] = from_lane_xor1(send[1]);
             const f16x4 other = __builtin_bit_cast(f16x4, recv);
             const f16x4 lo = odd ? other : u[0], hi = odd ? u[1] : other;
             const f16x8 piece = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
