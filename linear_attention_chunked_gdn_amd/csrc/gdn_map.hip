@@ -111,54 +111,78 @@ static_assert(Cfg<__bf16, 64>::T16_OFF >= Cfg<__bf16, 64>::M_BYTES &&
 static_assert(sizeof(Smem<__bf16, 64, true>) <= 160 * 1024 / 4 && sizeof(Smem<_Float16, 64, true>) <= 160 * 1024 / 4,
               "four chunk-64 workgroups share a CU's LDS");
 
-// Tile (I, J), I >= J, of A and P.  The product is taken transposed (K_J X_I^T), so the
-// lane holds row r = 16I + l16 and columns 16J + 4g4 .. 16J + 4g4 + 3; P goes to the
-// workspace as fp16 (its half of fragment P(I, J / 2)), the beta-scaled A is returned (it
-// goes to LDS once every wave is done reading the k and q tiles it would overlay).
+// Tiles (I, 2 kb) and (I, 2 kb + 1) of A and P, the second only where it is on or below
+// the diagonal (2 kb + 1 <= I).  The products are taken transposed (K_J X_I^T), so the
+// lane holds row r = 16I + l16 and columns 16J + 4g4 .. 16J + 4g4 + 3 of each; both P
+// tiles go to the workspace as fp16 in one 16-byte piece of fragment P(I, kb) (zeros for
+// a missing second tile), the beta-scaled A tiles are returned (they go to LDS once every
+// wave is done reading the k and q tiles they would overlay).
 template <typename IO, int C, bool PRO>
-__device__ __forceinline__ f32x4 gram_tile(const Smem<IO, C, PRO> &s, char *tile, int I, int J, int l16, int g4) {
-    f32x4 accA = zero4(), accP = zero4();
+__device__ __forceinline__ void gram_pair(const Smem<IO, C, PRO> &s, char *tile, int I, int kb, int l16, int g4,
+                                          f32x4 (&va)[2]) {
+    const bool two = 2 * kb + 1 <= I;
+    f32x4 accA[2] = {zero4(), zero4()}, accP[2] = {zero4(), zero4()};
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-        Frag<IO> kj, ki, qi;
-        kj.load8(s.K() + (16 * J + l16) * XS + 32 * kb + 8 * g4);
-        ki.load8(s.K() + (16 * I + l16) * XS + 32 * kb + 8 * g4);
-        qi.load8(s.Q() + (16 * I + l16) * XS + 32 * kb + 8 * g4);
-        mma(accA, kj, ki);
-        mma(accP, kj, qi);
-    }
-    const int r = 16 * I + l16, c0 = 16 * J + 4 * g4;
-    const float gr = s.gcum[r], br = s.beta[r];
-    f32x4 va;
-    f16x4 hp;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int c = c0 + i;
-        const float d = c <= r ? __expf(gr - s.gcum[c]) : 0.f;
-        float da = d, dp = d;
-        if constexpr (PRO) {   // the rows' and columns' reciprocal norms
-            da *= s.rn[0][r] * s.rn[0][c];
-            dp *= s.rn[1][r] * s.rn[0][c];
+    for (int k = 0; k < 4; ++k) {
+        Frag<IO> ki, qi, kj;
+        ki.load8(s.K() + (16 * I + l16) * XS + 32 * k + 8 * g4);
+        qi.load8(s.Q() + (16 * I + l16) * XS + 32 * k + 8 * g4);
+        kj.load8(s.K() + (32 * kb + l16) * XS + 32 * k + 8 * g4);
+        mma(accA[0], kj, ki);
+        mma(accP[0], kj, qi);
+        if (two) {
+            kj.load8(s.K() + (32 * kb + 16 + l16) * XS + 32 * k + 8 * g4);
+            mma(accA[1], kj, ki);
+            mma(accP[1], kj, qi);
         }
-        va[i] = c < r ? br * accA[i] * da : 0.f;
-        hp[i] = (hf)(accP[i] * dp);
     }
-    store_p_frag<C>(tile, I, J, l16, g4, hp);
-    return va;
+    const int r = 16 * I + l16;
+    const float gr = s.gcum[r], br = s.beta[r];
+    f16x8 hp = {};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int c0 = 32 * kb + 16 * h + 4 * g4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int c = c0 + i;
+            const float d = c <= r ? __expf(gr - s.gcum[c]) : 0.f;
+            float da = d, dp = d;
+            if constexpr (PRO) {   // the rows' and columns' reciprocal norms
+                da *= s.rn[0][r] * s.rn[0][c];
+                dp *= s.rn[1][r] * s.rn[0][c];
+            }
+            va[h][i] = c < r ? br * accA[h][i] * da : 0.f;
+            hp[4 * h + i] = (hf)(accP[h][i] * dp);
+        }
+    }
+    // a missing second tile lies above the diagonal: d = 0 there, so its half is zeros
+    *reinterpret_cast<f16x8 *>(tile + Tile<C>::p(I, kb) + 16 * (16 * g4 + l16)) = hp;
 }
 
-// The lower tiles (I, J), I >= J, numbered row by row: job j <-> (I, J)
-__device__ __forceinline__ void tile_of_job(int j, int &I, int &J) {
-    I = 0;
-    while ((I + 1) * (I + 2) / 2 <= j) ++I;
-    J = j - I * (I + 1) / 2;
+// The pairs (I, kb) of P fragments, numbered for the waves: first those with two tiles
+// (2 kb + 1 <= I, row by row), then the diagonal fragments of even I with one; job j <->
+// (I, kb).  Row I has (I + 1) / 2 pairs of the first kind.
+template <int NT>
+__device__ __forceinline__ void pair_of_job(int j, int &I, int &kb) {
+    constexpr int N2 = (NT / 2) * (NT / 2);   // sum over I < NT of (I + 1) / 2
+    if (j >= N2) {
+        I = 2 * (j - N2);
+        kb = j - N2;
+        return;
+    }
+    I = 1;
+    while (j >= (I + 1) / 2) {
+        j -= (I + 1) / 2;
+        ++I;
+    }
+    kb = j;
 }
 
 template <typename IO, int C, bool PRO>
 __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(C <= 64 ? 4 : 1))) void gdn_map_kernel(const KdaArgs a) {
     using F = Cfg<IO, C>;
     constexpr int NT = F::NT, AS = F::AS;
-    constexpr int NJOBS = NT * (NT + 1) / 2;
+    constexpr int NJOBS = Tile<C>::NPF;       // P fragments: pairs of gram tiles
     constexpr int JPW = (NJOBS + 3) / 4;   // gram jobs per wave
     __shared__ Smem<IO, C, PRO> s;
     const int tid = threadIdx.x;
@@ -314,14 +338,14 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(C <= 64
 
     // #2 the lower 16x16 tiles of A and P, round-robin over the waves; zeros for P's tiles
     // above the diagonal.  A stays in registers until every wave is done with k and q.
-    f32x4 av[JPW];
+    f32x4 av[JPW][2];
 #pragma unroll
     for (int k = 0; k < JPW; ++k) {
         const int j = wave + 4 * k;
         if (j < NJOBS) {
-            int I, J;
-            tile_of_job(j, I, J);
-            av[k] = gram_tile(s, tile, I, J, l16, g4);
+            int I, kb;
+            pair_of_job<NT>(j, I, kb);
+            gram_pair(s, tile, I, kb, l16, g4, av[k]);
         }
     }
     __syncthreads();   // k and q are dead: A and T go over them
@@ -332,10 +356,15 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(C <= 64
     for (int k = 0; k < JPW; ++k) {
         const int j = wave + 4 * k;
         if (j < NJOBS) {
-            int I, J;
-            tile_of_job(j, I, J);
+            int I, kb;
+            pair_of_job<NT>(j, I, kb);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) M[(16 * J + 4 * g4 + i) * AS + 16 * I + l16] = av[k][i];
+            for (int h = 0; h < 2; ++h) {
+                const int J = 2 * kb + h;
+                if (J > I) break;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) M[(16 * J + 4 * g4 + i) * AS + 16 * I + l16] = av[k][h][i];
+            }
         }
     }
     __syncthreads();
