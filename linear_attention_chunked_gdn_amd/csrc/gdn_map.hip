@@ -336,8 +336,9 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(C <= 64
         }
     }
 
-    // #2 the lower 16x16 tiles of A and P, round-robin over the waves; zeros for P's tiles
-    // above the diagonal.  A stays in registers until every wave is done with k and q.
+    // #2 the lower 16x16 tiles of A and P, in pairs per P fragment (pair_of_job's order),
+    // round-robin over the waves; zeros for P's tiles above the diagonal.  A stays in
+    // registers until every wave is done with k and q.
     f32x4 av[JPW][2];
 #pragma unroll
     for (int k = 0; k < JPW; ++k) {
